@@ -1,0 +1,202 @@
+"""Plain fp64 CPU oracle for the unified linear-attention recurrence.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and
+the CPU-baseline leg of ``bench.py`` may import this package.  It shares no
+code with the GPU library: the arithmetic lives in ``oracle.c`` (fp64, libm,
+pthreads over (batch, head) pairs) and this module only marshals numpy arrays
+through ctypes.
+
+Forms (all compute the same function; see ``oracle.c`` for the citations):
+
+* :func:`run`        -- the token-by-token recurrence, the definition.
+* :func:`parallel`   -- the all-pairs masked form with direct decay products.
+* :func:`chunkwise`  -- the chunkwise form with a ragged last chunk.
+
+Layouts follow the GPU boundary: q, k ``[B,H,L,dk]``, v and out
+``[B,H,L,dv]``, S ``[B,H,dk,dv]`` (rows indexed by the key channel), z
+``[B,H,dk]``, gamma ``[H]``, log_alpha ``[B,H,L,dk]``.  2-D ``[L,d]`` inputs
+are treated as B = H = 1.
+
+Parity: every form is pinned by tests that do not call the oracle's own
+formula (the pages' worked examples, closed forms, textbook masked matmuls,
+chunk-size invariance and state hand-off invariants).
+"""
+from __future__ import annotations
+
+import contextlib
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+GATE_NONE, GATE_GAMMA, GATE_DIAG = 0, 1, 2
+PHI_IDENTITY, PHI_ELU1 = 0, 1
+
+# Planted mistakes (test-only), mirrored from oracle.c.
+MUTATIONS = {
+    "z_frozen": 1,
+    "no_divide": 2,
+    "read_before_update": 3,
+    "transposed_state": 4,
+    "decay_after_add": 5,
+    "phi_on_v": 6,
+    "gate_dropped": 7,
+    "cross_off_by_one": 8,
+    "state_off_by_one": 9,
+    "gamma_squared": 10,
+}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile ``oracle.c`` into ``liboracle.so`` (gcc, -O2, no fast-math)."""
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(
+            ["gcc", "-O2", "-std=c99", "-fPIC", "-shared", "-pthread",
+             "-Wall", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=False)
+        lib = ctypes.CDLL(_LIB)
+        dp = ctypes.POINTER(ctypes.c_double)
+        i = ctypes.c_int
+        common = [i, i, i, i, i, i, dp, dp, i, i, dp, dp, dp, dp, dp]
+        lib.oracle_run.argtypes = common + [dp, dp, dp, i]
+        lib.oracle_parallel.argtypes = common + [dp, dp, dp]
+        lib.oracle_chunkwise.argtypes = common + [i, dp, dp, dp, i]
+        for f in (lib.oracle_run, lib.oracle_parallel, lib.oracle_chunkwise):
+            f.restype = ctypes.c_int
+        lib.oracle_multiscale_decays.argtypes = [i, dp]
+        lib.oracle_phi.argtypes = [i, ctypes.c_double]
+        lib.oracle_phi.restype = ctypes.c_double
+        lib.oracle_set_mutation.argtypes = [i]
+        _lib = lib
+    return _lib
+
+
+def _f64(x):
+    if x is None:
+        return None
+    if hasattr(x, "detach"):  # torch tensor
+        x = x.detach().cpu().double().numpy()
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(a):
+    if a is None:
+        return None
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def _prep(q, k, v, gate_mode, gamma, log_alpha, S0, z0):
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    two_d = q.ndim == 2
+    if two_d:
+        q, k, v = q[None, None], k[None, None], v[None, None]
+    if q.ndim != 4 or k.shape != q.shape or v.shape[:3] != q.shape[:3]:
+        raise ValueError("q, k must be [B,H,L,dk] and v [B,H,L,dv]")
+    B, H, L, dk = q.shape
+    dv = v.shape[3]
+    g = la = None
+    if gate_mode == GATE_GAMMA:
+        g = _f64(np.broadcast_to(np.asarray(gamma, dtype=np.float64).reshape(-1), (H,)))
+    elif gate_mode == GATE_DIAG:
+        la = _f64(log_alpha)
+        if two_d and la.ndim == 2:
+            la = la[None, None]
+        la = np.ascontiguousarray(np.broadcast_to(la, (B, H, L, dk)))
+    elif gate_mode != GATE_NONE:
+        raise ValueError("unknown gate mode")
+    S0 = _f64(S0)
+    z0 = _f64(z0)
+    if S0 is not None:
+        S0 = np.ascontiguousarray(S0.reshape(B, H, dk, dv))
+    if z0 is not None:
+        z0 = np.ascontiguousarray(z0.reshape(B, H, dk))
+    return two_d, (B, H, L, dk, dv), q, k, v, g, la, S0, z0
+
+
+def _finish(two_d, out, S, z):
+    if two_d:
+        return out[0, 0], S[0, 0], z[0, 0]
+    return out, S, z
+
+
+def _call(fn, extra_mid, extra_tail, q, k, v, gate_mode, gamma, log_alpha,
+          phi, normalize, S0, z0):
+    two_d, (B, H, L, dk, dv), q, k, v, g, la, S0, z0 = _prep(
+        q, k, v, gate_mode, gamma, log_alpha, S0, z0)
+    out = np.zeros((B, H, L, dv))
+    S = np.zeros((B, H, dk, dv))
+    z = np.zeros((B, H, dk))
+    args = [B, H, L, dk, dv, int(gate_mode), _ptr(g), _ptr(la), int(phi),
+            int(bool(normalize)), _ptr(q), _ptr(k), _ptr(v), _ptr(S0), _ptr(z0)]
+    args += extra_mid + [_ptr(out), _ptr(S), _ptr(z)] + extra_tail
+    rc = fn(*args)
+    if rc != 0:
+        raise ValueError(f"oracle rejected its arguments (rc={rc})")
+    return _finish(two_d, out, S, z)
+
+
+def run(q, k, v, gate_mode=GATE_NONE, gamma=None, log_alpha=None,
+        phi=PHI_IDENTITY, normalize=False, S0=None, z0=None, nthreads=1):
+    """Token-by-token recurrence. Returns ``(out, S_final, z_final)`` (fp64)."""
+    lib = _load()
+    return _call(lib.oracle_run, [], [int(nthreads)], q, k, v, gate_mode,
+                 gamma, log_alpha, phi, normalize, S0, z0)
+
+
+def parallel(q, k, v, gate_mode=GATE_NONE, gamma=None, log_alpha=None,
+             phi=PHI_IDENTITY, normalize=False, S0=None, z0=None):
+    """All-pairs masked form (tiny L only). Returns ``(out, S_final, z_final)``."""
+    lib = _load()
+    return _call(lib.oracle_parallel, [], [], q, k, v, gate_mode, gamma,
+                 log_alpha, phi, normalize, S0, z0)
+
+
+def chunkwise(q, k, v, chunk, gate_mode=GATE_NONE, gamma=None, log_alpha=None,
+              phi=PHI_IDENTITY, normalize=False, S0=None, z0=None, nthreads=1):
+    """Chunkwise form with chunk length ``chunk``."""
+    lib = _load()
+    return _call(lib.oracle_chunkwise, [int(chunk)], [int(nthreads)], q, k, v,
+                 gate_mode, gamma, log_alpha, phi, normalize, S0, z0)
+
+
+def multiscale_decays(n: int) -> np.ndarray:
+    """gamma_h = 1 - 2^(-5-h) for h = 0..n-1 (multi-scale retention)."""
+    lib = _load()
+    out = np.zeros(n)
+    lib.oracle_multiscale_decays(int(n), _ptr(out))
+    return out
+
+
+def phi(kind: int, x: float) -> float:
+    """The feature map as the oracle evaluates it (identity or elu+1)."""
+    return _load().oracle_phi(int(kind), float(x))
+
+
+@contextlib.contextmanager
+def mutation(name: str):
+    """Plant a known mistake in the oracle for the duration of the block.
+
+    Used only by the mutation tests that show each pin catches a plausible
+    error.  Not thread-safe with concurrent oracle calls.
+    """
+    lib = _load()
+    lib.oracle_set_mutation(MUTATIONS[name])
+    try:
+        yield
+    finally:
+        lib.oracle_set_mutation(0)

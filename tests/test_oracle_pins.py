@@ -1,0 +1,412 @@
+"""Pins for the fp64 oracle: values, closed forms and invariants fixed by the
+pages and by mathematics, none of which re-runs the oracle's own formula.
+
+Sources (page title, section):
+* "Linear attention and hybrid models", Part 1: Example 1.1 and "Your turn"
+  (tests/golden/worked_example_1_1.json, tests/golden/your_turn.json).
+* "Module 22: Linear & Recurrent Attention": the two faces of linear
+  attention (parallel == recurrent), incremental decoding, the three faces of
+  retention (parallel == recurrent == chunkwise at L=12, d=6, gamma=0.9,
+  chunk 4), the gamma -> 1 / gamma -> 0 limits, multi-scale decays
+  (tests/golden/multiscale_decays.json), the gated exercise.
+* "linear_sparse_attention.py": checks [a] chunkwise == recurrent for
+  C in {1, 4, 7, L} at L = 13 (ragged), [b] chunk-size invariance, [c] the
+  state is d_k x d_v whatever L is.
+
+The textbook references below are written with numpy matrix products
+(masked (Q K^T * D) V); they are independent of the oracle's C loops.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _elu1(x):
+    return np.where(x > 0, x + 1.0, np.exp(np.minimum(x, 0.0)))
+
+
+def _seed0(L, d, n=3):
+    torch.manual_seed(0)
+    return [torch.randn(L, d).double().numpy() for _ in range(n)]
+
+
+# ---------------------------------------------------------------- worked examples
+
+def _normalised_identity(keys, values, query):
+    """Run the oracle with identity phi and the normaliser on; the query is
+    placed at the last token (earlier queries are (1,1) and unused)."""
+    keys = np.array(keys, float)
+    values = np.array(values, float)
+    q = np.ones_like(keys)
+    q[-1] = query
+    return oracle.run(q, keys, values, phi=oracle.PHI_IDENTITY, normalize=True)
+
+
+def test_worked_example_1_1():
+    g = _golden("worked_example_1_1.json")
+    out, S, z = _normalised_identity(g["keys"], g["values"], g["query"])
+    q = np.array(g["query"], float)
+    assert np.array_equal(S, np.array(g["S"], float))
+    assert np.array_equal(z, np.array(g["z"], float))
+    assert np.array_equal(q @ S, np.array(g["qT_S"], float))
+    assert q @ z == g["q_dot_z"]
+    assert np.array_equal(out[-1], np.array(g["answer"], float))
+    # the direct route of the example: score, blend, divide
+    keys = np.array(g["keys"], float)
+    assert np.array_equal(keys @ q, np.array(g["scores"], float))
+
+
+def test_your_turn():
+    g = _golden("your_turn.json")
+    out, S, z = _normalised_identity(g["keys"], g["values"], g["query"])
+    q = np.array(g["query"], float)
+    assert np.array_equal(S, np.array(g["S"], float))
+    assert np.array_equal(z, np.array(g["z"], float))
+    assert np.array_equal(q @ S, np.array(g["qT_S"], float))
+    assert q @ z == g["q_dot_z"]
+    expected = np.array(g["qT_S"], float) / g["q_dot_z"]
+    assert np.array_equal(out[-1], expected)          # (1.5, 2.5)
+    assert np.array_equal(expected, np.array([1.5, 2.5]))
+
+
+def test_your_turn_distractors_come_from_planted_mistakes():
+    """The wrong answers the page names are what the planted mistakes give."""
+    g = _golden("your_turn.json")
+    keys = np.array(g["keys"], float)
+    values = np.array(g["values"], float)
+    q = np.ones_like(keys)
+    q[-1] = g["query"]
+    # first two tokens correctly, then the third with z left alone
+    _, S2, z2 = oracle.run(q[:2], keys[:2], values[:2], normalize=True)
+    with oracle.mutation("z_frozen"):
+        o3, _, _ = oracle.run(q[2:], keys[2:], values[2:], normalize=True,
+                              S0=S2, z0=z2)
+    assert np.allclose(o3[0], g["distractor_z_left_alone"], atol=5e-3)
+    with oracle.mutation("no_divide"):
+        o, _, _ = oracle.run(q, keys, values, normalize=True)
+    assert np.array_equal(o[-1], np.array(g["distractor_no_divide"], float))
+
+
+# ---------------------------------------------------------------- feature map
+
+def test_feature_map_closed_form():
+    assert oracle.phi(oracle.PHI_ELU1, 2.0) == 3.0
+    assert oracle.phi(oracle.PHI_ELU1, 0.0) == 1.0
+    assert oracle.phi(oracle.PHI_ELU1, -1.0) == math.exp(-1.0)
+    assert oracle.phi(oracle.PHI_ELU1, -800.0) == 0.0
+    assert oracle.phi(oracle.PHI_IDENTITY, -3.5) == -3.5
+
+
+def test_phi_positive_and_output_shape():
+    # seed 0, L=6, d=8 as in the first linear-attention code cell
+    Q, K, V = _seed0(6, 8)
+    assert (_elu1(K) > 0).all()
+    out, S, z = oracle.run(Q, K, V, phi=oracle.PHI_ELU1, normalize=True)
+    assert out.shape == (6, 8) and S.shape == (8, 8) and z.shape == (8,)
+
+
+# ---------------------------------------------------------------- textbook forms
+
+def _linear_parallel_textbook(Q, K, V):
+    """Masked score matrix A_ij = phi(q_i).phi(k_j), j <= i, rows normalised."""
+    A = np.tril(_elu1(Q) @ _elu1(K).T)
+    return (A @ V) / A.sum(axis=1, keepdims=True)
+
+
+def _retention_parallel_textbook(Q, K, V, gamma):
+    """(Q K^T * D) V with D_nm = gamma^(n-m) for n >= m, else 0; 0^0 = 1."""
+    L = Q.shape[0]
+    n = np.arange(L)[:, None]
+    m = np.arange(L)[None, :]
+    with np.errstate(divide="ignore"):
+        D = np.where(n >= m, np.power(float(gamma), np.maximum(n - m, 0)), 0.0)
+    return (Q @ K.T * D) @ V
+
+
+def test_linear_two_faces_agree():
+    Q, K, V = _seed0(6, 8)
+    out, _, _ = oracle.run(Q, K, V, phi=oracle.PHI_ELU1, normalize=True)
+    assert np.allclose(out, _linear_parallel_textbook(Q, K, V), rtol=0, atol=1e-12)
+    par, _, _ = oracle.parallel(Q, K, V, phi=oracle.PHI_ELU1, normalize=True)
+    assert np.allclose(par, out, rtol=0, atol=1e-12)
+
+
+def test_incremental_decode_equals_full():
+    Q, K, V = _seed0(6, 8)
+    full, Sf, zf = oracle.run(Q, K, V, phi=oracle.PHI_ELU1, normalize=True)
+    S = z = None
+    rows = []
+    for t in range(6):
+        o, S, z = oracle.run(Q[t:t + 1], K[t:t + 1], V[t:t + 1],
+                             phi=oracle.PHI_ELU1, normalize=True, S0=S, z0=z)
+        rows.append(o[0])
+    assert np.allclose(np.stack(rows), full, rtol=0, atol=1e-12)
+    assert np.allclose(S, Sf, atol=1e-12) and np.allclose(z, zf, atol=1e-12)
+
+
+def test_retention_three_faces():
+    torch.manual_seed(0)
+    Q, K, V = (torch.randn(12, 6).double().numpy() for _ in range(3))
+    ref = _retention_parallel_textbook(Q, K, V, 0.9)
+    kw = dict(gate_mode=oracle.GATE_GAMMA, gamma=[0.9])
+    rec, _, _ = oracle.run(Q, K, V, **kw)
+    par, _, _ = oracle.parallel(Q, K, V, **kw)
+    chk, _, _ = oracle.chunkwise(Q, K, V, 4, **kw)
+    for got in (rec, par, chk):
+        assert np.allclose(got, ref, rtol=0, atol=1e-12)
+
+
+def test_gamma_one_is_unnormalised_causal_attention():
+    Q, K, V = _seed0(9, 5)
+    ref = np.tril(Q @ K.T) @ V
+    out, _, _ = oracle.run(Q, K, V, gate_mode=oracle.GATE_GAMMA, gamma=[1.0])
+    assert np.allclose(out, ref, rtol=0, atol=1e-12)
+    out2, _, _ = oracle.run(Q, K, V)                       # A_t = 1
+    assert np.allclose(out2, ref, rtol=0, atol=1e-12)
+
+
+def test_gamma_zero_keeps_only_the_diagonal():
+    Q, K, V = _seed0(9, 5)
+    ref = (Q * K).sum(axis=1, keepdims=True) * V
+    for form in (oracle.run, oracle.parallel):
+        out, S, _ = form(Q, K, V, gate_mode=oracle.GATE_GAMMA, gamma=[0.0])
+        assert np.allclose(out, ref, rtol=0, atol=1e-12)
+        assert np.allclose(S, np.outer(K[-1], V[-1]), atol=1e-12)
+    for C in (1, 4, 9):
+        out, _, _ = oracle.chunkwise(Q, K, V, C, gate_mode=oracle.GATE_GAMMA,
+                                     gamma=[0.0])
+        assert np.allclose(out, ref, rtol=0, atol=1e-12)
+
+
+def test_multiscale_decays_printed_values():
+    g = _golden("multiscale_decays.json")
+    got = oracle.multiscale_decays(g["n"])
+    assert [round(x, 4) for x in got.tolist()] == g["printed"]
+    assert np.array_equal(got, 1.0 - 2.0 ** (-5.0 - np.arange(4)))
+
+
+# ---------------------------------------------------------------- gated (diagonal)
+
+def _diag_textbook(Q, K, V, log_alpha, S0=None):
+    """o_t = sum_{s<=t} sum_i q_ti k_si exp(sum_{r=s+1..t} la_ri) v_s
+             + sum_i q_ti exp(sum_{r<=t} la_ri) S0[i,:]   (cumulative sums)."""
+    L, dk = Q.shape
+    cs = np.concatenate([np.zeros((1, dk)), np.cumsum(log_alpha, axis=0)])  # cs[t+1]
+    out = np.zeros((L, V.shape[1]))
+    for t in range(L):
+        for s in range(t + 1):
+            w = np.exp(cs[t + 1] - cs[s + 1])
+            out[t] += (Q[t] * K[s] * w).sum() * V[s]
+        if S0 is not None:
+            out[t] += (Q[t] * np.exp(cs[t + 1])) @ S0
+    return out
+
+
+@pytest.mark.parametrize("with_state", [False, True])
+def test_diag_gate_matches_cumulative_sum_form(with_state):
+    rng = np.random.default_rng(3)
+    L, dk, dv = 7, 3, 4
+    Q, K = rng.standard_normal((L, dk)), rng.standard_normal((L, dk))
+    V = rng.standard_normal((L, dv))
+    la = -rng.uniform(0.0, 1.5, size=(L, dk))
+    S0 = rng.standard_normal((dk, dv)) if with_state else None
+    ref = _diag_textbook(Q, K, V, la, S0)
+    kw = dict(gate_mode=oracle.GATE_DIAG, log_alpha=la, S0=S0)
+    for got in (oracle.run(Q, K, V, **kw)[0], oracle.parallel(Q, K, V, **kw)[0],
+                oracle.chunkwise(Q, K, V, 3, **kw)[0]):
+        assert np.allclose(got, ref, rtol=0, atol=1e-12)
+
+
+def test_diag_reduces_to_gamma_and_to_none():
+    rng = np.random.default_rng(4)
+    B, H, L, d = 2, 3, 10, 4
+    q, k, v = (rng.standard_normal((B, H, L, d)) for _ in range(3))
+    gam = np.array([0.5, 0.9, 0.99])
+    la = np.broadcast_to(np.log(gam)[None, :, None, None], (B, H, L, d))
+    a, Sa, _ = oracle.run(q, k, v, gate_mode=oracle.GATE_DIAG, log_alpha=la)
+    b, Sb, _ = oracle.run(q, k, v, gate_mode=oracle.GATE_GAMMA, gamma=gam)
+    assert np.allclose(a, b, rtol=1e-12, atol=1e-12)
+    assert np.allclose(Sa, Sb, rtol=1e-12, atol=1e-12)
+    c, _, _ = oracle.run(q, k, v, gate_mode=oracle.GATE_DIAG,
+                         log_alpha=np.zeros((B, H, L, d)))
+    e, _, _ = oracle.run(q, k, v)
+    assert np.array_equal(c, e)
+
+
+def test_gated_output_differs_from_any_fixed_decay():
+    """You-are-the-gate exercise: high gate (0.95) at positions 2 and 5, low
+    (0.1) elsewhere; no single retention decay reproduces it."""
+    Q, K, V = _seed0(8, 4)
+    gate = np.full(8, 0.1)
+    gate[[2, 5]] = 0.95
+    la = np.log(gate)[:, None] * np.ones((8, 4))
+    gated, _, _ = oracle.run(Q, K, V, gate_mode=oracle.GATE_DIAG, log_alpha=la)
+    for gamma in np.linspace(0.0, 1.0, 21):
+        ret, _, _ = oracle.run(Q, K, V, gate_mode=oracle.GATE_GAMMA, gamma=[gamma])
+        assert np.abs(gated - ret).max() > 1e-3
+
+
+# ---------------------------------------------------------------- chunkwise form
+
+MODES = [
+    dict(gate_mode=oracle.GATE_NONE),
+    dict(gate_mode=oracle.GATE_NONE, phi=oracle.PHI_ELU1, normalize=True),
+    dict(gate_mode=oracle.GATE_GAMMA, gamma=[0.9, 0.5]),
+    dict(gate_mode=oracle.GATE_GAMMA, gamma=[0.0, 1.0]),
+    dict(gate_mode=oracle.GATE_DIAG),
+    dict(gate_mode=oracle.GATE_DIAG, phi=oracle.PHI_ELU1, normalize=True),
+]
+
+
+def _mode_inputs(mode, B=1, H=2, L=13, d=6, seed=0):
+    torch.manual_seed(seed)
+    q, k, v = (torch.randn(B, H, L, d).double().numpy() for _ in range(3))
+    kw = dict(mode)
+    if kw["gate_mode"] == oracle.GATE_DIAG:
+        kw["log_alpha"] = torch.nn.functional.logsigmoid(
+            torch.randn(B, H, L, d)).double().numpy()
+    S0 = torch.randn(B, H, d, d).double().numpy()
+    z0 = 1.0 + np.abs(torch.randn(B, H, d).double().numpy())
+    return q, k, v, kw, S0, z0
+
+
+@pytest.mark.parametrize("mode", MODES)
+@pytest.mark.parametrize("with_state", [False, True])
+def test_chunkwise_equals_recurrent_for_every_chunk(mode, with_state):
+    """Check [a]/[b]: L = 13 (ragged for C = 4, 7), C in {1, 4, 7, L}."""
+    q, k, v, kw, S0, z0 = _mode_inputs(mode)
+    st = dict(S0=S0, z0=z0) if with_state else {}
+    ref, Sr, zr = oracle.run(q, k, v, **kw, **st)
+    outs = []
+    for C in (1, 4, 7, 13):
+        o, S, z = oracle.chunkwise(q, k, v, C, **kw, **st)
+        assert np.allclose(o, ref, rtol=1e-12, atol=1e-12)
+        assert np.allclose(S, Sr, rtol=1e-12, atol=1e-12)
+        assert np.allclose(z, zr, rtol=1e-12, atol=1e-12)
+        outs.append(o)
+    for o in outs[1:]:
+        assert np.allclose(o, outs[0], rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_parallel_form_equals_recurrent(mode):
+    q, k, v, kw, S0, z0 = _mode_inputs(mode, L=9, d=4)
+    ref = oracle.run(q, k, v, **kw, S0=S0, z0=z0)
+    got = oracle.parallel(q, k, v, **kw, S0=S0, z0=z0)
+    for a, b in zip(got, ref):
+        assert np.allclose(a, b, rtol=1e-11, atol=1e-11)
+
+
+def test_state_shape_is_independent_of_length():
+    shapes = set()
+    for L in (1, 5, 13, 40):
+        q, k, v = _seed0(L, 6)
+        _, S, z = oracle.run(q, k, v)
+        shapes.add(S.shape)
+    assert shapes == {(6, 6)}
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_state_hand_off(mode):
+    """run(L1) then run(L2 from its final state) == run(L1 + L2); with L2 = 1
+    this is prefill followed by one decode step."""
+    q, k, v, kw, S0, z0 = _mode_inputs(mode, L=13)
+    ref, Sr, zr = oracle.run(q, k, v, **kw, S0=S0, z0=z0)
+    for L1 in (5, 12):
+        kw1, kw2 = dict(kw), dict(kw)
+        if "log_alpha" in kw:
+            kw1["log_alpha"] = kw["log_alpha"][:, :, :L1]
+            kw2["log_alpha"] = kw["log_alpha"][:, :, L1:]
+        o1, S1, z1 = oracle.run(q[:, :, :L1], k[:, :, :L1], v[:, :, :L1], **kw1,
+                                S0=S0, z0=z0)
+        o2, S2, z2 = oracle.run(q[:, :, L1:], k[:, :, L1:], v[:, :, L1:], **kw2,
+                                S0=S1, z0=z1)
+        assert np.allclose(np.concatenate([o1, o2], axis=2), ref, rtol=1e-12, atol=1e-12)
+        assert np.allclose(S2, Sr, rtol=1e-12, atol=1e-12)
+        assert np.allclose(z2, zr, rtol=1e-12, atol=1e-12)
+
+
+def test_initial_state_is_decayed_by_the_first_gate():
+    """S_1 = A_1 S_0 + k_1^T v_1: with a zero key the first output reads the
+    once-decayed initial state."""
+    S0 = np.arange(12, dtype=float).reshape(3, 4)
+    q = np.array([[1.0, -2.0, 0.5]])
+    k = np.zeros((1, 3))
+    v = np.ones((1, 4))
+    la = np.log(np.array([[0.5, 0.25, 1.0]]))
+    out, S, _ = oracle.run(q, k, v, gate_mode=oracle.GATE_DIAG, log_alpha=la, S0=S0)
+    expect_S = np.array([0.5, 0.25, 1.0])[:, None] * S0
+    assert np.allclose(S, expect_S, atol=1e-15)
+    assert np.allclose(out[0], q[0] @ expect_S, atol=1e-14)
+
+
+def test_threads_do_not_change_results():
+    rng = np.random.default_rng(7)
+    q, k, v = (rng.standard_normal((3, 4, 20, 5)) for _ in range(3))
+    a = oracle.run(q, k, v, gate_mode=oracle.GATE_GAMMA, gamma=[0.9] * 4, nthreads=1)
+    b = oracle.run(q, k, v, gate_mode=oracle.GATE_GAMMA, gamma=[0.9] * 4, nthreads=5)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+def test_chunkwise_matches_loop_at_larger_size():
+    """Self-consistency at a size beyond the hand-checkable ones."""
+    rng = np.random.default_rng(11)
+    L, d = 300, 16
+    q, k, v = (rng.standard_normal((1, 2, L, d)) / 4 for _ in range(3))
+    la = -rng.uniform(0, 0.2, size=(1, 2, L, d))
+    a = oracle.run(q, k, v, gate_mode=oracle.GATE_DIAG, log_alpha=la)
+    b = oracle.chunkwise(q, k, v, 64, gate_mode=oracle.GATE_DIAG, log_alpha=la)
+    for x, y in zip(a, b):
+        assert np.abs(x - y).max() <= 1e-12 * max(1.0, np.abs(x).max())
+
+
+# ---------------------------------------------------------------- mutation check
+
+def _pin_failures():
+    """Run the pins above and return the names of those that fail."""
+    checks = {
+        "worked_example": test_worked_example_1_1,
+        "your_turn": test_your_turn,
+        "two_faces": test_linear_two_faces_agree,
+        "three_faces": test_retention_three_faces,
+        "gamma_one": test_gamma_one_is_unnormalised_causal_attention,
+        "gamma_zero": test_gamma_zero_keeps_only_the_diagonal,
+        "diag_textbook": lambda: test_diag_gate_matches_cumulative_sum_form(True),
+        "first_gate": test_initial_state_is_decayed_by_the_first_gate,
+    }
+    for i, mode in enumerate(MODES):
+        checks[f"chunk_invariance_{i}"] = (
+            lambda m=mode: test_chunkwise_equals_recurrent_for_every_chunk(m, True))
+    failed = []
+    for name, fn in checks.items():
+        try:
+            with np.errstate(all="ignore"):
+                fn()
+        except AssertionError:
+            failed.append(name)
+    return failed
+
+
+def test_pins_pass_on_the_correct_oracle():
+    assert _pin_failures() == []
+
+
+@pytest.mark.parametrize("name", sorted(oracle.MUTATIONS))
+def test_every_planted_mistake_is_caught(name):
+    with oracle.mutation(name):
+        failed = _pin_failures()
+    assert failed, f"planted mistake {name!r} passed every pin"
