@@ -1,0 +1,182 @@
+/*
+ * la.h -- C ABI of liblinattn, causal linear attention run as the unified
+ * recurrence on MI355X (gfx950).
+ *
+ * The operation (per batch b, head h; "Module 22: Linear & Recurrent
+ * Attention", section "Interactive Exploration: The One Recurrence Behind
+ * Them All", with the feature map and normaliser of section "The Math:
+ * Linear Attention"):
+ *
+ *     S_t = A_t S_{t-1} + phi(k_t)^T v_t          S is d_k x d_v, fp32
+ *     z_t = A_t z_{t-1} + phi(k_t)                 (only when normalising)
+ *     o_t = phi(q_t) S_t   [ / (phi(q_t) . z_t) ]  read after the update
+ *
+ * with the gate A_t = 1 (linear attention), a per-head scalar gamma
+ * (retention, section "Retention: Add a Decay to the State") or a diagonal
+ * d_k x d_k gate exp(log_alpha_t) (gated linear attention, the
+ * input-dependent row of the gate table).  Under a gate, z is decayed by the
+ * same A_t as S.  There is no epsilon in the divide.
+ *
+ * la_chunk_fwd computes a whole prefill in the chunkwise-parallel form
+ * ("Module 22", section "The Three Faces of Retention"; "linear_sparse_
+ * attention.py", linear_attn_chunkwise, including a ragged last chunk):
+ * inside a chunk the in-chunk causal (decay-masked) scores times V plus the
+ * query times the carried state; between chunks the carried state update.
+ * la_decode_step folds one new token per (b,h) into a resident state, the
+ * recurrent face ("Module 22", incremental decoding with a running state;
+ * "causal linear attention as an RNN").
+ *
+ * Conventions shared by every entry point
+ *  - Layouts are dense and row-major with the last index fastest:
+ *      q, k  [B,H,L,dk]   v, out [B,H,L,dv]   (dtype of la_desc.dtype)
+ *      S     [B,H,dk,dv]  fp32, rows indexed by the key channel
+ *      z     [B,H,dk]     fp32
+ *      log_alpha [B,H,L,dk] fp32 natural-log gates, every value <= 0
+ *  - Device pointers are device (HBM) addresses; `gamma` is a host array.
+ *  - The caller owns every buffer.  The library never allocates device
+ *    memory, frees or synchronises; work is enqueued on `stream` (a
+ *    hipStream_t; NULL = the null stream) and runs asynchronously.
+ *  - Validation runs on the host before anything is enqueued; on any error
+ *    nothing is enqueued, the status is returned and a message is available
+ *    from la_last_error_message() (thread-local).  No C++ exception crosses
+ *    the ABI.
+ *  - Device pointers must be 16-byte aligned.
+ *  - log_alpha is read on the device and is not validated; values > 0 are
+ *    outside the contract.
+ */
+#ifndef LINATTN_LA_H
+#define LINATTN_LA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define LA_VERSION 1
+#define LA_MAX_GAMMA_HEADS 256 /* heads supported with LA_GATE_GAMMA */
+
+typedef enum la_status {
+    LA_OK = 0,
+    LA_ERR_INVALID = 1,     /* bad argument (checked on the host)         */
+    LA_ERR_UNSUPPORTED = 2, /* valid, but outside the built kernel shapes */
+    LA_ERR_HIP = 3          /* the HIP runtime reported an error          */
+} la_status;
+
+typedef enum la_gate_mode {
+    LA_GATE_NONE = 0,  /* A_t = 1                                          */
+    LA_GATE_GAMMA = 1, /* A_t = gamma[h]; host float[H], 0 <= gamma <= 1     */
+    LA_GATE_DIAG = 2   /* A_t = diag(exp(log_alpha[b,h,t,:])); device fp32   */
+} la_gate_mode;
+
+typedef enum la_dtype { LA_F32 = 0, LA_BF16 = 1 } la_dtype;
+
+typedef enum la_phi {
+    LA_PHI_IDENTITY = 0, /* phi(x) = x                                      */
+    LA_PHI_ELU1 = 1      /* phi(x) = elu(x) + 1: x + 1 if x > 0, else exp(x) */
+} la_phi;
+
+typedef struct la_desc {
+    int B, H;      /* batch, heads (>= 1)                                   */
+    int L;         /* tokens per sequence (>= 1); must be 1 for decode      */
+    int dk, dv;    /* key and value width                                    */
+    int dtype;     /* la_dtype of q, k, v and out (states are always fp32)  */
+    int phi;       /* la_phi, applied to q and k only                        */
+    int normalize; /* 1: divide by phi(q).z and carry z; 0: no z at all     */
+    int segments;  /* prefill: sequence segments per (b,h) that run in
+                      parallel and are joined by a state scan; 0 = choose
+                      automatically, otherwise 1..ceil(L/chunk)             */
+} la_desc;
+
+/*
+ * Supported kernel shapes (else LA_ERR_UNSUPPORTED):
+ *   dk == dv, dk in {16, 32, 64, 128}; chunk in {16, 32, 64}.
+ *   LA_F32 runs fp32 matrix cores (no bf16 rounding); LA_BF16 runs bf16
+ *   matrix cores with fp32 accumulation and fp32 states.
+ *   LA_GATE_GAMMA needs H <= LA_MAX_GAMMA_HEADS.
+ *   LA_GATE_DIAG: the factorised in-chunk form multiplies by exp of the
+ *   chunk-local cumulative log-gate measured from the chunk middle, so the
+ *   per-channel sum of log_alpha over any half chunk must stay above about
+ *   -80 (e.g. mean log_alpha >= -2.5 per token at chunk 64); beyond that
+ *   fp32 overflows.  Use a smaller chunk for stronger gates.
+ */
+
+/*
+ * la_chunk_fwd -- chunkwise-parallel prefill of L tokens per (b,h).
+ *   d                  shape, dtype, phi, normalize, segments
+ *   q, k, v            device, [B,H,L,dk|dv] of d->dtype, read only
+ *   gate_mode          la_gate_mode
+ *   gamma_or_log_alpha NONE: ignored (may be NULL); GAMMA: host float[H];
+ *                      DIAG: device float[B,H,L,dk]
+ *   S0, z0             device fp32 initial state [B,H,dk,dv] and [B,H,dk];
+ *                      NULL = zeros.  z0 must be NULL unless normalize.
+ *   chunk              chunk length C (see supported shapes)
+ *   out                device [B,H,L,dv] of d->dtype, written
+ *   S_final, z_final   device fp32 final state / normaliser, or NULL (not
+ *                      returned).  They may alias S0 / z0 (in-place
+ *                      resumption).  z_final must be NULL unless normalize.
+ *   workspace          device scratch of at least
+ *                      la_chunk_fwd_workspace_bytes(d, chunk) bytes (may be
+ *                      NULL when that is 0); contents are clobbered
+ *   stream             hipStream_t
+ */
+la_status la_chunk_fwd(const la_desc* d, const void* q, const void* k,
+                       const void* v, int gate_mode,
+                       const float* gamma_or_log_alpha, const float* S0,
+                       const float* z0, int chunk, void* out, float* S_final,
+                       float* z_final, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/* Bytes of device workspace la_chunk_fwd needs for this shape (segment
+ * states, their decays and normaliser parts); 0 for a single segment.
+ * Returns 0 for an invalid descriptor as well. */
+size_t la_chunk_fwd_workspace_bytes(const la_desc* d, int chunk);
+
+/* Number of segments la_chunk_fwd will run per (b,h) for this shape. */
+int la_chunk_fwd_segments(const la_desc* d, int chunk);
+
+/*
+ * la_decode_step -- fold one token per (b,h) into the resident state.
+ *   d          shape with d->L == 1 (B = sequences, H = heads)
+ *   q, k, v    device [B,H,dk|dv] of d->dtype
+ *   gate_mode  la_gate_mode
+ *   gate       NONE: ignored; GAMMA: host float[H]; DIAG: device fp32
+ *              log-gates [B,H,dk]
+ *   S          device fp32 [B,H,dk,dv], updated in place to A S + phi(k) v^T
+ *   z          device fp32 [B,H,dk], updated in place; NULL iff !normalize
+ *   out        device [B,H,dv] of d->dtype: phi(q)^T S_new [/ phi(q).z_new]
+ *   stream     hipStream_t
+ */
+la_status la_decode_step(const la_desc* d, const void* q, const void* k,
+                         const void* v, int gate_mode, const float* gate,
+                         float* S, float* z, void* out, void* stream);
+
+/* Static description of a status code. */
+const char* la_status_string(la_status s);
+
+/* Detail of the last error returned on the calling thread ("" if none). */
+const char* la_last_error_message(void);
+
+/* LA_VERSION of the built library. */
+int la_version(void);
+
+/*
+ * Kernel timing for benchmarks.  Between la_profile_begin() and
+ * la_profile_end() every kernel the library enqueues is bracketed by a pair
+ * of HIP events recorded on the stream it is launched on.  la_profile_query
+ * waits for those events and reports, for one kernel family
+ * ("chunk_main", "chunk_state", "state_scan", "decode"), the number of
+ * launches and their summed duration in milliseconds.  la_profile_begin
+ * clears earlier records.  Event creation happens inside la_profile_begin /
+ * the first profiled launch; not for use under graph capture.
+ */
+la_status la_profile_begin(void);
+la_status la_profile_end(void);
+la_status la_profile_query(const char* kernel, int* launches,
+                           double* total_ms);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LINATTN_LA_H */

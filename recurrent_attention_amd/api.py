@@ -1,0 +1,271 @@
+"""Thin ctypes binding of ``liblinattn.so`` (the C ABI of ``include/la.h``).
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity and their data pointers are handed to the library, which runs
+every step on the GPU.  Outputs and workspaces that the caller does not pass
+are allocated with torch (device memory is PyTorch's job here).  There is no
+CPU fallback: a missing library or a tensor that is not on a GPU raises.
+
+Functions named ``la_*`` mirror the C entry points one to one;
+:func:`chunk_fwd` and :func:`decode_step` are conveniences around them.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+LA_OK, LA_ERR_INVALID, LA_ERR_UNSUPPORTED, LA_ERR_HIP = 0, 1, 2, 3
+LA_GATE_NONE, LA_GATE_GAMMA, LA_GATE_DIAG = 0, 1, 2
+LA_F32, LA_BF16 = 0, 1
+LA_PHI_IDENTITY, LA_PHI_ELU1 = 0, 1
+LA_MAX_GAMMA_HEADS = 256
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "liblinattn.so")
+_lib = None
+
+# every symbol include/la.h declares
+EXPORTED = (
+    "la_chunk_fwd", "la_chunk_fwd_workspace_bytes", "la_chunk_fwd_segments",
+    "la_decode_step", "la_status_string", "la_last_error_message",
+    "la_version", "la_profile_begin", "la_profile_end", "la_profile_query",
+)
+
+
+class LaError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{message} (status {status})")
+        self.status = status
+
+
+class LaDesc(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int) for n in
+                ("B", "H", "L", "dk", "dv", "dtype", "phi", "normalize", "segments")]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load ``liblinattn.so`` (built by ``recurrent_attention_amd.build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(
+            f"{_LIB_PATH} is missing: build it with "
+            "`python -m recurrent_attention_amd.build` (there is no CPU fallback)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    dp = ctypes.POINTER(LaDesc)
+    fp = ctypes.POINTER(ctypes.c_float)
+    lib.la_chunk_fwd.argtypes = [dp, vp, vp, vp, i, vp, vp, vp, i, vp, vp, vp, vp, sz, vp]
+    lib.la_chunk_fwd.restype = i
+    lib.la_chunk_fwd_workspace_bytes.argtypes = [dp, i]
+    lib.la_chunk_fwd_workspace_bytes.restype = sz
+    lib.la_chunk_fwd_segments.argtypes = [dp, i]
+    lib.la_chunk_fwd_segments.restype = i
+    lib.la_decode_step.argtypes = [dp, vp, vp, vp, i, vp, vp, vp, vp, vp]
+    lib.la_decode_step.restype = i
+    lib.la_status_string.argtypes = [i]
+    lib.la_status_string.restype = ctypes.c_char_p
+    lib.la_last_error_message.argtypes = []
+    lib.la_last_error_message.restype = ctypes.c_char_p
+    lib.la_version.restype = i
+    lib.la_profile_begin.restype = i
+    lib.la_profile_end.restype = i
+    lib.la_profile_query.argtypes = [ctypes.c_char_p, ctypes.POINTER(i),
+                                     ctypes.POINTER(ctypes.c_double)]
+    lib.la_profile_query.restype = i
+    del fp
+    _lib = lib
+    return lib
+
+
+def _check(status):
+    if status != LA_OK:
+        lib = load_library()
+        raise LaError(status, lib.la_last_error_message().decode() or
+                      lib.la_status_string(status).decode())
+
+
+# ------------------------------------------------------------------ raw entry points
+
+def make_desc(B, H, L, dk, dv, dtype=LA_BF16, phi=LA_PHI_IDENTITY,
+              normalize=False, segments=0) -> LaDesc:
+    return LaDesc(int(B), int(H), int(L), int(dk), int(dv), int(dtype), int(phi),
+                  int(bool(normalize)), int(segments))
+
+
+def la_chunk_fwd(desc, q, k, v, gate_mode, gamma_or_log_alpha, S0, z0, chunk,
+                 out, S_final, z_final, workspace, workspace_bytes, stream):
+    """Raw call; pointer arguments are ints (0 = NULL) or ctypes pointers."""
+    return load_library().la_chunk_fwd(
+        ctypes.byref(desc), q, k, v, int(gate_mode), gamma_or_log_alpha, S0, z0,
+        int(chunk), out, S_final, z_final, workspace, int(workspace_bytes), stream)
+
+
+def la_decode_step(desc, q, k, v, gate_mode, gate, S, z, out, stream):
+    return load_library().la_decode_step(
+        ctypes.byref(desc), q, k, v, int(gate_mode), gate, S, z, out, stream)
+
+
+def la_chunk_fwd_workspace_bytes(desc, chunk) -> int:
+    return int(load_library().la_chunk_fwd_workspace_bytes(ctypes.byref(desc), int(chunk)))
+
+
+def la_chunk_fwd_segments(desc, chunk) -> int:
+    return int(load_library().la_chunk_fwd_segments(ctypes.byref(desc), int(chunk)))
+
+
+def la_status_string(status) -> str:
+    return load_library().la_status_string(int(status)).decode()
+
+
+def la_last_error_message() -> str:
+    return load_library().la_last_error_message().decode()
+
+
+def la_version() -> int:
+    return int(load_library().la_version())
+
+
+def la_profile_begin():
+    _check(load_library().la_profile_begin())
+
+
+def la_profile_end():
+    _check(load_library().la_profile_end())
+
+
+def la_profile_query(kernel: str):
+    """(launches, total_ms) recorded for one kernel family since begin."""
+    n = ctypes.c_int(0)
+    ms = ctypes.c_double(0.0)
+    _check(load_library().la_profile_query(kernel.encode(), ctypes.byref(n), ctypes.byref(ms)))
+    return n.value, ms.value
+
+
+# ------------------------------------------------------------------ torch conveniences
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dev_ptr(t, name, dtype=None):
+    if t is None:
+        return None
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device (got {t.device}); there is no CPU path")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    return t.data_ptr()
+
+
+def _stream_ptr(stream, device):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _la_dtype(t):
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return LA_BF16
+    if t.dtype == torch.float32:
+        return LA_F32
+    raise TypeError(f"q/k/v must be bfloat16 or float32 (got {t.dtype})")
+
+
+def _gamma_host(gamma, H):
+    torch = _torch()
+    g = torch.as_tensor(gamma, dtype=torch.float32).detach().cpu().reshape(-1)
+    if g.numel() == 1:
+        g = g.expand(H)
+    g = g.contiguous()
+    if g.numel() != H:
+        raise ValueError(f"gamma needs {H} values (got {g.numel()})")
+    return g
+
+
+def chunk_fwd(q, k, v, gate_mode=LA_GATE_NONE, gamma=None, log_alpha=None,
+              S0=None, z0=None, chunk=64, phi=LA_PHI_IDENTITY, normalize=False,
+              segments=0, out=None, S_final=None, z_final=None,
+              return_state=True, workspace=None, stream=None):
+    """Chunkwise prefill.  q, k: [B,H,L,dk]; v: [B,H,L,dv] (bf16 or fp32, on
+    the GPU).  Returns ``(out, S_final, z_final)``; the states are fp32 and
+    z_final is None unless ``normalize``."""
+    torch = _torch()
+    B, H, L, dk = q.shape
+    dv = v.shape[-1]
+    dt = _la_dtype(q)
+    desc = make_desc(B, H, L, dk, dv, dt, phi, normalize, segments)
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, H, L, dv), dtype=q.dtype, device=dev)
+    if return_state and S_final is None:
+        S_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    if return_state and normalize and z_final is None:
+        z_final = torch.empty((B, H, dk), dtype=torch.float32, device=dev)
+    need = la_chunk_fwd_workspace_bytes(desc, chunk)
+    if need and workspace is None:
+        workspace = torch.empty(need // 4 + 4, dtype=torch.float32, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    g_arg = None
+    g_keep = None
+    if gate_mode == LA_GATE_GAMMA:
+        g_keep = _gamma_host(gamma, H)
+        g_arg = ctypes.c_void_p(g_keep.data_ptr())
+    elif gate_mode == LA_GATE_DIAG:
+        g_arg = _dev_ptr(log_alpha, "log_alpha", torch.float32)
+    st = la_chunk_fwd(
+        desc, _dev_ptr(q, "q"), _dev_ptr(k, "k", q.dtype), _dev_ptr(v, "v", q.dtype),
+        gate_mode, g_arg, _dev_ptr(S0, "S0", torch.float32),
+        _dev_ptr(z0, "z0", torch.float32), chunk, _dev_ptr(out, "out", q.dtype),
+        _dev_ptr(S_final, "S_final", torch.float32),
+        _dev_ptr(z_final, "z_final", torch.float32),
+        _dev_ptr(workspace, "workspace"), ws_bytes, _stream_ptr(stream, dev))
+    _check(st)
+    del g_keep
+    return out, S_final, z_final
+
+
+def decode_step(q, k, v, S, z=None, gate_mode=LA_GATE_NONE, gamma=None,
+                log_alpha=None, phi=LA_PHI_IDENTITY, out=None, stream=None):
+    """One recurrent step.  q, k: [B,H,dk]; v: [B,H,dv]; S: [B,H,dk,dv] fp32
+    (updated in place); z: [B,H,dk] fp32 or None (normalise iff given).
+    Returns ``out`` [B,H,dv]."""
+    torch = _torch()
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    desc = make_desc(B, H, 1, dk, dv, _la_dtype(q), phi, z is not None, 0)
+    if out is None:
+        out = torch.empty((B, H, dv), dtype=q.dtype, device=q.device)
+    g_arg = None
+    g_keep = None
+    if gate_mode == LA_GATE_GAMMA:
+        g_keep = _gamma_host(gamma, H)
+        g_arg = ctypes.c_void_p(g_keep.data_ptr())
+    elif gate_mode == LA_GATE_DIAG:
+        g_arg = _dev_ptr(log_alpha, "log_alpha", torch.float32)
+    st = la_decode_step(
+        desc, _dev_ptr(q, "q"), _dev_ptr(k, "k", q.dtype), _dev_ptr(v, "v", q.dtype),
+        gate_mode, g_arg, _dev_ptr(S, "S", torch.float32), _dev_ptr(z, "z", torch.float32),
+        _dev_ptr(out, "out", q.dtype), _stream_ptr(stream, q.device))
+    _check(st)
+    del g_keep
+    return out
+
+
+def chunk_fwd_workspace_bytes(B, H, L, dk, dv, chunk, dtype=LA_BF16,
+                              normalize=False, segments=0) -> int:
+    return la_chunk_fwd_workspace_bytes(
+        make_desc(B, H, L, dk, dv, dtype, 0, normalize, segments), chunk)

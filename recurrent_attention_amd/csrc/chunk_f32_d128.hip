@@ -1,0 +1,6 @@
+// chunk_f32_d128.hip -- chunkwise prefill kernels for d_k = d_v = 128, f32 inputs.
+#include "chunk_kernel.h"
+
+namespace la {
+LA_DEFINE_CHUNK_LAUNCHER(launch_chunk_f32_d128, 128, false)
+}  // namespace la

@@ -1,0 +1,6 @@
+// chunk_f32_d64.hip -- chunkwise prefill kernels for d_k = d_v = 64, f32 inputs.
+#include "chunk_kernel.h"
+
+namespace la {
+LA_DEFINE_CHUNK_LAUNCHER(launch_chunk_f32_d64, 64, false)
+}  // namespace la

@@ -1,0 +1,347 @@
+// la_api.hip -- host side of the C ABI declared in include/la.h: argument
+// validation, the choice of sequence segments, launch sequencing and the
+// optional per-kernel event timing.  Nothing here allocates device memory or
+// synchronises outside the profiling query.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "la_internal.h"
+
+namespace {
+
+thread_local char g_errmsg[512] = "";
+
+la_status fail(la_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_errmsg, sizeof g_errmsg, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Workgroups the automatic segment choice aims for: one per compute unit of
+// an MI355X (256 CUs).
+constexpr int kTargetBlocks = 256;
+
+struct Plan {
+    int nchunks, P, cps;
+};
+
+Plan make_plan(const la_desc* d, int chunk) {
+    Plan pl;
+    pl.nchunks = (d->L + chunk - 1) / chunk;
+    const long bh = (long)d->B * d->H;
+    int P = d->segments;
+    if (P <= 0) P = (int)((kTargetBlocks + bh - 1) / bh);
+    if (P < 1) P = 1;
+    if (P > pl.nchunks) P = pl.nchunks;
+    pl.cps = (pl.nchunks + P - 1) / P;
+    pl.P = (pl.nchunks + pl.cps - 1) / pl.cps;  // every segment non-empty
+    return pl;
+}
+
+size_t workspace_bytes(const la_desc* d, const Plan& pl) {
+    if (pl.P <= 1) return 0;
+    const size_t slots = (size_t)d->B * d->H * pl.P;
+    return slots * ((size_t)d->dk * d->dv + 2 * (size_t)d->dk) * sizeof(float);
+}
+
+bool supported_d(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+bool supported_chunk(int c) { return c == 16 || c == 32 || c == 64; }
+
+la_status check_desc(const la_desc* d) {
+    if (!d) return fail(LA_ERR_INVALID, "descriptor is NULL");
+    if (d->B < 1 || d->H < 1 || d->L < 1 || d->dk < 1 || d->dv < 1)
+        return fail(LA_ERR_INVALID, "dimensions must be >= 1 (B=%d H=%d L=%d dk=%d dv=%d)", d->B,
+                    d->H, d->L, d->dk, d->dv);
+    if (d->dtype != LA_F32 && d->dtype != LA_BF16)
+        return fail(LA_ERR_INVALID, "unknown dtype %d", d->dtype);
+    if (d->phi != LA_PHI_IDENTITY && d->phi != LA_PHI_ELU1)
+        return fail(LA_ERR_INVALID, "unknown feature map %d", d->phi);
+    if (d->normalize != 0 && d->normalize != 1)
+        return fail(LA_ERR_INVALID, "normalize must be 0 or 1");
+    if (d->segments < 0) return fail(LA_ERR_INVALID, "segments must be >= 0");
+    if ((long long)d->B * d->H > (1LL << 24))
+        return fail(LA_ERR_UNSUPPORTED, "B*H = %lld exceeds 2^24", (long long)d->B * d->H);
+    if (!supported_d(d->dk) || d->dk != d->dv)
+        return fail(LA_ERR_UNSUPPORTED, "built shapes need dk == dv in {16,32,64,128} (dk=%d dv=%d)",
+                    d->dk, d->dv);
+    if (d->dtype == LA_BF16 && d->dk < 32)
+        return fail(LA_ERR_UNSUPPORTED, "bf16 inputs need dk >= 32 (dk=%d)", d->dk);
+    return LA_OK;
+}
+
+la_status check_gate(const la_desc* d, int gate_mode, const float* g, bool device_diag,
+                     float* log2_gamma, float* gamma) {
+    if (gate_mode == LA_GATE_NONE) return LA_OK;
+    if (gate_mode == LA_GATE_GAMMA) {
+        if (!g) return fail(LA_ERR_INVALID, "GAMMA gate needs a host gamma[H] array");
+        if (d->H > LA_MAX_GAMMA_HEADS)
+            return fail(LA_ERR_UNSUPPORTED, "GAMMA gate supports at most %d heads (H=%d)",
+                        LA_MAX_GAMMA_HEADS, d->H);
+        for (int h = 0; h < d->H; ++h) {
+            const float x = g[h];
+            if (!(x >= 0.0f && x <= 1.0f))
+                return fail(LA_ERR_INVALID, "gamma[%d] = %g is outside [0, 1]", h, (double)x);
+            if (log2_gamma) log2_gamma[h] = x > 0.0f ? (float)std::log2((double)x) : -INFINITY;
+            if (gamma) gamma[h] = x;
+        }
+        return LA_OK;
+    }
+    if (gate_mode == LA_GATE_DIAG) {
+        if (!g) return fail(LA_ERR_INVALID, "DIAG gate needs a device log-gate array");
+        if (device_diag && !aligned16(g)) return fail(LA_ERR_INVALID, "log-gate pointer is not 16-byte aligned");
+        return LA_OK;
+    }
+    return fail(LA_ERR_INVALID, "unknown gate mode %d", gate_mode);
+}
+
+// ------------------------------------------------------------------ profiling
+struct ProfRec {
+    int kernel;
+    hipEvent_t a, b;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfRec> g_prof;
+std::vector<hipEvent_t> g_event_pool;
+
+const char* kKernelNames[la::K_COUNT] = {"chunk_main", "chunk_state", "state_scan", "decode"};
+
+hipEvent_t take_event() {
+    if (!g_event_pool.empty()) {
+        hipEvent_t e = g_event_pool.back();
+        g_event_pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+// Wraps one launch; records an event pair around it while profiling.
+template <class F>
+hipError_t timed_launch(int kernel, hipStream_t s, F&& launch) {
+    std::unique_lock<std::mutex> lk(g_prof_mu);
+    if (!g_prof_on) {
+        lk.unlock();
+        return launch();
+    }
+    ProfRec rec{kernel, take_event(), take_event()};
+    if (!rec.a || !rec.b) return hipErrorOutOfMemory;
+    hipError_t e = hipEventRecord(rec.a, s);
+    if (e != hipSuccess) return e;
+    e = launch();
+    if (e != hipSuccess) return e;
+    e = hipEventRecord(rec.b, s);
+    if (e != hipSuccess) return e;
+    g_prof.push_back(rec);
+    return hipSuccess;
+}
+
+la_status hip_fail(hipError_t e, const char* what) {
+    return fail(LA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* la_status_string(la_status s) {
+    switch (s) {
+        case LA_OK: return "ok";
+        case LA_ERR_INVALID: return "invalid argument";
+        case LA_ERR_UNSUPPORTED: return "unsupported shape or mode";
+        case LA_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char* la_last_error_message(void) { return g_errmsg; }
+
+int la_version(void) { return LA_VERSION; }
+
+int la_chunk_fwd_segments(const la_desc* d, int chunk) {
+    if (check_desc(d) != LA_OK || !supported_chunk(chunk)) return 0;
+    return make_plan(d, chunk).P;
+}
+
+size_t la_chunk_fwd_workspace_bytes(const la_desc* d, int chunk) {
+    if (check_desc(d) != LA_OK || !supported_chunk(chunk)) return 0;
+    return workspace_bytes(d, make_plan(d, chunk));
+}
+
+la_status la_chunk_fwd(const la_desc* d, const void* q, const void* k, const void* v,
+                       int gate_mode, const float* gamma_or_log_alpha, const float* S0,
+                       const float* z0, int chunk, void* out, float* S_final, float* z_final,
+                       void* workspace, size_t ws_bytes, void* stream) {
+    g_errmsg[0] = '\0';
+    la_status st = check_desc(d);
+    if (st != LA_OK) return st;
+    if (!supported_chunk(chunk))
+        return fail(LA_ERR_UNSUPPORTED, "chunk must be 16, 32 or 64 (got %d)", chunk);
+    if (!q || !k || !v || !out) return fail(LA_ERR_INVALID, "q, k, v and out must be non-NULL");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+        (S0 && !aligned16(S0)) || (z0 && !aligned16(z0)) || (S_final && !aligned16(S_final)) ||
+        (z_final && !aligned16(z_final)))
+        return fail(LA_ERR_INVALID, "device pointers must be 16-byte aligned");
+    if (!d->normalize && (z0 || z_final))
+        return fail(LA_ERR_INVALID, "z0/z_final given without normalize");
+    if (d->segments > 0 && d->segments > (d->L + chunk - 1) / chunk)
+        return fail(LA_ERR_INVALID, "segments=%d exceeds the %d chunks", d->segments,
+                    (d->L + chunk - 1) / chunk);
+
+    la::ChunkParams p;
+    std::memset(&p, 0, sizeof p);
+    st = check_gate(d, gate_mode, gamma_or_log_alpha, true, p.log2_gamma, nullptr);
+    if (st != LA_OK) return st;
+
+    const Plan pl = make_plan(d, chunk);
+    const size_t need = workspace_bytes(d, pl);
+    if (need > 0) {
+        if (!workspace) return fail(LA_ERR_INVALID, "workspace of %zu bytes is required", need);
+        if (!aligned16(workspace)) return fail(LA_ERR_INVALID, "workspace must be 16-byte aligned");
+        if (ws_bytes < need)
+            return fail(LA_ERR_INVALID, "workspace has %zu bytes, %zu required", ws_bytes, need);
+    }
+
+    const int BH = d->B * d->H;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.log_alpha = gate_mode == LA_GATE_DIAG ? gamma_or_log_alpha : nullptr;
+    p.S0 = S0;
+    p.z0 = z0;
+    p.out = out;
+    p.S_final = S_final;
+    p.z_final = z_final;
+    p.L = d->L;
+    p.H = d->H;
+    p.BH = BH;
+    p.P = pl.P;
+    p.cps = pl.cps;
+    p.nchunks = pl.nchunks;
+    p.phi_elu1 = d->phi == LA_PHI_ELU1;
+    p.normalize = d->normalize;
+    if (pl.P > 1) {
+        float* ws = static_cast<float*>(workspace);
+        const size_t slots = (size_t)BH * pl.P;
+        p.ws_S = ws;
+        p.ws_a = ws + slots * d->dk * d->dv;
+        p.ws_z = p.ws_a + slots * d->dk;
+    }
+
+    const bool bf16 = d->dtype == LA_BF16;
+    auto chunk_launch = [&](bool sonly, int nblocks) -> hipError_t {
+        hipStream_t s = static_cast<hipStream_t>(stream);
+        switch (d->dk) {
+            case 16: return la::launch_chunk_f32_d16(p, chunk, gate_mode, sonly, s, nblocks);
+            case 32: return bf16 ? la::launch_chunk_bf16_d32(p, chunk, gate_mode, sonly, s, nblocks)
+                                 : la::launch_chunk_f32_d32(p, chunk, gate_mode, sonly, s, nblocks);
+            case 64: return bf16 ? la::launch_chunk_bf16_d64(p, chunk, gate_mode, sonly, s, nblocks)
+                                 : la::launch_chunk_f32_d64(p, chunk, gate_mode, sonly, s, nblocks);
+            default: return bf16 ? la::launch_chunk_bf16_d128(p, chunk, gate_mode, sonly, s, nblocks)
+                                 : la::launch_chunk_f32_d128(p, chunk, gate_mode, sonly, s, nblocks);
+        }
+    };
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (pl.P > 1) {
+        // state pass over every segment but the last, then the segment scan
+        e = timed_launch(la::K_CHUNK_STATE, s, [&] { return chunk_launch(true, BH * (pl.P - 1)); });
+        if (e != hipSuccess) return hip_fail(e, "state pass launch");
+        e = timed_launch(la::K_STATE_SCAN, s, [&] { return la::launch_state_scan(p, d->dk, s); });
+        if (e != hipSuccess) return hip_fail(e, "segment scan launch");
+    }
+    e = timed_launch(la::K_CHUNK_MAIN, s, [&] { return chunk_launch(false, BH * pl.P); });
+    if (e != hipSuccess) return hip_fail(e, "main pass launch");
+    return LA_OK;
+}
+
+la_status la_decode_step(const la_desc* d, const void* q, const void* k, const void* v,
+                         int gate_mode, const float* gate, float* S, float* z, void* out,
+                         void* stream) {
+    g_errmsg[0] = '\0';
+    la_status st = check_desc(d);
+    if (st != LA_OK) return st;
+    if (d->L != 1) return fail(LA_ERR_INVALID, "decode needs L == 1 (L=%d)", d->L);
+    if (!q || !k || !v || !out || !S) return fail(LA_ERR_INVALID, "q, k, v, S and out must be non-NULL");
+    if (d->normalize && !z) return fail(LA_ERR_INVALID, "normalize needs z");
+    if (!d->normalize && z) return fail(LA_ERR_INVALID, "z given without normalize");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(S) ||
+        (z && !aligned16(z)))
+        return fail(LA_ERR_INVALID, "device pointers must be 16-byte aligned");
+    la::DecodeParams p;
+    std::memset(&p, 0, sizeof p);
+    st = check_gate(d, gate_mode, gate, true, nullptr, p.gamma);
+    if (st != LA_OK) return st;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.log_alpha = gate_mode == LA_GATE_DIAG ? gate : nullptr;
+    p.S = S;
+    p.z = z;
+    p.out = out;
+    p.H = d->H;
+    p.BH = d->B * d->H;
+    p.phi_elu1 = d->phi == LA_PHI_ELU1;
+    p.normalize = d->normalize;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const hipError_t e = timed_launch(la::K_DECODE, s, [&] {
+        return la::launch_decode(p, d->dk, d->dtype == LA_BF16, gate_mode, s);
+    });
+    if (e != hipSuccess) return hip_fail(e, "decode launch");
+    return LA_OK;
+}
+
+la_status la_profile_begin(void) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    for (auto& r : g_prof) {
+        g_event_pool.push_back(r.a);
+        g_event_pool.push_back(r.b);
+    }
+    g_prof.clear();
+    g_prof_on = true;
+    return LA_OK;
+}
+
+la_status la_profile_end(void) {
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_prof_on = false;
+    return LA_OK;
+}
+
+la_status la_profile_query(const char* kernel, int* launches, double* total_ms) {
+    if (!kernel || !launches || !total_ms) return fail(LA_ERR_INVALID, "NULL argument");
+    int id = -1;
+    for (int i = 0; i < la::K_COUNT; ++i)
+        if (std::strcmp(kernel, kKernelNames[i]) == 0) id = i;
+    if (id < 0) return fail(LA_ERR_INVALID, "unknown kernel family '%s'", kernel);
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    int n = 0;
+    double ms = 0.0;
+    for (auto& r : g_prof) {
+        if (r.kernel != id) continue;
+        hipError_t e = hipEventSynchronize(r.b);
+        if (e != hipSuccess) return hip_fail(e, "event synchronize");
+        float x = 0.f;
+        e = hipEventElapsedTime(&x, r.a, r.b);
+        if (e != hipSuccess) return hip_fail(e, "event elapsed time");
+        ms += x;
+        ++n;
+    }
+    *launches = n;
+    *total_ms = ms;
+    return LA_OK;
+}
+
+}  // extern "C"

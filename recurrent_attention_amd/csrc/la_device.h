@@ -1,0 +1,138 @@
+// la_device.h -- device-side helpers for the gfx950 kernels: bf16 packing,
+// matrix-core (MFMA) wrappers and fragment loaders.
+//
+// Matrix-core conventions used throughout (16x16 output tiles, wave64):
+//   lane = 16*g + r  with  r = lane & 15, g = lane >> 4 (0..3)
+//   A operand (16 x K):  lane holds row m = r, k-slots j of k-group g
+//   B operand (K x 16):  lane holds column n = r, k-slots j of k-group g
+//   C/D (16 x 16 fp32):  lane holds D[4g + i][r], i = 0..3
+// bf16 (v_mfma_f32_16x16x32_bf16): K = 32, 8 k-slots per lane, and the
+// k index of (g, j) is 8g + j for A and B alike.  fp32
+// (v_mfma_f32_16x16x4_f32): K = 4, one k-slot per lane, k = g.  Only the
+// pairing "same (g, j) in A and B" matters for a contraction, so operands
+// may permute k as long as both sides use the same permutation.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace la {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(2))) float f32x2_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+
+// ---------------------------------------------------------------- bf16 bits
+__device__ __forceinline__ float bf16lo(uint32_t p) { return __uint_as_float(p << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t p) { return __uint_as_float(p & 0xffff0000u); }
+__device__ __forceinline__ float bf16f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Two floats -> two bf16 (round to nearest even) packed low/high.
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+    f32x2_t v = {lo, hi};
+    bf16x2_t h = __builtin_convertvector(v, bf16x2_t);
+    return __builtin_bit_cast(uint32_t, h);
+}
+__device__ __forceinline__ uint16_t to_bf16(float x) {
+    return (uint16_t)(pack_bf16(x, 0.0f) & 0xffffu);
+}
+
+// ---------------------------------------------------------------- element traits
+// E is the element type of LDS tiles and matrix-core operands: uint16_t
+// (bf16 bits) for bf16 inputs, float for fp32 inputs.
+template <bool BF16> struct Elem;
+template <> struct Elem<true> {
+    using E = uint16_t;
+    using Pair = uint32_t;            // two adjacent bf16 of a row
+    using Frag = bf16x8_t;            // one matrix-core operand per lane
+    static constexpr int KPL = 8;     // k-slots per lane
+    static constexpr int MK = 32;     // K of one instruction
+    __device__ static float lo(Pair p) { return bf16lo(p); }
+    __device__ static float hi(Pair p) { return bf16hi(p); }
+    __device__ static Pair pack(float a, float b) { return pack_bf16(a, b); }
+    __device__ static float tof(E e) { return bf16f(e); }
+    __device__ static E fromf(float x) { return to_bf16(x); }
+    __device__ static Pair zero() { return 0u; }
+    __device__ static f32x4_t mma(Frag a, Frag b, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+    // KPL contiguous elements starting at p (16-byte aligned)
+    __device__ static Frag load(const E* p) {
+        return __builtin_bit_cast(Frag, *reinterpret_cast<const uint4*>(p));
+    }
+    // two runs of 4 contiguous elements (8-byte aligned each)
+    __device__ static Frag load2x4(const E* p0, const E* p1) {
+        uint2 a = *reinterpret_cast<const uint2*>(p0);
+        uint2 b = *reinterpret_cast<const uint2*>(p1);
+        uint4 u = {a.x, a.y, b.x, b.y};
+        return __builtin_bit_cast(Frag, u);
+    }
+    // 8 fp32 -> fragment (RNE)
+    __device__ static Frag from8(const float* x) {
+        uint4 u = {pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3]),
+                   pack_bf16(x[4], x[5]), pack_bf16(x[6], x[7])};
+        return __builtin_bit_cast(Frag, u);
+    }
+};
+template <> struct Elem<false> {
+    using E = float;
+    using Pair = float2;
+    using Frag = float;
+    static constexpr int KPL = 1;
+    static constexpr int MK = 4;
+    __device__ static float lo(Pair p) { return p.x; }
+    __device__ static float hi(Pair p) { return p.y; }
+    __device__ static Pair pack(float a, float b) { return make_float2(a, b); }
+    __device__ static float tof(E e) { return e; }
+    __device__ static E fromf(float x) { return x; }
+    __device__ static Pair zero() { return make_float2(0.f, 0.f); }
+    __device__ static f32x4_t mma(Frag a, Frag b, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+    }
+    __device__ static Frag load(const E* p) { return *p; }
+};
+
+// Store N consecutive elements held as N/2 pairs (row segment of an LDS
+// tile) with the widest aligned vector stores available.
+template <bool BF16, int N>
+__device__ __forceinline__ void store_run(typename Elem<BF16>::E* dst, const float* x) {
+    if constexpr (BF16) {
+        static_assert(N % 2 == 0, "bf16 runs are stored as pairs");
+        uint32_t w[N / 2];
+#pragma unroll
+        for (int j = 0; j < N / 2; ++j) w[j] = pack_bf16(x[2 * j], x[2 * j + 1]);
+        if constexpr (N % 8 == 0) {
+#pragma unroll
+            for (int j = 0; j < N / 8; ++j)
+                reinterpret_cast<uint4*>(dst)[j] = make_uint4(w[4 * j], w[4 * j + 1], w[4 * j + 2], w[4 * j + 3]);
+        } else if constexpr (N % 4 == 0) {
+#pragma unroll
+            for (int j = 0; j < N / 4; ++j)
+                reinterpret_cast<uint2*>(dst)[j] = make_uint2(w[2 * j], w[2 * j + 1]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < N / 2; ++j) reinterpret_cast<uint32_t*>(dst)[j] = w[j];
+        }
+    } else {
+        if constexpr (N % 4 == 0) {
+#pragma unroll
+            for (int j = 0; j < N / 4; ++j)
+                reinterpret_cast<float4*>(dst)[j] = make_float4(x[4 * j], x[4 * j + 1], x[4 * j + 2], x[4 * j + 3]);
+        } else if constexpr (N % 2 == 0) {
+#pragma unroll
+            for (int j = 0; j < N / 2; ++j)
+                reinterpret_cast<float2*>(dst)[j] = make_float2(x[2 * j], x[2 * j + 1]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < N; ++j) dst[j] = x[j];
+        }
+    }
+}
+
+// phi = elu + 1 (x + 1 for x > 0, exp(x) otherwise) or identity.
+__device__ __forceinline__ float feature(float x, int elu1) {
+    return elu1 ? (x > 0.0f ? x + 1.0f : __expf(x)) : x;
+}
+
+}  // namespace la

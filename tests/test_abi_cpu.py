@@ -1,0 +1,178 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments on the host before anything is
+enqueued (fake, never-dereferenced pointers are enough for that)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from recurrent_attention_amd import api
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "la.h")
+
+A = 0x10000          # a 16-byte aligned fake device address
+MIS = 0x10004        # a misaligned one
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(la_[a-z_]+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert sorted(api.EXPORTED) == _declared()
+
+
+def test_library_exports_every_declared_symbol():
+    lib = api.load_library()
+    for name in _declared():
+        assert hasattr(lib, name), name
+    assert api.la_version() == 1
+
+
+def test_status_strings():
+    assert api.la_status_string(0) == "ok"
+    assert "invalid" in api.la_status_string(1)
+    assert "unsupported" in api.la_status_string(2)
+    assert "HIP" in api.la_status_string(3)
+
+
+def _desc(**kw):
+    base = dict(B=1, H=2, L=100, dk=64, dv=64, dtype=api.LA_BF16, phi=0,
+                normalize=False, segments=0)
+    base.update(kw)
+    return api.make_desc(**base)
+
+
+def _chunk(desc, gate_mode=0, gate=None, S0=None, z0=None, chunk=64, out=A,
+           S_final=None, z_final=None, ws=None, ws_bytes=0, q=A, k=A, v=A):
+    return api.la_chunk_fwd(desc, q, k, v, gate_mode, gate, S0, z0, chunk, out,
+                            S_final, z_final, ws, ws_bytes, None)
+
+
+def _gamma(vals):
+    arr = (ctypes.c_float * len(vals))(*vals)
+    return ctypes.cast(arr, ctypes.c_void_p), arr
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("B", 0, api.LA_ERR_INVALID), ("H", -1, api.LA_ERR_INVALID),
+    ("L", 0, api.LA_ERR_INVALID), ("dk", 0, api.LA_ERR_INVALID),
+    ("dtype", 7, api.LA_ERR_INVALID), ("phi", 3, api.LA_ERR_INVALID),
+    ("normalize", 2, api.LA_ERR_INVALID), ("segments", -1, api.LA_ERR_INVALID),
+    ("dk", 48, api.LA_ERR_UNSUPPORTED), ("dv", 32, api.LA_ERR_UNSUPPORTED),
+])
+def test_chunk_rejects_bad_descriptor(field, value, status):
+    d = _desc(**{field: value})
+    assert _chunk(d) == status
+    assert api.la_last_error_message() != ""
+
+
+def test_chunk_rejects_null_descriptor():
+    lib = api.load_library()
+    st = lib.la_chunk_fwd(None, A, A, A, 0, None, None, None, 64, A, None, None,
+                          None, 0, None)
+    assert st == api.LA_ERR_INVALID
+
+
+def test_bf16_needs_dk_32():
+    assert _chunk(_desc(dk=16, dv=16)) == api.LA_ERR_UNSUPPORTED
+    assert "dk >= 32" in api.la_last_error_message()
+
+
+@pytest.mark.parametrize("chunk", [0, 8, 48, 128])
+def test_chunk_rejects_unsupported_chunk(chunk):
+    assert _chunk(_desc(), chunk=chunk) == api.LA_ERR_UNSUPPORTED
+
+
+def test_chunk_rejects_null_and_misaligned_pointers():
+    d = _desc(L=64)
+    assert _chunk(d, q=None) == api.LA_ERR_INVALID
+    assert _chunk(d, out=None) == api.LA_ERR_INVALID
+    assert _chunk(d, k=MIS) == api.LA_ERR_INVALID
+    assert "aligned" in api.la_last_error_message()
+    assert _chunk(d, S0=MIS) == api.LA_ERR_INVALID
+
+
+def test_chunk_gate_validation():
+    d = _desc(L=64, H=2)
+    assert _chunk(d, gate_mode=api.LA_GATE_GAMMA, gate=None) == api.LA_ERR_INVALID
+    p, keep = _gamma([0.5, 1.5])
+    assert _chunk(d, gate_mode=api.LA_GATE_GAMMA, gate=p) == api.LA_ERR_INVALID
+    assert "outside [0, 1]" in api.la_last_error_message()
+    p, keep = _gamma([0.5, float("nan")])
+    assert _chunk(d, gate_mode=api.LA_GATE_GAMMA, gate=p) == api.LA_ERR_INVALID
+    p, keep = _gamma([-0.1, 0.5])
+    assert _chunk(d, gate_mode=api.LA_GATE_GAMMA, gate=p) == api.LA_ERR_INVALID
+    assert _chunk(d, gate_mode=api.LA_GATE_DIAG, gate=None) == api.LA_ERR_INVALID
+    assert _chunk(d, gate_mode=api.LA_GATE_DIAG, gate=MIS) == api.LA_ERR_INVALID
+    assert _chunk(d, gate_mode=5, gate=A) == api.LA_ERR_INVALID
+    big = _desc(L=64, H=257)
+    p, keep = _gamma([0.5] * 257)
+    assert _chunk(big, gate_mode=api.LA_GATE_GAMMA, gate=p) == api.LA_ERR_UNSUPPORTED
+
+
+def test_chunk_normaliser_contract():
+    d = _desc(L=64, normalize=False)
+    assert _chunk(d, z0=A) == api.LA_ERR_INVALID
+    assert _chunk(d, z_final=A) == api.LA_ERR_INVALID
+
+
+def test_chunk_workspace_contract():
+    d = _desc(B=1, H=1, L=4096, segments=4)
+    need = api.la_chunk_fwd_workspace_bytes(d, 64)
+    assert need == 1 * 1 * 4 * (64 * 64 + 2 * 64) * 4
+    assert _chunk(d, ws=None) == api.LA_ERR_INVALID
+    assert _chunk(d, ws=A, ws_bytes=need - 4) == api.LA_ERR_INVALID
+    assert _chunk(d, ws=MIS, ws_bytes=need) == api.LA_ERR_INVALID
+    too_many = _desc(L=100, segments=3)   # 2 chunks of 64
+    assert _chunk(too_many) == api.LA_ERR_INVALID
+
+
+@pytest.mark.parametrize("B,H,L,chunk,segments,P", [
+    (1, 16, 32768, 64, 0, 16),    # 16 pairs -> 16 segments of 32 chunks
+    (2, 16, 8192, 64, 0, 8),
+    (4, 8, 2048, 64, 0, 8),
+    (1, 1, 64, 16, 0, 4),         # never more segments than chunks
+    (1, 1, 100, 64, 5, 2),
+    (256, 1, 100, 16, 0, 1),
+    (1, 1, 1000, 64, 3, 3),       # 16 chunks: 6 + 6 + 4
+    (1, 1, 1000, 64, 5, 4),       # 16 chunks: cps 4 -> 4 segments
+])
+def test_segment_plan(B, H, L, chunk, segments, P):
+    d = _desc(B=B, H=H, L=L, segments=segments)
+    assert api.la_chunk_fwd_segments(d, chunk) == P
+    ws = api.la_chunk_fwd_workspace_bytes(d, chunk)
+    assert ws == (0 if P == 1 else B * H * P * (64 * 64 + 128) * 4)
+
+
+def test_decode_validation():
+    d = _desc(L=2)
+    st = api.la_decode_step(d, A, A, A, 0, None, A, None, A, None)
+    assert st == api.LA_ERR_INVALID and "L == 1" in api.la_last_error_message()
+    d = _desc(L=1, normalize=True)
+    assert api.la_decode_step(d, A, A, A, 0, None, A, None, A, None) == api.LA_ERR_INVALID
+    d = _desc(L=1, normalize=False)
+    assert api.la_decode_step(d, A, A, A, 0, None, A, A, A, None) == api.LA_ERR_INVALID
+    assert api.la_decode_step(d, A, A, A, 0, None, None, None, A, None) == api.LA_ERR_INVALID
+    assert api.la_decode_step(d, A, A, A, 0, None, MIS, None, A, None) == api.LA_ERR_INVALID
+    p, keep = _gamma([2.0, 0.5])
+    assert api.la_decode_step(d, A, A, A, api.LA_GATE_GAMMA, p, A, None, A,
+                              None) == api.LA_ERR_INVALID
+
+
+def test_profile_interface_without_launches():
+    api.la_profile_begin()
+    assert api.la_profile_query("chunk_main") == (0, 0.0)
+    api.la_profile_end()
+    with pytest.raises(api.LaError):
+        api.la_profile_query("no_such_kernel")
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        api.chunk_fwd(q, q, q)
