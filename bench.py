@@ -1,0 +1,304 @@
+#!/usr/bin/env python3
+"""Benchmark of the hot path on one MI355X; prints ONE JSON line.
+
+Step = one chunkwise prefill of the gated-linear-attention workload
+``gla_B1H16_L32768_d128`` (B=1, H=16, L=32768, d_k=d_v=128, bf16 q/k/v,
+fp32 diagonal log-gates, chunk 64): state pass, segment scan and main pass,
+inputs resident in HBM.  ``value`` is sequence tokens per second.
+
+Also reported, in the same line:
+* ``roofline``: the dominant kernel (the main chunk pass), its algorithmic
+  bytes per launch over its average duration measured with HIP events that
+  the library records on the launch stream, against 8 TB/s; ``traffic`` is
+  the measured HBM bytes per launch from rocprofv3 counters (see
+  profiles/), null when the kernel sources changed since.
+* ``decode``: 1000 consecutive recurrent steps of
+  ``decode_retention_256x32_d128`` (256 sequences x 32 heads, fp32 state,
+  gamma = 0.97): algorithmic GB/s and its roofline.
+* ``cpu_baseline``: the fp64 oracle (test infrastructure, untuned) on the
+  same prefill workload drawn on the host, timed on this machine's cores.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("chunkwise fwd tokens/s + % bf16 MFMA peak (H16 d128 L32k); "
+          "decode HBM GB/s")
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_hash():
+    """Hash of the sources the main chunk kernel is built from."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "recurrent_attention_amd", "csrc")
+    for f in ("chunk_kernel.h", "la_device.h", "la_internal.h", "chunk_bf16_d128.hip"):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def decode_source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "recurrent_attention_amd", "csrc")
+    for f in ("decode_kernel.hip", "la_device.h", "la_internal.h"):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(name, src_hash):
+    """HBM bytes per launch from a committed counter summary, or None when
+    there is none or it was taken from other kernel sources."""
+    path = os.path.join(PROFILES, f"traffic_{name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha256") != src_hash:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def prefill_bytes(w):
+    """Algorithmic bytes of one prefill: q, k, v, out in bf16 (+ fp32 log
+    gates) per token-head, plus the fp32 final state per (b,h)."""
+    per_th = 2 * (2 * w.dk + w.dv) + 2 * w.dv + (4 * w.dk if w.gate_mode == 2 else 0)
+    return w.B * w.H * w.L * per_th + w.B * w.H * w.dk * w.dv * 4
+
+
+def prefill_flops(w):
+    """Dense chunk-form flops: 2C(dk+dv) + 4 dk dv per token-head."""
+    return w.B * w.H * w.L * (2 * w.chunk * (w.dk + w.dv) + 4 * w.dk * w.dv)
+
+
+def bench_prefill(args, torch, api, workloads):
+    w = workloads.WORKLOADS[workloads.PREFILL_HEADLINE]
+    dev = torch.device("cuda", 0)
+    inp = workloads.workload_inputs(w.name, seed=0, device=dev)
+    q, k, v, la = inp["q"], inp["k"], inp["v"], inp["log_alpha"]
+    desc = api.make_desc(w.B, w.H, w.L, w.dk, w.dv, api.LA_BF16, w.phi, w.normalize, 0)
+    P = api.la_chunk_fwd_segments(desc, w.chunk)
+    need = api.la_chunk_fwd_workspace_bytes(desc, w.chunk)
+    out = torch.empty_like(v)
+    S_final = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(need // 4, 1), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    lib = api.load_library()
+    dref = ctypes.byref(desc)
+    argv = (dref, q.data_ptr(), k.data_ptr(), v.data_ptr(), w.gate_mode, la.data_ptr(),
+            None, None, w.chunk, out.data_ptr(), S_final.data_ptr(), None,
+            ws.data_ptr(), need, sp)
+
+    def step():
+        st = lib.la_chunk_fwd(*argv)
+        if st != 0:
+            raise RuntimeError(api.la_last_error_message())
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    # second pass over the same steps with per-kernel HIP events on the stream
+    api.la_profile_begin()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    api.la_profile_end()
+    kern = {}
+    for name in ("chunk_main", "chunk_state", "state_scan"):
+        n, ms = api.la_profile_query(name)
+        kern[name] = {"launches": n, "avg_us": (ms / n * 1e3) if n else None}
+
+    ms_step = elapsed / args.steps * 1e3
+    tokens = w.B * w.L
+    bytes_alg = prefill_bytes(w)
+    flops = prefill_flops(w)
+    main_us = kern["chunk_main"]["avg_us"]
+    achieved = bytes_alg / (main_us * 1e-6) / 1e9
+    traffic = measured_traffic(f"chunk_main_{w.name}", kernel_source_hash())
+    return {
+        "w": w, "P": P, "ms_step": ms_step, "tokens_per_s": tokens / (ms_step * 1e-3),
+        "kernels": kern, "bytes": bytes_alg, "flops": flops,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": "chunk_main",
+                     "bytes_per_launch": bytes_alg, "avg_launch_us": round(main_us, 2)},
+        "mfma_pct": 100.0 * flops / (ms_step * 1e-3) / (BF16_PEAK_TFLOPS * 1e12),
+        "hbm_pct_step": 100.0 * bytes_alg / (ms_step * 1e-3) / (HBM_PEAK_GBS * 1e9),
+    }
+
+
+def bench_decode(args, torch, api, workloads):
+    w = workloads.WORKLOADS[workloads.DECODE_HEADLINE]
+    dev = torch.device("cuda", 0)
+    steps = args.decode_steps
+    S0, _ = workloads.decode_state(w.B, w.H, w.dk, w.dv, seed=0, device=dev)
+    q, k, v, _ = workloads.decode_tokens(w.B, w.H, w.dk, w.dv, steps, seed=1, device=dev)
+    S = S0.clone()
+    out = torch.empty((w.B, w.H, w.dv), dtype=torch.bfloat16, device=dev)
+    gamma = torch.tensor(w.gamma, dtype=torch.float32)
+    g_ptr = ctypes.c_void_p(gamma.data_ptr())
+    desc = api.make_desc(w.B, w.H, 1, w.dk, w.dv, api.LA_BF16, w.phi, False, 0)
+    dref = ctypes.byref(desc)
+    sp = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    lib = api.load_library()
+    qp = [q[t].data_ptr() for t in range(steps)]
+    kp = [k[t].data_ptr() for t in range(steps)]
+    vp = [v[t].data_ptr() for t in range(steps)]
+    Sp, op = S.data_ptr(), out.data_ptr()
+
+    def run(n):
+        for t in range(n):
+            st = lib.la_decode_step(dref, qp[t], kp[t], vp[t], w.gate_mode, g_ptr, Sp,
+                                    None, op, sp)
+            if st != 0:
+                raise RuntimeError(api.la_last_error_message())
+
+    run(min(steps, 20))
+    S.copy_(S0)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    run(steps)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    S.copy_(S0)
+    torch.cuda.synchronize()
+    api.la_profile_begin()
+    run(steps)
+    torch.cuda.synchronize()
+    api.la_profile_end()
+    n, ms = api.la_profile_query("decode")
+    avg_us = ms / n * 1e3
+    state_bytes = w.B * w.H * w.dk * w.dv * 4
+    step_bytes = 2 * state_bytes + w.B * w.H * (2 * w.dk + 2 * w.dv) * 2   # + tokens and out
+    us_step = elapsed / steps * 1e6
+    gbs = step_bytes / (us_step * 1e-6) / 1e9
+    achieved = step_bytes / (avg_us * 1e-6) / 1e9
+    del q, k, v
+    return {
+        "workload": w.name, "steps": steps, "us_per_step": round(us_step, 2),
+        "value": round(gbs, 1), "unit": "GB/s", "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
+        "steps_per_s": round(1e6 / us_step, 1), "tokens_per_s": round(w.B * 1e6 / us_step, 1),
+        "bytes_per_step": step_bytes,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(f"decode_{w.name}", decode_source_hash()),
+                     "kernel": "decode", "avg_launch_us": round(avg_us, 2)},
+    }
+
+
+def cpu_baseline(workloads, w):
+    """The fp64 oracle, as it stands, on the same prefill workload drawn on
+    the host (all 16 heads, all 32768 tokens)."""
+    import oracle
+    inp = workloads.workload_inputs(w.name, seed=0, device="cpu")
+    q, k, v = (inp[x].double().numpy() for x in ("q", "k", "v"))
+    la = inp["log_alpha"].double().numpy()
+    nthreads = max(1, min(w.B * w.H, os.cpu_count() or 1, 16))
+    t0 = time.perf_counter()
+    oracle.run(q, k, v, gate_mode=w.gate_mode, log_alpha=la, phi=w.phi,
+               normalize=w.normalize, nthreads=nthreads)
+    dt = time.perf_counter() - t0
+    return {"value": round(w.B * w.L / dt, 1), "unit": "tokens/s", "cores": nthreads,
+            "kind": "oracle",
+            "sample": f"whole workload {w.name} (B={w.B}, H={w.H}, L={w.L}) drawn on the host; "
+                      f"fp64 token loop, {nthreads} threads over (b,h) pairs, {dt:.2f} s"}
+
+
+def copy_calibration(torch, nbytes=1 << 30):
+    """A plain device copy of known size, for scaling rocprofv3 byte counters."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_each_way": nbytes, "launches": 3}), flush=True)
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__,
+                                 formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a 1 GiB device copy (for counter scaling)")
+    args = ap.parse_args(argv)
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, "
+              f"WORLD_SIZE={world}); multi-GPU sharding is not part of this build.",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    from recurrent_attention_amd import api, workloads
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    api.load_library()
+
+    if args.copy_calibration:
+        copy_calibration(torch)
+    pre = bench_prefill(args, torch, api, workloads)
+    dec = None if args.no_decode else bench_decode(args, torch, api, workloads)
+    w = pre["w"]
+    line = {
+        "metric": METRIC,
+        "value": round(pre["tokens_per_s"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(pre["ms_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded torch.randn on the GPU (q,k,v ~ N(0,1)/sqrt(d) in bf16, "
+                "log-gates logsigmoid(N(0,1))/16 in fp32)",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "L": w.L, "dk": w.dk, "dv": w.dv,
+                   "chunk": w.chunk, "gate": "diag", "segments": pre["P"],
+                   "parallelism": "single GPU"},
+        "pct_of_bf16_mfma_peak": round(pre["mfma_pct"], 3),
+        "tflops": round(pre["flops"] / (pre["ms_step"] * 1e-3) / 1e12, 2),
+        "pct_of_hbm_peak_step": round(pre["hbm_pct_step"], 2),
+        "kernels_avg_us": {k: (round(v["avg_us"], 2) if v["avg_us"] else None)
+                           for k, v in pre["kernels"].items()},
+        "roofline": pre["roofline"],
+    }
+    if dec is not None:
+        line["decode"] = dec
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(workloads, w)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
