@@ -1,0 +1,144 @@
+"""Summaries of rocprofv3 output for the library's kernels.
+
+``python -m recurrent_attention_amd.profiling stats <kernel_stats.csv>``
+    prints a markdown table of the library's kernels (calls, average, min,
+    max duration) from a ``rocprofv3 --kernel-trace --stats`` CSV.
+``python -m recurrent_attention_amd.profiling counters <counter_collection.csv> ...``
+    prints the per-dispatch average of each counter for each of the
+    library's kernels from ``rocprofv3 --pmc`` CSVs (one file per pass).
+``python -m recurrent_attention_amd.profiling traffic --fetch F.csv --write W.csv
+    --kernel NAME --copy-bytes N --out profiles/traffic_X.json --hash H``
+    scales FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of one kernel by what
+    the same counters read for a plain device copy of N bytes each way.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import json
+import re
+import sys
+from collections import defaultdict
+
+FAMILIES = [
+    ("chunk_main", re.compile(r"la::chunk_kernel<la::ChunkCfg<(\d+), (\d+), (\d+), (\w+), (\d), false>")),
+    ("chunk_state", re.compile(r"la::chunk_kernel<la::ChunkCfg<(\d+), (\d+), (\d+), (\w+), (\d), true>")),
+    ("state_scan", re.compile(r"la::state_scan_kernel")),
+    ("decode", re.compile(r"la::decode_kernel")),
+    ("copy", re.compile(r"copyBuffer|elementwise_kernel.*copy|vectorized_elementwise_kernel.*copy")),
+]
+
+
+def family(name: str):
+    for fam, rx in FAMILIES:
+        if rx.search(name):
+            return fam
+    return None
+
+
+def stats_table(path: str) -> str:
+    rows = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            fam = family(r["Name"])
+            if fam in (None, "copy"):
+                continue
+            rows.append((fam, r["Name"], int(r["Calls"]), float(r["AverageNs"]) / 1e3,
+                         float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3))
+    out = ["| family | kernel | calls | avg us | min us | max us |",
+           "|---|---|---:|---:|---:|---:|"]
+    for fam, name, n, avg, mn, mx in rows:
+        out.append(f"| {fam} | `{name}` | {n} | {avg:.2f} | {mn:.2f} | {mx:.2f} |")
+    return "\n".join(out)
+
+
+def counter_means(paths):
+    """{kernel name: {counter: mean per dispatch}} over the given CSVs."""
+    acc = defaultdict(lambda: defaultdict(list))
+    for path in paths:
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                name = r.get("Kernel_Name") or r.get("Kernel-Name") or ""
+                cname = r.get("Counter_Name") or r.get("Counter-Name")
+                val = r.get("Counter_Value") or r.get("Counter-Value")
+                if cname is None or val is None:
+                    continue
+                disp = r.get("Dispatch_Id") or r.get("Dispatch-Id") or ""
+                acc[name][cname].append((disp, float(val)))
+    means = {}
+    for name, cs in acc.items():
+        means[name] = {}
+        for cname, vals in cs.items():
+            per_disp = defaultdict(float)
+            for disp, v in vals:
+                per_disp[disp] += v      # counters split over agents/XCDs add up
+            means[name][cname] = sum(per_disp.values()) / max(len(per_disp), 1)
+    return means
+
+
+def traffic(fetch_csv, write_csv, kernel_family, copy_bytes, out, src_hash, note=""):
+    fm = counter_means([fetch_csv])
+    wm = counter_means([write_csv])
+
+    def pick(means, fam, counter):
+        vals = [cs[counter] for n, cs in means.items() if family(n) == fam and counter in cs]
+        return max(vals) if vals else None
+
+    f_kern = pick(fm, kernel_family, "FETCH_SIZE")
+    w_kern = pick(wm, kernel_family, "WRITE_SIZE")
+    f_copy = pick(fm, "copy", "FETCH_SIZE")
+    w_copy = pick(wm, "copy", "WRITE_SIZE")
+    if None in (f_kern, w_kern, f_copy, w_copy):
+        raise SystemExit(f"missing counters: kernel {f_kern} {w_kern}, copy {f_copy} {w_copy}")
+    f_scale = copy_bytes / f_copy      # bytes per counter unit, from the copy
+    w_scale = copy_bytes / w_copy
+    rec = {
+        "kernel_family": kernel_family,
+        "fetch_counter_per_launch": f_kern, "write_counter_per_launch": w_kern,
+        "copy_bytes_each_way": copy_bytes,
+        "copy_fetch_counter": f_copy, "copy_write_counter": w_copy,
+        "fetch_bytes_per_launch": f_kern * f_scale,
+        "write_bytes_per_launch": w_kern * w_scale,
+        "hbm_bytes_per_launch": f_kern * f_scale + w_kern * w_scale,
+        "source_sha256": src_hash,
+        "note": note,
+    }
+    with open(out, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps(rec, indent=1))
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__,
+                                 formatter_class=argparse.RawDescriptionHelpFormatter)
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("csv")
+    c = sub.add_parser("counters")
+    c.add_argument("csv", nargs="+")
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--kernel", required=True)
+    t.add_argument("--copy-bytes", type=int, required=True)
+    t.add_argument("--out", required=True)
+    t.add_argument("--hash", required=True)
+    t.add_argument("--note", default="")
+    a = ap.parse_args(argv)
+    if a.cmd == "stats":
+        print(stats_table(a.csv))
+    elif a.cmd == "counters":
+        for name, cs in counter_means(a.csv).items():
+            fam = family(name)
+            if fam is None:
+                continue
+            print(f"{fam}: {name}")
+            for k, v in sorted(cs.items()):
+                print(f"    {k} = {v:.6g}")
+    else:
+        traffic(a.fetch, a.write, a.kernel, a.copy_bytes, a.out, a.hash, a.note)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
