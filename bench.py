@@ -245,8 +245,9 @@ def main(argv=None):
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run a 1 GiB device copy (for counter scaling)")
+    ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
+                    help="run one part only (copy: a 1 GiB device copy used to scale "
+                         "rocprofv3 byte counters); prints no metric line")
     args = ap.parse_args(argv)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -263,8 +264,17 @@ def main(argv=None):
         return 1
     api.load_library()
 
-    if args.copy_calibration:
+    if args.only == "copy":
         copy_calibration(torch)
+        return 0
+    if args.only == "decode":
+        print(json.dumps(bench_decode(args, torch, api, workloads)), flush=True)
+        return 0
+    if args.only == "prefill":
+        pre = bench_prefill(args, torch, api, workloads)
+        print(json.dumps({"ms_per_step": pre["ms_step"], "kernels": pre["kernels"],
+                          "roofline": pre["roofline"]}), flush=True)
+        return 0
     pre = bench_prefill(args, torch, api, workloads)
     dec = None if args.no_decode else bench_decode(args, torch, api, workloads)
     w = pre["w"]

@@ -7,9 +7,11 @@
     prints the per-dispatch average of each counter for each of the
     library's kernels from ``rocprofv3 --pmc`` CSVs (one file per pass).
 ``python -m recurrent_attention_amd.profiling traffic --fetch F.csv --write W.csv
-    --kernel NAME --copy-bytes N --out profiles/traffic_X.json --hash H``
-    scales FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of one kernel by what
-    the same counters read for a plain device copy of N bytes each way.
+    --fetch-copy FC.csv --write-copy WC.csv --kernel NAME --copy-bytes N
+    --out profiles/traffic_X.json --hash H``
+    scales FETCH_SIZE / WRITE_SIZE (per dispatch) of one kernel family by
+    what the same counters read for a plain device copy of N bytes each way
+    (``bench.py --only copy``, a 1 GiB copy), giving HBM bytes per launch.
 """
 from __future__ import annotations
 
@@ -25,7 +27,7 @@ FAMILIES = [
     ("chunk_state", re.compile(r"la::chunk_kernel<la::ChunkCfg<(\d+), (\d+), (\d+), (\w+), (\d), true>")),
     ("state_scan", re.compile(r"la::state_scan_kernel")),
     ("decode", re.compile(r"la::decode_kernel")),
-    ("copy", re.compile(r"copyBuffer|elementwise_kernel.*copy|vectorized_elementwise_kernel.*copy")),
+    ("copy", re.compile(r"__amd_rocclr_copyBuffer")),
 ]
 
 
@@ -76,9 +78,12 @@ def counter_means(paths):
     return means
 
 
-def traffic(fetch_csv, write_csv, kernel_family, copy_bytes, out, src_hash, note=""):
+def traffic(fetch_csv, write_csv, fetch_copy_csv, write_copy_csv, kernel_family, copy_bytes,
+            out, src_hash, note=""):
     fm = counter_means([fetch_csv])
     wm = counter_means([write_csv])
+    fcm = counter_means([fetch_copy_csv])
+    wcm = counter_means([write_copy_csv])
 
     def pick(means, fam, counter):
         vals = [cs[counter] for n, cs in means.items() if family(n) == fam and counter in cs]
@@ -86,8 +91,8 @@ def traffic(fetch_csv, write_csv, kernel_family, copy_bytes, out, src_hash, note
 
     f_kern = pick(fm, kernel_family, "FETCH_SIZE")
     w_kern = pick(wm, kernel_family, "WRITE_SIZE")
-    f_copy = pick(fm, "copy", "FETCH_SIZE")
-    w_copy = pick(wm, "copy", "WRITE_SIZE")
+    f_copy = pick(fcm, "copy", "FETCH_SIZE")
+    w_copy = pick(wcm, "copy", "WRITE_SIZE")
     if None in (f_kern, w_kern, f_copy, w_copy):
         raise SystemExit(f"missing counters: kernel {f_kern} {w_kern}, copy {f_copy} {w_copy}")
     f_scale = copy_bytes / f_copy      # bytes per counter unit, from the copy
@@ -119,6 +124,8 @@ def main(argv=None):
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
+    t.add_argument("--fetch-copy", required=True, help="FETCH_SIZE run of bench.py --only copy")
+    t.add_argument("--write-copy", required=True, help="WRITE_SIZE run of bench.py --only copy")
     t.add_argument("--kernel", required=True)
     t.add_argument("--copy-bytes", type=int, required=True)
     t.add_argument("--out", required=True)
@@ -136,7 +143,8 @@ def main(argv=None):
             for k, v in sorted(cs.items()):
                 print(f"    {k} = {v:.6g}")
     else:
-        traffic(a.fetch, a.write, a.kernel, a.copy_bytes, a.out, a.hash, a.note)
+        traffic(a.fetch, a.write, a.fetch_copy, a.write_copy, a.kernel, a.copy_bytes, a.out,
+                a.hash, a.note)
     return 0
 
 
