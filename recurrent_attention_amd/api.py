@@ -44,7 +44,8 @@ class LaDesc(ctypes.Structure):
 
 
 def library_path() -> str:
-    return _LIB_PATH
+    """Path of the library to load: LINATTN_LIBRARY if set, else the in-tree build."""
+    return os.environ.get("LINATTN_LIBRARY") or _LIB_PATH
 
 
 def load_library():
@@ -52,11 +53,12 @@ def load_library():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB_PATH):
+    path = library_path()
+    if not os.path.exists(path):
         raise RuntimeError(
-            f"{_LIB_PATH} is missing: build it with "
+            f"{path} is missing: build it with "
             "`python -m recurrent_attention_amd.build` (there is no CPU fallback)")
-    lib = ctypes.CDLL(_LIB_PATH)
+    lib = ctypes.CDLL(path)
     vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     dp = ctypes.POINTER(LaDesc)
     fp = ctypes.POINTER(ctypes.c_float)

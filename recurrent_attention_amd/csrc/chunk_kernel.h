@@ -12,24 +12,38 @@
 //         + sum_{s<=t} [sum_i phi(q_ti) phi(k_si) e^{b_ti - b_si}] v_s
 //   S_new = diag(e^{b_{c-1}}) S_prev + sum_s (phi(k_s) * e^{b_{c-1} - b_s}) v_s^T
 //
-// Matrix-core mapping per chunk (C tokens, d_k x d_v state, fp32 accum):
-//   op1  P   = Qh Kh^T        [C x C], lower-triangular 16x16 tiles only
-//   op2  O   = Qh S' + P V    [C x d_v]
-//   op3  S'' = Kt^T V         [d_k x d_v], accumulated onto the scaled state
+// Matrix-core mapping per chunk (C tokens, d_k x d_v state, fp32 accum).
+// The score and output products are computed transposed so that every lane
+// ends up holding four consecutive s (or output columns) and writes them as
+// one packed run:
+//   op1  P^T = Kh Qh^T                [C x C], lower-triangular 16x16 tiles
+//   op2  O^T = S'^T Qh^T + V^T P^T    [d_v x C]
+//   op3  S'' = Kt^T V                 [d_k x d_v], onto the scaled state
 // Decay placement by gate mode:
 //   NONE  : no scaling.
 //   GAMMA : P masked by gamma^(t-s) elementwise (exact for gamma = 0); the
-//           Q S term scaled per row by gamma^(t+1); Kt by gamma^(c-1-s);
-//           state scaled by gamma^c.  All factors <= 1.
+//           S'^T Qh^T term scaled per token by gamma^(t+1); Kt by
+//           gamma^(c-1-s); the state by gamma^c.  All factors <= 1.
 //   DIAG  : factorised around a reference r = b at the chunk middle:
-//           Qh = q e^{b_t - r}, Kh = Kt = k e^{r - b_s}; the state is scaled
-//           per row by e^{r} before use and by e^{b_{c-1} - r} after the
-//           update, so S_new = e^{b_{c-1}-r} (e^{r} S + Kh^T V).
+//           Qh = q e^{b_t - r}, Kh = Kt = k e^{r - b_s}; the state rows are
+//           scaled by e^{r} before use and by e^{b_{c-1} - r} after the
+//           update, so S_new = e^{b_{c-1}-r} (e^{r} S + Kh^T V).  The
+//           after-factor of one chunk and the before-factor of the next are
+//           applied as one product.
 // The state S stays in fp32 matrix-core accumulators for the whole segment;
-// wave w owns state columns [w*WN, (w+1)*WN).  For the Q S product the
-// accumulators are converted in registers into B operands: lane (n, g) holds
-// state rows 16m + 4g + i of column n, so the A operand (Qh) is read with the
-// same permutation of the d_k index.
+// wave w owns state columns [w*WN, (w+1)*WN).  For the S'^T Qh^T product the
+// accumulators are converted in registers into A operands: lane (n, g) holds
+// state rows 16m + 4g + i of column n, so Qh is stored with its d_k index
+// permuted within every 32 channels such that one 16-byte read returns the
+// matching rows (Kh uses the same layout, which leaves Kh Qh^T unchanged).
+//
+// LDS tiles are unpadded and XOR-swizzled in 16-byte units so that both the
+// fragment reads (16 consecutive rows, one unit) and the transposed tile
+// writes (rows two apart) spread over the banks.
+//
+// Global memory is read through buffer descriptors covering one (b,h) slice:
+// tokens past L read as zeros and output rows past L are dropped by the
+// hardware range check, so the ragged tail needs no branches.
 //
 // One workgroup runs one (b,h) segment of consecutive chunks.  SONLY = true
 // is the state pass: the same loop without q, P and outputs, started from a
@@ -42,30 +56,34 @@
 
 namespace la {
 
-template <int DK_, int DV_, int C_, bool BF16_, int GATE_, bool SONLY_>
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2_t;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;
+
+template <int DK_, int DV_, int C_, bool BF16_, int GATE_, bool SONLY_, int NW_>
 struct ChunkCfg {
-    static constexpr int DK = DK_, DV = DV_, C = C_, GATE = GATE_;
+    static constexpr int DK = DK_, DV = DV_, C = C_, GATE = GATE_, NW = NW_;
     static constexpr bool BF16 = BF16_, SONLY = SONLY_;
     using T = Elem<BF16>;
     using E = typename T::E;
     using Pair = typename T::Pair;
     using Frag = typename T::Frag;
-    static constexpr int NW = (DV / 16) < 4 ? (DV / 16) : 4;  // waves
-    static constexpr int NT = 64 * NW;                         // threads
-    static constexpr int WN = DV / NW;                         // state columns per wave
-    static constexpr int NB = WN / 16;                         // 16-column blocks per wave
-    static constexpr int MB = DK / 16;                         // 16-row blocks of the state
-    static constexpr int TB = C / 16;                          // 16-row blocks of a chunk
+    static constexpr int NT = 64 * NW;                 // threads
+    static constexpr int WN = DV / NW;                 // state columns per wave
+    static constexpr int NB = WN / 16;                 // 16-column blocks per wave
+    static constexpr int MB = DK / 16;                 // 16-row blocks of the state
+    static constexpr int TB = C / 16;                  // 16-row blocks of a chunk
     static constexpr int KPL = T::KPL, MK = T::MK;
-    static constexpr int CP = C < MK ? MK : C;                 // token extent of s-contractions
+    static constexpr int CP = C < MK ? MK : C;         // token extent of s-contractions
+    static constexpr int UE = 16 / (int)sizeof(E);     // elements per 16-byte unit
+    static constexpr int QU = DK / UE;                 // units per q/k row
+    static constexpr int TU = CP / UE;                 // units per transposed row / P row
+    static constexpr int QMASK = (QU < 8 ? QU : 8) - 1;
+    static constexpr int TMASK = (TU < 8 ? TU : 8) - 1;
     // global -> register mapping: each thread owns two adjacent channels
     // (a column pair) over a run of consecutive tokens
     static constexpr int KCP = DK / 2, KTG = NT / KCP, KTPG = C / KTG;
     static constexpr int VCP = DV / 2, VTG = NT / VCP, VTPG = C / VTG;
-    static constexpr int PADE = 16 / (int)sizeof(E);           // 16-byte row padding
-    static constexpr int QS = DK + PADE;                       // row stride, q/k tiles
-    static constexpr int TS = CP + PADE;                       // row stride, transposed tiles and P
-    static_assert(DV % 16 == 0 && DK % 16 == 0 && C % 16 == 0, "tile shape");
+    static_assert(DV % (16 * NW) == 0 && DK % 16 == 0 && C % 16 == 0, "tile shape");
     static_assert(!BF16 || DK % 32 == 0, "bf16 needs d_k >= 32");
     static_assert(NT % KCP == 0 && NT % VCP == 0, "column-pair mapping");
     static_assert(KTG >= 2 && KTG % 2 == 0 && KTPG >= 1 && VTPG >= 1, "token groups");
@@ -76,28 +94,85 @@ template <class Cfg>
 struct ChunkSmem {
     using E = typename Cfg::E;
     static constexpr int CQ = Cfg::SONLY ? 1 : Cfg::C;
-    alignas(16) E q[CQ][Cfg::QS];     // Qh, row-major [t][i]
-    alignas(16) E k[CQ][Cfg::QS];     // Kh, row-major [s][i]
-    alignas(16) E kt[Cfg::DK][Cfg::TS];  // Kt, transposed [i][s]
-    alignas(16) E vt[Cfg::DV][Cfg::TS];  // V, transposed [n][s]
-    alignas(16) E p[CQ][Cfg::TS];     // masked scores [t][s]
+    alignas(16) E q[CQ][Cfg::DK];        // Qh, [t][permuted, swizzled i]
+    alignas(16) E k[CQ][Cfg::DK];        // Kh, [s][permuted, swizzled i]
+    alignas(16) E kt[Cfg::DK][Cfg::CP];  // Kt, [i][swizzled s]
+    alignas(16) E vt[Cfg::DV][Cfg::CP];  // V^T, [n][swizzled s]
+    alignas(16) E p[CQ][Cfg::CP];        // masked scores, [t][swizzled s]
     alignas(16) float tot[Cfg::KTG][Cfg::DK];  // per token-group log-gate sums
-    float pre[Cfg::DK], post[Cfg::DK];
-    float gpow[Cfg::C + 2];           // gamma^j
+    alignas(16) float scale[Cfg::DK];    // per-row state factor applied this chunk
+    alignas(16) float pre[Cfg::DK];      // this chunk's before/after factors
+    alignas(16) float post[Cfg::DK];
+    float gpow[Cfg::C + 2];              // gamma^j
     float z[Cfg::DK];
     float den[Cfg::C];
 };
 
+// Position of logical channel l in row `row` of a q/k tile.  bf16 tiles
+// store, within every 32 channels, the channels 4g..4g+3 next to
+// 16+4g..16+4g+3 (the order in which the state accumulators hand out their
+// rows), then swizzle 16-byte units by the row.
+template <class Cfg>
+__device__ __forceinline__ int qk_pos(int row, int l) {
+    int p = l;
+    if constexpr (Cfg::BF16) p = (l & ~31) + 8 * ((l & 15) >> 2) + 4 * ((l & 31) >> 4) + (l & 3);
+    const int u = p / Cfg::UE, e = p % Cfg::UE;
+    return ((u ^ (row & Cfg::QMASK)) * Cfg::UE) + e;
+}
+// Position of the physical k-slot run that starts at permuted position pp
+// (a multiple of the unit, or of the slot count for fp32) in row `row`.
+template <class Cfg>
+__device__ __forceinline__ int qk_phys(int row, int pp) {
+    const int u = pp / Cfg::UE, e = pp % Cfg::UE;
+    return ((u ^ (row & Cfg::QMASK)) * Cfg::UE) + e;
+}
+// Position of token s in row `row` of a transposed tile (kt, vt).
+template <class Cfg>
+__device__ __forceinline__ int tr_pos(int row, int s) {
+    const int u = s / Cfg::UE, e = s % Cfg::UE;
+    return ((u ^ ((row ^ (row >> 3)) & Cfg::TMASK)) * Cfg::UE) + e;
+}
+// Position of token s in row t of the score tile.
+template <class Cfg>
+__device__ __forceinline__ int p_pos(int t, int s) {
+    const int u = s / Cfg::UE, e = s % Cfg::UE;
+    return ((u ^ (t & Cfg::TMASK)) * Cfg::UE) + e;
+}
+
+// Store N consecutive tokens (starting at s0, a multiple of N) of one
+// transposed-tile row, one 16-byte unit at a time.
+template <class Cfg, int N>
+__device__ __forceinline__ void store_tr_run(typename Cfg::E* rowp, int row, int s0, const float* x) {
+    constexpr int PIECE = N < Cfg::UE ? N : Cfg::UE;
+#pragma unroll
+    for (int q = 0; q < N / PIECE; ++q)
+        store_run<Cfg::BF16, PIECE>(rowp + tr_pos<Cfg>(row, s0 + q * PIECE), x + q * PIECE);
+}
+
 template <class Cfg>
 __device__ __forceinline__ void scale_rows(f32x4_t (&acc)[Cfg::MB][Cfg::NB], const float* f, int g) {
 #pragma unroll
-    for (int mb = 0; mb < Cfg::MB; ++mb)
+    for (int mb = 0; mb < Cfg::MB; ++mb) {
+        const f32x4_t s = *reinterpret_cast<const f32x4_t*>(&f[16 * mb + 4 * g]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float s = f[16 * mb + 4 * g + i];
-#pragma unroll
-            for (int nb = 0; nb < Cfg::NB; ++nb) acc[mb][nb][i] *= s;
-        }
+        for (int nb = 0; nb < Cfg::NB; ++nb) acc[mb][nb] *= s;
+    }
+}
+
+// Buffer descriptor over [base, base + bytes); reads past the end return 0
+// and writes past the end are dropped.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+template <class Pair>
+__device__ __forceinline__ Pair buf_load_pair(__amdgpu_buffer_rsrc_t r, uint32_t off);
+template <>
+__device__ __forceinline__ uint32_t buf_load_pair<uint32_t>(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
+template <>
+__device__ __forceinline__ float2 buf_load_pair<float2>(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
 }
 
 template <class Cfg>
@@ -108,6 +183,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
     constexpr int KCP = Cfg::KCP, KTG = Cfg::KTG, KTPG = Cfg::KTPG;
     constexpr int VCP = Cfg::VCP, VTPG = Cfg::VTPG;
     constexpr bool SONLY = Cfg::SONLY, BF16 = Cfg::BF16;
+    constexpr int ES = (int)sizeof(typename Cfg::E);
     using T = typename Cfg::T;
     using E = typename Cfg::E;
     using Pair = typename Cfg::Pair;
@@ -133,15 +209,32 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
     const int vcp = tid % VCP, vtg = tid / VCP;
     const int colbase = wave * Cfg::WN;
 
+    // ---- buffer descriptors over this (b,h) slice
+    const size_t rows0 = (size_t)bh * L;
+    const __amdgpu_buffer_rsrc_t rq =
+        make_rsrc(reinterpret_cast<const E*>(p.q) + rows0 * DK, (uint32_t)L * DK * ES);
+    const __amdgpu_buffer_rsrc_t rk =
+        make_rsrc(reinterpret_cast<const E*>(p.k) + rows0 * DK, (uint32_t)L * DK * ES);
+    const __amdgpu_buffer_rsrc_t rv =
+        make_rsrc(reinterpret_cast<const E*>(p.v) + rows0 * DV, (uint32_t)L * DV * ES);
+    const __amdgpu_buffer_rsrc_t rla =
+        make_rsrc(GATE == LA_GATE_DIAG ? (const void*)(p.log_alpha + rows0 * DK) : p.q,
+                  GATE == LA_GATE_DIAG ? (uint32_t)L * DK * 4 : 0u);
+    const __amdgpu_buffer_rsrc_t ro =
+        make_rsrc(SONLY ? p.q : (const void*)(reinterpret_cast<const E*>(p.out) + rows0 * DV),
+                  SONLY ? 0u : (uint32_t)L * DV * ES);
+
     // ---- one-time LDS set-up: zero the tiles whose padding is read as zeros
     {
-        E* z0p = &sm.kt[0][0];
-        for (int i = tid; i < DK * Cfg::TS; i += Cfg::NT) z0p[i] = E(0);
-        E* z1p = &sm.vt[0][0];
-        for (int i = tid; i < DV * Cfg::TS; i += Cfg::NT) z1p[i] = E(0);
+        if constexpr (CP > C) {
+            E* z0p = &sm.kt[0][0];
+            for (int i = tid; i < DK * CP; i += Cfg::NT) z0p[i] = E(0);
+            E* z1p = &sm.vt[0][0];
+            for (int i = tid; i < DV * CP; i += Cfg::NT) z1p[i] = E(0);
+        }
         if constexpr (!SONLY) {
             E* z2p = &sm.p[0][0];
-            for (int i = tid; i < C * Cfg::TS; i += Cfg::NT) z2p[i] = E(0);
+            for (int i = tid; i < C * CP; i += Cfg::NT) z2p[i] = E(0);
         }
         if constexpr (GATE == LA_GATE_GAMMA) {
             const float l2g = p.log2_gamma[h];
@@ -175,32 +268,24 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
     // segment decay product (state pass)
     float seg_la = 0.0f, seg_lb = 0.0f;  // DIAG: summed log-gates of this thread's channels
     float seg_g = 1.0f;                  // GAMMA: product of gamma^c
+    float post_a = 1.0f, post_b = 1.0f;  // DIAG: after-factor of the previous chunk
 
-    // ---- register prefetch of one chunk
-    const Pair* qp = reinterpret_cast<const Pair*>(p.q);
-    const Pair* kp = reinterpret_cast<const Pair*>(p.k);
-    const Pair* vp = reinterpret_cast<const Pair*>(p.v);
-    const float2* lap = reinterpret_cast<const float2*>(p.log_alpha);
-    Pair rq[KTPG], rk[KTPG], rv[VTPG];
-    float2 rla[KTPG];
+    // ---- register prefetch of one chunk (byte offsets within the slice)
+    Pair rgq[KTPG], rgk[KTPG], rgv[VTPG];
+    float2 rgla[KTPG];
     auto load_chunk = [&](int c) {
-        const int t0 = c * C;
+        const uint32_t t0 = (uint32_t)c * C;
+        const uint32_t okk = ((t0 + ktg * KTPG) * DK + 2 * kcp) * ES;
+        const uint32_t ovv = ((t0 + vtg * VTPG) * DV + 2 * vcp) * ES;
+        const uint32_t oaa = ((t0 + ktg * KTPG) * DK + 2 * kcp) * 4;
 #pragma unroll
         for (int j = 0; j < KTPG; ++j) {
-            const int t = t0 + ktg * KTPG + j;
-            const bool ok = t < L;
-            const size_t off = ((size_t)bh * L + t) * (DK / 2) + kcp;
-            if constexpr (!SONLY) rq[j] = ok ? qp[off] : T::zero();
-            rk[j] = ok ? kp[off] : T::zero();
-            if constexpr (GATE == LA_GATE_DIAG) rla[j] = ok ? lap[off] : make_float2(0.f, 0.f);
+            if constexpr (!SONLY) rgq[j] = buf_load_pair<Pair>(rq, okk + j * DK * ES);
+            rgk[j] = buf_load_pair<Pair>(rk, okk + j * DK * ES);
+            if constexpr (GATE == LA_GATE_DIAG) rgla[j] = buf_load_pair<float2>(rla, oaa + j * DK * 4);
         }
 #pragma unroll
-        for (int j = 0; j < VTPG; ++j) {
-            const int t = t0 + vtg * VTPG + j;
-            const bool ok = t < L;
-            const size_t off = ((size_t)bh * L + t) * (DV / 2) + vcp;
-            rv[j] = ok ? vp[off] : T::zero();
-        }
+        for (int j = 0; j < VTPG; ++j) rgv[j] = buf_load_pair<Pair>(rv, ovv + j * DV * ES);
     };
     if (c_begin < c_end) load_chunk(c_begin);
 
@@ -208,31 +293,16 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
         const int t0 = c * C;
         const int clen = min(C, L - t0);
 
-        // ---- a1: features; a2: chunk-local inclusive log-gate prefix
-        float qa[KTPG], qb[KTPG], ka[KTPG], kb[KTPG], ba[KTPG], bb[KTPG];
-        {
+        // ---- a2: chunk-local inclusive log-gate prefix of this thread's run
+        if constexpr (GATE == LA_GATE_DIAG) {
             float ca = 0.f, cb = 0.f;
 #pragma unroll
             for (int j = 0; j < KTPG; ++j) {
-                const bool ok = (ktg * KTPG + j) < clen;
-                ka[j] = ok ? feature(T::lo(rk[j]), elu1) : 0.f;
-                kb[j] = ok ? feature(T::hi(rk[j]), elu1) : 0.f;
-                if constexpr (!SONLY) {
-                    qa[j] = feature(T::lo(rq[j]), elu1);
-                    qb[j] = feature(T::hi(rq[j]), elu1);
-                }
-                if constexpr (GATE == LA_GATE_DIAG) {
-                    ca += rla[j].x;
-                    cb += rla[j].y;
-                    ba[j] = ca;
-                    bb[j] = cb;
-                }
+                ca += rgla[j].x;
+                cb += rgla[j].y;
             }
-            if constexpr (GATE == LA_GATE_DIAG) {
-                __syncthreads();  // the previous chunk is done with every LDS tile
-                sm.tot[ktg][2 * kcp] = ca;
-                sm.tot[ktg][2 * kcp + 1] = cb;
-            }
+            __syncthreads();  // the previous chunk is done with every LDS tile
+            *reinterpret_cast<float2*>(&sm.tot[ktg][2 * kcp]) = make_float2(ca, cb);
         }
         // NONE/GAMMA: the previous chunk is done with every LDS tile.
         // DIAG: the token-group sums are visible.
@@ -253,55 +323,89 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
         }
         if constexpr (GATE == LA_GATE_GAMMA) seg_g *= sm.gpow[clen];
 
-        // ---- write the chunk's tiles to LDS
+        // ---- a1: features and decay factors, written to the LDS tiles
         {
+            float fk[KTPG][2], fq[SONLY ? 1 : KTPG][2];
+#pragma unroll
+            for (int j = 0; j < KTPG; ++j) {
+                fk[j][0] = T::lo(rgk[j]);
+                fk[j][1] = T::hi(rgk[j]);
+                if constexpr (!SONLY) {
+                    fq[j][0] = T::lo(rgq[j]);
+                    fq[j][1] = T::hi(rgq[j]);
+                }
+            }
+            if (elu1) {  // uniform: one branch per chunk
+#pragma unroll
+                for (int j = 0; j < KTPG; ++j) {
+                    fk[j][0] = elu1f(fk[j][0]);
+                    fk[j][1] = elu1f(fk[j][1]);
+                    if constexpr (!SONLY) {
+                        fq[j][0] = elu1f(fq[j][0]);
+                        fq[j][1] = elu1f(fq[j][1]);
+                    }
+                }
+            }
             float kta[KTPG], ktb[KTPG];
+            float ba = offa, bb = offb;
 #pragma unroll
             for (int j = 0; j < KTPG; ++j) {
                 const int t = ktg * KTPG + j;
+                const bool ok = t < clen;
+                const float ka = ok ? fk[j][0] : 0.f;
+                const float kb = ok ? fk[j][1] : 0.f;
                 float fqa = 1.f, fqb = 1.f, fka = 1.f, fkb = 1.f, fta = 1.f, ftb = 1.f;
                 if constexpr (GATE == LA_GATE_DIAG) {
-                    const float bta = offa + ba[j], btb = offb + bb[j];
-                    fqa = __expf(bta - refa);
-                    fqb = __expf(btb - refb);
-                    fka = __expf(refa - bta);
-                    fkb = __expf(refb - btb);
+                    ba += rgla[j].x;
+                    bb += rgla[j].y;
+                    fqa = __expf(ba - refa);
+                    fqb = __expf(bb - refb);
+                    fka = __expf(refa - ba);
+                    fkb = __expf(refb - bb);
                     fta = fka;
                     ftb = fkb;
                 } else if constexpr (GATE == LA_GATE_GAMMA) {
-                    fta = ftb = t < clen ? sm.gpow[clen - 1 - t] : 0.f;
+                    fta = ftb = ok ? sm.gpow[clen - 1 - t] : 0.f;
                 }
                 if constexpr (!SONLY) {
-                    *reinterpret_cast<Pair*>(&sm.q[t][2 * kcp]) = T::pack(qa[j] * fqa, qb[j] * fqb);
-                    *reinterpret_cast<Pair*>(&sm.k[t][2 * kcp]) = T::pack(ka[j] * fka, kb[j] * fkb);
+                    const float qa = fq[j][0];
+                    const float qb = fq[j][1];
+                    const int pos = qk_pos<Cfg>(t, 2 * kcp);
+                    *reinterpret_cast<Pair*>(&sm.q[t][pos]) = T::pack(qa * fqa, qb * fqb);
+                    *reinterpret_cast<Pair*>(&sm.k[t][pos]) = T::pack(ka * fka, kb * fkb);
                 }
-                kta[j] = ka[j] * fta;
-                ktb[j] = kb[j] * ftb;
+                kta[j] = ka * fta;
+                ktb[j] = kb * ftb;
             }
-            store_run<BF16, KTPG>(&sm.kt[2 * kcp][ktg * KTPG], kta);
-            store_run<BF16, KTPG>(&sm.kt[2 * kcp + 1][ktg * KTPG], ktb);
+            store_tr_run<Cfg, KTPG>(&sm.kt[2 * kcp][0], 2 * kcp, ktg * KTPG, kta);
+            store_tr_run<Cfg, KTPG>(&sm.kt[2 * kcp + 1][0], 2 * kcp + 1, ktg * KTPG, ktb);
             float va[VTPG], vb[VTPG];
 #pragma unroll
             for (int j = 0; j < VTPG; ++j) {
-                va[j] = T::lo(rv[j]);
-                vb[j] = T::hi(rv[j]);
+                va[j] = T::lo(rgv[j]);
+                vb[j] = T::hi(rgv[j]);
             }
-            store_run<BF16, VTPG>(&sm.vt[2 * vcp][vtg * VTPG], va);
-            store_run<BF16, VTPG>(&sm.vt[2 * vcp + 1][vtg * VTPG], vb);
+            store_tr_run<Cfg, VTPG>(&sm.vt[2 * vcp][0], 2 * vcp, vtg * VTPG, va);
+            store_tr_run<Cfg, VTPG>(&sm.vt[2 * vcp + 1][0], 2 * vcp + 1, vtg * VTPG, vb);
             if (ktg == 0) {
-                float prea = 1.f, preb = 1.f, posta = 1.f, postb = 1.f;
+                // per-row state factors: DIAG applies post(previous) * pre(this)
+                // before the chunk; GAMMA applies gamma^c after op2
+                float sa = 1.f, sb = 1.f, prea = 1.f, preb = 1.f, pa = 1.f, pb = 1.f;
                 if constexpr (GATE == LA_GATE_DIAG) {
                     prea = __expf(refa);
                     preb = __expf(refb);
-                    posta = __expf(tota - refa);
-                    postb = __expf(totb - refb);
+                    pa = __expf(tota - refa);
+                    pb = __expf(totb - refb);
+                    sa = post_a * prea;
+                    sb = post_b * preb;
+                    post_a = pa;
+                    post_b = pb;
                 } else if constexpr (GATE == LA_GATE_GAMMA) {
-                    prea = preb = sm.gpow[clen];
+                    sa = sb = prea = preb = sm.gpow[clen];
                 }
-                sm.pre[2 * kcp] = prea;
-                sm.pre[2 * kcp + 1] = preb;
-                sm.post[2 * kcp] = posta;
-                sm.post[2 * kcp + 1] = postb;
+                *reinterpret_cast<float2*>(&sm.scale[2 * kcp]) = make_float2(sa, sb);
+                *reinterpret_cast<float2*>(&sm.pre[2 * kcp]) = make_float2(prea, preb);
+                *reinterpret_cast<float2*>(&sm.post[2 * kcp]) = make_float2(pa, pb);
             }
         }
 
@@ -309,7 +413,8 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
         if (c + 1 < c_end) load_chunk(c + 1);
         __syncthreads();
 
-        // ---- op1: masked in-chunk scores, lower-triangular tiles
+        // ---- op1: P^T = Kh Qh^T on the lower-triangular tiles; each lane
+        // gets four consecutive s of one row t and writes them packed
         if constexpr (!SONLY) {
             int idx = 0;
 #pragma unroll
@@ -318,20 +423,24 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
                 for (int sb = 0; sb <= tb; ++sb, ++idx) {
                     if (idx % NW != wave) continue;
                     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+                    const int rs = 16 * sb + r, rt = 16 * tb + r;
 #pragma unroll
                     for (int kk = 0; kk < DK / MK; ++kk) {
-                        const Frag a = T::load(&sm.q[16 * tb + r][kk * MK + KPL * g]);
-                        const Frag b = T::load(&sm.k[16 * sb + r][kk * MK + KPL * g]);
+                        const int pp = kk * MK + KPL * g;  // this lane's k-slots (permuted order)
+                        const Frag a = T::load(&sm.k[rs][qk_phys<Cfg>(rs, pp)]);
+                        const Frag b = T::load(&sm.q[rt][qk_phys<Cfg>(rt, pp)]);
                         acc = T::mma(a, b, acc);
                     }
+                    float x[4];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const int t = 16 * tb + 4 * g + i, s = 16 * sb + r;
+                        const int s = 16 * sb + 4 * g + i;
                         float val = acc[i];
-                        if (s > t) val = 0.f;
-                        else if constexpr (GATE == LA_GATE_GAMMA) val *= sm.gpow[t - s];
-                        sm.p[t][s] = T::fromf(val);
+                        if (s > rt) val = 0.f;
+                        else if constexpr (GATE == LA_GATE_GAMMA) val *= sm.gpow[rt - s];
+                        x[i] = val;
                     }
+                    store_run<BF16, 4>(&sm.p[rt][p_pos<Cfg>(rt, 16 * sb + 4 * g)], x);
                 }
             }
             __syncthreads();
@@ -340,16 +449,16 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
             if (norm) {
                 if (tid < C) {
                     const int t = tid;
-                    float rs = 0.f;
-                    for (int s = 0; s <= t; ++s) rs += T::tof(sm.p[t][s]);
+                    float rsum = 0.f;
+                    for (int s = 0; s <= t; ++s) rsum += T::tof(sm.p[t][p_pos<Cfg>(t, s)]);
                     float dq = 0.f;
                     for (int i = 0; i < DK; ++i) {
                         float zz = sm.z[i];
                         if constexpr (GATE == LA_GATE_DIAG) zz *= sm.pre[i];
-                        dq += T::tof(sm.q[t][i]) * zz;
+                        dq += T::tof(sm.q[t][qk_pos<Cfg>(t, i)]) * zz;
                     }
                     if constexpr (GATE == LA_GATE_GAMMA) dq *= sm.gpow[t + 1];
-                    sm.den[t] = dq + rs;
+                    sm.den[t] = dq + rsum;
                 }
                 __syncthreads();
             }
@@ -357,45 +466,48 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
         // z <- post * (pre * z + sum_s Kt[:, s])  (each thread its own channel)
         if (norm && tid < DK) {
             float cs = 0.f;
-            for (int s = 0; s < C; ++s) cs += T::tof(sm.kt[tid][s]);
+            for (int s = 0; s < C; ++s) cs += T::tof(sm.kt[tid][tr_pos<Cfg>(tid, s)]);
             sm.z[tid] = sm.post[tid] * (sm.pre[tid] * sm.z[tid] + cs);
         }
 
-        // ---- value fragments, shared by op2 and op3
+        // ---- value fragments: A operand of op2 and B operand of op3
         Frag vf[CP / MK][NB];
 #pragma unroll
         for (int kk = 0; kk < CP / MK; ++kk)
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb)
-                vf[kk][nb] = T::load(&sm.vt[colbase + 16 * nb + r][kk * MK + KPL * g]);
+            for (int nb = 0; nb < NB; ++nb) {
+                const int row = colbase + 16 * nb + r;
+                vf[kk][nb] = T::load(&sm.vt[row][tr_pos<Cfg>(row, kk * MK + KPL * g)]);
+            }
 
-        if constexpr (GATE == LA_GATE_DIAG) scale_rows<Cfg>(accS, sm.pre, g);
+        if constexpr (GATE == LA_GATE_DIAG) scale_rows<Cfg>(accS, sm.scale, g);
 
         if constexpr (!SONLY) {
-            // ---- op2: O = Qh S' (+ row decay) + P V
-            f32x4_t accO[TB][NB];
+            // ---- op2: O^T = S'^T Qh^T (+ per-token decay) + V^T P^T
+            f32x4_t accO[NB][TB];
 #pragma unroll
-            for (int tb = 0; tb < TB; ++tb)
+            for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb) accO[tb][nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                for (int tb = 0; tb < TB; ++tb) accO[nb][tb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             if constexpr (BF16) {
 #pragma unroll
                 for (int k2 = 0; k2 < DK / 32; ++k2) {
-                    Frag bs[NB];
+                    Frag as[NB];
 #pragma unroll
                     for (int nb = 0; nb < NB; ++nb) {
                         const float x[8] = {accS[2 * k2][nb][0], accS[2 * k2][nb][1],
                                             accS[2 * k2][nb][2], accS[2 * k2][nb][3],
                                             accS[2 * k2 + 1][nb][0], accS[2 * k2 + 1][nb][1],
                                             accS[2 * k2 + 1][nb][2], accS[2 * k2 + 1][nb][3]};
-                        bs[nb] = T::from8(x);
+                        as[nb] = T::from8(x);
                     }
 #pragma unroll
                     for (int tb = 0; tb < TB; ++tb) {
-                        const Frag a = T::load2x4(&sm.q[16 * tb + r][32 * k2 + 4 * g],
-                                                  &sm.q[16 * tb + r][32 * k2 + 16 + 4 * g]);
+                        const int t = 16 * tb + r;
+                        // one unit of the permuted layout = state rows 4g.. and 16+4g..
+                        const Frag b = T::load(&sm.q[t][qk_phys<Cfg>(t, 32 * k2 + 8 * g)]);
 #pragma unroll
-                        for (int nb = 0; nb < NB; ++nb) accO[tb][nb] = T::mma(a, bs[nb], accO[tb][nb]);
+                        for (int nb = 0; nb < NB; ++nb) accO[nb][tb] = T::mma(as[nb], b, accO[nb][tb]);
                     }
                 }
             } else {
@@ -405,58 +517,69 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
                     for (int i = 0; i < 4; ++i)
 #pragma unroll
                         for (int tb = 0; tb < TB; ++tb) {
-                            const Frag a = sm.q[16 * tb + r][16 * mb + 4 * g + i];
+                            const int t = 16 * tb + r;
+                            const Frag b = sm.q[t][qk_pos<Cfg>(t, 16 * mb + 4 * g + i)];
 #pragma unroll
                             for (int nb = 0; nb < NB; ++nb)
-                                accO[tb][nb] = T::mma(a, accS[mb][nb][i], accO[tb][nb]);
+                                accO[nb][tb] = T::mma(accS[mb][nb][i], b, accO[nb][tb]);
                         }
             }
             if constexpr (GATE == LA_GATE_GAMMA) {
 #pragma unroll
-                for (int tb = 0; tb < TB; ++tb)
+                for (int tb = 0; tb < TB; ++tb) {
+                    const float f = sm.gpow[16 * tb + r + 1];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const float f = sm.gpow[16 * tb + 4 * g + i + 1];
-#pragma unroll
-                        for (int nb = 0; nb < NB; ++nb) accO[tb][nb][i] *= f;
-                    }
+                    for (int nb = 0; nb < NB; ++nb) accO[nb][tb] *= f;
+                }
             }
 #pragma unroll
             for (int tb = 0; tb < TB; ++tb) {
+                const int t = 16 * tb + r;
 #pragma unroll
                 for (int kk = 0; kk <= (16 * tb + 15) / MK; ++kk) {
-                    const Frag a = T::load(&sm.p[16 * tb + r][kk * MK + KPL * g]);
+                    const Frag b = T::load(&sm.p[t][p_pos<Cfg>(t, kk * MK + KPL * g)]);
 #pragma unroll
-                    for (int nb = 0; nb < NB; ++nb) accO[tb][nb] = T::mma(a, vf[kk][nb], accO[tb][nb]);
+                    for (int nb = 0; nb < NB; ++nb) accO[nb][tb] = T::mma(vf[kk][nb], b, accO[nb][tb]);
                 }
             }
-            // ---- store the chunk's outputs
-            E* outp = reinterpret_cast<E*>(p.out);
+            // ---- store: lane (r, g) holds 4 consecutive columns of token row t
 #pragma unroll
-            for (int tb = 0; tb < TB; ++tb)
+            for (int tb = 0; tb < TB; ++tb) {
+                const int t = 16 * tb + r;
+                const float inv = norm ? 1.0f / sm.den[t] : 1.0f;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int t = 16 * tb + 4 * g + i;
-                    if (t < clen) {
-                        const float inv = norm ? 1.0f / sm.den[t] : 1.0f;
-                        E* row = outp + ((size_t)bh * L + t0 + t) * DV + colbase + r;
-#pragma unroll
-                        for (int nb = 0; nb < NB; ++nb) row[16 * nb] = T::fromf(accO[tb][nb][i] * inv);
+                for (int nb = 0; nb < NB; ++nb) {
+                    const uint32_t off = ((uint32_t)(t0 + t) * DV + colbase + 16 * nb + 4 * g) * ES;
+                    const f32x4_t o = accO[nb][tb] * inv;
+                    if constexpr (BF16) {
+                        const u32x2_t w = {pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3])};
+                        __builtin_amdgcn_raw_buffer_store_b64(w, ro, off, 0, 0);
+                    } else {
+                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, o), ro, off, 0, 0);
                     }
                 }
+            }
         }
 
         // ---- op3: state update
-        if constexpr (GATE == LA_GATE_GAMMA) scale_rows<Cfg>(accS, sm.pre, g);
+        if constexpr (GATE == LA_GATE_GAMMA) scale_rows<Cfg>(accS, sm.scale, g);
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
+        for (int mb = 0; mb < MB; ++mb) {
+            const int row = 16 * mb + r;
 #pragma unroll
             for (int kk = 0; kk < CP / MK; ++kk) {
-                const Frag a = T::load(&sm.kt[16 * mb + r][kk * MK + KPL * g]);
+                const Frag a = T::load(&sm.kt[row][tr_pos<Cfg>(row, kk * MK + KPL * g)]);
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) accS[mb][nb] = T::mma(a, vf[kk][nb], accS[mb][nb]);
             }
-        if constexpr (GATE == LA_GATE_DIAG) scale_rows<Cfg>(accS, sm.post, g);
+        }
+    }
+    // DIAG: the last chunk's after-factor
+    if constexpr (GATE == LA_GATE_DIAG) {
+        __syncthreads();
+        if (ktg == 0) *reinterpret_cast<float2*>(&sm.scale[2 * kcp]) = make_float2(post_a, post_b);
+        __syncthreads();
+        scale_rows<Cfg>(accS, sm.scale, g);
     }
 
     // ---- epilogue
@@ -476,8 +599,8 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
         }
     } else {
         if (seg != P - 1) return;
-        Sout = p.S_final;
-        zout = p.z_final;
+        Sout = p.S_final ? p.S_final + (size_t)bh * SS : nullptr;
+        zout = p.z_final ? p.z_final + (size_t)bh * DK : nullptr;
     }
     if (Sout) {
 #pragma unroll
@@ -528,13 +651,20 @@ __global__ __launch_bounds__(256) void state_scan_kernel(const ChunkParams p) {
     }
 }
 
+// Waves per workgroup for a state width: 32 state columns per wave at 128,
+// 16 otherwise.
+template <int D>
+struct ChunkWaves {
+    static constexpr int value = D >= 128 ? 8 : (D / 16 < 4 ? D / 16 : 4);
+};
+
 // Host-side dispatch over chunk length and gate mode for one (d, dtype).
-template <int D, bool BF>
+template <int D, bool BF, int NWV = ChunkWaves<D>::value>
 hipError_t launch_chunk_dt(const ChunkParams& p, int chunk, int gate, bool sonly, hipStream_t s,
                            int nblocks) {
 #define LA_CHUNK_LAUNCH(CC, GG, SO)                                                      \
     do {                                                                                 \
-        using Cfg = ChunkCfg<D, D, CC, BF, GG, SO>;                                      \
+        using Cfg = ChunkCfg<D, D, CC, BF, GG, SO, NWV>;                                 \
         hipLaunchKernelGGL((chunk_kernel<Cfg>), dim3(nblocks), dim3(Cfg::NT), 0, s, p);  \
         return hipGetLastError();                                                        \
     } while (0)

@@ -77,6 +77,9 @@ la_status check_desc(const la_desc* d) {
                     d->dk, d->dv);
     if (d->dtype == LA_BF16 && d->dk < 32)
         return fail(LA_ERR_UNSUPPORTED, "bf16 inputs need dk >= 32 (dk=%d)", d->dk);
+    // kernels address one (b,h) slice of a tensor with 32-bit byte offsets
+    if ((long long)d->L * (d->dk > d->dv ? d->dk : d->dv) * 4 > 0xFFFFFFFFLL)
+        return fail(LA_ERR_UNSUPPORTED, "L*d*4 must stay below 2^32 bytes (L=%d)", d->L);
     return LA_OK;
 }
 

@@ -134,5 +134,10 @@ __device__ __forceinline__ void store_run(typename Elem<BF16>::E* dst, const flo
 __device__ __forceinline__ float feature(float x, int elu1) {
     return elu1 ? (x > 0.0f ? x + 1.0f : __expf(x)) : x;
 }
+// elu + 1 without a branch (both sides evaluated, then selected).
+__device__ __forceinline__ float elu1f(float x) {
+    const float e = __expf(fminf(x, 0.0f));
+    return x > 0.0f ? x + 1.0f : e;
+}
 
 }  // namespace la
