@@ -51,6 +51,8 @@
 // normaliser part to the workspace.
 #pragma once
 
+#include <type_traits>
+
 #include "la_device.h"
 #include "la_internal.h"
 
@@ -83,6 +85,9 @@ struct ChunkCfg {
     // (a column pair) over a run of consecutive tokens
     static constexpr int KCP = DK / 2, KTG = NT / KCP, KTPG = C / KTG;
     static constexpr int VCP = DV / 2, VTG = NT / VCP, VTPG = C / VTG;
+    // chunks of k, v and gates held in registers ahead of use (fp32 pairs
+    // are twice as large, so fp32 keeps one)
+    static constexpr int PD = BF16 ? 2 : 1;
     static_assert(DV % (16 * NW) == 0 && DK % 16 == 0 && C % 16 == 0, "tile shape");
     static_assert(!BF16 || DK % 32 == 0, "bf16 needs d_k >= 32");
     static_assert(NT % KCP == 0 && NT % VCP == 0, "column-pair mapping");
@@ -103,6 +108,7 @@ struct ChunkSmem {
     alignas(16) float scale[Cfg::DK];    // per-row state factor applied this chunk
     alignas(16) float pre[Cfg::DK];      // this chunk's before/after factors
     alignas(16) float post[Cfg::DK];
+    alignas(16) float segsum[Cfg::DK];   // DIAG: summed log2-gates of this segment
     float gpow[Cfg::C + 2];              // gamma^j
     float z[Cfg::DK];
     float den[Cfg::C];
@@ -139,14 +145,36 @@ __device__ __forceinline__ int p_pos(int t, int s) {
     return ((u ^ (t & Cfg::TMASK)) * Cfg::UE) + e;
 }
 
-// Store N consecutive tokens (starting at s0, a multiple of N) of one
-// transposed-tile row, one 16-byte unit at a time.
+// Store a run of N consecutive tokens (starting at s0, a multiple of N) of
+// one transposed-tile row, held as N/2 packed token pairs, one 16-byte unit
+// (or less) per vector write.
 template <class Cfg, int N>
-__device__ __forceinline__ void store_tr_run(typename Cfg::E* rowp, int row, int s0, const float* x) {
-    constexpr int PIECE = N < Cfg::UE ? N : Cfg::UE;
+__device__ __forceinline__ void store_pairs(typename Cfg::E* rowp, int row, int s0,
+                                            const typename Cfg::Pair* w) {
+    using E = typename Cfg::E;
+    constexpr int PIECE = N < Cfg::UE ? N : Cfg::UE;      // elements per write
+    constexpr int BYTES = PIECE * (int)sizeof(E);
+    using V = typename std::conditional<
+        BYTES == 16, uint4, typename std::conditional<BYTES == 8, uint2, uint32_t>::type>::type;
+    constexpr int PP = PIECE / 2;                          // pairs per write
 #pragma unroll
-    for (int q = 0; q < N / PIECE; ++q)
-        store_run<Cfg::BF16, PIECE>(rowp + tr_pos<Cfg>(row, s0 + q * PIECE), x + q * PIECE);
+    for (int q = 0; q < N / PIECE; ++q) {
+        V v;
+        __builtin_memcpy(&v, w + q * PP, sizeof v);
+        *reinterpret_cast<V*>(rowp + tr_pos<Cfg>(row, s0 + q * PIECE)) = v;
+    }
+}
+// (lo of a, lo of b) and (hi of a, hi of b) for pairs of two channels at two
+// consecutive tokens: turns channel pairs into token pairs.
+template <class Cfg>
+__device__ __forceinline__ typename Cfg::Pair lo_pair(typename Cfg::Pair a, typename Cfg::Pair b) {
+    if constexpr (Cfg::BF16) return __builtin_amdgcn_perm(b, a, 0x05040100u);
+    else return make_float2(a.x, b.x);
+}
+template <class Cfg>
+__device__ __forceinline__ typename Cfg::Pair hi_pair(typename Cfg::Pair a, typename Cfg::Pair b) {
+    if constexpr (Cfg::BF16) return __builtin_amdgcn_perm(b, a, 0x07060302u);
+    else return make_float2(a.y, b.y);
 }
 
 template <class Cfg>
@@ -236,6 +264,14 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
             E* z2p = &sm.p[0][0];
             for (int i = tid; i < C * CP; i += Cfg::NT) z2p[i] = E(0);
         }
+        if constexpr (!SONLY) {
+            // without the normaliser every row divides by one, so the output
+            // epilogue has no branch: a uniform branch between the last
+            // matrix-core write of the accumulators and their first VALU read
+            // has been seen to lose the wait states that read needs
+            if (!norm)
+                for (int j = tid; j < C; j += Cfg::NT) sm.den[j] = 1.0f;
+        }
         if constexpr (GATE == LA_GATE_GAMMA) {
             const float l2g = p.log2_gamma[h];
             for (int j = tid; j < C + 2; j += Cfg::NT) sm.gpow[j] = j == 0 ? 1.0f : exp2f((float)j * l2g);
@@ -265,41 +301,56 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
                 accS[mb][nb][i] = Sin ? Sin[(size_t)(16 * mb + 4 * g + i) * DV + colbase + 16 * nb + r] : 0.0f;
     if (norm && tid < DK) sm.z[tid] = zin ? zin[tid] : 0.0f;
 
-    // segment decay product (state pass)
-    float seg_la = 0.0f, seg_lb = 0.0f;  // DIAG: summed log-gates of this thread's channels
+    // segment bookkeeping of the ktg == 0 threads lives in LDS: the previous
+    // chunk's after-factor (post) and the segment's summed log2-gates
+    if (tid < DK) {
+        sm.post[tid] = 1.0f;
+        sm.segsum[tid] = 0.0f;
+    }
     float seg_g = 1.0f;                  // GAMMA: product of gamma^c
-    float post_a = 1.0f, post_b = 1.0f;  // DIAG: after-factor of the previous chunk
 
-    // ---- register prefetch of one chunk (byte offsets within the slice)
-    Pair rgq[KTPG], rgk[KTPG], rgv[VTPG];
-    float2 rgla[KTPG];
-    auto load_chunk = [&](int c) {
+    // ---- register prefetch, two chunks ahead (byte offsets within the slice)
+    // k, v and the gates run PD chunks ahead (PD register sets); q, needed
+    // only by the main pass, one chunk ahead
+    struct ChunkRegs {
+        Pair k[KTPG], v[VTPG];
+        float2 la[GATE == LA_GATE_DIAG ? KTPG : 1];
+    };
+    Pair qreg[SONLY ? 1 : KTPG];
+    auto load_chunk = [&](int c, ChunkRegs& rg) {
         const uint32_t t0 = (uint32_t)c * C;
         const uint32_t okk = ((t0 + ktg * KTPG) * DK + 2 * kcp) * ES;
         const uint32_t ovv = ((t0 + vtg * VTPG) * DV + 2 * vcp) * ES;
         const uint32_t oaa = ((t0 + ktg * KTPG) * DK + 2 * kcp) * 4;
 #pragma unroll
         for (int j = 0; j < KTPG; ++j) {
-            if constexpr (!SONLY) rgq[j] = buf_load_pair<Pair>(rq, okk + j * DK * ES);
-            rgk[j] = buf_load_pair<Pair>(rk, okk + j * DK * ES);
-            if constexpr (GATE == LA_GATE_DIAG) rgla[j] = buf_load_pair<float2>(rla, oaa + j * DK * 4);
+            rg.k[j] = buf_load_pair<Pair>(rk, okk + j * DK * ES);
+            if constexpr (GATE == LA_GATE_DIAG) rg.la[j] = buf_load_pair<float2>(rla, oaa + j * DK * 4);
         }
 #pragma unroll
-        for (int j = 0; j < VTPG; ++j) rgv[j] = buf_load_pair<Pair>(rv, ovv + j * DV * ES);
+        for (int j = 0; j < VTPG; ++j) rg.v[j] = buf_load_pair<Pair>(rv, ovv + j * DV * ES);
     };
-    if (c_begin < c_end) load_chunk(c_begin);
+    auto load_q = [&](int c) {
+        if constexpr (!SONLY) {
+            const uint32_t okk = (((uint32_t)c * C + ktg * KTPG) * DK + 2 * kcp) * ES;
+#pragma unroll
+            for (int j = 0; j < KTPG; ++j) qreg[j] = buf_load_pair<Pair>(rq, okk + j * DK * ES);
+        }
+    };
+    constexpr float kLog2e = 1.4426950408889634f;
 
-    for (int c = c_begin; c < c_end; ++c) {
+    // one chunk: consumes rg, then refills it with chunk c + 2
+    auto step = [&](const int c, ChunkRegs& rg) {
         const int t0 = c * C;
         const int clen = min(C, L - t0);
 
-        // ---- a2: chunk-local inclusive log-gate prefix of this thread's run
+        // ---- a2: chunk-local inclusive log2-gate prefix of this thread's run
         if constexpr (GATE == LA_GATE_DIAG) {
             float ca = 0.f, cb = 0.f;
 #pragma unroll
             for (int j = 0; j < KTPG; ++j) {
-                ca += rgla[j].x;
-                cb += rgla[j].y;
+                ca += rg.la[j].x * kLog2e;
+                cb += rg.la[j].y * kLog2e;
             }
             __syncthreads();  // the previous chunk is done with every LDS tile
             *reinterpret_cast<float2*>(&sm.tot[ktg][2 * kcp]) = make_float2(ca, cb);
@@ -308,98 +359,98 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
         // DIAG: the token-group sums are visible.
         __syncthreads();
 
+        // exclusive prefix of the token-group sums (this group's offset), the
+        // chunk-middle reference and the chunk total, in log2 units
         float refa = 0.f, refb = 0.f, tota = 0.f, totb = 0.f, offa = 0.f, offb = 0.f;
         if constexpr (GATE == LA_GATE_DIAG) {
 #pragma unroll
             for (int g2 = 0; g2 < KTG; ++g2) {
+                if (g2 == ktg) { offa = tota; offb = totb; }
+                if (g2 == KTG / 2) { refa = tota; refb = totb; }
                 const float2 tv = *reinterpret_cast<const float2*>(&sm.tot[g2][2 * kcp]);
-                if (g2 < ktg) { offa += tv.x; offb += tv.y; }
-                if (g2 < KTG / 2) { refa += tv.x; refb += tv.y; }
                 tota += tv.x;
                 totb += tv.y;
             }
-            seg_la += tota;
-            seg_lb += totb;
         }
         if constexpr (GATE == LA_GATE_GAMMA) seg_g *= sm.gpow[clen];
 
-        // ---- a1: features and decay factors, written to the LDS tiles
+        // ---- a1: features and decay factors, written to the LDS tiles,
+        // one token at a time; the transposed runs are packed as they go
         {
-            float fk[KTPG][2], fq[SONLY ? 1 : KTPG][2];
-#pragma unroll
-            for (int j = 0; j < KTPG; ++j) {
-                fk[j][0] = T::lo(rgk[j]);
-                fk[j][1] = T::hi(rgk[j]);
-                if constexpr (!SONLY) {
-                    fq[j][0] = T::lo(rgq[j]);
-                    fq[j][1] = T::hi(rgq[j]);
-                }
-            }
-            if (elu1) {  // uniform: one branch per chunk
-#pragma unroll
-                for (int j = 0; j < KTPG; ++j) {
-                    fk[j][0] = elu1f(fk[j][0]);
-                    fk[j][1] = elu1f(fk[j][1]);
-                    if constexpr (!SONLY) {
-                        fq[j][0] = elu1f(fq[j][0]);
-                        fq[j][1] = elu1f(fq[j][1]);
-                    }
-                }
-            }
-            float kta[KTPG], ktb[KTPG];
+            static_assert(KTPG % 2 == 0 && VTPG % 2 == 0, "transposed runs are whole token pairs");
+            using W = typename Cfg::Pair;   // two consecutive tokens of one channel
+            W kpa[KTPG / 2], kpb[KTPG / 2];
             float ba = offa, bb = offb;
+            float prev_ka = 0.f, prev_kb = 0.f;
 #pragma unroll
             for (int j = 0; j < KTPG; ++j) {
                 const int t = ktg * KTPG + j;
                 const bool ok = t < clen;
-                const float ka = ok ? fk[j][0] : 0.f;
-                const float kb = ok ? fk[j][1] : 0.f;
+                float ka = T::lo(rg.k[j]), kb = T::hi(rg.k[j]);
+                if (elu1) {
+                    ka = elu1f(ka);
+                    kb = elu1f(kb);
+                }
+                ka = ok ? ka : 0.f;
+                kb = ok ? kb : 0.f;
                 float fqa = 1.f, fqb = 1.f, fka = 1.f, fkb = 1.f, fta = 1.f, ftb = 1.f;
                 if constexpr (GATE == LA_GATE_DIAG) {
-                    ba += rgla[j].x;
-                    bb += rgla[j].y;
-                    fqa = __expf(ba - refa);
-                    fqb = __expf(bb - refb);
-                    fka = __expf(refa - ba);
-                    fkb = __expf(refb - bb);
+                    ba += rg.la[j].x * kLog2e;
+                    bb += rg.la[j].y * kLog2e;
+                    const float da = ba - refa, db = bb - refb;
+                    fqa = __builtin_amdgcn_exp2f(da);
+                    fqb = __builtin_amdgcn_exp2f(db);
+                    fka = __builtin_amdgcn_exp2f(-da);
+                    fkb = __builtin_amdgcn_exp2f(-db);
                     fta = fka;
                     ftb = fkb;
                 } else if constexpr (GATE == LA_GATE_GAMMA) {
                     fta = ftb = ok ? sm.gpow[clen - 1 - t] : 0.f;
                 }
                 if constexpr (!SONLY) {
-                    const float qa = fq[j][0];
-                    const float qb = fq[j][1];
+                    float qa = T::lo(qreg[j]), qb = T::hi(qreg[j]);
+                    if (elu1) {
+                        qa = elu1f(qa);
+                        qb = elu1f(qb);
+                    }
                     const int pos = qk_pos<Cfg>(t, 2 * kcp);
                     *reinterpret_cast<Pair*>(&sm.q[t][pos]) = T::pack(qa * fqa, qb * fqb);
                     *reinterpret_cast<Pair*>(&sm.k[t][pos]) = T::pack(ka * fka, kb * fkb);
                 }
-                kta[j] = ka * fta;
-                ktb[j] = kb * ftb;
+                const float xa = ka * fta, xb = kb * ftb;
+                if (j & 1) {
+                    kpa[j / 2] = T::pack(prev_ka, xa);
+                    kpb[j / 2] = T::pack(prev_kb, xb);
+                } else {
+                    prev_ka = xa;
+                    prev_kb = xb;
+                }
             }
-            store_tr_run<Cfg, KTPG>(&sm.kt[2 * kcp][0], 2 * kcp, ktg * KTPG, kta);
-            store_tr_run<Cfg, KTPG>(&sm.kt[2 * kcp + 1][0], 2 * kcp + 1, ktg * KTPG, ktb);
-            float va[VTPG], vb[VTPG];
+            store_pairs<Cfg, KTPG>(&sm.kt[2 * kcp][0], 2 * kcp, ktg * KTPG, kpa);
+            store_pairs<Cfg, KTPG>(&sm.kt[2 * kcp + 1][0], 2 * kcp + 1, ktg * KTPG, kpb);
+            // V^T: regroup the loaded (channel, channel) pairs into (token, token) pairs
+            W vpa[VTPG / 2], vpb[VTPG / 2];
 #pragma unroll
-            for (int j = 0; j < VTPG; ++j) {
-                va[j] = T::lo(rgv[j]);
-                vb[j] = T::hi(rgv[j]);
+            for (int j = 0; j < VTPG / 2; ++j) {
+                vpa[j] = lo_pair<Cfg>(rg.v[2 * j], rg.v[2 * j + 1]);
+                vpb[j] = hi_pair<Cfg>(rg.v[2 * j], rg.v[2 * j + 1]);
             }
-            store_tr_run<Cfg, VTPG>(&sm.vt[2 * vcp][0], 2 * vcp, vtg * VTPG, va);
-            store_tr_run<Cfg, VTPG>(&sm.vt[2 * vcp + 1][0], 2 * vcp + 1, vtg * VTPG, vb);
+            store_pairs<Cfg, VTPG>(&sm.vt[2 * vcp][0], 2 * vcp, vtg * VTPG, vpa);
+            store_pairs<Cfg, VTPG>(&sm.vt[2 * vcp + 1][0], 2 * vcp + 1, vtg * VTPG, vpb);
             if (ktg == 0) {
                 // per-row state factors: DIAG applies post(previous) * pre(this)
                 // before the chunk; GAMMA applies gamma^c after op2
                 float sa = 1.f, sb = 1.f, prea = 1.f, preb = 1.f, pa = 1.f, pb = 1.f;
                 if constexpr (GATE == LA_GATE_DIAG) {
-                    prea = __expf(refa);
-                    preb = __expf(refb);
-                    pa = __expf(tota - refa);
-                    pb = __expf(totb - refb);
-                    sa = post_a * prea;
-                    sb = post_b * preb;
-                    post_a = pa;
-                    post_b = pb;
+                    const float2 pprev = *reinterpret_cast<const float2*>(&sm.post[2 * kcp]);
+                    float2& ss = *reinterpret_cast<float2*>(&sm.segsum[2 * kcp]);
+                    ss = make_float2(ss.x + tota, ss.y + totb);
+                    prea = __builtin_amdgcn_exp2f(refa);
+                    preb = __builtin_amdgcn_exp2f(refb);
+                    pa = __builtin_amdgcn_exp2f(tota - refa);
+                    pb = __builtin_amdgcn_exp2f(totb - refb);
+                    sa = pprev.x * prea;
+                    sb = pprev.y * preb;
                 } else if constexpr (GATE == LA_GATE_GAMMA) {
                     sa = sb = prea = preb = sm.gpow[clen];
                 }
@@ -409,8 +460,9 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
             }
         }
 
-        // ---- prefetch the next chunk while this one is computed
-        if (c + 1 < c_end) load_chunk(c + 1);
+        // ---- refill the registers: q with chunk c + 1, this set with c + PD
+        if (c + 1 < c_end) load_q(c + 1);
+        if (c + Cfg::PD < c_end) load_chunk(c + Cfg::PD, rg);
         __syncthreads();
 
         // ---- op1: P^T = Kh Qh^T on the lower-triangular tiles; each lane
@@ -546,7 +598,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
 #pragma unroll
             for (int tb = 0; tb < TB; ++tb) {
                 const int t = 16 * tb + r;
-                const float inv = norm ? 1.0f / sm.den[t] : 1.0f;
+                const float inv = __builtin_amdgcn_rcpf(sm.den[t]);
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {
                     const uint32_t off = ((uint32_t)(t0 + t) * DV + colbase + 16 * nb + 4 * g) * ES;
@@ -573,13 +625,27 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
                 for (int nb = 0; nb < NB; ++nb) accS[mb][nb] = T::mma(a, vf[kk][nb], accS[mb][nb]);
             }
         }
+    };
+    {
+        if (c_begin < c_end) load_q(c_begin);
+        if constexpr (Cfg::PD == 2) {
+            ChunkRegs ra, rb;
+            if (c_begin < c_end) load_chunk(c_begin, ra);
+            if (c_begin + 1 < c_end) load_chunk(c_begin + 1, rb);
+            for (int c = c_begin; c < c_end; c += 2) {
+                step(c, ra);
+                if (c + 1 < c_end) step(c + 1, rb);
+            }
+        } else {
+            ChunkRegs ra;
+            if (c_begin < c_end) load_chunk(c_begin, ra);
+            for (int c = c_begin; c < c_end; ++c) step(c, ra);
+        }
     }
     // DIAG: the last chunk's after-factor
     if constexpr (GATE == LA_GATE_DIAG) {
         __syncthreads();
-        if (ktg == 0) *reinterpret_cast<float2*>(&sm.scale[2 * kcp]) = make_float2(post_a, post_b);
-        __syncthreads();
-        scale_rows<Cfg>(accS, sm.scale, g);
+        scale_rows<Cfg>(accS, sm.post, g);
     }
 
     // ---- epilogue
@@ -590,10 +656,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
         zout = p.ws_z + ((size_t)bh * P + seg) * DK;
         float* aout = p.ws_a + ((size_t)bh * P + seg) * DK;
         if constexpr (GATE == LA_GATE_DIAG) {
-            if (ktg == 0) {
-                aout[2 * kcp] = __expf(seg_la);
-                aout[2 * kcp + 1] = __expf(seg_lb);
-            }
+            if (tid < DK) aout[tid] = __builtin_amdgcn_exp2f(sm.segsum[tid]);
         } else {
             if (tid < DK) aout[tid] = GATE == LA_GATE_GAMMA ? seg_g : 1.0f;
         }
