@@ -4,6 +4,9 @@ Every ``csrc/*.hip`` file is compiled by hipcc into ``_build/`` (in parallel)
 and the objects are linked into ``recurrent_attention_amd/liblinattn.so``.
 ``python -m recurrent_attention_amd.build`` rebuilds everything;
 ``--incremental`` skips objects newer than their sources and headers.
+``--check-hazards`` also compiles each source to device assembly and checks
+every path from a matrix-core instruction to the first reader of its result
+(:mod:`recurrent_attention_amd.hazards`); a violation fails the build.
 """
 from __future__ import annotations
 
@@ -74,13 +77,50 @@ def build(incremental: bool = False, jobs: int | None = None, verbose: bool = Fa
     return LIB
 
 
+def _assemble(src, out_dir):
+    asm = os.path.join(out_dir, os.path.basename(src)[:-4] + ".s")
+    cmd = [HIPCC] + CFLAGS + ["--cuda-device-only", "-S", src, "-o", asm]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc -S failed on {os.path.basename(src)}:\n{res.stderr}")
+    return asm
+
+
+def device_assembly(out_dir: str | None = None, jobs: int | None = None) -> list:
+    """Compile every source to gfx950 assembly (same flags as the library)."""
+    out_dir = out_dir or os.path.join(BUILD, "asm")
+    os.makedirs(out_dir, exist_ok=True)
+    srcs = _sources()
+    jobs = jobs or min(len(srcs), max(1, min(8, os.cpu_count() or 1)))
+    with ThreadPoolExecutor(jobs) as ex:
+        return list(ex.map(lambda s: _assemble(s, out_dir), srcs))
+
+
+def check_hazards(out_dir: str | None = None, jobs: int | None = None) -> list:
+    """Violations (see :mod:`.hazards`) over the assembly of every source."""
+    from . import hazards
+    found = []
+    for path in device_assembly(out_dir, jobs):
+        with open(path) as f:
+            found += [(os.path.basename(path), v) for v in hazards.check_asm(f.read())]
+    return found
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--incremental", action="store_true")
     ap.add_argument("-j", "--jobs", type=int, default=None)
     ap.add_argument("-v", "--verbose", action="store_true")
+    ap.add_argument("--check-hazards", action="store_true")
     a = ap.parse_args(argv)
     print(build(a.incremental, a.jobs, a.verbose))
+    if a.check_hazards:
+        found = check_hazards(jobs=a.jobs)
+        for name, v in found:
+            print(f"{name}: {v}")
+        print(f"{len(found)} matrix-core hazard(s)")
+        return 1 if found else 0
+    return 0
 
 
 if __name__ == "__main__":
