@@ -61,6 +61,13 @@ namespace la {
 typedef __attribute__((ext_vector_type(2))) unsigned int u32x2_t;
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;
 
+// Channels per thread in the global -> register mapping: 4 where the chunk
+// still leaves every thread an even run of tokens, else 2.
+constexpr int run_width(int D, int NT, int C) {
+    return (NT % (D / 4) == 0 && NT / (D / 4) >= 2 && C % (NT / (D / 4)) == 0 &&
+            (C / (NT / (D / 4))) % 2 == 0) ? 4 : 2;
+}
+
 template <int DK_, int DV_, int C_, bool BF16_, int GATE_, bool SONLY_, int NW_>
 struct ChunkCfg {
     static constexpr int DK = DK_, DV = DV_, C = C_, GATE = GATE_, NW = NW_;
@@ -81,16 +88,23 @@ struct ChunkCfg {
     static constexpr int TU = CP / UE;                 // units per transposed row / P row
     static constexpr int QMASK = (QU < 8 ? QU : 8) - 1;
     static constexpr int TMASK = (TU < 8 ? TU : 8) - 1;
-    // global -> register mapping: each thread owns two adjacent channels
-    // (a column pair) over a run of consecutive tokens
-    static constexpr int KCP = DK / 2, KTG = NT / KCP, KTPG = C / KTG;
-    static constexpr int VCP = DV / 2, VTG = NT / VCP, VTPG = C / VTG;
-    // chunks of k, v and gates held in registers ahead of use (fp32 pairs
-    // are twice as large, so fp32 keeps one)
-    static constexpr int PD = BF16 ? 2 : 1;
+    // global -> register mapping: each thread owns a run of CW adjacent key
+    // channels (VW value channels) over KTPG (VTPG) consecutive tokens and
+    // reads it with one buffer load per token
+    static constexpr int CW = run_width(DK, NT, C), VW = run_width(DV, NT, C);
+    static constexpr int KCP = DK / CW, KTG = NT / KCP, KTPG = C / KTG;
+    static constexpr int VCP = DV / VW, VTG = NT / VCP, VTPG = C / VTG;
+    static constexpr int KWORDS = CW * (int)sizeof(E) / 4;   // 32-bit words per run
+    static constexpr int VWORDS = VW * (int)sizeof(E) / 4;
+    // chunks of k, v and gates held in registers ahead of use: one chunk of
+    // work covers the memory latency, and a second register set only takes
+    // registers from the rest of the loop
+    static constexpr int PD = 1;
     static_assert(DV % (16 * NW) == 0 && DK % 16 == 0 && C % 16 == 0, "tile shape");
     static_assert(!BF16 || DK % 32 == 0, "bf16 needs d_k >= 32");
-    static_assert(NT % KCP == 0 && NT % VCP == 0, "column-pair mapping");
+    static_assert(NT % KCP == 0 && NT % VCP == 0, "channel-run mapping");
+    static_assert(KTPG * (int)sizeof(E) <= 16 && VTPG * (int)sizeof(E) <= 16,
+                  "a transposed run stays within one 16-byte unit");
     static_assert(KTG >= 2 && KTG % 2 == 0 && KTPG >= 1 && VTPG >= 1, "token groups");
     static_assert(KTG * KTPG == C && VTG * VTPG == C, "token groups cover the chunk");
 };
@@ -104,7 +118,7 @@ struct ChunkSmem {
     alignas(16) E kt[Cfg::DK][Cfg::CP];  // Kt, [i][swizzled s]
     alignas(16) E vt[Cfg::DV][Cfg::CP];  // V^T, [n][swizzled s]
     alignas(16) E p[CQ][Cfg::CP];        // masked scores, [t][swizzled s]
-    alignas(16) float tot[Cfg::KTG][Cfg::DK];  // per token-group log-gate sums
+    alignas(16) float tot[Cfg::NW][Cfg::DK];   // per-wave log2-gate sums
     alignas(16) float scale[Cfg::DK];    // per-row state factor applied this chunk
     alignas(16) float pre[Cfg::DK];      // this chunk's before/after factors
     alignas(16) float post[Cfg::DK];
@@ -164,17 +178,47 @@ __device__ __forceinline__ void store_pairs(typename Cfg::E* rowp, int row, int 
         *reinterpret_cast<V*>(rowp + tr_pos<Cfg>(row, s0 + q * PIECE)) = v;
     }
 }
-// (lo of a, lo of b) and (hi of a, hi of b) for pairs of two channels at two
-// consecutive tokens: turns channel pairs into token pairs.
-template <class Cfg>
-__device__ __forceinline__ typename Cfg::Pair lo_pair(typename Cfg::Pair a, typename Cfg::Pair b) {
-    if constexpr (Cfg::BF16) return __builtin_amdgcn_perm(b, a, 0x05040100u);
-    else return make_float2(a.x, b.x);
+// A run of adjacent channels of one token as raw 32-bit words.
+template <int N>
+struct Words {
+    uint32_t w[N];
+};
+// Channel c of a run as a float (bf16 runs hold two channels per word).
+template <bool BF16, int N>
+__device__ __forceinline__ float run_elem(const Words<N>& x, int c) {
+    if constexpr (BF16) return (c & 1) ? bf16hi(x.w[c >> 1]) : bf16lo(x.w[c >> 1]);
+    else return __uint_as_float(x.w[c]);
 }
-template <class Cfg>
-__device__ __forceinline__ typename Cfg::Pair hi_pair(typename Cfg::Pair a, typename Cfg::Pair b) {
-    if constexpr (Cfg::BF16) return __builtin_amdgcn_perm(b, a, 0x07060302u);
-    else return make_float2(a.y, b.y);
+// N floats as a run of the tile element type.
+template <bool BF16, int N>
+__device__ __forceinline__ Words<(BF16 ? N / 2 : N)> pack_run(const float* x) {
+    Words<(BF16 ? N / 2 : N)> o;
+    if constexpr (BF16) {
+#pragma unroll
+        for (int i = 0; i < N / 2; ++i) o.w[i] = pack_bf16(x[2 * i], x[2 * i + 1]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < N; ++i) o.w[i] = __float_as_uint(x[i]);
+    }
+    return o;
+}
+template <int N>
+__device__ __forceinline__ void lds_store_words(void* p, const Words<N>& x) {
+    if constexpr (N == 1) *reinterpret_cast<uint32_t*>(p) = x.w[0];
+    else if constexpr (N == 2) *reinterpret_cast<uint2*>(p) = make_uint2(x.w[0], x.w[1]);
+    else *reinterpret_cast<uint4*>(p) = make_uint4(x.w[0], x.w[1], x.w[2], x.w[3]);
+}
+// Value of x in lane src of the wave (an LDS-crossbar permute).
+__device__ __forceinline__ float lane_read(float x, int src) {
+    return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(x)));
+}
+// Channel c of two runs at consecutive tokens as one token pair.
+template <class Cfg, int N>
+__device__ __forceinline__ typename Cfg::Pair token_pair(const Words<N>& a, const Words<N>& b, int c) {
+    if constexpr (Cfg::BF16)
+        return __builtin_amdgcn_perm(b.w[c >> 1], a.w[c >> 1], (c & 1) ? 0x07060302u : 0x05040100u);
+    else
+        return make_float2(__uint_as_float(a.w[c]), __uint_as_float(b.w[c]));
 }
 
 template <class Cfg>
@@ -192,24 +236,25 @@ __device__ __forceinline__ void scale_rows(f32x4_t (&acc)[Cfg::MB][Cfg::NB], con
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
-template <class Pair>
-__device__ __forceinline__ Pair buf_load_pair(__amdgpu_buffer_rsrc_t r, uint32_t off);
-template <>
-__device__ __forceinline__ uint32_t buf_load_pair<uint32_t>(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
-}
-template <>
-__device__ __forceinline__ float2 buf_load_pair<float2>(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    return __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+template <int N>
+__device__ __forceinline__ Words<N> buf_load_words(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    if constexpr (N == 1) {
+        return Words<1>{{__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0)}};
+    } else if constexpr (N == 2) {
+        return __builtin_bit_cast(Words<2>, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+    } else {
+        static_assert(N == 4, "runs are 4, 8 or 16 bytes");
+        return __builtin_bit_cast(Words<4>, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    }
 }
 
-template <class Cfg>
+template <class Cfg, bool ELU1>
 __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
     constexpr int DK = Cfg::DK, DV = Cfg::DV, C = Cfg::C, GATE = Cfg::GATE;
     constexpr int NB = Cfg::NB, MB = Cfg::MB, TB = Cfg::TB, NW = Cfg::NW;
     constexpr int KPL = Cfg::KPL, MK = Cfg::MK, CP = Cfg::CP;
-    constexpr int KCP = Cfg::KCP, KTG = Cfg::KTG, KTPG = Cfg::KTPG;
-    constexpr int VCP = Cfg::VCP, VTPG = Cfg::VTPG;
+    constexpr int KCP = Cfg::KCP, KTG = Cfg::KTG, KTPG = Cfg::KTPG, CW = Cfg::CW;
+    constexpr int VCP = Cfg::VCP, VTPG = Cfg::VTPG, VW = Cfg::VW;
     constexpr bool SONLY = Cfg::SONLY, BF16 = Cfg::BF16;
     constexpr int ES = (int)sizeof(typename Cfg::E);
     using T = typename Cfg::T;
@@ -221,6 +266,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     const int r = lane & 15, g = lane >> 4;
     const int P = p.P;
     const int PS = SONLY ? P - 1 : P;  // the state pass skips the last segment
@@ -230,7 +276,6 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
     const int L = p.L;
     const int c_begin = seg * p.cps;
     const int c_end = min(c_begin + p.cps, p.nchunks);
-    const int elu1 = p.phi_elu1;
     const bool norm = p.normalize != 0;
 
     const int kcp = tid % KCP, ktg = tid / KCP;
@@ -313,150 +358,200 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
     // k, v and the gates run PD chunks ahead (PD register sets); q, needed
     // only by the main pass, one chunk ahead
     struct ChunkRegs {
-        Pair k[KTPG], v[VTPG];
-        float2 la[GATE == LA_GATE_DIAG ? KTPG : 1];
+        Words<Cfg::KWORDS> k[KTPG];
+        Words<Cfg::VWORDS> v[VTPG];
+        Words<CW> la[GATE == LA_GATE_DIAG ? KTPG : 1];
     };
-    Pair qreg[SONLY ? 1 : KTPG];
+    Words<Cfg::KWORDS> qreg[SONLY ? 1 : KTPG];
     auto load_chunk = [&](int c, ChunkRegs& rg) {
         const uint32_t t0 = (uint32_t)c * C;
-        const uint32_t okk = ((t0 + ktg * KTPG) * DK + 2 * kcp) * ES;
-        const uint32_t ovv = ((t0 + vtg * VTPG) * DV + 2 * vcp) * ES;
-        const uint32_t oaa = ((t0 + ktg * KTPG) * DK + 2 * kcp) * 4;
+        const uint32_t okk = ((t0 + ktg * KTPG) * DK + CW * kcp) * ES;
+        const uint32_t ovv = ((t0 + vtg * VTPG) * DV + VW * vcp) * ES;
+        const uint32_t oaa = ((t0 + ktg * KTPG) * DK + CW * kcp) * 4;
 #pragma unroll
         for (int j = 0; j < KTPG; ++j) {
-            rg.k[j] = buf_load_pair<Pair>(rk, okk + j * DK * ES);
-            if constexpr (GATE == LA_GATE_DIAG) rg.la[j] = buf_load_pair<float2>(rla, oaa + j * DK * 4);
+            rg.k[j] = buf_load_words<Cfg::KWORDS>(rk, okk + j * DK * ES);
+            if constexpr (GATE == LA_GATE_DIAG) rg.la[j] = buf_load_words<CW>(rla, oaa + j * DK * 4);
         }
 #pragma unroll
-        for (int j = 0; j < VTPG; ++j) rg.v[j] = buf_load_pair<Pair>(rv, ovv + j * DV * ES);
+        for (int j = 0; j < VTPG; ++j) rg.v[j] = buf_load_words<Cfg::VWORDS>(rv, ovv + j * DV * ES);
     };
     auto load_q = [&](int c) {
         if constexpr (!SONLY) {
-            const uint32_t okk = (((uint32_t)c * C + ktg * KTPG) * DK + 2 * kcp) * ES;
+            const uint32_t okk = (((uint32_t)c * C + ktg * KTPG) * DK + CW * kcp) * ES;
 #pragma unroll
-            for (int j = 0; j < KTPG; ++j) qreg[j] = buf_load_pair<Pair>(rq, okk + j * DK * ES);
+            for (int j = 0; j < KTPG; ++j) qreg[j] = buf_load_words<Cfg::KWORDS>(rq, okk + j * DK * ES);
         }
     };
     constexpr float kLog2e = 1.4426950408889634f;
 
-    // one chunk: consumes rg, then refills it with chunk c + 2
+    // one chunk: consumes rg, then refills it with chunk c + PD
     auto step = [&](const int c, ChunkRegs& rg) {
         const int t0 = c * C;
         const int clen = min(C, L - t0);
 
-        // ---- a2: chunk-local inclusive log2-gate prefix of this thread's run
-        if constexpr (GATE == LA_GATE_DIAG) {
-            float ca = 0.f, cb = 0.f;
+        // ---- a2: chunk-local log2-gate sums.  Each thread sums its own run;
+        // the token groups of one wave (lanes KCP apart hold the same channels
+        // at consecutive groups) are combined by a scan over lane shuffles,
+        // and only the wave totals go through LDS.
+        float gexc[CW], gmid[CW];   // earlier groups of this wave; one wave: chunk middle
 #pragma unroll
-            for (int j = 0; j < KTPG; ++j) {
-                ca += rg.la[j].x * kLog2e;
-                cb += rg.la[j].y * kLog2e;
+        for (int i = 0; i < CW; ++i) gexc[i] = gmid[i] = 0.f;
+        if constexpr (GATE == LA_GATE_DIAG) {
+            float gsum[CW], incl[CW], wsum[CW];
+#pragma unroll
+            for (int i = 0; i < CW; ++i) gsum[i] = 0.f;
+#pragma unroll
+            for (int j = 0; j < KTPG; ++j)
+#pragma unroll
+                for (int i = 0; i < CW; ++i) gsum[i] += run_elem<false>(rg.la[j], i) * kLog2e;
+#pragma unroll
+            for (int i = 0; i < CW; ++i) incl[i] = gsum[i];
+#pragma unroll
+            for (int sft = KCP; sft < 64; sft *= 2)
+#pragma unroll
+                for (int i = 0; i < CW; ++i) {
+                    const float y = lane_read(incl[i], lane - sft);
+                    if (lane >= sft) incl[i] += y;
+                }
+#pragma unroll
+            for (int i = 0; i < CW; ++i) {
+                gexc[i] = incl[i] - gsum[i];
+                wsum[i] = KCP < 64 ? lane_read(incl[i], 64 - KCP + lane % KCP) : incl[i];
+                if constexpr (NW == 1) gmid[i] = lane_read(incl[i], (KTG / 2 - 1) * KCP + lane % KCP);
             }
             __syncthreads();  // the previous chunk is done with every LDS tile
-            *reinterpret_cast<float2*>(&sm.tot[ktg][2 * kcp]) = make_float2(ca, cb);
+            if (lane < KCP) lds_store_words<CW>(&sm.tot[wave][CW * kcp], pack_run<false, CW>(wsum));
         }
         // NONE/GAMMA: the previous chunk is done with every LDS tile.
-        // DIAG: the token-group sums are visible.
+        // DIAG: the wave sums are visible.
         __syncthreads();
 
-        // exclusive prefix of the token-group sums (this group's offset), the
+        // this group's offset (exclusive prefix over the chunk), the
         // chunk-middle reference and the chunk total, in log2 units
-        float refa = 0.f, refb = 0.f, tota = 0.f, totb = 0.f, offa = 0.f, offb = 0.f;
-        if constexpr (GATE == LA_GATE_DIAG) {
+        float gref[CW], gtot[CW], goff[CW];
 #pragma unroll
-            for (int g2 = 0; g2 < KTG; ++g2) {
-                if (g2 == ktg) { offa = tota; offb = totb; }
-                if (g2 == KTG / 2) { refa = tota; refb = totb; }
-                const float2 tv = *reinterpret_cast<const float2*>(&sm.tot[g2][2 * kcp]);
-                tota += tv.x;
-                totb += tv.y;
+        for (int i = 0; i < CW; ++i) gref[i] = gtot[i] = goff[i] = 0.f;
+        if constexpr (GATE == LA_GATE_DIAG) {
+            // all wave sums are read before any is used, so the reads overlap
+            float x[NW][CW];
+#pragma unroll
+            for (int w2 = 0; w2 < NW; ++w2) {
+                const float* tv = &sm.tot[w2][CW * kcp];
+                if constexpr (CW == 4) {
+                    const float4 v4 = *reinterpret_cast<const float4*>(tv);
+                    x[w2][0] = v4.x; x[w2][1] = v4.y; x[w2][2] = v4.z; x[w2][3] = v4.w;
+                } else {
+                    const float2 v2 = *reinterpret_cast<const float2*>(tv);
+                    x[w2][0] = v2.x; x[w2][1] = v2.y;
+                }
+            }
+            float wpre[CW];
+#pragma unroll
+            for (int i = 0; i < CW; ++i) wpre[i] = 0.f;
+#pragma unroll
+            for (int w2 = 0; w2 < NW; ++w2) {
+                if (w2 == wave_u) {   // uniform: the earlier waves' total
+#pragma unroll
+                    for (int i = 0; i < CW; ++i) wpre[i] = gtot[i];
+                }
+#pragma unroll
+                for (int i = 0; i < CW; ++i) gtot[i] += x[w2][i];
+                if (NW > 1 && w2 == NW / 2 - 1) {
+#pragma unroll
+                    for (int i = 0; i < CW; ++i) gref[i] = gtot[i];
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < CW; ++i) {
+                goff[i] = wpre[i] + gexc[i];
+                if constexpr (NW == 1) gref[i] = gmid[i];
             }
         }
         if constexpr (GATE == LA_GATE_GAMMA) seg_g *= sm.gpow[clen];
 
-        // ---- a1: features and decay factors, written to the LDS tiles,
-        // one token at a time; the transposed runs are packed as they go
+        // ---- a1: features and decay factors, written to the LDS tiles, one
+        // token at a time; the transposed runs are packed as they go
         {
             static_assert(KTPG % 2 == 0 && VTPG % 2 == 0, "transposed runs are whole token pairs");
             using W = typename Cfg::Pair;   // two consecutive tokens of one channel
-            W kpa[KTPG / 2], kpb[KTPG / 2];
-            float ba = offa, bb = offb;
-            float prev_ka = 0.f, prev_kb = 0.f;
+            W kp[CW][KTPG / 2];
+            float bcur[CW], prev[CW];
+#pragma unroll
+            for (int i = 0; i < CW; ++i) {
+                bcur[i] = goff[i];
+                prev[i] = 0.f;
+            }
 #pragma unroll
             for (int j = 0; j < KTPG; ++j) {
                 const int t = ktg * KTPG + j;
                 const bool ok = t < clen;
-                float ka = T::lo(rg.k[j]), kb = T::hi(rg.k[j]);
-                if (elu1) {
-                    ka = elu1f(ka);
-                    kb = elu1f(kb);
-                }
-                ka = ok ? ka : 0.f;
-                kb = ok ? kb : 0.f;
-                float fqa = 1.f, fqb = 1.f, fka = 1.f, fkb = 1.f, fta = 1.f, ftb = 1.f;
-                if constexpr (GATE == LA_GATE_DIAG) {
-                    ba += rg.la[j].x * kLog2e;
-                    bb += rg.la[j].y * kLog2e;
-                    const float da = ba - refa, db = bb - refb;
-                    fqa = __builtin_amdgcn_exp2f(da);
-                    fqb = __builtin_amdgcn_exp2f(db);
-                    fka = __builtin_amdgcn_exp2f(-da);
-                    fkb = __builtin_amdgcn_exp2f(-db);
-                    fta = fka;
-                    ftb = fkb;
-                } else if constexpr (GATE == LA_GATE_GAMMA) {
-                    fta = ftb = ok ? sm.gpow[clen - 1 - t] : 0.f;
+                float qv[CW], kv[CW];
+                float ftok = 1.f;
+                if constexpr (GATE == LA_GATE_GAMMA) ftok = ok ? sm.gpow[clen - 1 - t] : 0.f;
+#pragma unroll
+                for (int i = 0; i < CW; ++i) {
+                    float ka = run_elem<BF16>(rg.k[j], i);
+                    if constexpr (ELU1) ka = elu1f(ka);
+                    ka = ok ? ka : 0.f;
+                    float fq = 1.f, fk = 1.f, ft = ftok;
+                    if constexpr (GATE == LA_GATE_DIAG) {
+                        bcur[i] += run_elem<false>(rg.la[j], i) * kLog2e;
+                        const float d = bcur[i] - gref[i];
+                        fq = __builtin_amdgcn_exp2f(d);
+                        fk = __builtin_amdgcn_exp2f(-d);
+                        ft = fk;
+                    }
+                    if constexpr (!SONLY) {
+                        float qa = run_elem<BF16>(qreg[j], i);
+                        if constexpr (ELU1) qa = elu1f(qa);
+                        qv[i] = qa * fq;
+                        kv[i] = ka * fk;
+                    }
+                    const float x = ka * ft;
+                    if (j & 1) kp[i][j / 2] = T::pack(prev[i], x);
+                    else prev[i] = x;
                 }
                 if constexpr (!SONLY) {
-                    float qa = T::lo(qreg[j]), qb = T::hi(qreg[j]);
-                    if (elu1) {
-                        qa = elu1f(qa);
-                        qb = elu1f(qb);
-                    }
-                    const int pos = qk_pos<Cfg>(t, 2 * kcp);
-                    *reinterpret_cast<Pair*>(&sm.q[t][pos]) = T::pack(qa * fqa, qb * fqb);
-                    *reinterpret_cast<Pair*>(&sm.k[t][pos]) = T::pack(ka * fka, kb * fkb);
-                }
-                const float xa = ka * fta, xb = kb * ftb;
-                if (j & 1) {
-                    kpa[j / 2] = T::pack(prev_ka, xa);
-                    kpb[j / 2] = T::pack(prev_kb, xb);
-                } else {
-                    prev_ka = xa;
-                    prev_kb = xb;
+                    const int pos = qk_pos<Cfg>(t, CW * kcp);
+                    lds_store_words(&sm.q[t][pos], pack_run<BF16, CW>(qv));
+                    lds_store_words(&sm.k[t][pos], pack_run<BF16, CW>(kv));
                 }
             }
-            store_pairs<Cfg, KTPG>(&sm.kt[2 * kcp][0], 2 * kcp, ktg * KTPG, kpa);
-            store_pairs<Cfg, KTPG>(&sm.kt[2 * kcp + 1][0], 2 * kcp + 1, ktg * KTPG, kpb);
-            // V^T: regroup the loaded (channel, channel) pairs into (token, token) pairs
-            W vpa[VTPG / 2], vpb[VTPG / 2];
 #pragma unroll
-            for (int j = 0; j < VTPG / 2; ++j) {
-                vpa[j] = lo_pair<Cfg>(rg.v[2 * j], rg.v[2 * j + 1]);
-                vpb[j] = hi_pair<Cfg>(rg.v[2 * j], rg.v[2 * j + 1]);
-            }
-            store_pairs<Cfg, VTPG>(&sm.vt[2 * vcp][0], 2 * vcp, vtg * VTPG, vpa);
-            store_pairs<Cfg, VTPG>(&sm.vt[2 * vcp + 1][0], 2 * vcp + 1, vtg * VTPG, vpb);
+            for (int i = 0; i < CW; ++i)
+                store_pairs<Cfg, KTPG>(&sm.kt[CW * kcp + i][0], CW * kcp + i, ktg * KTPG, kp[i]);
+            // V^T: regroup the loaded channel runs into token pairs
+            W vp[VW][VTPG / 2];
+#pragma unroll
+            for (int m = 0; m < VTPG / 2; ++m)
+#pragma unroll
+                for (int i = 0; i < VW; ++i) vp[i][m] = token_pair<Cfg>(rg.v[2 * m], rg.v[2 * m + 1], i);
+#pragma unroll
+            for (int i = 0; i < VW; ++i)
+                store_pairs<Cfg, VTPG>(&sm.vt[VW * vcp + i][0], VW * vcp + i, vtg * VTPG, vp[i]);
             if (ktg == 0) {
                 // per-row state factors: DIAG applies post(previous) * pre(this)
                 // before the chunk; GAMMA applies gamma^c after op2
-                float sa = 1.f, sb = 1.f, prea = 1.f, preb = 1.f, pa = 1.f, pb = 1.f;
+                float sc[CW], pr[CW], po[CW];
+#pragma unroll
+                for (int i = 0; i < CW; ++i) sc[i] = pr[i] = po[i] = 1.f;
                 if constexpr (GATE == LA_GATE_DIAG) {
-                    const float2 pprev = *reinterpret_cast<const float2*>(&sm.post[2 * kcp]);
-                    float2& ss = *reinterpret_cast<float2*>(&sm.segsum[2 * kcp]);
-                    ss = make_float2(ss.x + tota, ss.y + totb);
-                    prea = __builtin_amdgcn_exp2f(refa);
-                    preb = __builtin_amdgcn_exp2f(refb);
-                    pa = __builtin_amdgcn_exp2f(tota - refa);
-                    pb = __builtin_amdgcn_exp2f(totb - refb);
-                    sa = pprev.x * prea;
-                    sb = pprev.y * preb;
+#pragma unroll
+                    for (int i = 0; i < CW; ++i) {
+                        const int row = CW * kcp + i;
+                        sm.segsum[row] += gtot[i];
+                        pr[i] = __builtin_amdgcn_exp2f(gref[i]);
+                        po[i] = __builtin_amdgcn_exp2f(gtot[i] - gref[i]);
+                        sc[i] = sm.post[row] * pr[i];
+                    }
                 } else if constexpr (GATE == LA_GATE_GAMMA) {
-                    sa = sb = prea = preb = sm.gpow[clen];
+#pragma unroll
+                    for (int i = 0; i < CW; ++i) sc[i] = pr[i] = sm.gpow[clen];
                 }
-                *reinterpret_cast<float2*>(&sm.scale[2 * kcp]) = make_float2(sa, sb);
-                *reinterpret_cast<float2*>(&sm.pre[2 * kcp]) = make_float2(prea, preb);
-                *reinterpret_cast<float2*>(&sm.post[2 * kcp]) = make_float2(pa, pb);
+                lds_store_words<CW>(&sm.scale[CW * kcp], pack_run<false, CW>(sc));
+                lds_store_words<CW>(&sm.pre[CW * kcp], pack_run<false, CW>(pr));
+                lds_store_words<CW>(&sm.post[CW * kcp], pack_run<false, CW>(po));
             }
         }
 
@@ -728,7 +823,10 @@ hipError_t launch_chunk_dt(const ChunkParams& p, int chunk, int gate, bool sonly
 #define LA_CHUNK_LAUNCH(CC, GG, SO)                                                      \
     do {                                                                                 \
         using Cfg = ChunkCfg<D, D, CC, BF, GG, SO, NWV>;                                 \
-        hipLaunchKernelGGL((chunk_kernel<Cfg>), dim3(nblocks), dim3(Cfg::NT), 0, s, p);  \
+        if (p.phi_elu1)                                                                  \
+            hipLaunchKernelGGL((chunk_kernel<Cfg, true>), dim3(nblocks), dim3(Cfg::NT), 0, s, p); \
+        else                                                                             \
+            hipLaunchKernelGGL((chunk_kernel<Cfg, false>), dim3(nblocks), dim3(Cfg::NT), 0, s, p); \
         return hipGetLastError();                                                        \
     } while (0)
 #define LA_CHUNK_GATES(CC, SO)                                   \

@@ -23,8 +23,8 @@ import sys
 from collections import defaultdict
 
 FAMILIES = [
-    ("chunk_main", re.compile(r"la::chunk_kernel<la::ChunkCfg<(\d+), (\d+), (\d+), (\w+), (\d), false>")),
-    ("chunk_state", re.compile(r"la::chunk_kernel<la::ChunkCfg<(\d+), (\d+), (\d+), (\w+), (\d), true>")),
+    ("chunk_main", re.compile(r"la::chunk_kernel<la::ChunkCfg<(\d+), (\d+), (\d+), (\w+), (\d), false(, \d+)?>")),
+    ("chunk_state", re.compile(r"la::chunk_kernel<la::ChunkCfg<(\d+), (\d+), (\d+), (\w+), (\d), true(, \d+)?>")),
     ("state_scan", re.compile(r"la::state_scan_kernel")),
     ("decode", re.compile(r"la::decode_kernel")),
     ("copy", re.compile(r"__amd_rocclr_copyBuffer")),
