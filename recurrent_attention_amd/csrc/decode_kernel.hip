@@ -6,24 +6,34 @@
 //   S <- A S + phi(k) v^T,  z <- A z + phi(k),  o = phi(q)^T S [/ phi(q).z]
 //
 // The step is a streaming read-modify-write of the fp32 state (64 KiB per
-// pair at d = 128), so it is HBM-bound.  One 256-thread workgroup per pair:
-// each thread owns a quad of consecutive columns (16-byte accesses, a whole
-// 512-byte row per 32 threads) over DK / rows-per-pass rows, issues all its
-// state loads before using them, and the partial outputs of the row groups
-// are reduced through LDS.
+// pair at d = 128), so it is HBM-bound.  One workgroup per pair (512 threads
+// at d = 128, where that streams best, else 256): each thread owns a quad of
+// consecutive columns (16-byte non-temporal accesses, a whole 512-byte row
+// per 32 threads) over DK / rows-per-pass rows, issues all its state loads
+// before using them, and the partial outputs of the row groups are reduced
+// through LDS.
 #include "la_device.h"
 #include "la_internal.h"
 
 namespace la {
 
+template <int DK, int DV>
+struct DecodeShape {
+    static constexpr int NT = DK * DV >= 128 * 128 ? 512 : 256;   // threads
+};
+
+// eight waves per SIMD (at most 64 registers) keep four 512-thread
+// workgroups, 256 KiB of state reads, in flight per CU
 template <int DK, int DV, bool BF16, int GATE>
-__global__ __launch_bounds__(256) void decode_kernel(const DecodeParams p) {
+__global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) __attribute__((amdgpu_waves_per_eu(8, 8)))
+void decode_kernel(const DecodeParams p) {
     using T = Elem<BF16>;
     using E = typename T::E;
+    constexpr int NT = DecodeShape<DK, DV>::NT;
     constexpr int CQ = DV / 4;               // column quads per row
-    constexpr int RPP = 256 / CQ;            // rows per pass
+    constexpr int RPP = NT / CQ;             // rows per pass
     constexpr int NPASS = (DK + RPP - 1) / RPP;
-    static_assert(256 % CQ == 0, "column quads must divide the workgroup");
+    static_assert(NT % CQ == 0, "column quads must divide the workgroup");
 
     __shared__ float sq[DK], sk[DK], sa[DK], sqz[DK];
     __shared__ float sv[DV];
@@ -103,7 +113,7 @@ __global__ __launch_bounds__(256) void decode_kernel(const DecodeParams p) {
 
 template <int D, bool BF>
 static hipError_t launch_decode_dt(const DecodeParams& p, int gate, hipStream_t s) {
-    const dim3 grid(p.BH), block(256);
+    const dim3 grid(p.BH), block(DecodeShape<D, D>::NT);
     if (gate == LA_GATE_NONE) hipLaunchKernelGGL((decode_kernel<D, D, BF, 0>), grid, block, 0, s, p);
     else if (gate == LA_GATE_GAMMA) hipLaunchKernelGGL((decode_kernel<D, D, BF, 1>), grid, block, 0, s, p);
     else hipLaunchKernelGGL((decode_kernel<D, D, BF, 2>), grid, block, 0, s, p);
