@@ -774,10 +774,14 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
 
 // Segment scan: S_in[0] = S0, S_in[j+1] = a_j * S_in[j] + U_j, written in
 // place over the workspace slots (slot j holds U_j on entry, S_in[j] on exit).
+// Only the multiply-adds are sequential: each thread reads a batch of its
+// segment slots and factors before running the chain over them, so the
+// memory latency is paid once per batch rather than once per segment.
 template <int DK, int DV>
 __global__ __launch_bounds__(256) void state_scan_kernel(const ChunkParams p) {
     constexpr int N4 = DK * DV / 4;
     constexpr int NBX = (N4 + 255) / 256;
+    constexpr int NBATCH = 8;
     const int bh = blockIdx.x / NBX;
     const int bx = blockIdx.x % NBX;
     const int e4 = bx * 256 + threadIdx.x;
@@ -787,25 +791,52 @@ __global__ __launch_bounds__(256) void state_scan_kernel(const ChunkParams p) {
         const int row = (e4 * 4) / DV;
         float4 x = p.S0 ? reinterpret_cast<const float4*>(p.S0 + (size_t)bh * SS)[e4]
                         : make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int j = 0; j < P - 1; ++j) {
-            float4* slot = reinterpret_cast<float4*>(p.ws_S + ((size_t)bh * P + j) * SS) + e4;
-            const float4 u = *slot;
-            *slot = x;
-            const float a = p.ws_a[((size_t)bh * P + j) * DK + row];
-            x = make_float4(a * x.x + u.x, a * x.y + u.y, a * x.z + u.z, a * x.w + u.w);
+        float4* slots = reinterpret_cast<float4*>(p.ws_S + (size_t)bh * P * SS) + e4;
+        const float* as = p.ws_a + (size_t)bh * P * DK + row;
+        for (int j0 = 0; j0 < P - 1; j0 += NBATCH) {
+            float4 u[NBATCH];
+            float a[NBATCH];
+#pragma unroll
+            for (int jj = 0; jj < NBATCH; ++jj) {
+                if (j0 + jj < P - 1) {
+                    u[jj] = slots[(size_t)(j0 + jj) * (SS / 4)];
+                    a[jj] = as[(size_t)(j0 + jj) * DK];
+                }
+            }
+#pragma unroll
+            for (int jj = 0; jj < NBATCH; ++jj) {
+                if (j0 + jj < P - 1) {
+                    slots[(size_t)(j0 + jj) * (SS / 4)] = x;
+                    x = make_float4(a[jj] * x.x + u[jj].x, a[jj] * x.y + u[jj].y,
+                                    a[jj] * x.z + u[jj].z, a[jj] * x.w + u[jj].w);
+                }
+            }
         }
-        reinterpret_cast<float4*>(p.ws_S + ((size_t)bh * P + P - 1) * SS)[e4] = x;
+        slots[(size_t)(P - 1) * (SS / 4)] = x;
     }
     if (p.normalize && bx == 0 && threadIdx.x < DK) {
         const int i = threadIdx.x;
         float zx = p.z0 ? p.z0[(size_t)bh * DK + i] : 0.f;
-        for (int j = 0; j < P - 1; ++j) {
-            float* slot = p.ws_z + ((size_t)bh * P + j) * DK + i;
-            const float u = *slot;
-            *slot = zx;
-            zx = p.ws_a[((size_t)bh * P + j) * DK + i] * zx + u;
+        float* zs = p.ws_z + (size_t)bh * P * DK + i;
+        const float* as = p.ws_a + (size_t)bh * P * DK + i;
+        for (int j0 = 0; j0 < P - 1; j0 += NBATCH) {
+            float u[NBATCH], a[NBATCH];
+#pragma unroll
+            for (int jj = 0; jj < NBATCH; ++jj) {
+                if (j0 + jj < P - 1) {
+                    u[jj] = zs[(size_t)(j0 + jj) * DK];
+                    a[jj] = as[(size_t)(j0 + jj) * DK];
+                }
+            }
+#pragma unroll
+            for (int jj = 0; jj < NBATCH; ++jj) {
+                if (j0 + jj < P - 1) {
+                    zs[(size_t)(j0 + jj) * DK] = zx;
+                    zx = a[jj] * zx + u[jj];
+                }
+            }
         }
-        p.ws_z[((size_t)bh * P + P - 1) * DK + i] = zx;
+        zs[(size_t)(P - 1) * DK] = zx;
     }
 }
 
