@@ -96,10 +96,11 @@ struct ChunkCfg {
     static constexpr int VCP = DV / VW, VTG = NT / VCP, VTPG = C / VTG;
     static constexpr int KWORDS = CW * (int)sizeof(E) / 4;   // 32-bit words per run
     static constexpr int VWORDS = VW * (int)sizeof(E) / 4;
-    // chunks of k, v and gates held in registers ahead of use: one chunk of
-    // work covers the memory latency, and a second register set only takes
-    // registers from the rest of the loop
-    static constexpr int PD = 1;
+    // chunks of k, v and gates held in registers ahead of use.  One chunk of
+    // main-pass work covers the memory latency, and a second register set
+    // would only take registers from the rest of its loop; the state pass
+    // has a shorter chunk and registers to spare, so it keeps two (bf16)
+    static constexpr int PD = (SONLY && BF16) ? 2 : 1;
     static_assert(DV % (16 * NW) == 0 && DK % 16 == 0 && C % 16 == 0, "tile shape");
     static_assert(!BF16 || DK % 32 == 0, "bf16 needs d_k >= 32");
     static_assert(NT % KCP == 0 && NT % VCP == 0, "channel-run mapping");
