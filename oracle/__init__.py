@@ -11,6 +11,8 @@ Forms (all compute the same function; see ``oracle.c`` for the citations):
 * :func:`run`        -- the token-by-token recurrence, the definition.
 * :func:`parallel`   -- the all-pairs masked form with direct decay products.
 * :func:`chunkwise`  -- the chunkwise form with a ragged last chunk.
+* :func:`backward`   -- reverse-mode derivative of the token loop (no
+  normaliser): dq, dk, dv, d log_alpha, dS0 from dout and dS_final.
 
 Layouts follow the GPU boundary: q, k ``[B,H,L,dk]``, v and out
 ``[B,H,L,dv]``, S ``[B,H,dk,dv]`` (rows indexed by the key channel), z
@@ -45,6 +47,8 @@ MUTATIONS = {
     "cross_off_by_one": 8,
     "state_off_by_one": 9,
     "gamma_squared": 10,
+    "bwd_no_decay": 11,
+    "bwd_dq_prev": 12,
 }
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -78,6 +82,9 @@ def _load():
         lib.oracle_chunkwise.argtypes = common + [i, dp, dp, dp, i]
         for f in (lib.oracle_run, lib.oracle_parallel, lib.oracle_chunkwise):
             f.restype = ctypes.c_int
+        lib.oracle_backward.argtypes = [i, i, i, i, i, i, dp, dp, i, dp, dp, dp, dp, dp, dp,
+                                        dp, dp, dp, dp, dp, i, i]
+        lib.oracle_backward.restype = ctypes.c_int
         lib.oracle_multiscale_decays.argtypes = [i, dp]
         lib.oracle_phi.argtypes = [i, ctypes.c_double]
         lib.oracle_phi.restype = ctypes.c_double
@@ -172,6 +179,41 @@ def chunkwise(q, k, v, chunk, gate_mode=GATE_NONE, gamma=None, log_alpha=None,
     lib = _load()
     return _call(lib.oracle_chunkwise, [int(chunk)], [int(nthreads)], q, k, v,
                  gate_mode, gamma, log_alpha, phi, normalize, S0, z0)
+
+
+def backward(q, k, v, dout, gate_mode=GATE_NONE, gamma=None, log_alpha=None,
+             phi=PHI_IDENTITY, S0=None, dS_final=None, checkpoint=64, nthreads=1):
+    """Gradients of the token loop (no normaliser).
+
+    ``dout`` is the gradient of the loss with respect to ``out`` and
+    ``dS_final`` (optional) with respect to the final state.  Returns a dict
+    with ``dq``, ``dk``, ``dv`` (fp64, the layouts of q, k, v), ``dlog_alpha``
+    (diagonal gate only, else None) and ``dS0`` ``[B,H,dk,dv]`` (the
+    gradient of the initial state, zero-state runs included).
+    """
+    lib = _load()
+    two_d, (B, H, L, dk, dv), q, k, v, g, la, S0, _ = _prep(
+        q, k, v, gate_mode, gamma, log_alpha, S0, None)
+    do = _f64(dout)
+    do = np.ascontiguousarray(do.reshape(B, H, L, dv))
+    dSf = _f64(dS_final)
+    if dSf is not None:
+        dSf = np.ascontiguousarray(dSf.reshape(B, H, dk, dv))
+    dq = np.zeros((B, H, L, dk))
+    dk_ = np.zeros((B, H, L, dk))
+    dv_ = np.zeros((B, H, L, dv))
+    dla = np.zeros((B, H, L, dk)) if gate_mode == GATE_DIAG else None
+    dS0 = np.zeros((B, H, dk, dv))
+    rc = lib.oracle_backward(B, H, L, dk, dv, int(gate_mode), _ptr(g), _ptr(la), int(phi),
+                             _ptr(q), _ptr(k), _ptr(v), _ptr(S0), _ptr(do), _ptr(dSf),
+                             _ptr(dq), _ptr(dk_), _ptr(dv_), _ptr(dla), _ptr(dS0),
+                             int(checkpoint), int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle rejected its arguments (rc={rc})")
+    res = {"dq": dq, "dk": dk_, "dv": dv_, "dlog_alpha": dla, "dS0": dS0}
+    if two_d:
+        res = {n: (a[0, 0] if a is not None else None) for n, a in res.items()}
+    return res
 
 
 def multiscale_decays(n: int) -> np.ndarray:

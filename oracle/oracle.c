@@ -47,6 +47,23 @@
  *  - elu uses alpha = 1;
  *  - S0 is decayed by the first token's gate like any older state.
  *
+ * oracle_backward is the reverse-mode derivative of the token loop above,
+ * written out step by step in reverse (no chunking, no cumulative-sum
+ * identities): with G the gradient of the loss with respect to the state
+ * after token t,
+ *
+ *   G     += qf_t do_t^T              (o_t = qf_t^T S_t reads S_t)
+ *   dqf_t  = S_t do_t
+ *   dkf_t  = G v_t,   dv_t = G^T kf_t  (S_t = diag(a_t) S_{t-1} + kf_t v_t^T)
+ *   d log a_t,i = a_t,i sum_j G[i,j] S_{t-1}[i,j]   (diagonal gate only)
+ *   G      = diag(a_t) G               (the gradient of S_{t-1})
+ *
+ * starting from G = dS_final and ending with dS0 = G; the chain rule through
+ * phi gives dq = dqf phi'(q), dk = dkf phi'(k).  The states S_t are
+ * recomputed block by block from checkpoints every `ck` tokens.  The
+ * normalised read-out has no backward here.  None of this comes from the
+ * pages (they give no gradients); it is the plain derivative of the loop.
+ *
  * The global `oracle_mutation` plants a known mistake for the mutation tests
  * that prove the pins can catch it; it is 0 (no mutation) everywhere else.
  */
@@ -70,7 +87,9 @@ enum {
     MUT_GATE_DROPPED = 7,  /* A_t treated as 1                        */
     MUT_CROSS_OFF_BY_1 = 8,/* chunkwise: cross term decayed to t-1     */
     MUT_STATE_OFF_BY_1 = 9,/* chunkwise: carried state decayed c-1     */
-    MUT_GAMMA_SQUARED = 10 /* retention gate applied twice per token  */
+    MUT_GAMMA_SQUARED = 10,/* retention gate applied twice per token  */
+    MUT_BWD_NO_DECAY = 11, /* backward: G not decayed by a_t           */
+    MUT_BWD_DQ_PREV = 12   /* backward: dq read from S_{t-1}           */
 };
 
 int oracle_mutation = 0;
@@ -101,7 +120,12 @@ typedef struct {
     double* out;             /* [B,H,L,dv]              */
     double *S_final, *z_final; /* may be NULL           */
     int chunk;               /* chunkwise form only     */
-    int form;                /* 0 loop, 1 parallel, 2 chunkwise */
+    /* backward (form 3) */
+    const double *dout, *dS_final;          /* [B,H,L,dv], [B,H,dk,dv] (may be NULL) */
+    double *dq, *dk_out, *dv_out;           /* [B,H,L,dk|dv]          */
+    double *dlog_alpha, *dS0;               /* [B,H,L,dk], [B,H,dk,dv] (may be NULL) */
+    int ck;                                 /* checkpoint spacing      */
+    int form;                /* 0 loop, 1 parallel, 2 chunkwise, 3 backward */
     int nthreads;
     int next_pair;           /* work counter (guarded by mu) */
     pthread_mutex_t mu;
@@ -363,6 +387,97 @@ static void run_chunk_pair(const job_t* J, int bh) {
     free(R); free(zr); free(A); free(G); free(QF); free(KF); free(Rn); free(zn);
 }
 
+/* ---------------------------------------------------------------------- */
+/* Backward of the token loop (no normaliser).                             */
+/* ---------------------------------------------------------------------- */
+static double phi_prime(int phi, double x) {
+    if (phi == PHI_ELU1) return x > 0.0 ? 1.0 : exp(x);
+    return 1.0;
+}
+
+/* One forward step S <- diag(a_t) S + kf_t v_t^T for token t of pair bh. */
+static void fwd_step(const job_t* J, int bh, int t, double* S) {
+    const int L = J->L, dk = J->dk, dv = J->dv;
+    const double* kt = J->k + ((size_t)bh * L + t) * dk;
+    const double* vt = J->v + ((size_t)bh * L + t) * dv;
+    for (int i = 0; i < dk; ++i) {
+        const double a = gate_at(J, bh, t, i), kf = oracle_phi(J->phi, kt[i]);
+        double* Si = S + (size_t)i * dv;
+        for (int j = 0; j < dv; ++j) Si[j] = a * Si[j] + kf * vt[j];
+    }
+}
+
+static void run_backward_pair(const job_t* J, int bh) {
+    const int L = J->L, dk = J->dk, dv = J->dv, ck = J->ck;
+    const size_t SS = (size_t)dk * dv;
+    const int nblk = (L + ck - 1) / ck;
+    /* checkpoints: the state before token b*ck */
+    double* cp = (double*)calloc((size_t)(nblk > 0 ? nblk : 1) * SS, sizeof(double));
+    double* S = (double*)calloc(SS, sizeof(double));
+    if (J->S0) memcpy(S, J->S0 + (size_t)bh * SS, sizeof(double) * SS);
+    for (int t = 0; t < L; ++t) {
+        if (t % ck == 0) memcpy(cp + (size_t)(t / ck) * SS, S, sizeof(double) * SS);
+        fwd_step(J, bh, t, S);
+    }
+    /* states inside one block: blk[m] = state after token b*ck + m - 1 */
+    double* blk = (double*)malloc((size_t)(ck + 1) * SS * sizeof(double));
+    double* G = (double*)calloc(SS, sizeof(double));
+    if (J->dS_final) memcpy(G, J->dS_final + (size_t)bh * SS, sizeof(double) * SS);
+    for (int b = nblk - 1; b >= 0; --b) {
+        const int t0 = b * ck, t1 = (t0 + ck < L) ? t0 + ck : L;
+        memcpy(blk, cp + (size_t)b * SS, sizeof(double) * SS);
+        for (int t = t0; t < t1; ++t) {
+            memcpy(blk + (size_t)(t - t0 + 1) * SS, blk + (size_t)(t - t0) * SS, sizeof(double) * SS);
+            fwd_step(J, bh, t, blk + (size_t)(t - t0 + 1) * SS);
+        }
+        for (int t = t1 - 1; t >= t0; --t) {
+            const double* St = blk + (size_t)(t - t0 + 1) * SS;   /* after token t  */
+            const double* Sp = blk + (size_t)(t - t0) * SS;       /* before token t */
+            const double* qt = J->q + ((size_t)bh * L + t) * dk;
+            const double* kt = J->k + ((size_t)bh * L + t) * dk;
+            const double* vt = J->v + ((size_t)bh * L + t) * dv;
+            const double* dot = J->dout + ((size_t)bh * L + t) * dv;
+            double* dqt = J->dq + ((size_t)bh * L + t) * dk;
+            double* dkt = J->dk_out + ((size_t)bh * L + t) * dk;
+            double* dvt = J->dv_out + ((size_t)bh * L + t) * dv;
+            const double* Sq = oracle_mutation == MUT_BWD_DQ_PREV ? Sp : St;
+            for (int i = 0; i < dk; ++i) {
+                const double qf = oracle_phi(J->phi, qt[i]);
+                double acc = 0.0;
+                for (int j = 0; j < dv; ++j) {
+                    G[(size_t)i * dv + j] += qf * dot[j];
+                    acc += Sq[(size_t)i * dv + j] * dot[j];
+                }
+                dqt[i] = acc * phi_prime(J->phi, qt[i]);
+            }
+            for (int j = 0; j < dv; ++j) dvt[j] = 0.0;
+            for (int i = 0; i < dk; ++i) {
+                const double kf = oracle_phi(J->phi, kt[i]);
+                const double* Gi = G + (size_t)i * dv;
+                double acc = 0.0;
+                for (int j = 0; j < dv; ++j) {
+                    acc += Gi[j] * vt[j];
+                    dvt[j] += Gi[j] * kf;
+                }
+                dkt[i] = acc * phi_prime(J->phi, kt[i]);
+            }
+            for (int i = 0; i < dk; ++i) {
+                const double a = gate_at(J, bh, t, i);
+                double* Gi = G + (size_t)i * dv;
+                if (J->gate_mode == GATE_DIAG && J->dlog_alpha) {
+                    double acc = 0.0;
+                    for (int j = 0; j < dv; ++j) acc += Gi[j] * Sp[(size_t)i * dv + j];
+                    J->dlog_alpha[((size_t)bh * L + t) * dk + i] = a * acc;
+                }
+                if (oracle_mutation != MUT_BWD_NO_DECAY)
+                    for (int j = 0; j < dv; ++j) Gi[j] *= a;
+            }
+        }
+    }
+    if (J->dS0) memcpy(J->dS0 + (size_t)bh * SS, G, sizeof(double) * SS);
+    free(cp); free(S); free(blk); free(G);
+}
+
 static void* worker(void* arg) {
     job_t* J = (job_t*)arg;
     const int npairs = J->B * J->H;
@@ -373,7 +488,8 @@ static void* worker(void* arg) {
         if (bh >= npairs) break;
         if (J->form == 0) run_loop_pair(J, bh);
         else if (J->form == 1) run_parallel_pair(J, bh);
-        else run_chunk_pair(J, bh);
+        else if (J->form == 2) run_chunk_pair(J, bh);
+        else run_backward_pair(J, bh);
     }
     return NULL;
 }
@@ -383,6 +499,8 @@ static int run_job(job_t* J) {
     if (J->gate_mode == GATE_GAMMA && !J->gamma) return 1;
     if (J->gate_mode == GATE_DIAG && !J->log_alpha) return 1;
     if (J->form == 2 && J->chunk < 1) return 1;
+    if (J->form == 3 && (J->normalize || J->ck < 1 || !J->dout || !J->dq || !J->dk_out || !J->dv_out))
+        return 1;
     const int npairs = J->B * J->H;
     int nt = J->nthreads < 1 ? 1 : J->nthreads;
     if (nt > npairs) nt = npairs;
@@ -439,5 +557,25 @@ int oracle_chunkwise(int B, int H, int L, int dk, int dv, int gate_mode,
                      int chunk, double* out, double* S_final, double* z_final,
                      int nthreads) {
     FILL_JOB(2, chunk, nthreads)
+    return run_job(&J);
+}
+
+/* Backward of the token loop: given dout (and optionally dS_final), the
+ * gradients dq, dk, dv, d log_alpha (diagonal gate, may be NULL) and dS0
+ * (may be NULL).  `ck` is the checkpoint spacing (any value >= 1 gives the
+ * same result).  The normalised read-out is not supported (returns 1). */
+int oracle_backward(int B, int H, int L, int dk, int dv, int gate_mode,
+                    const double* gamma, const double* log_alpha, int phi,
+                    const double* q, const double* k, const double* v,
+                    const double* S0, const double* dout, const double* dS_final,
+                    double* dq, double* dk_out, double* dv_out,
+                    double* dlog_alpha, double* dS0, int ck, int nthreads) {
+    const int normalize = 0;
+    const double* z0 = NULL;
+    double *out = NULL, *S_final = NULL, *z_final = NULL;
+    FILL_JOB(3, 0, nthreads)
+    J.dout = dout; J.dS_final = dS_final;
+    J.dq = dq; J.dk_out = dk_out; J.dv_out = dv_out;
+    J.dlog_alpha = dlog_alpha; J.dS0 = dS0; J.ck = ck;
     return run_job(&J);
 }
