@@ -136,6 +136,53 @@ size_t la_chunk_fwd_workspace_bytes(const la_desc* d, int chunk);
 int la_chunk_fwd_segments(const la_desc* d, int chunk);
 
 /*
+ * la_chunk_bwd -- gradients of a prefill (the reverse-mode derivative of
+ * la_chunk_fwd without the normaliser) for the loss
+ *     sum(dout * out) + sum(dS_final * S_final).
+ * The derivative of the recurrence written out per chunk: the states before
+ * every chunk are recomputed, the state gradient G runs the same recurrence
+ * from the end (G_{t-1} = A_t G_t + phi(q_t)^T dout_t), and each chunk then
+ * forms its gradients from its own tokens, the state before it and G after
+ * it ("Module 22: Linear & Recurrent Attention", sections "The Three Faces
+ * of Retention" and "The One Recurrence Behind Them All" for the forward
+ * it differentiates).  The chunk length is the library's own
+ * (la_chunk_bwd_chunk); the result does not depend on it beyond rounding.
+ *   d                  as for la_chunk_fwd; normalize must be 0
+ *                      (LA_ERR_UNSUPPORTED otherwise)
+ *   q, k, v            device, [B,H,L,dk|dv] of d->dtype, the forward inputs
+ *   dout               device [B,H,L,dv] of d->dtype, gradient of out
+ *   gate_mode, gamma_or_log_alpha   as for la_chunk_fwd
+ *   S0                 device fp32 [B,H,dk,dv] forward initial state, or NULL
+ *   dS_final           device fp32 [B,H,dk,dv] gradient of S_final, or NULL
+ *   dq, dk, dv         device [B,H,L,dk|dv] of d->dtype, written: gradients
+ *                      of the raw q, k (through phi) and v
+ *   dlog_alpha         DIAG: device fp32 [B,H,L,dk], written; must be NULL
+ *                      for the other gates (gamma gets no gradient)
+ *   dS0                device fp32 [B,H,dk,dv] gradient of S0, written, or
+ *                      NULL (not returned)
+ *   workspace          device scratch of at least
+ *                      la_chunk_bwd_workspace_bytes(d) bytes; clobbered
+ *   stream             hipStream_t
+ * Outputs must not alias inputs.
+ */
+la_status la_chunk_bwd(const la_desc* d, const void* q, const void* k,
+                       const void* v, const void* dout, int gate_mode,
+                       const float* gamma_or_log_alpha, const float* S0,
+                       const float* dS_final, void* dq, void* dk, void* dv,
+                       float* dlog_alpha, float* dS0, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace la_chunk_bwd needs: fp32 states at every chunk
+ * boundary (B*H*(3*ceil(L/C)+1)*dk*dv floats: the state before each chunk
+ * and the final state, the state gradient after each chunk row-major and
+ * transposed) plus the segment slots.
+ * Returns 0 for an invalid descriptor. */
+size_t la_chunk_bwd_workspace_bytes(const la_desc* d);
+
+/* Chunk length C the backward uses for this shape (0 if invalid). */
+int la_chunk_bwd_chunk(const la_desc* d);
+
+/*
  * la_decode_step -- fold one token per (b,h) into the resident state.
  *   d          shape with d->L == 1 (B = sequences, H = heads)
  *   q, k, v    device [B,H,dk|dv] of d->dtype
@@ -165,7 +212,8 @@ int la_version(void);
  * la_profile_end() every kernel the library enqueues is bracketed by a pair
  * of HIP events recorded on the stream it is launched on.  la_profile_query
  * waits for those events and reports, for one kernel family
- * ("chunk_main", "chunk_state", "state_scan", "decode"), the number of
+ * ("chunk_main", "chunk_state", "state_scan", "decode", "chunk_store",
+ * "chunk_bwd"), the number of
  * launches and their summed duration in milliseconds.  la_profile_begin
  * clears earlier records.  Event creation happens inside la_profile_begin /
  * the first profiled launch; not for use under graph capture.

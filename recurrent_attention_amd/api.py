@@ -7,7 +7,8 @@ are allocated with torch (device memory is PyTorch's job here).  There is no
 CPU fallback: a missing library or a tensor that is not on a GPU raises.
 
 Functions named ``la_*`` mirror the C entry points one to one;
-:func:`chunk_fwd` and :func:`decode_step` are conveniences around them.
+:func:`chunk_fwd`, :func:`chunk_bwd` and :func:`decode_step` are
+conveniences around them.
 """
 from __future__ import annotations
 
@@ -29,6 +30,7 @@ EXPORTED = (
     "la_chunk_fwd", "la_chunk_fwd_workspace_bytes", "la_chunk_fwd_segments",
     "la_decode_step", "la_status_string", "la_last_error_message",
     "la_version", "la_profile_begin", "la_profile_end", "la_profile_query",
+    "la_chunk_bwd", "la_chunk_bwd_workspace_bytes", "la_chunk_bwd_chunk",
 )
 
 
@@ -68,6 +70,12 @@ def load_library():
     lib.la_chunk_fwd_workspace_bytes.restype = sz
     lib.la_chunk_fwd_segments.argtypes = [dp, i]
     lib.la_chunk_fwd_segments.restype = i
+    lib.la_chunk_bwd.argtypes = [dp, vp, vp, vp, vp, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.la_chunk_bwd.restype = i
+    lib.la_chunk_bwd_workspace_bytes.argtypes = [dp]
+    lib.la_chunk_bwd_workspace_bytes.restype = sz
+    lib.la_chunk_bwd_chunk.argtypes = [dp]
+    lib.la_chunk_bwd_chunk.restype = i
     lib.la_decode_step.argtypes = [dp, vp, vp, vp, i, vp, vp, vp, vp, vp]
     lib.la_decode_step.restype = i
     lib.la_status_string.argtypes = [i]
@@ -106,6 +114,22 @@ def la_chunk_fwd(desc, q, k, v, gate_mode, gamma_or_log_alpha, S0, z0, chunk,
     return load_library().la_chunk_fwd(
         ctypes.byref(desc), q, k, v, int(gate_mode), gamma_or_log_alpha, S0, z0,
         int(chunk), out, S_final, z_final, workspace, int(workspace_bytes), stream)
+
+
+def la_chunk_bwd(desc, q, k, v, dout, gate_mode, gamma_or_log_alpha, S0, dS_final,
+                 dq, dk, dv, dlog_alpha, dS0, workspace, workspace_bytes, stream):
+    """Raw call; pointer arguments are ints (0 = NULL) or ctypes pointers."""
+    return load_library().la_chunk_bwd(
+        ctypes.byref(desc), q, k, v, dout, int(gate_mode), gamma_or_log_alpha, S0, dS_final,
+        dq, dk, dv, dlog_alpha, dS0, workspace, int(workspace_bytes), stream)
+
+
+def la_chunk_bwd_workspace_bytes(desc) -> int:
+    return int(load_library().la_chunk_bwd_workspace_bytes(ctypes.byref(desc)))
+
+
+def la_chunk_bwd_chunk(desc) -> int:
+    return int(load_library().la_chunk_bwd_chunk(ctypes.byref(desc)))
 
 
 def la_decode_step(desc, q, k, v, gate_mode, gate, S, z, out, stream):
@@ -156,7 +180,7 @@ def _torch():
     return torch
 
 
-def _dev_ptr(t, name, dtype=None):
+def _dev_ptr(t, name, dtype=None, shape=None):
     if t is None:
         return None
     torch = _torch()
@@ -168,6 +192,8 @@ def _dev_ptr(t, name, dtype=None):
         raise ValueError(f"{name} must be contiguous")
     if dtype is not None and t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
     return t.data_ptr()
 
 
@@ -227,13 +253,15 @@ def chunk_fwd(q, k, v, gate_mode=LA_GATE_NONE, gamma=None, log_alpha=None,
         g_keep = _gamma_host(gamma, H)
         g_arg = ctypes.c_void_p(g_keep.data_ptr())
     elif gate_mode == LA_GATE_DIAG:
-        g_arg = _dev_ptr(log_alpha, "log_alpha", torch.float32)
+        g_arg = _dev_ptr(log_alpha, "log_alpha", torch.float32, (B, H, L, dk))
     st = la_chunk_fwd(
-        desc, _dev_ptr(q, "q"), _dev_ptr(k, "k", q.dtype), _dev_ptr(v, "v", q.dtype),
-        gate_mode, g_arg, _dev_ptr(S0, "S0", torch.float32),
-        _dev_ptr(z0, "z0", torch.float32), chunk, _dev_ptr(out, "out", q.dtype),
-        _dev_ptr(S_final, "S_final", torch.float32),
-        _dev_ptr(z_final, "z_final", torch.float32),
+        desc, _dev_ptr(q, "q"), _dev_ptr(k, "k", q.dtype, (B, H, L, dk)),
+        _dev_ptr(v, "v", q.dtype, (B, H, L, dv)),
+        gate_mode, g_arg, _dev_ptr(S0, "S0", torch.float32, (B, H, dk, dv)),
+        _dev_ptr(z0, "z0", torch.float32, (B, H, dk)), chunk,
+        _dev_ptr(out, "out", q.dtype, (B, H, L, dv)),
+        _dev_ptr(S_final, "S_final", torch.float32, (B, H, dk, dv)),
+        _dev_ptr(z_final, "z_final", torch.float32, (B, H, dk)),
         _dev_ptr(workspace, "workspace"), ws_bytes, _stream_ptr(stream, dev))
     _check(st)
     del g_keep
@@ -257,14 +285,63 @@ def decode_step(q, k, v, S, z=None, gate_mode=LA_GATE_NONE, gamma=None,
         g_keep = _gamma_host(gamma, H)
         g_arg = ctypes.c_void_p(g_keep.data_ptr())
     elif gate_mode == LA_GATE_DIAG:
-        g_arg = _dev_ptr(log_alpha, "log_alpha", torch.float32)
+        g_arg = _dev_ptr(log_alpha, "log_alpha", torch.float32, (B, H, dk))
     st = la_decode_step(
-        desc, _dev_ptr(q, "q"), _dev_ptr(k, "k", q.dtype), _dev_ptr(v, "v", q.dtype),
-        gate_mode, g_arg, _dev_ptr(S, "S", torch.float32), _dev_ptr(z, "z", torch.float32),
-        _dev_ptr(out, "out", q.dtype), _stream_ptr(stream, q.device))
+        desc, _dev_ptr(q, "q"), _dev_ptr(k, "k", q.dtype, (B, H, dk)),
+        _dev_ptr(v, "v", q.dtype, (B, H, dv)),
+        gate_mode, g_arg, _dev_ptr(S, "S", torch.float32, (B, H, dk, dv)),
+        _dev_ptr(z, "z", torch.float32, (B, H, dk)),
+        _dev_ptr(out, "out", q.dtype, (B, H, dv)), _stream_ptr(stream, q.device))
     _check(st)
     del g_keep
     return out
+
+
+def chunk_bwd(q, k, v, dout, gate_mode=LA_GATE_NONE, gamma=None, log_alpha=None,
+              S0=None, dS_final=None, phi=LA_PHI_IDENTITY, segments=0,
+              workspace=None, stream=None):
+    """Gradients of :func:`chunk_fwd` (no normaliser) for the loss
+    ``sum(dout * out) + sum(dS_final * S_final)``.  Returns a dict with
+    ``dq``, ``dk``, ``dv`` (dtype of q), ``dlog_alpha`` (fp32, DIAG gate
+    only, else None) and ``dS0`` (fp32)."""
+    torch = _torch()
+    B, H, L, dk = q.shape
+    dv = v.shape[-1]
+    dt = _la_dtype(q)
+    desc = make_desc(B, H, L, dk, dv, dt, phi, False, segments)
+    dev = q.device
+    dq = torch.empty((B, H, L, dk), dtype=q.dtype, device=dev)
+    dkk = torch.empty((B, H, L, dk), dtype=q.dtype, device=dev)
+    dvv = torch.empty((B, H, L, dv), dtype=q.dtype, device=dev)
+    dS0 = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    dla = (torch.empty((B, H, L, dk), dtype=torch.float32, device=dev)
+           if gate_mode == LA_GATE_DIAG else None)
+    need = la_chunk_bwd_workspace_bytes(desc)
+    if workspace is None and need:
+        workspace = torch.empty(need // 4 + 4, dtype=torch.float32, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    g_arg = None
+    g_keep = None
+    if gate_mode == LA_GATE_GAMMA:
+        g_keep = _gamma_host(gamma, H)
+        g_arg = ctypes.c_void_p(g_keep.data_ptr())
+    elif gate_mode == LA_GATE_DIAG:
+        g_arg = _dev_ptr(log_alpha, "log_alpha", torch.float32, (B, H, L, dk))
+    st = la_chunk_bwd(
+        desc, _dev_ptr(q, "q"), _dev_ptr(k, "k", q.dtype, (B, H, L, dk)),
+        _dev_ptr(v, "v", q.dtype, (B, H, L, dv)), _dev_ptr(dout, "dout", q.dtype, (B, H, L, dv)),
+        gate_mode, g_arg, _dev_ptr(S0, "S0", torch.float32, (B, H, dk, dv)),
+        _dev_ptr(dS_final, "dS_final", torch.float32, (B, H, dk, dv)),
+        _dev_ptr(dq, "dq"), _dev_ptr(dkk, "dk"), _dev_ptr(dvv, "dv"), _dev_ptr(dla, "dlog_alpha"),
+        _dev_ptr(dS0, "dS0"), _dev_ptr(workspace, "workspace"), ws_bytes,
+        _stream_ptr(stream, dev))
+    _check(st)
+    del g_keep
+    return {"dq": dq, "dk": dkk, "dv": dvv, "dlog_alpha": dla, "dS0": dS0}
+
+
+def chunk_bwd_workspace_bytes(B, H, L, dk, dv, dtype=LA_BF16, segments=0) -> int:
+    return la_chunk_bwd_workspace_bytes(make_desc(B, H, L, dk, dv, dtype, 0, False, segments))
 
 
 def chunk_fwd_workspace_bytes(B, H, L, dk, dv, chunk, dtype=LA_BF16,

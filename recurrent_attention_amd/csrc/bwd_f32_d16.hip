@@ -1,0 +1,6 @@
+// bwd_f32_d16.hip -- chunkwise backward kernels for d_k = d_v = 16, fp32 inputs.
+#include "bwd_kernel.h"
+
+namespace la {
+LA_DEFINE_BWD_LAUNCHER(launch_bwd_f32_d16, 16, false)
+}  // namespace la

@@ -1,0 +1,515 @@
+// bwd_kernel.h -- gradients of one chunk of the unified recurrence on gfx950
+// matrix cores, given the state at the chunk's start and the gradient of the
+// state at its end.
+//
+// With S = the state before the chunk, G = the gradient of the state after
+// it, chunk-local t, s, b_t = sum_{r<=t} log a_r (per key channel, natural
+// log) and B = b at the chunk's last token, the forward chunk ("Module 22:
+// Linear & Recurrent Attention", "The Three Faces of Retention", with the
+// diagonal gate of "The One Recurrence Behind Them All") is
+//   o_t = (q_t * e^{b_t})^T S + sum_{s<=t} [sum_i q_ti k_si e^{b_ti - b_si}] v_s
+// and its reverse-mode derivative, written per chunk, is
+//   dq_t = e^{b_t} * (S do_t) + sum_{s<=t} (do_t . v_s) k_s * e^{b_t - b_s}
+//   dk_s = e^{B - b_s} * (G v_s) + sum_{t>=s} (do_t . v_s) q_t * e^{b_t - b_s}
+//   dv_s = G^T (k_s * e^{B - b_s}) + sum_{t>=s} P[t][s] do_t
+//   d log a_t = sum_{u>=t} (q_u * dq_u - k_u * dk_u)      (features q, k)
+// where P[t][s] is the forward score with its decay.  The suffix sum that
+// reaches into later chunks, sum over all tokens after this chunk, equals
+// rowsum(G * S_next) with S_next the state after this chunk, so each chunk
+// finishes its own d log a without a pass over the sequence.
+//
+// Matrix-core mapping (C tokens, D = d_k = d_v; wave w owns channel block
+// [16w, 16w+16) of dq, dk and of dv):
+//   P   = Qh Kh^T and dP = dO V^T on the lower-triangular 16x16 tiles
+//         (Qh = q e^{b - r}, Kh = k e^{r - b}, r = b at the chunk middle),
+//         stored transposed, [s][t], with the causal mask (and gamma^(t-s));
+//   dQ^T = e^{r} S dO^T + Kh^T dP^T,   then * e^{b - r}
+//   dK^T = e^{B - r} G V^T + Qh^T dP,  then * e^{r - b}
+//   dV^T = (G^T * e^{B - r}) Kh^T + dO^T P
+// Every output lane holds 4 consecutive channels of one token, which are
+// the same elements the thread loaded and whose decay factors it computed.
+// Operands with the token index as the contraction are read from row-major
+// LDS tiles with the transposing LDS read of gfx950 (ds_read_b64_tr_b16).
+#pragma once
+
+#include "la_device.h"
+#include "la_internal.h"
+
+namespace la {
+
+typedef short bw_i16x4 __attribute__((ext_vector_type(4)));
+
+template <int D_, int C_, bool BF16_, int GATE_>
+struct BwdCfg {
+    static constexpr int D = D_, C = C_, GATE = GATE_;
+    static constexpr bool BF16 = BF16_;
+    using T = Elem<BF16>;
+    using E = typename T::E;
+    using Frag = typename T::Frag;
+    static constexpr int NW = D / 16;                  // waves: one channel block each
+    static constexpr int NT = 64 * NW;
+    static constexpr int TB = C / 16;                  // token blocks
+    static constexpr int KPL = T::KPL, MK = T::MK;
+    static constexpr int UE = 16 / (int)sizeof(E);     // elements per 16-byte unit
+    static constexpr int DU = D / UE, TU = C / UE;     // units per row
+    static constexpr int DMASK = (DU < 8 ? DU : 8) - 1;
+    static constexpr int TMASK = (TU < 8 ? TU : 8) - 1;
+    static constexpr int RW = 4 * (int)sizeof(E) / 4;  // words of a 4-channel run
+    static_assert(D % 16 == 0 && C % MK == 0 && C % 16 == 0, "tile shape");
+    static_assert(!BF16 || D % 32 == 0, "bf16 needs d >= 32");
+};
+
+template <class Cfg>
+struct BwdSmem {
+    using E = typename Cfg::E;
+    alignas(16) E qh[Cfg::C][Cfg::D];     // Qh   [t][swizzled i]
+    alignas(16) E kh[Cfg::C][Cfg::D];     // Kh   [s][swizzled i]
+    alignas(16) E dout[Cfg::C][Cfg::D];   // dO   [t][swizzled n]
+    alignas(16) E vv[Cfg::C][Cfg::D];     // V    [s][swizzled n]
+    alignas(16) E pt[Cfg::C][Cfg::C];     // P^T  [s][swizzled t]
+    alignas(16) E dpt[Cfg::C][Cfg::C];    // dP^T [s][swizzled t]
+    alignas(16) float ebr[Cfg::D];        // e^{B - r} per channel (DIAG)
+    float gpow[Cfg::C + 2];               // gamma^j
+};
+
+// Position of column `col` in row `row` of a tile with `mask`-wide swizzle.
+template <class Cfg, int MASK>
+__device__ __forceinline__ int bw_pos(int row, int col) {
+    const int u = col / Cfg::UE, e = col % Cfg::UE;
+    return ((u ^ (row & MASK)) * Cfg::UE) + e;
+}
+
+// Operand whose 16 rows/columns are tile columns c0..c0+15 and whose k-slots
+// are tile rows k0 + (slots of this lane): the transposed read of a
+// row-major tile.  bf16: two ds_read_b64_tr_b16 (4 rows each); fp32: one
+// element.
+template <class Cfg, int MASK>
+__device__ __forceinline__ typename Cfg::Frag tr_frag(const typename Cfg::E* tile, int ld, int k0,
+                                                      int c0, int lane) {
+    using Frag = typename Cfg::Frag;
+    const int g = lane >> 4;
+    if constexpr (Cfg::BF16) {
+        const int m = lane & 15;
+        const int rowa = k0 + 8 * g + (m >> 2), rowb = rowa + 4;
+        const int col = c0 + 4 * (m & 3);
+        const auto* pa = tile + rowa * ld + bw_pos<Cfg, MASK>(rowa, col);
+        const auto* pb = tile + rowb * ld + bw_pos<Cfg, MASK>(rowb, col);
+        const bw_i16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) bw_i16x4*)(pa));
+        const bw_i16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) bw_i16x4*)(pb));
+        const uint2 ua = __builtin_bit_cast(uint2, a), ub = __builtin_bit_cast(uint2, b);
+        return __builtin_bit_cast(Frag, make_uint4(ua.x, ua.y, ub.x, ub.y));
+    } else {
+        const int row = k0 + g, col = c0 + (lane & 15);
+        return tile[row * ld + bw_pos<Cfg, MASK>(row, col)];
+    }
+}
+
+// Operand whose 16 rows/columns are tile rows r0..r0+15 and whose k-slots
+// are tile columns k0 + (slots of this lane): a direct read.
+template <class Cfg, int MASK>
+__device__ __forceinline__ typename Cfg::Frag row_frag(const typename Cfg::E* tile, int ld, int r0,
+                                                       int k0, int lane) {
+    const int row = r0 + (lane & 15);
+    const int col = k0 + Cfg::KPL * (lane >> 4);
+    return Cfg::T::load(tile + row * ld + bw_pos<Cfg, MASK>(row, col));
+}
+
+// Operand from an fp32 state in memory: rows r0..r0+15 (lane & 15), k-slots
+// the row's elements k0 + (slots of this lane); times f[k] when SCALE, and
+// the unscaled values copied to raw when RAW.  Both are compile-time
+// choices: a uniform branch between matrix-core instructions and the
+// registers they use has been seen to lose the wait states they need.
+template <class Cfg, bool SCALE, bool RAW>
+__device__ __forceinline__ typename Cfg::Frag mem_frag(const float* M, int ld, int r0, int k0,
+                                                       int lane, const float* f, float* raw) {
+    const int row = r0 + (lane & 15);
+    const int col = k0 + Cfg::KPL * (lane >> 4);
+    const float* src = M + (size_t)row * ld + col;
+    if constexpr (Cfg::BF16) {
+        const float4 a = *reinterpret_cast<const float4*>(src);
+        const float4 b = *reinterpret_cast<const float4*>(src + 4);
+        float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if constexpr (RAW) raw[j] = x[j];
+            if constexpr (SCALE) x[j] *= f[col + j];
+        }
+        return Cfg::T::from8(x);
+    } else {
+        float x = *src;
+        if constexpr (RAW) raw[0] = x;
+        if constexpr (SCALE) x *= f[col];
+        return x;
+    }
+}
+
+// x of the lane CTRL selects within the 16-lane row (a DPP row shift), 0
+// where that lane lies outside the row.
+template <int CTRL>
+__device__ __forceinline__ float dpp_row(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+// Inclusive scan over the 16 lanes of a row (lanes r' <= r), or the suffix
+// (lanes r' >= r) when SUFFIX: row_shr:n reads lane r - n, row_shl:n lane r + n.
+template <bool SUFFIX>
+__device__ __forceinline__ float row_scan16(float x) {
+    constexpr int base = SUFFIX ? 0x100 : 0x110;
+    x += dpp_row<base + 1>(x);
+    x += dpp_row<base + 2>(x);
+    x += dpp_row<base + 4>(x);
+    x += dpp_row<base + 8>(x);
+    return x;
+}
+
+template <class Cfg, bool ELU1>
+__global__ __launch_bounds__(Cfg::NT) void bwd_kernel(const BwdParams p) {
+    constexpr int D = Cfg::D, C = Cfg::C, GATE = Cfg::GATE, TB = Cfg::TB, NW = Cfg::NW;
+    constexpr int MK = Cfg::MK, RW = Cfg::RW;
+    constexpr bool BF16 = Cfg::BF16;
+    constexpr int ES = (int)sizeof(typename Cfg::E);
+    constexpr int DM = Cfg::DMASK, TM = Cfg::TMASK;
+    using T = typename Cfg::T;
+    using E = typename Cfg::E;
+    using Frag = typename Cfg::Frag;
+    constexpr float kLog2e = 1.4426950408889634f;
+
+    __shared__ BwdSmem<Cfg> sm;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int r = lane & 15, g = lane >> 4;
+    const int c = blockIdx.x % p.nchunks;
+    const int bh = blockIdx.x / p.nchunks;
+    const int h = bh % p.H;
+    const int L = p.L;
+    const int t0 = c * C;
+    const int clen = min(C, L - t0);
+    const int ch0 = 16 * wave + 4 * g;    // this thread's 4 channels (keys and values)
+
+    const size_t rows0 = (size_t)bh * L;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(reinterpret_cast<const E*>(p.q) + rows0 * D, (uint32_t)L * D * ES);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(reinterpret_cast<const E*>(p.k) + rows0 * D, (uint32_t)L * D * ES);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(reinterpret_cast<const E*>(p.v) + rows0 * D, (uint32_t)L * D * ES);
+    const __amdgpu_buffer_rsrc_t rdo = make_rsrc(reinterpret_cast<const E*>(p.dout) + rows0 * D, (uint32_t)L * D * ES);
+    const __amdgpu_buffer_rsrc_t rla =
+        make_rsrc(GATE == LA_GATE_DIAG ? (const void*)(p.log_alpha + rows0 * D) : p.q,
+                  GATE == LA_GATE_DIAG ? (uint32_t)L * D * 4 : 0u);
+    const __amdgpu_buffer_rsrc_t rdq = make_rsrc(reinterpret_cast<E*>(p.dq) + rows0 * D, (uint32_t)L * D * ES);
+    const __amdgpu_buffer_rsrc_t rdk = make_rsrc(reinterpret_cast<E*>(p.dk) + rows0 * D, (uint32_t)L * D * ES);
+    const __amdgpu_buffer_rsrc_t rdv = make_rsrc(reinterpret_cast<E*>(p.dv) + rows0 * D, (uint32_t)L * D * ES);
+    const __amdgpu_buffer_rsrc_t rdla =
+        make_rsrc(GATE == LA_GATE_DIAG ? (void*)(p.dlog_alpha + rows0 * D) : p.dq,
+                  GATE == LA_GATE_DIAG ? (uint32_t)L * D * 4 : 0u);
+
+    // ---- loads: per owned token, one 4-channel run of q, k, v, dO (and gates)
+    Words<RW> qr[TB], kr[TB], vr[TB], dr[TB];
+    Words<4> lar[GATE == LA_GATE_DIAG ? TB : 1];
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+        const uint32_t row = (uint32_t)(t0 + 16 * tb + r);
+        const uint32_t off = (row * D + ch0) * ES;
+        qr[tb] = buf_load_words<RW>(rq, off);
+        kr[tb] = buf_load_words<RW>(rk, off);
+        vr[tb] = buf_load_words<RW>(rv, off);
+        dr[tb] = buf_load_words<RW>(rdo, off);
+        if constexpr (GATE == LA_GATE_DIAG) lar[tb] = buf_load_words<4>(rla, (row * D + ch0) * 4);
+    }
+    if constexpr (GATE == LA_GATE_GAMMA) {
+        const float l2g = p.log2_gamma[h];
+        for (int j = tid; j < C + 2; j += Cfg::NT) sm.gpow[j] = j == 0 ? 1.0f : exp2f((float)j * l2g);
+    }
+    // zero the score tiles (their upper triangles and any padding are read as zeros)
+    {
+        E* z0 = &sm.pt[0][0];
+        E* z1 = &sm.dpt[0][0];
+        for (int i = tid; i < C * C; i += Cfg::NT) {
+            z0[i] = E(0);
+            z1[i] = E(0);
+        }
+    }
+
+    // ---- features, gate prefix and factors of the owned elements
+    float qf[TB][4], kf[TB][4], fq[TB][4], fk[TB][4];
+    float er[4], ebr[4];   // e^{r}, e^{B - r} of the owned channels (DIAG)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) er[i] = ebr[i] = 1.f;
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+        const bool ok = 16 * tb + r < clen;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float qa = run_elem<BF16>(qr[tb], i), ka = run_elem<BF16>(kr[tb], i);
+            if constexpr (ELU1) {
+                qa = elu1f(qa);
+                ka = elu1f(ka);
+            }
+            qf[tb][i] = ok ? qa : 0.f;
+            kf[tb][i] = ok ? ka : 0.f;
+            fq[tb][i] = fk[tb][i] = 1.f;
+        }
+    }
+    if constexpr (GATE == LA_GATE_DIAG) {
+        // inclusive prefix over the chunk's tokens: within each 16-token block
+        // across the lanes of a row, then the earlier blocks' totals
+        float b[TB][4];
+        float carry[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float x = row_scan16<false>(run_elem<false>(lar[tb], i) * kLog2e);
+                b[tb][i] = x + carry[i];
+                carry[i] += lane_read(x, 16 * g + 15);
+            }
+        constexpr int tmid = C / 2 - 1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float ref = lane_read(b[tmid / 16][i], 16 * g + tmid % 16);
+            const float tot = carry[i];
+            er[i] = __builtin_amdgcn_exp2f(ref);
+            ebr[i] = __builtin_amdgcn_exp2f(tot - ref);
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb) {
+                const float d = b[tb][i] - ref;
+                fq[tb][i] = __builtin_amdgcn_exp2f(d);
+                fk[tb][i] = __builtin_amdgcn_exp2f(-d);
+            }
+        }
+        if (r == 0)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sm.ebr[ch0 + i] = ebr[i];
+    }
+
+    // ---- tiles: Qh, Kh, dO, V row-major (one 4-channel run per token)
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+        const int t = 16 * tb + r;
+        float x[4], y[4], vo[4], dd[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[i] = qf[tb][i] * fq[tb][i];
+            y[i] = kf[tb][i] * fk[tb][i];
+            vo[i] = run_elem<BF16>(vr[tb], i);
+            dd[i] = run_elem<BF16>(dr[tb], i);
+        }
+        const int pos = bw_pos<Cfg, DM>(t, ch0);
+        lds_store_words(&sm.qh[t][pos], pack_run<BF16, 4>(x));
+        lds_store_words(&sm.kh[t][pos], pack_run<BF16, 4>(y));
+        lds_store_words(&sm.vv[t][pos], pack_run<BF16, 4>(vo));
+        lds_store_words(&sm.dout[t][pos], pack_run<BF16, 4>(dd));
+    }
+    __syncthreads();
+
+    // ---- P and dP on the lower-triangular tiles, stored transposed [s][t]:
+    // the output lane holds four consecutive t of one s
+    {
+        int idx = 0;
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+            for (int sb = 0; sb <= tb; ++sb, ++idx) {
+                if (idx % NW != wave) continue;
+                f32x4_t ap = {0.f, 0.f, 0.f, 0.f}, ad = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < D / MK; ++kk) {
+                    ap = T::mma(row_frag<Cfg, DM>(&sm.qh[0][0], D, 16 * tb, kk * MK, lane),
+                                row_frag<Cfg, DM>(&sm.kh[0][0], D, 16 * sb, kk * MK, lane), ap);
+                    ad = T::mma(row_frag<Cfg, DM>(&sm.dout[0][0], D, 16 * tb, kk * MK, lane),
+                                row_frag<Cfg, DM>(&sm.vv[0][0], D, 16 * sb, kk * MK, lane), ad);
+                }
+                const int s = 16 * sb + r;
+                float xp[4], xd[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int t = 16 * tb + 4 * g + i;
+                    float m = t >= s ? 1.f : 0.f;
+                    if constexpr (GATE == LA_GATE_GAMMA) m = t >= s ? sm.gpow[t - s] : 0.f;
+                    xp[i] = ap[i] * m;
+                    xd[i] = ad[i] * m;
+                }
+                store_run<BF16, 4>(&sm.pt[s][bw_pos<Cfg, TM>(s, 16 * tb + 4 * g)], xp);
+                store_run<BF16, 4>(&sm.dpt[s][bw_pos<Cfg, TM>(s, 16 * tb + 4 * g)], xd);
+            }
+    }
+    __syncthreads();
+
+    const int nb = wave;   // channel block of this wave
+    const float* Sc = p.st_fwd + ((size_t)bh * (p.nchunks + 1) + c) * D * D;
+    const float* Sn = Sc + (size_t)D * D;                       // state after this chunk
+    const float* Gc = p.st_rows + ((size_t)bh * p.nchunks + c) * D * D;
+    const float* Gt = p.st_cols + ((size_t)bh * p.nchunks + c) * D * D;
+
+    // ---- dQ^T = e^{r} S dO^T + Kh^T dP^T, then * e^{b - r}
+    float dqf[TB][4];
+    {
+        f32x4_t acc[TB];
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) acc[tb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < D / MK; ++kk) {
+            const Frag a = mem_frag<Cfg, false, false>(Sc, D, 16 * nb, kk * MK, lane, nullptr, nullptr);
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb)
+                acc[tb] = T::mma(a, row_frag<Cfg, DM>(&sm.dout[0][0], D, 16 * tb, kk * MK, lane), acc[tb]);
+        }
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float f = er[i];
+                if constexpr (GATE == LA_GATE_GAMMA) f = sm.gpow[16 * tb + r + 1];
+                acc[tb][i] *= f;
+            }
+#pragma unroll
+            for (int kk = 0; kk <= (16 * tb + 15) / MK; ++kk)
+                acc[tb] = T::mma(tr_frag<Cfg, DM>(&sm.kh[0][0], D, kk * MK, 16 * nb, lane),
+                                 tr_frag<Cfg, TM>(&sm.dpt[0][0], C, kk * MK, 16 * tb, lane), acc[tb]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dqf[tb][i] = acc[tb][i] * fq[tb][i];
+        }
+    }
+    // ---- dK^T = e^{B - r} G V^T + Qh^T dP, then * e^{r - b}; with the
+    // chunk's carry rowsum(G * S_next) from the same rows of G
+    float dkf[TB][4];
+    float gsn = 0.f;   // partial rowsum(G * S_next) of row 16 nb + r
+    {
+        f32x4_t acc[TB];
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) acc[tb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < D / MK; ++kk) {
+            float raw[Cfg::KPL];
+            const Frag a = mem_frag<Cfg, false, GATE == LA_GATE_DIAG>(Gc, D, 16 * nb, kk * MK, lane, nullptr, raw);
+            if constexpr (GATE == LA_GATE_DIAG) {
+                const float* sn = Sn + (size_t)(16 * nb + r) * D + kk * MK + Cfg::KPL * g;
+#pragma unroll
+                for (int j = 0; j < Cfg::KPL; ++j) gsn += raw[j] * sn[j];
+            }
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb)
+                acc[tb] = T::mma(a, row_frag<Cfg, DM>(&sm.vv[0][0], D, 16 * tb, kk * MK, lane), acc[tb]);
+        }
+#pragma unroll
+        for (int sb = 0; sb < TB; ++sb) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float f = ebr[i];
+                if constexpr (GATE == LA_GATE_GAMMA) {
+                    const int s = 16 * sb + r;
+                    f = s < clen ? sm.gpow[clen - 1 - s] : 0.f;
+                }
+                acc[sb][i] *= f;
+            }
+#pragma unroll
+            for (int kk = (16 * sb) / MK; kk < C / MK; ++kk)
+                acc[sb] = T::mma(tr_frag<Cfg, DM>(&sm.qh[0][0], D, kk * MK, 16 * nb, lane),
+                                 row_frag<Cfg, TM>(&sm.dpt[0][0], C, 16 * sb, kk * MK, lane), acc[sb]);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dkf[sb][i] = acc[sb][i] * fk[sb][i];
+        }
+    }
+    // ---- dV^T = (G^T * e^{B - r}) Kh^T + dO^T P
+    {
+        f32x4_t acc[TB];
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) acc[tb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < D / MK; ++kk) {
+            const Frag a = mem_frag<Cfg, GATE == LA_GATE_DIAG, false>(Gt, D, 16 * nb, kk * MK, lane, sm.ebr, nullptr);
+#pragma unroll
+            for (int sb = 0; sb < TB; ++sb)
+                acc[sb] = T::mma(a, row_frag<Cfg, DM>(&sm.kh[0][0], D, 16 * sb, kk * MK, lane), acc[sb]);
+        }
+#pragma unroll
+        for (int sb = 0; sb < TB; ++sb) {
+            if constexpr (GATE == LA_GATE_GAMMA) {
+                const int s = 16 * sb + r;
+                const float f = s < clen ? sm.gpow[clen - 1 - s] : 0.f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[sb][i] *= f;
+            }
+#pragma unroll
+            for (int kk = (16 * sb) / MK; kk < C / MK; ++kk)
+                acc[sb] = T::mma(tr_frag<Cfg, DM>(&sm.dout[0][0], D, kk * MK, 16 * nb, lane),
+                                 row_frag<Cfg, TM>(&sm.pt[0][0], C, 16 * sb, kk * MK, lane), acc[sb]);
+            const uint32_t off = ((uint32_t)(t0 + 16 * sb + r) * D + ch0) * ES;
+            float x[4] = {acc[sb][0], acc[sb][1], acc[sb][2], acc[sb][3]};
+            buf_store_run4<BF16>(rdv, off, x);
+        }
+    }
+
+    // ---- dq, dk (chain rule through phi) and the gate gradient
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+        const uint32_t off = ((uint32_t)(t0 + 16 * tb + r) * D + ch0) * ES;
+        float xq[4], xk[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            xq[i] = dqf[tb][i];
+            xk[i] = dkf[tb][i];
+            if constexpr (ELU1) {
+                // phi' = 1 where phi = x + 1 > 1, else phi' = phi = e^x
+                xq[i] *= fminf(qf[tb][i], 1.f);
+                xk[i] *= fminf(kf[tb][i], 1.f);
+            }
+        }
+        buf_store_run4<BF16>(rdq, off, xq);
+        buf_store_run4<BF16>(rdk, off, xk);
+    }
+    if constexpr (GATE == LA_GATE_DIAG) {
+        // carry of this chunk per owned channel: rowsum over the four lanes
+        // holding row 16 nb + r, then read from the lane of each channel
+        float rs = gsn;
+        rs += lane_read(rs, lane ^ 16);
+        rs += lane_read(rs, lane ^ 32);
+        float cin[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cin[i] = lane_read(rs, 4 * g + i);
+        // suffix sums of db = q dq - k dk over the chunk's tokens: within each
+        // block across the lanes, then the later blocks' totals
+        float later[4] = {cin[0], cin[1], cin[2], cin[3]};
+#pragma unroll
+        for (int tb = TB - 1; tb >= 0; --tb) {
+            float out[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float db = qf[tb][i] * dqf[tb][i] - kf[tb][i] * dkf[tb][i];
+                const float x = row_scan16<true>(db);
+                out[i] = x + later[i];
+                later[i] += lane_read(x, 16 * g);
+            }
+            const uint32_t off = ((uint32_t)(t0 + 16 * tb + r) * D + ch0) * 4;
+            __builtin_amdgcn_raw_buffer_store_b128(
+                __builtin_bit_cast(u32x4_t, f32x4_t{out[0], out[1], out[2], out[3]}), rdla, off, 0, 0);
+        }
+    }
+}
+
+// Host-side dispatch over gate mode and feature map for one (d, dtype): one
+// workgroup per (b,h, chunk).
+template <int D, bool BF>
+hipError_t launch_bwd_dt(const BwdParams& p, int gate, hipStream_t s) {
+    constexpr int C = bwd_chunk(D, BF);
+    const dim3 grid((unsigned)(p.BH * p.nchunks));
+#define LA_BWD_LAUNCH(GG)                                                                       \
+    do {                                                                                        \
+        using Cfg = BwdCfg<D, C, BF, GG>;                                                       \
+        if (p.phi_elu1)                                                                         \
+            hipLaunchKernelGGL((bwd_kernel<Cfg, true>), grid, dim3(Cfg::NT), 0, s, p);          \
+        else                                                                                    \
+            hipLaunchKernelGGL((bwd_kernel<Cfg, false>), grid, dim3(Cfg::NT), 0, s, p);         \
+        return hipGetLastError();                                                               \
+    } while (0)
+    if (gate == LA_GATE_NONE) LA_BWD_LAUNCH(LA_GATE_NONE);
+    if (gate == LA_GATE_GAMMA) LA_BWD_LAUNCH(LA_GATE_GAMMA);
+    if (gate == LA_GATE_DIAG) LA_BWD_LAUNCH(LA_GATE_DIAG);
+    return hipErrorInvalidValue;
+#undef LA_BWD_LAUNCH
+}
+
+#define LA_DEFINE_BWD_LAUNCHER(NAME, D, BF) \
+    hipError_t NAME(const BwdParams& p, int gate, hipStream_t s) { return launch_bwd_dt<D, BF>(p, gate, s); }
+
+}  // namespace la

@@ -49,6 +49,15 @@
 // is the state pass: the same loop without q, P and outputs, started from a
 // zero state, writing the segment's end state, its decay product and its
 // normaliser part to the workspace.
+//
+// Two more state-only variants serve the backward pass:
+//  * STORE starts each segment from its entry state (after the segment
+//    scan) and writes the true state at every chunk boundary;
+//  * REV runs the recurrence of the state gradient, G_prev = A_c G +
+//    sum_t (phi(q_t) * e^{b_t}) do_t^T, which is the state update with k ->
+//    phi(q), v -> do, the key factor replaced by the query factor, the
+//    before/after factors swapped, and the chunks taken in reverse order
+//    (the caller passes q and do in the k and v slots).
 #pragma once
 
 #include <type_traits>
@@ -57,9 +66,6 @@
 #include "la_internal.h"
 
 namespace la {
-
-typedef __attribute__((ext_vector_type(2))) unsigned int u32x2_t;
-typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;
 
 // Channels per thread in the global -> register mapping: 4 where the chunk
 // still leaves every thread an even run of tokens, else 2.
@@ -179,40 +185,6 @@ __device__ __forceinline__ void store_pairs(typename Cfg::E* rowp, int row, int 
         *reinterpret_cast<V*>(rowp + tr_pos<Cfg>(row, s0 + q * PIECE)) = v;
     }
 }
-// A run of adjacent channels of one token as raw 32-bit words.
-template <int N>
-struct Words {
-    uint32_t w[N];
-};
-// Channel c of a run as a float (bf16 runs hold two channels per word).
-template <bool BF16, int N>
-__device__ __forceinline__ float run_elem(const Words<N>& x, int c) {
-    if constexpr (BF16) return (c & 1) ? bf16hi(x.w[c >> 1]) : bf16lo(x.w[c >> 1]);
-    else return __uint_as_float(x.w[c]);
-}
-// N floats as a run of the tile element type.
-template <bool BF16, int N>
-__device__ __forceinline__ Words<(BF16 ? N / 2 : N)> pack_run(const float* x) {
-    Words<(BF16 ? N / 2 : N)> o;
-    if constexpr (BF16) {
-#pragma unroll
-        for (int i = 0; i < N / 2; ++i) o.w[i] = pack_bf16(x[2 * i], x[2 * i + 1]);
-    } else {
-#pragma unroll
-        for (int i = 0; i < N; ++i) o.w[i] = __float_as_uint(x[i]);
-    }
-    return o;
-}
-template <int N>
-__device__ __forceinline__ void lds_store_words(void* p, const Words<N>& x) {
-    if constexpr (N == 1) *reinterpret_cast<uint32_t*>(p) = x.w[0];
-    else if constexpr (N == 2) *reinterpret_cast<uint2*>(p) = make_uint2(x.w[0], x.w[1]);
-    else *reinterpret_cast<uint4*>(p) = make_uint4(x.w[0], x.w[1], x.w[2], x.w[3]);
-}
-// Value of x in lane src of the wave (an LDS-crossbar permute).
-__device__ __forceinline__ float lane_read(float x, int src) {
-    return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(x)));
-}
 // Channel c of two runs at consecutive tokens as one token pair.
 template <class Cfg, int N>
 __device__ __forceinline__ typename Cfg::Pair token_pair(const Words<N>& a, const Words<N>& b, int c) {
@@ -232,24 +204,7 @@ __device__ __forceinline__ void scale_rows(f32x4_t (&acc)[Cfg::MB][Cfg::NB], con
     }
 }
 
-// Buffer descriptor over [base, base + bytes); reads past the end return 0
-// and writes past the end are dropped.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-template <int N>
-__device__ __forceinline__ Words<N> buf_load_words(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-    if constexpr (N == 1) {
-        return Words<1>{{__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0)}};
-    } else if constexpr (N == 2) {
-        return __builtin_bit_cast(Words<2>, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
-    } else {
-        static_assert(N == 4, "runs are 4, 8 or 16 bytes");
-        return __builtin_bit_cast(Words<4>, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-    }
-}
-
-template <class Cfg, bool ELU1>
+template <class Cfg, bool ELU1, bool REV = false, bool STORE = false>
 __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
     constexpr int DK = Cfg::DK, DV = Cfg::DV, C = Cfg::C, GATE = Cfg::GATE;
     constexpr int NB = Cfg::NB, MB = Cfg::MB, TB = Cfg::TB, NW = Cfg::NW;
@@ -270,8 +225,12 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     const int r = lane & 15, g = lane >> 4;
     const int P = p.P;
-    const int PS = SONLY ? P - 1 : P;  // the state pass skips the last segment
-    const int seg = blockIdx.x % PS;
+    static_assert(SONLY || (!REV && !STORE), "backward variants are state-only");
+    // the aggregate pass skips the segment it would end with (the last one,
+    // or the first one when reversed)
+    constexpr bool AGG = SONLY && !STORE;
+    const int PS = AGG ? P - 1 : P;
+    const int seg = blockIdx.x % PS + ((AGG && REV) ? 1 : 0);
     const int bh = blockIdx.x / PS;
     const int h = bh % p.H;
     const int L = p.L;
@@ -328,7 +287,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
     const size_t SS = (size_t)DK * DV;
     const float* Sin = nullptr;
     const float* zin = nullptr;
-    if constexpr (!SONLY) {
+    if constexpr (!AGG) {
         if (P > 1) {
             Sin = p.ws_S + ((size_t)bh * P + seg) * SS;
             zin = p.ws_z + ((size_t)bh * P + seg) * DK;
@@ -386,8 +345,33 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
     };
     constexpr float kLog2e = 1.4426950408889634f;
 
-    // one chunk: consumes rg, then refills it with chunk c + PD
-    auto step = [&](const int c, ChunkRegs& rg) {
+    // chunk handled at iteration ci (reverse order for the gradient pass)
+    auto cof = [&](int ci) { return REV ? c_begin + c_end - 1 - ci : ci; };
+    // the true state in the accumulators, into boundary slot `slot`: rows
+    // times the after-factor still pending (diagonal gate), row-major and,
+    // when asked, transposed
+    auto store_state = [&](int slot) {
+        float* rows = p.st_rows + ((size_t)bh * p.st_slots + slot) * SS;
+        float* cols = p.st_cols ? p.st_cols + ((size_t)bh * p.st_slots + slot) * SS : nullptr;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+            f32x4_t f = {1.f, 1.f, 1.f, 1.f};
+            if constexpr (GATE == LA_GATE_DIAG) f = *reinterpret_cast<const f32x4_t*>(&sm.post[16 * mb + 4 * g]);
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const f32x4_t x = accS[mb][nb] * f;
+                const int col = colbase + 16 * nb + r;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) rows[(size_t)(16 * mb + 4 * g + i) * DV + col] = x[i];
+                if (cols) *reinterpret_cast<f32x4_t*>(&cols[(size_t)col * DK + 16 * mb + 4 * g]) = x;
+            }
+        }
+    };
+
+    // one chunk (iteration ci): consumes rg, then refills it with the chunk
+    // PD iterations ahead
+    auto step = [&](const int ci, ChunkRegs& rg) {
+        const int c = cof(ci);
         const int t0 = c * C;
         const int clen = min(C, L - t0);
 
@@ -489,7 +473,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
                 const bool ok = t < clen;
                 float qv[CW], kv[CW];
                 float ftok = 1.f;
-                if constexpr (GATE == LA_GATE_GAMMA) ftok = ok ? sm.gpow[clen - 1 - t] : 0.f;
+                if constexpr (GATE == LA_GATE_GAMMA) ftok = ok ? sm.gpow[REV ? t + 1 : clen - 1 - t] : 0.f;
 #pragma unroll
                 for (int i = 0; i < CW; ++i) {
                     float ka = run_elem<BF16>(rg.k[j], i);
@@ -501,7 +485,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
                         const float d = bcur[i] - gref[i];
                         fq = __builtin_amdgcn_exp2f(d);
                         fk = __builtin_amdgcn_exp2f(-d);
-                        ft = fk;
+                        ft = REV ? fq : fk;
                     }
                     if constexpr (!SONLY) {
                         float qa = run_elem<BF16>(qreg[j], i);
@@ -542,8 +526,8 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
                     for (int i = 0; i < CW; ++i) {
                         const int row = CW * kcp + i;
                         sm.segsum[row] += gtot[i];
-                        pr[i] = __builtin_amdgcn_exp2f(gref[i]);
-                        po[i] = __builtin_amdgcn_exp2f(gtot[i] - gref[i]);
+                        pr[i] = __builtin_amdgcn_exp2f(REV ? gtot[i] - gref[i] : gref[i]);
+                        po[i] = __builtin_amdgcn_exp2f(REV ? gref[i] : gtot[i] - gref[i]);
                         sc[i] = sm.post[row] * pr[i];
                     }
                 } else if constexpr (GATE == LA_GATE_GAMMA) {
@@ -557,8 +541,8 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
         }
 
         // ---- refill the registers: q with chunk c + 1, this set with c + PD
-        if (c + 1 < c_end) load_q(c + 1);
-        if (c + Cfg::PD < c_end) load_chunk(c + Cfg::PD, rg);
+        if (ci + 1 < c_end) load_q(cof(ci + 1));
+        if (ci + Cfg::PD < c_end) load_chunk(cof(ci + Cfg::PD), rg);
         __syncthreads();
 
         // ---- op1: P^T = Kh Qh^T on the lower-triangular tiles; each lane
@@ -721,21 +705,36 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
                 for (int nb = 0; nb < NB; ++nb) accS[mb][nb] = T::mma(a, vf[kk][nb], accS[mb][nb]);
             }
         }
+        // ---- the state at the next chunk boundary (the entry state of the
+        // next segment is stored by that segment's workgroup)
+        if constexpr (STORE) {
+            const int nxt = REV ? c - 1 : c + 1;
+            const bool own = REV ? (nxt >= c_begin) : (nxt < c_end || seg == P - 1);
+            if (own) store_state(nxt);
+        }
     };
+    if constexpr (STORE) {
+        // the segment's entry state is the first boundary it owns (the
+        // diagonal after-factor of a previous chunk is 1 here)
+        if (c_begin < c_end) {
+            __syncthreads();   // sm.post set up
+            store_state(REV ? c_end - 1 : c_begin);
+        }
+    }
     {
-        if (c_begin < c_end) load_q(c_begin);
+        if (c_begin < c_end) load_q(cof(c_begin));
         if constexpr (Cfg::PD == 2) {
             ChunkRegs ra, rb;
-            if (c_begin < c_end) load_chunk(c_begin, ra);
-            if (c_begin + 1 < c_end) load_chunk(c_begin + 1, rb);
-            for (int c = c_begin; c < c_end; c += 2) {
-                step(c, ra);
-                if (c + 1 < c_end) step(c + 1, rb);
+            if (c_begin < c_end) load_chunk(cof(c_begin), ra);
+            if (c_begin + 1 < c_end) load_chunk(cof(c_begin + 1), rb);
+            for (int ci = c_begin; ci < c_end; ci += 2) {
+                step(ci, ra);
+                if (ci + 1 < c_end) step(ci + 1, rb);
             }
         } else {
             ChunkRegs ra;
-            if (c_begin < c_end) load_chunk(c_begin, ra);
-            for (int c = c_begin; c < c_end; ++c) step(c, ra);
+            if (c_begin < c_end) load_chunk(cof(c_begin), ra);
+            for (int ci = c_begin; ci < c_end; ++ci) step(ci, ra);
         }
     }
     // DIAG: the last chunk's after-factor
@@ -747,7 +746,14 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
     // ---- epilogue
     float* Sout;
     float* zout;
-    if constexpr (SONLY) {
+    if constexpr (STORE) {
+        // the state after the whole segment: S_final (forward) or the
+        // gradient of the initial state (reverse), from the segment that
+        // ends the sequence
+        if (seg != (REV ? 0 : P - 1)) return;
+        Sout = p.S_final ? p.S_final + (size_t)bh * SS : nullptr;
+        zout = nullptr;
+    } else if constexpr (SONLY) {
         Sout = p.ws_S + ((size_t)bh * P + seg) * SS;
         zout = p.ws_z + ((size_t)bh * P + seg) * DK;
         float* aout = p.ws_a + ((size_t)bh * P + seg) * DK;
@@ -778,7 +784,10 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
 // Only the multiply-adds are sequential: each thread reads a batch of its
 // segment slots and factors before running the chain over them, so the
 // memory latency is paid once per batch rather than once per segment.
-template <int DK, int DV>
+// With REV the scan runs from the last segment to the first: slot P-1
+// starts from the initial value (S0 holds it) and G_in[j] = a_{j+1} *
+// G_in[j+1] + U_{j+1}, the composition of the gradient recurrence.
+template <int DK, int DV, bool REV = false>
 __global__ __launch_bounds__(256) void state_scan_kernel(const ChunkParams p) {
     constexpr int N4 = DK * DV / 4;
     constexpr int NBX = (N4 + 255) / 256;
@@ -794,26 +803,28 @@ __global__ __launch_bounds__(256) void state_scan_kernel(const ChunkParams p) {
                         : make_float4(0.f, 0.f, 0.f, 0.f);
         float4* slots = reinterpret_cast<float4*>(p.ws_S + (size_t)bh * P * SS) + e4;
         const float* as = p.ws_a + (size_t)bh * P * DK + row;
+        // position k of the chain reads and writes slot sj(k)
+        auto sj = [&](int k) { return REV ? P - 1 - k : k; };
         for (int j0 = 0; j0 < P - 1; j0 += NBATCH) {
             float4 u[NBATCH];
             float a[NBATCH];
 #pragma unroll
             for (int jj = 0; jj < NBATCH; ++jj) {
                 if (j0 + jj < P - 1) {
-                    u[jj] = slots[(size_t)(j0 + jj) * (SS / 4)];
-                    a[jj] = as[(size_t)(j0 + jj) * DK];
+                    u[jj] = slots[(size_t)sj(j0 + jj) * (SS / 4)];
+                    a[jj] = as[(size_t)sj(j0 + jj) * DK];
                 }
             }
 #pragma unroll
             for (int jj = 0; jj < NBATCH; ++jj) {
                 if (j0 + jj < P - 1) {
-                    slots[(size_t)(j0 + jj) * (SS / 4)] = x;
+                    slots[(size_t)sj(j0 + jj) * (SS / 4)] = x;
                     x = make_float4(a[jj] * x.x + u[jj].x, a[jj] * x.y + u[jj].y,
                                     a[jj] * x.z + u[jj].z, a[jj] * x.w + u[jj].w);
                 }
             }
         }
-        slots[(size_t)(P - 1) * (SS / 4)] = x;
+        slots[(size_t)sj(P - 1) * (SS / 4)] = x;
     }
     if (p.normalize && bx == 0 && threadIdx.x < DK) {
         const int i = threadIdx.x;
@@ -848,44 +859,51 @@ struct ChunkWaves {
     static constexpr int value = D >= 128 ? 8 : (D / 16 < 4 ? D / 16 : 4);
 };
 
-// Host-side dispatch over chunk length and gate mode for one (d, dtype).
+// Host-side dispatch over chunk length, gate mode and pass for one (d, dtype).
+// The backward passes exist for the backward's chunk length only.
 template <int D, bool BF, int NWV = ChunkWaves<D>::value>
-hipError_t launch_chunk_dt(const ChunkParams& p, int chunk, int gate, bool sonly, hipStream_t s,
+hipError_t launch_chunk_dt(const ChunkParams& p, int chunk, int gate, int pass, hipStream_t s,
                            int nblocks) {
-#define LA_CHUNK_LAUNCH(CC, GG, SO)                                                      \
-    do {                                                                                 \
-        using Cfg = ChunkCfg<D, D, CC, BF, GG, SO, NWV>;                                 \
-        if (p.phi_elu1)                                                                  \
-            hipLaunchKernelGGL((chunk_kernel<Cfg, true>), dim3(nblocks), dim3(Cfg::NT), 0, s, p); \
-        else                                                                             \
-            hipLaunchKernelGGL((chunk_kernel<Cfg, false>), dim3(nblocks), dim3(Cfg::NT), 0, s, p); \
-        return hipGetLastError();                                                        \
+#define LA_CHUNK_LAUNCH(CC, GG, SO, RV, ST)                                                \
+    do {                                                                                   \
+        using Cfg = ChunkCfg<D, D, CC, BF, GG, SO, NWV>;                                   \
+        if (p.phi_elu1)                                                                    \
+            hipLaunchKernelGGL((chunk_kernel<Cfg, true, RV, ST>), dim3(nblocks), dim3(Cfg::NT), 0, s, p); \
+        else                                                                               \
+            hipLaunchKernelGGL((chunk_kernel<Cfg, false, RV, ST>), dim3(nblocks), dim3(Cfg::NT), 0, s, p); \
+        return hipGetLastError();                                                          \
     } while (0)
-#define LA_CHUNK_GATES(CC, SO)                                   \
-    do {                                                         \
-        if (gate == LA_GATE_NONE) LA_CHUNK_LAUNCH(CC, 0, SO);    \
-        if (gate == LA_GATE_GAMMA) LA_CHUNK_LAUNCH(CC, 1, SO);   \
-        LA_CHUNK_LAUNCH(CC, 2, SO);                              \
+#define LA_CHUNK_GATES(CC, SO, RV, ST)                                   \
+    do {                                                                 \
+        if (gate == LA_GATE_NONE) LA_CHUNK_LAUNCH(CC, 0, SO, RV, ST);    \
+        if (gate == LA_GATE_GAMMA) LA_CHUNK_LAUNCH(CC, 1, SO, RV, ST);   \
+        LA_CHUNK_LAUNCH(CC, 2, SO, RV, ST);                              \
     } while (0)
-#define LA_CHUNK_SONLY(CC)                             \
-    do {                                               \
-        if (sonly) LA_CHUNK_GATES(CC, true);           \
-        LA_CHUNK_GATES(CC, false);                     \
+#define LA_CHUNK_FWD(CC)                                                 \
+    do {                                                                 \
+        if (pass == PASS_STATE) LA_CHUNK_GATES(CC, true, false, false);  \
+        if (pass == PASS_MAIN) LA_CHUNK_GATES(CC, false, false, false);  \
     } while (0)
-    if (chunk == 16) LA_CHUNK_SONLY(16);
-    if (chunk == 32) LA_CHUNK_SONLY(32);
-    if (chunk == 64) LA_CHUNK_SONLY(64);
+    constexpr int CB = bwd_chunk(D, BF);
+    if (chunk == CB) {
+        if (pass == PASS_STATE_REV) LA_CHUNK_GATES(CB, true, true, false);
+        if (pass == PASS_STORE) LA_CHUNK_GATES(CB, true, false, true);
+        if (pass == PASS_STORE_REV) LA_CHUNK_GATES(CB, true, true, true);
+    }
+    if (chunk == 16) LA_CHUNK_FWD(16);
+    if (chunk == 32) LA_CHUNK_FWD(32);
+    if (chunk == 64) LA_CHUNK_FWD(64);
     return hipErrorInvalidValue;
-#undef LA_CHUNK_SONLY
+#undef LA_CHUNK_FWD
 #undef LA_CHUNK_GATES
 #undef LA_CHUNK_LAUNCH
 }
 
 // One explicit (d, dtype) instantiation per translation unit.
 #define LA_DEFINE_CHUNK_LAUNCHER(NAME, D, BF)                                                      \
-    hipError_t NAME(const ChunkParams& p, int chunk, int gate, bool sonly, hipStream_t s,          \
+    hipError_t NAME(const ChunkParams& p, int chunk, int gate, int pass, hipStream_t s,            \
                     int nblocks) {                                                                 \
-        return launch_chunk_dt<D, BF>(p, chunk, gate, sonly, s, nblocks);                          \
+        return launch_chunk_dt<D, BF>(p, chunk, gate, pass, s, nblocks);                           \
     }
 
 }  // namespace la

@@ -118,7 +118,8 @@ bool g_prof_on = false;
 std::vector<ProfRec> g_prof;
 std::vector<hipEvent_t> g_event_pool;
 
-const char* kKernelNames[la::K_COUNT] = {"chunk_main", "chunk_state", "state_scan", "decode"};
+const char* kKernelNames[la::K_COUNT] = {"chunk_main", "chunk_state", "state_scan", "decode",
+                                         "chunk_store", "chunk_bwd"};
 
 hipEvent_t take_event() {
     if (!g_event_pool.empty()) {
@@ -149,6 +150,47 @@ hipError_t timed_launch(int kernel, hipStream_t s, F&& launch) {
     if (e != hipSuccess) return e;
     g_prof.push_back(rec);
     return hipSuccess;
+}
+
+hipError_t chunk_launch(const la_desc* d, const la::ChunkParams& p, int chunk, int gate, int pass,
+                        hipStream_t s, int nblocks) {
+    const bool bf16 = d->dtype == LA_BF16;
+    switch (d->dk) {
+        case 16: return la::launch_chunk_f32_d16(p, chunk, gate, pass, s, nblocks);
+        case 32: return bf16 ? la::launch_chunk_bf16_d32(p, chunk, gate, pass, s, nblocks)
+                             : la::launch_chunk_f32_d32(p, chunk, gate, pass, s, nblocks);
+        case 64: return bf16 ? la::launch_chunk_bf16_d64(p, chunk, gate, pass, s, nblocks)
+                             : la::launch_chunk_f32_d64(p, chunk, gate, pass, s, nblocks);
+        default: return bf16 ? la::launch_chunk_bf16_d128(p, chunk, gate, pass, s, nblocks)
+                             : la::launch_chunk_f32_d128(p, chunk, gate, pass, s, nblocks);
+    }
+}
+
+hipError_t bwd_launch(const la_desc* d, const la::BwdParams& p, int gate, hipStream_t s) {
+    const bool bf16 = d->dtype == LA_BF16;
+    switch (d->dk) {
+        case 16: return la::launch_bwd_f32_d16(p, gate, s);
+        case 32: return bf16 ? la::launch_bwd_bf16_d32(p, gate, s) : la::launch_bwd_f32_d32(p, gate, s);
+        case 64: return bf16 ? la::launch_bwd_bf16_d64(p, gate, s) : la::launch_bwd_f32_d64(p, gate, s);
+        default: return bf16 ? la::launch_bwd_bf16_d128(p, gate, s) : la::launch_bwd_f32_d128(p, gate, s);
+    }
+}
+
+// Backward workspace, in floats: the state before every chunk and the final
+// state, the state gradient after every chunk (row-major and transposed),
+// then the segment slots of the state passes.
+struct BwdLayout {
+    size_t fwd, rows, cols, seg, total;
+};
+BwdLayout bwd_layout(const la_desc* d, const Plan& pl) {
+    const size_t bh = (size_t)d->B * d->H, dd = (size_t)d->dk * d->dv;
+    BwdLayout w;
+    w.fwd = 0;
+    w.rows = w.fwd + bh * (pl.nchunks + 1) * dd;
+    w.cols = w.rows + bh * pl.nchunks * dd;
+    w.seg = w.cols + bh * pl.nchunks * dd;
+    w.total = w.seg + (pl.P > 1 ? bh * pl.P * (dd + 2 * (size_t)d->dk) : 0);
+    return w;
 }
 
 la_status hip_fail(hipError_t e, const char* what) {
@@ -243,30 +285,157 @@ la_status la_chunk_fwd(const la_desc* d, const void* q, const void* k, const voi
         p.ws_z = p.ws_a + slots * d->dk;
     }
 
-    const bool bf16 = d->dtype == LA_BF16;
-    auto chunk_launch = [&](bool sonly, int nblocks) -> hipError_t {
-        hipStream_t s = static_cast<hipStream_t>(stream);
-        switch (d->dk) {
-            case 16: return la::launch_chunk_f32_d16(p, chunk, gate_mode, sonly, s, nblocks);
-            case 32: return bf16 ? la::launch_chunk_bf16_d32(p, chunk, gate_mode, sonly, s, nblocks)
-                                 : la::launch_chunk_f32_d32(p, chunk, gate_mode, sonly, s, nblocks);
-            case 64: return bf16 ? la::launch_chunk_bf16_d64(p, chunk, gate_mode, sonly, s, nblocks)
-                                 : la::launch_chunk_f32_d64(p, chunk, gate_mode, sonly, s, nblocks);
-            default: return bf16 ? la::launch_chunk_bf16_d128(p, chunk, gate_mode, sonly, s, nblocks)
-                                 : la::launch_chunk_f32_d128(p, chunk, gate_mode, sonly, s, nblocks);
-        }
-    };
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
     if (pl.P > 1) {
         // state pass over every segment but the last, then the segment scan
-        e = timed_launch(la::K_CHUNK_STATE, s, [&] { return chunk_launch(true, BH * (pl.P - 1)); });
+        e = timed_launch(la::K_CHUNK_STATE, s, [&] {
+            return chunk_launch(d, p, chunk, gate_mode, la::PASS_STATE, s, BH * (pl.P - 1));
+        });
         if (e != hipSuccess) return hip_fail(e, "state pass launch");
-        e = timed_launch(la::K_STATE_SCAN, s, [&] { return la::launch_state_scan(p, d->dk, s); });
+        e = timed_launch(la::K_STATE_SCAN, s, [&] { return la::launch_state_scan(p, d->dk, false, s); });
         if (e != hipSuccess) return hip_fail(e, "segment scan launch");
     }
-    e = timed_launch(la::K_CHUNK_MAIN, s, [&] { return chunk_launch(false, BH * pl.P); });
+    e = timed_launch(la::K_CHUNK_MAIN, s, [&] {
+        return chunk_launch(d, p, chunk, gate_mode, la::PASS_MAIN, s, BH * pl.P);
+    });
     if (e != hipSuccess) return hip_fail(e, "main pass launch");
+    return LA_OK;
+}
+
+size_t la_chunk_bwd_workspace_bytes(const la_desc* d) {
+    if (check_desc(d) != LA_OK) return 0;
+    const int chunk = la::bwd_chunk(d->dk, d->dtype == LA_BF16);
+    return bwd_layout(d, make_plan(d, chunk)).total * sizeof(float);
+}
+
+int la_chunk_bwd_chunk(const la_desc* d) {
+    if (check_desc(d) != LA_OK) return 0;
+    return la::bwd_chunk(d->dk, d->dtype == LA_BF16);
+}
+
+la_status la_chunk_bwd(const la_desc* d, const void* q, const void* k, const void* v,
+                       const void* dout, int gate_mode, const float* gamma_or_log_alpha,
+                       const float* S0, const float* dS_final, void* dq, void* dk, void* dv,
+                       float* dlog_alpha, float* dS0, void* workspace, size_t ws_bytes,
+                       void* stream) {
+    g_errmsg[0] = '\0';
+    la_status st = check_desc(d);
+    if (st != LA_OK) return st;
+    if (d->normalize) return fail(LA_ERR_UNSUPPORTED, "the backward has no normaliser (normalize=1)");
+    if (!q || !k || !v || !dout || !dq || !dk || !dv)
+        return fail(LA_ERR_INVALID, "q, k, v, dout, dq, dk and dv must be non-NULL");
+    if (gate_mode == LA_GATE_DIAG && !dlog_alpha)
+        return fail(LA_ERR_INVALID, "DIAG gate needs dlog_alpha");
+    if (gate_mode != LA_GATE_DIAG && dlog_alpha)
+        return fail(LA_ERR_INVALID, "dlog_alpha given without the DIAG gate");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) || !aligned16(dq) ||
+        !aligned16(dk) || !aligned16(dv) || (dlog_alpha && !aligned16(dlog_alpha)) ||
+        (S0 && !aligned16(S0)) || (dS_final && !aligned16(dS_final)) || (dS0 && !aligned16(dS0)))
+        return fail(LA_ERR_INVALID, "device pointers must be 16-byte aligned");
+    const int chunk = la::bwd_chunk(d->dk, d->dtype == LA_BF16);
+    if (d->segments > 0 && d->segments > (d->L + chunk - 1) / chunk)
+        return fail(LA_ERR_INVALID, "segments=%d exceeds the %d chunks", d->segments,
+                    (d->L + chunk - 1) / chunk);
+
+    la::ChunkParams p;
+    std::memset(&p, 0, sizeof p);
+    st = check_gate(d, gate_mode, gamma_or_log_alpha, true, p.log2_gamma, nullptr);
+    if (st != LA_OK) return st;
+    const Plan pl = make_plan(d, chunk);
+    const BwdLayout w = bwd_layout(d, pl);
+    if (!workspace) return fail(LA_ERR_INVALID, "workspace of %zu bytes is required", w.total * sizeof(float));
+    if (!aligned16(workspace)) return fail(LA_ERR_INVALID, "workspace must be 16-byte aligned");
+    if (ws_bytes < w.total * sizeof(float))
+        return fail(LA_ERR_INVALID, "workspace has %zu bytes, %zu required", ws_bytes,
+                    w.total * sizeof(float));
+
+    const int BH = d->B * d->H;
+    float* ws = static_cast<float*>(workspace);
+    p.log_alpha = gate_mode == LA_GATE_DIAG ? gamma_or_log_alpha : nullptr;
+    p.L = d->L;
+    p.H = d->H;
+    p.BH = BH;
+    p.P = pl.P;
+    p.cps = pl.cps;
+    p.nchunks = pl.nchunks;
+    p.phi_elu1 = d->phi == LA_PHI_ELU1;
+    if (pl.P > 1) {
+        const size_t slots = (size_t)BH * pl.P;
+        p.ws_S = ws + w.seg;
+        p.ws_a = p.ws_S + slots * d->dk * d->dv;
+        p.ws_z = p.ws_a + slots * d->dk;
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+
+    // the states before every chunk: the forward state recurrence
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.S0 = S0;
+    p.S_final = nullptr;
+    p.st_rows = ws + w.fwd;
+    p.st_cols = nullptr;
+    p.st_slots = pl.nchunks + 1;
+    if (pl.P > 1) {
+        e = timed_launch(la::K_CHUNK_STATE, s, [&] {
+            return chunk_launch(d, p, chunk, gate_mode, la::PASS_STATE, s, BH * (pl.P - 1));
+        });
+        if (e != hipSuccess) return hip_fail(e, "state pass launch");
+        e = timed_launch(la::K_STATE_SCAN, s, [&] { return la::launch_state_scan(p, d->dk, false, s); });
+        if (e != hipSuccess) return hip_fail(e, "segment scan launch");
+    }
+    e = timed_launch(la::K_CHUNK_STORE, s, [&] {
+        return chunk_launch(d, p, chunk, gate_mode, la::PASS_STORE, s, BH * pl.P);
+    });
+    if (e != hipSuccess) return hip_fail(e, "state store launch");
+
+    // the state gradient after every chunk: the same recurrence run from the
+    // end with phi(q) and dout in the places of phi(k) and v
+    p.k = q;
+    p.v = dout;
+    p.S0 = dS_final;
+    p.S_final = dS0;
+    p.st_rows = ws + w.rows;
+    p.st_cols = ws + w.cols;
+    p.st_slots = pl.nchunks;
+    if (pl.P > 1) {
+        e = timed_launch(la::K_CHUNK_STATE, s, [&] {
+            return chunk_launch(d, p, chunk, gate_mode, la::PASS_STATE_REV, s, BH * (pl.P - 1));
+        });
+        if (e != hipSuccess) return hip_fail(e, "reverse state pass launch");
+        e = timed_launch(la::K_STATE_SCAN, s, [&] { return la::launch_state_scan(p, d->dk, true, s); });
+        if (e != hipSuccess) return hip_fail(e, "reverse segment scan launch");
+    }
+    e = timed_launch(la::K_CHUNK_STORE, s, [&] {
+        return chunk_launch(d, p, chunk, gate_mode, la::PASS_STORE_REV, s, BH * pl.P);
+    });
+    if (e != hipSuccess) return hip_fail(e, "gradient store launch");
+
+    // per-chunk gradients
+    la::BwdParams b;
+    std::memset(&b, 0, sizeof b);
+    b.q = q;
+    b.k = k;
+    b.v = v;
+    b.dout = dout;
+    b.log_alpha = p.log_alpha;
+    b.st_fwd = ws + w.fwd;
+    b.st_rows = ws + w.rows;
+    b.st_cols = ws + w.cols;
+    b.dq = dq;
+    b.dk = dk;
+    b.dv = dv;
+    b.dlog_alpha = dlog_alpha;
+    b.L = d->L;
+    b.H = d->H;
+    b.BH = BH;
+    b.nchunks = pl.nchunks;
+    b.phi_elu1 = p.phi_elu1;
+    std::memcpy(b.log2_gamma, p.log2_gamma, sizeof b.log2_gamma);
+    e = timed_launch(la::K_BWD, s, [&] { return bwd_launch(d, b, gate_mode, s); });
+    if (e != hipSuccess) return hip_fail(e, "backward launch");
     return LA_OK;
 }
 

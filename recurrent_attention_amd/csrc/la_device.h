@@ -22,6 +22,8 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 typedef __attribute__((ext_vector_type(2))) float f32x2_t;
 typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2_t;
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4_t;
 
 // ---------------------------------------------------------------- bf16 bits
 __device__ __forceinline__ float bf16lo(uint32_t p) { return __uint_as_float(p << 16); }
@@ -127,6 +129,70 @@ __device__ __forceinline__ void store_run(typename Elem<BF16>::E* dst, const flo
 #pragma unroll
             for (int j = 0; j < N; ++j) dst[j] = x[j];
         }
+    }
+}
+
+// A run of adjacent channels of one token as raw 32-bit words.
+template <int N>
+struct Words {
+    uint32_t w[N];
+};
+// Channel c of a run as a float (bf16 runs hold two channels per word).
+template <bool BF16, int N>
+__device__ __forceinline__ float run_elem(const Words<N>& x, int c) {
+    if constexpr (BF16) return (c & 1) ? bf16hi(x.w[c >> 1]) : bf16lo(x.w[c >> 1]);
+    else return __uint_as_float(x.w[c]);
+}
+// N floats as a run of the tile element type.
+template <bool BF16, int N>
+__device__ __forceinline__ Words<(BF16 ? N / 2 : N)> pack_run(const float* x) {
+    Words<(BF16 ? N / 2 : N)> o;
+    if constexpr (BF16) {
+#pragma unroll
+        for (int i = 0; i < N / 2; ++i) o.w[i] = pack_bf16(x[2 * i], x[2 * i + 1]);
+    } else {
+#pragma unroll
+        for (int i = 0; i < N; ++i) o.w[i] = __float_as_uint(x[i]);
+    }
+    return o;
+}
+template <int N>
+__device__ __forceinline__ void lds_store_words(void* p, const Words<N>& x) {
+    if constexpr (N == 1) *reinterpret_cast<uint32_t*>(p) = x.w[0];
+    else if constexpr (N == 2) *reinterpret_cast<uint2*>(p) = make_uint2(x.w[0], x.w[1]);
+    else *reinterpret_cast<uint4*>(p) = make_uint4(x.w[0], x.w[1], x.w[2], x.w[3]);
+}
+// Value of x in lane src of the wave (an LDS-crossbar permute).
+__device__ __forceinline__ float lane_read(float x, int src) {
+    return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(x)));
+}
+// Buffer descriptor over [base, base + bytes); reads past the end return 0
+// and writes past the end are dropped.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+template <int N>
+__device__ __forceinline__ Words<N> buf_load_words(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    if constexpr (N == 1) {
+        return Words<1>{{__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0)}};
+    } else if constexpr (N == 2) {
+        return __builtin_bit_cast(Words<2>, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+    } else {
+        static_assert(N == 4, "runs are 4, 8 or 16 bytes");
+        return __builtin_bit_cast(Words<4>, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+    }
+}
+
+// A run of 4 channels of one token (fp32 values) written to global memory as
+// the element type through a buffer descriptor.
+template <bool BF16>
+__device__ __forceinline__ void buf_store_run4(__amdgpu_buffer_rsrc_t r, uint32_t off, const float* x) {
+    if constexpr (BF16) {
+        const u32x2_t w = {pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3])};
+        __builtin_amdgcn_raw_buffer_store_b64(w, r, off, 0, 0);
+    } else {
+        const f32x4_t v = {x[0], x[1], x[2], x[3]};
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, v), r, off, 0, 0);
     }
 }
 

@@ -25,6 +25,9 @@ struct ChunkParams {
     float* ws_S;            // [BH, P, dk*dv] segment states (P > 1)
     float* ws_a;            // [BH, P, dk]    segment decay products
     float* ws_z;            // [BH, P, dk]    segment normaliser parts
+    float* st_rows;         // backward: state at every chunk boundary [BH, st_slots, dk, dv]
+    float* st_cols;         // backward: the same transposed [BH, st_slots, dv, dk], or null
+    int st_slots;           // boundary slots per (b,h)
     int L, H, BH;
     int P;                  // segments per (b,h)
     int cps;                // chunks per segment (last one may be shorter)
@@ -46,14 +49,46 @@ struct DecodeParams {
     float gamma[LA_MAX_GAMMA_HEADS];
 };
 
+// Backward (chunkwise) parameters: one workgroup per (b,h, chunk).
+struct BwdParams {
+    const void* q;          // [BH, L, d] dtype
+    const void* k;          // [BH, L, d] dtype
+    const void* v;          // [BH, L, d] dtype
+    const void* dout;       // [BH, L, d] dtype
+    const float* log_alpha; // [BH, L, d] (DIAG)
+    const float* st_fwd;    // [BH, nchunks + 1, d, d] state before each chunk, then the final state
+    const float* st_rows;   // [BH, nchunks, d, d] gradient of the state after each chunk
+    const float* st_cols;   // [BH, nchunks, d, d] the same transposed
+    void* dq;               // [BH, L, d] dtype
+    void* dk;               // [BH, L, d] dtype
+    void* dv;               // [BH, L, d] dtype
+    float* dlog_alpha;      // [BH, L, d] (DIAG)
+    int L, H, BH;
+    int nchunks;
+    int phi_elu1;
+    float log2_gamma[LA_MAX_GAMMA_HEADS];
+};
+
+// Passes of the chunk kernel.  MAIN and STATE serve the forward; the
+// backward adds the reversed state pass and the two passes that store the
+// state (or its gradient) at every chunk boundary.
+enum ChunkPass { PASS_MAIN = 0, PASS_STATE = 1, PASS_STATE_REV = 2, PASS_STORE = 3, PASS_STORE_REV = 4 };
+
+// Chunk length of the backward: 64 tokens, 32 for fp32 at d = 128 (whose
+// six tiles of 64 tokens would not fit in the 160 KiB of LDS).
+constexpr int bwd_chunk(int d, bool bf16) { return (!bf16 && d >= 128) ? 32 : 64; }
+
 // Kernel families, as named by the profiling interface.
-enum KernelId { K_CHUNK_MAIN = 0, K_CHUNK_STATE = 1, K_STATE_SCAN = 2, K_DECODE = 3, K_COUNT = 4 };
+enum KernelId {
+    K_CHUNK_MAIN = 0, K_CHUNK_STATE = 1, K_STATE_SCAN = 2, K_DECODE = 3,
+    K_CHUNK_STORE = 4, K_BWD = 5, K_COUNT = 6
+};
 
 // Launch hooks implemented in the kernel files.  Each returns hipSuccess or
 // the launch error; shapes have been validated by the caller.  The chunk
-// launchers take `sonly` = true for the state pass and `nblocks` workgroups.
+// launchers take the pass (ChunkPass) and `nblocks` workgroups.
 #define LA_DECLARE_CHUNK_LAUNCHER(NAME) \
-    hipError_t NAME(const ChunkParams& p, int chunk, int gate, bool sonly, hipStream_t s, int nblocks);
+    hipError_t NAME(const ChunkParams& p, int chunk, int gate, int pass, hipStream_t s, int nblocks);
 LA_DECLARE_CHUNK_LAUNCHER(launch_chunk_f32_d16)
 LA_DECLARE_CHUNK_LAUNCHER(launch_chunk_f32_d32)
 LA_DECLARE_CHUNK_LAUNCHER(launch_chunk_f32_d64)
@@ -62,7 +97,17 @@ LA_DECLARE_CHUNK_LAUNCHER(launch_chunk_bf16_d32)
 LA_DECLARE_CHUNK_LAUNCHER(launch_chunk_bf16_d64)
 LA_DECLARE_CHUNK_LAUNCHER(launch_chunk_bf16_d128)
 #undef LA_DECLARE_CHUNK_LAUNCHER
-hipError_t launch_state_scan(const ChunkParams& p, int d, hipStream_t s);
+hipError_t launch_state_scan(const ChunkParams& p, int d, bool rev, hipStream_t s);
+#define LA_DECLARE_BWD_LAUNCHER(NAME) \
+    hipError_t NAME(const BwdParams& p, int gate, hipStream_t s);
+LA_DECLARE_BWD_LAUNCHER(launch_bwd_f32_d16)
+LA_DECLARE_BWD_LAUNCHER(launch_bwd_f32_d32)
+LA_DECLARE_BWD_LAUNCHER(launch_bwd_f32_d64)
+LA_DECLARE_BWD_LAUNCHER(launch_bwd_f32_d128)
+LA_DECLARE_BWD_LAUNCHER(launch_bwd_bf16_d32)
+LA_DECLARE_BWD_LAUNCHER(launch_bwd_bf16_d64)
+LA_DECLARE_BWD_LAUNCHER(launch_bwd_bf16_d128)
+#undef LA_DECLARE_BWD_LAUNCHER
 hipError_t launch_decode(const DecodeParams& p, int d, bool bf16, int gate, hipStream_t s);
 
 }  // namespace la

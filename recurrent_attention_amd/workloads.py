@@ -27,9 +27,10 @@ Draw order for prefill workloads: one ``torch.Generator`` seeded with
 ``seed`` draws q, k, v (each ``randn([B,H,L,d])`` in fp32, scaled by 1/sqrt(d)
 in fp32, then rounded to bf16 with round-to-nearest-even), then the gate
 pre-activation g.  The decode workload draws S0, then the tokens step by
-step.  Streams drawn on a CUDA device differ from CPU streams (different
-generators); every run is self-consistent because the oracle receives the
-same tensors.
+step.  A backward draws, from its own generator, dout like the tokens and
+then dS_final ~ N(0,1).  Streams drawn on a CUDA device differ from CPU
+streams (different generators); every run is self-consistent because the
+oracle receives the same tensors.
 """
 from __future__ import annotations
 
@@ -137,6 +138,18 @@ def workload_inputs(name: str, seed: int = 0, device="cpu", L=None, B=None):
                           w.gate_mode, seed=seed, device=device,
                           scale_inputs=w.scale_inputs,
                           gamma=w.gamma if w.gate_mode == GATE_GAMMA else None)
+
+
+def backward_inputs(B, H, L, dk, dv, dtype=torch.bfloat16, seed=100, device="cpu",
+                    scale_inputs=True, with_state_grad=True):
+    """Seeded gradients for a prefill backward: dout [B,H,L,dv] drawn like the
+    tokens, and dS_final ~ N(0,1) fp32 [B,H,dk,dv] when asked."""
+    gen = generator(seed, device)
+    dout = _tokens(gen, (B, H, L, dv), dv, dtype, scale_inputs, device)
+    dS = None
+    if with_state_grad:
+        dS = torch.randn((B, H, dk, dv), generator=gen, dtype=torch.float32, device=device)
+    return {"dout": dout, "dS_final": dS}
 
 
 def decode_state(nseq, H, dk, dv, seed=0, device="cpu", with_z=False):

@@ -176,3 +176,48 @@ def test_binding_refuses_cpu_tensors():
     q = torch.zeros(1, 1, 64, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="GPU"):
         api.chunk_fwd(q, q, q)
+
+
+def _bwd(desc, gate_mode=0, gate=None, S0=None, dSf=None, dla=None, dS0=None,
+         ws=A, ws_bytes=1 << 40, q=A, k=A, v=A, do=A, dq=A, dk=A, dv=A):
+    return api.la_chunk_bwd(desc, q, k, v, do, gate_mode, gate, S0, dSf, dq, dk, dv,
+                            dla, dS0, ws, ws_bytes, None)
+
+
+def test_bwd_chunk_and_workspace_size():
+    # states at every chunk boundary: (3 * nchunks + 1) d x d fp32 per (b,h)
+    # (the state before each chunk and the final one, the gradient after each
+    # chunk row-major and transposed),
+    # plus the segment slots of the state passes
+    d = _desc(B=1, H=2, L=1000, dk=64, dv=64, dtype=api.LA_BF16, segments=1)
+    assert api.la_chunk_bwd_chunk(d) == 64
+    assert api.la_chunk_bwd_workspace_bytes(d) == 2 * (3 * 16 + 1) * 64 * 64 * 4
+    d = _desc(B=1, H=2, L=1000, dk=64, dv=64, dtype=api.LA_BF16, segments=4)
+    assert api.la_chunk_bwd_workspace_bytes(d) == (
+        2 * (3 * 16 + 1) * 64 * 64 * 4 + 2 * 4 * (64 * 64 + 128) * 4)
+    f32_128 = _desc(dk=128, dv=128, dtype=api.LA_F32)
+    assert api.la_chunk_bwd_chunk(f32_128) == 32
+    assert api.la_chunk_bwd_workspace_bytes(_desc(L=0)) == 0
+
+
+def test_bwd_validation():
+    d = _desc(L=128)
+    assert _bwd(_desc(L=128, normalize=True)) == api.LA_ERR_UNSUPPORTED
+    assert _bwd(_desc(L=0)) == api.LA_ERR_INVALID
+    for name in ("q", "k", "v", "do", "dq", "dk", "dv"):
+        assert _bwd(d, **{name: None}) == api.LA_ERR_INVALID
+        assert _bwd(d, **{name: MIS}) == api.LA_ERR_INVALID
+    assert _bwd(d, S0=MIS) == api.LA_ERR_INVALID
+    assert _bwd(d, dSf=MIS) == api.LA_ERR_INVALID
+    assert _bwd(d, dS0=MIS) == api.LA_ERR_INVALID
+    # the gate gradient goes with the diagonal gate and nothing else
+    assert _bwd(d, gate_mode=api.LA_GATE_DIAG, gate=A, dla=None) == api.LA_ERR_INVALID
+    assert _bwd(d, gate_mode=api.LA_GATE_NONE, dla=A) == api.LA_ERR_INVALID
+    p, keep = _gamma([0.5, 1.5])
+    assert _bwd(d, gate_mode=api.LA_GATE_GAMMA, gate=p) == api.LA_ERR_INVALID
+    need = api.la_chunk_bwd_workspace_bytes(d)
+    assert _bwd(d, ws=None) == api.LA_ERR_INVALID
+    assert _bwd(d, ws_bytes=need - 4) == api.LA_ERR_INVALID
+    assert _bwd(d, ws=MIS) == api.LA_ERR_INVALID
+    assert _bwd(_desc(L=128, segments=3)) == api.LA_ERR_INVALID   # 2 chunks
+

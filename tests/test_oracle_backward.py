@@ -138,7 +138,7 @@ def test_checkpoint_spacing_does_not_change_the_result():
             np.testing.assert_array_equal(got[name], ref[name])
 
 
-@pytest.mark.parametrize("mutation", ["bwd_no_decay", "bwd_dq_prev"])
+@pytest.mark.parametrize("mutation", sorted(m for m in oracle.MUTATIONS if m.startswith("bwd_")))
 def test_planted_backward_mistakes_are_caught(mutation):
     case = (oracle.GATE_DIAG, None, oracle.PHI_IDENTITY, True, True)
     with oracle.mutation(mutation):
