@@ -15,6 +15,9 @@ Also reported, in the same line:
 * ``decode``: 1000 consecutive recurrent steps of
   ``decode_retention_256x32_d128`` (256 sequences x 32 heads, fp32 state,
   gamma = 0.97): algorithmic GB/s and its roofline.
+* ``backward``: the chunkwise backward of the same prefill (dq, dk, dv,
+  log-gate gradient and dS0 from seeded dout), per-kernel times and the
+  roofline of the per-chunk gradient kernel.
 * ``cpu_baseline``: the fp64 oracle (test infrastructure, untuned) on the
   same prefill workload drawn on the host, timed on this machine's cores.
 
@@ -148,6 +151,83 @@ def bench_prefill(args, torch, api, workloads):
     }
 
 
+def backward_bytes(w):
+    """Algorithmic bytes of one backward of the prefill (no S0, no dS_final):
+    q, k, v, dout read and dq, dk, dv written in bf16, log-gates read and
+    their gradient written in fp32, per token-head, plus dS0 per (b,h)."""
+    per_th = 2 * (4 * w.dk + 3 * w.dv) + (8 * w.dk if w.gate_mode == 2 else 0)
+    return w.B * w.H * w.L * per_th + w.B * w.H * w.dk * w.dv * 4
+
+
+def backward_kernel_bytes(w, chunk):
+    """Bytes the per-chunk gradient kernel must move as designed: the token
+    tensors of the backward plus, per chunk, the state before it and the
+    state gradient after it, in bf16."""
+    nchunks = -(-w.L // chunk)
+    return backward_bytes(w) - w.B * w.H * w.dk * w.dv * 4 + \
+        w.B * w.H * nchunks * 2 * w.dk * w.dv * 2
+
+
+def bench_backward(args, torch, api, workloads):
+    w = workloads.WORKLOADS[workloads.PREFILL_HEADLINE]
+    dev = torch.device("cuda", 0)
+    inp = workloads.workload_inputs(w.name, seed=0, device=dev)
+    grads = workloads.backward_inputs(w.B, w.H, w.L, w.dk, w.dv, torch.bfloat16, seed=100,
+                                      device=dev, with_state_grad=False)
+    q, k, v, la, do = inp["q"], inp["k"], inp["v"], inp["log_alpha"], grads["dout"]
+    desc = api.make_desc(w.B, w.H, w.L, w.dk, w.dv, api.LA_BF16, w.phi, False, 0)
+    chunk = api.la_chunk_bwd_chunk(desc)
+    need = api.la_chunk_bwd_workspace_bytes(desc)
+    ws = torch.empty(max(need // 4, 1), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dla = torch.empty_like(la)
+    dS0 = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
+    sp = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    lib = api.load_library()
+    argv = (ctypes.byref(desc), q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(),
+            w.gate_mode, la.data_ptr(), None, None, dq.data_ptr(), dk.data_ptr(),
+            dv.data_ptr(), dla.data_ptr(), dS0.data_ptr(), ws.data_ptr(), need, sp)
+
+    def step():
+        st = lib.la_chunk_bwd(*argv)
+        if st != 0:
+            raise RuntimeError(api.la_last_error_message())
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    api.la_profile_begin()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    api.la_profile_end()
+    kern = {}
+    for name in ("chunk_state", "state_scan", "chunk_store", "chunk_bwd"):
+        n, ms = api.la_profile_query(name)
+        kern[name] = round(ms / n * 1e3, 2) if n else None
+    ms_step = elapsed / args.steps * 1e3
+    bw_us = kern["chunk_bwd"]
+    kb = backward_kernel_bytes(w, chunk)
+    achieved = kb / (bw_us * 1e-6) / 1e9
+    alg = backward_bytes(w)
+    return {
+        "workload": w.name, "chunk": chunk, "ms_per_step": round(ms_step, 4),
+        "tokens_per_s": round(w.B * w.L / (ms_step * 1e-3), 1),
+        "algorithmic_bytes": alg,
+        "pct_of_hbm_peak_step": round(100.0 * alg / (ms_step * 1e-3) / (HBM_PEAK_GBS * 1e9), 2),
+        "kernels_avg_us": kern,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "kernel": "chunk_bwd", "bytes_per_launch": kb,
+                     "avg_launch_us": bw_us},
+    }
+
+
 def bench_decode(args, torch, api, workloads):
     w = workloads.WORKLOADS[workloads.DECODE_HEADLINE]
     dev = torch.device("cuda", 0)
@@ -244,8 +324,9 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
-    ap.add_argument("--only", choices=["prefill", "decode", "copy"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "backward", "copy"], default=None,
                     help="run one part only (copy: a 1 GiB device copy used to scale "
                          "rocprofv3 byte counters); prints no metric line")
     args = ap.parse_args(argv)
@@ -270,6 +351,9 @@ def main(argv=None):
     if args.only == "decode":
         print(json.dumps(bench_decode(args, torch, api, workloads)), flush=True)
         return 0
+    if args.only == "backward":
+        print(json.dumps(bench_backward(args, torch, api, workloads)), flush=True)
+        return 0
     if args.only == "prefill":
         pre = bench_prefill(args, torch, api, workloads)
         print(json.dumps({"ms_per_step": pre["ms_step"], "kernels": pre["kernels"],
@@ -277,6 +361,7 @@ def main(argv=None):
         return 0
     pre = bench_prefill(args, torch, api, workloads)
     dec = None if args.no_decode else bench_decode(args, torch, api, workloads)
+    bwd = None if args.no_backward else bench_backward(args, torch, api, workloads)
     w = pre["w"]
     line = {
         "metric": METRIC,
@@ -304,6 +389,8 @@ def main(argv=None):
     }
     if dec is not None:
         line["decode"] = dec
+    if bwd is not None:
+        line["backward"] = bwd
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(workloads, w)
     print(json.dumps(line), flush=True)

@@ -172,10 +172,10 @@ la_status la_chunk_bwd(const la_desc* d, const void* q, const void* k,
                        float* dlog_alpha, float* dS0, void* workspace,
                        size_t workspace_bytes, void* stream);
 
-/* Bytes of device workspace la_chunk_bwd needs: fp32 states at every chunk
- * boundary (B*H*(3*ceil(L/C)+1)*dk*dv floats: the state before each chunk
- * and the final state, the state gradient after each chunk row-major and
- * transposed) plus the segment slots.
+/* Bytes of device workspace la_chunk_bwd needs: states at every chunk
+ * boundary in the element type of q/k/v (B*H*(2*ceil(L/C)+1)*dk*dv
+ * elements: the state before each chunk and the final state, the state
+ * gradient after each chunk) plus the fp32 segment slots.
  * Returns 0 for an invalid descriptor. */
 size_t la_chunk_bwd_workspace_bytes(const la_desc* d);
 

@@ -16,7 +16,11 @@
 // where P[t][s] is the forward score with its decay.  The suffix sum that
 // reaches into later chunks, sum over all tokens after this chunk, equals
 // rowsum(G * S_next) with S_next the state after this chunk, so each chunk
-// finishes its own d log a without a pass over the sequence.
+// finishes its own d log a without a pass over the sequence.  S_next is not
+// read: with S_next = e^{B} S + sum_s (k_s e^{B - b_s}) v_s^T,
+//   rowsum(G * S_next)_i = e^{B_i} rowsum(G * S)_i
+//                          + sum_s k_si e^{B_i - b_si} (G v_s)_i
+// and G v_s is the first term of dk_s, already in the accumulators.
 //
 // Matrix-core mapping (C tokens, D = d_k = d_v; wave w owns channel block
 // [16w, 16w+16) of dq, dk and of dv):
@@ -24,12 +28,15 @@
 //         (Qh = q e^{b - r}, Kh = k e^{r - b}, r = b at the chunk middle),
 //         stored transposed, [s][t], with the causal mask (and gamma^(t-s));
 //   dQ^T = e^{r} S dO^T + Kh^T dP^T,   then * e^{b - r}
-//   dK^T = e^{B - r} G V^T + Qh^T dP,  then * e^{r - b}
-//   dV^T = (G^T * e^{B - r}) Kh^T + dO^T P
-// Every output lane holds 4 consecutive channels of one token, which are
-// the same elements the thread loaded and whose decay factors it computed.
-// Operands with the token index as the contraction are read from row-major
-// LDS tiles with the transposing LDS read of gfx950 (ds_read_b64_tr_b16).
+//   dK^T = Gs V^T + Qh^T dP,           then * e^{r - b}
+//   dV^T = Gs^T Kh^T + dO^T P
+// with Gs = diag(e^{B - r}) G held in LDS (row-major; its transpose is read
+// from the same tile).  S comes from memory in the element type.  Every
+// output lane holds 4 consecutive channels of one token, which are the same
+// elements the thread loaded and whose decay factors it computed.  Operands
+// with the token index (or G's row index) as the contraction are read from
+// row-major LDS tiles with the transposing LDS read of gfx950
+// (ds_read_b64_tr_b16).
 #pragma once
 
 #include "la_device.h"
@@ -68,6 +75,7 @@ struct BwdSmem {
     alignas(16) E vv[Cfg::C][Cfg::D];     // V    [s][swizzled n]
     alignas(16) E pt[Cfg::C][Cfg::C];     // P^T  [s][swizzled t]
     alignas(16) E dpt[Cfg::C][Cfg::C];    // dP^T [s][swizzled t]
+    alignas(16) E gs[Cfg::D][Cfg::D];     // Gs   [i][swizzled n]
     alignas(16) float ebr[Cfg::D];        // e^{B - r} per channel (DIAG)
     float gpow[Cfg::C + 2];               // gamma^j
 };
@@ -116,32 +124,28 @@ __device__ __forceinline__ typename Cfg::Frag row_frag(const typename Cfg::E* ti
     return Cfg::T::load(tile + row * ld + bw_pos<Cfg, MASK>(row, col));
 }
 
-// Operand from an fp32 state in memory: rows r0..r0+15 (lane & 15), k-slots
-// the row's elements k0 + (slots of this lane); times f[k] when SCALE, and
-// the unscaled values copied to raw when RAW.  Both are compile-time
-// choices: a uniform branch between matrix-core instructions and the
-// registers they use has been seen to lose the wait states they need.
-template <class Cfg, bool SCALE, bool RAW>
-__device__ __forceinline__ typename Cfg::Frag mem_frag(const float* M, int ld, int r0, int k0,
-                                                       int lane, const float* f, float* raw) {
+// Operand from a state in memory (element type): rows r0..r0+15 (lane & 15),
+// k-slots the row's elements k0 + (slots of this lane).
+template <class Cfg>
+__device__ __forceinline__ typename Cfg::Frag mem_frag(const typename Cfg::E* M, int ld, int r0,
+                                                       int k0, int lane) {
     const int row = r0 + (lane & 15);
     const int col = k0 + Cfg::KPL * (lane >> 4);
-    const float* src = M + (size_t)row * ld + col;
+    return Cfg::T::load(M + (size_t)row * ld + col);
+}
+// The k-slots of an operand as floats.
+template <class Cfg>
+__device__ __forceinline__ void frag_floats(const typename Cfg::Frag& f, float* x) {
     if constexpr (Cfg::BF16) {
-        const float4 a = *reinterpret_cast<const float4*>(src);
-        const float4 b = *reinterpret_cast<const float4*>(src + 4);
-        float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+        const uint4 w = __builtin_bit_cast(uint4, f);
+        const uint32_t u[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            if constexpr (RAW) raw[j] = x[j];
-            if constexpr (SCALE) x[j] *= f[col + j];
+        for (int j = 0; j < 4; ++j) {
+            x[2 * j] = bf16lo(u[j]);
+            x[2 * j + 1] = bf16hi(u[j]);
         }
-        return Cfg::T::from8(x);
     } else {
-        float x = *src;
-        if constexpr (RAW) raw[0] = x;
-        if constexpr (SCALE) x *= f[col];
-        return x;
+        x[0] = f;
     }
 }
 
@@ -166,7 +170,7 @@ __device__ __forceinline__ float row_scan16(float x) {
 template <class Cfg, bool ELU1>
 __global__ __launch_bounds__(Cfg::NT) void bwd_kernel(const BwdParams p) {
     constexpr int D = Cfg::D, C = Cfg::C, GATE = Cfg::GATE, TB = Cfg::TB, NW = Cfg::NW;
-    constexpr int MK = Cfg::MK, RW = Cfg::RW;
+    constexpr int MK = Cfg::MK, RW = Cfg::RW, KPL = Cfg::KPL, UE = Cfg::UE, DU = Cfg::DU;
     constexpr bool BF16 = Cfg::BF16;
     constexpr int ES = (int)sizeof(typename Cfg::E);
     constexpr int DM = Cfg::DMASK, TM = Cfg::TMASK;
@@ -174,6 +178,9 @@ __global__ __launch_bounds__(Cfg::NT) void bwd_kernel(const BwdParams p) {
     using E = typename Cfg::E;
     using Frag = typename Cfg::Frag;
     constexpr float kLog2e = 1.4426950408889634f;
+    // 16-byte units of G each thread copies into LDS
+    constexpr int GU = D * D / UE / Cfg::NT;
+    static_assert(GU * UE * Cfg::NT == D * D, "G copy mapping");
 
     __shared__ BwdSmem<Cfg> sm;
 
@@ -202,10 +209,14 @@ __global__ __launch_bounds__(Cfg::NT) void bwd_kernel(const BwdParams p) {
     const __amdgpu_buffer_rsrc_t rdla =
         make_rsrc(GATE == LA_GATE_DIAG ? (void*)(p.dlog_alpha + rows0 * D) : p.dq,
                   GATE == LA_GATE_DIAG ? (uint32_t)L * D * 4 : 0u);
+    const E* Sc = reinterpret_cast<const E*>(p.st_fwd) + ((size_t)bh * (p.nchunks + 1) + c) * D * D;
+    const E* Gc = reinterpret_cast<const E*>(p.st_rows) + ((size_t)bh * p.nchunks + c) * D * D;
 
-    // ---- loads: per owned token, one 4-channel run of q, k, v, dO (and gates)
+    // ---- loads: per owned token, one 4-channel run of q, k, v, dO (and
+    // gates); the state gradient G in 16-byte units
     Words<RW> qr[TB], kr[TB], vr[TB], dr[TB];
     Words<4> lar[GATE == LA_GATE_DIAG ? TB : 1];
+    uint4 gw[GU];
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) {
         const uint32_t row = (uint32_t)(t0 + 16 * tb + r);
@@ -216,11 +227,13 @@ __global__ __launch_bounds__(Cfg::NT) void bwd_kernel(const BwdParams p) {
         dr[tb] = buf_load_words<RW>(rdo, off);
         if constexpr (GATE == LA_GATE_DIAG) lar[tb] = buf_load_words<4>(rla, (row * D + ch0) * 4);
     }
+#pragma unroll
+    for (int j = 0; j < GU; ++j) gw[j] = reinterpret_cast<const uint4*>(Gc)[tid + j * Cfg::NT];
     if constexpr (GATE == LA_GATE_GAMMA) {
         const float l2g = p.log2_gamma[h];
         for (int j = tid; j < C + 2; j += Cfg::NT) sm.gpow[j] = j == 0 ? 1.0f : exp2f((float)j * l2g);
     }
-    // zero the score tiles (their upper triangles and any padding are read as zeros)
+    // zero the score tiles (their upper triangles are read as zeros)
     {
         E* z0 = &sm.pt[0][0];
         E* z1 = &sm.dpt[0][0];
@@ -302,6 +315,29 @@ __global__ __launch_bounds__(Cfg::NT) void bwd_kernel(const BwdParams p) {
     }
     __syncthreads();
 
+    // ---- Gs = diag(e^{B - r}) G into LDS (the factor table is visible now)
+#pragma unroll
+    for (int j = 0; j < GU; ++j) {
+        const int u = tid + j * Cfg::NT;
+        const int row = u / DU, col = (u % DU) * UE;
+        uint4 w = gw[j];
+        if constexpr (GATE == LA_GATE_DIAG) {
+            const float f = sm.ebr[row];
+            if constexpr (BF16) {
+                w.x = pack_bf16(bf16lo(w.x) * f, bf16hi(w.x) * f);
+                w.y = pack_bf16(bf16lo(w.y) * f, bf16hi(w.y) * f);
+                w.z = pack_bf16(bf16lo(w.z) * f, bf16hi(w.z) * f);
+                w.w = pack_bf16(bf16lo(w.w) * f, bf16hi(w.w) * f);
+            } else {
+                w.x = __float_as_uint(__uint_as_float(w.x) * f);
+                w.y = __float_as_uint(__uint_as_float(w.y) * f);
+                w.z = __float_as_uint(__uint_as_float(w.z) * f);
+                w.w = __float_as_uint(__uint_as_float(w.w) * f);
+            }
+        }
+        *reinterpret_cast<uint4*>(&sm.gs[row][bw_pos<Cfg, DM>(row, col)]) = w;
+    }
+
     // ---- P and dP on the lower-triangular tiles, stored transposed [s][t]:
     // the output lane holds four consecutive t of one s
     {
@@ -336,20 +372,25 @@ __global__ __launch_bounds__(Cfg::NT) void bwd_kernel(const BwdParams p) {
     __syncthreads();
 
     const int nb = wave;   // channel block of this wave
-    const float* Sc = p.st_fwd + ((size_t)bh * (p.nchunks + 1) + c) * D * D;
-    const float* Sn = Sc + (size_t)D * D;                       // state after this chunk
-    const float* Gc = p.st_rows + ((size_t)bh * p.nchunks + c) * D * D;
-    const float* Gt = p.st_cols + ((size_t)bh * p.nchunks + c) * D * D;
 
-    // ---- dQ^T = e^{r} S dO^T + Kh^T dP^T, then * e^{b - r}
+    // ---- dQ^T = e^{r} S dO^T + Kh^T dP^T, then * e^{b - r}; with the
+    // partial rowsum(Gs * S) of row 16 nb + r (diagonal gate)
     float dqf[TB][4];
+    float gss = 0.f;
     {
         f32x4_t acc[TB];
 #pragma unroll
         for (int tb = 0; tb < TB; ++tb) acc[tb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < D / MK; ++kk) {
-            const Frag a = mem_frag<Cfg, false, false>(Sc, D, 16 * nb, kk * MK, lane, nullptr, nullptr);
+            const Frag a = mem_frag<Cfg>(Sc, D, 16 * nb, kk * MK, lane);
+            if constexpr (GATE == LA_GATE_DIAG) {
+                float xs[KPL], xg[KPL];
+                frag_floats<Cfg>(a, xs);
+                frag_floats<Cfg>(row_frag<Cfg, DM>(&sm.gs[0][0], D, 16 * nb, kk * MK, lane), xg);
+#pragma unroll
+                for (int j = 0; j < KPL; ++j) gss += xs[j] * xg[j];
+            }
 #pragma unroll
             for (int tb = 0; tb < TB; ++tb)
                 acc[tb] = T::mma(a, row_frag<Cfg, DM>(&sm.dout[0][0], D, 16 * tb, kk * MK, lane), acc[tb]);
@@ -370,37 +411,32 @@ __global__ __launch_bounds__(Cfg::NT) void bwd_kernel(const BwdParams p) {
             for (int i = 0; i < 4; ++i) dqf[tb][i] = acc[tb][i] * fq[tb][i];
         }
     }
-    // ---- dK^T = e^{B - r} G V^T + Qh^T dP, then * e^{r - b}; with the
-    // chunk's carry rowsum(G * S_next) from the same rows of G
+    // ---- dK^T = Gs V^T + Qh^T dP, then * e^{r - b}; with the partial
+    // sum_s Kh[s][i] (Gs v_s)_i of the chunk's carry (diagonal gate)
     float dkf[TB][4];
-    float gsn = 0.f;   // partial rowsum(G * S_next) of row 16 nb + r
+    float kgv[4] = {0.f, 0.f, 0.f, 0.f};
     {
         f32x4_t acc[TB];
 #pragma unroll
         for (int tb = 0; tb < TB; ++tb) acc[tb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < D / MK; ++kk) {
-            float raw[Cfg::KPL];
-            const Frag a = mem_frag<Cfg, false, GATE == LA_GATE_DIAG>(Gc, D, 16 * nb, kk * MK, lane, nullptr, raw);
-            if constexpr (GATE == LA_GATE_DIAG) {
-                const float* sn = Sn + (size_t)(16 * nb + r) * D + kk * MK + Cfg::KPL * g;
-#pragma unroll
-                for (int j = 0; j < Cfg::KPL; ++j) gsn += raw[j] * sn[j];
-            }
+            const Frag a = row_frag<Cfg, DM>(&sm.gs[0][0], D, 16 * nb, kk * MK, lane);
 #pragma unroll
             for (int tb = 0; tb < TB; ++tb)
                 acc[tb] = T::mma(a, row_frag<Cfg, DM>(&sm.vv[0][0], D, 16 * tb, kk * MK, lane), acc[tb]);
         }
 #pragma unroll
         for (int sb = 0; sb < TB; ++sb) {
+            if constexpr (GATE == LA_GATE_DIAG) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float f = ebr[i];
-                if constexpr (GATE == LA_GATE_GAMMA) {
-                    const int s = 16 * sb + r;
-                    f = s < clen ? sm.gpow[clen - 1 - s] : 0.f;
-                }
-                acc[sb][i] *= f;
+                for (int i = 0; i < 4; ++i) kgv[i] += acc[sb][i] * (kf[sb][i] * fk[sb][i]);
+            }
+            if constexpr (GATE == LA_GATE_GAMMA) {
+                const int s = 16 * sb + r;
+                const float f = s < clen ? sm.gpow[clen - 1 - s] : 0.f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[sb][i] *= f;
             }
 #pragma unroll
             for (int kk = (16 * sb) / MK; kk < C / MK; ++kk)
@@ -410,14 +446,14 @@ __global__ __launch_bounds__(Cfg::NT) void bwd_kernel(const BwdParams p) {
             for (int i = 0; i < 4; ++i) dkf[sb][i] = acc[sb][i] * fk[sb][i];
         }
     }
-    // ---- dV^T = (G^T * e^{B - r}) Kh^T + dO^T P
+    // ---- dV^T = Gs^T Kh^T + dO^T P
     {
         f32x4_t acc[TB];
 #pragma unroll
         for (int tb = 0; tb < TB; ++tb) acc[tb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < D / MK; ++kk) {
-            const Frag a = mem_frag<Cfg, GATE == LA_GATE_DIAG, false>(Gt, D, 16 * nb, kk * MK, lane, sm.ebr, nullptr);
+            const Frag a = tr_frag<Cfg, DM>(&sm.gs[0][0], D, kk * MK, 16 * nb, lane);
 #pragma unroll
             for (int sb = 0; sb < TB; ++sb)
                 acc[sb] = T::mma(a, row_frag<Cfg, DM>(&sm.kh[0][0], D, 16 * sb, kk * MK, lane), acc[sb]);
@@ -459,17 +495,21 @@ __global__ __launch_bounds__(Cfg::NT) void bwd_kernel(const BwdParams p) {
         buf_store_run4<BF16>(rdk, off, xk);
     }
     if constexpr (GATE == LA_GATE_DIAG) {
-        // carry of this chunk per owned channel: rowsum over the four lanes
-        // holding row 16 nb + r, then read from the lane of each channel
-        float rs = gsn;
+        // the chunk's carry rowsum(G * S_next) per owned channel i:
+        //   e^{r_i} rowsum(Gs * S)_i + sum_s Kh[s][i] (Gs v_s)_i
+        // the first sum over the four lanes holding row 16 nb + r, read from
+        // the lane of each channel; the second over the 16 token lanes
+        float rs = gss;
         rs += lane_read(rs, lane ^ 16);
         rs += lane_read(rs, lane ^ 32);
-        float cin[4];
+        float later[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) cin[i] = lane_read(rs, 4 * g + i);
+        for (int i = 0; i < 4; ++i) {
+            const float tok = lane_read(row_scan16<false>(kgv[i]), 16 * g + 15);
+            later[i] = er[i] * lane_read(rs, 4 * g + i) + tok;
+        }
         // suffix sums of db = q dq - k dk over the chunk's tokens: within each
         // block across the lanes, then the later blocks' totals
-        float later[4] = {cin[0], cin[1], cin[2], cin[3]};
 #pragma unroll
         for (int tb = TB - 1; tb >= 0; --tb) {
             float out[4];

@@ -204,6 +204,26 @@ __device__ __forceinline__ void scale_rows(f32x4_t (&acc)[Cfg::MB][Cfg::NB], con
     }
 }
 
+// 4x4 transpose within each quad of lanes: on entry lane q of a quad holds
+// x[j] = M[j][q], on exit x[j] = M[q][j].  Two butterfly exchanges (lanes
+// q ^ 1, then q ^ 2), each moving two of the four values.
+__device__ __forceinline__ void quad_transpose(float (&x)[4], int q) {
+    {
+        const bool odd = q & 1;
+        const float a = odd ? x[0] : x[1], b = odd ? x[2] : x[3];
+        const float a2 = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), 0xB1, 0xF, 0xF, false));
+        const float b2 = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(b), 0xB1, 0xF, 0xF, false));
+        if (odd) { x[0] = a2; x[2] = b2; } else { x[1] = a2; x[3] = b2; }
+    }
+    {
+        const bool hi = q & 2;
+        const float a = hi ? x[0] : x[2], b = hi ? x[1] : x[3];
+        const float a2 = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), 0x4E, 0xF, 0xF, false));
+        const float b2 = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(b), 0x4E, 0xF, 0xF, false));
+        if (hi) { x[0] = a2; x[1] = b2; } else { x[2] = a2; x[3] = b2; }
+    }
+}
+
 template <class Cfg, bool ELU1, bool REV = false, bool STORE = false>
 __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
     constexpr int DK = Cfg::DK, DV = Cfg::DV, C = Cfg::C, GATE = Cfg::GATE;
@@ -347,23 +367,24 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
 
     // chunk handled at iteration ci (reverse order for the gradient pass)
     auto cof = [&](int ci) { return REV ? c_begin + c_end - 1 - ci : ci; };
-    // the true state in the accumulators, into boundary slot `slot`: rows
-    // times the after-factor still pending (diagonal gate), row-major and,
-    // when asked, transposed
+    // the true state in the accumulators, into boundary slot `slot` in the
+    // element type: rows times the after-factor still pending (diagonal
+    // gate), then a 4x4 transpose within each lane quad so that every lane
+    // writes four consecutive columns of one row
     auto store_state = [&](int slot) {
-        float* rows = p.st_rows + ((size_t)bh * p.st_slots + slot) * SS;
-        float* cols = p.st_cols ? p.st_cols + ((size_t)bh * p.st_slots + slot) * SS : nullptr;
+        E* rows = reinterpret_cast<E*>(p.st_rows) + ((size_t)bh * p.st_slots + slot) * SS;
+        const int q4 = lane & 3;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
             f32x4_t f = {1.f, 1.f, 1.f, 1.f};
             if constexpr (GATE == LA_GATE_DIAG) f = *reinterpret_cast<const f32x4_t*>(&sm.post[16 * mb + 4 * g]);
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
-                const f32x4_t x = accS[mb][nb] * f;
-                const int col = colbase + 16 * nb + r;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) rows[(size_t)(16 * mb + 4 * g + i) * DV + col] = x[i];
-                if (cols) *reinterpret_cast<f32x4_t*>(&cols[(size_t)col * DK + 16 * mb + 4 * g]) = x;
+                float x[4] = {accS[mb][nb][0] * f[0], accS[mb][nb][1] * f[1],
+                              accS[mb][nb][2] * f[2], accS[mb][nb][3] * f[3]};
+                quad_transpose(x, q4);
+                E* dst = rows + (size_t)(16 * mb + 4 * g + q4) * DV + colbase + 16 * nb + (r & ~3);
+                store_run<BF16, 4>(dst, x);
             }
         }
     };

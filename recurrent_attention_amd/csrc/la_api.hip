@@ -176,20 +176,20 @@ hipError_t bwd_launch(const la_desc* d, const la::BwdParams& p, int gate, hipStr
     }
 }
 
-// Backward workspace, in floats: the state before every chunk and the final
-// state, the state gradient after every chunk (row-major and transposed),
-// then the segment slots of the state passes.
+// Backward workspace, in bytes: the state before every chunk and the final
+// state, then the state gradient after every chunk, both in the element
+// type of q/k/v; then the fp32 segment slots of the state passes.
 struct BwdLayout {
-    size_t fwd, rows, cols, seg, total;
+    size_t fwd, rows, seg, total;
 };
 BwdLayout bwd_layout(const la_desc* d, const Plan& pl) {
     const size_t bh = (size_t)d->B * d->H, dd = (size_t)d->dk * d->dv;
+    const size_t es = d->dtype == LA_BF16 ? 2 : 4;
     BwdLayout w;
     w.fwd = 0;
-    w.rows = w.fwd + bh * (pl.nchunks + 1) * dd;
-    w.cols = w.rows + bh * pl.nchunks * dd;
-    w.seg = w.cols + bh * pl.nchunks * dd;
-    w.total = w.seg + (pl.P > 1 ? bh * pl.P * (dd + 2 * (size_t)d->dk) : 0);
+    w.rows = w.fwd + bh * (pl.nchunks + 1) * dd * es;
+    w.seg = w.rows + bh * pl.nchunks * dd * es;
+    w.total = w.seg + (pl.P > 1 ? bh * pl.P * (dd + 2 * (size_t)d->dk) * sizeof(float) : 0);
     return w;
 }
 
@@ -306,7 +306,7 @@ la_status la_chunk_fwd(const la_desc* d, const void* q, const void* k, const voi
 size_t la_chunk_bwd_workspace_bytes(const la_desc* d) {
     if (check_desc(d) != LA_OK) return 0;
     const int chunk = la::bwd_chunk(d->dk, d->dtype == LA_BF16);
-    return bwd_layout(d, make_plan(d, chunk)).total * sizeof(float);
+    return bwd_layout(d, make_plan(d, chunk)).total;
 }
 
 int la_chunk_bwd_chunk(const la_desc* d) {
@@ -344,14 +344,13 @@ la_status la_chunk_bwd(const la_desc* d, const void* q, const void* k, const voi
     if (st != LA_OK) return st;
     const Plan pl = make_plan(d, chunk);
     const BwdLayout w = bwd_layout(d, pl);
-    if (!workspace) return fail(LA_ERR_INVALID, "workspace of %zu bytes is required", w.total * sizeof(float));
+    if (!workspace) return fail(LA_ERR_INVALID, "workspace of %zu bytes is required", w.total);
     if (!aligned16(workspace)) return fail(LA_ERR_INVALID, "workspace must be 16-byte aligned");
-    if (ws_bytes < w.total * sizeof(float))
-        return fail(LA_ERR_INVALID, "workspace has %zu bytes, %zu required", ws_bytes,
-                    w.total * sizeof(float));
+    if (ws_bytes < w.total)
+        return fail(LA_ERR_INVALID, "workspace has %zu bytes, %zu required", ws_bytes, w.total);
 
     const int BH = d->B * d->H;
-    float* ws = static_cast<float*>(workspace);
+    char* ws = static_cast<char*>(workspace);
     p.log_alpha = gate_mode == LA_GATE_DIAG ? gamma_or_log_alpha : nullptr;
     p.L = d->L;
     p.H = d->H;
@@ -362,7 +361,7 @@ la_status la_chunk_bwd(const la_desc* d, const void* q, const void* k, const voi
     p.phi_elu1 = d->phi == LA_PHI_ELU1;
     if (pl.P > 1) {
         const size_t slots = (size_t)BH * pl.P;
-        p.ws_S = ws + w.seg;
+        p.ws_S = reinterpret_cast<float*>(ws + w.seg);
         p.ws_a = p.ws_S + slots * d->dk * d->dv;
         p.ws_z = p.ws_a + slots * d->dk;
     }
@@ -376,7 +375,6 @@ la_status la_chunk_bwd(const la_desc* d, const void* q, const void* k, const voi
     p.S0 = S0;
     p.S_final = nullptr;
     p.st_rows = ws + w.fwd;
-    p.st_cols = nullptr;
     p.st_slots = pl.nchunks + 1;
     if (pl.P > 1) {
         e = timed_launch(la::K_CHUNK_STATE, s, [&] {
@@ -398,7 +396,6 @@ la_status la_chunk_bwd(const la_desc* d, const void* q, const void* k, const voi
     p.S0 = dS_final;
     p.S_final = dS0;
     p.st_rows = ws + w.rows;
-    p.st_cols = ws + w.cols;
     p.st_slots = pl.nchunks;
     if (pl.P > 1) {
         e = timed_launch(la::K_CHUNK_STATE, s, [&] {
@@ -423,7 +420,6 @@ la_status la_chunk_bwd(const la_desc* d, const void* q, const void* k, const voi
     b.log_alpha = p.log_alpha;
     b.st_fwd = ws + w.fwd;
     b.st_rows = ws + w.rows;
-    b.st_cols = ws + w.cols;
     b.dq = dq;
     b.dk = dk;
     b.dv = dv;

@@ -25,8 +25,7 @@ struct ChunkParams {
     float* ws_S;            // [BH, P, dk*dv] segment states (P > 1)
     float* ws_a;            // [BH, P, dk]    segment decay products
     float* ws_z;            // [BH, P, dk]    segment normaliser parts
-    float* st_rows;         // backward: state at every chunk boundary [BH, st_slots, dk, dv]
-    float* st_cols;         // backward: the same transposed [BH, st_slots, dv, dk], or null
+    void* st_rows;          // backward: state at every chunk boundary [BH, st_slots, dk, dv] dtype
     int st_slots;           // boundary slots per (b,h)
     int L, H, BH;
     int P;                  // segments per (b,h)
@@ -56,9 +55,8 @@ struct BwdParams {
     const void* v;          // [BH, L, d] dtype
     const void* dout;       // [BH, L, d] dtype
     const float* log_alpha; // [BH, L, d] (DIAG)
-    const float* st_fwd;    // [BH, nchunks + 1, d, d] state before each chunk, then the final state
-    const float* st_rows;   // [BH, nchunks, d, d] gradient of the state after each chunk
-    const float* st_cols;   // [BH, nchunks, d, d] the same transposed
+    const void* st_fwd;     // [BH, nchunks + 1, d, d] dtype: state before each chunk, then the final state
+    const void* st_rows;    // [BH, nchunks, d, d] dtype: gradient of the state after each chunk
     void* dq;               // [BH, L, d] dtype
     void* dk;               // [BH, L, d] dtype
     void* dv;               // [BH, L, d] dtype

@@ -98,6 +98,7 @@ def _check(got, ref, dtype, what):
             assert got[k] is None, k
             continue
         errs[k] = slice_rel_err(got[k], ref[k])
+    print(f"{what}: " + ", ".join(f"{k} {v:.2e}" for k, v in errs.items()))
     bad = {k: v for k, v in errs.items() if not v <= tol}
     assert not bad, f"{what}: errors {errs} exceed {tol}"
     return errs
