@@ -127,6 +127,44 @@ la_status la_chunk_fwd(const la_desc* d, const void* q, const void* k,
                        float* z_final, void* workspace, size_t workspace_bytes,
                        void* stream);
 
+/*
+ * la_chunk_fwd_varlen -- the same prefill over B packed sequences of
+ * different lengths that share each head's token axis, each with its own
+ * initial and final state (the batched prefill before recurrent decoding:
+ * "Module 22", incremental decoding with a running state; the S_final of
+ * each sequence is the state la_decode_step continues from).
+ *   d            d->B = number of sequences, d->L = T = total tokens;
+ *                d->segments as for la_chunk_fwd, counted for max_seqlen
+ *   cu_seqlens   device int32 [B+1]: sequence n owns tokens
+ *                [cu_seqlens[n], cu_seqlens[n+1]) of every head; the
+ *                caller guarantees 0 = cu[0] <= cu[1] <= ... <= cu[B] <= T
+ *                and every length <= max_seqlen (device data, not
+ *                validated; the kernels clamp offsets to [0, T], so a
+ *                violation gives wrong values but no access outside the
+ *                tensors).  Empty sequences are allowed (S_final = S0).
+ *   max_seqlen   host int, 1 <= max_seqlen <= T: the longest sequence
+ *   q, k         device [H,T,dk] (a [1,H,T,dk] tensor) of d->dtype
+ *   v, out       device [H,T,dv]
+ *   log_alpha    DIAG: device fp32 [H,T,dk]
+ *   S0, S_final  device fp32 [B,H,dk,dv] per sequence (NULL as before)
+ *   z0, z_final  device fp32 [B,H,dk]
+ *   workspace    la_chunk_fwd_varlen_workspace_bytes(d, max_seqlen, chunk)
+ * Everything else as for la_chunk_fwd.
+ */
+la_status la_chunk_fwd_varlen(const la_desc* d, const int* cu_seqlens,
+                              int max_seqlen, const void* q, const void* k,
+                              const void* v, int gate_mode,
+                              const float* gamma_or_log_alpha,
+                              const float* S0, const float* z0, int chunk,
+                              void* out, float* S_final, float* z_final,
+                              void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/* Workspace bytes of la_chunk_fwd_varlen (0 if none is needed or the
+ * arguments are invalid). */
+size_t la_chunk_fwd_varlen_workspace_bytes(const la_desc* d, int max_seqlen,
+                                           int chunk);
+
 /* Bytes of device workspace la_chunk_fwd needs for this shape (segment
  * states, their decays and normaliser parts); 0 for a single segment.
  * Returns 0 for an invalid descriptor as well. */

@@ -7,8 +7,8 @@ are allocated with torch (device memory is PyTorch's job here).  There is no
 CPU fallback: a missing library or a tensor that is not on a GPU raises.
 
 Functions named ``la_*`` mirror the C entry points one to one;
-:func:`chunk_fwd`, :func:`chunk_bwd` and :func:`decode_step` are
-conveniences around them.
+:func:`chunk_fwd`, :func:`chunk_fwd_varlen`, :func:`chunk_bwd` and
+:func:`decode_step` are conveniences around them.
 """
 from __future__ import annotations
 
@@ -31,6 +31,7 @@ EXPORTED = (
     "la_decode_step", "la_status_string", "la_last_error_message",
     "la_version", "la_profile_begin", "la_profile_end", "la_profile_query",
     "la_chunk_bwd", "la_chunk_bwd_workspace_bytes", "la_chunk_bwd_chunk",
+    "la_chunk_fwd_varlen", "la_chunk_fwd_varlen_workspace_bytes",
 )
 
 
@@ -70,6 +71,11 @@ def load_library():
     lib.la_chunk_fwd_workspace_bytes.restype = sz
     lib.la_chunk_fwd_segments.argtypes = [dp, i]
     lib.la_chunk_fwd_segments.restype = i
+    lib.la_chunk_fwd_varlen.argtypes = [dp, vp, i, vp, vp, vp, i, vp, vp, vp, i, vp, vp, vp,
+                                         vp, sz, vp]
+    lib.la_chunk_fwd_varlen.restype = i
+    lib.la_chunk_fwd_varlen_workspace_bytes.argtypes = [dp, i, i]
+    lib.la_chunk_fwd_varlen_workspace_bytes.restype = sz
     lib.la_chunk_bwd.argtypes = [dp, vp, vp, vp, vp, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.la_chunk_bwd.restype = i
     lib.la_chunk_bwd_workspace_bytes.argtypes = [dp]
@@ -114,6 +120,21 @@ def la_chunk_fwd(desc, q, k, v, gate_mode, gamma_or_log_alpha, S0, z0, chunk,
     return load_library().la_chunk_fwd(
         ctypes.byref(desc), q, k, v, int(gate_mode), gamma_or_log_alpha, S0, z0,
         int(chunk), out, S_final, z_final, workspace, int(workspace_bytes), stream)
+
+
+def la_chunk_fwd_varlen(desc, cu_seqlens, max_seqlen, q, k, v, gate_mode,
+                        gamma_or_log_alpha, S0, z0, chunk, out, S_final, z_final,
+                        workspace, workspace_bytes, stream):
+    """Raw call; pointer arguments are ints (0 = NULL) or ctypes pointers."""
+    return load_library().la_chunk_fwd_varlen(
+        ctypes.byref(desc), cu_seqlens, int(max_seqlen), q, k, v, int(gate_mode),
+        gamma_or_log_alpha, S0, z0, int(chunk), out, S_final, z_final, workspace,
+        int(workspace_bytes), stream)
+
+
+def la_chunk_fwd_varlen_workspace_bytes(desc, max_seqlen, chunk) -> int:
+    return int(load_library().la_chunk_fwd_varlen_workspace_bytes(
+        ctypes.byref(desc), int(max_seqlen), int(chunk)))
 
 
 def la_chunk_bwd(desc, q, k, v, dout, gate_mode, gamma_or_log_alpha, S0, dS_final,
@@ -295,6 +316,68 @@ def decode_step(q, k, v, S, z=None, gate_mode=LA_GATE_NONE, gamma=None,
     _check(st)
     del g_keep
     return out
+
+
+def chunk_fwd_varlen(q, k, v, cu_seqlens, max_seqlen=None, gate_mode=LA_GATE_NONE,
+                     gamma=None, log_alpha=None, S0=None, z0=None, chunk=64,
+                     phi=LA_PHI_IDENTITY, normalize=False, segments=0, out=None,
+                     S_final=None, z_final=None, return_state=True, workspace=None,
+                     stream=None):
+    """Prefill of packed sequences.  q, k: [1,H,T,dk] (or [H,T,dk]); v:
+    [1,H,T,dv]; cu_seqlens: int32 [N+1] on the GPU.  ``max_seqlen`` is the
+    longest sequence (read from cu_seqlens when omitted, which copies it to
+    the host).  Returns ``(out, S_final, z_final)`` with per-sequence states
+    [N,H,dk,dv]."""
+    torch = _torch()
+    if q.dim() == 3:
+        q, k, v = q[None], k[None], v[None]
+        if log_alpha is not None and log_alpha.dim() == 3:
+            log_alpha = log_alpha[None]
+    one, H, T, dk = q.shape
+    if one != 1:
+        raise ValueError("packed sequences need q of shape [1,H,T,dk]")
+    dv = v.shape[-1]
+    if cu_seqlens.dtype != torch.int32:
+        raise TypeError("cu_seqlens must be int32")
+    N = cu_seqlens.numel() - 1
+    if N < 1:
+        raise ValueError("cu_seqlens needs at least two entries")
+    if max_seqlen is None:
+        lens = cu_seqlens.diff()
+        max_seqlen = max(1, int(lens.max().item()))
+    dt = _la_dtype(q)
+    desc = make_desc(N, H, T, dk, dv, dt, phi, normalize, segments)
+    dev = q.device
+    if out is None:
+        out = torch.empty((1, H, T, dv), dtype=q.dtype, device=dev)
+    if return_state and S_final is None:
+        S_final = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    if return_state and normalize and z_final is None:
+        z_final = torch.empty((N, H, dk), dtype=torch.float32, device=dev)
+    need = la_chunk_fwd_varlen_workspace_bytes(desc, max_seqlen, chunk)
+    if need and workspace is None:
+        workspace = torch.empty(need // 4 + 4, dtype=torch.float32, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    g_arg = None
+    g_keep = None
+    if gate_mode == LA_GATE_GAMMA:
+        g_keep = _gamma_host(gamma, H)
+        g_arg = ctypes.c_void_p(g_keep.data_ptr())
+    elif gate_mode == LA_GATE_DIAG:
+        g_arg = _dev_ptr(log_alpha, "log_alpha", torch.float32, (1, H, T, dk))
+    st = la_chunk_fwd_varlen(
+        desc, _dev_ptr(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,)), max_seqlen,
+        _dev_ptr(q, "q"), _dev_ptr(k, "k", q.dtype, (1, H, T, dk)),
+        _dev_ptr(v, "v", q.dtype, (1, H, T, dv)),
+        gate_mode, g_arg, _dev_ptr(S0, "S0", torch.float32, (N, H, dk, dv)),
+        _dev_ptr(z0, "z0", torch.float32, (N, H, dk)), chunk,
+        _dev_ptr(out, "out", q.dtype, (1, H, T, dv)),
+        _dev_ptr(S_final, "S_final", torch.float32, (N, H, dk, dv)),
+        _dev_ptr(z_final, "z_final", torch.float32, (N, H, dk)),
+        _dev_ptr(workspace, "workspace"), ws_bytes, _stream_ptr(stream, dev))
+    _check(st)
+    del g_keep
+    return out, S_final, z_final
 
 
 def chunk_bwd(q, k, v, dout, gate_mode=LA_GATE_NONE, gamma=None, log_alpha=None,

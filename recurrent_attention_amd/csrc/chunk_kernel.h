@@ -253,9 +253,21 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
     const int seg = blockIdx.x % PS + ((AGG && REV) ? 1 : 0);
     const int bh = blockIdx.x / PS;
     const int h = bh % p.H;
-    const int L = p.L;
+    // the token range of this (b,h) slice: all L tokens of slice bh, or
+    // (packed sequences) tokens [cu[n], cu[n+1]) of head h's p.L tokens,
+    // clamped to that head's range
+    int L = p.L;
+    size_t rows0 = (size_t)bh * L;
+    if (p.cu_seqlens) {
+        const int n = bh / p.H;
+        const int s0 = min(max(p.cu_seqlens[n], 0), p.L);
+        const int s1 = min(max(p.cu_seqlens[n + 1], s0), p.L);
+        L = s1 - s0;
+        rows0 = (size_t)h * p.L + s0;
+    }
+    const int nchunks = (L + C - 1) / C;
     const int c_begin = seg * p.cps;
-    const int c_end = min(c_begin + p.cps, p.nchunks);
+    const int c_end = min(c_begin + p.cps, nchunks);
     const bool norm = p.normalize != 0;
 
     const int kcp = tid % KCP, ktg = tid / KCP;
@@ -263,7 +275,6 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
     const int colbase = wave * Cfg::WN;
 
     // ---- buffer descriptors over this (b,h) slice
-    const size_t rows0 = (size_t)bh * L;
     const __amdgpu_buffer_rsrc_t rq =
         make_rsrc(reinterpret_cast<const E*>(p.q) + rows0 * DK, (uint32_t)L * DK * ES);
     const __amdgpu_buffer_rsrc_t rk =

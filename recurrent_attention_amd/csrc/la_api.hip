@@ -193,8 +193,108 @@ BwdLayout bwd_layout(const la_desc* d, const Plan& pl) {
     return w;
 }
 
+// The descriptor the segment plan is made for: packed sequences plan for the
+// longest one (every sequence gets the same number of segments; those past
+// a shorter sequence's end are empty and compose as the identity).
+la_desc plan_desc(const la_desc* d, const void* packed, int max_seqlen) {
+    la_desc dp = *d;
+    if (packed) dp.L = max_seqlen;
+    return dp;
+}
+
+la_status check_varlen(const la_desc* d, const int* cu_seqlens, int max_seqlen) {
+    const la_status st = check_desc(d);
+    if (st != LA_OK) return st;
+    if (!cu_seqlens) return fail(LA_ERR_INVALID, "cu_seqlens must be non-NULL");
+    if (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u)
+        return fail(LA_ERR_INVALID, "cu_seqlens must be 4-byte aligned");
+    if (max_seqlen < 1 || max_seqlen > d->L)
+        return fail(LA_ERR_INVALID, "max_seqlen=%d must be in [1, L=%d]", max_seqlen, d->L);
+    return LA_OK;
+}
+
 la_status hip_fail(hipError_t e, const char* what) {
     return fail(LA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+la_status chunk_fwd_impl(const la_desc* d, const int* cu_seqlens, int max_seqlen, const void* q,
+                         const void* k, const void* v, int gate_mode,
+                         const float* gamma_or_log_alpha, const float* S0, const float* z0,
+                         int chunk, void* out, float* S_final, float* z_final, void* workspace,
+                         size_t ws_bytes, void* stream) {
+    // packed sequences plan their segments for the longest one
+    const la_desc dp = plan_desc(d, cu_seqlens, max_seqlen);
+    la_status st;
+    if (!supported_chunk(chunk))
+        return fail(LA_ERR_UNSUPPORTED, "chunk must be 16, 32 or 64 (got %d)", chunk);
+    if (!q || !k || !v || !out) return fail(LA_ERR_INVALID, "q, k, v and out must be non-NULL");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+        (S0 && !aligned16(S0)) || (z0 && !aligned16(z0)) || (S_final && !aligned16(S_final)) ||
+        (z_final && !aligned16(z_final)))
+        return fail(LA_ERR_INVALID, "device pointers must be 16-byte aligned");
+    if (!d->normalize && (z0 || z_final))
+        return fail(LA_ERR_INVALID, "z0/z_final given without normalize");
+    if (d->segments > 0 && d->segments > (dp.L + chunk - 1) / chunk)
+        return fail(LA_ERR_INVALID, "segments=%d exceeds the %d chunks", d->segments,
+                    (dp.L + chunk - 1) / chunk);
+
+    la::ChunkParams p;
+    std::memset(&p, 0, sizeof p);
+    st = check_gate(d, gate_mode, gamma_or_log_alpha, true, p.log2_gamma, nullptr);
+    if (st != LA_OK) return st;
+
+    const Plan pl = make_plan(&dp, chunk);
+    const size_t need = workspace_bytes(&dp, pl);
+    if (need > 0) {
+        if (!workspace) return fail(LA_ERR_INVALID, "workspace of %zu bytes is required", need);
+        if (!aligned16(workspace)) return fail(LA_ERR_INVALID, "workspace must be 16-byte aligned");
+        if (ws_bytes < need)
+            return fail(LA_ERR_INVALID, "workspace has %zu bytes, %zu required", ws_bytes, need);
+    }
+
+    const int BH = d->B * d->H;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.log_alpha = gate_mode == LA_GATE_DIAG ? gamma_or_log_alpha : nullptr;
+    p.S0 = S0;
+    p.z0 = z0;
+    p.out = out;
+    p.S_final = S_final;
+    p.z_final = z_final;
+    p.L = d->L;
+    p.H = d->H;
+    p.BH = BH;
+    p.P = pl.P;
+    p.cps = pl.cps;
+    p.nchunks = pl.nchunks;
+    p.phi_elu1 = d->phi == LA_PHI_ELU1;
+    p.normalize = d->normalize;
+    p.cu_seqlens = cu_seqlens;
+    if (pl.P > 1) {
+        float* ws = static_cast<float*>(workspace);
+        const size_t slots = (size_t)BH * pl.P;
+        p.ws_S = ws;
+        p.ws_a = ws + slots * d->dk * d->dv;
+        p.ws_z = p.ws_a + slots * d->dk;
+    }
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (pl.P > 1) {
+        // state pass over every segment but the last, then the segment scan
+        e = timed_launch(la::K_CHUNK_STATE, s, [&] {
+            return chunk_launch(d, p, chunk, gate_mode, la::PASS_STATE, s, BH * (pl.P - 1));
+        });
+        if (e != hipSuccess) return hip_fail(e, "state pass launch");
+        e = timed_launch(la::K_STATE_SCAN, s, [&] { return la::launch_state_scan(p, d->dk, false, s); });
+        if (e != hipSuccess) return hip_fail(e, "segment scan launch");
+    }
+    e = timed_launch(la::K_CHUNK_MAIN, s, [&] {
+        return chunk_launch(d, p, chunk, gate_mode, la::PASS_MAIN, s, BH * pl.P);
+    });
+    if (e != hipSuccess) return hip_fail(e, "main pass launch");
+    return LA_OK;
 }
 
 }  // namespace
@@ -230,77 +330,29 @@ la_status la_chunk_fwd(const la_desc* d, const void* q, const void* k, const voi
                        const float* z0, int chunk, void* out, float* S_final, float* z_final,
                        void* workspace, size_t ws_bytes, void* stream) {
     g_errmsg[0] = '\0';
-    la_status st = check_desc(d);
+    const la_status st = check_desc(d);
     if (st != LA_OK) return st;
-    if (!supported_chunk(chunk))
-        return fail(LA_ERR_UNSUPPORTED, "chunk must be 16, 32 or 64 (got %d)", chunk);
-    if (!q || !k || !v || !out) return fail(LA_ERR_INVALID, "q, k, v and out must be non-NULL");
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
-        (S0 && !aligned16(S0)) || (z0 && !aligned16(z0)) || (S_final && !aligned16(S_final)) ||
-        (z_final && !aligned16(z_final)))
-        return fail(LA_ERR_INVALID, "device pointers must be 16-byte aligned");
-    if (!d->normalize && (z0 || z_final))
-        return fail(LA_ERR_INVALID, "z0/z_final given without normalize");
-    if (d->segments > 0 && d->segments > (d->L + chunk - 1) / chunk)
-        return fail(LA_ERR_INVALID, "segments=%d exceeds the %d chunks", d->segments,
-                    (d->L + chunk - 1) / chunk);
+    return chunk_fwd_impl(d, nullptr, 0, q, k, v, gate_mode, gamma_or_log_alpha, S0, z0, chunk,
+                          out, S_final, z_final, workspace, ws_bytes, stream);
+}
 
-    la::ChunkParams p;
-    std::memset(&p, 0, sizeof p);
-    st = check_gate(d, gate_mode, gamma_or_log_alpha, true, p.log2_gamma, nullptr);
+la_status la_chunk_fwd_varlen(const la_desc* d, const int* cu_seqlens, int max_seqlen,
+                              const void* q, const void* k, const void* v, int gate_mode,
+                              const float* gamma_or_log_alpha, const float* S0, const float* z0,
+                              int chunk, void* out, float* S_final, float* z_final,
+                              void* workspace, size_t ws_bytes, void* stream) {
+    g_errmsg[0] = '\0';
+    const la_status st = check_varlen(d, cu_seqlens, max_seqlen);
     if (st != LA_OK) return st;
+    return chunk_fwd_impl(d, cu_seqlens, max_seqlen, q, k, v, gate_mode, gamma_or_log_alpha, S0,
+                          z0, chunk, out, S_final, z_final, workspace, ws_bytes, stream);
+}
 
-    const Plan pl = make_plan(d, chunk);
-    const size_t need = workspace_bytes(d, pl);
-    if (need > 0) {
-        if (!workspace) return fail(LA_ERR_INVALID, "workspace of %zu bytes is required", need);
-        if (!aligned16(workspace)) return fail(LA_ERR_INVALID, "workspace must be 16-byte aligned");
-        if (ws_bytes < need)
-            return fail(LA_ERR_INVALID, "workspace has %zu bytes, %zu required", ws_bytes, need);
-    }
-
-    const int BH = d->B * d->H;
-    p.q = q;
-    p.k = k;
-    p.v = v;
-    p.log_alpha = gate_mode == LA_GATE_DIAG ? gamma_or_log_alpha : nullptr;
-    p.S0 = S0;
-    p.z0 = z0;
-    p.out = out;
-    p.S_final = S_final;
-    p.z_final = z_final;
-    p.L = d->L;
-    p.H = d->H;
-    p.BH = BH;
-    p.P = pl.P;
-    p.cps = pl.cps;
-    p.nchunks = pl.nchunks;
-    p.phi_elu1 = d->phi == LA_PHI_ELU1;
-    p.normalize = d->normalize;
-    if (pl.P > 1) {
-        float* ws = static_cast<float*>(workspace);
-        const size_t slots = (size_t)BH * pl.P;
-        p.ws_S = ws;
-        p.ws_a = ws + slots * d->dk * d->dv;
-        p.ws_z = p.ws_a + slots * d->dk;
-    }
-
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e;
-    if (pl.P > 1) {
-        // state pass over every segment but the last, then the segment scan
-        e = timed_launch(la::K_CHUNK_STATE, s, [&] {
-            return chunk_launch(d, p, chunk, gate_mode, la::PASS_STATE, s, BH * (pl.P - 1));
-        });
-        if (e != hipSuccess) return hip_fail(e, "state pass launch");
-        e = timed_launch(la::K_STATE_SCAN, s, [&] { return la::launch_state_scan(p, d->dk, false, s); });
-        if (e != hipSuccess) return hip_fail(e, "segment scan launch");
-    }
-    e = timed_launch(la::K_CHUNK_MAIN, s, [&] {
-        return chunk_launch(d, p, chunk, gate_mode, la::PASS_MAIN, s, BH * pl.P);
-    });
-    if (e != hipSuccess) return hip_fail(e, "main pass launch");
-    return LA_OK;
+size_t la_chunk_fwd_varlen_workspace_bytes(const la_desc* d, int max_seqlen, int chunk) {
+    if (check_desc(d) != LA_OK || !supported_chunk(chunk) || max_seqlen < 1 || max_seqlen > d->L)
+        return 0;
+    const la_desc dp = plan_desc(d, d, max_seqlen);
+    return workspace_bytes(&dp, make_plan(&dp, chunk));
 }
 
 size_t la_chunk_bwd_workspace_bytes(const la_desc* d) {

@@ -25,6 +25,7 @@ struct ChunkParams {
     float* ws_S;            // [BH, P, dk*dv] segment states (P > 1)
     float* ws_a;            // [BH, P, dk]    segment decay products
     float* ws_z;            // [BH, P, dk]    segment normaliser parts
+    const int* cu_seqlens;  // packed sequences: [B + 1] token offsets into each head's L tokens, or null
     void* st_rows;          // backward: state at every chunk boundary [BH, st_slots, dk, dv] dtype
     int st_slots;           // boundary slots per (b,h)
     int L, H, BH;

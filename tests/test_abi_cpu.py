@@ -220,3 +220,31 @@ def test_bwd_validation():
     assert _bwd(d, ws=MIS) == api.LA_ERR_INVALID
     assert _bwd(_desc(L=128, segments=3)) == api.LA_ERR_INVALID   # 2 chunks
 
+
+
+def _varlen(desc, cu=A, max_seqlen=64, chunk=64, ws=None, ws_bytes=0, q=A, out=A):
+    return api.la_chunk_fwd_varlen(desc, cu, max_seqlen, q, A, A, 0, None, None, None, chunk,
+                                   out, None, None, ws, ws_bytes, None)
+
+
+def test_varlen_validation():
+    d = _desc(B=3, H=2, L=300)
+    assert _varlen(d, cu=None) == api.LA_ERR_INVALID
+    assert _varlen(d, cu=A + 2) == api.LA_ERR_INVALID          # not 4-byte aligned
+    assert _varlen(d, max_seqlen=0) == api.LA_ERR_INVALID
+    assert _varlen(d, max_seqlen=301) == api.LA_ERR_INVALID
+    assert _varlen(d, q=None) == api.LA_ERR_INVALID
+    assert _varlen(d, chunk=48) == api.LA_ERR_UNSUPPORTED
+    assert _varlen(_desc(B=3, H=2, L=300, segments=3), max_seqlen=100) == api.LA_ERR_INVALID
+    assert _varlen(_desc(B=0, H=2, L=300)) == api.LA_ERR_INVALID
+
+
+def test_varlen_workspace_plans_for_the_longest_sequence():
+    # 3 sequences x 2 heads, longest 1000 tokens (16 chunks of 64): the
+    # automatic plan gives every (sequence, head) ceil(256 / 6) -> 16 segments
+    d = _desc(B=3, H=2, L=1500)
+    need = api.la_chunk_fwd_varlen_workspace_bytes(d, 1000, 64)
+    assert need == 3 * 2 * 16 * (64 * 64 + 2 * 64) * 4
+    assert api.la_chunk_fwd_varlen_workspace_bytes(d, 1501, 64) == 0   # invalid
+    assert _varlen(d, max_seqlen=1000, ws=None) == api.LA_ERR_INVALID
+    assert _varlen(d, max_seqlen=1000, ws=A, ws_bytes=need - 16) == api.LA_ERR_INVALID
