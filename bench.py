@@ -18,6 +18,9 @@ Also reported, in the same line:
 * ``backward``: the chunkwise backward of the same prefill (dq, dk, dv,
   log-gate gradient and dS0 from seeded dout), per-kernel times and the
   roofline of the per-chunk gradient kernel.
+* ``varlen``: the packed-sequence prefill of ``gla_varlen_32seq_H16_d128``
+  (32 sequences, seeded lengths in [1, 4096]) and one decode step of all of
+  them from their final states.
 * ``cpu_baseline``: the fp64 oracle (test infrastructure, untuned) on the
   same prefill workload drawn on the host, timed on this machine's cores.
 
@@ -28,6 +31,7 @@ from __future__ import annotations
 import argparse
 import ctypes
 import hashlib
+import itertools
 import json
 import math
 import os
@@ -58,6 +62,16 @@ def decode_source_hash():
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "recurrent_attention_amd", "csrc")
     for f in ("decode_kernel.hip", "la_device.h", "la_internal.h"):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def bwd_source_hash():
+    """Hash of the sources the per-chunk gradient kernel is built from."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "recurrent_attention_amd", "csrc")
+    for f in ("bwd_kernel.h", "la_device.h", "la_internal.h", "bwd_bf16_d128.hip"):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
@@ -223,8 +237,87 @@ def bench_backward(args, torch, api, workloads):
         "kernels_avg_us": kern,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None, "kernel": "chunk_bwd", "bytes_per_launch": kb,
+                     "traffic": measured_traffic(f"chunk_bwd_{w.name}", bwd_source_hash()),
+                     "kernel": "chunk_bwd", "bytes_per_launch": kb,
                      "avg_launch_us": bw_us},
+    }
+
+
+def bench_varlen(args, torch, api, workloads):
+    """Packed-sequence prefill of the varlen workload, then one decode step
+    of every sequence from its S_final (the hand-off)."""
+    spec = workloads.VARLEN_SPEC
+    lens = workloads.varlen_lengths(spec["n"], spec["lo"], spec["hi"], spec["seed"])
+    N, H, d, chunk = len(lens), spec["H"], spec["d"], spec["chunk"]
+    T, maxlen = sum(lens), max(lens)
+    dev = torch.device("cuda", 0)
+    inp = workloads.prefill_inputs(1, H, T, d, d, torch.bfloat16, workloads.GATE_DIAG, seed=0,
+                                   device=dev)
+    q, k, v, la = inp["q"], inp["k"], inp["v"], inp["log_alpha"]
+    cu = torch.tensor([0] + list(itertools.accumulate(lens)), dtype=torch.int32,
+                      device=dev)
+    desc = api.make_desc(N, H, T, d, d, api.LA_BF16, 0, False, 0)
+    need = api.la_chunk_fwd_varlen_workspace_bytes(desc, maxlen, chunk)
+    out = torch.empty_like(v)
+    S = torch.empty((N, H, d, d), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(need // 4, 1), dtype=torch.float32, device=dev)
+    sp = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    lib = api.load_library()
+    argv = (ctypes.byref(desc), cu.data_ptr(), maxlen, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+            2, la.data_ptr(), None, None, chunk, out.data_ptr(), S.data_ptr(), None,
+            ws.data_ptr(), need, sp)
+
+    def step():
+        st = lib.la_chunk_fwd_varlen(*argv)
+        if st != 0:
+            raise RuntimeError(api.la_last_error_message())
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    api.la_profile_begin()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    api.la_profile_end()
+    kern = {}
+    for name in ("chunk_main", "chunk_state", "state_scan"):
+        n, ms = api.la_profile_query(name)
+        kern[name] = round(ms / n * 1e3, 2) if n else None
+    # hand-off: one decode step of all N sequences from their prefill states
+    qd, kd, vd, lad = workloads.decode_tokens(N, H, d, d, 1, seed=1, device=dev, gate=True)
+    od = torch.empty((N, H, d), dtype=torch.bfloat16, device=dev)
+    ddesc = api.make_desc(N, H, 1, d, d, api.LA_BF16, 0, False, 0)
+    st = lib.la_decode_step(ctypes.byref(ddesc), qd[0].data_ptr(), kd[0].data_ptr(),
+                            vd[0].data_ptr(), 2, lad[0].data_ptr(), S.data_ptr(), None,
+                            od.data_ptr(), sp)
+    if st != 0:
+        raise RuntimeError(api.la_last_error_message())
+    torch.cuda.synchronize()
+    ms_step = elapsed / args.steps * 1e3
+    per_th = 2 * (3 * d) + 4 * d + 2 * d          # q, k, v, log-gates in; out
+    alg = H * T * per_th + N * H * d * d * 4
+    main_us = kern["chunk_main"]
+    achieved = alg / (main_us * 1e-6) / 1e9
+    return {
+        "workload": workloads.VARLEN_HEADLINE, "sequences": N, "tokens": T, "max_seqlen": maxlen,
+        "segments": api.la_chunk_fwd_segments(api.make_desc(N, H, maxlen, d, d, api.LA_BF16,
+                                                            0, False, 0), chunk),
+        "ms_per_step": round(ms_step, 4), "tokens_per_s": round(T / (ms_step * 1e-3), 1),
+        "algorithmic_bytes": alg,
+        "pct_of_hbm_peak_step": round(100.0 * alg / (ms_step * 1e-3) / (HBM_PEAK_GBS * 1e9), 2),
+        "kernels_avg_us": kern,
+        "decode_hand_off_finite": bool(torch.isfinite(od.float()).all().item()),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(f"chunk_main_{workloads.VARLEN_HEADLINE}",
+                                                 kernel_source_hash()),
+                     "kernel": "chunk_main", "bytes_per_launch": alg, "avg_launch_us": main_us},
     }
 
 
@@ -325,8 +418,9 @@ def main(argv=None):
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-varlen", action="store_true")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
-    ap.add_argument("--only", choices=["prefill", "decode", "backward", "copy"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "backward", "varlen", "copy"], default=None,
                     help="run one part only (copy: a 1 GiB device copy used to scale "
                          "rocprofv3 byte counters); prints no metric line")
     args = ap.parse_args(argv)
@@ -354,6 +448,9 @@ def main(argv=None):
     if args.only == "backward":
         print(json.dumps(bench_backward(args, torch, api, workloads)), flush=True)
         return 0
+    if args.only == "varlen":
+        print(json.dumps(bench_varlen(args, torch, api, workloads)), flush=True)
+        return 0
     if args.only == "prefill":
         pre = bench_prefill(args, torch, api, workloads)
         print(json.dumps({"ms_per_step": pre["ms_step"], "kernels": pre["kernels"],
@@ -362,6 +459,7 @@ def main(argv=None):
     pre = bench_prefill(args, torch, api, workloads)
     dec = None if args.no_decode else bench_decode(args, torch, api, workloads)
     bwd = None if args.no_backward else bench_backward(args, torch, api, workloads)
+    vl = None if args.no_varlen else bench_varlen(args, torch, api, workloads)
     w = pre["w"]
     line = {
         "metric": METRIC,
@@ -391,6 +489,8 @@ def main(argv=None):
         line["decode"] = dec
     if bwd is not None:
         line["backward"] = bwd
+    if vl is not None:
+        line["varlen"] = vl
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(workloads, w)
     print(json.dumps(line), flush=True)

@@ -22,10 +22,14 @@ import re
 import sys
 from collections import defaultdict
 
+# chunk_kernel<ChunkCfg<dk, dv, C, bf16, gate, state-only, waves>, elu1, reversed, store>
+_CHUNK = r"la::chunk_kernel<la::ChunkCfg<\d+, \d+, \d+, \w+, \d, {so}(, \d+)?>, \w+{tail}"
 FAMILIES = [
-    ("chunk_main", re.compile(r"la::chunk_kernel<la::ChunkCfg<(\d+), (\d+), (\d+), (\w+), (\d), false(, \d+)?>")),
-    ("chunk_state", re.compile(r"la::chunk_kernel<la::ChunkCfg<(\d+), (\d+), (\d+), (\w+), (\d), true(, \d+)?>")),
+    ("chunk_main", re.compile(_CHUNK.format(so="false", tail=""))),
+    ("chunk_store", re.compile(_CHUNK.format(so="true", tail=r", \w+, true>"))),
+    ("chunk_state", re.compile(_CHUNK.format(so="true", tail=r"(, \w+, false)?>"))),
     ("state_scan", re.compile(r"la::state_scan_kernel")),
+    ("chunk_bwd", re.compile(r"la::bwd_kernel")),
     ("decode", re.compile(r"la::decode_kernel")),
     ("copy", re.compile(r"__amd_rocclr_copyBuffer")),
 ]

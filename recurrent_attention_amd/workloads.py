@@ -21,6 +21,9 @@ name                                   contents
 ``decode_retention_256x32_d128``       256 sequences x 32 heads, d=128, fp32
                                        S ~ N(0,1), one bf16 token per step,
                                        gamma = 0.97, 1000 steps
+``gla_varlen_32seq_H16_d128``          32 packed sequences, lengths uniform
+                                       in [1, 4096] (seed 7), H=16, d=128,
+                                       bf16, GLA gates as above, C=64
 =====================================  ======================================
 
 Draw order for prefill workloads: one ``torch.Generator`` seeded with
@@ -89,6 +92,14 @@ WORKLOADS = {
 
 PREFILL_HEADLINE = "gla_B1H16_L32768_d128"
 DECODE_HEADLINE = "decode_retention_256x32_d128"
+VARLEN_HEADLINE = "gla_varlen_32seq_H16_d128"
+VARLEN_SPEC = {"n": 32, "lo": 1, "hi": 4096, "seed": 7, "H": 16, "d": 128, "chunk": 64}
+
+
+def varlen_lengths(n, lo, hi, seed):
+    """Seeded sequence lengths: n integers uniform in [lo, hi]."""
+    gen = generator(seed)
+    return torch.randint(lo, hi + 1, (n,), generator=gen).tolist()
 
 
 def generator(seed: int, device="cpu") -> torch.Generator:
