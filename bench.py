@@ -21,6 +21,8 @@ Also reported, in the same line:
 * ``varlen``: the packed-sequence prefill of ``gla_varlen_32seq_H16_d128``
   (32 sequences, seeded lengths in [1, 4096]) and one decode step of all of
   them from their final states.
+* ``scalar_gate``: the same prefill with one gate per token and head
+  (``scalar_gate_B1H16_L32768_d128``), which drops the d_k-wide gate stream.
 * ``cpu_baseline``: the fp64 oracle (test infrastructure, untuned) on the
   same prefill workload drawn on the host, timed on this machine's cores.
 
@@ -92,8 +94,10 @@ def measured_traffic(name, src_hash):
 
 def prefill_bytes(w):
     """Algorithmic bytes of one prefill: q, k, v, out in bf16 (+ fp32 log
-    gates) per token-head, plus the fp32 final state per (b,h)."""
-    per_th = 2 * (2 * w.dk + w.dv) + 2 * w.dv + (4 * w.dk if w.gate_mode == 2 else 0)
+    gates: d_k per token-head for the diagonal gate, one for the scalar
+    gate) per token-head, plus the fp32 final state per (b,h)."""
+    gate = {2: 4 * w.dk, 3: 4}.get(w.gate_mode, 0)
+    per_th = 2 * (2 * w.dk + w.dv) + 2 * w.dv + gate
     return w.B * w.H * w.L * per_th + w.B * w.H * w.dk * w.dv * 4
 
 
@@ -102,8 +106,8 @@ def prefill_flops(w):
     return w.B * w.H * w.L * (2 * w.chunk * (w.dk + w.dv) + 4 * w.dk * w.dv)
 
 
-def bench_prefill(args, torch, api, workloads):
-    w = workloads.WORKLOADS[workloads.PREFILL_HEADLINE]
+def bench_prefill(args, torch, api, workloads, name=None):
+    w = workloads.WORKLOADS[name or workloads.PREFILL_HEADLINE]
     dev = torch.device("cuda", 0)
     inp = workloads.workload_inputs(w.name, seed=0, device=dev)
     q, k, v, la = inp["q"], inp["k"], inp["v"], inp["log_alpha"]
@@ -419,8 +423,9 @@ def main(argv=None):
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-varlen", action="store_true")
+    ap.add_argument("--no-scalar", action="store_true")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
-    ap.add_argument("--only", choices=["prefill", "decode", "backward", "varlen", "copy"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "backward", "varlen", "scalar", "copy"], default=None,
                     help="run one part only (copy: a 1 GiB device copy used to scale "
                          "rocprofv3 byte counters); prints no metric line")
     args = ap.parse_args(argv)
@@ -451,6 +456,11 @@ def main(argv=None):
     if args.only == "varlen":
         print(json.dumps(bench_varlen(args, torch, api, workloads)), flush=True)
         return 0
+    if args.only == "scalar":
+        sc = bench_prefill(args, torch, api, workloads, "scalar_gate_B1H16_L32768_d128")
+        print(json.dumps({"ms_per_step": sc["ms_step"], "kernels": sc["kernels"],
+                          "roofline": sc["roofline"]}), flush=True)
+        return 0
     if args.only == "prefill":
         pre = bench_prefill(args, torch, api, workloads)
         print(json.dumps({"ms_per_step": pre["ms_step"], "kernels": pre["kernels"],
@@ -460,6 +470,8 @@ def main(argv=None):
     dec = None if args.no_decode else bench_decode(args, torch, api, workloads)
     bwd = None if args.no_backward else bench_backward(args, torch, api, workloads)
     vl = None if args.no_varlen else bench_varlen(args, torch, api, workloads)
+    sc = None if args.no_scalar else bench_prefill(args, torch, api, workloads,
+                                                   "scalar_gate_B1H16_L32768_d128")
     w = pre["w"]
     line = {
         "metric": METRIC,
@@ -491,6 +503,14 @@ def main(argv=None):
         line["backward"] = bwd
     if vl is not None:
         line["varlen"] = vl
+    if sc is not None:
+        line["scalar_gate"] = {
+            "workload": sc["w"].name, "ms_per_step": round(sc["ms_step"], 4),
+            "tokens_per_s": round(sc["tokens_per_s"], 1),
+            "pct_of_bf16_mfma_peak": round(sc["mfma_pct"], 3),
+            "kernels_avg_us": {k: (round(v["avg_us"], 2) if v["avg_us"] else None)
+                               for k, v in sc["kernels"].items()},
+            "roofline": sc["roofline"]}
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(workloads, w)
     print(json.dumps(line), flush=True)

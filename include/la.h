@@ -12,9 +12,11 @@
  *     o_t = phi(q_t) S_t   [ / (phi(q_t) . z_t) ]  read after the update
  *
  * with the gate A_t = 1 (linear attention), a per-head scalar gamma
- * (retention, section "Retention: Add a Decay to the State") or a diagonal
+ * (retention, section "Retention: Add a Decay to the State"), a diagonal
  * d_k x d_k gate exp(log_alpha_t) (gated linear attention, the
- * input-dependent row of the gate table).  Under a gate, z is decayed by the
+ * input-dependent row of the gate table) or an input-dependent scalar gate
+ * exp(log_alpha_t) I per token and head (the same row with one gate value,
+ * as in the section's scalar demonstration gate).  Under a gate, z is decayed by the
  * same A_t as S.  There is no epsilon in the divide.
  *
  * la_chunk_fwd computes a whole prefill in the chunkwise-parallel form
@@ -31,7 +33,8 @@
  *      q, k  [B,H,L,dk]   v, out [B,H,L,dv]   (dtype of la_desc.dtype)
  *      S     [B,H,dk,dv]  fp32, rows indexed by the key channel
  *      z     [B,H,dk]     fp32
- *      log_alpha [B,H,L,dk] fp32 natural-log gates, every value <= 0
+ *      log_alpha [B,H,L,dk] (DIAG) or [B,H,L] (SCALAR) fp32 natural-log
+ *                gates, every value <= 0
  *  - Device pointers are device (HBM) addresses; `gamma` is a host array.
  *  - The caller owns every buffer.  The library never allocates device
  *    memory, frees or synchronises; work is enqueued on `stream` (a
@@ -66,7 +69,9 @@ typedef enum la_status {
 typedef enum la_gate_mode {
     LA_GATE_NONE = 0,  /* A_t = 1                                          */
     LA_GATE_GAMMA = 1, /* A_t = gamma[h]; host float[H], 0 <= gamma <= 1     */
-    LA_GATE_DIAG = 2   /* A_t = diag(exp(log_alpha[b,h,t,:])); device fp32   */
+    LA_GATE_DIAG = 2,  /* A_t = diag(exp(log_alpha[b,h,t,:])); device fp32   */
+    LA_GATE_SCALAR = 3 /* A_t = exp(log_alpha[b,h,t]) I; device fp32, one
+                          gate per token and head                          */
 } la_gate_mode;
 
 typedef enum la_dtype { LA_F32 = 0, LA_BF16 = 1 } la_dtype;
@@ -107,7 +112,8 @@ typedef struct la_desc {
  *   q, k, v            device, [B,H,L,dk|dv] of d->dtype, read only
  *   gate_mode          la_gate_mode
  *   gamma_or_log_alpha NONE: ignored (may be NULL); GAMMA: host float[H];
- *                      DIAG: device float[B,H,L,dk]
+ *                      DIAG: device float[B,H,L,dk]; SCALAR: device
+ *                      float[B,H,L]
  *   S0, z0             device fp32 initial state [B,H,dk,dv] and [B,H,dk];
  *                      NULL = zeros.  z0 must be NULL unless normalize.
  *   chunk              chunk length C (see supported shapes)
@@ -145,7 +151,7 @@ la_status la_chunk_fwd(const la_desc* d, const void* q, const void* k,
  *   max_seqlen   host int, 1 <= max_seqlen <= T: the longest sequence
  *   q, k         device [H,T,dk] (a [1,H,T,dk] tensor) of d->dtype
  *   v, out       device [H,T,dv]
- *   log_alpha    DIAG: device fp32 [H,T,dk]
+ *   log_alpha    DIAG: device fp32 [H,T,dk]; SCALAR: [H,T]
  *   S0, S_final  device fp32 [B,H,dk,dv] per sequence (NULL as before)
  *   z0, z_final  device fp32 [B,H,dk]
  *   workspace    la_chunk_fwd_varlen_workspace_bytes(d, max_seqlen, chunk)
@@ -194,8 +200,9 @@ int la_chunk_fwd_segments(const la_desc* d, int chunk);
  *   dS_final           device fp32 [B,H,dk,dv] gradient of S_final, or NULL
  *   dq, dk, dv         device [B,H,L,dk|dv] of d->dtype, written: gradients
  *                      of the raw q, k (through phi) and v
- *   dlog_alpha         DIAG: device fp32 [B,H,L,dk], written; must be NULL
- *                      for the other gates (gamma gets no gradient)
+ *   dlog_alpha         DIAG: device fp32 [B,H,L,dk], SCALAR: [B,H,L],
+ *                      written; must be NULL for the other gates (gamma
+ *                      gets no gradient)
  *   dS0                device fp32 [B,H,dk,dv] gradient of S0, written, or
  *                      NULL (not returned)
  *   workspace          device scratch of at least
@@ -226,7 +233,7 @@ int la_chunk_bwd_chunk(const la_desc* d);
  *   q, k, v    device [B,H,dk|dv] of d->dtype
  *   gate_mode  la_gate_mode
  *   gate       NONE: ignored; GAMMA: host float[H]; DIAG: device fp32
- *              log-gates [B,H,dk]
+ *              log-gates [B,H,dk]; SCALAR: device fp32 [B,H]
  *   S          device fp32 [B,H,dk,dv], updated in place to A S + phi(k) v^T
  *   z          device fp32 [B,H,dk], updated in place; NULL iff !normalize
  *   out        device [B,H,dv] of d->dtype: phi(q)^T S_new [/ phi(q).z_new]

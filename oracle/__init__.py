@@ -16,8 +16,14 @@ Forms (all compute the same function; see ``oracle.c`` for the citations):
 
 Layouts follow the GPU boundary: q, k ``[B,H,L,dk]``, v and out
 ``[B,H,L,dv]``, S ``[B,H,dk,dv]`` (rows indexed by the key channel), z
-``[B,H,dk]``, gamma ``[H]``, log_alpha ``[B,H,L,dk]``.  2-D ``[L,d]`` inputs
-are treated as B = H = 1.
+``[B,H,dk]``, gamma ``[H]``, log_alpha ``[B,H,L,dk]`` (diagonal gate) or
+``[B,H,L]`` (scalar gate).  2-D ``[L,d]`` inputs are treated as B = H = 1.
+
+The per-token scalar gate A_t = alpha_t I is, by definition, the diagonal
+gate with every channel equal: its log-gate is repeated over the key
+channels and run as the diagonal gate, and its gradient is the sum of the
+diagonal gate's gradient over those channels (the chain rule of the
+repetition).
 
 Parity: every form is pinned by tests that do not call the oracle's own
 formula (the pages' worked examples, closed forms, textbook masked matmuls,
@@ -32,7 +38,7 @@ import subprocess
 
 import numpy as np
 
-GATE_NONE, GATE_GAMMA, GATE_DIAG = 0, 1, 2
+GATE_NONE, GATE_GAMMA, GATE_DIAG, GATE_SCALAR = 0, 1, 2, 3
 PHI_IDENTITY, PHI_ELU1 = 0, 1
 
 # Planted mistakes (test-only), mirrored from oracle.c.
@@ -124,6 +130,11 @@ def _prep(q, k, v, gate_mode, gamma, log_alpha, S0, z0):
         if two_d and la.ndim == 2:
             la = la[None, None]
         la = np.ascontiguousarray(np.broadcast_to(la, (B, H, L, dk)))
+    elif gate_mode == GATE_SCALAR:
+        la = _f64(log_alpha)
+        if two_d and la.ndim == 1:
+            la = la[None, None]
+        la = np.ascontiguousarray(np.broadcast_to(la.reshape(B, H, L)[..., None], (B, H, L, dk)))
     elif gate_mode != GATE_NONE:
         raise ValueError("unknown gate mode")
     S0 = _f64(S0)
@@ -148,7 +159,8 @@ def _call(fn, extra_mid, extra_tail, q, k, v, gate_mode, gamma, log_alpha,
     out = np.zeros((B, H, L, dv))
     S = np.zeros((B, H, dk, dv))
     z = np.zeros((B, H, dk))
-    args = [B, H, L, dk, dv, int(gate_mode), _ptr(g), _ptr(la), int(phi),
+    cmode = GATE_DIAG if gate_mode == GATE_SCALAR else int(gate_mode)
+    args = [B, H, L, dk, dv, cmode, _ptr(g), _ptr(la), int(phi),
             int(bool(normalize)), _ptr(q), _ptr(k), _ptr(v), _ptr(S0), _ptr(z0)]
     args += extra_mid + [_ptr(out), _ptr(S), _ptr(z)] + extra_tail
     rc = fn(*args)
@@ -188,8 +200,9 @@ def backward(q, k, v, dout, gate_mode=GATE_NONE, gamma=None, log_alpha=None,
     ``dout`` is the gradient of the loss with respect to ``out`` and
     ``dS_final`` (optional) with respect to the final state.  Returns a dict
     with ``dq``, ``dk``, ``dv`` (fp64, the layouts of q, k, v), ``dlog_alpha``
-    (diagonal gate only, else None) and ``dS0`` ``[B,H,dk,dv]`` (the
-    gradient of the initial state, zero-state runs included).
+    (diagonal and scalar gates, in the layout of log_alpha, else None) and
+    ``dS0`` ``[B,H,dk,dv]`` (the gradient of the initial state, zero-state
+    runs included).
     """
     lib = _load()
     two_d, (B, H, L, dk, dv), q, k, v, g, la, S0, _ = _prep(
@@ -202,14 +215,17 @@ def backward(q, k, v, dout, gate_mode=GATE_NONE, gamma=None, log_alpha=None,
     dq = np.zeros((B, H, L, dk))
     dk_ = np.zeros((B, H, L, dk))
     dv_ = np.zeros((B, H, L, dv))
-    dla = np.zeros((B, H, L, dk)) if gate_mode == GATE_DIAG else None
+    dla = np.zeros((B, H, L, dk)) if gate_mode in (GATE_DIAG, GATE_SCALAR) else None
     dS0 = np.zeros((B, H, dk, dv))
-    rc = lib.oracle_backward(B, H, L, dk, dv, int(gate_mode), _ptr(g), _ptr(la), int(phi),
+    cmode = GATE_DIAG if gate_mode == GATE_SCALAR else int(gate_mode)
+    rc = lib.oracle_backward(B, H, L, dk, dv, cmode, _ptr(g), _ptr(la), int(phi),
                              _ptr(q), _ptr(k), _ptr(v), _ptr(S0), _ptr(do), _ptr(dSf),
                              _ptr(dq), _ptr(dk_), _ptr(dv_), _ptr(dla), _ptr(dS0),
                              int(checkpoint), int(nthreads))
     if rc != 0:
         raise ValueError(f"oracle rejected its arguments (rc={rc})")
+    if gate_mode == GATE_SCALAR:
+        dla = dla.sum(axis=-1)
     res = {"dq": dq, "dk": dk_, "dv": dv_, "dlog_alpha": dla, "dS0": dS0}
     if two_d:
         res = {n: (a[0, 0] if a is not None else None) for n, a in res.items()}

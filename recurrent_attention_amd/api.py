@@ -16,7 +16,7 @@ import ctypes
 import os
 
 LA_OK, LA_ERR_INVALID, LA_ERR_UNSUPPORTED, LA_ERR_HIP = 0, 1, 2, 3
-LA_GATE_NONE, LA_GATE_GAMMA, LA_GATE_DIAG = 0, 1, 2
+LA_GATE_NONE, LA_GATE_GAMMA, LA_GATE_DIAG, LA_GATE_SCALAR = 0, 1, 2, 3
 LA_F32, LA_BF16 = 0, 1
 LA_PHI_IDENTITY, LA_PHI_ELU1 = 0, 1
 LA_MAX_GAMMA_HEADS = 256
@@ -273,8 +273,9 @@ def chunk_fwd(q, k, v, gate_mode=LA_GATE_NONE, gamma=None, log_alpha=None,
     if gate_mode == LA_GATE_GAMMA:
         g_keep = _gamma_host(gamma, H)
         g_arg = ctypes.c_void_p(g_keep.data_ptr())
-    elif gate_mode == LA_GATE_DIAG:
-        g_arg = _dev_ptr(log_alpha, "log_alpha", torch.float32, (B, H, L, dk))
+    elif gate_mode in (LA_GATE_DIAG, LA_GATE_SCALAR):
+        g_arg = _dev_ptr(log_alpha, "log_alpha", torch.float32,
+                         (B, H, L, dk) if gate_mode == LA_GATE_DIAG else (B, H, L))
     st = la_chunk_fwd(
         desc, _dev_ptr(q, "q"), _dev_ptr(k, "k", q.dtype, (B, H, L, dk)),
         _dev_ptr(v, "v", q.dtype, (B, H, L, dv)),
@@ -305,8 +306,9 @@ def decode_step(q, k, v, S, z=None, gate_mode=LA_GATE_NONE, gamma=None,
     if gate_mode == LA_GATE_GAMMA:
         g_keep = _gamma_host(gamma, H)
         g_arg = ctypes.c_void_p(g_keep.data_ptr())
-    elif gate_mode == LA_GATE_DIAG:
-        g_arg = _dev_ptr(log_alpha, "log_alpha", torch.float32, (B, H, dk))
+    elif gate_mode in (LA_GATE_DIAG, LA_GATE_SCALAR):
+        g_arg = _dev_ptr(log_alpha, "log_alpha", torch.float32,
+                         (B, H, dk) if gate_mode == LA_GATE_DIAG else (B, H))
     st = la_decode_step(
         desc, _dev_ptr(q, "q"), _dev_ptr(k, "k", q.dtype, (B, H, dk)),
         _dev_ptr(v, "v", q.dtype, (B, H, dv)),
@@ -331,7 +333,7 @@ def chunk_fwd_varlen(q, k, v, cu_seqlens, max_seqlen=None, gate_mode=LA_GATE_NON
     torch = _torch()
     if q.dim() == 3:
         q, k, v = q[None], k[None], v[None]
-        if log_alpha is not None and log_alpha.dim() == 3:
+        if log_alpha is not None and log_alpha.dim() == (3 if gate_mode == LA_GATE_DIAG else 2):
             log_alpha = log_alpha[None]
     one, H, T, dk = q.shape
     if one != 1:
@@ -363,8 +365,9 @@ def chunk_fwd_varlen(q, k, v, cu_seqlens, max_seqlen=None, gate_mode=LA_GATE_NON
     if gate_mode == LA_GATE_GAMMA:
         g_keep = _gamma_host(gamma, H)
         g_arg = ctypes.c_void_p(g_keep.data_ptr())
-    elif gate_mode == LA_GATE_DIAG:
-        g_arg = _dev_ptr(log_alpha, "log_alpha", torch.float32, (1, H, T, dk))
+    elif gate_mode in (LA_GATE_DIAG, LA_GATE_SCALAR):
+        g_arg = _dev_ptr(log_alpha, "log_alpha", torch.float32,
+                         (1, H, T, dk) if gate_mode == LA_GATE_DIAG else (1, H, T))
     st = la_chunk_fwd_varlen(
         desc, _dev_ptr(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,)), max_seqlen,
         _dev_ptr(q, "q"), _dev_ptr(k, "k", q.dtype, (1, H, T, dk)),
@@ -385,8 +388,9 @@ def chunk_bwd(q, k, v, dout, gate_mode=LA_GATE_NONE, gamma=None, log_alpha=None,
               workspace=None, stream=None):
     """Gradients of :func:`chunk_fwd` (no normaliser) for the loss
     ``sum(dout * out) + sum(dS_final * S_final)``.  Returns a dict with
-    ``dq``, ``dk``, ``dv`` (dtype of q), ``dlog_alpha`` (fp32, DIAG gate
-    only, else None) and ``dS0`` (fp32)."""
+    ``dq``, ``dk``, ``dv`` (dtype of q), ``dlog_alpha`` (fp32, DIAG and
+    SCALAR gates, in the layout of log_alpha, else None) and ``dS0``
+    (fp32)."""
     torch = _torch()
     B, H, L, dk = q.shape
     dv = v.shape[-1]
@@ -397,8 +401,11 @@ def chunk_bwd(q, k, v, dout, gate_mode=LA_GATE_NONE, gamma=None, log_alpha=None,
     dkk = torch.empty((B, H, L, dk), dtype=q.dtype, device=dev)
     dvv = torch.empty((B, H, L, dv), dtype=q.dtype, device=dev)
     dS0 = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
-    dla = (torch.empty((B, H, L, dk), dtype=torch.float32, device=dev)
-           if gate_mode == LA_GATE_DIAG else None)
+    dla = None
+    if gate_mode == LA_GATE_DIAG:
+        dla = torch.empty((B, H, L, dk), dtype=torch.float32, device=dev)
+    elif gate_mode == LA_GATE_SCALAR:
+        dla = torch.empty((B, H, L), dtype=torch.float32, device=dev)
     need = la_chunk_bwd_workspace_bytes(desc)
     if workspace is None and need:
         workspace = torch.empty(need // 4 + 4, dtype=torch.float32, device=dev)
@@ -408,8 +415,9 @@ def chunk_bwd(q, k, v, dout, gate_mode=LA_GATE_NONE, gamma=None, log_alpha=None,
     if gate_mode == LA_GATE_GAMMA:
         g_keep = _gamma_host(gamma, H)
         g_arg = ctypes.c_void_p(g_keep.data_ptr())
-    elif gate_mode == LA_GATE_DIAG:
-        g_arg = _dev_ptr(log_alpha, "log_alpha", torch.float32, (B, H, L, dk))
+    elif gate_mode in (LA_GATE_DIAG, LA_GATE_SCALAR):
+        g_arg = _dev_ptr(log_alpha, "log_alpha", torch.float32,
+                         (B, H, L, dk) if gate_mode == LA_GATE_DIAG else (B, H, L))
     st = la_chunk_bwd(
         desc, _dev_ptr(q, "q"), _dev_ptr(k, "k", q.dtype, (B, H, L, dk)),
         _dev_ptr(v, "v", q.dtype, (B, H, L, dv)), _dev_ptr(dout, "dout", q.dtype, (B, H, L, dv)),

@@ -76,6 +76,7 @@ struct BwdSmem {
     alignas(16) E pt[Cfg::C][Cfg::C];     // P^T  [s][swizzled t]
     alignas(16) E dpt[Cfg::C][Cfg::C];    // dP^T [s][swizzled t]
     alignas(16) E gs[Cfg::D][Cfg::D];     // Gs   [i][swizzled n]
+    float red[Cfg::NW][Cfg::C];           // per-wave token sums (scalar gate)
     alignas(16) float ebr[Cfg::D];        // e^{B - r} per channel (DIAG)
     float gpow[Cfg::C + 2];               // gamma^j
 };
@@ -178,6 +179,8 @@ __global__ __launch_bounds__(Cfg::NT) void bwd_kernel(const BwdParams p) {
     using E = typename Cfg::E;
     using Frag = typename Cfg::Frag;
     constexpr float kLog2e = 1.4426950408889634f;
+    // the diagonal and the per-token scalar gate share one path
+    constexpr bool VG = GATE == LA_GATE_DIAG || GATE == LA_GATE_SCALAR;
     // 16-byte units of G each thread copies into LDS
     constexpr int GU = D * D / UE / Cfg::NT;
     static_assert(GU * UE * Cfg::NT == D * D, "G copy mapping");
@@ -201,21 +204,25 @@ __global__ __launch_bounds__(Cfg::NT) void bwd_kernel(const BwdParams p) {
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(reinterpret_cast<const E*>(p.v) + rows0 * D, (uint32_t)L * D * ES);
     const __amdgpu_buffer_rsrc_t rdo = make_rsrc(reinterpret_cast<const E*>(p.dout) + rows0 * D, (uint32_t)L * D * ES);
     const __amdgpu_buffer_rsrc_t rla =
-        make_rsrc(GATE == LA_GATE_DIAG ? (const void*)(p.log_alpha + rows0 * D) : p.q,
-                  GATE == LA_GATE_DIAG ? (uint32_t)L * D * 4 : 0u);
+        make_rsrc(GATE == LA_GATE_DIAG ? (const void*)(p.log_alpha + rows0 * D)
+                  : GATE == LA_GATE_SCALAR ? (const void*)(p.log_alpha + rows0) : p.q,
+                  GATE == LA_GATE_DIAG ? (uint32_t)L * D * 4
+                  : GATE == LA_GATE_SCALAR ? (uint32_t)L * 4 : 0u);
     const __amdgpu_buffer_rsrc_t rdq = make_rsrc(reinterpret_cast<E*>(p.dq) + rows0 * D, (uint32_t)L * D * ES);
     const __amdgpu_buffer_rsrc_t rdk = make_rsrc(reinterpret_cast<E*>(p.dk) + rows0 * D, (uint32_t)L * D * ES);
     const __amdgpu_buffer_rsrc_t rdv = make_rsrc(reinterpret_cast<E*>(p.dv) + rows0 * D, (uint32_t)L * D * ES);
     const __amdgpu_buffer_rsrc_t rdla =
-        make_rsrc(GATE == LA_GATE_DIAG ? (void*)(p.dlog_alpha + rows0 * D) : p.dq,
-                  GATE == LA_GATE_DIAG ? (uint32_t)L * D * 4 : 0u);
+        make_rsrc(GATE == LA_GATE_DIAG ? (void*)(p.dlog_alpha + rows0 * D)
+                  : GATE == LA_GATE_SCALAR ? (void*)(p.dlog_alpha + rows0) : p.dq,
+                  GATE == LA_GATE_DIAG ? (uint32_t)L * D * 4
+                  : GATE == LA_GATE_SCALAR ? (uint32_t)L * 4 : 0u);
     const E* Sc = reinterpret_cast<const E*>(p.st_fwd) + ((size_t)bh * (p.nchunks + 1) + c) * D * D;
     const E* Gc = reinterpret_cast<const E*>(p.st_rows) + ((size_t)bh * p.nchunks + c) * D * D;
 
     // ---- loads: per owned token, one 4-channel run of q, k, v, dO (and
     // gates); the state gradient G in 16-byte units
     Words<RW> qr[TB], kr[TB], vr[TB], dr[TB];
-    Words<4> lar[GATE == LA_GATE_DIAG ? TB : 1];
+    Words<4> lar[VG ? TB : 1];
     uint4 gw[GU];
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) {
@@ -226,6 +233,10 @@ __global__ __launch_bounds__(Cfg::NT) void bwd_kernel(const BwdParams p) {
         vr[tb] = buf_load_words<RW>(rv, off);
         dr[tb] = buf_load_words<RW>(rdo, off);
         if constexpr (GATE == LA_GATE_DIAG) lar[tb] = buf_load_words<4>(rla, (row * D + ch0) * 4);
+        if constexpr (GATE == LA_GATE_SCALAR) {
+            const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(rla, row * 4, 0, 0);
+            lar[tb] = Words<4>{{w, w, w, w}};
+        }
     }
 #pragma unroll
     for (int j = 0; j < GU; ++j) gw[j] = reinterpret_cast<const uint4*>(Gc)[tid + j * Cfg::NT];
@@ -263,7 +274,7 @@ __global__ __launch_bounds__(Cfg::NT) void bwd_kernel(const BwdParams p) {
             fq[tb][i] = fk[tb][i] = 1.f;
         }
     }
-    if constexpr (GATE == LA_GATE_DIAG) {
+    if constexpr (VG) {
         // inclusive prefix over the chunk's tokens: within each 16-token block
         // across the lanes of a row, then the earlier blocks' totals
         float b[TB][4];
@@ -321,7 +332,7 @@ __global__ __launch_bounds__(Cfg::NT) void bwd_kernel(const BwdParams p) {
         const int u = tid + j * Cfg::NT;
         const int row = u / DU, col = (u % DU) * UE;
         uint4 w = gw[j];
-        if constexpr (GATE == LA_GATE_DIAG) {
+        if constexpr (VG) {
             const float f = sm.ebr[row];
             if constexpr (BF16) {
                 w.x = pack_bf16(bf16lo(w.x) * f, bf16hi(w.x) * f);
@@ -384,7 +395,7 @@ __global__ __launch_bounds__(Cfg::NT) void bwd_kernel(const BwdParams p) {
 #pragma unroll
         for (int kk = 0; kk < D / MK; ++kk) {
             const Frag a = mem_frag<Cfg>(Sc, D, 16 * nb, kk * MK, lane);
-            if constexpr (GATE == LA_GATE_DIAG) {
+            if constexpr (VG) {
                 float xs[KPL], xg[KPL];
                 frag_floats<Cfg>(a, xs);
                 frag_floats<Cfg>(row_frag<Cfg, DM>(&sm.gs[0][0], D, 16 * nb, kk * MK, lane), xg);
@@ -428,7 +439,7 @@ __global__ __launch_bounds__(Cfg::NT) void bwd_kernel(const BwdParams p) {
         }
 #pragma unroll
         for (int sb = 0; sb < TB; ++sb) {
-            if constexpr (GATE == LA_GATE_DIAG) {
+            if constexpr (VG) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) kgv[i] += acc[sb][i] * (kf[sb][i] * fk[sb][i]);
             }
@@ -494,7 +505,7 @@ __global__ __launch_bounds__(Cfg::NT) void bwd_kernel(const BwdParams p) {
         buf_store_run4<BF16>(rdq, off, xq);
         buf_store_run4<BF16>(rdk, off, xk);
     }
-    if constexpr (GATE == LA_GATE_DIAG) {
+    if constexpr (VG) {
         // the chunk's carry rowsum(G * S_next) per owned channel i:
         //   e^{r_i} rowsum(Gs * S)_i + sum_s Kh[s][i] (Gs v_s)_i
         // the first sum over the four lanes holding row 16 nb + r, read from
@@ -520,9 +531,28 @@ __global__ __launch_bounds__(Cfg::NT) void bwd_kernel(const BwdParams p) {
                 out[i] = x + later[i];
                 later[i] += lane_read(x, 16 * g);
             }
-            const uint32_t off = ((uint32_t)(t0 + 16 * tb + r) * D + ch0) * 4;
-            __builtin_amdgcn_raw_buffer_store_b128(
-                __builtin_bit_cast(u32x4_t, f32x4_t{out[0], out[1], out[2], out[3]}), rdla, off, 0, 0);
+            if constexpr (GATE == LA_GATE_DIAG) {
+                const uint32_t off = ((uint32_t)(t0 + 16 * tb + r) * D + ch0) * 4;
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    __builtin_bit_cast(u32x4_t, f32x4_t{out[0], out[1], out[2], out[3]}), rdla, off, 0, 0);
+            } else {
+                // one gate per token: the sum over all channels, first over
+                // the 4 x 4 channels of this wave's lanes of the token
+                float sum = out[0] + out[1] + out[2] + out[3];
+                sum += lane_read(sum, lane ^ 16);
+                sum += lane_read(sum, lane ^ 32);
+                if (g == 0) sm.red[wave][16 * tb + r] = sum;
+            }
+        }
+        if constexpr (GATE == LA_GATE_SCALAR) {
+            // then over the waves
+            __syncthreads();
+            if (tid < C) {
+                float sum = 0.f;
+#pragma unroll
+                for (int w2 = 0; w2 < NW; ++w2) sum += sm.red[w2][tid];
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sum), rdla, (uint32_t)(t0 + tid) * 4, 0, 0);
+            }
         }
     }
 }
@@ -545,6 +575,7 @@ hipError_t launch_bwd_dt(const BwdParams& p, int gate, hipStream_t s) {
     if (gate == LA_GATE_NONE) LA_BWD_LAUNCH(LA_GATE_NONE);
     if (gate == LA_GATE_GAMMA) LA_BWD_LAUNCH(LA_GATE_GAMMA);
     if (gate == LA_GATE_DIAG) LA_BWD_LAUNCH(LA_GATE_DIAG);
+    if (gate == LA_GATE_SCALAR) LA_BWD_LAUNCH(LA_GATE_SCALAR);
     return hipErrorInvalidValue;
 #undef LA_BWD_LAUNCH
 }

@@ -237,6 +237,9 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
     using E = typename Cfg::E;
     using Pair = typename Cfg::Pair;
     using Frag = typename Cfg::Frag;
+    // the diagonal and the per-token scalar gate share one path (a scalar
+    // gate is a diagonal one with equal channels)
+    constexpr bool VG = GATE == LA_GATE_DIAG || GATE == LA_GATE_SCALAR;
 
     __shared__ ChunkSmem<Cfg> sm;
 
@@ -281,9 +284,12 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
         make_rsrc(reinterpret_cast<const E*>(p.k) + rows0 * DK, (uint32_t)L * DK * ES);
     const __amdgpu_buffer_rsrc_t rv =
         make_rsrc(reinterpret_cast<const E*>(p.v) + rows0 * DV, (uint32_t)L * DV * ES);
+    // log-gates: DIAG one per token and key channel, SCALAR one per token
     const __amdgpu_buffer_rsrc_t rla =
-        make_rsrc(GATE == LA_GATE_DIAG ? (const void*)(p.log_alpha + rows0 * DK) : p.q,
-                  GATE == LA_GATE_DIAG ? (uint32_t)L * DK * 4 : 0u);
+        make_rsrc(GATE == LA_GATE_DIAG ? (const void*)(p.log_alpha + rows0 * DK)
+                  : GATE == LA_GATE_SCALAR ? (const void*)(p.log_alpha + rows0) : p.q,
+                  GATE == LA_GATE_DIAG ? (uint32_t)L * DK * 4
+                  : GATE == LA_GATE_SCALAR ? (uint32_t)L * 4 : 0u);
     const __amdgpu_buffer_rsrc_t ro =
         make_rsrc(SONLY ? p.q : (const void*)(reinterpret_cast<const E*>(p.out) + rows0 * DV),
                   SONLY ? 0u : (uint32_t)L * DV * ES);
@@ -351,7 +357,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
     struct ChunkRegs {
         Words<Cfg::KWORDS> k[KTPG];
         Words<Cfg::VWORDS> v[VTPG];
-        Words<CW> la[GATE == LA_GATE_DIAG ? KTPG : 1];
+        Words<CW> la[VG ? KTPG : 1];
     };
     Words<Cfg::KWORDS> qreg[SONLY ? 1 : KTPG];
     auto load_chunk = [&](int c, ChunkRegs& rg) {
@@ -363,6 +369,12 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
         for (int j = 0; j < KTPG; ++j) {
             rg.k[j] = buf_load_words<Cfg::KWORDS>(rk, okk + j * DK * ES);
             if constexpr (GATE == LA_GATE_DIAG) rg.la[j] = buf_load_words<CW>(rla, oaa + j * DK * 4);
+            if constexpr (GATE == LA_GATE_SCALAR) {
+                // one gate per token, the same for every channel of the run
+                const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(rla, (t0 + ktg * KTPG + j) * 4, 0, 0);
+#pragma unroll
+                for (int i = 0; i < CW; ++i) rg.la[j].w[i] = w;
+            }
         }
 #pragma unroll
         for (int j = 0; j < VTPG; ++j) rg.v[j] = buf_load_words<Cfg::VWORDS>(rv, ovv + j * DV * ES);
@@ -388,7 +400,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
             f32x4_t f = {1.f, 1.f, 1.f, 1.f};
-            if constexpr (GATE == LA_GATE_DIAG) f = *reinterpret_cast<const f32x4_t*>(&sm.post[16 * mb + 4 * g]);
+            if constexpr (VG) f = *reinterpret_cast<const f32x4_t*>(&sm.post[16 * mb + 4 * g]);
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
                 float x[4] = {accS[mb][nb][0] * f[0], accS[mb][nb][1] * f[1],
@@ -414,7 +426,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
         float gexc[CW], gmid[CW];   // earlier groups of this wave; one wave: chunk middle
 #pragma unroll
         for (int i = 0; i < CW; ++i) gexc[i] = gmid[i] = 0.f;
-        if constexpr (GATE == LA_GATE_DIAG) {
+        if constexpr (VG) {
             float gsum[CW], incl[CW], wsum[CW];
 #pragma unroll
             for (int i = 0; i < CW; ++i) gsum[i] = 0.f;
@@ -449,7 +461,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
         float gref[CW], gtot[CW], goff[CW];
 #pragma unroll
         for (int i = 0; i < CW; ++i) gref[i] = gtot[i] = goff[i] = 0.f;
-        if constexpr (GATE == LA_GATE_DIAG) {
+        if constexpr (VG) {
             // all wave sums are read before any is used, so the reads overlap
             float x[NW][CW];
 #pragma unroll
@@ -512,7 +524,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
                     if constexpr (ELU1) ka = elu1f(ka);
                     ka = ok ? ka : 0.f;
                     float fq = 1.f, fk = 1.f, ft = ftok;
-                    if constexpr (GATE == LA_GATE_DIAG) {
+                    if constexpr (VG) {
                         bcur[i] += run_elem<false>(rg.la[j], i) * kLog2e;
                         const float d = bcur[i] - gref[i];
                         fq = __builtin_amdgcn_exp2f(d);
@@ -553,7 +565,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
                 float sc[CW], pr[CW], po[CW];
 #pragma unroll
                 for (int i = 0; i < CW; ++i) sc[i] = pr[i] = po[i] = 1.f;
-                if constexpr (GATE == LA_GATE_DIAG) {
+                if constexpr (VG) {
 #pragma unroll
                     for (int i = 0; i < CW; ++i) {
                         const int row = CW * kcp + i;
@@ -618,7 +630,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
                     float dq = 0.f;
                     for (int i = 0; i < DK; ++i) {
                         float zz = sm.z[i];
-                        if constexpr (GATE == LA_GATE_DIAG) zz *= sm.pre[i];
+                        if constexpr (VG) zz *= sm.pre[i];
                         dq += T::tof(sm.q[t][qk_pos<Cfg>(t, i)]) * zz;
                     }
                     if constexpr (GATE == LA_GATE_GAMMA) dq *= sm.gpow[t + 1];
@@ -644,7 +656,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
                 vf[kk][nb] = T::load(&sm.vt[row][tr_pos<Cfg>(row, kk * MK + KPL * g)]);
             }
 
-        if constexpr (GATE == LA_GATE_DIAG) scale_rows<Cfg>(accS, sm.scale, g);
+        if constexpr (VG) scale_rows<Cfg>(accS, sm.scale, g);
 
         if constexpr (!SONLY) {
             // ---- op2: O^T = S'^T Qh^T (+ per-token decay) + V^T P^T
@@ -770,7 +782,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
         }
     }
     // DIAG: the last chunk's after-factor
-    if constexpr (GATE == LA_GATE_DIAG) {
+    if constexpr (VG) {
         __syncthreads();
         scale_rows<Cfg>(accS, sm.post, g);
     }
@@ -789,7 +801,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
         Sout = p.ws_S + ((size_t)bh * P + seg) * SS;
         zout = p.ws_z + ((size_t)bh * P + seg) * DK;
         float* aout = p.ws_a + ((size_t)bh * P + seg) * DK;
-        if constexpr (GATE == LA_GATE_DIAG) {
+        if constexpr (VG) {
             if (tid < DK) aout[tid] = __builtin_amdgcn_exp2f(sm.segsum[tid]);
         } else {
             if (tid < DK) aout[tid] = GATE == LA_GATE_GAMMA ? seg_g : 1.0f;
@@ -909,7 +921,8 @@ hipError_t launch_chunk_dt(const ChunkParams& p, int chunk, int gate, int pass, 
     do {                                                                 \
         if (gate == LA_GATE_NONE) LA_CHUNK_LAUNCH(CC, 0, SO, RV, ST);    \
         if (gate == LA_GATE_GAMMA) LA_CHUNK_LAUNCH(CC, 1, SO, RV, ST);   \
-        LA_CHUNK_LAUNCH(CC, 2, SO, RV, ST);                              \
+        if (gate == LA_GATE_DIAG) LA_CHUNK_LAUNCH(CC, 2, SO, RV, ST);    \
+        if (gate == LA_GATE_SCALAR) LA_CHUNK_LAUNCH(CC, 3, SO, RV, ST);  \
     } while (0)
 #define LA_CHUNK_FWD(CC)                                                 \
     do {                                                                 \

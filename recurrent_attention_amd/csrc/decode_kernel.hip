@@ -65,6 +65,7 @@ void decode_kernel(const DecodeParams p) {
         float a = 1.0f;
         if constexpr (GATE == LA_GATE_GAMMA) a = p.gamma[h];
         if constexpr (GATE == LA_GATE_DIAG) a = __expf(p.log_alpha[(size_t)bh * DK + tid]);
+        if constexpr (GATE == LA_GATE_SCALAR) a = __expf(p.log_alpha[bh]);
         sa[tid] = a;
     }
     if (tid < DV) sv[tid] = T::tof(v[tid]);
@@ -116,7 +117,9 @@ static hipError_t launch_decode_dt(const DecodeParams& p, int gate, hipStream_t 
     const dim3 grid(p.BH), block(DecodeShape<D, D>::NT);
     if (gate == LA_GATE_NONE) hipLaunchKernelGGL((decode_kernel<D, D, BF, 0>), grid, block, 0, s, p);
     else if (gate == LA_GATE_GAMMA) hipLaunchKernelGGL((decode_kernel<D, D, BF, 1>), grid, block, 0, s, p);
-    else hipLaunchKernelGGL((decode_kernel<D, D, BF, 2>), grid, block, 0, s, p);
+    else if (gate == LA_GATE_DIAG) hipLaunchKernelGGL((decode_kernel<D, D, BF, 2>), grid, block, 0, s, p);
+    else if (gate == LA_GATE_SCALAR) hipLaunchKernelGGL((decode_kernel<D, D, BF, 3>), grid, block, 0, s, p);
+    else return hipErrorInvalidValue;
     return hipGetLastError();
 }
 

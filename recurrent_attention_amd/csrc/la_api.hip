@@ -83,6 +83,9 @@ la_status check_desc(const la_desc* d) {
     return LA_OK;
 }
 
+// Gates read from device memory (one per token and channel, or per token).
+bool device_gate(int gate_mode) { return gate_mode == LA_GATE_DIAG || gate_mode == LA_GATE_SCALAR; }
+
 la_status check_gate(const la_desc* d, int gate_mode, const float* g, bool device_diag,
                      float* log2_gamma, float* gamma) {
     if (gate_mode == LA_GATE_NONE) return LA_OK;
@@ -100,8 +103,9 @@ la_status check_gate(const la_desc* d, int gate_mode, const float* g, bool devic
         }
         return LA_OK;
     }
-    if (gate_mode == LA_GATE_DIAG) {
-        if (!g) return fail(LA_ERR_INVALID, "DIAG gate needs a device log-gate array");
+    if (gate_mode == LA_GATE_DIAG || gate_mode == LA_GATE_SCALAR) {
+        if (!g) return fail(LA_ERR_INVALID, "%s gate needs a device log-gate array",
+                            gate_mode == LA_GATE_DIAG ? "DIAG" : "SCALAR");
         if (device_diag && !aligned16(g)) return fail(LA_ERR_INVALID, "log-gate pointer is not 16-byte aligned");
         return LA_OK;
     }
@@ -256,7 +260,7 @@ la_status chunk_fwd_impl(const la_desc* d, const int* cu_seqlens, int max_seqlen
     p.q = q;
     p.k = k;
     p.v = v;
-    p.log_alpha = gate_mode == LA_GATE_DIAG ? gamma_or_log_alpha : nullptr;
+    p.log_alpha = device_gate(gate_mode) ? gamma_or_log_alpha : nullptr;
     p.S0 = S0;
     p.z0 = z0;
     p.out = out;
@@ -377,10 +381,10 @@ la_status la_chunk_bwd(const la_desc* d, const void* q, const void* k, const voi
     if (d->normalize) return fail(LA_ERR_UNSUPPORTED, "the backward has no normaliser (normalize=1)");
     if (!q || !k || !v || !dout || !dq || !dk || !dv)
         return fail(LA_ERR_INVALID, "q, k, v, dout, dq, dk and dv must be non-NULL");
-    if (gate_mode == LA_GATE_DIAG && !dlog_alpha)
-        return fail(LA_ERR_INVALID, "DIAG gate needs dlog_alpha");
-    if (gate_mode != LA_GATE_DIAG && dlog_alpha)
-        return fail(LA_ERR_INVALID, "dlog_alpha given without the DIAG gate");
+    if (device_gate(gate_mode) && !dlog_alpha)
+        return fail(LA_ERR_INVALID, "DIAG and SCALAR gates need dlog_alpha");
+    if (!device_gate(gate_mode) && dlog_alpha)
+        return fail(LA_ERR_INVALID, "dlog_alpha given without a DIAG or SCALAR gate");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) || !aligned16(dq) ||
         !aligned16(dk) || !aligned16(dv) || (dlog_alpha && !aligned16(dlog_alpha)) ||
         (S0 && !aligned16(S0)) || (dS_final && !aligned16(dS_final)) || (dS0 && !aligned16(dS0)))
@@ -403,7 +407,7 @@ la_status la_chunk_bwd(const la_desc* d, const void* q, const void* k, const voi
 
     const int BH = d->B * d->H;
     char* ws = static_cast<char*>(workspace);
-    p.log_alpha = gate_mode == LA_GATE_DIAG ? gamma_or_log_alpha : nullptr;
+    p.log_alpha = device_gate(gate_mode) ? gamma_or_log_alpha : nullptr;
     p.L = d->L;
     p.H = d->H;
     p.BH = BH;
@@ -507,7 +511,7 @@ la_status la_decode_step(const la_desc* d, const void* q, const void* k, const v
     p.q = q;
     p.k = k;
     p.v = v;
-    p.log_alpha = gate_mode == LA_GATE_DIAG ? gate : nullptr;
+    p.log_alpha = device_gate(gate_mode) ? gate : nullptr;
     p.S = S;
     p.z = z;
     p.out = out;

@@ -21,6 +21,9 @@ name                                   contents
 ``decode_retention_256x32_d128``       256 sequences x 32 heads, d=128, fp32
                                        S ~ N(0,1), one bf16 token per step,
                                        gamma = 0.97, 1000 steps
+``scalar_gate_B1H16_L32768_d128``      as the GLA workload with one gate per
+                                       token and head (log alpha =
+                                       logsigmoid(g)/16, g ~ N(0,1) [B,H,L])
 ``gla_varlen_32seq_H16_d128``          32 packed sequences, lengths uniform
                                        in [1, 4096] (seed 7), H=16, d=128,
                                        bf16, GLA gates as above, C=64
@@ -42,7 +45,7 @@ from dataclasses import dataclass, field
 
 import torch
 
-GATE_NONE, GATE_GAMMA, GATE_DIAG = 0, 1, 2
+GATE_NONE, GATE_GAMMA, GATE_DIAG, GATE_SCALAR = 0, 1, 2, 3
 PHI_IDENTITY, PHI_ELU1 = 0, 1
 
 
@@ -84,6 +87,8 @@ WORKLOADS = {
                  gamma=retention_gammas(16)),
         Workload("gla_B1H16_L32768_d128", 1, 16, 32768, 128, 128,
                  torch.bfloat16, GATE_DIAG, PHI_IDENTITY, False, 64),
+        Workload("scalar_gate_B1H16_L32768_d128", 1, 16, 32768, 128, 128,
+                 torch.bfloat16, GATE_SCALAR, PHI_IDENTITY, False, 64),
         Workload("decode_retention_256x32_d128", 256, 32, 1, 128, 128,
                  torch.bfloat16, GATE_GAMMA, PHI_IDENTITY, False, 0,
                  gamma=(0.97,) * 32, steps=1000),
@@ -132,6 +137,10 @@ def prefill_inputs(B, H, L, dk, dv, dtype=torch.bfloat16, gate_mode=GATE_NONE,
         g = torch.randn((B, H, L, dk), generator=gen, dtype=torch.float32,
                         device=device)
         # alpha = sigmoid(g)^(1/16), kept in log space
+        out["log_alpha"] = torch.nn.functional.logsigmoid(g) / 16.0
+    elif gate_mode == GATE_SCALAR:
+        # one gate per token and head, drawn like the diagonal ones
+        g = torch.randn((B, H, L), generator=gen, dtype=torch.float32, device=device)
         out["log_alpha"] = torch.nn.functional.logsigmoid(g) / 16.0
     if with_state:
         out["S0"] = state_scale * torch.randn((B, H, dk, dv), generator=gen,

@@ -45,7 +45,8 @@ def run_pair(inp, gate_mode, chunk, phi=0, normalize=False, S0=None, z0=None,
     q, k, v = inp["q"], inp["k"], inp["v"]
     B, H, L, dk = q.shape
     dq, dkk, dvv = (x.to(device) for x in (q, k, v))
-    la_dev = inp["log_alpha"].to(device) if gate_mode == api.LA_GATE_DIAG else None
+    gated = gate_mode in (api.LA_GATE_DIAG, api.LA_GATE_SCALAR)
+    la_dev = inp["log_alpha"].to(device) if gated else None
     S0d = S0.to(device) if S0 is not None else None
     z0d = z0.to(device) if z0 is not None else None
     out, S, z = api.chunk_fwd(dq, dkk, dvv, gate_mode=gate_mode, gamma=inp["gamma"],
@@ -67,7 +68,7 @@ def run_pair(inp, gate_mode, chunk, phi=0, normalize=False, S0=None, z0=None,
         g = inp["gamma"].double().numpy()
         gam = g if pairs is None else None
     qn, kn, vn = (sel(to_host64(x)) for x in (q, k, v))
-    lan = sel(to_host64(inp["log_alpha"])) if gate_mode == api.LA_GATE_DIAG else None
+    lan = sel(to_host64(inp["log_alpha"])) if gated else None
     S0n = sel(to_host64(S0)) if S0 is not None else None
     z0n = sel(to_host64(z0)) if z0 is not None else None
     if pairs is not None and gate_mode == api.LA_GATE_GAMMA:

@@ -21,7 +21,9 @@ from parity_util import TOL, slice_rel_err, to_host64
 
 pytestmark = pytest.mark.gpu
 
-NONE, GAMMA, DIAG = api.LA_GATE_NONE, api.LA_GATE_GAMMA, api.LA_GATE_DIAG
+NONE, GAMMA, DIAG, SCALAR = (api.LA_GATE_NONE, api.LA_GATE_GAMMA, api.LA_GATE_DIAG,
+                              api.LA_GATE_SCALAR)
+GATED = (DIAG, SCALAR)
 DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
 NAMES = ("dq", "dk", "dv", "dlog_alpha", "dS0")
 
@@ -48,7 +50,7 @@ def _gpu_bwd(inp, mode, phi=0, segments=0):
     dev = "cuda"
     t = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
     g = api.chunk_bwd(t["q"], t["k"], t["v"], t["dout"], gate_mode=mode, gamma=inp["gamma"],
-                      log_alpha=t["log_alpha"] if mode == DIAG else None,
+                      log_alpha=t["log_alpha"] if mode in GATED else None,
                       S0=t.get("S0"), dS_final=t["dS_final"], phi=phi, segments=segments)
     torch.cuda.synchronize()
     return {k: to_host64(v) for k, v in g.items()}
@@ -63,7 +65,7 @@ def _oracle_bwd(inp, mode, phi=0, pairs=None):
         return oracle.backward(
             f64["q"], f64["k"], f64["v"], f64["dout"], gate_mode=mode,
             gamma=None if inp["gamma"] is None else inp["gamma"].double().numpy(),
-            log_alpha=f64["log_alpha"] if mode == DIAG else None, phi=phi,
+            log_alpha=f64["log_alpha"] if mode in GATED else None, phi=phi,
             S0=f64.get("S0"), dS_final=f64["dS_final"], nthreads=8)
     out = {k: [] for k in NAMES}
     for p in pairs:
@@ -72,7 +74,7 @@ def _oracle_bwd(inp, mode, phi=0, pairs=None):
         r = oracle.backward(
             sl(f64["q"]), sl(f64["k"]), sl(f64["v"]), sl(f64["dout"]), gate_mode=mode,
             gamma=None if inp["gamma"] is None else [float(inp["gamma"][h])],
-            log_alpha=sl(f64["log_alpha"]) if mode == DIAG else None, phi=phi,
+            log_alpha=sl(f64["log_alpha"]) if mode in GATED else None, phi=phi,
             S0=sl(f64.get("S0")), dS_final=sl(f64["dS_final"]))
         for k in NAMES:
             out[k].append(r[k])
@@ -107,7 +109,7 @@ def _check(got, ref, dtype, what):
 GRID = [(dt, d, mode)
         for dt in ("f32", "bf16")
         for d in ((16, 32, 64, 128) if dt == "f32" else (32, 64, 128))
-        for mode in (NONE, GAMMA, DIAG)]
+        for mode in (NONE, GAMMA, DIAG, SCALAR)]
 
 
 @pytest.mark.parametrize("dt,d,mode", GRID)
@@ -121,7 +123,7 @@ def test_chunk_bwd_grid(dt, d, mode):
     _check(got, ref, dtype, f"{dt} d={d} mode={mode}")
 
 
-@pytest.mark.parametrize("mode", [NONE, GAMMA, DIAG])
+@pytest.mark.parametrize("mode", [NONE, GAMMA, DIAG, SCALAR])
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_chunk_bwd_elu1_features(mode, dt):
     dtype = DTYPES[dt]
@@ -140,7 +142,7 @@ def test_chunk_bwd_segmentations_agree(segments):
 
 
 @pytest.mark.parametrize("L", [1, 31, 63, 64, 65, 129])
-@pytest.mark.parametrize("mode", [NONE, DIAG])
+@pytest.mark.parametrize("mode", [NONE, DIAG, SCALAR])
 def test_chunk_bwd_edge_lengths(L, mode):
     inp = _case(2, 1, L, 64, torch.bfloat16, mode, seed=L, state=True)
     got = _gpu_bwd(inp, mode, phi=api.LA_PHI_ELU1)
@@ -182,6 +184,15 @@ def test_chunk_bwd_is_linear_in_the_loss_gradients():
     c = _gpu_bwd(inp3, DIAG)
     for k in NAMES:
         assert slice_rel_err(c[k], a[k] + b[k]) <= 1e-4, k
+
+
+def test_chunk_bwd_scalar_gate_full_size_sampled():
+    # the per-token scalar gate at the full size; the oracle checks one head
+    inp = _case(1, 16, 32768, 128, torch.bfloat16, SCALAR, seed=33, state=True)
+    got = _gpu_bwd(inp, SCALAR)
+    pairs = [5]
+    ref = _oracle_bwd(inp, SCALAR, pairs=pairs)
+    _check(_select(got, pairs), ref, torch.bfloat16, "scalar gate, full size, sampled head")
 
 
 def test_chunk_bwd_full_size_sampled():

@@ -15,7 +15,8 @@ from parity_util import TOL, check, run_pair, slice_rel_err, to_host64
 
 pytestmark = pytest.mark.gpu
 
-NONE, GAMMA, DIAG = api.LA_GATE_NONE, api.LA_GATE_GAMMA, api.LA_GATE_DIAG
+NONE, GAMMA, DIAG, SCALAR = (api.LA_GATE_NONE, api.LA_GATE_GAMMA, api.LA_GATE_DIAG,
+                              api.LA_GATE_SCALAR)
 DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
 
 
@@ -40,7 +41,7 @@ GRID = [(dt, d, C, mode)
         for dt in ("f32", "bf16")
         for d in ((16, 32, 64, 128) if dt == "f32" else (32, 64, 128))
         for C in (16, 32, 64)
-        for mode in (NONE, GAMMA, DIAG)]
+        for mode in (NONE, GAMMA, DIAG, SCALAR)]
 
 
 @pytest.mark.parametrize("dt,d,C,mode", GRID)
@@ -52,7 +53,7 @@ def test_chunk_fwd_grid(dt, d, C, mode):
     check(got, ref, dtype, f"{dt} d={d} C={C} mode={mode}")
 
 
-@pytest.mark.parametrize("mode", [NONE, GAMMA, DIAG])
+@pytest.mark.parametrize("mode", [NONE, GAMMA, DIAG, SCALAR])
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 def test_chunk_fwd_normalised_elu1_with_state(mode, dt):
     dtype = DTYPES[dt]
@@ -62,7 +63,7 @@ def test_chunk_fwd_normalised_elu1_with_state(mode, dt):
     check(got, ref, dtype, f"normalised {dt} mode={mode}", normalize=True)
 
 
-@pytest.mark.parametrize("mode", [NONE, GAMMA, DIAG])
+@pytest.mark.parametrize("mode", [NONE, GAMMA, DIAG, SCALAR])
 def test_chunk_fwd_initial_state(mode):
     inp = _inputs(1, 4, 700, 128, torch.bfloat16, mode, seed=9, state=True)
     got, ref = run_pair(inp, mode, 64, S0=inp["S0"])
@@ -156,7 +157,7 @@ def test_resume_equals_one_pass():
 
 @pytest.mark.parametrize("d", [16, 32, 64, 128])
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
-@pytest.mark.parametrize("mode", [NONE, GAMMA, DIAG])
+@pytest.mark.parametrize("mode", [NONE, GAMMA, DIAG, SCALAR])
 @pytest.mark.parametrize("normalize", [False, True])
 def test_decode_steps(d, dt, mode, normalize):
     dtype = DTYPES[dt]
@@ -168,6 +169,10 @@ def test_decode_steps(d, dt, mode, normalize):
     q, k, v, la = workloads.decode_tokens(B, H, d, d, steps, seed=d + 1, dtype=dtype,
                                           scale_inputs=dtype != torch.float32,
                                           gate=mode == DIAG)
+    if mode == SCALAR:
+        # one gate per step, sequence and head
+        g = torch.randn((steps, B, H), generator=workloads.generator(d + 2))
+        la = torch.nn.functional.logsigmoid(g) / 16.0
     gamma = torch.tensor([0.97, 0.5, 1.0, 0.0], dtype=torch.float32)
     dev = "cuda"
     S = S0.to(dev).clone()
@@ -176,14 +181,16 @@ def test_decode_steps(d, dt, mode, normalize):
     for t in range(steps):
         outs.append(api.decode_step(q[t].to(dev), k[t].to(dev), v[t].to(dev), S, z,
                                     gate_mode=mode, gamma=gamma,
-                                    log_alpha=la[t].to(dev) if mode == DIAG else None,
+                                    log_alpha=la[t].to(dev) if mode in (DIAG, SCALAR) else None,
                                     phi=phi))
     torch.cuda.synchronize()
     got_o = np.stack([to_host64(o) for o in outs], axis=2)       # [B,H,steps,d]
     perm = lambda x: to_host64(x).transpose(1, 2, 0, 3)          # [steps,B,H,d] -> [B,H,steps,d]
     ref = oracle.run(perm(q), perm(k), perm(v), gate_mode=mode,
                      gamma=gamma.double().numpy() if mode == GAMMA else None,
-                     log_alpha=perm(la) if mode == DIAG else None, phi=phi,
+                     log_alpha=(perm(la) if mode == DIAG else
+                                to_host64(la).transpose(1, 2, 0) if mode == SCALAR else None),
+                     phi=phi,
                      normalize=normalize, S0=to_host64(S0),
                      z0=to_host64(z0) if normalize else None)
     tol = TOL[dtype]

@@ -18,7 +18,8 @@ from parity_util import TOL, slice_rel_err, to_host64
 
 pytestmark = pytest.mark.gpu
 
-NONE, GAMMA, DIAG = api.LA_GATE_NONE, api.LA_GATE_GAMMA, api.LA_GATE_DIAG
+NONE, GAMMA, DIAG, SCALAR = (api.LA_GATE_NONE, api.LA_GATE_GAMMA, api.LA_GATE_DIAG,
+                              api.LA_GATE_SCALAR)
 DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
 
 
@@ -60,7 +61,7 @@ def _run_oracle(inp, mode, phi=0, normalize=False):
     """Each sequence on its own: out [1,H,T,d], S [N,H,d,d], z [N,H,d]."""
     cu = inp["cu"].numpy()
     q, k, v = (to_host64(inp[x]) for x in ("q", "k", "v"))
-    la = to_host64(inp["log_alpha"]) if mode == DIAG else None
+    la = to_host64(inp["log_alpha"]) if mode in (DIAG, SCALAR) else None
     gam = inp["gamma"].double().numpy() if mode == GAMMA else None
     S0 = to_host64(inp["S0"])
     z0 = to_host64(inp["z0"])
@@ -111,7 +112,7 @@ def _check(got, ref, cu, dtype, what, normalize=False):
 LENS = [100, 0, 1, 64, 63, 65, 700, 17, 0, 300]
 
 
-@pytest.mark.parametrize("mode", [NONE, GAMMA, DIAG])
+@pytest.mark.parametrize("mode", [NONE, GAMMA, DIAG, SCALAR])
 @pytest.mark.parametrize("dt,d", [("f32", 16), ("f32", 64), ("bf16", 64), ("bf16", 128)])
 def test_varlen_matches_per_sequence_oracle(dt, d, mode):
     dtype = DTYPES[dt]

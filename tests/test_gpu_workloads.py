@@ -48,6 +48,10 @@ def test_gla_B1H16_L32768_d128_sampled():
     _prefill("gla_B1H16_L32768_d128", pairs=[0, 7, 15])
 
 
+def test_scalar_gate_B1H16_L32768_d128_sampled():
+    _prefill("scalar_gate_B1H16_L32768_d128", pairs=[3, 12])
+
+
 def _decode_setup(w, steps, with_z, phi):
     dev = torch.device("cuda", 0)
     S0, z0 = workloads.decode_state(w.B, w.H, w.dk, w.dv, seed=0, device=dev, with_z=with_z)

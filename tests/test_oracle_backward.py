@@ -24,7 +24,11 @@ def _inputs(seed, gate_mode, with_s0):
     q = r.standard_normal((B, H, L, DK))
     k = r.standard_normal((B, H, L, DK))
     v = r.standard_normal((B, H, L, DV))
-    la = -np.abs(r.standard_normal((B, H, L, DK))) * 0.5 if gate_mode == oracle.GATE_DIAG else None
+    la = None
+    if gate_mode == oracle.GATE_DIAG:
+        la = -np.abs(r.standard_normal((B, H, L, DK))) * 0.5
+    elif gate_mode == oracle.GATE_SCALAR:
+        la = -np.abs(r.standard_normal((B, H, L))) * 0.5
     S0 = r.standard_normal((B, H, DK, DV)) if with_s0 else None
     Wo = r.standard_normal((B, H, L, DV))
     WS = r.standard_normal((B, H, DK, DV))
@@ -63,6 +67,8 @@ CASES = [
     (oracle.GATE_GAMMA, [0.0, 1.0], oracle.PHI_IDENTITY, True, False),
     (oracle.GATE_DIAG, None, oracle.PHI_IDENTITY, False, True),
     (oracle.GATE_DIAG, None, oracle.PHI_ELU1, True, True),
+    (oracle.GATE_SCALAR, None, oracle.PHI_IDENTITY, True, True),
+    (oracle.GATE_SCALAR, None, oracle.PHI_ELU1, False, True),
 ]
 
 
@@ -75,7 +81,7 @@ def _check_fd(case, seed=0, rtol=1e-6):
                         phi=phi, S0=S0, dS_final=WS)
     f = lambda: _loss(q, k, v, la, S0, Wo, WS, gate_mode, gamma, phi)
     checks = [("dq", q), ("dk", k), ("dv", v)]
-    if gate_mode == oracle.GATE_DIAG:
+    if gate_mode in (oracle.GATE_DIAG, oracle.GATE_SCALAR):
         checks.append(("dlog_alpha", la))
     if with_s0:
         checks.append(("dS0", S0))

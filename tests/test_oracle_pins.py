@@ -246,6 +246,36 @@ def test_diag_reduces_to_gamma_and_to_none():
     assert np.array_equal(c, e)
 
 
+def _scalar_textbook(Q, K, V, log_alpha, S0=None):
+    """Per-token scalar gate as masked attention: the score q_t . k_s weighted
+    by prod_{s<r<=t} alpha_r, plus q_t (prod_{r<=t} alpha_r) S0."""
+    L = Q.shape[0]
+    cs = np.concatenate([[0.0], np.cumsum(log_alpha)])
+    D = np.tril(np.exp(cs[1:, None] - cs[None, 1:]))          # D[t, s]
+    out = ((Q @ K.T) * D) @ V
+    if S0 is not None:
+        out += (Q * np.exp(cs[1:])[:, None]) @ S0
+    return out
+
+
+@pytest.mark.parametrize("with_state", [False, True])
+def test_scalar_gate_matches_decay_masked_attention(with_state):
+    rng = np.random.default_rng(13)
+    L, dk, dv = 9, 3, 4
+    Q, K = rng.standard_normal((L, dk)), rng.standard_normal((L, dk))
+    V = rng.standard_normal((L, dv))
+    la = -rng.uniform(0.0, 1.5, size=L)
+    S0 = rng.standard_normal((dk, dv)) if with_state else None
+    ref = _scalar_textbook(Q, K, V, la, S0)
+    got, S, _ = oracle.run(Q, K, V, gate_mode=oracle.GATE_SCALAR, log_alpha=la, S0=S0)
+    assert np.allclose(got, ref, rtol=0, atol=1e-12)
+    # and a constant gate is retention with gamma = alpha
+    g = 0.7
+    a, Sa, _ = oracle.run(Q, K, V, gate_mode=oracle.GATE_SCALAR, log_alpha=np.full(L, np.log(g)))
+    b, Sb, _ = oracle.run(Q, K, V, gate_mode=oracle.GATE_GAMMA, gamma=[g])
+    assert np.allclose(a, b, rtol=1e-12, atol=1e-12) and np.allclose(Sa, Sb, rtol=1e-12, atol=1e-12)
+
+
 def test_gated_output_differs_from_any_fixed_decay():
     """You-are-the-gate exercise: high gate (0.95) at positions 2 and 5, low
     (0.1) elsewhere; no single retention decay reproduces it."""
