@@ -23,6 +23,9 @@ Also reported, in the same line:
   them from their final states.
 * ``scalar_gate``: the same prefill with one gate per token and head
   (``scalar_gate_B1H16_L32768_d128``), which drops the d_k-wide gate stream.
+* ``retention``: the retention workload (B=2, H=16, L=8192, d=128,
+  multi-scale gamma), plain and with the fused group-norm / swish-gate
+  output epilogue.
 * ``cpu_baseline``: the fp64 oracle (test infrastructure, untuned) on the
   same prefill workload drawn on the host, timed on this machine's cores.
 
@@ -325,6 +328,67 @@ def bench_varlen(args, torch, api, workloads):
     }
 
 
+def bench_retention(args, torch, api, workloads):
+    """The retention workload, plain and with the fused group-norm / swish
+    output epilogue (la_chunk_fwd_groupnorm)."""
+    name = "retention_B2H16_L8192_d128"
+    w = workloads.WORKLOADS[name]
+    dev = torch.device("cuda", 0)
+    inp = workloads.workload_inputs(name, seed=0, device=dev)
+    q, k, v = inp["q"], inp["k"], inp["v"]
+    gen = workloads.generator(404, dev)
+    gnw = 1.0 + 0.5 * torch.randn((w.H, w.dv), generator=gen, device=dev)
+    gnb = 0.3 * torch.randn((w.H, w.dv), generator=gen, device=dev)
+    gate = torch.randn((w.B, w.H, w.L, w.dv), generator=gen, device=dev).to(torch.bfloat16)
+    desc = api.make_desc(w.B, w.H, w.L, w.dk, w.dv, api.LA_BF16, w.phi, False, 0)
+    need = api.la_chunk_fwd_workspace_bytes(desc, w.chunk)
+    out = torch.empty_like(v)
+    S = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(need // 4, 1), dtype=torch.float32, device=dev)
+    g_host = torch.tensor(w.gamma, dtype=torch.float32)
+    gp = ctypes.c_void_p(g_host.data_ptr())
+    sp = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    lib = api.load_library()
+    gn = api.LaGroupNorm(gnw.data_ptr(), gnb.data_ptr(), gate.data_ptr(), 1e-5)
+    head = (ctypes.byref(desc), q.data_ptr(), k.data_ptr(), v.data_ptr(), w.gate_mode, gp,
+            None, None, w.chunk)
+    tail = (out.data_ptr(), S.data_ptr(), None, ws.data_ptr(), need, sp)
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            fn()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) / args.steps * 1e3
+        api.la_profile_begin()
+        for _ in range(args.steps):
+            fn()
+        torch.cuda.synchronize()
+        api.la_profile_end()
+        n, kms = api.la_profile_query("chunk_main")
+        return ms, kms / n * 1e3
+
+    def plain():
+        if lib.la_chunk_fwd(*head, *tail) != 0:
+            raise RuntimeError(api.la_last_error_message())
+
+    def normed():
+        if lib.la_chunk_fwd_groupnorm(*head, ctypes.byref(gn), *tail) != 0:
+            raise RuntimeError(api.la_last_error_message())
+
+    ms0, k0 = timed(plain)
+    ms1, k1 = timed(normed)
+    tokens = w.B * w.L
+    return {"workload": name, "tokens_per_s": round(tokens / (ms0 * 1e-3), 1),
+            "ms_per_step": round(ms0, 4), "main_avg_us": round(k0, 2),
+            "groupnorm_swish": {"tokens_per_s": round(tokens / (ms1 * 1e-3), 1),
+                                "ms_per_step": round(ms1, 4), "main_avg_us": round(k1, 2),
+                                "extra_bytes": w.B * w.H * w.L * w.dv * 2}}
+
+
 def bench_decode(args, torch, api, workloads):
     w = workloads.WORKLOADS[workloads.DECODE_HEADLINE]
     dev = torch.device("cuda", 0)
@@ -424,8 +488,9 @@ def main(argv=None):
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-varlen", action="store_true")
     ap.add_argument("--no-scalar", action="store_true")
+    ap.add_argument("--no-retention", action="store_true")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
-    ap.add_argument("--only", choices=["prefill", "decode", "backward", "varlen", "scalar", "copy"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "backward", "varlen", "scalar", "retention", "copy"], default=None,
                     help="run one part only (copy: a 1 GiB device copy used to scale "
                          "rocprofv3 byte counters); prints no metric line")
     args = ap.parse_args(argv)
@@ -456,6 +521,9 @@ def main(argv=None):
     if args.only == "varlen":
         print(json.dumps(bench_varlen(args, torch, api, workloads)), flush=True)
         return 0
+    if args.only == "retention":
+        print(json.dumps(bench_retention(args, torch, api, workloads)), flush=True)
+        return 0
     if args.only == "scalar":
         sc = bench_prefill(args, torch, api, workloads, "scalar_gate_B1H16_L32768_d128")
         print(json.dumps({"ms_per_step": sc["ms_step"], "kernels": sc["kernels"],
@@ -472,6 +540,7 @@ def main(argv=None):
     vl = None if args.no_varlen else bench_varlen(args, torch, api, workloads)
     sc = None if args.no_scalar else bench_prefill(args, torch, api, workloads,
                                                    "scalar_gate_B1H16_L32768_d128")
+    ret = None if args.no_retention else bench_retention(args, torch, api, workloads)
     w = pre["w"]
     line = {
         "metric": METRIC,
@@ -503,6 +572,8 @@ def main(argv=None):
         line["backward"] = bwd
     if vl is not None:
         line["varlen"] = vl
+    if ret is not None:
+        line["retention"] = ret
     if sc is not None:
         line["scalar_gate"] = {
             "workload": sc["w"].name, "ms_per_step": round(sc["ms_step"], 4),

@@ -171,6 +171,39 @@ la_status la_chunk_fwd_varlen(const la_desc* d, const int* cu_seqlens,
 size_t la_chunk_fwd_varlen_workspace_bytes(const la_desc* d, int max_seqlen,
                                            int chunk);
 
+/*
+ * Output epilogue of retention (RetNet): each token's head output, after
+ * the optional normaliser, is normalised over its d_v channels (group norm
+ * with one group per head) and multiplied by swish of a gate tensor ("Module
+ * 22", section "Retention: Add a Decay to the State", which names this
+ * GroupNorm and swish gate as RetNet's stabiliser in place of a divide):
+ *     y = (o - mean(o)) / sqrt(var(o) + eps) * weight + bias
+ *     out = y * gate * sigmoid(gate)       (or out = y without a gate)
+ * mean and var are over the d_v outputs of one token and head (biased
+ * variance), computed in fp32.
+ */
+typedef struct la_groupnorm {
+    const float* weight; /* device fp32 [H,dv], or NULL (ones)                 */
+    const float* bias;   /* device fp32 [H,dv], or NULL (zeros)                */
+    const void* gate;    /* device [B,H,L,dv] of d->dtype, or NULL (no gate)   */
+    float eps;           /* > 0                                                 */
+} la_groupnorm;
+
+/*
+ * la_chunk_fwd_groupnorm -- la_chunk_fwd with the epilogue above fused into
+ * the store of each output chunk (out holds the epilogue's result; S_final
+ * and z_final are unchanged).  Built for chunk 64 (LA_ERR_UNSUPPORTED for
+ * other chunks).  Arguments as for la_chunk_fwd, plus gn (not NULL).
+ */
+la_status la_chunk_fwd_groupnorm(const la_desc* d, const void* q, const void* k,
+                                 const void* v, int gate_mode,
+                                 const float* gamma_or_log_alpha,
+                                 const float* S0, const float* z0, int chunk,
+                                 const la_groupnorm* gn, void* out,
+                                 float* S_final, float* z_final,
+                                 void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
 /* Bytes of device workspace la_chunk_fwd needs for this shape (segment
  * states, their decays and normaliser parts); 0 for a single segment.
  * Returns 0 for an invalid descriptor as well. */

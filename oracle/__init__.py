@@ -13,6 +13,8 @@ Forms (all compute the same function; see ``oracle.c`` for the citations):
 * :func:`chunkwise`  -- the chunkwise form with a ragged last chunk.
 * :func:`backward`   -- reverse-mode derivative of the token loop (no
   normaliser): dq, dk, dv, d log_alpha, dS0 from dout and dS_final.
+* :func:`groupnorm_swish` -- retention's output epilogue (group norm over
+  each token's head output, times swish of a gate), numpy fp64.
 
 Layouts follow the GPU boundary: q, k ``[B,H,L,dk]``, v and out
 ``[B,H,L,dv]``, S ``[B,H,dk,dv]`` (rows indexed by the key channel), z
@@ -230,6 +232,26 @@ def backward(q, k, v, dout, gate_mode=GATE_NONE, gamma=None, log_alpha=None,
     if two_d:
         res = {n: (a[0, 0] if a is not None else None) for n, a in res.items()}
     return res
+
+
+def groupnorm_swish(out, weight=None, bias=None, gate=None, eps=1e-5):
+    """Retention's output epilogue, in fp64: each token's head output is
+    normalised over its d_v channels (group norm, one group per head, biased
+    variance), scaled and shifted per channel, then multiplied by
+    swish(gate) = gate * sigmoid(gate).  out, gate [B,H,L,dv]; weight, bias
+    [H,dv]."""
+    o = _f64(out)
+    mean = o.mean(axis=-1, keepdims=True)
+    var = ((o - mean) ** 2).mean(axis=-1, keepdims=True)
+    y = (o - mean) / np.sqrt(var + eps)
+    if weight is not None:
+        y = y * _f64(weight)[None, :, None, :]
+    if bias is not None:
+        y = y + _f64(bias)[None, :, None, :]
+    if gate is not None:
+        g = _f64(gate)
+        y = y * (g / (1.0 + np.exp(-g)))
+    return y
 
 
 def multiscale_decays(n: int) -> np.ndarray:

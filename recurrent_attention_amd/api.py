@@ -32,6 +32,7 @@ EXPORTED = (
     "la_version", "la_profile_begin", "la_profile_end", "la_profile_query",
     "la_chunk_bwd", "la_chunk_bwd_workspace_bytes", "la_chunk_bwd_chunk",
     "la_chunk_fwd_varlen", "la_chunk_fwd_varlen_workspace_bytes",
+    "la_chunk_fwd_groupnorm",
 )
 
 
@@ -44,6 +45,11 @@ class LaError(RuntimeError):
 class LaDesc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in
                 ("B", "H", "L", "dk", "dv", "dtype", "phi", "normalize", "segments")]
+
+
+class LaGroupNorm(ctypes.Structure):
+    _fields_ = [("weight", ctypes.c_void_p), ("bias", ctypes.c_void_p),
+                ("gate", ctypes.c_void_p), ("eps", ctypes.c_float)]
 
 
 def library_path() -> str:
@@ -71,6 +77,9 @@ def load_library():
     lib.la_chunk_fwd_workspace_bytes.restype = sz
     lib.la_chunk_fwd_segments.argtypes = [dp, i]
     lib.la_chunk_fwd_segments.restype = i
+    lib.la_chunk_fwd_groupnorm.argtypes = [dp, vp, vp, vp, i, vp, vp, vp, i,
+                                            ctypes.POINTER(LaGroupNorm), vp, vp, vp, vp, sz, vp]
+    lib.la_chunk_fwd_groupnorm.restype = i
     lib.la_chunk_fwd_varlen.argtypes = [dp, vp, i, vp, vp, vp, i, vp, vp, vp, i, vp, vp, vp,
                                          vp, sz, vp]
     lib.la_chunk_fwd_varlen.restype = i
@@ -120,6 +129,15 @@ def la_chunk_fwd(desc, q, k, v, gate_mode, gamma_or_log_alpha, S0, z0, chunk,
     return load_library().la_chunk_fwd(
         ctypes.byref(desc), q, k, v, int(gate_mode), gamma_or_log_alpha, S0, z0,
         int(chunk), out, S_final, z_final, workspace, int(workspace_bytes), stream)
+
+
+def la_chunk_fwd_groupnorm(desc, q, k, v, gate_mode, gamma_or_log_alpha, S0, z0, chunk, gn,
+                           out, S_final, z_final, workspace, workspace_bytes, stream):
+    """Raw call; ``gn`` is a LaGroupNorm (or None for NULL)."""
+    return load_library().la_chunk_fwd_groupnorm(
+        ctypes.byref(desc), q, k, v, int(gate_mode), gamma_or_log_alpha, S0, z0, int(chunk),
+        None if gn is None else ctypes.byref(gn), out, S_final, z_final, workspace,
+        int(workspace_bytes), stream)
 
 
 def la_chunk_fwd_varlen(desc, cu_seqlens, max_seqlen, q, k, v, gate_mode,
@@ -248,10 +266,12 @@ def _gamma_host(gamma, H):
 def chunk_fwd(q, k, v, gate_mode=LA_GATE_NONE, gamma=None, log_alpha=None,
               S0=None, z0=None, chunk=64, phi=LA_PHI_IDENTITY, normalize=False,
               segments=0, out=None, S_final=None, z_final=None,
-              return_state=True, workspace=None, stream=None):
+              return_state=True, workspace=None, stream=None, groupnorm=None):
     """Chunkwise prefill.  q, k: [B,H,L,dk]; v: [B,H,L,dv] (bf16 or fp32, on
     the GPU).  Returns ``(out, S_final, z_final)``; the states are fp32 and
-    z_final is None unless ``normalize``."""
+    z_final is None unless ``normalize``.  ``groupnorm`` = dict(weight=[H,dv]
+    fp32 or None, bias=[H,dv] fp32 or None, gate=[B,H,L,dv] or None, eps)
+    fuses the retention output epilogue (la_chunk_fwd_groupnorm)."""
     torch = _torch()
     B, H, L, dk = q.shape
     dv = v.shape[-1]
@@ -276,15 +296,23 @@ def chunk_fwd(q, k, v, gate_mode=LA_GATE_NONE, gamma=None, log_alpha=None,
     elif gate_mode in (LA_GATE_DIAG, LA_GATE_SCALAR):
         g_arg = _dev_ptr(log_alpha, "log_alpha", torch.float32,
                          (B, H, L, dk) if gate_mode == LA_GATE_DIAG else (B, H, L))
-    st = la_chunk_fwd(
-        desc, _dev_ptr(q, "q"), _dev_ptr(k, "k", q.dtype, (B, H, L, dk)),
-        _dev_ptr(v, "v", q.dtype, (B, H, L, dv)),
-        gate_mode, g_arg, _dev_ptr(S0, "S0", torch.float32, (B, H, dk, dv)),
-        _dev_ptr(z0, "z0", torch.float32, (B, H, dk)), chunk,
-        _dev_ptr(out, "out", q.dtype, (B, H, L, dv)),
-        _dev_ptr(S_final, "S_final", torch.float32, (B, H, dk, dv)),
-        _dev_ptr(z_final, "z_final", torch.float32, (B, H, dk)),
-        _dev_ptr(workspace, "workspace"), ws_bytes, _stream_ptr(stream, dev))
+    ptrs = (_dev_ptr(q, "q"), _dev_ptr(k, "k", q.dtype, (B, H, L, dk)),
+            _dev_ptr(v, "v", q.dtype, (B, H, L, dv)))
+    mid = (gate_mode, g_arg, _dev_ptr(S0, "S0", torch.float32, (B, H, dk, dv)),
+           _dev_ptr(z0, "z0", torch.float32, (B, H, dk)), chunk)
+    tail = (_dev_ptr(out, "out", q.dtype, (B, H, L, dv)),
+            _dev_ptr(S_final, "S_final", torch.float32, (B, H, dk, dv)),
+            _dev_ptr(z_final, "z_final", torch.float32, (B, H, dk)),
+            _dev_ptr(workspace, "workspace"), ws_bytes, _stream_ptr(stream, dev))
+    if groupnorm is None:
+        st = la_chunk_fwd(desc, *ptrs, *mid, *tail)
+    else:
+        gn = LaGroupNorm(
+            _dev_ptr(groupnorm.get("weight"), "groupnorm weight", torch.float32, (H, dv)),
+            _dev_ptr(groupnorm.get("bias"), "groupnorm bias", torch.float32, (H, dv)),
+            _dev_ptr(groupnorm.get("gate"), "groupnorm gate", q.dtype, (B, H, L, dv)),
+            float(groupnorm.get("eps", 1e-5)))
+        st = la_chunk_fwd_groupnorm(desc, *ptrs, *mid, gn, *tail)
     _check(st)
     del g_keep
     return out, S_final, z_final

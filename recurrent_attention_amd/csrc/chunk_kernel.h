@@ -133,6 +133,7 @@ struct ChunkSmem {
     float gpow[Cfg::C + 2];              // gamma^j
     float z[Cfg::DK];
     float den[Cfg::C];
+    float2 gnp[Cfg::SONLY ? 1 : Cfg::NW][Cfg::SONLY ? 1 : Cfg::C];  // group norm: per-wave token sums
 };
 
 // Position of logical channel l in row `row` of a q/k tile.  bf16 tiles
@@ -224,7 +225,7 @@ __device__ __forceinline__ void quad_transpose(float (&x)[4], int q) {
     }
 }
 
-template <class Cfg, bool ELU1, bool REV = false, bool STORE = false>
+template <class Cfg, bool ELU1, bool REV = false, bool STORE = false, bool EPI = false>
 __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
     constexpr int DK = Cfg::DK, DV = Cfg::DV, C = Cfg::C, GATE = Cfg::GATE;
     constexpr int NB = Cfg::NB, MB = Cfg::MB, TB = Cfg::TB, NW = Cfg::NW;
@@ -249,6 +250,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
     const int r = lane & 15, g = lane >> 4;
     const int P = p.P;
     static_assert(SONLY || (!REV && !STORE), "backward variants are state-only");
+    static_assert(!(SONLY && EPI), "the output epilogue belongs to the main pass");
     // the aggregate pass skips the segment it would end with (the last one,
     // or the first one when reversed)
     constexpr bool AGG = SONLY && !STORE;
@@ -360,6 +362,25 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
         Words<CW> la[VG ? KTPG : 1];
     };
     Words<Cfg::KWORDS> qreg[SONLY ? 1 : KTPG];
+    // output epilogue (group norm over each token's d_v outputs, then times
+    // swish of the gate): the gate runs of this lane's outputs, one chunk
+    // ahead, and the norm's per-channel scale and shift
+    constexpr int OW = 4 * ES / 4;   // words of a 4-channel output run
+    Words<OW> greg[EPI ? NB : 1][EPI ? TB : 1];
+    float gnw[EPI ? NB : 1][4], gnb[EPI ? NB : 1][4];
+    const __amdgpu_buffer_rsrc_t rgate =
+        make_rsrc(EPI && p.gn_gate ? (const void*)(reinterpret_cast<const E*>(p.gn_gate) + rows0 * DV) : p.q,
+                  EPI && p.gn_gate ? (uint32_t)L * DV * ES : 0u);
+    if constexpr (EPI) {
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int n = colbase + 16 * nb + 4 * g + i;
+                gnw[nb][i] = p.gn_w ? p.gn_w[(size_t)h * DV + n] : 1.0f;
+                gnb[nb][i] = p.gn_b ? p.gn_b[(size_t)h * DV + n] : 0.0f;
+            }
+    }
     auto load_chunk = [&](int c, ChunkRegs& rg) {
         const uint32_t t0 = (uint32_t)c * C;
         const uint32_t okk = ((t0 + ktg * KTPG) * DK + CW * kcp) * ES;
@@ -384,6 +405,19 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
             const uint32_t okk = (((uint32_t)c * C + ktg * KTPG) * DK + CW * kcp) * ES;
 #pragma unroll
             for (int j = 0; j < KTPG; ++j) qreg[j] = buf_load_words<Cfg::KWORDS>(rq, okk + j * DK * ES);
+        }
+    };
+    // the gate runs of chunk c's outputs (loaded after the previous chunk's
+    // outputs are stored; without a gate tensor the descriptor is empty)
+    auto load_gate = [&](int c) {
+        if constexpr (EPI) {
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                for (int tb = 0; tb < TB; ++tb) {
+                    const uint32_t og = (((uint32_t)c * C + 16 * tb + r) * DV + colbase + 16 * nb + 4 * g) * ES;
+                    greg[nb][tb] = buf_load_words<OW>(rgate, og);
+                }
         }
     };
     constexpr float kLog2e = 1.4426950408889634f;
@@ -719,6 +753,45 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
                 }
             }
             // ---- store: lane (r, g) holds 4 consecutive columns of token row t
+            float gmean[EPI ? TB : 1], grstd[EPI ? TB : 1];
+            if constexpr (EPI) {
+                // group norm statistics of each token's d_v outputs: the
+                // lane's 4 NB values, the 4 lanes of the token in this wave,
+                // then the waves through LDS
+#pragma unroll
+                for (int tb = 0; tb < TB; ++tb) {
+                    const float inv = __builtin_amdgcn_rcpf(sm.den[16 * tb + r]);
+                    float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const float o = accO[nb][tb][i] * inv;
+                            s1 += o;
+                            s2 += o * o;
+                        }
+                    s1 += lane_read(s1, lane ^ 16);
+                    s2 += lane_read(s2, lane ^ 16);
+                    s1 += lane_read(s1, lane ^ 32);
+                    s2 += lane_read(s2, lane ^ 32);
+                    if (g == 0) sm.gnp[wave][16 * tb + r] = make_float2(s1, s2);
+                }
+                __syncthreads();
+#pragma unroll
+                for (int tb = 0; tb < TB; ++tb) {
+                    float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+                    for (int w2 = 0; w2 < NW; ++w2) {
+                        const float2 x = sm.gnp[w2][16 * tb + r];
+                        s1 += x.x;
+                        s2 += x.y;
+                    }
+                    const float mean = s1 * (1.0f / DV);
+                    const float var = fmaxf(s2 * (1.0f / DV) - mean * mean, 0.f);
+                    gmean[tb] = mean;
+                    grstd[tb] = __builtin_amdgcn_rsqf(var + p.gn_eps);
+                }
+            }
 #pragma unroll
             for (int tb = 0; tb < TB; ++tb) {
                 const int t = 16 * tb + r;
@@ -726,7 +799,17 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb) {
                     const uint32_t off = ((uint32_t)(t0 + t) * DV + colbase + 16 * nb + 4 * g) * ES;
-                    const f32x4_t o = accO[nb][tb] * inv;
+                    f32x4_t o = accO[nb][tb] * inv;
+                    if constexpr (EPI) {
+                        const bool gated = p.gn_gate != nullptr;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const float y = (o[i] - gmean[tb]) * grstd[tb] * gnw[nb][i] + gnb[nb][i];
+                            const float a = run_elem<BF16>(greg[nb][tb], i);
+                            const float sw = a * __builtin_amdgcn_rcpf(1.0f + __expf(-a));
+                            o[i] = gated ? y * sw : y;
+                        }
+                    }
                     if constexpr (BF16) {
                         const u32x2_t w = {pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3])};
                         __builtin_amdgcn_raw_buffer_store_b64(w, ro, off, 0, 0);
@@ -735,6 +818,10 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
                     }
                 }
             }
+        }
+
+        if constexpr (EPI) {
+            if (ci + 1 < c_end) load_gate(cof(ci + 1));
         }
 
         // ---- op3: state update
@@ -767,6 +854,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
     }
     {
         if (c_begin < c_end) load_q(cof(c_begin));
+        if (c_begin < c_end) load_gate(cof(c_begin));
         if constexpr (Cfg::PD == 2) {
             ChunkRegs ra, rb;
             if (c_begin < c_end) load_chunk(cof(c_begin), ra);
@@ -908,22 +996,23 @@ struct ChunkWaves {
 template <int D, bool BF, int NWV = ChunkWaves<D>::value>
 hipError_t launch_chunk_dt(const ChunkParams& p, int chunk, int gate, int pass, hipStream_t s,
                            int nblocks) {
-#define LA_CHUNK_LAUNCH(CC, GG, SO, RV, ST)                                                \
+#define LA_CHUNK_LAUNCH(CC, GG, SO, RV, ST, EP)                                            \
     do {                                                                                   \
         using Cfg = ChunkCfg<D, D, CC, BF, GG, SO, NWV>;                                   \
         if (p.phi_elu1)                                                                    \
-            hipLaunchKernelGGL((chunk_kernel<Cfg, true, RV, ST>), dim3(nblocks), dim3(Cfg::NT), 0, s, p); \
+            hipLaunchKernelGGL((chunk_kernel<Cfg, true, RV, ST, EP>), dim3(nblocks), dim3(Cfg::NT), 0, s, p); \
         else                                                                               \
-            hipLaunchKernelGGL((chunk_kernel<Cfg, false, RV, ST>), dim3(nblocks), dim3(Cfg::NT), 0, s, p); \
+            hipLaunchKernelGGL((chunk_kernel<Cfg, false, RV, ST, EP>), dim3(nblocks), dim3(Cfg::NT), 0, s, p); \
         return hipGetLastError();                                                          \
     } while (0)
-#define LA_CHUNK_GATES(CC, SO, RV, ST)                                   \
-    do {                                                                 \
-        if (gate == LA_GATE_NONE) LA_CHUNK_LAUNCH(CC, 0, SO, RV, ST);    \
-        if (gate == LA_GATE_GAMMA) LA_CHUNK_LAUNCH(CC, 1, SO, RV, ST);   \
-        if (gate == LA_GATE_DIAG) LA_CHUNK_LAUNCH(CC, 2, SO, RV, ST);    \
-        if (gate == LA_GATE_SCALAR) LA_CHUNK_LAUNCH(CC, 3, SO, RV, ST);  \
+#define LA_CHUNK_GATES_EP(CC, SO, RV, ST, EP)                                \
+    do {                                                                     \
+        if (gate == LA_GATE_NONE) LA_CHUNK_LAUNCH(CC, 0, SO, RV, ST, EP);    \
+        if (gate == LA_GATE_GAMMA) LA_CHUNK_LAUNCH(CC, 1, SO, RV, ST, EP);   \
+        if (gate == LA_GATE_DIAG) LA_CHUNK_LAUNCH(CC, 2, SO, RV, ST, EP);    \
+        if (gate == LA_GATE_SCALAR) LA_CHUNK_LAUNCH(CC, 3, SO, RV, ST, EP);  \
     } while (0)
+#define LA_CHUNK_GATES(CC, SO, RV, ST) LA_CHUNK_GATES_EP(CC, SO, RV, ST, false)
 #define LA_CHUNK_FWD(CC)                                                 \
     do {                                                                 \
         if (pass == PASS_STATE) LA_CHUNK_GATES(CC, true, false, false);  \
@@ -935,12 +1024,14 @@ hipError_t launch_chunk_dt(const ChunkParams& p, int chunk, int gate, int pass, 
         if (pass == PASS_STORE) LA_CHUNK_GATES(CB, true, false, true);
         if (pass == PASS_STORE_REV) LA_CHUNK_GATES(CB, true, true, true);
     }
+    if (pass == PASS_MAIN_NORM && chunk == 64) LA_CHUNK_GATES_EP(64, false, false, false, true);
     if (chunk == 16) LA_CHUNK_FWD(16);
     if (chunk == 32) LA_CHUNK_FWD(32);
     if (chunk == 64) LA_CHUNK_FWD(64);
     return hipErrorInvalidValue;
 #undef LA_CHUNK_FWD
 #undef LA_CHUNK_GATES
+#undef LA_CHUNK_GATES_EP
 #undef LA_CHUNK_LAUNCH
 }
 

@@ -224,8 +224,8 @@ la_status hip_fail(hipError_t e, const char* what) {
 la_status chunk_fwd_impl(const la_desc* d, const int* cu_seqlens, int max_seqlen, const void* q,
                          const void* k, const void* v, int gate_mode,
                          const float* gamma_or_log_alpha, const float* S0, const float* z0,
-                         int chunk, void* out, float* S_final, float* z_final, void* workspace,
-                         size_t ws_bytes, void* stream) {
+                         int chunk, const la_groupnorm* gn, void* out, float* S_final,
+                         float* z_final, void* workspace, size_t ws_bytes, void* stream) {
     // packed sequences plan their segments for the longest one
     const la_desc dp = plan_desc(d, cu_seqlens, max_seqlen);
     la_status st;
@@ -241,9 +241,22 @@ la_status chunk_fwd_impl(const la_desc* d, const int* cu_seqlens, int max_seqlen
     if (d->segments > 0 && d->segments > (dp.L + chunk - 1) / chunk)
         return fail(LA_ERR_INVALID, "segments=%d exceeds the %d chunks", d->segments,
                     (dp.L + chunk - 1) / chunk);
+    if (gn) {
+        if (chunk != 64) return fail(LA_ERR_UNSUPPORTED, "the group-norm epilogue is built for chunk 64");
+        if (!(gn->eps > 0.0f)) return fail(LA_ERR_INVALID, "group-norm eps must be > 0");
+        if ((gn->weight && !aligned16(gn->weight)) || (gn->bias && !aligned16(gn->bias)) ||
+            (gn->gate && !aligned16(gn->gate)))
+            return fail(LA_ERR_INVALID, "device pointers must be 16-byte aligned");
+    }
 
     la::ChunkParams p;
     std::memset(&p, 0, sizeof p);
+    if (gn) {
+        p.gn_w = gn->weight;
+        p.gn_b = gn->bias;
+        p.gn_gate = gn->gate;
+        p.gn_eps = gn->eps;
+    }
     st = check_gate(d, gate_mode, gamma_or_log_alpha, true, p.log2_gamma, nullptr);
     if (st != LA_OK) return st;
 
@@ -295,7 +308,8 @@ la_status chunk_fwd_impl(const la_desc* d, const int* cu_seqlens, int max_seqlen
         if (e != hipSuccess) return hip_fail(e, "segment scan launch");
     }
     e = timed_launch(la::K_CHUNK_MAIN, s, [&] {
-        return chunk_launch(d, p, chunk, gate_mode, la::PASS_MAIN, s, BH * pl.P);
+        return chunk_launch(d, p, chunk, gate_mode, gn ? la::PASS_MAIN_NORM : la::PASS_MAIN, s,
+                            BH * pl.P);
     });
     if (e != hipSuccess) return hip_fail(e, "main pass launch");
     return LA_OK;
@@ -337,7 +351,20 @@ la_status la_chunk_fwd(const la_desc* d, const void* q, const void* k, const voi
     const la_status st = check_desc(d);
     if (st != LA_OK) return st;
     return chunk_fwd_impl(d, nullptr, 0, q, k, v, gate_mode, gamma_or_log_alpha, S0, z0, chunk,
-                          out, S_final, z_final, workspace, ws_bytes, stream);
+                          nullptr, out, S_final, z_final, workspace, ws_bytes, stream);
+}
+
+la_status la_chunk_fwd_groupnorm(const la_desc* d, const void* q, const void* k, const void* v,
+                                 int gate_mode, const float* gamma_or_log_alpha, const float* S0,
+                                 const float* z0, int chunk, const la_groupnorm* gn, void* out,
+                                 float* S_final, float* z_final, void* workspace, size_t ws_bytes,
+                                 void* stream) {
+    g_errmsg[0] = '\0';
+    const la_status st = check_desc(d);
+    if (st != LA_OK) return st;
+    if (!gn) return fail(LA_ERR_INVALID, "the group-norm description is NULL");
+    return chunk_fwd_impl(d, nullptr, 0, q, k, v, gate_mode, gamma_or_log_alpha, S0, z0, chunk,
+                          gn, out, S_final, z_final, workspace, ws_bytes, stream);
 }
 
 la_status la_chunk_fwd_varlen(const la_desc* d, const int* cu_seqlens, int max_seqlen,
@@ -349,7 +376,7 @@ la_status la_chunk_fwd_varlen(const la_desc* d, const int* cu_seqlens, int max_s
     const la_status st = check_varlen(d, cu_seqlens, max_seqlen);
     if (st != LA_OK) return st;
     return chunk_fwd_impl(d, cu_seqlens, max_seqlen, q, k, v, gate_mode, gamma_or_log_alpha, S0,
-                          z0, chunk, out, S_final, z_final, workspace, ws_bytes, stream);
+                          z0, chunk, nullptr, out, S_final, z_final, workspace, ws_bytes, stream);
 }
 
 size_t la_chunk_fwd_varlen_workspace_bytes(const la_desc* d, int max_seqlen, int chunk) {

@@ -26,6 +26,10 @@ struct ChunkParams {
     float* ws_a;            // [BH, P, dk]    segment decay products
     float* ws_z;            // [BH, P, dk]    segment normaliser parts
     const int* cu_seqlens;  // packed sequences: [B + 1] token offsets into each head's L tokens, or null
+    const float* gn_w;      // output group norm: per-channel scale [H, dv] or null (ones)
+    const float* gn_b;      //   per-channel shift [H, dv] or null (zeros)
+    const void* gn_gate;    //   swish gate [BH, L, dv] dtype, or null
+    float gn_eps;
     void* st_rows;          // backward: state at every chunk boundary [BH, st_slots, dk, dv] dtype
     int st_slots;           // boundary slots per (b,h)
     int L, H, BH;
@@ -71,7 +75,10 @@ struct BwdParams {
 // Passes of the chunk kernel.  MAIN and STATE serve the forward; the
 // backward adds the reversed state pass and the two passes that store the
 // state (or its gradient) at every chunk boundary.
-enum ChunkPass { PASS_MAIN = 0, PASS_STATE = 1, PASS_STATE_REV = 2, PASS_STORE = 3, PASS_STORE_REV = 4 };
+enum ChunkPass {
+    PASS_MAIN = 0, PASS_STATE = 1, PASS_STATE_REV = 2, PASS_STORE = 3, PASS_STORE_REV = 4,
+    PASS_MAIN_NORM = 5   // main pass with the group-norm / swish-gate output epilogue (chunk 64)
+};
 
 // Chunk length of the backward: 64 tokens, 32 for fp32 at d = 128 (whose
 // six tiles of 64 tokens would not fit in the 160 KiB of LDS).

@@ -248,3 +248,16 @@ def test_varlen_workspace_plans_for_the_longest_sequence():
     assert api.la_chunk_fwd_varlen_workspace_bytes(d, 1501, 64) == 0   # invalid
     assert _varlen(d, max_seqlen=1000, ws=None) == api.LA_ERR_INVALID
     assert _varlen(d, max_seqlen=1000, ws=A, ws_bytes=need - 16) == api.LA_ERR_INVALID
+
+
+def test_groupnorm_validation():
+    d = _desc(L=128)
+    gn = api.LaGroupNorm(None, None, None, 1e-5)
+    call = lambda g, chunk=64, desc=d: api.la_chunk_fwd_groupnorm(
+        desc, A, A, A, 0, None, None, None, chunk, g, A, None, None, None, 0, None)
+    assert call(None) == api.LA_ERR_INVALID
+    assert call(gn, chunk=32) == api.LA_ERR_UNSUPPORTED
+    assert call(api.LaGroupNorm(None, None, None, 0.0)) == api.LA_ERR_INVALID
+    assert call(api.LaGroupNorm(MIS, None, None, 1e-5)) == api.LA_ERR_INVALID
+    assert call(api.LaGroupNorm(None, None, MIS, 1e-5)) == api.LA_ERR_INVALID
+    assert call(gn, desc=_desc(L=0)) == api.LA_ERR_INVALID

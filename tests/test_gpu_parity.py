@@ -218,3 +218,88 @@ def test_prefill_then_decode_hand_off():
                      log_alpha=to_host64(inp["log_alpha"]))
     assert slice_rel_err(to_host64(o)[:, :, None], ref[0][:, :, L:]) <= 2e-2
     assert slice_rel_err(to_host64(full)[:, :, L:], to_host64(o)[:, :, None]) <= 2e-2
+
+
+# ------------------------------------------------------------------ retention output epilogue
+
+def _gn_case(B, H, L, d, dtype, mode, seed, with_affine=True, with_gate=True):
+    inp = _inputs(B, H, L, d, dtype, mode, seed=seed)
+    gen = workloads.generator(seed + 99)
+    w = (1.0 + 0.5 * torch.randn((H, d), generator=gen)) if with_affine else None
+    b = 0.3 * torch.randn((H, d), generator=gen) if with_affine else None
+    gate = torch.randn((B, H, L, d), generator=gen).to(dtype) if with_gate else None
+    return inp, w, b, gate
+
+
+def _gn_run(inp, mode, w, b, gate, eps, phi=0, normalize=False, segments=0):
+    dev = "cuda"
+    g = lambda x: None if x is None else x.to(dev)
+    la = g(inp["log_alpha"]) if mode in (DIAG, SCALAR) else None
+    out, S, _ = api.chunk_fwd(g(inp["q"]), g(inp["k"]), g(inp["v"]), gate_mode=mode,
+                              gamma=inp["gamma"], log_alpha=la, chunk=64, phi=phi,
+                              normalize=normalize, segments=segments,
+                              groupnorm=dict(weight=g(w), bias=g(b), gate=g(gate), eps=eps))
+    torch.cuda.synchronize()
+    ref_o, ref_S, _ = oracle.run(
+        *(to_host64(inp[x]) for x in ("q", "k", "v")), gate_mode=mode,
+        gamma=inp["gamma"].double().numpy() if mode == GAMMA else None,
+        log_alpha=to_host64(inp["log_alpha"]) if mode in (DIAG, SCALAR) else None,
+        phi=phi, normalize=normalize, nthreads=8)
+    ref = oracle.groupnorm_swish(ref_o, None if w is None else to_host64(w),
+                                 None if b is None else to_host64(b),
+                                 None if gate is None else to_host64(gate), eps)
+    return to_host64(out), to_host64(S), ref, ref_S
+
+
+@pytest.mark.parametrize("segments", [1, 0])
+@pytest.mark.parametrize("mode", [NONE, GAMMA, DIAG, SCALAR])
+@pytest.mark.parametrize("dt,d", [("f32", 16), ("f32", 128), ("bf16", 64), ("bf16", 128)])
+def test_groupnorm_swish_epilogue(dt, d, mode, segments):
+    # one segment: six chunks in one workgroup; automatic: one chunk each
+    dtype = DTYPES[dt]
+    inp, w, b, gate = _gn_case(2, 2, 5 * 64 + 7, d, dtype, mode, seed=d + mode)
+    got, S, ref, ref_S = _gn_run(inp, mode, w, b, gate, 1e-5, segments=segments)
+    tol = TOL[dtype]
+    e = slice_rel_err(got, ref)
+    print(f"groupnorm {dt} d={d} mode={mode}: out {e:.2e}")
+    assert e <= tol
+    assert slice_rel_err(S, ref_S) <= tol    # the state is unaffected
+
+
+def test_groupnorm_without_gate_and_affine_and_with_normaliser():
+    inp, w, b, gate = _gn_case(1, 3, 200, 64, torch.float32, NONE, seed=5, with_affine=False,
+                               with_gate=False)
+    got, _, ref, _ = _gn_run(inp, NONE, w, b, gate, 1e-3, phi=api.LA_PHI_ELU1, normalize=True)
+    assert slice_rel_err(got, ref) <= 1e-4
+    # plain standardisation: every token's head output has mean 0
+    assert np.abs(got.mean(axis=-1)).max() < 1e-4
+
+
+def test_groupnorm_retention_workload_sampled():
+    # the retention workload (B=2, H=16, L=8192, d=128, bf16, multi-scale
+    # gamma) with the epilogue; the oracle checks three sampled heads
+    name = "retention_B2H16_L8192_d128"
+    wl = workloads.WORKLOADS[name]
+    inp = workloads.workload_inputs(name, seed=0)
+    gen = workloads.generator(404)
+    H, d = wl.H, wl.dv
+    w = 1.0 + 0.5 * torch.randn((H, d), generator=gen)
+    b = 0.3 * torch.randn((H, d), generator=gen)
+    gate = torch.randn((wl.B, H, wl.L, d), generator=gen).to(torch.bfloat16)
+    dev = "cuda"
+    out, _, _ = api.chunk_fwd(inp["q"].to(dev), inp["k"].to(dev), inp["v"].to(dev),
+                              gate_mode=GAMMA, gamma=inp["gamma"], chunk=64,
+                              groupnorm=dict(weight=w.to(dev), bias=b.to(dev),
+                                             gate=gate.to(dev), eps=1e-5))
+    torch.cuda.synchronize()
+    got = to_host64(out)
+    for pair in (0, 9, 31):
+        bb, h = divmod(pair, H)
+        sl = lambda x: to_host64(x)[bb:bb + 1, h:h + 1]
+        o, _, _ = oracle.run(sl(inp["q"]), sl(inp["k"]), sl(inp["v"]), gate_mode=GAMMA,
+                             gamma=[float(inp["gamma"][h])])
+        ref = oracle.groupnorm_swish(o, to_host64(w)[h:h + 1], to_host64(b)[h:h + 1],
+                                     sl(gate), 1e-5)
+        e = slice_rel_err(got[bb:bb + 1, h:h + 1], ref)
+        print(f"retention groupnorm pair {pair}: {e:.2e}")
+        assert e <= TOL[torch.bfloat16]

@@ -442,3 +442,26 @@ def test_every_planted_mistake_is_caught(name):
     with oracle.mutation(name):
         failed = _pin_failures()
     assert failed, f"planted mistake {name!r} passed every pin"
+
+
+def test_groupnorm_swish_matches_library_routines():
+    # the epilogue is torch's group_norm (one group per head, over d_v) and
+    # silu, applied per token; computed here by the library in fp64
+    import torch
+    rng = np.random.default_rng(17)
+    B, H, L, dv = 2, 3, 5, 8
+    out = rng.standard_normal((B, H, L, dv)) * 3 + 1
+    w, b = rng.standard_normal((H, dv)), rng.standard_normal((H, dv))
+    gate = rng.standard_normal((B, H, L, dv))
+    got = oracle.groupnorm_swish(out, w, b, gate, eps=1e-3)
+    x = torch.tensor(out).permute(0, 2, 1, 3).reshape(B * L, H * dv)
+    y = torch.nn.functional.group_norm(x, H, torch.tensor(w).reshape(-1),
+                                       torch.tensor(b).reshape(-1), eps=1e-3)
+    y = y.reshape(B, L, H, dv).permute(0, 2, 1, 3)
+    ref = (y * torch.nn.functional.silu(torch.tensor(gate))).numpy()
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-12)
+    # without weight, bias and gate it is the plain standardisation
+    plain = oracle.groupnorm_swish(out, eps=1e-3)
+    assert np.allclose(plain.mean(axis=-1), 0, atol=1e-12)
+    assert np.allclose((plain ** 2).mean(axis=-1), out.var(axis=-1) / (out.var(axis=-1) + 1e-3),
+                       rtol=1e-12)
