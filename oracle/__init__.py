@@ -13,6 +13,7 @@ Forms (all compute the same function; see ``oracle.c`` for the citations):
 * :func:`chunkwise`  -- the chunkwise form with a ragged last chunk.
 * :func:`backward`   -- reverse-mode derivative of the token loop (no
   normaliser): dq, dk, dv, d log_alpha, dS0 from dout and dS_final.
+* :func:`delta_run`  -- the delta rule's token loop (DeltaNet recurrence).
 * :func:`groupnorm_swish` -- retention's output epilogue (group norm over
   each token's head output, times swish of a gate), numpy fp64.
 
@@ -57,6 +58,8 @@ MUTATIONS = {
     "gamma_squared": 10,
     "bwd_no_decay": 11,
     "bwd_dq_prev": 12,
+    "delta_no_erase": 13,
+    "delta_erase_after": 14,
 }
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -93,6 +96,8 @@ def _load():
         lib.oracle_backward.argtypes = [i, i, i, i, i, i, dp, dp, i, dp, dp, dp, dp, dp, dp,
                                         dp, dp, dp, dp, dp, i, i]
         lib.oracle_backward.restype = ctypes.c_int
+        lib.oracle_delta_run.argtypes = [i, i, i, i, i, dp, dp, dp, dp, dp, dp, dp, i, i]
+        lib.oracle_delta_run.restype = ctypes.c_int
         lib.oracle_multiscale_decays.argtypes = [i, dp]
         lib.oracle_phi.argtypes = [i, ctypes.c_double]
         lib.oracle_phi.restype = ctypes.c_double
@@ -232,6 +237,33 @@ def backward(q, k, v, dout, gate_mode=GATE_NONE, gamma=None, log_alpha=None,
     if two_d:
         res = {n: (a[0, 0] if a is not None else None) for n, a in res.items()}
     return res
+
+
+def delta_run(q, k, v, beta, S0=None, use_delta=True, nthreads=1):
+    """The delta rule's token loop: S_t = (I - beta_t k_t k_t^T) S_{t-1} +
+    beta_t k_t v_t^T, o_t = q_t^T S_t.  q, k [B,H,L,dk], v [B,H,L,dv], beta
+    [B,H,L] (2-D [L,d] / 1-D [L] inputs are one head).  Returns
+    ``(out, S_final)`` in fp64."""
+    lib = _load()
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    two_d = q.ndim == 2
+    if two_d:
+        q, k, v = q[None, None], k[None, None], v[None, None]
+    B, H, L, dk = q.shape
+    dv = v.shape[3]
+    b = np.ascontiguousarray(_f64(beta).reshape(B, H, L))
+    S0 = _f64(S0)
+    if S0 is not None:
+        S0 = np.ascontiguousarray(S0.reshape(B, H, dk, dv))
+    out = np.zeros((B, H, L, dv))
+    S = np.zeros((B, H, dk, dv))
+    rc = lib.oracle_delta_run(B, H, L, dk, dv, _ptr(b), _ptr(q), _ptr(k), _ptr(v), _ptr(S0),
+                              _ptr(out), _ptr(S), int(bool(use_delta)), int(nthreads))
+    if rc != 0:
+        raise ValueError(f"oracle rejected its arguments (rc={rc})")
+    if two_d:
+        return out[0, 0], S[0, 0]
+    return out, S
 
 
 def groupnorm_swish(out, weight=None, bias=None, gate=None, eps=1e-5):

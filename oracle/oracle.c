@@ -64,6 +64,8 @@
  * normalised read-out has no backward here.  None of this comes from the
  * pages (they give no gradients); it is the plain derivative of the loop.
  *
+ * oracle_delta_run is the delta rule's token loop (see form 4 below).
+ *
  * The global `oracle_mutation` plants a known mistake for the mutation tests
  * that prove the pins can catch it; it is 0 (no mutation) everywhere else.
  */
@@ -89,7 +91,9 @@ enum {
     MUT_STATE_OFF_BY_1 = 9,/* chunkwise: carried state decayed c-1     */
     MUT_GAMMA_SQUARED = 10,/* retention gate applied twice per token  */
     MUT_BWD_NO_DECAY = 11, /* backward: G not decayed by a_t           */
-    MUT_BWD_DQ_PREV = 12   /* backward: dq read from S_{t-1}           */
+    MUT_BWD_DQ_PREV = 12,  /* backward: dq read from S_{t-1}           */
+    MUT_DELTA_NO_ERASE = 13,   /* delta rule: erase term dropped       */
+    MUT_DELTA_ERASE_AFTER = 14 /* delta rule: erase applied after write */
 };
 
 int oracle_mutation = 0;
@@ -125,7 +129,10 @@ typedef struct {
     double *dq, *dk_out, *dv_out;           /* [B,H,L,dk|dv]          */
     double *dlog_alpha, *dS0;               /* [B,H,L,dk], [B,H,dk,dv] (may be NULL) */
     int ck;                                 /* checkpoint spacing      */
-    int form;                /* 0 loop, 1 parallel, 2 chunkwise, 3 backward */
+    /* delta rule (form 4) */
+    const double* beta;                     /* [B,H,L] write strengths */
+    int use_delta;                          /* 0: additive S += k v^T  */
+    int form;                /* 0 loop, 1 parallel, 2 chunkwise, 3 backward, 4 delta */
     int nthreads;
     int next_pair;           /* work counter (guarded by mu) */
     pthread_mutex_t mu;
@@ -478,6 +485,60 @@ static void run_backward_pair(const job_t* J, int bh) {
     free(cp); free(S); free(blk); free(G);
 }
 
+/* ---------------------------------------------------------------------- */
+/* Form 4: the delta rule ("linear_sparse_attention.py", function          */
+/* delta_rule_recurrent).  The page writes S_t = S_{t-1}(I - beta_t k_t     */
+/* k_t^T) + beta_t v_t k_t^T with S indexed [d_v][d_k]; in the [d_k][d_v]  */
+/* orientation used everywhere here that is                                 */
+/*     S_t = (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T,              */
+/* first erasing what the state returns for k_t, then writing v_t there.    */
+/* The erase is applied as S - beta k (k^T S), the same product.  Keys are  */
+/* used as given (the page's function assumes the caller normalised them). */
+/* The read-out o_t = q_t^T S_t after the update follows the rest of the   */
+/* pages (the page's function returns the states only).  use_delta = 0     */
+/* drops the erase (additive linear attention, the page's fallback).       */
+/* ---------------------------------------------------------------------- */
+static void run_delta_pair(const job_t* J, int bh) {
+    const int L = J->L, dk = J->dk, dv = J->dv;
+    double* S = (double*)calloc((size_t)dk * dv, sizeof(double));
+    double* u = (double*)malloc(sizeof(double) * dv);
+    if (J->S0) memcpy(S, J->S0 + (size_t)bh * dk * dv, sizeof(double) * dk * dv);
+    for (int t = 0; t < L; ++t) {
+        const double* qt = J->q + ((size_t)bh * L + t) * dk;
+        const double* kt = J->k + ((size_t)bh * L + t) * dk;
+        const double* vt = J->v + ((size_t)bh * L + t) * dv;
+        const double b = J->beta[(size_t)bh * L + t];
+        const int erase = J->use_delta && oracle_mutation != MUT_DELTA_NO_ERASE;
+        const int after = oracle_mutation == MUT_DELTA_ERASE_AFTER;
+        if (erase && !after) {
+            /* u = S^T k: what the state returns for k_t */
+            for (int j = 0; j < dv; ++j) u[j] = 0.0;
+            for (int i = 0; i < dk; ++i)
+                for (int j = 0; j < dv; ++j) u[j] += kt[i] * S[(size_t)i * dv + j];
+            for (int i = 0; i < dk; ++i)
+                for (int j = 0; j < dv; ++j) S[(size_t)i * dv + j] -= b * kt[i] * u[j];
+        }
+        for (int i = 0; i < dk; ++i)
+            for (int j = 0; j < dv; ++j) S[(size_t)i * dv + j] += b * kt[i] * vt[j];
+        if (erase && after) {
+            for (int j = 0; j < dv; ++j) u[j] = 0.0;
+            for (int i = 0; i < dk; ++i)
+                for (int j = 0; j < dv; ++j) u[j] += kt[i] * S[(size_t)i * dv + j];
+            for (int i = 0; i < dk; ++i)
+                for (int j = 0; j < dv; ++j) S[(size_t)i * dv + j] -= b * kt[i] * u[j];
+        }
+        double* ot = J->out + ((size_t)bh * L + t) * dv;
+        for (int j = 0; j < dv; ++j) {
+            double acc = 0.0;
+            for (int i = 0; i < dk; ++i) acc += qt[i] * S[(size_t)i * dv + j];
+            ot[j] = acc;
+        }
+    }
+    if (J->S_final) memcpy(J->S_final + (size_t)bh * dk * dv, S, sizeof(double) * dk * dv);
+    free(u);
+    free(S);
+}
+
 static void* worker(void* arg) {
     job_t* J = (job_t*)arg;
     const int npairs = J->B * J->H;
@@ -489,7 +550,8 @@ static void* worker(void* arg) {
         if (J->form == 0) run_loop_pair(J, bh);
         else if (J->form == 1) run_parallel_pair(J, bh);
         else if (J->form == 2) run_chunk_pair(J, bh);
-        else run_backward_pair(J, bh);
+        else if (J->form == 3) run_backward_pair(J, bh);
+        else run_delta_pair(J, bh);
     }
     return NULL;
 }
@@ -501,6 +563,7 @@ static int run_job(job_t* J) {
     if (J->form == 2 && J->chunk < 1) return 1;
     if (J->form == 3 && (J->normalize || J->ck < 1 || !J->dout || !J->dq || !J->dk_out || !J->dv_out))
         return 1;
+    if (J->form == 4 && (!J->beta || !J->out)) return 1;
     const int npairs = J->B * J->H;
     int nt = J->nthreads < 1 ? 1 : J->nthreads;
     if (nt > npairs) nt = npairs;
@@ -577,5 +640,22 @@ int oracle_backward(int B, int H, int L, int dk, int dv, int gate_mode,
     J.dout = dout; J.dS_final = dS_final;
     J.dq = dq; J.dk_out = dk_out; J.dv_out = dv_out;
     J.dlog_alpha = dlog_alpha; J.dS0 = dS0; J.ck = ck;
+    return run_job(&J);
+}
+
+/* The delta rule's token loop (form 4): out [B,H,L,dv] and S_final
+ * [B,H,dk,dv] (may be NULL) from q, k [B,H,L,dk], v [B,H,L,dv], the write
+ * strengths beta [B,H,L] and S0 (may be NULL).  use_delta = 0 gives the
+ * additive fallback. */
+int oracle_delta_run(int B, int H, int L, int dk, int dv, const double* beta,
+                     const double* q, const double* k, const double* v,
+                     const double* S0, double* out, double* S_final,
+                     int use_delta, int nthreads) {
+    const int gate_mode = GATE_NONE, phi = PHI_IDENTITY, normalize = 0;
+    const double *gamma = NULL, *log_alpha = NULL, *z0 = NULL;
+    double* z_final = NULL;
+    FILL_JOB(4, 0, nthreads)
+    J.beta = beta;
+    J.use_delta = use_delta;
     return run_job(&J);
 }

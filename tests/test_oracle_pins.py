@@ -435,9 +435,10 @@ def test_pins_pass_on_the_correct_oracle():
     assert _pin_failures() == []
 
 
-# mistakes planted in the backward are caught by the backward's own pins
-# (finite differences, in test_oracle_backward.py)
-@pytest.mark.parametrize("name", sorted(m for m in oracle.MUTATIONS if not m.startswith("bwd_")))
+# mistakes planted in the backward and in the delta rule are caught by their
+# own pins (test_oracle_backward.py, test_oracle_delta.py)
+@pytest.mark.parametrize("name", sorted(m for m in oracle.MUTATIONS
+                                        if not m.startswith(("bwd_", "delta_"))))
 def test_every_planted_mistake_is_caught(name):
     with oracle.mutation(name):
         failed = _pin_failures()
