@@ -276,6 +276,46 @@ la_status la_decode_step(const la_desc* d, const void* q, const void* k,
                          const void* v, int gate_mode, const float* gate,
                          float* S, float* z, void* out, void* stream);
 
+/*
+ * The delta rule (DeltaNet; "linear_sparse_attention.py", function
+ * delta_rule_recurrent):
+ *     S_t = (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T,
+ *     o_t = q_t^T S_t
+ * in the [dk][dv] state orientation used throughout (the page writes the
+ * transpose): each token first erases what the state returns for k_t, then
+ * writes v_t there with strength beta_t.  Keys are used as given (the page's
+ * function assumes the caller normalised them); there is no feature map and
+ * no normaliser (d->phi must be LA_PHI_IDENTITY, d->normalize 0, else
+ * LA_ERR_UNSUPPORTED).  d->segments is ignored: each (b,h) runs its chunks
+ * in order.
+ *
+ * la_delta_fwd -- prefill, in the chunkwise form with the triangular
+ * factorisation of each chunk's erase products (chunk length
+ * la_delta_chunk(d)).
+ *   q, k     device [B,H,L,dk] of d->dtype;  v, out  device [B,H,L,dv]
+ *   beta     device fp32 [B,H,L] write strengths (not validated; the page
+ *            uses beta in [0, 1])
+ *   S0       device fp32 [B,H,dk,dv] or NULL (zeros)
+ *   S_final  device fp32 [B,H,dk,dv] or NULL; may alias S0
+ * No workspace.
+ */
+la_status la_delta_fwd(const la_desc* d, const void* q, const void* k,
+                       const void* v, const float* beta, const float* S0,
+                       void* out, float* S_final, void* stream);
+
+/*
+ * la_delta_decode_step -- one token per (b,h) folded into the resident
+ * state S (device fp32 [B,H,dk,dv], updated in place); q, k, v device
+ * [B,H,dk|dv] of d->dtype, beta device fp32 [B,H], out device [B,H,dv].
+ * d->L must be 1.
+ */
+la_status la_delta_decode_step(const la_desc* d, const void* q, const void* k,
+                               const void* v, const float* beta, float* S,
+                               void* out, void* stream);
+
+/* Chunk length la_delta_fwd uses for this shape (0 if invalid). */
+int la_delta_chunk(const la_desc* d);
+
 /* Static description of a status code. */
 const char* la_status_string(la_status s);
 
@@ -291,7 +331,7 @@ int la_version(void);
  * of HIP events recorded on the stream it is launched on.  la_profile_query
  * waits for those events and reports, for one kernel family
  * ("chunk_main", "chunk_state", "state_scan", "decode", "chunk_store",
- * "chunk_bwd"), the number of
+ * "chunk_bwd", "delta_chunk", "delta_decode"), the number of
  * launches and their summed duration in milliseconds.  la_profile_begin
  * clears earlier records.  Event creation happens inside la_profile_begin /
  * the first profiled launch; not for use under graph capture.

@@ -32,7 +32,7 @@ EXPORTED = (
     "la_version", "la_profile_begin", "la_profile_end", "la_profile_query",
     "la_chunk_bwd", "la_chunk_bwd_workspace_bytes", "la_chunk_bwd_chunk",
     "la_chunk_fwd_varlen", "la_chunk_fwd_varlen_workspace_bytes",
-    "la_chunk_fwd_groupnorm",
+    "la_chunk_fwd_groupnorm", "la_delta_fwd", "la_delta_decode_step", "la_delta_chunk",
 )
 
 
@@ -80,6 +80,12 @@ def load_library():
     lib.la_chunk_fwd_groupnorm.argtypes = [dp, vp, vp, vp, i, vp, vp, vp, i,
                                             ctypes.POINTER(LaGroupNorm), vp, vp, vp, vp, sz, vp]
     lib.la_chunk_fwd_groupnorm.restype = i
+    lib.la_delta_fwd.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.la_delta_fwd.restype = i
+    lib.la_delta_decode_step.argtypes = [dp, vp, vp, vp, vp, vp, vp, vp]
+    lib.la_delta_decode_step.restype = i
+    lib.la_delta_chunk.argtypes = [dp]
+    lib.la_delta_chunk.restype = i
     lib.la_chunk_fwd_varlen.argtypes = [dp, vp, i, vp, vp, vp, i, vp, vp, vp, i, vp, vp, vp,
                                          vp, sz, vp]
     lib.la_chunk_fwd_varlen.restype = i
@@ -138,6 +144,20 @@ def la_chunk_fwd_groupnorm(desc, q, k, v, gate_mode, gamma_or_log_alpha, S0, z0,
         ctypes.byref(desc), q, k, v, int(gate_mode), gamma_or_log_alpha, S0, z0, int(chunk),
         None if gn is None else ctypes.byref(gn), out, S_final, z_final, workspace,
         int(workspace_bytes), stream)
+
+
+def la_delta_fwd(desc, q, k, v, beta, S0, out, S_final, stream):
+    """Raw call; pointer arguments are ints (0 = NULL) or ctypes pointers."""
+    return load_library().la_delta_fwd(ctypes.byref(desc), q, k, v, beta, S0, out, S_final,
+                                       stream)
+
+
+def la_delta_decode_step(desc, q, k, v, beta, S, out, stream):
+    return load_library().la_delta_decode_step(ctypes.byref(desc), q, k, v, beta, S, out, stream)
+
+
+def la_delta_chunk(desc) -> int:
+    return int(load_library().la_delta_chunk(ctypes.byref(desc)))
 
 
 def la_chunk_fwd_varlen(desc, cu_seqlens, max_seqlen, q, k, v, gate_mode,
@@ -409,6 +429,47 @@ def chunk_fwd_varlen(q, k, v, cu_seqlens, max_seqlen=None, gate_mode=LA_GATE_NON
     _check(st)
     del g_keep
     return out, S_final, z_final
+
+
+def delta_fwd(q, k, v, beta, S0=None, out=None, S_final=None, return_state=True,
+              stream=None):
+    """Delta-rule prefill.  q, k: [B,H,L,dk]; v: [B,H,L,dv] (bf16 or fp32 on
+    the GPU); beta: fp32 [B,H,L].  Returns ``(out, S_final)``."""
+    torch = _torch()
+    B, H, L, dk = q.shape
+    dv = v.shape[-1]
+    desc = make_desc(B, H, L, dk, dv, _la_dtype(q), LA_PHI_IDENTITY, False, 0)
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, H, L, dv), dtype=q.dtype, device=dev)
+    if return_state and S_final is None:
+        S_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    st = la_delta_fwd(
+        desc, _dev_ptr(q, "q"), _dev_ptr(k, "k", q.dtype, (B, H, L, dk)),
+        _dev_ptr(v, "v", q.dtype, (B, H, L, dv)), _dev_ptr(beta, "beta", torch.float32, (B, H, L)),
+        _dev_ptr(S0, "S0", torch.float32, (B, H, dk, dv)),
+        _dev_ptr(out, "out", q.dtype, (B, H, L, dv)),
+        _dev_ptr(S_final, "S_final", torch.float32, (B, H, dk, dv)), _stream_ptr(stream, dev))
+    _check(st)
+    return out, S_final
+
+
+def delta_decode_step(q, k, v, beta, S, out=None, stream=None):
+    """One delta-rule step.  q, k: [B,H,dk]; v: [B,H,dv]; beta: fp32 [B,H];
+    S: fp32 [B,H,dk,dv] (updated in place).  Returns ``out`` [B,H,dv]."""
+    torch = _torch()
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    desc = make_desc(B, H, 1, dk, dv, _la_dtype(q), LA_PHI_IDENTITY, False, 0)
+    if out is None:
+        out = torch.empty((B, H, dv), dtype=q.dtype, device=q.device)
+    st = la_delta_decode_step(
+        desc, _dev_ptr(q, "q"), _dev_ptr(k, "k", q.dtype, (B, H, dk)),
+        _dev_ptr(v, "v", q.dtype, (B, H, dv)), _dev_ptr(beta, "beta", torch.float32, (B, H)),
+        _dev_ptr(S, "S", torch.float32, (B, H, dk, dv)), _dev_ptr(out, "out", q.dtype, (B, H, dv)),
+        _stream_ptr(stream, q.device))
+    _check(st)
+    return out
 
 
 def chunk_bwd(q, k, v, dout, gate_mode=LA_GATE_NONE, gamma=None, log_alpha=None,

@@ -1,0 +1,6 @@
+// delta_f32_d16.hip -- delta-rule kernels for d_k = d_v = 16, fp32 inputs.
+#include "delta_kernel.h"
+
+namespace la {
+LA_DEFINE_DELTA_LAUNCHER(launch_delta_f32_d16, 16, false)
+}  // namespace la

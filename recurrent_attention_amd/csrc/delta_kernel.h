@@ -1,0 +1,453 @@
+// delta_kernel.h -- the delta rule (DeltaNet recurrence of
+// "linear_sparse_attention.py", function delta_rule_recurrent) on gfx950:
+//
+//   S_t = (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T,   o_t = q_t^T S_t
+//
+// in the [d_k][d_v] state orientation of the rest of the library (the page
+// writes the transpose).  Keys are used as given.
+//
+// Prefill, chunkwise (the pages give the recurrence only; this is the
+// standard triangular factorisation of the product of the chunk's erase
+// matrices, restated): for a chunk of C tokens with state S before it,
+//   A  = strict_lower(diag(beta) K K^T),  T = (I + A)^-1 diag(beta)
+//   W  = T K,  U = T V,  U' = U - W S
+//   O  = Q S + (Q K^T * inclusive causal mask) U',   S <- S + K^T U'
+// because the chunk's product of (I - beta k k^T) factors is I - K^T W and
+// its accumulated writes are K^T U.  Everything but T is a dense product on
+// the matrix cores; T is formed in fp32 by blocked forward substitution
+// (16 x 16 diagonal blocks inverted by one lane per column, the blocks
+// below them by fp32 matrix-core products, one block diagonal at a time).
+//
+// One workgroup per (b,h) runs the chunks in order (the chunk-to-chunk map
+// S -> (I - K^T W) S + K^T U is a full d_k x d_k matrix, so the segment
+// split of the gated kernels does not carry over cheaply).  Wave w owns
+// value columns [16w, 16w+16): its state block stays in fp32 accumulators
+// and it produces those columns of U' and of the outputs.
+//
+// Decode: one workgroup per (b,h) streams its fp32 state once:
+//   u = S^T k, w = S^T q (one reduction pass), S += beta k (v - u)^T,
+//   o = w + beta (q . k) (v - u).
+#pragma once
+
+#include "la_device.h"
+#include "la_internal.h"
+#include "tile_ops.h"
+
+namespace la {
+
+template <int D_, int C_, bool BF16_>
+struct DeltaCfg {
+    static constexpr int D = D_, C = C_;
+    static constexpr bool BF16 = BF16_;
+    using T = Elem<BF16>;
+    using E = typename T::E;
+    using Frag = typename T::Frag;
+    static constexpr int NW = D / 16;                  // waves: one value block each
+    static constexpr int NT = 64 * NW;
+    static constexpr int TB = C / 16, NBLK = C / 16, MB = D / 16;
+    static constexpr int KPL = T::KPL, MK = T::MK;
+    static constexpr int UE = 16 / (int)sizeof(E);
+    static constexpr int DU = D / UE, TU = C / UE;
+    static constexpr int DMASK = (DU < 8 ? DU : 8) - 1;
+    static constexpr int TMASK = (TU < 8 ? TU : 8) - 1;
+    static constexpr int RUNS = D / 4;                 // 4-channel runs per token row
+    static constexpr int RPP = NT / RUNS;              // token rows per load pass (16)
+    static constexpr int NPASS = C / RPP;
+    static constexpr int RW = 4 * (int)sizeof(E) / 4;  // words of a 4-channel run
+    static_assert(D % 16 == 0 && C % 16 == 0 && C % MK == 0, "tile shape");
+    static_assert(!BF16 || D % 32 == 0, "bf16 needs d >= 32");
+    static_assert(NT % RUNS == 0 && C % RPP == 0, "load mapping");
+};
+
+template <class Cfg>
+struct DeltaSmem {
+    using E = typename Cfg::E;
+    static constexpr int C = Cfg::C, D = Cfg::D;
+    alignas(16) E q[C][D];        // Q   [t][swizzled i]
+    alignas(16) E k[C][D];        // K   [s][swizzled i]
+    alignas(16) E v[C][D];        // V   [s][swizzled n]
+    alignas(16) E w[C][D];        // W   [s][swizzled i]
+    alignas(16) E up[C][D];       // U'  [s][swizzled n]
+    alignas(16) E pm[C][C];       // P = Q K^T * mask  [t][swizzled s]
+    alignas(16) E tm[C][C];       // T   [s][swizzled j]
+    alignas(16) float lm[C][C];   // A (strictly lower)
+    alignas(16) float nm[C][C];   // (I + A)^-1
+    alignas(16) float xs[Cfg::NW][16][16];   // per-wave staging of a 16 x 16 block
+    float beta[C];
+};
+
+template <class Cfg>
+__global__ __launch_bounds__(Cfg::NT) void delta_chunk_kernel(const DeltaParams p) {
+    constexpr int D = Cfg::D, C = Cfg::C, TB = Cfg::TB, NW = Cfg::NW, NBLK = Cfg::NBLK;
+    constexpr int MB = Cfg::MB, MK = Cfg::MK, KPL = Cfg::KPL, RW = Cfg::RW;
+    constexpr int RUNS = Cfg::RUNS, NPASS = Cfg::NPASS, RPP = Cfg::RPP;
+    constexpr int DM = Cfg::DMASK, TM = Cfg::TMASK;
+    constexpr bool BF16 = Cfg::BF16;
+    constexpr int ES = (int)sizeof(typename Cfg::E);
+    using T = typename Cfg::T;
+    using F = Elem<false>;   // fp32 matrix cores for the triangular solve
+    using E = typename Cfg::E;
+    using Frag = typename Cfg::Frag;
+
+    __shared__ DeltaSmem<Cfg> sm;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int r = lane & 15, g = lane >> 4;
+    const int bh = blockIdx.x;
+    const int L = p.L;
+    const int nchunks = (L + C - 1) / C;
+    const int n0 = 16 * wave;   // this wave's value columns
+
+    const size_t rows0 = (size_t)bh * L;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(reinterpret_cast<const E*>(p.q) + rows0 * D, (uint32_t)L * D * ES);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(reinterpret_cast<const E*>(p.k) + rows0 * D, (uint32_t)L * D * ES);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(reinterpret_cast<const E*>(p.v) + rows0 * D, (uint32_t)L * D * ES);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.beta + rows0, (uint32_t)L * 4);
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(reinterpret_cast<E*>(p.out) + rows0 * D, (uint32_t)L * D * ES);
+
+    // the triangular tiles: only their lower parts are ever written
+    for (int i = tid; i < C * C; i += Cfg::NT) {
+        (&sm.pm[0][0])[i] = E(0);
+        (&sm.tm[0][0])[i] = E(0);
+        (&sm.lm[0][0])[i] = 0.f;
+        (&sm.nm[0][0])[i] = 0.f;
+    }
+
+    // state block of this wave: rows 16 mb + 4 g + i, column n0 + r
+    f32x4_t accS[MB];
+    const float* S0 = p.S0 ? p.S0 + (size_t)bh * D * D : nullptr;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            accS[mb][i] = S0 ? S0[(size_t)(16 * mb + 4 * g + i) * D + n0 + r] : 0.f;
+
+    // global -> registers, one chunk ahead: a 4-channel run of q, k, v for
+    // NPASS token rows, and one write strength
+    const int run = tid % RUNS, row0 = tid / RUNS;
+    Words<RW> qr[NPASS], kr[NPASS], vr[NPASS];
+    uint32_t br = 0;
+    auto load = [&](int c) {
+#pragma unroll
+        for (int ps = 0; ps < NPASS; ++ps) {
+            const uint32_t off = (((uint32_t)c * C + row0 + RPP * ps) * D + 4 * run) * ES;
+            qr[ps] = buf_load_words<RW>(rq, off);
+            kr[ps] = buf_load_words<RW>(rk, off);
+            vr[ps] = buf_load_words<RW>(rv, off);
+        }
+        if (tid < C) br = __builtin_amdgcn_raw_buffer_load_b32(rb, ((uint32_t)c * C + tid) * 4, 0, 0);
+    };
+    if (nchunks > 0) load(0);
+
+    for (int c = 0; c < nchunks; ++c) {
+        const int t0 = c * C;
+        // ---- tiles (tokens past the end read as zeros: no key, no write)
+#pragma unroll
+        for (int ps = 0; ps < NPASS; ++ps) {
+            const int t = row0 + RPP * ps;
+            const int pos = bw_pos<Cfg, DM>(t, 4 * run);
+            lds_store_words(&sm.q[t][pos], qr[ps]);
+            lds_store_words(&sm.k[t][pos], kr[ps]);
+            lds_store_words(&sm.v[t][pos], vr[ps]);
+        }
+        if (tid < C) sm.beta[tid] = __uint_as_float(br);
+        __syncthreads();
+        if (c + 1 < nchunks) load(c + 1);
+
+        // ---- A = strict_lower(diag(beta) K K^T) and P = Q K^T * inclusive
+        // mask, computed transposed ([s][t] tiles) so each lane holds 4
+        // consecutive s of one t
+        {
+            int idx = 0;
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+                for (int sb = 0; sb <= tb; ++sb, ++idx) {
+                    if (idx % NW != wave) continue;
+                    f32x4_t ag = {0.f, 0.f, 0.f, 0.f}, ap = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kk = 0; kk < D / MK; ++kk) {
+                        const Frag a = row_frag<Cfg, DM>(&sm.k[0][0], D, 16 * sb, kk * MK, lane);
+                        ag = T::mma(a, row_frag<Cfg, DM>(&sm.k[0][0], D, 16 * tb, kk * MK, lane), ag);
+                        ap = T::mma(a, row_frag<Cfg, DM>(&sm.q[0][0], D, 16 * tb, kk * MK, lane), ap);
+                    }
+                    const int t = 16 * tb + r, s0 = 16 * sb + 4 * g;
+                    const float bt = sm.beta[t];
+                    float xl[4], xp[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        xl[i] = s0 + i < t ? bt * ag[i] : 0.f;
+                        xp[i] = s0 + i <= t ? ap[i] : 0.f;
+                    }
+                    *reinterpret_cast<float4*>(&sm.lm[t][s0]) = make_float4(xl[0], xl[1], xl[2], xl[3]);
+                    store_run<BF16, 4>(&sm.pm[t][bw_pos<Cfg, TM>(t, s0)], xp);
+                }
+        }
+        __syncthreads();
+
+        // ---- (I + A)^-1: diagonal 16 x 16 blocks by forward substitution,
+        // lane j of the block's wave solving for column j
+        for (int blk = wave; blk < NBLK; blk += NW) {
+            if (lane < 16) {
+                const int b0 = 16 * blk, j = lane;
+                float x[16];
+#pragma unroll
+                for (int rr = 0; rr < 16; ++rr) {
+                    float acc = rr == j ? 1.f : 0.f;
+#pragma unroll
+                    for (int cc = 0; cc < rr; ++cc) acc -= sm.lm[b0 + rr][b0 + cc] * x[cc];
+                    x[rr] = acc;
+                }
+#pragma unroll
+                for (int rr = 0; rr < 16; ++rr) sm.nm[b0 + rr][b0 + j] = x[rr];
+            }
+        }
+        __syncthreads();
+        // blocks below the diagonal, one block diagonal at a time:
+        // N_ij = -N_ii sum_{j <= m < i} A_im N_mj
+        for (int dist = 1; dist < NBLK; ++dist) {
+            for (int b = wave; b < NBLK - dist; b += NW) {
+                const int bi = 16 * (b + dist), bj = 16 * b;
+                f32x4_t x = {0.f, 0.f, 0.f, 0.f};
+                for (int m = b; m < b + dist; ++m) {
+                    const int bm = 16 * m;
+#pragma unroll
+                    for (int k4 = 0; k4 < 4; ++k4)
+                        x = F::mma(sm.lm[bi + r][bm + 4 * k4 + g], sm.nm[bm + 4 * k4 + g][bj + r], x);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sm.xs[wave][4 * g + i][r] = x[i];
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+                f32x4_t y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int k4 = 0; k4 < 4; ++k4)
+                    y = F::mma(sm.nm[bi + r][bi + 4 * k4 + g], sm.xs[wave][4 * k4 + g][r], y);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sm.nm[bi + 4 * g + i][bj + r] = -y[i];
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            }
+            __syncthreads();
+        }
+
+        // ---- T = (I + A)^-1 diag(beta), lower blocks only
+        for (int e = tid; e < C * C; e += Cfg::NT) {
+            const int s = e / C, j = e % C;
+            if ((j >> 4) <= (s >> 4)) sm.tm[s][bw_pos<Cfg, TM>(s, j)] = T::fromf(sm.nm[s][j] * sm.beta[j]);
+        }
+        __syncthreads();
+
+        // ---- W^T = K^T T^T: wave w takes key channels [16w, 16w+16)
+#pragma unroll
+        for (int sb = 0; sb < TB; ++sb) {
+            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk <= (16 * sb + 15) / MK; ++kk)
+                acc = T::mma(tr_frag<Cfg, DM>(&sm.k[0][0], D, kk * MK, n0, lane),
+                             row_frag<Cfg, TM>(&sm.tm[0][0], C, 16 * sb, kk * MK, lane), acc);
+            const int s = 16 * sb + r;
+            float xw[4] = {acc[0], acc[1], acc[2], acc[3]};
+            store_run<BF16, 4>(&sm.w[s][bw_pos<Cfg, DM>(s, n0 + 4 * g)], xw);
+        }
+        __syncthreads();
+
+        // ---- the state as an operand: rows n of S^T, k-slots the state rows
+        // held by this lane (32 k2 + 4 g + i and 32 k2 + 16 + 4 g + i)
+        Frag sa[BF16 ? D / 32 : 1];
+        if constexpr (BF16) {
+#pragma unroll
+            for (int k2 = 0; k2 < D / 32; ++k2) {
+                const float x8[8] = {accS[2 * k2][0], accS[2 * k2][1], accS[2 * k2][2], accS[2 * k2][3],
+                                     accS[2 * k2 + 1][0], accS[2 * k2 + 1][1], accS[2 * k2 + 1][2],
+                                     accS[2 * k2 + 1][3]};
+                sa[k2] = T::from8(x8);
+            }
+        }
+        // S^T X^T for the rows s (or t) = 16 xb + r of tile X
+        auto state_times = [&](const E* X, int xb, f32x4_t acc) {
+            const int s = 16 * xb + r;
+            if constexpr (BF16) {
+#pragma unroll
+                for (int k2 = 0; k2 < D / 32; ++k2)
+                    acc = T::mma(sa[k2],
+                                 T::load2x4(X + s * D + bw_pos<Cfg, DM>(s, 32 * k2 + 4 * g),
+                                            X + s * D + bw_pos<Cfg, DM>(s, 32 * k2 + 16 + 4 * g)),
+                                 acc);
+            } else {
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        acc = T::mma(accS[mb][i], X[s * D + bw_pos<Cfg, DM>(s, 16 * mb + 4 * g + i)], acc);
+            }
+            return acc;
+        };
+
+        // ---- U'^T = V^T T^T - S^T W^T for this wave's value columns
+#pragma unroll
+        for (int sb = 0; sb < TB; ++sb) {
+            f32x4_t acc = state_times(&sm.w[0][0], sb, f32x4_t{0.f, 0.f, 0.f, 0.f});
+            acc = -acc;
+#pragma unroll
+            for (int kk = 0; kk <= (16 * sb + 15) / MK; ++kk)
+                acc = T::mma(tr_frag<Cfg, DM>(&sm.v[0][0], D, kk * MK, n0, lane),
+                             row_frag<Cfg, TM>(&sm.tm[0][0], C, 16 * sb, kk * MK, lane), acc);
+            const int s = 16 * sb + r;
+            float xu[4] = {acc[0], acc[1], acc[2], acc[3]};
+            store_run<BF16, 4>(&sm.up[s][bw_pos<Cfg, DM>(s, n0 + 4 * g)], xu);
+        }
+        __syncthreads();
+
+        // ---- O^T = S^T Q^T + U'^T P^T, then S += K^T U'
+        Frag uf[C / MK];
+#pragma unroll
+        for (int kk = 0; kk < C / MK; ++kk) uf[kk] = tr_frag<Cfg, DM>(&sm.up[0][0], D, kk * MK, n0, lane);
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) {
+            f32x4_t acc = state_times(&sm.q[0][0], tb, f32x4_t{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+            for (int kk = 0; kk <= (16 * tb + 15) / MK; ++kk)
+                acc = T::mma(uf[kk], row_frag<Cfg, TM>(&sm.pm[0][0], C, 16 * tb, kk * MK, lane), acc);
+            const uint32_t off = ((uint32_t)(t0 + 16 * tb + r) * D + n0 + 4 * g) * ES;
+            float xo[4] = {acc[0], acc[1], acc[2], acc[3]};
+            buf_store_run4<BF16>(ro, off, xo);
+        }
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int kk = 0; kk < C / MK; ++kk)
+                accS[mb] = T::mma(tr_frag<Cfg, DM>(&sm.k[0][0], D, kk * MK, 16 * mb, lane), uf[kk], accS[mb]);
+        __syncthreads();
+    }
+
+    if (p.S_final) {
+        float* Sf = p.S_final + (size_t)bh * D * D;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Sf[(size_t)(16 * mb + 4 * g + i) * D + n0 + r] = accS[mb][i];
+    }
+}
+
+// Decode: one step of the delta rule per (b,h).
+template <int D>
+struct DeltaDecodeShape {
+    static constexpr int NT = D >= 128 ? 512 : 256;
+};
+
+template <int D, bool BF16>
+__global__ __launch_bounds__((DeltaDecodeShape<D>::NT)) void delta_decode_kernel(const DeltaParams p) {
+    using T = Elem<BF16>;
+    using E = typename T::E;
+    constexpr int NT = DeltaDecodeShape<D>::NT;
+    constexpr int CQ = D / 4;                 // column quads per row
+    constexpr int RPP = NT / CQ;              // rows per pass
+    constexpr int NPASS = (D + RPP - 1) / RPP;
+    static_assert(NT % CQ == 0, "column quads must divide the workgroup");
+
+    __shared__ float sq[D], sk[D], sv[D], su[D], sw[D];
+    __shared__ float4 redu[RPP][CQ], redw[RPP][CQ];
+    __shared__ float sqk;
+
+    const int tid = threadIdx.x;
+    const int bh = blockIdx.x;
+    const E* q = reinterpret_cast<const E*>(p.q) + (size_t)bh * D;
+    const E* k = reinterpret_cast<const E*>(p.k) + (size_t)bh * D;
+    const E* v = reinterpret_cast<const E*>(p.v) + (size_t)bh * D;
+    f32x4_t* S = reinterpret_cast<f32x4_t*>(p.S + (size_t)bh * D * D);
+    const float beta = p.beta[bh];
+
+    const int cq = tid % CQ, rr = tid / CQ;
+    f32x4_t sreg[NPASS];
+#pragma unroll
+    for (int ps = 0; ps < NPASS; ++ps) {
+        const int row = ps * RPP + rr;
+        if (row < D) sreg[ps] = __builtin_nontemporal_load(&S[(size_t)row * CQ + cq]);
+    }
+    if (tid < D) {
+        sq[tid] = T::tof(q[tid]);
+        sk[tid] = T::tof(k[tid]);
+        sv[tid] = T::tof(v[tid]);
+    }
+    __syncthreads();
+
+    // u = S^T k and w = S^T q: this thread's rows, then the row groups
+    float4 pu = make_float4(0.f, 0.f, 0.f, 0.f), pw = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int ps = 0; ps < NPASS; ++ps) {
+        const int row = ps * RPP + rr;
+        if (row < D) {
+            const float kk = sk[row], qq = sq[row];
+            const f32x4_t s = sreg[ps];
+            pu.x += kk * s[0]; pu.y += kk * s[1]; pu.z += kk * s[2]; pu.w += kk * s[3];
+            pw.x += qq * s[0]; pw.y += qq * s[1]; pw.z += qq * s[2]; pw.w += qq * s[3];
+        }
+    }
+    redu[rr][cq] = pu;
+    redw[rr][cq] = pw;
+    if (tid == 0) {
+        float a = 0.f;
+        for (int i = 0; i < D; ++i) a += sq[i] * sk[i];
+        sqk = a;
+    }
+    __syncthreads();
+    if (tid < D) {
+        const int c4 = tid >> 2, e = tid & 3;
+        float u = 0.f, w = 0.f;
+        for (int j = 0; j < RPP; ++j) {
+            const float4 a = redu[j][c4], b = redw[j][c4];
+            u += e == 0 ? a.x : e == 1 ? a.y : e == 2 ? a.z : a.w;
+            w += e == 0 ? b.x : e == 1 ? b.y : e == 2 ? b.z : b.w;
+        }
+        su[tid] = u;
+        sw[tid] = w;
+    }
+    __syncthreads();
+
+    // S += beta k (v - u)^T, o = w + beta (q . k) (v - u)
+    const float4 vv = *reinterpret_cast<const float4*>(&sv[4 * cq]);
+    const float4 uu = *reinterpret_cast<const float4*>(&su[4 * cq]);
+    const float4 dlt = make_float4(beta * (vv.x - uu.x), beta * (vv.y - uu.y),
+                                   beta * (vv.z - uu.z), beta * (vv.w - uu.w));
+#pragma unroll
+    for (int ps = 0; ps < NPASS; ++ps) {
+        const int row = ps * RPP + rr;
+        if (row < D) {
+            const float kk = sk[row];
+            f32x4_t s = sreg[ps];
+            s[0] += kk * dlt.x;
+            s[1] += kk * dlt.y;
+            s[2] += kk * dlt.z;
+            s[3] += kk * dlt.w;
+            __builtin_nontemporal_store(s, &S[(size_t)row * CQ + cq]);
+        }
+    }
+    if (tid < D) {
+        const float o = sw[tid] + beta * sqk * (sv[tid] - su[tid]);
+        reinterpret_cast<E*>(p.out)[(size_t)bh * D + tid] = T::fromf(o);
+    }
+}
+
+// Chunk length of the delta prefill: 64 tokens, 32 for fp32 at d = 128
+// (LDS).
+constexpr int delta_chunk(int d, bool bf16) { return (!bf16 && d >= 128) ? 32 : 64; }
+
+template <int D, bool BF>
+hipError_t launch_delta_dt(const DeltaParams& p, bool decode, hipStream_t s) {
+    if (decode) {
+        hipLaunchKernelGGL((delta_decode_kernel<D, BF>), dim3(p.BH), dim3(DeltaDecodeShape<D>::NT), 0, s, p);
+    } else {
+        using Cfg = DeltaCfg<D, delta_chunk(D, BF), BF>;
+        hipLaunchKernelGGL((delta_chunk_kernel<Cfg>), dim3(p.BH), dim3(Cfg::NT), 0, s, p);
+    }
+    return hipGetLastError();
+}
+
+#define LA_DEFINE_DELTA_LAUNCHER(NAME, D, BF) \
+    hipError_t NAME(const DeltaParams& p, bool decode, hipStream_t s) { return launch_delta_dt<D, BF>(p, decode, s); }
+
+}  // namespace la

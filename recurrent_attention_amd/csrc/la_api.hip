@@ -123,7 +123,8 @@ std::vector<ProfRec> g_prof;
 std::vector<hipEvent_t> g_event_pool;
 
 const char* kKernelNames[la::K_COUNT] = {"chunk_main", "chunk_state", "state_scan", "decode",
-                                         "chunk_store", "chunk_bwd"};
+                                         "chunk_store", "chunk_bwd", "delta_chunk",
+                                         "delta_decode"};
 
 hipEvent_t take_event() {
     if (!g_event_pool.empty()) {
@@ -168,6 +169,27 @@ hipError_t chunk_launch(const la_desc* d, const la::ChunkParams& p, int chunk, i
         default: return bf16 ? la::launch_chunk_bf16_d128(p, chunk, gate, pass, s, nblocks)
                              : la::launch_chunk_f32_d128(p, chunk, gate, pass, s, nblocks);
     }
+}
+
+hipError_t delta_launch(const la_desc* d, const la::DeltaParams& p, bool decode, hipStream_t s) {
+    const bool bf16 = d->dtype == LA_BF16;
+    switch (d->dk) {
+        case 16: return la::launch_delta_f32_d16(p, decode, s);
+        case 32: return bf16 ? la::launch_delta_bf16_d32(p, decode, s) : la::launch_delta_f32_d32(p, decode, s);
+        case 64: return bf16 ? la::launch_delta_bf16_d64(p, decode, s) : la::launch_delta_f32_d64(p, decode, s);
+        default: return bf16 ? la::launch_delta_bf16_d128(p, decode, s) : la::launch_delta_f32_d128(p, decode, s);
+    }
+}
+
+// Shape checks shared by the delta-rule entry points: no feature map, no
+// normaliser (the rule has neither).
+la_status check_delta(const la_desc* d) {
+    const la_status st = check_desc(d);
+    if (st != LA_OK) return st;
+    if (d->phi != LA_PHI_IDENTITY)
+        return fail(LA_ERR_UNSUPPORTED, "the delta rule takes its keys as given (phi must be identity)");
+    if (d->normalize) return fail(LA_ERR_UNSUPPORTED, "the delta rule has no normaliser");
+    return LA_OK;
 }
 
 hipError_t bwd_launch(const la_desc* d, const la::BwdParams& p, int gate, hipStream_t s) {
@@ -515,6 +537,68 @@ la_status la_chunk_bwd(const la_desc* d, const void* q, const void* k, const voi
     std::memcpy(b.log2_gamma, p.log2_gamma, sizeof b.log2_gamma);
     e = timed_launch(la::K_BWD, s, [&] { return bwd_launch(d, b, gate_mode, s); });
     if (e != hipSuccess) return hip_fail(e, "backward launch");
+    return LA_OK;
+}
+
+int la_delta_chunk(const la_desc* d) {
+    if (check_desc(d) != LA_OK) return 0;
+    return (d->dtype != LA_BF16 && d->dk >= 128) ? 32 : 64;
+}
+
+la_status la_delta_fwd(const la_desc* d, const void* q, const void* k, const void* v,
+                       const float* beta, const float* S0, void* out, float* S_final,
+                       void* stream) {
+    g_errmsg[0] = '\0';
+    const la_status st = check_delta(d);
+    if (st != LA_OK) return st;
+    if (!q || !k || !v || !beta || !out)
+        return fail(LA_ERR_INVALID, "q, k, v, beta and out must be non-NULL");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(beta) || !aligned16(out) ||
+        (S0 && !aligned16(S0)) || (S_final && !aligned16(S_final)))
+        return fail(LA_ERR_INVALID, "device pointers must be 16-byte aligned");
+    la::DeltaParams p;
+    std::memset(&p, 0, sizeof p);
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.beta = beta;
+    p.S0 = S0;
+    p.out = out;
+    p.S_final = S_final;
+    p.L = d->L;
+    p.H = d->H;
+    p.BH = d->B * d->H;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const hipError_t e = timed_launch(la::K_DELTA, s, [&] { return delta_launch(d, p, false, s); });
+    if (e != hipSuccess) return hip_fail(e, "delta prefill launch");
+    return LA_OK;
+}
+
+la_status la_delta_decode_step(const la_desc* d, const void* q, const void* k, const void* v,
+                               const float* beta, float* S, void* out, void* stream) {
+    g_errmsg[0] = '\0';
+    const la_status st = check_delta(d);
+    if (st != LA_OK) return st;
+    if (d->L != 1) return fail(LA_ERR_INVALID, "decode needs L == 1 (L=%d)", d->L);
+    if (!q || !k || !v || !beta || !S || !out)
+        return fail(LA_ERR_INVALID, "q, k, v, beta, S and out must be non-NULL");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(beta) || !aligned16(S) ||
+        !aligned16(out))
+        return fail(LA_ERR_INVALID, "device pointers must be 16-byte aligned");
+    la::DeltaParams p;
+    std::memset(&p, 0, sizeof p);
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.beta = beta;
+    p.S = S;
+    p.out = out;
+    p.L = 1;
+    p.H = d->H;
+    p.BH = d->B * d->H;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const hipError_t e = timed_launch(la::K_DELTA_DECODE, s, [&] { return delta_launch(d, p, true, s); });
+    if (e != hipSuccess) return hip_fail(e, "delta decode launch");
     return LA_OK;
 }
 

@@ -72,6 +72,19 @@ struct BwdParams {
     float log2_gamma[LA_MAX_GAMMA_HEADS];
 };
 
+// Delta rule parameters (prefill and decode).
+struct DeltaParams {
+    const void* q;          // prefill [BH, L, d], decode [BH, d] dtype
+    const void* k;
+    const void* v;
+    const float* beta;      // prefill [BH, L], decode [BH]
+    const float* S0;        // prefill: [BH, d, d] or null (zeros)
+    void* out;              // prefill [BH, L, d], decode [BH, d] dtype
+    float* S_final;         // prefill: [BH, d, d] or null
+    float* S;               // decode: [BH, d, d], updated in place
+    int L, H, BH;
+};
+
 // Passes of the chunk kernel.  MAIN and STATE serve the forward; the
 // backward adds the reversed state pass and the two passes that store the
 // state (or its gradient) at every chunk boundary.
@@ -87,7 +100,7 @@ constexpr int bwd_chunk(int d, bool bf16) { return (!bf16 && d >= 128) ? 32 : 64
 // Kernel families, as named by the profiling interface.
 enum KernelId {
     K_CHUNK_MAIN = 0, K_CHUNK_STATE = 1, K_STATE_SCAN = 2, K_DECODE = 3,
-    K_CHUNK_STORE = 4, K_BWD = 5, K_COUNT = 6
+    K_CHUNK_STORE = 4, K_BWD = 5, K_DELTA = 6, K_DELTA_DECODE = 7, K_COUNT = 8
 };
 
 // Launch hooks implemented in the kernel files.  Each returns hipSuccess or
@@ -104,6 +117,16 @@ LA_DECLARE_CHUNK_LAUNCHER(launch_chunk_bf16_d64)
 LA_DECLARE_CHUNK_LAUNCHER(launch_chunk_bf16_d128)
 #undef LA_DECLARE_CHUNK_LAUNCHER
 hipError_t launch_state_scan(const ChunkParams& p, int d, bool rev, hipStream_t s);
+#define LA_DECLARE_DELTA_LAUNCHER(NAME) \
+    hipError_t NAME(const DeltaParams& p, bool decode, hipStream_t s);
+LA_DECLARE_DELTA_LAUNCHER(launch_delta_f32_d16)
+LA_DECLARE_DELTA_LAUNCHER(launch_delta_f32_d32)
+LA_DECLARE_DELTA_LAUNCHER(launch_delta_f32_d64)
+LA_DECLARE_DELTA_LAUNCHER(launch_delta_f32_d128)
+LA_DECLARE_DELTA_LAUNCHER(launch_delta_bf16_d32)
+LA_DECLARE_DELTA_LAUNCHER(launch_delta_bf16_d64)
+LA_DECLARE_DELTA_LAUNCHER(launch_delta_bf16_d128)
+#undef LA_DECLARE_DELTA_LAUNCHER
 #define LA_DECLARE_BWD_LAUNCHER(NAME) \
     hipError_t NAME(const BwdParams& p, int gate, hipStream_t s);
 LA_DECLARE_BWD_LAUNCHER(launch_bwd_f32_d16)

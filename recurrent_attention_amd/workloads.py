@@ -24,6 +24,9 @@ name                                   contents
 ``scalar_gate_B1H16_L32768_d128``      as the GLA workload with one gate per
                                        token and head (log alpha =
                                        logsigmoid(g)/16, g ~ N(0,1) [B,H,L])
+``delta_B8H16_L4096_d128``             delta rule: B=8, H=16, L=4096, d=128,
+                                       bf16; q N(0,1)/sqrt(d), unit-norm k,
+                                       v N(0,1), beta = sigmoid(N(0,1))
 ``gla_varlen_32seq_H16_d128``          32 packed sequences, lengths uniform
                                        in [1, 4096] (seed 7), H=16, d=128,
                                        bf16, GLA gates as above, C=64
@@ -98,6 +101,8 @@ WORKLOADS = {
 PREFILL_HEADLINE = "gla_B1H16_L32768_d128"
 DECODE_HEADLINE = "decode_retention_256x32_d128"
 VARLEN_HEADLINE = "gla_varlen_32seq_H16_d128"
+DELTA_HEADLINE = "delta_B8H16_L4096_d128"
+DELTA_SPEC = {"B": 8, "H": 16, "L": 4096, "d": 128}
 VARLEN_SPEC = {"n": 32, "lo": 1, "hi": 4096, "seed": 7, "H": 16, "d": 128, "chunk": 64}
 
 
@@ -158,6 +163,23 @@ def workload_inputs(name: str, seed: int = 0, device="cpu", L=None, B=None):
                           w.gate_mode, seed=seed, device=device,
                           scale_inputs=w.scale_inputs,
                           gamma=w.gamma if w.gate_mode == GATE_GAMMA else None)
+
+
+def delta_inputs(B, H, L, dk, dv, dtype=torch.bfloat16, seed=0, device="cpu",
+                 with_state=False):
+    """Seeded inputs of the delta rule: q ~ N(0,1)/sqrt(d_k); k = a N(0,1)
+    row scaled to unit norm (in fp32, then rounded to dtype); v ~ N(0,1);
+    beta = sigmoid(N(0,1)) in fp32 [B,H,L]; S0 ~ N(0,1) when asked."""
+    gen = generator(seed, device)
+    q = _tokens(gen, (B, H, L, dk), dk, dtype, True, device)
+    k = torch.randn((B, H, L, dk), generator=gen, dtype=torch.float32, device=device)
+    k = (k / k.norm(dim=-1, keepdim=True)).to(dtype)
+    v = torch.randn((B, H, L, dv), generator=gen, dtype=torch.float32, device=device).to(dtype)
+    beta = torch.sigmoid(torch.randn((B, H, L), generator=gen, dtype=torch.float32, device=device))
+    out = {"q": q, "k": k, "v": v, "beta": beta, "S0": None}
+    if with_state:
+        out["S0"] = torch.randn((B, H, dk, dv), generator=gen, dtype=torch.float32, device=device)
+    return out
 
 
 def backward_inputs(B, H, L, dk, dv, dtype=torch.bfloat16, seed=100, device="cpu",

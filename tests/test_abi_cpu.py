@@ -261,3 +261,21 @@ def test_groupnorm_validation():
     assert call(api.LaGroupNorm(MIS, None, None, 1e-5)) == api.LA_ERR_INVALID
     assert call(api.LaGroupNorm(None, None, MIS, 1e-5)) == api.LA_ERR_INVALID
     assert call(gn, desc=_desc(L=0)) == api.LA_ERR_INVALID
+
+
+def test_delta_validation():
+    d = _desc(L=100)
+    fwd = lambda desc, q=A, beta=A, out=A, S0=None: api.la_delta_fwd(desc, q, A, A, beta, S0,
+                                                                     out, None, None)
+    assert fwd(_desc(L=100, phi=1)) == api.LA_ERR_UNSUPPORTED
+    assert fwd(_desc(L=100, normalize=True)) == api.LA_ERR_UNSUPPORTED
+    assert fwd(_desc(L=100, dk=48, dv=48)) == api.LA_ERR_UNSUPPORTED
+    assert fwd(d, q=None) == api.LA_ERR_INVALID
+    assert fwd(d, beta=None) == api.LA_ERR_INVALID
+    assert fwd(d, beta=MIS) == api.LA_ERR_INVALID
+    assert fwd(d, S0=MIS) == api.LA_ERR_INVALID
+    dec = lambda desc, S=A: api.la_delta_decode_step(desc, A, A, A, A, S, A, None)
+    assert dec(_desc(L=2)) == api.LA_ERR_INVALID
+    assert dec(_desc(L=1), S=None) == api.LA_ERR_INVALID
+    assert api.la_delta_chunk(_desc(dk=128, dv=128, dtype=api.LA_F32)) == 32
+    assert api.la_delta_chunk(_desc(dk=128, dv=128, dtype=api.LA_BF16)) == 64
