@@ -26,6 +26,8 @@ Also reported, in the same line:
 * ``retention``: the retention workload (B=2, H=16, L=8192, d=128,
   multi-scale gamma), plain and with the fused group-norm / swish-gate
   output epilogue.
+* ``delta``: the delta rule's prefill (``delta_B16H16_L4096_d128``) and
+  100 decode steps at the decode workload's shape.
 * ``cpu_baseline``: the fp64 oracle (test infrastructure, untuned) on the
   same prefill workload drawn on the host, timed on this machine's cores.
 
@@ -389,6 +391,98 @@ def bench_retention(args, torch, api, workloads):
                                 "extra_bytes": w.B * w.H * w.L * w.dv * 2}}
 
 
+def bench_delta(args, torch, api, workloads):
+    """Delta-rule prefill of delta_B16H16_L4096_d128 and 100 decode steps of
+    the decode workload's shape (256 sequences x 32 heads, d = 128)."""
+    sp = workloads.DELTA_SPEC
+    B, H, L, d = sp["B"], sp["H"], sp["L"], sp["d"]
+    dev = torch.device("cuda", 0)
+    inp = workloads.delta_inputs(B, H, L, d, d, torch.bfloat16, seed=0, device=dev)
+    q, k, v, beta = inp["q"], inp["k"], inp["v"], inp["beta"]
+    out = torch.empty_like(v)
+    S = torch.empty((B, H, d, d), dtype=torch.float32, device=dev)
+    desc = api.make_desc(B, H, L, d, d, api.LA_BF16, 0, False, 0)
+    sp_ = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    lib = api.load_library()
+    argv = (ctypes.byref(desc), q.data_ptr(), k.data_ptr(), v.data_ptr(), beta.data_ptr(), None,
+            out.data_ptr(), S.data_ptr(), sp_)
+
+    def step():
+        if lib.la_delta_fwd(*argv) != 0:
+            raise RuntimeError(api.la_last_error_message())
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / args.steps * 1e3
+    api.la_profile_begin()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    api.la_profile_end()
+    n, kms = api.la_profile_query("delta_chunk")
+    kus = kms / n * 1e3
+    per_th = 2 * 4 * d + 4          # q, k, v, out bf16 + beta fp32
+    alg = B * H * L * per_th + B * H * d * d * 4
+    C = api.la_delta_chunk(desc)
+    flops_chunk = 2 * C * C * d * 4 + 2 * C * d * d * 4   # K K^T, Q K^T, W, U, P U'; W S, Q S, K^T U' (+T V)
+    flops = B * H * (-(-L // C)) * flops_chunk
+    del q, k, v, beta, out, S, inp
+    # decode: 256 x 32 pairs, d = 128, state N(0,1)
+    w = workloads.WORKLOADS[workloads.DECODE_HEADLINE]
+    S0, _ = workloads.decode_state(w.B, w.H, w.dk, w.dv, seed=0, device=dev)
+    dsteps = 100
+    dq, dk_, dv_, _ = workloads.decode_tokens(w.B, w.H, w.dk, w.dv, dsteps, seed=1, device=dev)
+    dk_ = (dk_.float() / dk_.float().norm(dim=-1, keepdim=True)).to(torch.bfloat16)
+    dbeta = torch.full((w.B, w.H), 0.5, dtype=torch.float32, device=dev)
+    Sd = S0.clone()
+    od = torch.empty((w.B, w.H, w.dv), dtype=torch.bfloat16, device=dev)
+    ddesc = api.make_desc(w.B, w.H, 1, w.dk, w.dv, api.LA_BF16, 0, False, 0)
+
+    def dstep(t):
+        if lib.la_delta_decode_step(ctypes.byref(ddesc), dq[t].data_ptr(), dk_[t].data_ptr(),
+                                    dv_[t].data_ptr(), dbeta.data_ptr(), Sd.data_ptr(),
+                                    od.data_ptr(), sp_) != 0:
+            raise RuntimeError(api.la_last_error_message())
+
+    for t in range(10):
+        dstep(t)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for t in range(dsteps):
+        dstep(t)
+    torch.cuda.synchronize()
+    dus = (time.perf_counter() - t0) / dsteps * 1e6
+    api.la_profile_begin()
+    for t in range(dsteps):
+        dstep(t)
+    torch.cuda.synchronize()
+    api.la_profile_end()
+    n, dms = api.la_profile_query("delta_decode")
+    dkus = dms / n * 1e3
+    step_bytes = 2 * w.B * w.H * w.dk * w.dv * 4 + w.B * w.H * (4 * w.dk * 2 + 4)
+    return {
+        "prefill": {"workload": workloads.DELTA_HEADLINE, "ms_per_step": round(ms, 4),
+                    "tokens_per_s": round(B * L / (ms * 1e-3), 1), "kernel_avg_us": round(kus, 2),
+                    "algorithmic_bytes": alg, "tflops": round(flops / (kus * 1e-6) / 1e12, 2),
+                    "roofline": {"bound": "hbm", "achieved": round(alg / (kus * 1e-6) / 1e9, 1),
+                                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                 "frac": round(alg / (kus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                                 "traffic": None, "kernel": "delta_chunk"}},
+        "decode": {"shape": "256 sequences x 32 heads, d=128, bf16 tokens, fp32 state",
+                   "us_per_step": round(dus, 2), "kernel_avg_us": round(dkus, 2),
+                   "bytes_per_step": step_bytes,
+                   "roofline": {"bound": "hbm", "achieved": round(step_bytes / (dkus * 1e-6) / 1e9, 1),
+                                "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                "frac": round(step_bytes / (dkus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+                                "traffic": None, "kernel": "delta_decode"}},
+    }
+
+
 def bench_decode(args, torch, api, workloads):
     w = workloads.WORKLOADS[workloads.DECODE_HEADLINE]
     dev = torch.device("cuda", 0)
@@ -489,8 +583,10 @@ def main(argv=None):
     ap.add_argument("--no-varlen", action="store_true")
     ap.add_argument("--no-scalar", action="store_true")
     ap.add_argument("--no-retention", action="store_true")
+    ap.add_argument("--no-delta", action="store_true")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
-    ap.add_argument("--only", choices=["prefill", "decode", "backward", "varlen", "scalar", "retention", "copy"], default=None,
+    ap.add_argument("--only", choices=["prefill", "decode", "backward", "varlen", "scalar", "retention", "delta",
+                             "copy"], default=None,
                     help="run one part only (copy: a 1 GiB device copy used to scale "
                          "rocprofv3 byte counters); prints no metric line")
     args = ap.parse_args(argv)
@@ -521,6 +617,9 @@ def main(argv=None):
     if args.only == "varlen":
         print(json.dumps(bench_varlen(args, torch, api, workloads)), flush=True)
         return 0
+    if args.only == "delta":
+        print(json.dumps(bench_delta(args, torch, api, workloads)), flush=True)
+        return 0
     if args.only == "retention":
         print(json.dumps(bench_retention(args, torch, api, workloads)), flush=True)
         return 0
@@ -541,6 +640,7 @@ def main(argv=None):
     sc = None if args.no_scalar else bench_prefill(args, torch, api, workloads,
                                                    "scalar_gate_B1H16_L32768_d128")
     ret = None if args.no_retention else bench_retention(args, torch, api, workloads)
+    dl = None if args.no_delta else bench_delta(args, torch, api, workloads)
     w = pre["w"]
     line = {
         "metric": METRIC,
@@ -574,6 +674,8 @@ def main(argv=None):
         line["varlen"] = vl
     if ret is not None:
         line["retention"] = ret
+    if dl is not None:
+        line["delta"] = dl
     if sc is not None:
         line["scalar_gate"] = {
             "workload": sc["w"].name, "ms_per_step": round(sc["ms_step"], 4),

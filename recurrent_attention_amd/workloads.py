@@ -24,7 +24,7 @@ name                                   contents
 ``scalar_gate_B1H16_L32768_d128``      as the GLA workload with one gate per
                                        token and head (log alpha =
                                        logsigmoid(g)/16, g ~ N(0,1) [B,H,L])
-``delta_B8H16_L4096_d128``             delta rule: B=8, H=16, L=4096, d=128,
+``delta_B16H16_L4096_d128``            delta rule: B=16, H=16, L=4096, d=128,
                                        bf16; q N(0,1)/sqrt(d), unit-norm k,
                                        v N(0,1), beta = sigmoid(N(0,1))
 ``gla_varlen_32seq_H16_d128``          32 packed sequences, lengths uniform
@@ -101,8 +101,8 @@ WORKLOADS = {
 PREFILL_HEADLINE = "gla_B1H16_L32768_d128"
 DECODE_HEADLINE = "decode_retention_256x32_d128"
 VARLEN_HEADLINE = "gla_varlen_32seq_H16_d128"
-DELTA_HEADLINE = "delta_B8H16_L4096_d128"
-DELTA_SPEC = {"B": 8, "H": 16, "L": 4096, "d": 128}
+DELTA_HEADLINE = "delta_B16H16_L4096_d128"
+DELTA_SPEC = {"B": 16, "H": 16, "L": 4096, "d": 128}
 VARLEN_SPEC = {"n": 32, "lo": 1, "hi": 4096, "seed": 7, "H": 16, "d": 128, "chunk": 64}
 
 
