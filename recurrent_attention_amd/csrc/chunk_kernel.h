@@ -254,6 +254,9 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
     // the aggregate pass skips the segment it would end with (the last one,
     // or the first one when reversed)
     constexpr bool AGG = SONLY && !STORE;
+    // the forward aggregate pass walks its segment from the last chunk to
+    // the first (see cof below)
+    constexpr bool BACKAGG = AGG && !REV;
     const int PS = AGG ? P - 1 : P;
     const int seg = blockIdx.x % PS + ((AGG && REV) ? 1 : 0);
     const int bh = blockIdx.x / PS;
@@ -422,8 +425,18 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
     };
     constexpr float kLog2e = 1.4426950408889634f;
 
-    // chunk handled at iteration ci (reverse order for the gradient pass)
-    auto cof = [&](int ci) { return REV ? c_begin + c_end - 1 - ci : ci; };
+    // chunk handled at iteration ci: reverse order for the gradient pass,
+    // and for the forward aggregate pass, whose result does not depend on
+    // the order (each chunk's K^T V is weighted by the decay of the chunks
+    // after it, accumulated as the walk goes) and whose last reads -- the
+    // segment's first chunks -- are then the most recently used data when
+    // the main pass starts there
+    auto cof = [&](int ci) { return (REV || BACKAGG) ? c_begin + c_end - 1 - ci : ci; };
+    // backward walk: log2 decay of the chunks already walked, per owned
+    // channel (vector gates) or as a product (gamma)
+    float eacc[CW];
+#pragma unroll
+    for (int i = 0; i < CW; ++i) eacc[i] = 0.f;
     // the true state in the accumulators, into boundary slot `slot` in the
     // element type: rows times the after-factor still pending (diagonal
     // gate), then a 4x4 transpose within each lane quad so that every lane
@@ -531,6 +544,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
                 if constexpr (NW == 1) gref[i] = gmid[i];
             }
         }
+        const float egam = seg_g;   // gamma^(tokens after this chunk), backward walk
         if constexpr (GATE == LA_GATE_GAMMA) seg_g *= sm.gpow[clen];
 
         // ---- a1: features and decay factors, written to the LDS tiles, one
@@ -551,7 +565,8 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
                 const bool ok = t < clen;
                 float qv[CW], kv[CW];
                 float ftok = 1.f;
-                if constexpr (GATE == LA_GATE_GAMMA) ftok = ok ? sm.gpow[REV ? t + 1 : clen - 1 - t] : 0.f;
+                if constexpr (GATE == LA_GATE_GAMMA)
+                    ftok = ok ? sm.gpow[REV ? t + 1 : clen - 1 - t] * (BACKAGG ? egam : 1.f) : 0.f;
 #pragma unroll
                 for (int i = 0; i < CW; ++i) {
                     float ka = run_elem<BF16>(rg.k[j], i);
@@ -564,6 +579,8 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
                         fq = __builtin_amdgcn_exp2f(d);
                         fk = __builtin_amdgcn_exp2f(-d);
                         ft = REV ? fq : fk;
+                        // backward walk: k e^{B - b} times the decay after the chunk
+                        if constexpr (BACKAGG) ft = __builtin_amdgcn_exp2f(gtot[i] - bcur[i] + eacc[i]);
                     }
                     if constexpr (!SONLY) {
                         float qa = run_elem<BF16>(qreg[j], i);
@@ -593,9 +610,14 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
 #pragma unroll
             for (int i = 0; i < VW; ++i)
                 store_pairs<Cfg, VTPG>(&sm.vt[VW * vcp + i][0], VW * vcp + i, vtg * VTPG, vp[i]);
+            if constexpr (BACKAGG && VG) {
+#pragma unroll
+                for (int i = 0; i < CW; ++i) eacc[i] += gtot[i];
+            }
             if (ktg == 0) {
                 // per-row state factors: DIAG applies post(previous) * pre(this)
-                // before the chunk; GAMMA applies gamma^c after op2
+                // before the chunk; GAMMA applies gamma^c after op2; the
+                // backward walk leaves the accumulated state unscaled
                 float sc[CW], pr[CW], po[CW];
 #pragma unroll
                 for (int i = 0; i < CW; ++i) sc[i] = pr[i] = po[i] = 1.f;
@@ -604,11 +626,13 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
                     for (int i = 0; i < CW; ++i) {
                         const int row = CW * kcp + i;
                         sm.segsum[row] += gtot[i];
-                        pr[i] = __builtin_amdgcn_exp2f(REV ? gtot[i] - gref[i] : gref[i]);
-                        po[i] = __builtin_amdgcn_exp2f(REV ? gref[i] : gtot[i] - gref[i]);
+                        if constexpr (!BACKAGG) {
+                            pr[i] = __builtin_amdgcn_exp2f(REV ? gtot[i] - gref[i] : gref[i]);
+                            po[i] = __builtin_amdgcn_exp2f(REV ? gref[i] : gtot[i] - gref[i]);
+                        }
                         sc[i] = sm.post[row] * pr[i];
                     }
-                } else if constexpr (GATE == LA_GATE_GAMMA) {
+                } else if constexpr (GATE == LA_GATE_GAMMA && !BACKAGG) {
 #pragma unroll
                     for (int i = 0; i < CW; ++i) sc[i] = pr[i] = sm.gpow[clen];
                 }

@@ -24,12 +24,15 @@ from collections import defaultdict
 
 # chunk_kernel<ChunkCfg<dk, dv, C, bf16, gate, state-only, waves>, elu1, reversed, store>
 _CHUNK = r"la::chunk_kernel<la::ChunkCfg<\d+, \d+, \d+, \w+, \d, {so}(, \d+)?>, \w+{tail}"
+# (chunk_main also matches the group-norm epilogue variant: <..., false, false, true>)
 FAMILIES = [
     ("chunk_main", re.compile(_CHUNK.format(so="false", tail=""))),
     ("chunk_store", re.compile(_CHUNK.format(so="true", tail=r", \w+, true>"))),
     ("chunk_state", re.compile(_CHUNK.format(so="true", tail=r"(, \w+, false)?>"))),
     ("state_scan", re.compile(r"la::state_scan_kernel")),
     ("chunk_bwd", re.compile(r"la::bwd_kernel")),
+    ("delta_chunk", re.compile(r"la::delta_chunk_kernel")),
+    ("delta_decode", re.compile(r"la::delta_decode_kernel")),
     ("decode", re.compile(r"la::decode_kernel")),
     ("copy", re.compile(r"__amd_rocclr_copyBuffer")),
 ]
