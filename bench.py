@@ -84,6 +84,16 @@ def bwd_source_hash():
     return h.hexdigest()
 
 
+def delta_source_hash():
+    """Hash of the sources the delta-rule kernels are built from."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "recurrent_attention_amd", "csrc")
+    for f in ("delta_kernel.h", "tile_ops.h", "la_device.h", "la_internal.h", "delta_bf16_d128.hip"):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
 def measured_traffic(name, src_hash):
     """HBM bytes per launch from a committed counter summary, or None when
     there is none or it was taken from other kernel sources."""
@@ -472,14 +482,18 @@ def bench_delta(args, torch, api, workloads):
                     "roofline": {"bound": "hbm", "achieved": round(alg / (kus * 1e-6) / 1e9, 1),
                                  "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                  "frac": round(alg / (kus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                                 "traffic": None, "kernel": "delta_chunk"}},
+                                 "traffic": measured_traffic(
+                                     f"delta_chunk_{workloads.DELTA_HEADLINE}", delta_source_hash()),
+                                 "kernel": "delta_chunk"}},
         "decode": {"shape": "256 sequences x 32 heads, d=128, bf16 tokens, fp32 state",
                    "us_per_step": round(dus, 2), "kernel_avg_us": round(dkus, 2),
                    "bytes_per_step": step_bytes,
                    "roofline": {"bound": "hbm", "achieved": round(step_bytes / (dkus * 1e-6) / 1e9, 1),
                                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                 "frac": round(step_bytes / (dkus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
-                                "traffic": None, "kernel": "delta_decode"}},
+                                "traffic": measured_traffic("delta_decode_256x32_d128",
+                                                            delta_source_hash()),
+                                "kernel": "delta_decode"}},
     }
 
 
