@@ -218,7 +218,7 @@ def bench_backward(args, torch, api, workloads):
     sp = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
     lib = api.load_library()
     argv = (ctypes.byref(desc), q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(),
-            w.gate_mode, la.data_ptr(), None, None, dq.data_ptr(), dk.data_ptr(),
+            w.gate_mode, la.data_ptr(), None, None, None, dq.data_ptr(), dk.data_ptr(),
             dv.data_ptr(), dla.data_ptr(), dS0.data_ptr(), ws.data_ptr(), need, sp)
 
     def step():
@@ -234,6 +234,32 @@ def bench_backward(args, torch, api, workloads):
         step()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    # a training step: the forward that keeps its boundary states, then the
+    # backward from them
+    nst = api.la_chunk_train_states_bytes(desc)
+    states = torch.empty(nst // 4 + 4, dtype=torch.float32, device=dev)
+    out = torch.empty_like(v)
+    Sf = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
+    fneed = api.la_chunk_fwd_workspace_bytes(desc, chunk)
+    fws = torch.empty(max(fneed // 4, 1), dtype=torch.float32, device=dev)
+    fargv = (ctypes.byref(desc), q.data_ptr(), k.data_ptr(), v.data_ptr(), w.gate_mode,
+             la.data_ptr(), None, out.data_ptr(), Sf.data_ptr(), states.data_ptr(), nst,
+             fws.data_ptr(), fneed, sp)
+    bargv = argv[:9] + (states.data_ptr(),) + argv[10:]
+
+    def train_step():
+        if lib.la_chunk_fwd_train(*fargv) != 0 or lib.la_chunk_bwd(*bargv) != 0:
+            raise RuntimeError(api.la_last_error_message())
+
+    for _ in range(args.warmup):
+        train_step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        train_step()
+    torch.cuda.synchronize()
+    train_ms = (time.perf_counter() - t0) / args.steps * 1e3
+
     api.la_profile_begin()
     for _ in range(args.steps):
         step()
@@ -251,6 +277,9 @@ def bench_backward(args, torch, api, workloads):
     return {
         "workload": w.name, "chunk": chunk, "ms_per_step": round(ms_step, 4),
         "tokens_per_s": round(w.B * w.L / (ms_step * 1e-3), 1),
+        "train_step": {"what": "la_chunk_fwd_train + la_chunk_bwd from its states",
+                       "ms_per_step": round(train_ms, 4),
+                       "tokens_per_s": round(w.B * w.L / (train_ms * 1e-3), 1)},
         "algorithmic_bytes": alg,
         "pct_of_hbm_peak_step": round(100.0 * alg / (ms_step * 1e-3) / (HBM_PEAK_GBS * 1e9), 2),
         "kernels_avg_us": kern,

@@ -231,6 +231,8 @@ int la_chunk_fwd_segments(const la_desc* d, int chunk);
  *   gate_mode, gamma_or_log_alpha   as for la_chunk_fwd
  *   S0                 device fp32 [B,H,dk,dv] forward initial state, or NULL
  *   dS_final           device fp32 [B,H,dk,dv] gradient of S_final, or NULL
+ *   states             the boundary states la_chunk_fwd_train wrote for
+ *                      these inputs, or NULL (recomputed here)
  *   dq, dk, dv         device [B,H,L,dk|dv] of d->dtype, written: gradients
  *                      of the raw q, k (through phi) and v
  *   dlog_alpha         DIAG: device fp32 [B,H,L,dk], SCALAR: [B,H,L],
@@ -246,9 +248,30 @@ int la_chunk_fwd_segments(const la_desc* d, int chunk);
 la_status la_chunk_bwd(const la_desc* d, const void* q, const void* k,
                        const void* v, const void* dout, int gate_mode,
                        const float* gamma_or_log_alpha, const float* S0,
-                       const float* dS_final, void* dq, void* dk, void* dv,
-                       float* dlog_alpha, float* dS0, void* workspace,
-                       size_t workspace_bytes, void* stream);
+                       const float* dS_final, const void* states, void* dq,
+                       void* dk, void* dv, float* dlog_alpha, float* dS0,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * la_chunk_fwd_train -- la_chunk_fwd (no normaliser, chunk
+ * la_chunk_bwd_chunk(d)) that also leaves behind, in `states`, the state
+ * before every chunk and the final state in the element type of q/k/v
+ * ([B,H,ceil(L/C)+1,dk,dv], row-major), which la_chunk_bwd then takes
+ * instead of recomputing them.
+ *   states, states_bytes   device buffer of at least
+ *                          la_chunk_train_states_bytes(d) bytes, written
+ *   workspace              la_chunk_fwd_workspace_bytes(d, la_chunk_bwd_chunk(d))
+ * Other arguments as for la_chunk_fwd (z0/z_final absent).
+ */
+la_status la_chunk_fwd_train(const la_desc* d, const void* q, const void* k,
+                             const void* v, int gate_mode,
+                             const float* gamma_or_log_alpha, const float* S0,
+                             void* out, float* S_final, void* states,
+                             size_t states_bytes, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
+/* Bytes of the boundary states la_chunk_fwd_train writes (0 if invalid). */
+size_t la_chunk_train_states_bytes(const la_desc* d);
 
 /* Bytes of device workspace la_chunk_bwd needs: states at every chunk
  * boundary in the element type of q/k/v (B*H*(2*ceil(L/C)+1)*dk*dv

@@ -33,6 +33,7 @@ EXPORTED = (
     "la_chunk_bwd", "la_chunk_bwd_workspace_bytes", "la_chunk_bwd_chunk",
     "la_chunk_fwd_varlen", "la_chunk_fwd_varlen_workspace_bytes",
     "la_chunk_fwd_groupnorm", "la_delta_fwd", "la_delta_decode_step", "la_delta_chunk",
+    "la_chunk_fwd_train", "la_chunk_train_states_bytes",
 )
 
 
@@ -91,7 +92,12 @@ def load_library():
     lib.la_chunk_fwd_varlen.restype = i
     lib.la_chunk_fwd_varlen_workspace_bytes.argtypes = [dp, i, i]
     lib.la_chunk_fwd_varlen_workspace_bytes.restype = sz
-    lib.la_chunk_bwd.argtypes = [dp, vp, vp, vp, vp, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.la_chunk_bwd.argtypes = [dp, vp, vp, vp, vp, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                                 vp]
+    lib.la_chunk_fwd_train.argtypes = [dp, vp, vp, vp, i, vp, vp, vp, vp, vp, sz, vp, sz, vp]
+    lib.la_chunk_fwd_train.restype = i
+    lib.la_chunk_train_states_bytes.argtypes = [dp]
+    lib.la_chunk_train_states_bytes.restype = sz
     lib.la_chunk_bwd.restype = i
     lib.la_chunk_bwd_workspace_bytes.argtypes = [dp]
     lib.la_chunk_bwd_workspace_bytes.restype = sz
@@ -175,12 +181,23 @@ def la_chunk_fwd_varlen_workspace_bytes(desc, max_seqlen, chunk) -> int:
         ctypes.byref(desc), int(max_seqlen), int(chunk)))
 
 
-def la_chunk_bwd(desc, q, k, v, dout, gate_mode, gamma_or_log_alpha, S0, dS_final,
+def la_chunk_bwd(desc, q, k, v, dout, gate_mode, gamma_or_log_alpha, S0, dS_final, states,
                  dq, dk, dv, dlog_alpha, dS0, workspace, workspace_bytes, stream):
     """Raw call; pointer arguments are ints (0 = NULL) or ctypes pointers."""
     return load_library().la_chunk_bwd(
         ctypes.byref(desc), q, k, v, dout, int(gate_mode), gamma_or_log_alpha, S0, dS_final,
-        dq, dk, dv, dlog_alpha, dS0, workspace, int(workspace_bytes), stream)
+        states, dq, dk, dv, dlog_alpha, dS0, workspace, int(workspace_bytes), stream)
+
+
+def la_chunk_fwd_train(desc, q, k, v, gate_mode, gamma_or_log_alpha, S0, out, S_final, states,
+                       states_bytes, workspace, workspace_bytes, stream):
+    return load_library().la_chunk_fwd_train(
+        ctypes.byref(desc), q, k, v, int(gate_mode), gamma_or_log_alpha, S0, out, S_final,
+        states, int(states_bytes), workspace, int(workspace_bytes), stream)
+
+
+def la_chunk_train_states_bytes(desc) -> int:
+    return int(load_library().la_chunk_train_states_bytes(ctypes.byref(desc)))
 
 
 def la_chunk_bwd_workspace_bytes(desc) -> int:
@@ -472,14 +489,49 @@ def delta_decode_step(q, k, v, beta, S, out=None, stream=None):
     return out
 
 
+def chunk_fwd_train(q, k, v, gate_mode=LA_GATE_NONE, gamma=None, log_alpha=None, S0=None,
+                    phi=LA_PHI_IDENTITY, segments=0, stream=None):
+    """Prefill that keeps its boundary states for :func:`chunk_bwd`.
+    Returns ``(out, S_final, states)``."""
+    torch = _torch()
+    B, H, L, dk = q.shape
+    dv = v.shape[-1]
+    desc = make_desc(B, H, L, dk, dv, _la_dtype(q), phi, False, segments)
+    dev = q.device
+    out = torch.empty((B, H, L, dv), dtype=q.dtype, device=dev)
+    S_final = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    nbytes = la_chunk_train_states_bytes(desc)
+    states = torch.empty(nbytes // 4 + 4, dtype=torch.float32, device=dev)
+    need = la_chunk_fwd_workspace_bytes(desc, la_chunk_bwd_chunk(desc))
+    ws = torch.empty(max(need // 4, 1) + 4, dtype=torch.float32, device=dev)
+    g_arg = None
+    g_keep = None
+    if gate_mode == LA_GATE_GAMMA:
+        g_keep = _gamma_host(gamma, H)
+        g_arg = ctypes.c_void_p(g_keep.data_ptr())
+    elif gate_mode in (LA_GATE_DIAG, LA_GATE_SCALAR):
+        g_arg = _dev_ptr(log_alpha, "log_alpha", torch.float32,
+                         (B, H, L, dk) if gate_mode == LA_GATE_DIAG else (B, H, L))
+    st = la_chunk_fwd_train(
+        desc, _dev_ptr(q, "q"), _dev_ptr(k, "k", q.dtype, (B, H, L, dk)),
+        _dev_ptr(v, "v", q.dtype, (B, H, L, dv)), gate_mode, g_arg,
+        _dev_ptr(S0, "S0", torch.float32, (B, H, dk, dv)), _dev_ptr(out, "out"),
+        _dev_ptr(S_final, "S_final"), _dev_ptr(states, "states"), states.numel() * 4,
+        _dev_ptr(ws, "workspace"), ws.numel() * 4, _stream_ptr(stream, dev))
+    _check(st)
+    del g_keep
+    return out, S_final, states
+
+
 def chunk_bwd(q, k, v, dout, gate_mode=LA_GATE_NONE, gamma=None, log_alpha=None,
               S0=None, dS_final=None, phi=LA_PHI_IDENTITY, segments=0,
-              workspace=None, stream=None):
+              workspace=None, stream=None, states=None):
     """Gradients of :func:`chunk_fwd` (no normaliser) for the loss
     ``sum(dout * out) + sum(dS_final * S_final)``.  Returns a dict with
     ``dq``, ``dk``, ``dv`` (dtype of q), ``dlog_alpha`` (fp32, DIAG and
     SCALAR gates, in the layout of log_alpha, else None) and ``dS0``
-    (fp32)."""
+    (fp32).  ``states`` from :func:`chunk_fwd_train` skips the recompute of
+    the forward states."""
     torch = _torch()
     B, H, L, dk = q.shape
     dv = v.shape[-1]
@@ -512,7 +564,7 @@ def chunk_bwd(q, k, v, dout, gate_mode=LA_GATE_NONE, gamma=None, log_alpha=None,
         _dev_ptr(v, "v", q.dtype, (B, H, L, dv)), _dev_ptr(dout, "dout", q.dtype, (B, H, L, dv)),
         gate_mode, g_arg, _dev_ptr(S0, "S0", torch.float32, (B, H, dk, dv)),
         _dev_ptr(dS_final, "dS_final", torch.float32, (B, H, dk, dv)),
-        _dev_ptr(dq, "dq"), _dev_ptr(dkk, "dk"), _dev_ptr(dvv, "dv"), _dev_ptr(dla, "dlog_alpha"),
+        _dev_ptr(states, "states"), _dev_ptr(dq, "dq"), _dev_ptr(dkk, "dk"), _dev_ptr(dvv, "dv"), _dev_ptr(dla, "dlog_alpha"),
         _dev_ptr(dS0, "dS0"), _dev_ptr(workspace, "workspace"), ws_bytes,
         _stream_ptr(stream, dev))
     _check(st)

@@ -52,7 +52,8 @@
 //
 // Two more state-only variants serve the backward pass:
 //  * STORE starts each segment from its entry state (after the segment
-//    scan) and writes the true state at every chunk boundary;
+//    scan) and writes the true state at every chunk boundary (also on the
+//    main pass, for a forward that keeps its states for the backward);
 //  * REV runs the recurrence of the state gradient, G_prev = A_c G +
 //    sum_t (phi(q_t) * e^{b_t}) do_t^T, which is the state update with k ->
 //    phi(q), v -> do, the key factor replaced by the query factor, the
@@ -249,7 +250,8 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     const int r = lane & 15, g = lane >> 4;
     const int P = p.P;
-    static_assert(SONLY || (!REV && !STORE), "backward variants are state-only");
+    static_assert(SONLY || !REV, "the reversed walk is state-only");
+    static_assert(!(STORE && EPI), "no epilogue with the boundary states");
     static_assert(!(SONLY && EPI), "the output epilogue belongs to the main pass");
     // the aggregate pass skips the segment it would end with (the last one,
     // or the first one when reversed)
@@ -902,7 +904,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
     // ---- epilogue
     float* Sout;
     float* zout;
-    if constexpr (STORE) {
+    if constexpr (STORE && SONLY) {
         // the state after the whole segment: S_final (forward) or the
         // gradient of the initial state (reverse), from the segment that
         // ends the sequence
@@ -1047,6 +1049,7 @@ hipError_t launch_chunk_dt(const ChunkParams& p, int chunk, int gate, int pass, 
         if (pass == PASS_STATE_REV) LA_CHUNK_GATES(CB, true, true, false);
         if (pass == PASS_STORE) LA_CHUNK_GATES(CB, true, false, true);
         if (pass == PASS_STORE_REV) LA_CHUNK_GATES(CB, true, true, true);
+        if (pass == PASS_MAIN_STORE) LA_CHUNK_GATES(CB, false, false, true);
     }
     if (pass == PASS_MAIN_NORM && chunk == 64) LA_CHUNK_GATES_EP(64, false, false, false, true);
     if (chunk == 16) LA_CHUNK_FWD(16);

@@ -247,7 +247,8 @@ la_status chunk_fwd_impl(const la_desc* d, const int* cu_seqlens, int max_seqlen
                          const void* k, const void* v, int gate_mode,
                          const float* gamma_or_log_alpha, const float* S0, const float* z0,
                          int chunk, const la_groupnorm* gn, void* out, float* S_final,
-                         float* z_final, void* workspace, size_t ws_bytes, void* stream) {
+                         float* z_final, void* workspace, size_t ws_bytes, void* stream,
+                         void* states = nullptr) {
     // packed sequences plan their segments for the longest one
     const la_desc dp = plan_desc(d, cu_seqlens, max_seqlen);
     la_status st;
@@ -310,6 +311,10 @@ la_status chunk_fwd_impl(const la_desc* d, const int* cu_seqlens, int max_seqlen
     p.phi_elu1 = d->phi == LA_PHI_ELU1;
     p.normalize = d->normalize;
     p.cu_seqlens = cu_seqlens;
+    if (states) {
+        p.st_rows = states;
+        p.st_slots = pl.nchunks + 1;
+    }
     if (pl.P > 1) {
         float* ws = static_cast<float*>(workspace);
         const size_t slots = (size_t)BH * pl.P;
@@ -330,8 +335,8 @@ la_status chunk_fwd_impl(const la_desc* d, const int* cu_seqlens, int max_seqlen
         if (e != hipSuccess) return hip_fail(e, "segment scan launch");
     }
     e = timed_launch(la::K_CHUNK_MAIN, s, [&] {
-        return chunk_launch(d, p, chunk, gate_mode, gn ? la::PASS_MAIN_NORM : la::PASS_MAIN, s,
-                            BH * pl.P);
+        const int pass = states ? la::PASS_MAIN_STORE : gn ? la::PASS_MAIN_NORM : la::PASS_MAIN;
+        return chunk_launch(d, p, chunk, gate_mode, pass, s, BH * pl.P);
     });
     if (e != hipSuccess) return hip_fail(e, "main pass launch");
     return LA_OK;
@@ -389,6 +394,32 @@ la_status la_chunk_fwd_groupnorm(const la_desc* d, const void* q, const void* k,
                           gn, out, S_final, z_final, workspace, ws_bytes, stream);
 }
 
+size_t la_chunk_train_states_bytes(const la_desc* d) {
+    if (check_desc(d) != LA_OK) return 0;
+    const int chunk = la::bwd_chunk(d->dk, d->dtype == LA_BF16);
+    const size_t n = (size_t)(d->L + chunk - 1) / chunk + 1;
+    return (size_t)d->B * d->H * n * d->dk * d->dv * (d->dtype == LA_BF16 ? 2 : 4);
+}
+
+la_status la_chunk_fwd_train(const la_desc* d, const void* q, const void* k, const void* v,
+                             int gate_mode, const float* gamma_or_log_alpha, const float* S0,
+                             void* out, float* S_final, void* states, size_t states_bytes,
+                             void* workspace, size_t ws_bytes, void* stream) {
+    g_errmsg[0] = '\0';
+    const la_status st = check_desc(d);
+    if (st != LA_OK) return st;
+    if (d->normalize) return fail(LA_ERR_UNSUPPORTED, "the training forward has no normaliser");
+    if (!states) return fail(LA_ERR_INVALID, "states must be non-NULL");
+    if (!aligned16(states)) return fail(LA_ERR_INVALID, "device pointers must be 16-byte aligned");
+    if (states_bytes < la_chunk_train_states_bytes(d))
+        return fail(LA_ERR_INVALID, "states has %zu bytes, %zu required", states_bytes,
+                    la_chunk_train_states_bytes(d));
+    const int chunk = la::bwd_chunk(d->dk, d->dtype == LA_BF16);
+    return chunk_fwd_impl(d, nullptr, 0, q, k, v, gate_mode, gamma_or_log_alpha, S0, nullptr,
+                          chunk, nullptr, out, S_final, nullptr, workspace, ws_bytes, stream,
+                          states);
+}
+
 la_status la_chunk_fwd_varlen(const la_desc* d, const int* cu_seqlens, int max_seqlen,
                               const void* q, const void* k, const void* v, int gate_mode,
                               const float* gamma_or_log_alpha, const float* S0, const float* z0,
@@ -421,9 +452,9 @@ int la_chunk_bwd_chunk(const la_desc* d) {
 
 la_status la_chunk_bwd(const la_desc* d, const void* q, const void* k, const void* v,
                        const void* dout, int gate_mode, const float* gamma_or_log_alpha,
-                       const float* S0, const float* dS_final, void* dq, void* dk, void* dv,
-                       float* dlog_alpha, float* dS0, void* workspace, size_t ws_bytes,
-                       void* stream) {
+                       const float* S0, const float* dS_final, const void* states, void* dq,
+                       void* dk, void* dv, float* dlog_alpha, float* dS0, void* workspace,
+                       size_t ws_bytes, void* stream) {
     g_errmsg[0] = '\0';
     la_status st = check_desc(d);
     if (st != LA_OK) return st;
@@ -436,7 +467,8 @@ la_status la_chunk_bwd(const la_desc* d, const void* q, const void* k, const voi
         return fail(LA_ERR_INVALID, "dlog_alpha given without a DIAG or SCALAR gate");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) || !aligned16(dq) ||
         !aligned16(dk) || !aligned16(dv) || (dlog_alpha && !aligned16(dlog_alpha)) ||
-        (S0 && !aligned16(S0)) || (dS_final && !aligned16(dS_final)) || (dS0 && !aligned16(dS0)))
+        (S0 && !aligned16(S0)) || (dS_final && !aligned16(dS_final)) || (dS0 && !aligned16(dS0)) ||
+        (states && !aligned16(states)))
         return fail(LA_ERR_INVALID, "device pointers must be 16-byte aligned");
     const int chunk = la::bwd_chunk(d->dk, d->dtype == LA_BF16);
     if (d->segments > 0 && d->segments > (d->L + chunk - 1) / chunk)
@@ -473,7 +505,8 @@ la_status la_chunk_bwd(const la_desc* d, const void* q, const void* k, const voi
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
 
-    // the states before every chunk: the forward state recurrence
+    // the states before every chunk: the forward state recurrence, unless
+    // the training forward left them behind
     p.q = q;
     p.k = k;
     p.v = v;
@@ -481,7 +514,7 @@ la_status la_chunk_bwd(const la_desc* d, const void* q, const void* k, const voi
     p.S_final = nullptr;
     p.st_rows = ws + w.fwd;
     p.st_slots = pl.nchunks + 1;
-    if (pl.P > 1) {
+    if (!states && pl.P > 1) {
         e = timed_launch(la::K_CHUNK_STATE, s, [&] {
             return chunk_launch(d, p, chunk, gate_mode, la::PASS_STATE, s, BH * (pl.P - 1));
         });
@@ -489,10 +522,12 @@ la_status la_chunk_bwd(const la_desc* d, const void* q, const void* k, const voi
         e = timed_launch(la::K_STATE_SCAN, s, [&] { return la::launch_state_scan(p, d->dk, false, s); });
         if (e != hipSuccess) return hip_fail(e, "segment scan launch");
     }
-    e = timed_launch(la::K_CHUNK_STORE, s, [&] {
-        return chunk_launch(d, p, chunk, gate_mode, la::PASS_STORE, s, BH * pl.P);
-    });
-    if (e != hipSuccess) return hip_fail(e, "state store launch");
+    if (!states) {
+        e = timed_launch(la::K_CHUNK_STORE, s, [&] {
+            return chunk_launch(d, p, chunk, gate_mode, la::PASS_STORE, s, BH * pl.P);
+        });
+        if (e != hipSuccess) return hip_fail(e, "state store launch");
+    }
 
     // the state gradient after every chunk: the same recurrence run from the
     // end with phi(q) and dout in the places of phi(k) and v
@@ -523,7 +558,7 @@ la_status la_chunk_bwd(const la_desc* d, const void* q, const void* k, const voi
     b.v = v;
     b.dout = dout;
     b.log_alpha = p.log_alpha;
-    b.st_fwd = ws + w.fwd;
+    b.st_fwd = states ? states : static_cast<const void*>(ws + w.fwd);
     b.st_rows = ws + w.rows;
     b.dq = dq;
     b.dk = dk;

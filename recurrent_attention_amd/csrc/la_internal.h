@@ -90,7 +90,8 @@ struct DeltaParams {
 // state (or its gradient) at every chunk boundary.
 enum ChunkPass {
     PASS_MAIN = 0, PASS_STATE = 1, PASS_STATE_REV = 2, PASS_STORE = 3, PASS_STORE_REV = 4,
-    PASS_MAIN_NORM = 5   // main pass with the group-norm / swish-gate output epilogue (chunk 64)
+    PASS_MAIN_NORM = 5,  // main pass with the group-norm / swish-gate output epilogue (chunk 64)
+    PASS_MAIN_STORE = 6  // main pass that also stores the state at every chunk boundary
 };
 
 // Chunk length of the backward: 64 tokens, 32 for fp32 at d = 128 (whose

@@ -180,7 +180,7 @@ def test_binding_refuses_cpu_tensors():
 
 def _bwd(desc, gate_mode=0, gate=None, S0=None, dSf=None, dla=None, dS0=None,
          ws=A, ws_bytes=1 << 40, q=A, k=A, v=A, do=A, dq=A, dk=A, dv=A):
-    return api.la_chunk_bwd(desc, q, k, v, do, gate_mode, gate, S0, dSf, dq, dk, dv,
+    return api.la_chunk_bwd(desc, q, k, v, do, gate_mode, gate, S0, dSf, None, dq, dk, dv,
                             dla, dS0, ws, ws_bytes, None)
 
 
@@ -279,3 +279,17 @@ def test_delta_validation():
     assert dec(_desc(L=1), S=None) == api.LA_ERR_INVALID
     assert api.la_delta_chunk(_desc(dk=128, dv=128, dtype=api.LA_F32)) == 32
     assert api.la_delta_chunk(_desc(dk=128, dv=128, dtype=api.LA_BF16)) == 64
+
+
+def test_train_forward_validation():
+    d = _desc(L=1000, dk=64, dv=64, dtype=api.LA_BF16)
+    # states: (ceil(1000/64) + 1) boundary states per (b,h), bf16
+    assert api.la_chunk_train_states_bytes(d) == 2 * 17 * 64 * 64 * 2
+    call = lambda desc, states=A, nbytes=1 << 40: api.la_chunk_fwd_train(
+        desc, A, A, A, 0, None, None, A, None, states, nbytes, A, 1 << 40, None)
+    assert call(_desc(L=1000, normalize=True)) == api.LA_ERR_UNSUPPORTED
+    assert call(d, states=None) == api.LA_ERR_INVALID
+    assert call(d, states=MIS) == api.LA_ERR_INVALID
+    assert call(d, nbytes=100) == api.LA_ERR_INVALID
+    assert api.la_chunk_bwd(d, A, A, A, A, 0, None, None, None, MIS, A, A, A, None, None, A,
+                            1 << 40, None) == api.LA_ERR_INVALID

@@ -205,3 +205,27 @@ def test_chunk_bwd_full_size_sampled():
     pairs = [0, 11]
     ref = _oracle_bwd(inp, DIAG, pairs=pairs)
     _check(_select(got, pairs), ref, torch.bfloat16, "full size, sampled heads")
+
+
+@pytest.mark.parametrize("mode", [NONE, GAMMA, DIAG, SCALAR])
+@pytest.mark.parametrize("dt,d", [("f32", 64), ("f32", 128), ("bf16", 128)])
+def test_training_forward_states_feed_the_backward(dt, d, mode):
+    # the training forward's outputs equal the plain prefill's, and the
+    # backward from its stored boundary states matches the oracle
+    dtype = DTYPES[dt]
+    C = api.la_chunk_bwd_chunk(api.make_desc(1, 2, 64, d, d, 1 if dt == "bf16" else 0))
+    inp = _case(1, 2, 7 * C + 5, d, dtype, mode, seed=40 + d + mode, state=True)
+    dev = "cuda"
+    t = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    la = t["log_alpha"] if mode in GATED else None
+    out, S, states = api.chunk_fwd_train(t["q"], t["k"], t["v"], gate_mode=mode,
+                                         gamma=inp["gamma"], log_alpha=la, S0=t["S0"])
+    out2, S2, _ = api.chunk_fwd(t["q"], t["k"], t["v"], gate_mode=mode, gamma=inp["gamma"],
+                                log_alpha=la, S0=t["S0"], chunk=C)
+    g = api.chunk_bwd(t["q"], t["k"], t["v"], t["dout"], gate_mode=mode, gamma=inp["gamma"],
+                      log_alpha=la, S0=t["S0"], dS_final=t["dS_final"], states=states)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2) and torch.equal(S, S2)
+    got = {k: to_host64(v) for k, v in g.items()}
+    ref = _oracle_bwd(inp, mode)
+    _check(got, ref, dtype, f"train states {dt} d={d} mode={mode}")
