@@ -291,7 +291,7 @@ def bench_backward(args, torch, api, workloads):
     }
 
 
-def bench_varlen(args, torch, api, workloads):
+def bench_varlen(args, torch, api, workloads, segments=0):
     """Packed-sequence prefill of the varlen workload, then one decode step
     of every sequence from its S_final (the hand-off)."""
     spec = workloads.VARLEN_SPEC
@@ -304,7 +304,7 @@ def bench_varlen(args, torch, api, workloads):
     q, k, v, la = inp["q"], inp["k"], inp["v"], inp["log_alpha"]
     cu = torch.tensor([0] + list(itertools.accumulate(lens)), dtype=torch.int32,
                       device=dev)
-    desc = api.make_desc(N, H, T, d, d, api.LA_BF16, 0, False, 0)
+    desc = api.make_desc(N, H, T, d, d, api.LA_BF16, 0, False, segments)
     need = api.la_chunk_fwd_varlen_workspace_bytes(desc, maxlen, chunk)
     out = torch.empty_like(v)
     S = torch.empty((N, H, d, d), dtype=torch.float32, device=dev)
@@ -627,6 +627,8 @@ def main(argv=None):
     ap.add_argument("--no-scalar", action="store_true")
     ap.add_argument("--no-retention", action="store_true")
     ap.add_argument("--no-delta", action="store_true")
+    ap.add_argument("--segments", type=int, default=0,
+                    help="segments per (b,h) for --only varlen (0 = automatic)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--only", choices=["prefill", "decode", "backward", "varlen", "scalar", "retention", "delta",
                              "copy"], default=None,
@@ -658,7 +660,7 @@ def main(argv=None):
         print(json.dumps(bench_backward(args, torch, api, workloads)), flush=True)
         return 0
     if args.only == "varlen":
-        print(json.dumps(bench_varlen(args, torch, api, workloads)), flush=True)
+        print(json.dumps(bench_varlen(args, torch, api, workloads, args.segments)), flush=True)
         return 0
     if args.only == "delta":
         print(json.dumps(bench_delta(args, torch, api, workloads)), flush=True)

@@ -83,7 +83,7 @@ void decode_kernel(const DecodeParams p) {
             s[1] = a * s[1] + kk * vv.y;
             s[2] = a * s[2] + kk * vv.z;
             s[3] = a * s[3] + kk * vv.w;
-            __builtin_nontemporal_store(s, &S[(size_t)row * CQ + cq]);
+            sreg[ps] = s;
             acc.x += qq * s[0];
             acc.y += qq * s[1];
             acc.z += qq * s[2];
@@ -99,6 +99,11 @@ void decode_kernel(const DecodeParams p) {
     }
     __syncthreads();
 
+#pragma unroll
+    for (int ps = 0; ps < NPASS; ++ps) {
+        const int row = ps * RPP + rr;
+        if (row < DK) __builtin_nontemporal_store(sreg[ps], &S[(size_t)row * CQ + cq]);
+    }
     if (tid < DV) {
         float o = 0.f;
 #pragma unroll
