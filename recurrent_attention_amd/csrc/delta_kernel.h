@@ -16,7 +16,7 @@
 // its accumulated writes are K^T U.  Everything but T is a dense product on
 // the matrix cores; T is formed in fp32 by blocked forward substitution
 // (16 x 16 diagonal blocks inverted by one lane per column, the blocks
-// below them by fp32 matrix-core products, one block diagonal at a time).
+// below them by fp32 matrix-core products, one block column per wave).
 //
 // One workgroup per (b,h) runs the chunks in order (the chunk-to-chunk map
 // S -> (I - K^T W) S + K^T U is a full d_k x d_k matrix, so the segment
@@ -70,8 +70,11 @@ struct DeltaSmem {
     alignas(16) E up[C][D];       // U'  [s][swizzled n]
     alignas(16) E pm[C][C];       // P = Q K^T * mask  [t][swizzled s]
     alignas(16) E tm[C][C];       // T   [s][swizzled j]
-    alignas(16) float lm[C][C];   // A (strictly lower)
-    alignas(16) float nm[C][C];   // (I + A)^-1
+    // fp32 rows padded by 4 so that 16 lanes reading one column of 16
+    // rows spread over the banks
+    static constexpr int LDP = C + 4;
+    alignas(16) float lm[C][LDP];   // A (strictly lower)
+    alignas(16) float nm[C][LDP];   // (I + A)^-1, lower blocks
     alignas(16) float xs[Cfg::NW][16][16];   // per-wave staging of a 16 x 16 block
     float beta[C];
 };
@@ -110,6 +113,8 @@ __global__ __launch_bounds__(Cfg::NT) void delta_chunk_kernel(const DeltaParams 
     for (int i = tid; i < C * C; i += Cfg::NT) {
         (&sm.pm[0][0])[i] = E(0);
         (&sm.tm[0][0])[i] = E(0);
+    }
+    for (int i = tid; i < C * DeltaSmem<Cfg>::LDP; i += Cfg::NT) {
         (&sm.lm[0][0])[i] = 0.f;
         (&sm.nm[0][0])[i] = 0.f;
     }
@@ -155,9 +160,8 @@ __global__ __launch_bounds__(Cfg::NT) void delta_chunk_kernel(const DeltaParams 
         __syncthreads();
         if (c + 1 < nchunks) load(c + 1);
 
-        // ---- A = strict_lower(diag(beta) K K^T) and P = Q K^T * inclusive
-        // mask, computed transposed ([s][t] tiles) so each lane holds 4
-        // consecutive s of one t
+        // ---- A = strict_lower(diag(beta) K K^T), computed transposed ([s][t]
+        // tiles) so each lane holds 4 consecutive s of one t
         {
             int idx = 0;
 #pragma unroll
@@ -165,57 +169,107 @@ __global__ __launch_bounds__(Cfg::NT) void delta_chunk_kernel(const DeltaParams 
 #pragma unroll
                 for (int sb = 0; sb <= tb; ++sb, ++idx) {
                     if (idx % NW != wave) continue;
-                    f32x4_t ag = {0.f, 0.f, 0.f, 0.f}, ap = {0.f, 0.f, 0.f, 0.f};
+                    f32x4_t ag = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int kk = 0; kk < D / MK; ++kk) {
-                        const Frag a = row_frag<Cfg, DM>(&sm.k[0][0], D, 16 * sb, kk * MK, lane);
-                        ag = T::mma(a, row_frag<Cfg, DM>(&sm.k[0][0], D, 16 * tb, kk * MK, lane), ag);
-                        ap = T::mma(a, row_frag<Cfg, DM>(&sm.q[0][0], D, 16 * tb, kk * MK, lane), ap);
-                    }
+                    for (int kk = 0; kk < D / MK; ++kk)
+                        ag = T::mma(row_frag<Cfg, DM>(&sm.k[0][0], D, 16 * sb, kk * MK, lane),
+                                    row_frag<Cfg, DM>(&sm.k[0][0], D, 16 * tb, kk * MK, lane), ag);
                     const int t = 16 * tb + r, s0 = 16 * sb + 4 * g;
                     const float bt = sm.beta[t];
-                    float xl[4], xp[4];
+                    float xl[4];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        xl[i] = s0 + i < t ? bt * ag[i] : 0.f;
-                        xp[i] = s0 + i <= t ? ap[i] : 0.f;
-                    }
+                    for (int i = 0; i < 4; ++i) xl[i] = s0 + i < t ? bt * ag[i] : 0.f;
                     *reinterpret_cast<float4*>(&sm.lm[t][s0]) = make_float4(xl[0], xl[1], xl[2], xl[3]);
-                    store_run<BF16, 4>(&sm.pm[t][bw_pos<Cfg, TM>(t, s0)], xp);
                 }
         }
         __syncthreads();
 
-        // ---- (I + A)^-1: diagonal 16 x 16 blocks by forward substitution,
-        // lane j of the block's wave solving for column j
-        for (int blk = wave; blk < NBLK; blk += NW) {
-            if (lane < 16) {
-                const int b0 = 16 * blk, j = lane;
-                float x[16];
+        // ---- the diagonal 16 x 16 blocks of N = (I + A)^-1 by forward
+        // substitution, one wave per block: the lane quad 4j..4j+3 solves
+        // for column j, lane q of it holding rows q, q+4, q+8, q+12 and
+        // summing every fourth term of each row's dot product; their part of
+        // T = N diag(beta) with them.  The other waves meanwhile form
+        // P = Q K^T * inclusive mask ([s][t] tiles, as for A)
+        {
+            constexpr int DW = NW > NBLK ? NBLK : NW;       // waves on diagonal blocks
+            constexpr int PW0 = NW > NBLK ? NBLK : 0;       // first wave on P tiles
+            constexpr int PW = NW - PW0;
+            if (wave < DW) {
+                const int j = lane >> 2, qq = lane & 3;
+                for (int blk = wave; blk < NBLK; blk += DW) {
+                    const int b0 = 16 * blk;
+                    float xo[4] = {0.f, 0.f, 0.f, 0.f};   // x[4 m + qq]
 #pragma unroll
-                for (int rr = 0; rr < 16; ++rr) {
-                    float acc = rr == j ? 1.f : 0.f;
+                    for (int rr = 0; rr < 16; ++rr) {
+                        float part = 0.f;
 #pragma unroll
-                    for (int cc = 0; cc < rr; ++cc) acc -= sm.lm[b0 + rr][b0 + cc] * x[cc];
-                    x[rr] = acc;
+                        for (int m = 0; m < 4; ++m) {
+                            if (4 * m >= rr) break;
+                            const int cc = 4 * m + qq;
+                            const float a = sm.lm[b0 + rr][b0 + cc];   // 0 for cc >= rr
+                            part += a * xo[m];
+                        }
+                        part += dpp_row<0xB1>(part);   // quad_perm [1,0,3,2]
+                        part += dpp_row<0x4E>(part);   // quad_perm [2,3,0,1]
+                        const float xr = (rr == j ? 1.f : 0.f) - part;
+                        if (qq == (rr & 3)) xo[rr >> 2] = xr;
+                    }
+                    const float bj = sm.beta[b0 + j];
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) {
+                        const int row = b0 + 4 * m + qq;
+                        sm.nm[row][b0 + j] = xo[m];
+                        sm.tm[row][bw_pos<Cfg, TM>(row, b0 + j)] = T::fromf(xo[m] * bj);
+                    }
                 }
+            }
+            if (wave >= PW0) {
+                int idx = 0;
 #pragma unroll
-                for (int rr = 0; rr < 16; ++rr) sm.nm[b0 + rr][b0 + j] = x[rr];
+                for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+                    for (int sb = 0; sb <= tb; ++sb, ++idx) {
+                        if (idx % PW != wave - PW0) continue;
+                        f32x4_t ap = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int kk = 0; kk < D / MK; ++kk)
+                            ap = T::mma(row_frag<Cfg, DM>(&sm.k[0][0], D, 16 * sb, kk * MK, lane),
+                                        row_frag<Cfg, DM>(&sm.q[0][0], D, 16 * tb, kk * MK, lane), ap);
+                        const int t = 16 * tb + r, s0 = 16 * sb + 4 * g;
+                        float xp[4];
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) xp[i] = s0 + i <= t ? ap[i] : 0.f;
+                        store_run<BF16, 4>(&sm.pm[t][bw_pos<Cfg, TM>(t, s0)], xp);
+                    }
             }
         }
         __syncthreads();
-        // blocks below the diagonal, one block diagonal at a time:
-        // N_ij = -N_ii sum_{j <= m < i} A_im N_mj
-        for (int dist = 1; dist < NBLK; ++dist) {
-            for (int b = wave; b < NBLK - dist; b += NW) {
-                const int bi = 16 * (b + dist), bj = 16 * b;
-                f32x4_t x = {0.f, 0.f, 0.f, 0.f};
-                for (int m = b; m < b + dist; ++m) {
+
+        // ---- the blocks below the diagonal, one block column per wave (the
+        // blocks of column j need only N_jj, the diagonal blocks and the
+        // column's own earlier blocks, so no workgroup barrier between them):
+        // N_ij = -N_ii sum_{j <= m < i} A_im N_mj, and T_ij = N_ij beta_j
+#pragma unroll
+        for (int jb = 0; jb < NBLK - 1; ++jb) {
+            if (jb % NW != wave) continue;   // uniform: compile-time block indices below
+            const int bj = 16 * jb;
+            const float betj = sm.beta[bj + r];
+#pragma unroll
+            for (int ib = jb + 1; ib < NBLK; ++ib) {
+                const int bi = 16 * ib;
+                // one accumulator per term, so the products do not wait on each other
+                f32x4_t xm[NBLK];
+#pragma unroll
+                for (int m = jb; m < ib; ++m) {
                     const int bm = 16 * m;
+                    xm[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int k4 = 0; k4 < 4; ++k4)
-                        x = F::mma(sm.lm[bi + r][bm + 4 * k4 + g], sm.nm[bm + 4 * k4 + g][bj + r], x);
+                        xm[m] = F::mma(sm.lm[bi + r][bm + 4 * k4 + g], sm.nm[bm + 4 * k4 + g][bj + r], xm[m]);
                 }
+                f32x4_t x = xm[jb];
+#pragma unroll
+                for (int m = jb + 1; m < ib; ++m) x += xm[m];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) sm.xs[wave][4 * g + i][r] = x[i];
                 __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -226,18 +280,15 @@ __global__ __launch_bounds__(Cfg::NT) void delta_chunk_kernel(const DeltaParams 
                 for (int k4 = 0; k4 < 4; ++k4)
                     y = F::mma(sm.nm[bi + r][bi + 4 * k4 + g], sm.xs[wave][4 * k4 + g][r], y);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) sm.nm[bi + 4 * g + i][bj + r] = -y[i];
+                for (int i = 0; i < 4; ++i) {
+                    const int row = bi + 4 * g + i;
+                    sm.nm[row][bj + r] = -y[i];
+                    sm.tm[row][bw_pos<Cfg, TM>(row, bj + r)] = T::fromf(-y[i] * betj);
+                }
                 __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
                 __builtin_amdgcn_wave_barrier();
                 __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             }
-            __syncthreads();
-        }
-
-        // ---- T = (I + A)^-1 diag(beta), lower blocks only
-        for (int e = tid; e < C * C; e += Cfg::NT) {
-            const int s = e / C, j = e % C;
-            if ((j >> 4) <= (s >> 4)) sm.tm[s][bw_pos<Cfg, TM>(s, j)] = T::fromf(sm.nm[s][j] * sm.beta[j]);
         }
         __syncthreads();
 
