@@ -334,7 +334,7 @@ def bench_varlen(args, torch, api, workloads, segments=0):
     torch.cuda.synchronize()
     api.la_profile_end()
     kern = {}
-    for name in ("chunk_main", "chunk_state", "state_scan"):
+    for name in ("seq_order", "chunk_main", "chunk_state", "state_scan"):
         n, ms = api.la_profile_query(name)
         kern[name] = round(ms / n * 1e3, 2) if n else None
     # hand-off: one decode step of all N sequences from their prefill states

@@ -155,6 +155,10 @@ la_status la_chunk_fwd(const la_desc* d, const void* q, const void* k,
  *   S0, S_final  device fp32 [B,H,dk,dv] per sequence (NULL as before)
  *   z0, z_final  device fp32 [B,H,dk]
  *   workspace    la_chunk_fwd_varlen_workspace_bytes(d, max_seqlen, chunk)
+ *                bytes, 16-byte aligned, never NULL: besides the segment
+ *                slots it holds the launch order of the sequences (longest
+ *                first, computed on the device; the order affects only
+ *                the scheduling, never a result)
  * Everything else as for la_chunk_fwd.
  */
 la_status la_chunk_fwd_varlen(const la_desc* d, const int* cu_seqlens,
@@ -166,8 +170,8 @@ la_status la_chunk_fwd_varlen(const la_desc* d, const int* cu_seqlens,
                               void* workspace, size_t workspace_bytes,
                               void* stream);
 
-/* Workspace bytes of la_chunk_fwd_varlen (0 if none is needed or the
- * arguments are invalid). */
+/* Workspace bytes of la_chunk_fwd_varlen (at least 16; 0 if the arguments
+ * are invalid). */
 size_t la_chunk_fwd_varlen_workspace_bytes(const la_desc* d, int max_seqlen,
                                            int chunk);
 

@@ -261,7 +261,13 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
     constexpr bool BACKAGG = AGG && !REV;
     const int PS = AGG ? P - 1 : P;
     const int seg = blockIdx.x % PS + ((AGG && REV) ? 1 : 0);
-    const int bh = blockIdx.x / PS;
+    // packed sequences run in the given order (longest first), the heads of
+    // one sequence side by side
+    int bh = blockIdx.x / PS;
+    if (p.seq_order) {
+        const int nseq = p.BH / p.H;
+        bh = min(max(p.seq_order[bh / p.H], 0), nseq - 1) * p.H + bh % p.H;
+    }
     const int h = bh % p.H;
     // the token range of this (b,h) slice: all L tokens of slice bh, or
     // (packed sequences) tokens [cu[n], cu[n+1]) of head h's p.L tokens,

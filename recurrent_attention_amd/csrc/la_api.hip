@@ -55,6 +55,11 @@ size_t workspace_bytes(const la_desc* d, const Plan& pl) {
     return slots * ((size_t)d->dk * d->dv + 2 * (size_t)d->dk) * sizeof(float);
 }
 
+// Packed sequences: after the segment slots, the launch order of the
+// sequences (int32 [B], rounded up to 16 bytes).
+size_t align16(size_t n) { return (n + 15) & ~(size_t)15; }
+size_t order_bytes(const la_desc* d) { return align16((size_t)d->B * sizeof(int)); }
+
 bool supported_d(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 bool supported_chunk(int c) { return c == 16 || c == 32 || c == 64; }
 
@@ -124,7 +129,7 @@ std::vector<hipEvent_t> g_event_pool;
 
 const char* kKernelNames[la::K_COUNT] = {"chunk_main", "chunk_state", "state_scan", "decode",
                                          "chunk_store", "chunk_bwd", "delta_chunk",
-                                         "delta_decode"};
+                                         "delta_decode", "seq_order"};
 
 hipEvent_t take_event() {
     if (!g_event_pool.empty()) {
@@ -222,7 +227,7 @@ BwdLayout bwd_layout(const la_desc* d, const Plan& pl) {
 // The descriptor the segment plan is made for: packed sequences plan for the
 // longest one (every sequence gets the same number of segments; those past
 // a shorter sequence's end are empty and compose as the identity).
-la_desc plan_desc(const la_desc* d, const void* packed, int max_seqlen) {
+la_desc plan_desc(const la_desc* d, bool packed, int max_seqlen) {
     la_desc dp = *d;
     if (packed) dp.L = max_seqlen;
     return dp;
@@ -250,7 +255,7 @@ la_status chunk_fwd_impl(const la_desc* d, const int* cu_seqlens, int max_seqlen
                          float* z_final, void* workspace, size_t ws_bytes, void* stream,
                          void* states = nullptr) {
     // packed sequences plan their segments for the longest one
-    const la_desc dp = plan_desc(d, cu_seqlens, max_seqlen);
+    const la_desc dp = plan_desc(d, cu_seqlens != nullptr, max_seqlen);
     la_status st;
     if (!supported_chunk(chunk))
         return fail(LA_ERR_UNSUPPORTED, "chunk must be 16, 32 or 64 (got %d)", chunk);
@@ -284,7 +289,8 @@ la_status chunk_fwd_impl(const la_desc* d, const int* cu_seqlens, int max_seqlen
     if (st != LA_OK) return st;
 
     const Plan pl = make_plan(&dp, chunk);
-    const size_t need = workspace_bytes(&dp, pl);
+    const size_t seg_bytes = align16(workspace_bytes(&dp, pl));
+    const size_t need = seg_bytes + (cu_seqlens ? order_bytes(d) : 0);
     if (need > 0) {
         if (!workspace) return fail(LA_ERR_INVALID, "workspace of %zu bytes is required", need);
         if (!aligned16(workspace)) return fail(LA_ERR_INVALID, "workspace must be 16-byte aligned");
@@ -325,6 +331,14 @@ la_status chunk_fwd_impl(const la_desc* d, const int* cu_seqlens, int max_seqlen
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
+    if (cu_seqlens) {
+        int* order = reinterpret_cast<int*>(static_cast<char*>(workspace) + seg_bytes);
+        e = timed_launch(la::K_SEQ_ORDER, s, [&] {
+            return la::launch_seq_order(cu_seqlens, d->B, d->L, chunk, max_seqlen, order, s);
+        });
+        if (e != hipSuccess) return hip_fail(e, "sequence order launch");
+        p.seq_order = order;
+    }
     if (pl.P > 1) {
         // state pass over every segment but the last, then the segment scan
         e = timed_launch(la::K_CHUNK_STATE, s, [&] {
@@ -435,8 +449,8 @@ la_status la_chunk_fwd_varlen(const la_desc* d, const int* cu_seqlens, int max_s
 size_t la_chunk_fwd_varlen_workspace_bytes(const la_desc* d, int max_seqlen, int chunk) {
     if (check_desc(d) != LA_OK || !supported_chunk(chunk) || max_seqlen < 1 || max_seqlen > d->L)
         return 0;
-    const la_desc dp = plan_desc(d, d, max_seqlen);
-    return workspace_bytes(&dp, make_plan(&dp, chunk));
+    const la_desc dp = plan_desc(d, true, max_seqlen);
+    return align16(workspace_bytes(&dp, make_plan(&dp, chunk))) + order_bytes(d);
 }
 
 size_t la_chunk_bwd_workspace_bytes(const la_desc* d) {

@@ -26,6 +26,7 @@ struct ChunkParams {
     float* ws_a;            // [BH, P, dk]    segment decay products
     float* ws_z;            // [BH, P, dk]    segment normaliser parts
     const int* cu_seqlens;  // packed sequences: [B + 1] token offsets into each head's L tokens, or null
+    const int* seq_order;   // packed sequences: the launch order of the sequences (a permutation of [0, B)), or null
     const float* gn_w;      // output group norm: per-channel scale [H, dv] or null (ones)
     const float* gn_b;      //   per-channel shift [H, dv] or null (zeros)
     const void* gn_gate;    //   swish gate [BH, L, dv] dtype, or null
@@ -101,7 +102,7 @@ constexpr int bwd_chunk(int d, bool bf16) { return (!bf16 && d >= 128) ? 32 : 64
 // Kernel families, as named by the profiling interface.
 enum KernelId {
     K_CHUNK_MAIN = 0, K_CHUNK_STATE = 1, K_STATE_SCAN = 2, K_DECODE = 3,
-    K_CHUNK_STORE = 4, K_BWD = 5, K_DELTA = 6, K_DELTA_DECODE = 7, K_COUNT = 8
+    K_CHUNK_STORE = 4, K_BWD = 5, K_DELTA = 6, K_DELTA_DECODE = 7, K_SEQ_ORDER = 8, K_COUNT = 9
 };
 
 // Launch hooks implemented in the kernel files.  Each returns hipSuccess or
@@ -118,6 +119,9 @@ LA_DECLARE_CHUNK_LAUNCHER(launch_chunk_bf16_d64)
 LA_DECLARE_CHUNK_LAUNCHER(launch_chunk_bf16_d128)
 #undef LA_DECLARE_CHUNK_LAUNCHER
 hipError_t launch_state_scan(const ChunkParams& p, int d, bool rev, hipStream_t s);
+// Packed sequences: order[0..B) = the sequences by decreasing chunk count.
+hipError_t launch_seq_order(const int* cu_seqlens, int B, int T, int chunk, int max_seqlen,
+                            int* order, hipStream_t s);
 #define LA_DECLARE_DELTA_LAUNCHER(NAME) \
     hipError_t NAME(const DeltaParams& p, bool decode, hipStream_t s);
 LA_DECLARE_DELTA_LAUNCHER(launch_delta_f32_d16)

@@ -34,6 +34,7 @@ FAMILIES = [
     ("delta_chunk", re.compile(r"la::delta_chunk_kernel")),
     ("delta_decode", re.compile(r"la::delta_decode_kernel")),
     ("decode", re.compile(r"la::decode_kernel")),
+    ("seq_order", re.compile(r"seq_order_kernel")),
     ("copy", re.compile(r"__amd_rocclr_copyBuffer")),
 ]
 

@@ -244,7 +244,12 @@ def test_varlen_workspace_plans_for_the_longest_sequence():
     # automatic plan gives every (sequence, head) ceil(256 / 6) -> 16 segments
     d = _desc(B=3, H=2, L=1500)
     need = api.la_chunk_fwd_varlen_workspace_bytes(d, 1000, 64)
-    assert need == 3 * 2 * 16 * (64 * 64 + 2 * 64) * 4
+    # segment slots, then the launch order of the 3 sequences (int32, 16-byte rounded)
+    assert need == 3 * 2 * 16 * (64 * 64 + 2 * 64) * 4 + 16
+    # one segment each: only the order array
+    d1 = _desc(B=3, H=2, L=1500, segments=1)
+    assert api.la_chunk_fwd_varlen_workspace_bytes(d1, 1000, 64) == 16
+    assert _varlen(d1, max_seqlen=1000, ws=None) == api.LA_ERR_INVALID
     assert api.la_chunk_fwd_varlen_workspace_bytes(d, 1501, 64) == 0   # invalid
     assert _varlen(d, max_seqlen=1000, ws=None) == api.LA_ERR_INVALID
     assert _varlen(d, max_seqlen=1000, ws=A, ws_bytes=need - 16) == api.LA_ERR_INVALID

@@ -191,3 +191,16 @@ def test_varlen_prefill_then_decode_hand_off():
         e = slice_rel_err(got[n:n + 1], ref[:, :, b - a:])
         assert e <= 2e-2, (n, e)
         assert slice_rel_err(to_host64(S)[n:n + 1], Sref) <= 2e-2, n
+
+
+@pytest.mark.parametrize("lens_kind", ["mixed", "equal"])
+def test_varlen_many_sequences_launch_order(lens_kind):
+    # more sequences than the ordering workgroup has threads, so the device
+    # sort of the launch order loops; many equal chunk counts (ties) and
+    # empty sequences.  The order must change no result.
+    rng = np.random.default_rng(31)
+    lens = (rng.integers(0, 41, size=1500) if lens_kind == "mixed" else np.full(1100, 32)).tolist()
+    inp = _packed(lens, 2, 16, torch.float32, DIAG, seed=33)
+    got = _run_gpu(inp, DIAG, 16)
+    ref = _run_oracle(inp, DIAG)
+    _check(got, ref, inp["cu"].numpy(), torch.float32, f"{len(lens)} sequences, {lens_kind}")
