@@ -10,8 +10,9 @@
 // at d = 128, where that streams best, else 256): each thread owns a quad of
 // consecutive columns (16-byte non-temporal accesses, a whole 512-byte row
 // per 32 threads) over DK / rows-per-pass rows, issues all its state loads
-// before using them, and the partial outputs of the row groups are reduced
-// through LDS.
+// before using them and keeps the updated rows in registers; the partial
+// outputs of the row groups are reduced through LDS, and the updated rows
+// are stored after that barrier.
 #include "la_device.h"
 #include "la_internal.h"
 
@@ -22,10 +23,11 @@ struct DecodeShape {
     static constexpr int NT = DK * DV >= 128 * 128 ? 512 : 256;   // threads
 };
 
-// eight waves per SIMD (at most 64 registers) keep four 512-thread
-// workgroups, 256 KiB of state reads, in flight per CU
+// four waves per SIMD (up to 128 registers; two 512-thread workgroups,
+// 128 KiB of state reads, in flight per CU) stream as fast as eight, which
+// would cap the kernel at 64 registers and spill the held rows to scratch
 template <int DK, int DV, bool BF16, int GATE>
-__global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) __attribute__((amdgpu_waves_per_eu(8, 8)))
+__global__ __launch_bounds__((DecodeShape<DK, DV>::NT)) __attribute__((amdgpu_waves_per_eu(4, 4)))
 void decode_kernel(const DecodeParams p) {
     using T = Elem<BF16>;
     using E = typename T::E;
