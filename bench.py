@@ -6,6 +6,15 @@ Step = one chunkwise prefill of the gated-linear-attention workload
 fp32 diagonal log-gates, chunk 64): state pass, segment scan and main pass,
 inputs resident in HBM.  ``value`` is sequence tokens per second.
 
+Timing of every prefill-like part (the prefill, its backward and training
+step, the packed, scalar-gate, retention and delta prefills): warm-up
+steps, then K steps, each after a 512 MiB write that evicts the 256 MB
+Infinity Cache and bracketed by HIP events on the stream; ``ms_per_step``
+is their mean (``step_ms`` adds the median, the minimum and the mean of K
+steps run back to back without the flush).  Per-kernel averages come from
+a further K flushed steps.  Decode steps run back to back (1 GiB of state
+per step leaves nothing to reuse).
+
 Also reported, in the same line:
 * ``roofline``: the dominant kernel (the main chunk pass), its algorithmic
   bytes per launch over its average duration measured with HIP events that
@@ -107,6 +116,72 @@ def measured_traffic(name, src_hash):
     return rec.get("hbm_bytes_per_launch")
 
 
+FLUSH_BYTES = 512 << 20
+
+
+class CacheFlush:
+    """Writes a 512 MiB scratch buffer, twice the 256 MB Infinity Cache, so
+    that a step timed after it finds none of its inputs cached (the 34 MB
+    and 270 MB workloads would otherwise run partly from the cache when
+    repeated back to back)."""
+
+    def __init__(self, torch, dev, on=True):
+        self.buf = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev) if on else None
+        self.n = 0
+
+    def __call__(self):
+        if self.buf is not None:
+            self.n += 1
+            self.buf.fill_(float(self.n & 7))
+
+
+def time_steps(torch, step, args, flush):
+    """Step times in ms: `warmup` steps, then `steps` steps each after a
+    cache flush and bracketed by events on the current stream (mean, median,
+    min), and the mean of as many steps run back to back without flushes."""
+    for _ in range(args.warmup):
+        flush()
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    for a, b in ev:
+        flush()
+        a.record()
+        step()
+        b.record()
+    torch.cuda.synchronize()
+    per = sorted(a.elapsed_time(b) for a, b in ev)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    b2b = (time.perf_counter() - t0) / args.steps * 1e3
+    return {"mean": sum(per) / len(per), "median": per[len(per) // 2], "min": per[0],
+            "back_to_back": b2b}
+
+
+def kernel_avgs(torch, api, step, args, flush, names):
+    """Average duration (us) of each named kernel family over `steps` steps,
+    each after a cache flush, from the library's per-launch HIP events."""
+    api.la_profile_begin()
+    for _ in range(args.steps):
+        flush()
+        step()
+    torch.cuda.synchronize()
+    api.la_profile_end()
+    out = {}
+    for name in names:
+        n, ms = api.la_profile_query(name)
+        out[name] = (ms / n * 1e3) if n else None
+    return out
+
+
+def step_times(t):
+    return {"median": round(t["median"], 4), "min": round(t["min"], 4),
+            "back_to_back": round(t["back_to_back"], 4)}
+
+
 def prefill_bytes(w):
     """Algorithmic bytes of one prefill: q, k, v, out in bf16 (+ fp32 log
     gates: d_k per token-head for the diagonal gate, one for the scalar
@@ -145,27 +220,14 @@ def bench_prefill(args, torch, api, workloads, name=None):
         if st != 0:
             raise RuntimeError(api.la_last_error_message())
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    flush = CacheFlush(torch, dev, not args.no_flush)
+    times = time_steps(torch, step, args, flush)
+    # a second pass over as many steps with per-kernel HIP events on the stream
+    kern = {name: {"avg_us": us} for name, us in
+            kernel_avgs(torch, api, step, args, flush,
+                        ("chunk_main", "chunk_state", "state_scan")).items()}
 
-    # second pass over the same steps with per-kernel HIP events on the stream
-    api.la_profile_begin()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    api.la_profile_end()
-    kern = {}
-    for name in ("chunk_main", "chunk_state", "state_scan"):
-        n, ms = api.la_profile_query(name)
-        kern[name] = {"launches": n, "avg_us": (ms / n * 1e3) if n else None}
-
-    ms_step = elapsed / args.steps * 1e3
+    ms_step = times["mean"]
     tokens = w.B * w.L
     bytes_alg = prefill_bytes(w)
     flops = prefill_flops(w)
@@ -174,6 +236,7 @@ def bench_prefill(args, torch, api, workloads, name=None):
     traffic = measured_traffic(f"chunk_main_{w.name}", kernel_source_hash())
     return {
         "w": w, "P": P, "ms_step": ms_step, "tokens_per_s": tokens / (ms_step * 1e-3),
+        "times": step_times(times),
         "kernels": kern, "bytes": bytes_alg, "flops": flops,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
@@ -226,14 +289,8 @@ def bench_backward(args, torch, api, workloads):
         if st != 0:
             raise RuntimeError(api.la_last_error_message())
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    flush = CacheFlush(torch, dev, not args.no_flush)
+    times = time_steps(torch, step, args, flush)
     # a training step: the forward that keeps its boundary states, then the
     # backward from them
     nst = api.la_chunk_train_states_bytes(desc)
@@ -251,34 +308,22 @@ def bench_backward(args, torch, api, workloads):
         if lib.la_chunk_fwd_train(*fargv) != 0 or lib.la_chunk_bwd(*bargv) != 0:
             raise RuntimeError(api.la_last_error_message())
 
-    for _ in range(args.warmup):
-        train_step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        train_step()
-    torch.cuda.synchronize()
-    train_ms = (time.perf_counter() - t0) / args.steps * 1e3
+    ttimes = time_steps(torch, train_step, args, flush)
+    train_ms = ttimes["mean"]
 
-    api.la_profile_begin()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    api.la_profile_end()
-    kern = {}
-    for name in ("chunk_state", "state_scan", "chunk_store", "chunk_bwd"):
-        n, ms = api.la_profile_query(name)
-        kern[name] = round(ms / n * 1e3, 2) if n else None
-    ms_step = elapsed / args.steps * 1e3
+    kern = {k: (round(v, 2) if v else None) for k, v in kernel_avgs(
+        torch, api, step, args, flush, ("chunk_state", "state_scan", "chunk_store", "chunk_bwd")).items()}
+    ms_step = times["mean"]
     bw_us = kern["chunk_bwd"]
     kb = backward_kernel_bytes(w, chunk)
     achieved = kb / (bw_us * 1e-6) / 1e9
     alg = backward_bytes(w)
     return {
         "workload": w.name, "chunk": chunk, "ms_per_step": round(ms_step, 4),
+        "step_ms": step_times(times),
         "tokens_per_s": round(w.B * w.L / (ms_step * 1e-3), 1),
         "train_step": {"what": "la_chunk_fwd_train + la_chunk_bwd from its states",
-                       "ms_per_step": round(train_ms, 4),
+                       "ms_per_step": round(train_ms, 4), "step_ms": step_times(ttimes),
                        "tokens_per_s": round(w.B * w.L / (train_ms * 1e-3), 1)},
         "algorithmic_bytes": alg,
         "pct_of_hbm_peak_step": round(100.0 * alg / (ms_step * 1e-3) / (HBM_PEAK_GBS * 1e9), 2),
@@ -320,23 +365,10 @@ def bench_varlen(args, torch, api, workloads, segments=0):
         if st != 0:
             raise RuntimeError(api.la_last_error_message())
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    api.la_profile_begin()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    api.la_profile_end()
-    kern = {}
-    for name in ("seq_order", "chunk_main", "chunk_state", "state_scan"):
-        n, ms = api.la_profile_query(name)
-        kern[name] = round(ms / n * 1e3, 2) if n else None
+    flush = CacheFlush(torch, dev, not args.no_flush)
+    times = time_steps(torch, step, args, flush)
+    kern = {k: (round(v, 2) if v else None) for k, v in kernel_avgs(
+        torch, api, step, args, flush, ("seq_order", "chunk_main", "chunk_state", "state_scan")).items()}
     # hand-off: one decode step of all N sequences from their prefill states
     qd, kd, vd, lad = workloads.decode_tokens(N, H, d, d, 1, seed=1, device=dev, gate=True)
     od = torch.empty((N, H, d), dtype=torch.bfloat16, device=dev)
@@ -347,7 +379,7 @@ def bench_varlen(args, torch, api, workloads, segments=0):
     if st != 0:
         raise RuntimeError(api.la_last_error_message())
     torch.cuda.synchronize()
-    ms_step = elapsed / args.steps * 1e3
+    ms_step = times["mean"]
     per_th = 2 * (3 * d) + 4 * d + 2 * d          # q, k, v, log-gates in; out
     alg = H * T * per_th + N * H * d * d * 4
     main_us = kern["chunk_main"]
@@ -356,7 +388,8 @@ def bench_varlen(args, torch, api, workloads, segments=0):
         "workload": workloads.VARLEN_HEADLINE, "sequences": N, "tokens": T, "max_seqlen": maxlen,
         "segments": api.la_chunk_fwd_segments(api.make_desc(N, H, maxlen, d, d, api.LA_BF16,
                                                             0, False, 0), chunk),
-        "ms_per_step": round(ms_step, 4), "tokens_per_s": round(T / (ms_step * 1e-3), 1),
+        "ms_per_step": round(ms_step, 4), "step_ms": step_times(times),
+        "tokens_per_s": round(T / (ms_step * 1e-3), 1),
         "algorithmic_bytes": alg,
         "pct_of_hbm_peak_step": round(100.0 * alg / (ms_step * 1e-3) / (HBM_PEAK_GBS * 1e9), 2),
         "kernels_avg_us": kern,
@@ -395,22 +428,11 @@ def bench_retention(args, torch, api, workloads):
             None, None, w.chunk)
     tail = (out.data_ptr(), S.data_ptr(), None, ws.data_ptr(), need, sp)
 
+    flush = CacheFlush(torch, dev, not args.no_flush)
+
     def timed(fn):
-        for _ in range(args.warmup):
-            fn()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            fn()
-        torch.cuda.synchronize()
-        ms = (time.perf_counter() - t0) / args.steps * 1e3
-        api.la_profile_begin()
-        for _ in range(args.steps):
-            fn()
-        torch.cuda.synchronize()
-        api.la_profile_end()
-        n, kms = api.la_profile_query("chunk_main")
-        return ms, kms / n * 1e3
+        t = time_steps(torch, fn, args, flush)
+        return t["mean"], kernel_avgs(torch, api, fn, args, flush, ("chunk_main",))["chunk_main"], t
 
     def plain():
         if lib.la_chunk_fwd(*head, *tail) != 0:
@@ -420,13 +442,14 @@ def bench_retention(args, torch, api, workloads):
         if lib.la_chunk_fwd_groupnorm(*head, ctypes.byref(gn), *tail) != 0:
             raise RuntimeError(api.la_last_error_message())
 
-    ms0, k0 = timed(plain)
-    ms1, k1 = timed(normed)
+    ms0, k0, t0 = timed(plain)
+    ms1, k1, t1 = timed(normed)
     tokens = w.B * w.L
     return {"workload": name, "tokens_per_s": round(tokens / (ms0 * 1e-3), 1),
-            "ms_per_step": round(ms0, 4), "main_avg_us": round(k0, 2),
+            "ms_per_step": round(ms0, 4), "step_ms": step_times(t0), "main_avg_us": round(k0, 2),
             "groupnorm_swish": {"tokens_per_s": round(tokens / (ms1 * 1e-3), 1),
-                                "ms_per_step": round(ms1, 4), "main_avg_us": round(k1, 2),
+                                "ms_per_step": round(ms1, 4), "step_ms": step_times(t1),
+                                "main_avg_us": round(k1, 2),
                                 "extra_bytes": w.B * w.H * w.L * w.dv * 2}}
 
 
@@ -450,21 +473,11 @@ def bench_delta(args, torch, api, workloads):
         if lib.la_delta_fwd(*argv) != 0:
             raise RuntimeError(api.la_last_error_message())
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) / args.steps * 1e3
-    api.la_profile_begin()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    api.la_profile_end()
-    n, kms = api.la_profile_query("delta_chunk")
-    kus = kms / n * 1e3
+    flush = CacheFlush(torch, dev, not args.no_flush)
+    ptimes = time_steps(torch, step, args, flush)
+    ms = ptimes["mean"]
+    kus = kernel_avgs(torch, api, step, args, flush, ("delta_chunk",))["delta_chunk"]
+    del flush
     per_th = 2 * 4 * d + 4          # q, k, v, out bf16 + beta fp32
     alg = B * H * L * per_th + B * H * d * d * 4
     C = api.la_delta_chunk(desc)
@@ -506,6 +519,7 @@ def bench_delta(args, torch, api, workloads):
     step_bytes = 2 * w.B * w.H * w.dk * w.dv * 4 + w.B * w.H * (4 * w.dk * 2 + 4)
     return {
         "prefill": {"workload": workloads.DELTA_HEADLINE, "ms_per_step": round(ms, 4),
+                    "step_ms": step_times(ptimes),
                     "tokens_per_s": round(B * L / (ms * 1e-3), 1), "kernel_avg_us": round(kus, 2),
                     "algorithmic_bytes": alg, "tflops": round(flops / (kus * 1e-6) / 1e12, 2),
                     "roofline": {"bound": "hbm", "achieved": round(alg / (kus * 1e-6) / 1e9, 1),
@@ -630,6 +644,8 @@ def main(argv=None):
     ap.add_argument("--segments", type=int, default=0,
                     help="segments per (b,h) for --only varlen (0 = automatic)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-flush", action="store_true",
+                    help="time prefill-like steps without the cache flush before each")
     ap.add_argument("--only", choices=["prefill", "decode", "backward", "varlen", "scalar", "retention", "delta",
                              "copy"], default=None,
                     help="run one part only (copy: a 1 GiB device copy used to scale "
@@ -695,6 +711,7 @@ def main(argv=None):
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(pre["ms_step"], 4),
+        "step_ms": pre["times"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -724,6 +741,7 @@ def main(argv=None):
     if sc is not None:
         line["scalar_gate"] = {
             "workload": sc["w"].name, "ms_per_step": round(sc["ms_step"], 4),
+            "step_ms": sc["times"],
             "tokens_per_s": round(sc["tokens_per_s"], 1),
             "pct_of_bf16_mfma_peak": round(sc["mfma_pct"], 3),
             "kernels_avg_us": {k: (round(v["avg_us"], 2) if v["avg_us"] else None)
