@@ -256,6 +256,10 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
     // the aggregate pass skips the segment it would end with (the last one,
     // or the first one when reversed)
     constexpr bool AGG = SONLY && !STORE;
+    // cache policy of the q, k, v and gate loads: non-temporal streams in
+    // the aggregate and main passes; the default in the passes that store
+    // every boundary state, whose inputs the gradient kernel reads next
+    constexpr int LAUX = STORE ? 0 : LOAD_NT;
     // the forward aggregate pass walks its segment from the last chunk to
     // the first (see cof below)
     constexpr bool BACKAGG = AGG && !REV;
@@ -399,23 +403,24 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
         const uint32_t oaa = ((t0 + ktg * KTPG) * DK + CW * kcp) * 4;
 #pragma unroll
         for (int j = 0; j < KTPG; ++j) {
-            rg.k[j] = buf_load_words<Cfg::KWORDS>(rk, okk + j * DK * ES);
-            if constexpr (GATE == LA_GATE_DIAG) rg.la[j] = buf_load_words<CW>(rla, oaa + j * DK * 4);
+            rg.k[j] = buf_load_words<Cfg::KWORDS, LAUX>(rk, okk + j * DK * ES);
+            if constexpr (GATE == LA_GATE_DIAG) rg.la[j] = buf_load_words<CW, LAUX>(rla, oaa + j * DK * 4);
             if constexpr (GATE == LA_GATE_SCALAR) {
                 // one gate per token, the same for every channel of the run
-                const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(rla, (t0 + ktg * KTPG + j) * 4, 0, 0);
+                const uint32_t w =
+                    __builtin_amdgcn_raw_buffer_load_b32(rla, (t0 + ktg * KTPG + j) * 4, 0, LAUX);
 #pragma unroll
                 for (int i = 0; i < CW; ++i) rg.la[j].w[i] = w;
             }
         }
 #pragma unroll
-        for (int j = 0; j < VTPG; ++j) rg.v[j] = buf_load_words<Cfg::VWORDS>(rv, ovv + j * DV * ES);
+        for (int j = 0; j < VTPG; ++j) rg.v[j] = buf_load_words<Cfg::VWORDS, LAUX>(rv, ovv + j * DV * ES);
     };
     auto load_q = [&](int c) {
         if constexpr (!SONLY) {
             const uint32_t okk = (((uint32_t)c * C + ktg * KTPG) * DK + CW * kcp) * ES;
 #pragma unroll
-            for (int j = 0; j < KTPG; ++j) qreg[j] = buf_load_words<Cfg::KWORDS>(rq, okk + j * DK * ES);
+            for (int j = 0; j < KTPG; ++j) qreg[j] = buf_load_words<Cfg::KWORDS, LAUX>(rq, okk + j * DK * ES);
         }
     };
     // the gate runs of chunk c's outputs (loaded after the previous chunk's

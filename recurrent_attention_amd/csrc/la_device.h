@@ -171,17 +171,21 @@ __device__ __forceinline__ float lane_read(float x, int src) {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
-template <int N>
+// AUX is the cache policy of the load: 0 by default, LOAD_NT (the nt,
+// non-temporal bit) for streams read once.
+constexpr int LOAD_NT = 2;
+template <int N, int AUX = 0>
 __device__ __forceinline__ Words<N> buf_load_words(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     if constexpr (N == 1) {
-        return Words<1>{{__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0)}};
+        return Words<1>{{__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, AUX)}};
     } else if constexpr (N == 2) {
-        return __builtin_bit_cast(Words<2>, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+        return __builtin_bit_cast(Words<2>, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, AUX));
     } else {
         static_assert(N == 4, "runs are 4, 8 or 16 bytes");
-        return __builtin_bit_cast(Words<4>, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+        return __builtin_bit_cast(Words<4>, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, AUX));
     }
 }
+
 
 // A run of 4 channels of one token (fp32 values) written to global memory as
 // the element type through a buffer descriptor.
