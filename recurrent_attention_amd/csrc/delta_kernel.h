@@ -129,7 +129,8 @@ __global__ __launch_bounds__(Cfg::NT) void delta_chunk_kernel(const DeltaParams 
             accS[mb][i] = S0 ? S0[(size_t)(16 * mb + 4 * g + i) * D + n0 + r] : 0.f;
 
     // global -> registers, one chunk ahead: a 4-channel run of q, k, v for
-    // NPASS token rows, and one write strength
+    // NPASS token rows, and one write strength (non-temporal loads: each
+    // element is read once)
     const int run = tid % RUNS, row0 = tid / RUNS;
     Words<RW> qr[NPASS], kr[NPASS], vr[NPASS];
     uint32_t br = 0;
@@ -137,11 +138,11 @@ __global__ __launch_bounds__(Cfg::NT) void delta_chunk_kernel(const DeltaParams 
 #pragma unroll
         for (int ps = 0; ps < NPASS; ++ps) {
             const uint32_t off = (((uint32_t)c * C + row0 + RPP * ps) * D + 4 * run) * ES;
-            qr[ps] = buf_load_words<RW>(rq, off);
-            kr[ps] = buf_load_words<RW>(rk, off);
-            vr[ps] = buf_load_words<RW>(rv, off);
+            qr[ps] = buf_load_words<RW, LOAD_NT>(rq, off);
+            kr[ps] = buf_load_words<RW, LOAD_NT>(rk, off);
+            vr[ps] = buf_load_words<RW, LOAD_NT>(rv, off);
         }
-        if (tid < C) br = __builtin_amdgcn_raw_buffer_load_b32(rb, ((uint32_t)c * C + tid) * 4, 0, 0);
+        if (tid < C) br = __builtin_amdgcn_raw_buffer_load_b32(rb, ((uint32_t)c * C + tid) * 4, 0, LOAD_NT);
     };
     if (nchunks > 0) load(0);
 
