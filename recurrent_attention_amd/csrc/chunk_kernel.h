@@ -487,27 +487,37 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
 #pragma unroll
         for (int i = 0; i < CW; ++i) gexc[i] = gmid[i] = 0.f;
         if constexpr (VG) {
+            // a scalar gate is the same in every channel: its sums are formed
+            // once (channel 0) and repeated, so that everything computed from
+            // them below is one value per token
+            constexpr int GC = GATE == LA_GATE_SCALAR ? 1 : CW;
             float gsum[CW], incl[CW], wsum[CW];
 #pragma unroll
-            for (int i = 0; i < CW; ++i) gsum[i] = 0.f;
+            for (int i = 0; i < GC; ++i) gsum[i] = 0.f;
 #pragma unroll
             for (int j = 0; j < KTPG; ++j)
 #pragma unroll
-                for (int i = 0; i < CW; ++i) gsum[i] += run_elem<false>(rg.la[j], i) * kLog2e;
+                for (int i = 0; i < GC; ++i) gsum[i] += run_elem<false>(rg.la[j], i) * kLog2e;
 #pragma unroll
-            for (int i = 0; i < CW; ++i) incl[i] = gsum[i];
+            for (int i = 0; i < GC; ++i) incl[i] = gsum[i];
 #pragma unroll
             for (int sft = KCP; sft < 64; sft *= 2)
 #pragma unroll
-                for (int i = 0; i < CW; ++i) {
+                for (int i = 0; i < GC; ++i) {
                     const float y = lane_read(incl[i], lane - sft);
                     if (lane >= sft) incl[i] += y;
                 }
 #pragma unroll
-            for (int i = 0; i < CW; ++i) {
+            for (int i = 0; i < GC; ++i) {
                 gexc[i] = incl[i] - gsum[i];
                 wsum[i] = KCP < 64 ? lane_read(incl[i], 64 - KCP + lane % KCP) : incl[i];
                 if constexpr (NW == 1) gmid[i] = lane_read(incl[i], (KTG / 2 - 1) * KCP + lane % KCP);
+            }
+#pragma unroll
+            for (int i = GC; i < CW; ++i) {
+                gexc[i] = gexc[0];
+                wsum[i] = wsum[0];
+                gmid[i] = gmid[0];
             }
             __syncthreads();  // the previous chunk is done with every LDS tile
             if (lane < KCP) lds_store_words<CW>(&sm.tot[wave][CW * kcp], pack_run<false, CW>(wsum));
@@ -527,7 +537,10 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
 #pragma unroll
             for (int w2 = 0; w2 < NW; ++w2) {
                 const float* tv = &sm.tot[w2][CW * kcp];
-                if constexpr (CW == 4) {
+                if constexpr (GATE == LA_GATE_SCALAR) {
+#pragma unroll
+                    for (int i = 0; i < CW; ++i) x[w2][i] = tv[0];
+                } else if constexpr (CW == 4) {
                     const float4 v4 = *reinterpret_cast<const float4*>(tv);
                     x[w2][0] = v4.x; x[w2][1] = v4.y; x[w2][2] = v4.z; x[w2][3] = v4.w;
                 } else {
@@ -580,13 +593,27 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
                 float ftok = 1.f;
                 if constexpr (GATE == LA_GATE_GAMMA)
                     ftok = ok ? sm.gpow[REV ? t + 1 : clen - 1 - t] * (BACKAGG ? egam : 1.f) : 0.f;
+                // scalar gate: the token's factors, once for all its channels
+                float sq = 1.f, sk = 1.f, st = 1.f;
+                if constexpr (GATE == LA_GATE_SCALAR) {
+                    bcur[0] += run_elem<false>(rg.la[j], 0) * kLog2e;
+                    const float d = bcur[0] - gref[0];
+                    sq = __builtin_amdgcn_exp2f(d);
+                    sk = __builtin_amdgcn_exp2f(-d);
+                    st = REV ? sq : sk;
+                    if constexpr (BACKAGG) st = __builtin_amdgcn_exp2f(gtot[0] - bcur[0] + eacc[0]);
+                }
 #pragma unroll
                 for (int i = 0; i < CW; ++i) {
                     float ka = run_elem<BF16>(rg.k[j], i);
                     if constexpr (ELU1) ka = elu1f(ka);
                     ka = ok ? ka : 0.f;
                     float fq = 1.f, fk = 1.f, ft = ftok;
-                    if constexpr (VG) {
+                    if constexpr (GATE == LA_GATE_SCALAR) {
+                        fq = sq;
+                        fk = sk;
+                        ft = st;
+                    } else if constexpr (VG) {
                         bcur[i] += run_elem<false>(rg.la[j], i) * kLog2e;
                         const float d = bcur[i] - gref[i];
                         fq = __builtin_amdgcn_exp2f(d);
