@@ -22,13 +22,15 @@ import re
 import sys
 from collections import defaultdict
 
-# chunk_kernel<ChunkCfg<dk, dv, C, bf16, gate, state-only, waves>, elu1, reversed, store>
-_CHUNK = r"la::chunk_kernel<la::ChunkCfg<\d+, \d+, \d+, \w+, \d, {so}(, \d+)?>, \w+{tail}"
-# (chunk_main also matches the group-norm epilogue variant: <..., false, false, true>)
+# chunk_kernel<ChunkCfg<dk, dv, C, bf16, gate, state-only, waves>, elu1, reversed, store, epilogue>
+_CHUNK = (r"la::chunk_kernel<la::ChunkCfg<\d+, \d+, \d+, \w+, \d, {so}, \d+>, "
+          r"\w+, \w+, {store}, \w+>")
+# chunk_main: every pass with outputs (the group-norm epilogue and the
+# training forward that also stores its boundary states included)
 FAMILIES = [
-    ("chunk_main", re.compile(_CHUNK.format(so="false", tail=""))),
-    ("chunk_store", re.compile(_CHUNK.format(so="true", tail=r", \w+, true>"))),
-    ("chunk_state", re.compile(_CHUNK.format(so="true", tail=r"(, \w+, false)?>"))),
+    ("chunk_main", re.compile(_CHUNK.format(so="false", store=r"\w+"))),
+    ("chunk_store", re.compile(_CHUNK.format(so="true", store="true"))),
+    ("chunk_state", re.compile(_CHUNK.format(so="true", store="false"))),
     ("state_scan", re.compile(r"la::state_scan_kernel")),
     ("chunk_bwd", re.compile(r"la::bwd_kernel")),
     ("delta_chunk", re.compile(r"la::delta_chunk_kernel")),
