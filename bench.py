@@ -178,8 +178,11 @@ def kernel_avgs(torch, api, step, args, flush, names):
 
 
 def step_times(t):
-    return {"median": round(t["median"], 4), "min": round(t["min"], 4),
-            "back_to_back": round(t["back_to_back"], 4)}
+    out = {"median": round(t["median"], 4), "min": round(t["min"], 4),
+           "back_to_back": round(t["back_to_back"], 4)}
+    if "graph" in t:
+        out["graph_replay"] = round(t["graph"], 4)
+    return out
 
 
 def prefill_bytes(w):
@@ -226,6 +229,21 @@ def bench_prefill(args, torch, api, workloads, name=None):
     kern = {name: {"avg_us": us} for name, us in
             kernel_avgs(torch, api, step, args, flush,
                         ("chunk_main", "chunk_state", "state_scan")).items()}
+    # the same step's launches captured once in a HIP graph and replayed
+    # (what a caller that captures its step gets): same protocol, and the
+    # replayed output must equal the direct call's bit for bit
+    ref = out.clone()
+    side = torch.cuda.Stream(dev)
+    gargv = argv[:-1] + (ctypes.c_void_p(side.cuda_stream),)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=side):
+        if lib.la_chunk_fwd(*gargv) != 0:
+            raise RuntimeError(api.la_last_error_message())
+    gtimes = time_steps(torch, graph.replay, args, flush)
+    torch.cuda.synchronize()
+    if not torch.equal(out, ref):
+        raise RuntimeError("graph replay differs from the direct call")
+    times["graph"] = gtimes["mean"]
 
     ms_step = times["mean"]
     tokens = w.B * w.L
