@@ -40,7 +40,7 @@
  *    to a ragged last chunk as in linear_attn_chunkwise of
  *    "linear_sparse_attention.py".  All decays are direct products.
  *
- * Readings taken where the pages are silent (each is listed in the design doc):
+ * Readings taken where the pages are silent:
  *  - under a gate, z follows the same gate as S (z is S for an all-ones
  *    value column);
  *  - no epsilon in the divide;
