@@ -159,7 +159,6 @@ __global__ __launch_bounds__(Cfg::NT) void delta_chunk_kernel(const DeltaParams 
         }
         if (tid < C) sm.beta[tid] = __uint_as_float(br);
         __syncthreads();
-        if (c + 1 < nchunks) load(c + 1);
 
         // ---- A = strict_lower(diag(beta) K K^T), computed transposed ([s][t]
         // tiles) so each lane holds 4 consecutive s of one t
@@ -291,6 +290,10 @@ __global__ __launch_bounds__(Cfg::NT) void delta_chunk_kernel(const DeltaParams 
                 __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             }
         }
+        // the next chunk's loads: issued here, where the waves without a block
+        // column would otherwise wait for the off-diagonal chain (the
+        // registers were emptied into this chunk's tiles)
+        if (c + 1 < nchunks) load(c + 1);
         __syncthreads();
 
         // ---- W^T = K^T T^T: wave w takes key channels [16w, 16w+16)
