@@ -682,9 +682,16 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
             }
         }
 
-        // ---- refill the registers: q with chunk c + 1, this set with c + PD
-        if (ci + 1 < c_end) load_q(cof(ci + 1));
-        if (ci + Cfg::PD < c_end) load_chunk(cof(ci + Cfg::PD), rg);
+        // ---- refill the registers: q with chunk c + 1, this set with c + PD.
+        // The waves with fewer op1 tiles issue theirs after their tiles,
+        // where they would otherwise wait for the others
+        constexpr int NTILE = TB * (TB + 1) / 2;
+        const bool late = !SONLY && NTILE % NW != 0 && wave_u >= NTILE % NW;
+        auto refill = [&]() {
+            if (ci + 1 < c_end) load_q(cof(ci + 1));
+            if (ci + Cfg::PD < c_end) load_chunk(cof(ci + Cfg::PD), rg);
+        };
+        if (!late) refill();
         __syncthreads();
 
         // ---- op1: P^T = Kh Qh^T on the lower-triangular tiles; each lane
@@ -717,6 +724,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
                     store_run<BF16, 4>(&sm.p[rt][p_pos<Cfg>(rt, 16 * sb + 4 * g)], x);
                 }
             }
+            if (late) refill();
             __syncthreads();
 
             // ---- a4: normaliser of each row, read with the state before this chunk
