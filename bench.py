@@ -273,13 +273,14 @@ def backward_bytes(w):
     return w.B * w.H * w.L * per_th + w.B * w.H * w.dk * w.dv * 4
 
 
-def backward_kernel_bytes(w, chunk):
-    """Bytes the per-chunk gradient kernel must move as designed: the token
-    tensors of the backward plus, per chunk, the state before it and the
-    state gradient after it, in bf16."""
+def backward_kernel_bytes(w, chunk, segments):
+    """Bytes the gradient kernel must move as designed: the token tensors of
+    the backward and dS0, the state before every chunk in bf16, and, with
+    several segments per (b,h), the fp32 state gradient entering each."""
     nchunks = -(-w.L // chunk)
-    return backward_bytes(w) - w.B * w.H * w.dk * w.dv * 4 + \
-        w.B * w.H * nchunks * 2 * w.dk * w.dv * 2
+    bh = w.B * w.H
+    return backward_bytes(w) + bh * nchunks * w.dk * w.dv * 2 + \
+        (bh * segments * w.dk * w.dv * 4 if segments > 1 else 0)
 
 
 def bench_backward(args, torch, api, workloads):
@@ -333,7 +334,7 @@ def bench_backward(args, torch, api, workloads):
         torch, api, step, args, flush, ("chunk_state", "state_scan", "chunk_store", "chunk_bwd")).items()}
     ms_step = times["mean"]
     bw_us = kern["chunk_bwd"]
-    kb = backward_kernel_bytes(w, chunk)
+    kb = backward_kernel_bytes(w, chunk, api.la_chunk_fwd_segments(desc, chunk))
     achieved = kb / (bw_us * 1e-6) / 1e9
     alg = backward_bytes(w)
     return {

@@ -277,10 +277,9 @@ la_status la_chunk_fwd_train(const la_desc* d, const void* q, const void* k,
 /* Bytes of the boundary states la_chunk_fwd_train writes (0 if invalid). */
 size_t la_chunk_train_states_bytes(const la_desc* d);
 
-/* Bytes of device workspace la_chunk_bwd needs: states at every chunk
- * boundary in the element type of q/k/v (B*H*(2*ceil(L/C)+1)*dk*dv
- * elements: the state before each chunk and the final state, the state
- * gradient after each chunk) plus the fp32 segment slots.
+/* Bytes of device workspace la_chunk_bwd needs: the state before each
+ * chunk and the final state in the element type of q/k/v
+ * (B*H*(ceil(L/C)+1)*dk*dv elements) plus the fp32 segment slots.
  * Returns 0 for an invalid descriptor. */
 size_t la_chunk_bwd_workspace_bytes(const la_desc* d);
 

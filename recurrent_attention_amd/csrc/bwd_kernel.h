@@ -1,8 +1,8 @@
-// bwd_kernel.h -- gradients of one chunk of the unified recurrence on gfx950
-// matrix cores, given the state at the chunk's start and the gradient of the
-// state at its end.
+// bwd_kernel.h -- gradients of the unified recurrence on gfx950 matrix
+// cores: one workgroup walks a (b,h) segment of chunks from its last chunk
+// to its first, carrying the gradient of the state through the walk.
 //
-// With S = the state before the chunk, G = the gradient of the state after
+// With S = the state before a chunk, G = the gradient of the state after
 // it, chunk-local t, s, b_t = sum_{r<=t} log a_r (per key channel, natural
 // log) and B = b at the chunk's last token, the forward chunk ("Module 22:
 // Linear & Recurrent Attention", "The Three Faces of Retention", with the
@@ -13,6 +13,7 @@
 //   dk_s = e^{B - b_s} * (G v_s) + sum_{t>=s} (do_t . v_s) q_t * e^{b_t - b_s}
 //   dv_s = G^T (k_s * e^{B - b_s}) + sum_{t>=s} P[t][s] do_t
 //   d log a_t = sum_{u>=t} (q_u * dq_u - k_u * dk_u)      (features q, k)
+//   G_prev = e^{B} * G + sum_t (q_t * e^{b_t}) do_t^T     (the chunk before)
 // where P[t][s] is the forward score with its decay.  The suffix sum that
 // reaches into later chunks, sum over all tokens after this chunk, equals
 // rowsum(G * S_next) with S_next the state after this chunk, so each chunk
@@ -23,19 +24,23 @@
 // and G v_s is the first term of dk_s, already in the accumulators.
 //
 // Matrix-core mapping (C tokens, D = d_k = d_v; wave w owns channel block
-// [16w, 16w+16) of dq, dk and of dv):
+// [16w, 16w+16) of dq, dk and of dv, and rows [16w, 16w+16) of G):
 //   P   = Qh Kh^T and dP = dO V^T on the lower-triangular 16x16 tiles
 //         (Qh = q e^{b - r}, Kh = k e^{r - b}, r = b at the chunk middle),
 //         stored transposed, [s][t], with the causal mask (and gamma^(t-s));
 //   dQ^T = e^{r} S dO^T + Kh^T dP^T,   then * e^{b - r}
 //   dK^T = Gs V^T + Qh^T dP,           then * e^{r - b}
 //   dV^T = Gs^T Kh^T + dO^T P
-// with Gs = diag(e^{B - r}) G held in LDS (row-major; its transpose is read
-// from the same tile).  S comes from memory in the element type.  Every
-// output lane holds 4 consecutive channels of one token, which are the same
-// elements the thread loaded and whose decay factors it computed.  Operands
-// with the token index (or G's row index) as the contraction are read from
-// row-major LDS tiles with the transposing LDS read of gfx950
+//   G_prev = e^{r} (Gs + Qh^T dO), formed as its transpose dO^T Qh
+// with Gs = diag(e^{B - r}) G.  G stays in LDS in fp32 for the whole walk
+// (row-major, 16-byte units swizzled by the row), is scaled to Gs in place
+// once the chunk's gate factors are known, and is rounded to the element
+// type where it is an operand.  S comes from memory in the element type.  Every output lane of the
+// gradient products holds 4 consecutive channels of one token, which are
+// the same elements the thread loaded and whose decay factors it computed;
+// every output lane of the G step holds 4 consecutive columns of one row of
+// G.  Operands with the token index (or G's row index) as the contraction
+// are read from row-major LDS tiles with the transposing LDS read of gfx950
 // (ds_read_b64_tr_b16).
 #pragma once
 
@@ -74,9 +79,10 @@ struct BwdSmem {
     alignas(16) E vv[Cfg::C][Cfg::D];     // V    [s][swizzled n]
     alignas(16) E pt[Cfg::C][Cfg::C];     // P^T  [s][swizzled t]
     alignas(16) E dpt[Cfg::C][Cfg::C];    // dP^T [s][swizzled t]
-    alignas(16) E gs[Cfg::D][Cfg::D];     // Gs   [i][swizzled n]
+    alignas(16) float gm[Cfg::D * Cfg::D];  // G, fp32 [i][swizzled n]
     float red[Cfg::NW][Cfg::C];           // per-wave token sums (scalar gate)
     alignas(16) float ebr[Cfg::D];        // e^{B - r} per channel (DIAG)
+    alignas(16) float er[Cfg::D];         // e^{r} per channel (DIAG)
     float gpow[Cfg::C + 2];               // gamma^j
 };
 
@@ -89,10 +95,41 @@ __device__ __forceinline__ typename Cfg::Frag mem_frag(const typename Cfg::E* M,
     const int col = k0 + Cfg::KPL * (lane >> 4);
     return Cfg::T::load(M + (size_t)row * ld + col);
 }
+// Position of (row, col) in the fp32 G tile: row-major, 16-byte units
+// XOR-swizzled by (row ^ row / 16), so that 16 consecutive rows, and rows
+// 16 apart, fall on different banks.
+template <int D>
+__device__ __forceinline__ int g_pos(int row, int col) {
+    constexpr int U = D / 4;
+    constexpr int M = (U < 16 ? U : 16) - 1;
+    return row * D + ((((col >> 2) ^ ((row ^ (row >> 4)) & M)) << 2) | (col & 3));
+}
+
+// The KPL k-slots of G's row `row` from column `col` on, as floats.
+template <class Cfg>
+__device__ __forceinline__ void g_row(const float* gm, int row, int col, float* x) {
+    constexpr int D = Cfg::D;
+    if constexpr (Cfg::BF16) {
+        const float4 a = *reinterpret_cast<const float4*>(gm + g_pos<D>(row, col));
+        const float4 b = *reinterpret_cast<const float4*>(gm + g_pos<D>(row, col + 4));
+        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+        x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    } else {
+        x[0] = gm[g_pos<D>(row, col)];
+    }
+}
+
+// KPL floats -> one operand in the element type.
+template <class Cfg>
+__device__ __forceinline__ typename Cfg::Frag to_frag(const float* x) {
+    if constexpr (Cfg::BF16) return Cfg::T::from8(x);
+    else return x[0];
+}
+
 template <class Cfg, bool ELU1>
 __global__ __launch_bounds__(Cfg::NT) void bwd_kernel(const BwdParams p) {
     constexpr int D = Cfg::D, C = Cfg::C, GATE = Cfg::GATE, TB = Cfg::TB, NW = Cfg::NW;
-    constexpr int MK = Cfg::MK, RW = Cfg::RW, KPL = Cfg::KPL, UE = Cfg::UE, DU = Cfg::DU;
+    constexpr int MK = Cfg::MK, RW = Cfg::RW, KPL = Cfg::KPL;
     constexpr bool BF16 = Cfg::BF16;
     constexpr int ES = (int)sizeof(typename Cfg::E);
     constexpr int DM = Cfg::DMASK, TM = Cfg::TMASK;
@@ -102,22 +139,21 @@ __global__ __launch_bounds__(Cfg::NT) void bwd_kernel(const BwdParams p) {
     constexpr float kLog2e = 1.4426950408889634f;
     // the diagonal and the per-token scalar gate share one path
     constexpr bool VG = GATE == LA_GATE_DIAG || GATE == LA_GATE_SCALAR;
-    // 16-byte units of G each thread copies into LDS
-    constexpr int GU = D * D / UE / Cfg::NT;
-    static_assert(GU * UE * Cfg::NT == D * D, "G copy mapping");
+    // float4 units of G each thread copies in (and out, for dS0)
+    constexpr int GQ = D * D / 4 / Cfg::NT;
+    static_assert(GQ * 4 * Cfg::NT == D * D, "G copy mapping");
 
     __shared__ BwdSmem<Cfg> sm;
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int r = lane & 15, g = lane >> 4;
-    const int c = blockIdx.x % p.nchunks;
-    const int bh = blockIdx.x / p.nchunks;
+    const int wave = tid >> 6;
+    const int seg = blockIdx.x % p.P;
+    const int bh = blockIdx.x / p.P;
     const int h = bh % p.H;
     const int L = p.L;
-    const int t0 = c * C;
-    const int clen = min(C, L - t0);
-    const int ch0 = 16 * wave + 4 * g;    // this thread's 4 channels (keys and values)
+    const int c_begin = seg * p.cps;
+    const int c_end = min(p.nchunks, c_begin + p.cps);
+    const int nb = wave;                  // channel block of this wave
 
     const size_t rows0 = (size_t)bh * L;
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(reinterpret_cast<const E*>(p.q) + rows0 * D, (uint32_t)L * D * ES);
@@ -137,35 +173,14 @@ __global__ __launch_bounds__(Cfg::NT) void bwd_kernel(const BwdParams p) {
                   : GATE == LA_GATE_SCALAR ? (void*)(p.dlog_alpha + rows0) : p.dq,
                   GATE == LA_GATE_DIAG ? (uint32_t)L * D * 4
                   : GATE == LA_GATE_SCALAR ? (uint32_t)L * 4 : 0u);
-    const E* Sc = reinterpret_cast<const E*>(p.st_fwd) + ((size_t)bh * (p.nchunks + 1) + c) * D * D;
-    const E* Gc = reinterpret_cast<const E*>(p.st_rows) + ((size_t)bh * p.nchunks + c) * D * D;
+    const E* Sbh = reinterpret_cast<const E*>(p.st_fwd) + (size_t)bh * (p.nchunks + 1) * D * D;
 
-    // ---- loads: per owned token, one 4-channel run of q, k, v, dO (and
-    // gates); the state gradient G in 16-byte units
-    Words<RW> qr[TB], kr[TB], vr[TB], dr[TB];
-    Words<4> lar[VG ? TB : 1];
-    uint4 gw[GU];
-#pragma unroll
-    for (int tb = 0; tb < TB; ++tb) {
-        const uint32_t row = (uint32_t)(t0 + 16 * tb + r);
-        const uint32_t off = (row * D + ch0) * ES;
-        qr[tb] = buf_load_words<RW>(rq, off);
-        kr[tb] = buf_load_words<RW>(rk, off);
-        vr[tb] = buf_load_words<RW>(rv, off);
-        dr[tb] = buf_load_words<RW>(rdo, off);
-        if constexpr (GATE == LA_GATE_DIAG) lar[tb] = buf_load_words<4>(rla, (row * D + ch0) * 4);
-        if constexpr (GATE == LA_GATE_SCALAR) {
-            const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(rla, row * 4, 0, 0);
-            lar[tb] = Words<4>{{w, w, w, w}};
-        }
-    }
-#pragma unroll
-    for (int j = 0; j < GU; ++j) gw[j] = reinterpret_cast<const uint4*>(Gc)[tid + j * Cfg::NT];
     if constexpr (GATE == LA_GATE_GAMMA) {
         const float l2g = p.log2_gamma[h];
         for (int j = tid; j < C + 2; j += Cfg::NT) sm.gpow[j] = j == 0 ? 1.0f : exp2f((float)j * l2g);
     }
-    // zero the score tiles (their upper triangles are read as zeros)
+    // zero the score tiles: only their lower-triangular 16x16 tiles are
+    // ever written, and the rest is read as zeros
     {
         E* z0 = &sm.pt[0][0];
         E* z1 = &sm.dpt[0][0];
@@ -174,316 +189,426 @@ __global__ __launch_bounds__(Cfg::NT) void bwd_kernel(const BwdParams p) {
             z1[i] = E(0);
         }
     }
-
-    // ---- features, gate prefix and factors of the owned elements
-    float qf[TB][4], kf[TB][4], fq[TB][4], fk[TB][4];
-    float er[4], ebr[4];   // e^{r}, e^{B - r} of the owned channels (DIAG)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) er[i] = ebr[i] = 1.f;
-#pragma unroll
-    for (int tb = 0; tb < TB; ++tb) {
-        const bool ok = 16 * tb + r < clen;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            float qa = run_elem<BF16>(qr[tb], i), ka = run_elem<BF16>(kr[tb], i);
-            if constexpr (ELU1) {
-                qa = elu1f(qa);
-                ka = elu1f(ka);
-            }
-            qf[tb][i] = ok ? qa : 0.f;
-            kf[tb][i] = ok ? ka : 0.f;
-            fq[tb][i] = fk[tb][i] = 1.f;
-        }
-    }
-    if constexpr (VG) {
-        // inclusive prefix over the chunk's tokens: within each 16-token block
-        // across the lanes of a row, then the earlier blocks' totals
-        float b[TB][4];
-        float carry[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int tb = 0; tb < TB; ++tb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float x = row_scan16<false>(run_elem<false>(lar[tb], i) * kLog2e);
-                b[tb][i] = x + carry[i];
-                carry[i] += lane_read(x, 16 * g + 15);
-            }
-        constexpr int tmid = C / 2 - 1;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float ref = lane_read(b[tmid / 16][i], 16 * g + tmid % 16);
-            const float tot = carry[i];
-            er[i] = __builtin_amdgcn_exp2f(ref);
-            ebr[i] = __builtin_amdgcn_exp2f(tot - ref);
-#pragma unroll
-            for (int tb = 0; tb < TB; ++tb) {
-                const float d = b[tb][i] - ref;
-                fq[tb][i] = __builtin_amdgcn_exp2f(d);
-                fk[tb][i] = __builtin_amdgcn_exp2f(-d);
-            }
-        }
-        if (r == 0)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sm.ebr[ch0 + i] = ebr[i];
-    }
-
-    // ---- tiles: Qh, Kh, dO, V row-major (one 4-channel run per token)
-#pragma unroll
-    for (int tb = 0; tb < TB; ++tb) {
-        const int t = 16 * tb + r;
-        float x[4], y[4], vo[4], dd[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            x[i] = qf[tb][i] * fq[tb][i];
-            y[i] = kf[tb][i] * fk[tb][i];
-            vo[i] = run_elem<BF16>(vr[tb], i);
-            dd[i] = run_elem<BF16>(dr[tb], i);
-        }
-        const int pos = bw_pos<Cfg, DM>(t, ch0);
-        lds_store_words(&sm.qh[t][pos], pack_run<BF16, 4>(x));
-        lds_store_words(&sm.kh[t][pos], pack_run<BF16, 4>(y));
-        lds_store_words(&sm.vv[t][pos], pack_run<BF16, 4>(vo));
-        lds_store_words(&sm.dout[t][pos], pack_run<BF16, 4>(dd));
-    }
-    __syncthreads();
-
-    // ---- Gs = diag(e^{B - r}) G into LDS (the factor table is visible now)
-#pragma unroll
-    for (int j = 0; j < GU; ++j) {
-        const int u = tid + j * Cfg::NT;
-        const int row = u / DU, col = (u % DU) * UE;
-        uint4 w = gw[j];
-        if constexpr (VG) {
-            const float f = sm.ebr[row];
-            if constexpr (BF16) {
-                w.x = pack_bf16(bf16lo(w.x) * f, bf16hi(w.x) * f);
-                w.y = pack_bf16(bf16lo(w.y) * f, bf16hi(w.y) * f);
-                w.z = pack_bf16(bf16lo(w.z) * f, bf16hi(w.z) * f);
-                w.w = pack_bf16(bf16lo(w.w) * f, bf16hi(w.w) * f);
-            } else {
-                w.x = __float_as_uint(__uint_as_float(w.x) * f);
-                w.y = __float_as_uint(__uint_as_float(w.y) * f);
-                w.z = __float_as_uint(__uint_as_float(w.z) * f);
-                w.w = __float_as_uint(__uint_as_float(w.w) * f);
-            }
-        }
-        *reinterpret_cast<uint4*>(&sm.gs[row][bw_pos<Cfg, DM>(row, col)]) = w;
-    }
-
-    // ---- P and dP on the lower-triangular tiles, stored transposed [s][t]:
-    // the output lane holds four consecutive t of one s
+    // G after the segment's last chunk (zeros without one); visible after
+    // the first chunk's tile barrier
     {
-        int idx = 0;
+        const float4* gin = p.g_entry
+            ? reinterpret_cast<const float4*>(p.g_entry + ((size_t)bh * p.P + seg) * D * D) : nullptr;
 #pragma unroll
-        for (int tb = 0; tb < TB; ++tb)
-#pragma unroll
-            for (int sb = 0; sb <= tb; ++sb, ++idx) {
-                if (idx % NW != wave) continue;
-                f32x4_t ap = {0.f, 0.f, 0.f, 0.f}, ad = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kk = 0; kk < D / MK; ++kk) {
-                    ap = T::mma(row_frag<Cfg, DM>(&sm.qh[0][0], D, 16 * tb, kk * MK, lane),
-                                row_frag<Cfg, DM>(&sm.kh[0][0], D, 16 * sb, kk * MK, lane), ap);
-                    ad = T::mma(row_frag<Cfg, DM>(&sm.dout[0][0], D, 16 * tb, kk * MK, lane),
-                                row_frag<Cfg, DM>(&sm.vv[0][0], D, 16 * sb, kk * MK, lane), ad);
-                }
-                const int s = 16 * sb + r;
-                float xp[4], xd[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int t = 16 * tb + 4 * g + i;
-                    float m = t >= s ? 1.f : 0.f;
-                    if constexpr (GATE == LA_GATE_GAMMA) m = t >= s ? sm.gpow[t - s] : 0.f;
-                    xp[i] = ap[i] * m;
-                    xd[i] = ad[i] * m;
-                }
-                store_run<BF16, 4>(&sm.pt[s][bw_pos<Cfg, TM>(s, 16 * tb + 4 * g)], xp);
-                store_run<BF16, 4>(&sm.dpt[s][bw_pos<Cfg, TM>(s, 16 * tb + 4 * g)], xd);
-            }
-    }
-    __syncthreads();
-
-    const int nb = wave;   // channel block of this wave
-
-    // ---- dQ^T = e^{r} S dO^T + Kh^T dP^T, then * e^{b - r}; with the
-    // partial rowsum(Gs * S) of row 16 nb + r (diagonal gate)
-    float dqf[TB][4];
-    float gss = 0.f;
-    {
-        f32x4_t acc[TB];
-#pragma unroll
-        for (int tb = 0; tb < TB; ++tb) acc[tb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < D / MK; ++kk) {
-            const Frag a = mem_frag<Cfg>(Sc, D, 16 * nb, kk * MK, lane);
-            if constexpr (VG) {
-                float xs[KPL], xg[KPL];
-                frag_floats<Cfg>(a, xs);
-                frag_floats<Cfg>(row_frag<Cfg, DM>(&sm.gs[0][0], D, 16 * nb, kk * MK, lane), xg);
-#pragma unroll
-                for (int j = 0; j < KPL; ++j) gss += xs[j] * xg[j];
-            }
-#pragma unroll
-            for (int tb = 0; tb < TB; ++tb)
-                acc[tb] = T::mma(a, row_frag<Cfg, DM>(&sm.dout[0][0], D, 16 * tb, kk * MK, lane), acc[tb]);
+        for (int j = 0; j < GQ; ++j) {
+            const int u = tid + j * Cfg::NT;
+            const float4 x = gin ? gin[u] : make_float4(0.f, 0.f, 0.f, 0.f);
+            *reinterpret_cast<float4*>(&sm.gm[g_pos<D>(u / (D / 4), 4 * (u % (D / 4)))]) = x;
         }
+    }
+
+    for (int c = c_end - 1; c >= c_begin; --c) {
+        // the lane index, opaque to the compiler in each chunk: otherwise the
+        // many lane-dependent LDS and memory addresses of a chunk are hoisted
+        // out of the walk and held in registers across it
+        int lane = tid & 63;
+        asm volatile("" : "+v"(lane));
+        const int r = lane & 15, g = lane >> 4;
+        const int ch0 = 16 * wave + 4 * g;    // this thread's 4 channels (keys and values)
+        const int t0 = c * C;
+        const int clen = min(C, L - t0);
+        const E* Sc = Sbh + (size_t)c * D * D;
+
+        // ---- loads: per owned token, one 4-channel run of q, k, v, dO (and
+        // gates)
+        Words<RW> qr[TB], kr[TB], vr[TB], dr[TB];
+        Words<4> lar[VG ? TB : 1];
 #pragma unroll
         for (int tb = 0; tb < TB; ++tb) {
+            const uint32_t row = (uint32_t)(t0 + 16 * tb + r);
+            const uint32_t off = (row * D + ch0) * ES;
+            qr[tb] = buf_load_words<RW>(rq, off);
+            kr[tb] = buf_load_words<RW>(rk, off);
+            vr[tb] = buf_load_words<RW>(rv, off);
+            dr[tb] = buf_load_words<RW>(rdo, off);
+            if constexpr (GATE == LA_GATE_DIAG) lar[tb] = buf_load_words<4>(rla, (row * D + ch0) * 4);
+            if constexpr (GATE == LA_GATE_SCALAR) {
+                const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(rla, row * 4, 0, 0);
+                lar[tb] = Words<4>{{w, w, w, w}};
+            }
+        }
+
+        // ---- features, gate prefix and factors of the owned elements
+        float qf[TB][4], kf[TB][4], fq[TB][4], fk[TB][4];
+        float er[4];   // e^{r} of the owned channels (DIAG)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) er[i] = 1.f;
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) {
+            const bool ok = 16 * tb + r < clen;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                float f = er[i];
-                if constexpr (GATE == LA_GATE_GAMMA) f = sm.gpow[16 * tb + r + 1];
-                acc[tb][i] *= f;
+                float qa = run_elem<BF16>(qr[tb], i), ka = run_elem<BF16>(kr[tb], i);
+                if constexpr (ELU1) {
+                    qa = elu1f(qa);
+                    ka = elu1f(ka);
+                }
+                qf[tb][i] = ok ? qa : 0.f;
+                kf[tb][i] = ok ? ka : 0.f;
+                fq[tb][i] = fk[tb][i] = 1.f;
             }
-#pragma unroll
-            for (int kk = 0; kk <= (16 * tb + 15) / MK; ++kk)
-                acc[tb] = T::mma(tr_frag<Cfg, DM>(&sm.kh[0][0], D, kk * MK, 16 * nb, lane),
-                                 tr_frag<Cfg, TM>(&sm.dpt[0][0], C, kk * MK, 16 * tb, lane), acc[tb]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) dqf[tb][i] = acc[tb][i] * fq[tb][i];
         }
-    }
-    // ---- dK^T = Gs V^T + Qh^T dP, then * e^{r - b}; with the partial
-    // sum_s Kh[s][i] (Gs v_s)_i of the chunk's carry (diagonal gate)
-    float dkf[TB][4];
-    float kgv[4] = {0.f, 0.f, 0.f, 0.f};
-    {
-        f32x4_t acc[TB];
-#pragma unroll
-        for (int tb = 0; tb < TB; ++tb) acc[tb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < D / MK; ++kk) {
-            const Frag a = row_frag<Cfg, DM>(&sm.gs[0][0], D, 16 * nb, kk * MK, lane);
+        if constexpr (VG) {
+            // inclusive prefix over the chunk's tokens: within each 16-token
+            // block across the lanes of a row, then the earlier blocks' totals
+            float b[TB][4];
+            float carry[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int tb = 0; tb < TB; ++tb)
-                acc[tb] = T::mma(a, row_frag<Cfg, DM>(&sm.vv[0][0], D, 16 * tb, kk * MK, lane), acc[tb]);
-        }
 #pragma unroll
-        for (int sb = 0; sb < TB; ++sb) {
-            if constexpr (VG) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) kgv[i] += acc[sb][i] * (kf[sb][i] * fk[sb][i]);
-            }
-            if constexpr (GATE == LA_GATE_GAMMA) {
-                const int s = 16 * sb + r;
-                const float f = s < clen ? sm.gpow[clen - 1 - s] : 0.f;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc[sb][i] *= f;
-            }
-#pragma unroll
-            for (int kk = (16 * sb) / MK; kk < C / MK; ++kk)
-                acc[sb] = T::mma(tr_frag<Cfg, DM>(&sm.qh[0][0], D, kk * MK, 16 * nb, lane),
-                                 row_frag<Cfg, TM>(&sm.dpt[0][0], C, 16 * sb, kk * MK, lane), acc[sb]);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) dkf[sb][i] = acc[sb][i] * fk[sb][i];
-        }
-    }
-    // ---- dV^T = Gs^T Kh^T + dO^T P
-    {
-        f32x4_t acc[TB];
-#pragma unroll
-        for (int tb = 0; tb < TB; ++tb) acc[tb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < D / MK; ++kk) {
-            const Frag a = tr_frag<Cfg, DM>(&sm.gs[0][0], D, kk * MK, 16 * nb, lane);
-#pragma unroll
-            for (int sb = 0; sb < TB; ++sb)
-                acc[sb] = T::mma(a, row_frag<Cfg, DM>(&sm.kh[0][0], D, 16 * sb, kk * MK, lane), acc[sb]);
-        }
-#pragma unroll
-        for (int sb = 0; sb < TB; ++sb) {
-            if constexpr (GATE == LA_GATE_GAMMA) {
-                const int s = 16 * sb + r;
-                const float f = s < clen ? sm.gpow[clen - 1 - s] : 0.f;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) acc[sb][i] *= f;
-            }
-#pragma unroll
-            for (int kk = (16 * sb) / MK; kk < C / MK; ++kk)
-                acc[sb] = T::mma(tr_frag<Cfg, DM>(&sm.dout[0][0], D, kk * MK, 16 * nb, lane),
-                                 row_frag<Cfg, TM>(&sm.pt[0][0], C, 16 * sb, kk * MK, lane), acc[sb]);
-            const uint32_t off = ((uint32_t)(t0 + 16 * sb + r) * D + ch0) * ES;
-            float x[4] = {acc[sb][0], acc[sb][1], acc[sb][2], acc[sb][3]};
-            buf_store_run4<BF16>(rdv, off, x);
-        }
-    }
-
-    // ---- dq, dk (chain rule through phi) and the gate gradient
-#pragma unroll
-    for (int tb = 0; tb < TB; ++tb) {
-        const uint32_t off = ((uint32_t)(t0 + 16 * tb + r) * D + ch0) * ES;
-        float xq[4], xk[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            xq[i] = dqf[tb][i];
-            xk[i] = dkf[tb][i];
-            if constexpr (ELU1) {
-                // phi' = 1 where phi = x + 1 > 1, else phi' = phi = e^x
-                xq[i] *= fminf(qf[tb][i], 1.f);
-                xk[i] *= fminf(kf[tb][i], 1.f);
-            }
-        }
-        buf_store_run4<BF16>(rdq, off, xq);
-        buf_store_run4<BF16>(rdk, off, xk);
-    }
-    if constexpr (VG) {
-        // the chunk's carry rowsum(G * S_next) per owned channel i:
-        //   e^{r_i} rowsum(Gs * S)_i + sum_s Kh[s][i] (Gs v_s)_i
-        // the first sum over the four lanes holding row 16 nb + r, read from
-        // the lane of each channel; the second over the 16 token lanes
-        float rs = gss;
-        rs += lane_read(rs, lane ^ 16);
-        rs += lane_read(rs, lane ^ 32);
-        float later[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float tok = lane_read(row_scan16<false>(kgv[i]), 16 * g + 15);
-            later[i] = er[i] * lane_read(rs, 4 * g + i) + tok;
-        }
-        // suffix sums of db = q dq - k dk over the chunk's tokens: within each
-        // block across the lanes, then the later blocks' totals
-#pragma unroll
-        for (int tb = TB - 1; tb >= 0; --tb) {
-            float out[4];
+                for (int i = 0; i < 4; ++i) {
+                    const float x = row_scan16<false>(run_elem<false>(lar[tb], i) * kLog2e);
+                    b[tb][i] = x + carry[i];
+                    carry[i] += lane_read(x, 16 * g + 15);
+                }
+            constexpr int tmid = C / 2 - 1;
+            float ebr[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float db = qf[tb][i] * dqf[tb][i] - kf[tb][i] * dkf[tb][i];
-                const float x = row_scan16<true>(db);
-                out[i] = x + later[i];
-                later[i] += lane_read(x, 16 * g);
+                const float ref = lane_read(b[tmid / 16][i], 16 * g + tmid % 16);
+                const float tot = carry[i];
+                er[i] = __builtin_amdgcn_exp2f(ref);
+                ebr[i] = __builtin_amdgcn_exp2f(tot - ref);
+#pragma unroll
+                for (int tb = 0; tb < TB; ++tb) {
+                    const float d = b[tb][i] - ref;
+                    fq[tb][i] = __builtin_amdgcn_exp2f(d);
+                    fk[tb][i] = __builtin_amdgcn_exp2f(-d);
+                }
             }
-            if constexpr (GATE == LA_GATE_DIAG) {
-                const uint32_t off = ((uint32_t)(t0 + 16 * tb + r) * D + ch0) * 4;
-                __builtin_amdgcn_raw_buffer_store_b128(
-                    __builtin_bit_cast(u32x4_t, f32x4_t{out[0], out[1], out[2], out[3]}), rdla, off, 0, 0);
-            } else {
-                // one gate per token: the sum over all channels, first over
-                // the 4 x 4 channels of this wave's lanes of the token
-                float sum = out[0] + out[1] + out[2] + out[3];
-                sum += lane_read(sum, lane ^ 16);
-                sum += lane_read(sum, lane ^ 32);
-                if (g == 0) sm.red[wave][16 * tb + r] = sum;
+            if (r == 0)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    sm.ebr[ch0 + i] = ebr[i];
+                    sm.er[ch0 + i] = er[i];
+                }
+        }
+
+        // ---- tiles: Qh, Kh, dO, V row-major (one 4-channel run per token)
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) {
+            const int t = 16 * tb + r;
+            float x[4], y[4], vo[4], dd[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                x[i] = qf[tb][i] * fq[tb][i];
+                y[i] = kf[tb][i] * fk[tb][i];
+                vo[i] = run_elem<BF16>(vr[tb], i);
+                dd[i] = run_elem<BF16>(dr[tb], i);
+            }
+            const int pos = bw_pos<Cfg, DM>(t, ch0);
+            lds_store_words(&sm.qh[t][pos], pack_run<BF16, 4>(x));
+            lds_store_words(&sm.kh[t][pos], pack_run<BF16, 4>(y));
+            lds_store_words(&sm.vv[t][pos], pack_run<BF16, 4>(vo));
+            lds_store_words(&sm.dout[t][pos], pack_run<BF16, 4>(dd));
+        }
+        __syncthreads();
+
+        // ---- Gs = diag(e^{B - r}) G in place (the factor table is visible now)
+        if constexpr (VG) {
+#pragma unroll
+            for (int j = 0; j < GQ; ++j) {
+                const int u = tid + j * Cfg::NT;
+                const int row = u / (D / 4);
+                float4* pg = reinterpret_cast<float4*>(&sm.gm[g_pos<D>(row, 4 * (u % (D / 4)))]);
+                const float f = sm.ebr[row];
+                float4 x = *pg;
+                x.x *= f;
+                x.y *= f;
+                x.z *= f;
+                x.w *= f;
+                *pg = x;
             }
         }
-        if constexpr (GATE == LA_GATE_SCALAR) {
-            // then over the waves
-            __syncthreads();
-            if (tid < C) {
-                float sum = 0.f;
+
+        // ---- P and dP on the lower-triangular tiles, stored transposed
+        // [s][t]: the output lane holds four consecutive t of one s
+        {
+            int idx = 0;
 #pragma unroll
-                for (int w2 = 0; w2 < NW; ++w2) sum += sm.red[w2][tid];
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sum), rdla, (uint32_t)(t0 + tid) * 4, 0, 0);
+            for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+                for (int sb = 0; sb <= tb; ++sb, ++idx) {
+                    if (idx % NW != wave) continue;
+                    f32x4_t ap = {0.f, 0.f, 0.f, 0.f}, ad = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kk = 0; kk < D / MK; ++kk) {
+                        ap = T::mma(row_frag<Cfg, DM>(&sm.qh[0][0], D, 16 * tb, kk * MK, lane),
+                                    row_frag<Cfg, DM>(&sm.kh[0][0], D, 16 * sb, kk * MK, lane), ap);
+                        ad = T::mma(row_frag<Cfg, DM>(&sm.dout[0][0], D, 16 * tb, kk * MK, lane),
+                                    row_frag<Cfg, DM>(&sm.vv[0][0], D, 16 * sb, kk * MK, lane), ad);
+                    }
+                    const int s = 16 * sb + r;
+                    float xp[4], xd[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int t = 16 * tb + 4 * g + i;
+                        float m = t >= s ? 1.f : 0.f;
+                        if constexpr (GATE == LA_GATE_GAMMA) m = t >= s ? sm.gpow[t - s] : 0.f;
+                        xp[i] = ap[i] * m;
+                        xd[i] = ad[i] * m;
+                    }
+                    store_run<BF16, 4>(&sm.pt[s][bw_pos<Cfg, TM>(s, 16 * tb + 4 * g)], xp);
+                    store_run<BF16, 4>(&sm.dpt[s][bw_pos<Cfg, TM>(s, 16 * tb + 4 * g)], xd);
+                }
+        }
+        __syncthreads();
+
+        // ---- dQ^T = e^{r} S dO^T + Kh^T dP^T, then * e^{b - r}; with the
+        // partial rowsum(Gs * S) of row 16 nb + r (diagonal gate)
+        float dqf[TB][4];
+        float gss = 0.f;
+        {
+            f32x4_t acc[TB];
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb) acc[tb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            // (at most 8 steps unrolled: fp32 has 32, whose state loads would
+            // all be issued at once)
+#pragma unroll 8
+            for (int kk = 0; kk < D / MK; ++kk) {
+                const Frag a = mem_frag<Cfg>(Sc, D, 16 * nb, kk * MK, lane);
+                if constexpr (VG) {
+                    float xs[KPL], xg[KPL];
+                    frag_floats<Cfg>(a, xs);
+                    g_row<Cfg>(sm.gm, 16 * nb + r, kk * MK + KPL * g, xg);
+#pragma unroll
+                    for (int j = 0; j < KPL; ++j) gss += xs[j] * xg[j];
+                }
+#pragma unroll
+                for (int tb = 0; tb < TB; ++tb)
+                    acc[tb] = T::mma(a, row_frag<Cfg, DM>(&sm.dout[0][0], D, 16 * tb, kk * MK, lane), acc[tb]);
             }
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float f = er[i];
+                    if constexpr (GATE == LA_GATE_GAMMA) f = sm.gpow[16 * tb + r + 1];
+                    acc[tb][i] *= f;
+                }
+#pragma unroll
+                for (int kk = 0; kk <= (16 * tb + 15) / MK; ++kk)
+                    acc[tb] = T::mma(tr_frag<Cfg, DM>(&sm.kh[0][0], D, kk * MK, 16 * nb, lane),
+                                     tr_frag<Cfg, TM>(&sm.dpt[0][0], C, kk * MK, 16 * tb, lane), acc[tb]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dqf[tb][i] = acc[tb][i] * fq[tb][i];
+            }
+        }
+        // ---- dK^T = Gs V^T + Qh^T dP, then * e^{r - b}; with the partial
+        // sum_s Kh[s][i] (Gs v_s)_i of the chunk's carry (diagonal gate)
+        float dkf[TB][4];
+        float kgv[4] = {0.f, 0.f, 0.f, 0.f};
+        {
+            f32x4_t acc[TB];
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb) acc[tb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < D / MK; ++kk) {
+                float xg[KPL];
+                g_row<Cfg>(sm.gm, 16 * nb + r, kk * MK + KPL * g, xg);
+                const Frag a = to_frag<Cfg>(xg);
+#pragma unroll
+                for (int tb = 0; tb < TB; ++tb)
+                    acc[tb] = T::mma(a, row_frag<Cfg, DM>(&sm.vv[0][0], D, 16 * tb, kk * MK, lane), acc[tb]);
+            }
+#pragma unroll
+            for (int sb = 0; sb < TB; ++sb) {
+                if constexpr (VG) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) kgv[i] += acc[sb][i] * (kf[sb][i] * fk[sb][i]);
+                }
+                if constexpr (GATE == LA_GATE_GAMMA) {
+                    const int s = 16 * sb + r;
+                    const float f = s < clen ? sm.gpow[clen - 1 - s] : 0.f;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[sb][i] *= f;
+                }
+#pragma unroll
+                for (int kk = (16 * sb) / MK; kk < C / MK; ++kk)
+                    acc[sb] = T::mma(tr_frag<Cfg, DM>(&sm.qh[0][0], D, kk * MK, 16 * nb, lane),
+                                     row_frag<Cfg, TM>(&sm.dpt[0][0], C, 16 * sb, kk * MK, lane), acc[sb]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dkf[sb][i] = acc[sb][i] * fk[sb][i];
+            }
+        }
+        // ---- dq, dk (chain rule through phi), and db = q dq - k dk for the
+        // gate gradient: the features and both gradients end here
+        float db[VG ? TB : 1][4];
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) {
+            const uint32_t off = ((uint32_t)(t0 + 16 * tb + r) * D + ch0) * ES;
+            float xq[4], xk[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if constexpr (VG) db[tb][i] = qf[tb][i] * dqf[tb][i] - kf[tb][i] * dkf[tb][i];
+                xq[i] = dqf[tb][i];
+                xk[i] = dkf[tb][i];
+                if constexpr (ELU1) {
+                    // phi' = 1 where phi = x + 1 > 1, else phi' = phi = e^x
+                    xq[i] *= fminf(qf[tb][i], 1.f);
+                    xk[i] *= fminf(kf[tb][i], 1.f);
+                }
+            }
+            buf_store_run4<BF16>(rdq, off, xq);
+            buf_store_run4<BF16>(rdk, off, xk);
+        }
+        // ---- dV^T = Gs^T Kh^T + dO^T P
+        {
+            f32x4_t acc[TB];
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb) acc[tb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < D / MK; ++kk) {
+                // Gs's rows kk MK + KPL g + j (the k-slots) in column 16 nb + r
+                float xg[KPL];
+#pragma unroll
+                for (int j = 0; j < KPL; ++j) xg[j] = sm.gm[g_pos<D>(kk * MK + KPL * g + j, 16 * nb + r)];
+                const Frag a = to_frag<Cfg>(xg);
+#pragma unroll
+                for (int sb = 0; sb < TB; ++sb)
+                    acc[sb] = T::mma(a, row_frag<Cfg, DM>(&sm.kh[0][0], D, 16 * sb, kk * MK, lane), acc[sb]);
+            }
+#pragma unroll
+            for (int sb = 0; sb < TB; ++sb) {
+                if constexpr (GATE == LA_GATE_GAMMA) {
+                    const int s = 16 * sb + r;
+                    const float f = s < clen ? sm.gpow[clen - 1 - s] : 0.f;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc[sb][i] *= f;
+                }
+#pragma unroll
+                for (int kk = (16 * sb) / MK; kk < C / MK; ++kk)
+                    acc[sb] = T::mma(tr_frag<Cfg, DM>(&sm.dout[0][0], D, kk * MK, 16 * nb, lane),
+                                     row_frag<Cfg, TM>(&sm.pt[0][0], C, 16 * sb, kk * MK, lane), acc[sb]);
+                const uint32_t off = ((uint32_t)(t0 + 16 * sb + r) * D + ch0) * ES;
+                float x[4] = {acc[sb][0], acc[sb][1], acc[sb][2], acc[sb][3]};
+                buf_store_run4<BF16>(rdv, off, x);
+            }
+        }
+
+        // ---- the gate gradient
+        if constexpr (VG) {
+            // the chunk's carry rowsum(G * S_next) per owned channel i:
+            //   e^{r_i} rowsum(Gs * S)_i + sum_s Kh[s][i] (Gs v_s)_i
+            // the first sum over the four lanes holding row 16 nb + r, read
+            // from the lane of each channel; the second over the 16 token lanes
+            float rs = gss;
+            rs += lane_read(rs, lane ^ 16);
+            rs += lane_read(rs, lane ^ 32);
+            float later[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float tok = lane_read(row_scan16<false>(kgv[i]), 16 * g + 15);
+                later[i] = er[i] * lane_read(rs, 4 * g + i) + tok;
+            }
+            // suffix sums of db = q dq - k dk over the chunk's tokens: within
+            // each block across the lanes, then the later blocks' totals
+#pragma unroll
+            for (int tb = TB - 1; tb >= 0; --tb) {
+                float out[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float x = row_scan16<true>(db[tb][i]);
+                    out[i] = x + later[i];
+                    later[i] += lane_read(x, 16 * g);
+                }
+                if constexpr (GATE == LA_GATE_DIAG) {
+                    const uint32_t off = ((uint32_t)(t0 + 16 * tb + r) * D + ch0) * 4;
+                    __builtin_amdgcn_raw_buffer_store_b128(
+                        __builtin_bit_cast(u32x4_t, f32x4_t{out[0], out[1], out[2], out[3]}), rdla, off, 0, 0);
+                } else {
+                    // one gate per token: the sum over all channels, first
+                    // over the 4 x 4 channels of this wave's lanes of the token
+                    float sum = out[0] + out[1] + out[2] + out[3];
+                    sum += lane_read(sum, lane ^ 16);
+                    sum += lane_read(sum, lane ^ 32);
+                    if (g == 0) sm.red[wave][16 * tb + r] = sum;
+                }
+            }
+            if constexpr (GATE == LA_GATE_SCALAR) {
+                // then over the waves
+                __syncthreads();
+                if (tid < C) {
+                    float sum = 0.f;
+#pragma unroll
+                    for (int w2 = 0; w2 < NW; ++w2) sum += sm.red[w2][tid];
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(sum), rdla, (uint32_t)(t0 + tid) * 4, 0, 0);
+                }
+            }
+        }
+
+        // ---- G of the chunk before: e^{r} (Gs + Qh^T dO) (diagonal gate),
+        // gamma^{clen} G + (q gamma^{t+1})^T dO (gamma), G + Q^T dO.  Wave w
+        // steps rows [16w, 16w+16) once every wave has read G; the product
+        // is formed as dO^T Qh so that the lane holds row 16w + r, columns
+        // 16 m + 4g .. +3 of each column block m.
+        __syncthreads();
+        {
+            const int gi = 16 * wave + r;
+            // factor on the held G (Gs for the vector gates), factor on the sum
+            const float fg = GATE == LA_GATE_GAMMA ? sm.gpow[clen] : 1.f;
+            const float fo = VG ? sm.er[gi] : 1.f;
+            // four column blocks at a time
+            constexpr int MG = NW < 4 ? NW : 4;
+#pragma unroll
+            for (int m0 = 0; m0 < NW; m0 += MG) {
+                f32x4_t acc[MG];
+#pragma unroll
+                for (int m = 0; m < MG; ++m) acc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < C / MK; ++kk) {
+                    Frag bq = tr_frag<Cfg, DM>(&sm.qh[0][0], D, kk * MK, 16 * wave, lane);
+                    if constexpr (GATE == LA_GATE_GAMMA) {
+                        float x[KPL];
+                        frag_floats<Cfg>(bq, x);
+#pragma unroll
+                        for (int j = 0; j < KPL; ++j) x[j] *= sm.gpow[kk * MK + KPL * g + j + 1];
+                        bq = to_frag<Cfg>(x);
+                    }
+#pragma unroll
+                    for (int m = 0; m < MG; ++m)
+                        acc[m] = T::mma(tr_frag<Cfg, DM>(&sm.dout[0][0], D, kk * MK, 16 * (m0 + m), lane),
+                                        bq, acc[m]);
+                }
+#pragma unroll
+                for (int m = 0; m < MG; ++m) {
+                    float4* pg = reinterpret_cast<float4*>(&sm.gm[g_pos<D>(gi, 16 * (m0 + m) + 4 * g)]);
+                    float4 x = *pg;
+                    x.x = fo * (fg * x.x + acc[m][0]);
+                    x.y = fo * (fg * x.y + acc[m][1]);
+                    x.z = fo * (fg * x.z + acc[m][2]);
+                    x.w = fo * (fg * x.w + acc[m][3]);
+                    *pg = x;
+                }
+            }
+        }
+        // G stepped; Qh, dO and the factor tables free for the next chunk
+        __syncthreads();
+    }
+
+    // ---- the gradient of the initial state, from the sequence's first segment
+    if (seg == 0 && p.dS0) {
+        __syncthreads();
+        float4* out = reinterpret_cast<float4*>(p.dS0 + (size_t)bh * D * D);
+#pragma unroll
+        for (int j = 0; j < GQ; ++j) {
+            const int u = tid + j * Cfg::NT;
+            out[u] = *reinterpret_cast<const float4*>(&sm.gm[g_pos<D>(u / (D / 4), 4 * (u % (D / 4)))]);
         }
     }
 }
 
 // Host-side dispatch over gate mode and feature map for one (d, dtype): one
-// workgroup per (b,h, chunk).
+// workgroup per (b,h) segment.
 template <int D, bool BF>
 hipError_t launch_bwd_dt(const BwdParams& p, int gate, hipStream_t s) {
     constexpr int C = bwd_chunk(D, BF);
-    const dim3 grid((unsigned)(p.BH * p.nchunks));
+    const dim3 grid((unsigned)(p.BH * p.P));
 #define LA_BWD_LAUNCH(GG)                                                                       \
     do {                                                                                        \
         using Cfg = BwdCfg<D, C, BF, GG>;                                                       \

@@ -54,11 +54,12 @@
 //  * STORE starts each segment from its entry state (after the segment
 //    scan) and writes the true state at every chunk boundary (also on the
 //    main pass, for a forward that keeps its states for the backward);
-//  * REV runs the recurrence of the state gradient, G_prev = A_c G +
-//    sum_t (phi(q_t) * e^{b_t}) do_t^T, which is the state update with k ->
-//    phi(q), v -> do, the key factor replaced by the query factor, the
-//    before/after factors swapped, and the chunks taken in reverse order
-//    (the caller passes q and do in the k and v slots).
+//  * REV aggregates the recurrence of the state gradient over a segment,
+//    G_prev = A_c G + sum_t (phi(q_t) * e^{b_t}) do_t^T, which is the state
+//    update with k -> phi(q), v -> do, the key factor replaced by the query
+//    factor, the before/after factors swapped, and the chunks taken in
+//    reverse order (the caller passes q and do in the k and v slots); the
+//    gradient kernel carries G through each segment itself.
 #pragma once
 
 #include <type_traits>
@@ -251,6 +252,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
     const int r = lane & 15, g = lane >> 4;
     const int P = p.P;
     static_assert(SONLY || !REV, "the reversed walk is state-only");
+    static_assert(!(REV && STORE), "the reversed walk only aggregates segments");
     static_assert(!(STORE && EPI), "no epilogue with the boundary states");
     static_assert(!(SONLY && EPI), "the output epilogue belongs to the main pass");
     // the aggregate pass skips the segment it would end with (the last one,
@@ -911,9 +913,8 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
         // ---- the state at the next chunk boundary (the entry state of the
         // next segment is stored by that segment's workgroup)
         if constexpr (STORE) {
-            const int nxt = REV ? c - 1 : c + 1;
-            const bool own = REV ? (nxt >= c_begin) : (nxt < c_end || seg == P - 1);
-            if (own) store_state(nxt);
+            const int nxt = c + 1;
+            if (nxt < c_end || seg == P - 1) store_state(nxt);
         }
     };
     if constexpr (STORE) {
@@ -921,7 +922,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
         // diagonal after-factor of a previous chunk is 1 here)
         if (c_begin < c_end) {
             __syncthreads();   // sm.post set up
-            store_state(REV ? c_end - 1 : c_begin);
+            store_state(c_begin);
         }
     }
     {
@@ -951,10 +952,8 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
     float* Sout;
     float* zout;
     if constexpr (STORE && SONLY) {
-        // the state after the whole segment: S_final (forward) or the
-        // gradient of the initial state (reverse), from the segment that
-        // ends the sequence
-        if (seg != (REV ? 0 : P - 1)) return;
+        // the state after the whole sequence, from its last segment
+        if (seg != P - 1) return;
         Sout = p.S_final ? p.S_final + (size_t)bh * SS : nullptr;
         zout = nullptr;
     } else if constexpr (SONLY) {
@@ -1094,7 +1093,6 @@ hipError_t launch_chunk_dt(const ChunkParams& p, int chunk, int gate, int pass, 
     if (chunk == CB) {
         if (pass == PASS_STATE_REV) LA_CHUNK_GATES(CB, true, true, false);
         if (pass == PASS_STORE) LA_CHUNK_GATES(CB, true, false, true);
-        if (pass == PASS_STORE_REV) LA_CHUNK_GATES(CB, true, true, true);
         if (pass == PASS_MAIN_STORE) LA_CHUNK_GATES(CB, false, false, true);
     }
     if (pass == PASS_MAIN_NORM && chunk == 64) LA_CHUNK_GATES_EP(64, false, false, false, true);

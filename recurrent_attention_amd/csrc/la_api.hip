@@ -208,18 +208,17 @@ hipError_t bwd_launch(const la_desc* d, const la::BwdParams& p, int gate, hipStr
 }
 
 // Backward workspace, in bytes: the state before every chunk and the final
-// state, then the state gradient after every chunk, both in the element
-// type of q/k/v; then the fp32 segment slots of the state passes.
+// state in the element type of q/k/v, then the fp32 segment slots of the
+// state passes.
 struct BwdLayout {
-    size_t fwd, rows, seg, total;
+    size_t fwd, seg, total;
 };
 BwdLayout bwd_layout(const la_desc* d, const Plan& pl) {
     const size_t bh = (size_t)d->B * d->H, dd = (size_t)d->dk * d->dv;
     const size_t es = d->dtype == LA_BF16 ? 2 : 4;
     BwdLayout w;
     w.fwd = 0;
-    w.rows = w.fwd + bh * (pl.nchunks + 1) * dd * es;
-    w.seg = w.rows + bh * pl.nchunks * dd * es;
+    w.seg = w.fwd + bh * (pl.nchunks + 1) * dd * es;
     w.total = w.seg + (pl.P > 1 ? bh * pl.P * (dd + 2 * (size_t)d->dk) * sizeof(float) : 0);
     return w;
 }
@@ -543,14 +542,14 @@ la_status la_chunk_bwd(const la_desc* d, const void* q, const void* k, const voi
         if (e != hipSuccess) return hip_fail(e, "state store launch");
     }
 
-    // the state gradient after every chunk: the same recurrence run from the
-    // end with phi(q) and dout in the places of phi(k) and v
+    // the state gradient entering each segment (P > 1): the same recurrence
+    // run from the end with phi(q) and dout in the places of phi(k) and v,
+    // aggregated per segment and composed from the last segment to the first
     p.k = q;
     p.v = dout;
     p.S0 = dS_final;
-    p.S_final = dS0;
-    p.st_rows = ws + w.rows;
-    p.st_slots = pl.nchunks;
+    p.S_final = nullptr;
+    p.st_rows = nullptr;
     if (pl.P > 1) {
         e = timed_launch(la::K_CHUNK_STATE, s, [&] {
             return chunk_launch(d, p, chunk, gate_mode, la::PASS_STATE_REV, s, BH * (pl.P - 1));
@@ -559,12 +558,9 @@ la_status la_chunk_bwd(const la_desc* d, const void* q, const void* k, const voi
         e = timed_launch(la::K_STATE_SCAN, s, [&] { return la::launch_state_scan(p, d->dk, true, s); });
         if (e != hipSuccess) return hip_fail(e, "reverse segment scan launch");
     }
-    e = timed_launch(la::K_CHUNK_STORE, s, [&] {
-        return chunk_launch(d, p, chunk, gate_mode, la::PASS_STORE_REV, s, BH * pl.P);
-    });
-    if (e != hipSuccess) return hip_fail(e, "gradient store launch");
 
-    // per-chunk gradients
+    // the gradients: each segment walked from its last chunk to its first,
+    // the state gradient carried along
     la::BwdParams b;
     std::memset(&b, 0, sizeof b);
     b.q = q;
@@ -573,7 +569,8 @@ la_status la_chunk_bwd(const la_desc* d, const void* q, const void* k, const voi
     b.dout = dout;
     b.log_alpha = p.log_alpha;
     b.st_fwd = states ? states : static_cast<const void*>(ws + w.fwd);
-    b.st_rows = ws + w.rows;
+    b.g_entry = pl.P > 1 ? p.ws_S : dS_final;
+    b.dS0 = dS0;
     b.dq = dq;
     b.dk = dk;
     b.dv = dv;
@@ -582,6 +579,8 @@ la_status la_chunk_bwd(const la_desc* d, const void* q, const void* k, const voi
     b.H = d->H;
     b.BH = BH;
     b.nchunks = pl.nchunks;
+    b.P = pl.P;
+    b.cps = pl.cps;
     b.phi_elu1 = p.phi_elu1;
     std::memcpy(b.log2_gamma, p.log2_gamma, sizeof b.log2_gamma);
     e = timed_launch(la::K_BWD, s, [&] { return bwd_launch(d, b, gate_mode, s); });

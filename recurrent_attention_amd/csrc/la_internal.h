@@ -62,13 +62,15 @@ struct BwdParams {
     const void* dout;       // [BH, L, d] dtype
     const float* log_alpha; // [BH, L, d] (DIAG)
     const void* st_fwd;     // [BH, nchunks + 1, d, d] dtype: state before each chunk, then the final state
-    const void* st_rows;    // [BH, nchunks, d, d] dtype: gradient of the state after each chunk
+    const float* g_entry;   // [BH, P, d, d]: gradient of the state after each segment's last chunk, or null (zeros)
+    float* dS0;             // [BH, d, d]: gradient of the initial state, or null
     void* dq;               // [BH, L, d] dtype
     void* dk;               // [BH, L, d] dtype
     void* dv;               // [BH, L, d] dtype
     float* dlog_alpha;      // [BH, L, d] (DIAG)
     int L, H, BH;
     int nchunks;
+    int P, cps;             // segments per (b,h) and chunks per segment
     int phi_elu1;
     float log2_gamma[LA_MAX_GAMMA_HEADS];
 };
@@ -87,10 +89,10 @@ struct DeltaParams {
 };
 
 // Passes of the chunk kernel.  MAIN and STATE serve the forward; the
-// backward adds the reversed state pass and the two passes that store the
-// state (or its gradient) at every chunk boundary.
+// backward adds the reversed state pass (segment aggregates of the state
+// gradient) and the pass that stores the state at every chunk boundary.
 enum ChunkPass {
-    PASS_MAIN = 0, PASS_STATE = 1, PASS_STATE_REV = 2, PASS_STORE = 3, PASS_STORE_REV = 4,
+    PASS_MAIN = 0, PASS_STATE = 1, PASS_STATE_REV = 2, PASS_STORE = 3,
     PASS_MAIN_NORM = 5,  // main pass with the group-norm / swish-gate output epilogue (chunk 64)
     PASS_MAIN_STORE = 6  // main pass that also stores the state at every chunk boundary
 };

@@ -185,15 +185,15 @@ def _bwd(desc, gate_mode=0, gate=None, S0=None, dSf=None, dla=None, dS0=None,
 
 
 def test_bwd_chunk_and_workspace_size():
-    # states at every chunk boundary: (2 * nchunks + 1) d x d per (b,h) in the
-    # input element type (the state before each chunk and the final one, the
-    # gradient after each chunk), plus the fp32 segment slots
+    # states at every chunk boundary: (nchunks + 1) d x d per (b,h) in the
+    # input element type (the state before each chunk and the final one),
+    # plus the fp32 segment slots
     d = _desc(B=1, H=2, L=1000, dk=64, dv=64, dtype=api.LA_BF16, segments=1)
     assert api.la_chunk_bwd_chunk(d) == 64
-    assert api.la_chunk_bwd_workspace_bytes(d) == 2 * (2 * 16 + 1) * 64 * 64 * 2
+    assert api.la_chunk_bwd_workspace_bytes(d) == 2 * (16 + 1) * 64 * 64 * 2
     d = _desc(B=1, H=2, L=1000, dk=64, dv=64, dtype=api.LA_F32, segments=4)
     assert api.la_chunk_bwd_workspace_bytes(d) == (
-        2 * (2 * 16 + 1) * 64 * 64 * 4 + 2 * 4 * (64 * 64 + 128) * 4)
+        2 * (16 + 1) * 64 * 64 * 4 + 2 * 4 * (64 * 64 + 128) * 4)
     f32_128 = _desc(dk=128, dv=128, dtype=api.LA_F32)
     assert api.la_chunk_bwd_chunk(f32_128) == 32
     assert api.la_chunk_bwd_workspace_bytes(_desc(L=0)) == 0
