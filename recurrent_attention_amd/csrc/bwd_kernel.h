@@ -24,7 +24,7 @@
 // and G v_s is the first term of dk_s, already in the accumulators.
 //
 // Matrix-core mapping (C tokens, D = d_k = d_v; wave w owns channel block
-// [16w, 16w+16) of dq, dk and of dv, and rows [16w, 16w+16) of G):
+// [16w, 16w+16) of dq, dk and of dv, and a block of G's tiles):
 //   P   = Qh Kh^T and dP = dO V^T on the lower-triangular 16x16 tiles
 //         (Qh = q e^{b - r}, Kh = k e^{r - b}, r = b at the chunk middle),
 //         stored transposed, [s][t], with the causal mask (and gamma^(t-s));
@@ -33,9 +33,9 @@
 //   dV^T = Gs^T Kh^T + dO^T P
 //   G_prev = e^{r} (Gs + Qh^T dO), formed as its transpose dO^T Qh
 // with Gs = diag(e^{B - r}) G.  G stays in LDS in fp32 for the whole walk
-// (row-major, 16-byte units swizzled by the row), is scaled to Gs in place
-// once the chunk's gate factors are known, and is rounded to the element
-// type where it is an operand.  S comes from memory in the element type.  Every output lane of the
+// (row-major, 16-byte units swizzled by the row); where it is an operand
+// it is read there, scaled by the row factor e^{B - r} and rounded to the
+// element type.  S comes from memory in the element type.  Every output lane of the
 // gradient products holds 4 consecutive channels of one token, which are
 // the same elements the thread loaded and whose decay factors it computed;
 // every output lane of the G step holds 4 consecutive columns of one row of
@@ -309,23 +309,6 @@ __global__ __launch_bounds__(Cfg::NT) void bwd_kernel(const BwdParams p) {
         }
         __syncthreads();
 
-        // ---- Gs = diag(e^{B - r}) G in place (the factor table is visible now)
-        if constexpr (VG) {
-#pragma unroll
-            for (int j = 0; j < GQ; ++j) {
-                const int u = tid + j * Cfg::NT;
-                const int row = u / (D / 4);
-                float4* pg = reinterpret_cast<float4*>(&sm.gm[g_pos<D>(row, 4 * (u % (D / 4)))]);
-                const float f = sm.ebr[row];
-                float4 x = *pg;
-                x.x *= f;
-                x.y *= f;
-                x.z *= f;
-                x.w *= f;
-                *pg = x;
-            }
-        }
-
         // ---- P and dP on the lower-triangular tiles, stored transposed
         // [s][t]: the output lane holds four consecutive t of one s
         {
@@ -358,6 +341,9 @@ __global__ __launch_bounds__(Cfg::NT) void bwd_kernel(const BwdParams p) {
                 }
         }
         __syncthreads();
+
+        // e^{B - r} of G's row 16 nb + r, the row this lane reads
+        const float frow = VG ? sm.ebr[16 * nb + r] : 1.f;
 
         // ---- dQ^T = e^{r} S dO^T + Kh^T dP^T, then * e^{b - r}; with the
         // partial rowsum(Gs * S) of row 16 nb + r (diagonal gate)
@@ -411,6 +397,8 @@ __global__ __launch_bounds__(Cfg::NT) void bwd_kernel(const BwdParams p) {
             for (int kk = 0; kk < D / MK; ++kk) {
                 float xg[KPL];
                 g_row<Cfg>(sm.gm, 16 * nb + r, kk * MK + KPL * g, xg);
+#pragma unroll
+                for (int j = 0; j < KPL; ++j) xg[j] *= frow;
                 const Frag a = to_frag<Cfg>(xg);
 #pragma unroll
                 for (int tb = 0; tb < TB; ++tb)
@@ -467,7 +455,11 @@ __global__ __launch_bounds__(Cfg::NT) void bwd_kernel(const BwdParams p) {
                 // Gs's rows kk MK + KPL g + j (the k-slots) in column 16 nb + r
                 float xg[KPL];
 #pragma unroll
-                for (int j = 0; j < KPL; ++j) xg[j] = sm.gm[g_pos<D>(kk * MK + KPL * g + j, 16 * nb + r)];
+                for (int j = 0; j < KPL; ++j) {
+                    const int i = kk * MK + KPL * g + j;
+                    xg[j] = sm.gm[g_pos<D>(i, 16 * nb + r)];
+                    if constexpr (VG) xg[j] *= sm.ebr[i];
+                }
                 const Frag a = to_frag<Cfg>(xg);
 #pragma unroll
                 for (int sb = 0; sb < TB; ++sb)
@@ -497,7 +489,7 @@ __global__ __launch_bounds__(Cfg::NT) void bwd_kernel(const BwdParams p) {
             //   e^{r_i} rowsum(Gs * S)_i + sum_s Kh[s][i] (Gs v_s)_i
             // the first sum over the four lanes holding row 16 nb + r, read
             // from the lane of each channel; the second over the 16 token lanes
-            float rs = gss;
+            float rs = gss * frow;
             rs += lane_read(rs, lane ^ 16);
             rs += lane_read(rs, lane ^ 32);
             float later[4];
@@ -543,46 +535,56 @@ __global__ __launch_bounds__(Cfg::NT) void bwd_kernel(const BwdParams p) {
         }
 
         // ---- G of the chunk before: e^{r} (Gs + Qh^T dO) (diagonal gate),
-        // gamma^{clen} G + (q gamma^{t+1})^T dO (gamma), G + Q^T dO.  Wave w
-        // steps rows [16w, 16w+16) once every wave has read G; the product
-        // is formed as dO^T Qh so that the lane holds row 16w + r, columns
-        // 16 m + 4g .. +3 of each column block m.
+        // gamma^{clen} G + (q gamma^{t+1})^T dO (gamma), G + Q^T dO, once
+        // every wave has read G.  Wave w steps IG row blocks times NG column
+        // blocks of G (a 2 x 4 block grid at d = 128, which reads a third
+        // less of Qh and dO than whole block rows); the product is formed
+        // as dO^T Qh so that the lane holds one row, 4 consecutive columns
+        // of each tile.
         __syncthreads();
         {
-            const int gi = 16 * wave + r;
-            // factor on the held G (Gs for the vector gates), factor on the sum
-            const float fg = GATE == LA_GATE_GAMMA ? sm.gpow[clen] : 1.f;
-            const float fo = VG ? sm.er[gi] : 1.f;
-            // four column blocks at a time
-            constexpr int MG = NW < 4 ? NW : 4;
+            constexpr int IG = NW >= 4 ? 2 : 1, NG = NW / IG;
+            const int ib0 = (wave % (NW / IG)) * IG, nb0 = (wave / (NW / IG)) * NG;
+            f32x4_t acc[IG][NG];
 #pragma unroll
-            for (int m0 = 0; m0 < NW; m0 += MG) {
-                f32x4_t acc[MG];
+            for (int ii = 0; ii < IG; ++ii)
 #pragma unroll
-                for (int m = 0; m < MG; ++m) acc[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                for (int m = 0; m < NG; ++m) acc[ii][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kk = 0; kk < C / MK; ++kk) {
-                    Frag bq = tr_frag<Cfg, DM>(&sm.qh[0][0], D, kk * MK, 16 * wave, lane);
+            for (int kk = 0; kk < C / MK; ++kk) {
+                Frag bq[IG];
+#pragma unroll
+                for (int ii = 0; ii < IG; ++ii) {
+                    bq[ii] = tr_frag<Cfg, DM>(&sm.qh[0][0], D, kk * MK, 16 * (ib0 + ii), lane);
                     if constexpr (GATE == LA_GATE_GAMMA) {
                         float x[KPL];
-                        frag_floats<Cfg>(bq, x);
+                        frag_floats<Cfg>(bq[ii], x);
 #pragma unroll
                         for (int j = 0; j < KPL; ++j) x[j] *= sm.gpow[kk * MK + KPL * g + j + 1];
-                        bq = to_frag<Cfg>(x);
+                        bq[ii] = to_frag<Cfg>(x);
                     }
-#pragma unroll
-                    for (int m = 0; m < MG; ++m)
-                        acc[m] = T::mma(tr_frag<Cfg, DM>(&sm.dout[0][0], D, kk * MK, 16 * (m0 + m), lane),
-                                        bq, acc[m]);
                 }
 #pragma unroll
-                for (int m = 0; m < MG; ++m) {
-                    float4* pg = reinterpret_cast<float4*>(&sm.gm[g_pos<D>(gi, 16 * (m0 + m) + 4 * g)]);
+                for (int m = 0; m < NG; ++m) {
+                    const Frag ad = tr_frag<Cfg, DM>(&sm.dout[0][0], D, kk * MK, 16 * (nb0 + m), lane);
+#pragma unroll
+                    for (int ii = 0; ii < IG; ++ii) acc[ii][m] = T::mma(ad, bq[ii], acc[ii][m]);
+                }
+            }
+#pragma unroll
+            for (int ii = 0; ii < IG; ++ii) {
+                const int gi = 16 * (ib0 + ii) + r;
+                // factor on the held G, factor on the sum
+                const float fg = GATE == LA_GATE_GAMMA ? sm.gpow[clen] : VG ? sm.ebr[gi] : 1.f;
+                const float fo = VG ? sm.er[gi] : 1.f;
+#pragma unroll
+                for (int m = 0; m < NG; ++m) {
+                    float4* pg = reinterpret_cast<float4*>(&sm.gm[g_pos<D>(gi, 16 * (nb0 + m) + 4 * g)]);
                     float4 x = *pg;
-                    x.x = fo * (fg * x.x + acc[m][0]);
-                    x.y = fo * (fg * x.y + acc[m][1]);
-                    x.z = fo * (fg * x.z + acc[m][2]);
-                    x.w = fo * (fg * x.w + acc[m][3]);
+                    x.x = fo * (fg * x.x + acc[ii][m][0]);
+                    x.y = fo * (fg * x.y + acc[ii][m][1]);
+                    x.z = fo * (fg * x.z + acc[ii][m][2]);
+                    x.w = fo * (fg * x.w + acc[ii][m][3]);
                     *pg = x;
                 }
             }
