@@ -35,9 +35,11 @@
 // with Gs = diag(e^{B - r}) G.  G stays in LDS in fp32 for the whole walk
 // (row-major, 16-byte units swizzled by the row); where it is an operand
 // it is read there, scaled by the row factor e^{B - r} and rounded to the
-// element type.  S comes from memory in the element type.  Every output lane of the
-// gradient products holds 4 consecutive channels of one token, which are
-// the same elements the thread loaded and whose decay factors it computed;
+// element type.  S comes from memory in the element type.  q, k, v and dO
+// are loaded in whole rows into their LDS tiles; each thread then takes
+// one 4-channel run of q and k per owned token from there.  Every output
+// lane of the gradient products holds 4 consecutive channels of one token,
+// the same elements whose features and decay factors that thread formed;
 // every output lane of the G step holds 4 consecutive columns of one row of
 // G.  Operands with the token index (or G's row index) as the contraction
 // are read from row-major LDS tiles with the transposing LDS read of gfx950
@@ -129,7 +131,7 @@ __device__ __forceinline__ typename Cfg::Frag to_frag(const float* x) {
 template <class Cfg, bool ELU1>
 __global__ __launch_bounds__(Cfg::NT) void bwd_kernel(const BwdParams p) {
     constexpr int D = Cfg::D, C = Cfg::C, GATE = Cfg::GATE, TB = Cfg::TB, NW = Cfg::NW;
-    constexpr int MK = Cfg::MK, RW = Cfg::RW, KPL = Cfg::KPL;
+    constexpr int MK = Cfg::MK, RW = Cfg::RW, KPL = Cfg::KPL, UE = Cfg::UE, DU = Cfg::DU;
     constexpr bool BF16 = Cfg::BF16;
     constexpr int ES = (int)sizeof(typename Cfg::E);
     constexpr int DM = Cfg::DMASK, TM = Cfg::TMASK;
@@ -141,6 +143,9 @@ __global__ __launch_bounds__(Cfg::NT) void bwd_kernel(const BwdParams p) {
     constexpr bool VG = GATE == LA_GATE_DIAG || GATE == LA_GATE_SCALAR;
     // float4 units of G each thread copies in (and out, for dS0)
     constexpr int GQ = D * D / 4 / Cfg::NT;
+    // 16-byte units of a C x D tile each thread loads
+    constexpr int VU = C * D / UE / Cfg::NT;
+    static_assert(VU * UE * Cfg::NT == C * D, "tile load mapping");
     static_assert(GQ * 4 * Cfg::NT == D * D, "G copy mapping");
 
     __shared__ BwdSmem<Cfg> sm;
@@ -214,18 +219,25 @@ __global__ __launch_bounds__(Cfg::NT) void bwd_kernel(const BwdParams p) {
         const int clen = min(C, L - t0);
         const E* Sc = Sbh + (size_t)c * D * D;
 
-        // ---- loads: per owned token, one 4-channel run of q, k, v, dO (and
-        // gates)
-        Words<RW> qr[TB], kr[TB], vr[TB], dr[TB];
+        // ---- loads.  q, k, v and dO land in their LDS tiles first: whole
+        // rows, 16 bytes a lane (a wave reading 16 tokens x 4 channels per
+        // instruction would touch 16 rows for 32 bytes each, and the memory
+        // pipeline's issue rate, not HBM, set the pace).  The gates come
+        // as one 4-channel run per owned token.
         Words<4> lar[VG ? TB : 1];
+        Words<4> qc[VU], kc[VU], vc[VU], dc[VU];
+#pragma unroll
+        for (int j = 0; j < VU; ++j) {
+            const int u = tid + j * Cfg::NT;
+            const uint32_t off = (uint32_t)t0 * D * ES + (uint32_t)u * 16;
+            qc[j] = buf_load_words<4>(rq, off);
+            kc[j] = buf_load_words<4>(rk, off);
+            vc[j] = buf_load_words<4>(rv, off);
+            dc[j] = buf_load_words<4>(rdo, off);
+        }
 #pragma unroll
         for (int tb = 0; tb < TB; ++tb) {
             const uint32_t row = (uint32_t)(t0 + 16 * tb + r);
-            const uint32_t off = (row * D + ch0) * ES;
-            qr[tb] = buf_load_words<RW>(rq, off);
-            kr[tb] = buf_load_words<RW>(rk, off);
-            vr[tb] = buf_load_words<RW>(rv, off);
-            dr[tb] = buf_load_words<RW>(rdo, off);
             if constexpr (GATE == LA_GATE_DIAG) lar[tb] = buf_load_words<4>(rla, (row * D + ch0) * 4);
             if constexpr (GATE == LA_GATE_SCALAR) {
                 const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(rla, row * 4, 0, 0);
@@ -233,26 +245,44 @@ __global__ __launch_bounds__(Cfg::NT) void bwd_kernel(const BwdParams p) {
             }
         }
 
-        // ---- features, gate prefix and factors of the owned elements
-        float qf[TB][4], kf[TB][4], fq[TB][4], fk[TB][4];
+        // ---- raw tiles, then each thread's own q, k runs (one 4-channel run
+        // per owned token) back from them
+#pragma unroll
+        for (int j = 0; j < VU; ++j) {
+            const int u = tid + j * Cfg::NT;
+            const int t = u / DU, col = (u % DU) * UE;
+            const int pos = bw_pos<Cfg, DM>(t, col);
+            lds_store_words(&sm.qh[t][pos], qc[j]);
+            lds_store_words(&sm.kh[t][pos], kc[j]);
+            lds_store_words(&sm.vv[t][pos], vc[j]);
+            lds_store_words(&sm.dout[t][pos], dc[j]);
+        }
+        __syncthreads();
+        Words<RW> qr[TB], kr[TB];
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) {
+            const int t = 16 * tb + r;
+            const int pos = bw_pos<Cfg, DM>(t, ch0);
+            qr[tb] = *reinterpret_cast<const Words<RW>*>(&sm.qh[t][pos]);
+            kr[tb] = *reinterpret_cast<const Words<RW>*>(&sm.kh[t][pos]);
+        }
+
+        // ---- features, gate prefix and factors of the owned elements.  Only
+        // the raw q, k runs and the factor e^{b - r} stay live through the
+        // chunk; the features and e^{r - b} are formed again where needed.
+        auto feat = [&](const Words<RW>& w, int tb, int i) {
+            float a = run_elem<BF16>(w, i);
+            if constexpr (ELU1) a = elu1f(a);
+            return 16 * tb + r < clen ? a : 0.f;
+        };
+        float fq[TB][4];
         float er[4];   // e^{r} of the owned channels (DIAG)
 #pragma unroll
         for (int i = 0; i < 4; ++i) er[i] = 1.f;
 #pragma unroll
-        for (int tb = 0; tb < TB; ++tb) {
-            const bool ok = 16 * tb + r < clen;
+        for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float qa = run_elem<BF16>(qr[tb], i), ka = run_elem<BF16>(kr[tb], i);
-                if constexpr (ELU1) {
-                    qa = elu1f(qa);
-                    ka = elu1f(ka);
-                }
-                qf[tb][i] = ok ? qa : 0.f;
-                kf[tb][i] = ok ? ka : 0.f;
-                fq[tb][i] = fk[tb][i] = 1.f;
-            }
-        }
+            for (int i = 0; i < 4; ++i) fq[tb][i] = 1.f;
         if constexpr (VG) {
             // inclusive prefix over the chunk's tokens: within each 16-token
             // block across the lanes of a row, then the earlier blocks' totals
@@ -278,7 +308,6 @@ __global__ __launch_bounds__(Cfg::NT) void bwd_kernel(const BwdParams p) {
                 for (int tb = 0; tb < TB; ++tb) {
                     const float d = b[tb][i] - ref;
                     fq[tb][i] = __builtin_amdgcn_exp2f(d);
-                    fk[tb][i] = __builtin_amdgcn_exp2f(-d);
                 }
             }
             if (r == 0)
@@ -289,24 +318,26 @@ __global__ __launch_bounds__(Cfg::NT) void bwd_kernel(const BwdParams p) {
                 }
         }
 
-        // ---- tiles: Qh, Kh, dO, V row-major (one 4-channel run per token)
+        // ---- Qh, Kh in place of the raw runs
 #pragma unroll
         for (int tb = 0; tb < TB; ++tb) {
             const int t = 16 * tb + r;
-            float x[4], y[4], vo[4], dd[4];
+            float x[4], y[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                x[i] = qf[tb][i] * fq[tb][i];
-                y[i] = kf[tb][i] * fk[tb][i];
-                vo[i] = run_elem<BF16>(vr[tb], i);
-                dd[i] = run_elem<BF16>(dr[tb], i);
+                x[i] = feat(qr[tb], tb, i) * fq[tb][i];
+                y[i] = feat(kr[tb], tb, i) * (VG ? __builtin_amdgcn_rcpf(fq[tb][i]) : 1.f);
             }
             const int pos = bw_pos<Cfg, DM>(t, ch0);
             lds_store_words(&sm.qh[t][pos], pack_run<BF16, 4>(x));
             lds_store_words(&sm.kh[t][pos], pack_run<BF16, 4>(y));
-            lds_store_words(&sm.vv[t][pos], pack_run<BF16, 4>(vo));
-            lds_store_words(&sm.dout[t][pos], pack_run<BF16, 4>(dd));
         }
+        // the raw runs, opaque from here on, so that the features are
+        // formed again from them rather than held through the products
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb)
+#pragma unroll
+            for (int j = 0; j < RW; ++j) asm volatile("" : "+v"(qr[tb].w[j]), "+v"(kr[tb].w[j]));
         __syncthreads();
 
         // ---- P and dP on the lower-triangular tiles, stored transposed
@@ -408,7 +439,8 @@ __global__ __launch_bounds__(Cfg::NT) void bwd_kernel(const BwdParams p) {
             for (int sb = 0; sb < TB; ++sb) {
                 if constexpr (VG) {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) kgv[i] += acc[sb][i] * (kf[sb][i] * fk[sb][i]);
+                    for (int i = 0; i < 4; ++i)
+                        kgv[i] += acc[sb][i] * (feat(kr[sb], sb, i) * __builtin_amdgcn_rcpf(fq[sb][i]));
                 }
                 if constexpr (GATE == LA_GATE_GAMMA) {
                     const int s = 16 * sb + r;
@@ -421,7 +453,8 @@ __global__ __launch_bounds__(Cfg::NT) void bwd_kernel(const BwdParams p) {
                     acc[sb] = T::mma(tr_frag<Cfg, DM>(&sm.qh[0][0], D, kk * MK, 16 * nb, lane),
                                      row_frag<Cfg, TM>(&sm.dpt[0][0], C, 16 * sb, kk * MK, lane), acc[sb]);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) dkf[sb][i] = acc[sb][i] * fk[sb][i];
+                for (int i = 0; i < 4; ++i)
+                    dkf[sb][i] = VG ? acc[sb][i] * __builtin_amdgcn_rcpf(fq[sb][i]) : acc[sb][i];
             }
         }
         // ---- dq, dk (chain rule through phi), and db = q dq - k dk for the
@@ -433,13 +466,14 @@ __global__ __launch_bounds__(Cfg::NT) void bwd_kernel(const BwdParams p) {
             float xq[4], xk[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                if constexpr (VG) db[tb][i] = qf[tb][i] * dqf[tb][i] - kf[tb][i] * dkf[tb][i];
+                const float qf = feat(qr[tb], tb, i), kf = feat(kr[tb], tb, i);
+                if constexpr (VG) db[tb][i] = qf * dqf[tb][i] - kf * dkf[tb][i];
                 xq[i] = dqf[tb][i];
                 xk[i] = dkf[tb][i];
                 if constexpr (ELU1) {
                     // phi' = 1 where phi = x + 1 > 1, else phi' = phi = e^x
-                    xq[i] *= fminf(qf[tb][i], 1.f);
-                    xk[i] *= fminf(kf[tb][i], 1.f);
+                    xq[i] *= fminf(qf, 1.f);
+                    xk[i] *= fminf(kf, 1.f);
                 }
             }
             buf_store_run4<BF16>(rdq, off, xq);
