@@ -267,6 +267,14 @@ __global__ __launch_bounds__(Cfg::NT) void bwd_kernel(const BwdParams p) {
             kr[tb] = *reinterpret_cast<const Words<RW>*>(&sm.kh[t][pos]);
         }
 
+        // the state before the chunk as this wave's dQ operands (bf16: four
+        // fragments, in flight through the feature and score stages)
+        Frag sfr[BF16 ? D / MK : 1];
+        if constexpr (BF16) {
+#pragma unroll
+            for (int kk = 0; kk < D / MK; ++kk) sfr[kk] = mem_frag<Cfg>(Sc, D, 16 * nb, kk * MK, lane);
+        }
+
         // ---- features, gate prefix and factors of the owned elements.  Only
         // the raw q, k runs and the factor e^{b - r} stay live through the
         // chunk; the features and e^{r - b} are formed again where needed.
@@ -388,7 +396,9 @@ __global__ __launch_bounds__(Cfg::NT) void bwd_kernel(const BwdParams p) {
             // all be issued at once)
 #pragma unroll 8
             for (int kk = 0; kk < D / MK; ++kk) {
-                const Frag a = mem_frag<Cfg>(Sc, D, 16 * nb, kk * MK, lane);
+                Frag a;
+                if constexpr (BF16) a = sfr[kk];
+                else a = mem_frag<Cfg>(Sc, D, 16 * nb, kk * MK, lane);
                 if constexpr (VG) {
                     float xs[KPL], xg[KPL];
                     frag_floats<Cfg>(a, xs);
