@@ -141,6 +141,20 @@ def test_chunk_bwd_segmentations_agree(segments):
     _check(got, ref, torch.bfloat16, f"segments={segments}")
 
 
+@pytest.mark.parametrize("dt,d,mode", [("bf16", 128, DIAG), ("bf16", 128, SCALAR),
+                                       ("bf16", 128, GAMMA), ("bf16", 64, NONE),
+                                       ("f32", 64, DIAG), ("f32", 128, DIAG)])
+def test_chunk_bwd_long_walk(dt, d, mode):
+    # one segment per (b,h): the gradient kernel carries the state gradient
+    # through every chunk of the sequence (96 chunks of 64 tokens, 192 of 32
+    # for fp32 at d = 128), ending on a ragged chunk
+    dtype = DTYPES[dt]
+    inp = _case(1, 2, 96 * 64 - 17, d, dtype, mode, seed=21, state=True)
+    got = _gpu_bwd(inp, mode, segments=1)
+    ref = _oracle_bwd(inp, mode)
+    _check(got, ref, dtype, f"long walk {dt} d={d} mode={mode}")
+
+
 @pytest.mark.parametrize("L", [1, 31, 63, 64, 65, 129])
 @pytest.mark.parametrize("mode", [NONE, DIAG, SCALAR])
 def test_chunk_bwd_edge_lengths(L, mode):
