@@ -197,13 +197,20 @@ __global__ __launch_bounds__(Cfg::NT) void bwd_kernel(const BwdParams p) {
     // G after the segment's last chunk (zeros without one); visible after
     // the first chunk's tile barrier
     {
-        const float4* gin = p.g_entry
-            ? reinterpret_cast<const float4*>(p.g_entry + ((size_t)bh * p.P + seg) * D * D) : nullptr;
+        // all of this thread's loads in flight before the first LDS write
+        float4 x[GQ];
+        if (p.g_entry) {
+            const float4* gin = reinterpret_cast<const float4*>(p.g_entry + ((size_t)bh * p.P + seg) * D * D);
+#pragma unroll
+            for (int j = 0; j < GQ; ++j) x[j] = gin[tid + j * Cfg::NT];
+        } else {
+#pragma unroll
+            for (int j = 0; j < GQ; ++j) x[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
 #pragma unroll
         for (int j = 0; j < GQ; ++j) {
             const int u = tid + j * Cfg::NT;
-            const float4 x = gin ? gin[u] : make_float4(0.f, 0.f, 0.f, 0.f);
-            *reinterpret_cast<float4*>(&sm.gm[g_pos<D>(u / (D / 4), 4 * (u % (D / 4)))]) = x;
+            *reinterpret_cast<float4*>(&sm.gm[g_pos<D>(u / (D / 4), 4 * (u % (D / 4)))]) = x[j];
         }
     }
 
