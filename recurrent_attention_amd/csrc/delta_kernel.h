@@ -147,6 +147,13 @@ __global__ __launch_bounds__(Cfg::NT) void delta_chunk_kernel(const DeltaParams 
     if (nchunks > 0) load(0);
 
     for (int c = 0; c < nchunks; ++c) {
+        // the lane index, opaque to the compiler in each chunk: otherwise the
+        // many lane-dependent LDS addresses of a chunk are hoisted out of the
+        // walk and held in registers across it
+        int lane_o = tid & 63;
+        asm volatile("" : "+v"(lane_o));
+        const int lane = lane_o;
+        const int r = lane & 15, g = lane >> 4;
         const int t0 = c * C;
         // ---- tiles (tokens past the end read as zeros: no key, no write)
 #pragma unroll
