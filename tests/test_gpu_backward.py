@@ -164,12 +164,14 @@ def test_chunk_bwd_edge_lengths(L, mode):
     _check(got, ref, torch.bfloat16, f"L={L} mode={mode}")
 
 
-def test_chunk_bwd_without_state_or_state_gradient():
-    # S0 = NULL and dS_final = NULL: zero initial state, loss on out only
+@pytest.mark.parametrize("segments", [0, 1])
+def test_chunk_bwd_without_state_or_state_gradient(segments):
+    # S0 = NULL and dS_final = NULL: zero initial state, loss on out only;
+    # with one segment the walk starts from no gradient at all
     inp = _case(1, 2, 300, 64, torch.float32, DIAG, seed=12, state=False, state_grad=False)
-    got = _gpu_bwd(inp, DIAG)
+    got = _gpu_bwd(inp, DIAG, segments=segments)
     ref = _oracle_bwd(inp, DIAG)
-    _check(got, ref, torch.float32, "no S0, no dS_final")
+    _check(got, ref, torch.float32, f"no S0, no dS_final, segments={segments}")
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
