@@ -534,6 +534,43 @@ __global__ __launch_bounds__(Cfg::NT) void bwd_kernel(const BwdParams p) {
             }
         }
 
+        // ---- G of the chunk before: e^{r} (Gs + Qh^T dO) (diagonal gate),
+        // gamma^{clen} G + (q gamma^{t+1})^T dO (gamma), G + Q^T dO, once
+        // every wave has read G.  Wave w steps IG row blocks times NG column
+        // blocks of G (a 2 x 4 block grid at d = 128, which reads a third
+        // less of Qh and dO than whole block rows); the product is formed
+        // as dO^T Qh so that the lane holds one row, 4 consecutive columns
+        // of each tile.  The product does not involve G and is formed before
+        // the barrier; only the read-modify-write of G waits for it.
+        constexpr int IG = NW >= 4 ? 2 : 1, NG = NW / IG;
+        const int ib0 = (wave % (NW / IG)) * IG, nb0 = (wave / (NW / IG)) * NG;
+        f32x4_t gacc[IG][NG];
+#pragma unroll
+        for (int ii = 0; ii < IG; ++ii)
+#pragma unroll
+            for (int m = 0; m < NG; ++m) gacc[ii][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < C / MK; ++kk) {
+            Frag bq[IG];
+#pragma unroll
+            for (int ii = 0; ii < IG; ++ii) {
+                bq[ii] = tr_frag<Cfg, DM>(&sm.qh[0][0], D, kk * MK, 16 * (ib0 + ii), lane);
+                if constexpr (GATE == LA_GATE_GAMMA) {
+                    float x[KPL];
+                    frag_floats<Cfg>(bq[ii], x);
+#pragma unroll
+                    for (int j = 0; j < KPL; ++j) x[j] *= sm.gpow[kk * MK + KPL * g + j + 1];
+                    bq[ii] = to_frag<Cfg>(x);
+                }
+            }
+#pragma unroll
+            for (int m = 0; m < NG; ++m) {
+                const Frag ad = tr_frag<Cfg, DM>(&sm.dout[0][0], D, kk * MK, 16 * (nb0 + m), lane);
+#pragma unroll
+                for (int ii = 0; ii < IG; ++ii) gacc[ii][m] = T::mma(ad, bq[ii], gacc[ii][m]);
+            }
+        }
+
         // ---- the gate gradient
         if constexpr (VG) {
             // the chunk's carry rowsum(G * S_next) per owned channel i:
@@ -585,43 +622,8 @@ __global__ __launch_bounds__(Cfg::NT) void bwd_kernel(const BwdParams p) {
             }
         }
 
-        // ---- G of the chunk before: e^{r} (Gs + Qh^T dO) (diagonal gate),
-        // gamma^{clen} G + (q gamma^{t+1})^T dO (gamma), G + Q^T dO, once
-        // every wave has read G.  Wave w steps IG row blocks times NG column
-        // blocks of G (a 2 x 4 block grid at d = 128, which reads a third
-        // less of Qh and dO than whole block rows); the product is formed
-        // as dO^T Qh so that the lane holds one row, 4 consecutive columns
-        // of each tile.
         __syncthreads();
         {
-            constexpr int IG = NW >= 4 ? 2 : 1, NG = NW / IG;
-            const int ib0 = (wave % (NW / IG)) * IG, nb0 = (wave / (NW / IG)) * NG;
-            f32x4_t acc[IG][NG];
-#pragma unroll
-            for (int ii = 0; ii < IG; ++ii)
-#pragma unroll
-                for (int m = 0; m < NG; ++m) acc[ii][m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < C / MK; ++kk) {
-                Frag bq[IG];
-#pragma unroll
-                for (int ii = 0; ii < IG; ++ii) {
-                    bq[ii] = tr_frag<Cfg, DM>(&sm.qh[0][0], D, kk * MK, 16 * (ib0 + ii), lane);
-                    if constexpr (GATE == LA_GATE_GAMMA) {
-                        float x[KPL];
-                        frag_floats<Cfg>(bq[ii], x);
-#pragma unroll
-                        for (int j = 0; j < KPL; ++j) x[j] *= sm.gpow[kk * MK + KPL * g + j + 1];
-                        bq[ii] = to_frag<Cfg>(x);
-                    }
-                }
-#pragma unroll
-                for (int m = 0; m < NG; ++m) {
-                    const Frag ad = tr_frag<Cfg, DM>(&sm.dout[0][0], D, kk * MK, 16 * (nb0 + m), lane);
-#pragma unroll
-                    for (int ii = 0; ii < IG; ++ii) acc[ii][m] = T::mma(ad, bq[ii], acc[ii][m]);
-                }
-            }
 #pragma unroll
             for (int ii = 0; ii < IG; ++ii) {
                 const int gi = 16 * (ib0 + ii) + r;
@@ -632,10 +634,10 @@ __global__ __launch_bounds__(Cfg::NT) void bwd_kernel(const BwdParams p) {
                 for (int m = 0; m < NG; ++m) {
                     float4* pg = reinterpret_cast<float4*>(&sm.gm[g_pos<D>(gi, 16 * (nb0 + m) + 4 * g)]);
                     float4 x = *pg;
-                    x.x = fo * (fg * x.x + acc[ii][m][0]);
-                    x.y = fo * (fg * x.y + acc[ii][m][1]);
-                    x.z = fo * (fg * x.z + acc[ii][m][2]);
-                    x.w = fo * (fg * x.w + acc[ii][m][3]);
+                    x.x = fo * (fg * x.x + gacc[ii][m][0]);
+                    x.y = fo * (fg * x.y + gacc[ii][m][1]);
+                    x.z = fo * (fg * x.z + gacc[ii][m][2]);
+                    x.w = fo * (fg * x.w + gacc[ii][m][3]);
                     *pg = x;
                 }
             }
