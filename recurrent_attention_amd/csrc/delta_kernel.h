@@ -252,6 +252,45 @@ __global__ __launch_bounds__(Cfg::NT) void delta_chunk_kernel(const DeltaParams 
         }
         __syncthreads();
 
+        // ---- the state as an operand: rows n of S^T, k-slots the state rows
+        // held by this lane (32 k2 + 4 g + i and 32 k2 + 16 + 4 g + i)
+        Frag sa[BF16 ? D / 32 : 1];
+        if constexpr (BF16) {
+#pragma unroll
+            for (int k2 = 0; k2 < D / 32; ++k2) {
+                const float x8[8] = {accS[2 * k2][0], accS[2 * k2][1], accS[2 * k2][2], accS[2 * k2][3],
+                                     accS[2 * k2 + 1][0], accS[2 * k2 + 1][1], accS[2 * k2 + 1][2],
+                                     accS[2 * k2 + 1][3]};
+                sa[k2] = T::from8(x8);
+            }
+        }
+        // S^T X^T for the rows s (or t) = 16 xb + r of tile X
+        auto state_times = [&](const E* X, int xb, f32x4_t acc) {
+            const int s = 16 * xb + r;
+            if constexpr (BF16) {
+#pragma unroll
+                for (int k2 = 0; k2 < D / 32; ++k2)
+                    acc = T::mma(sa[k2],
+                                 T::load2x4(X + s * D + bw_pos<Cfg, DM>(s, 32 * k2 + 4 * g),
+                                            X + s * D + bw_pos<Cfg, DM>(s, 32 * k2 + 16 + 4 * g)),
+                                 acc);
+            } else {
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        acc = T::mma(accS[mb][i], X[s * D + bw_pos<Cfg, DM>(s, 16 * mb + 4 * g + i)], acc);
+            }
+            return acc;
+        };
+
+        // S^T Q^T of the output, formed by the waves other than wave 0 while
+        // wave 0 runs the longest off-diagonal chain (it involves neither T
+        // nor this chunk's update)
+        f32x4_t oq[TB];
+#pragma unroll
+        for (int tb = 0; tb < TB; ++tb) oq[tb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
         // ---- the blocks below the diagonal, one block column per wave (the
         // blocks of column j need only N_jj, the diagonal blocks and the
         // column's own earlier blocks, so no workgroup barrier between them):
@@ -301,6 +340,10 @@ __global__ __launch_bounds__(Cfg::NT) void delta_chunk_kernel(const DeltaParams 
         // column would otherwise wait for the off-diagonal chain (the
         // registers were emptied into this chunk's tiles)
         if (c + 1 < nchunks) load(c + 1);
+        if (wave != 0) {
+#pragma unroll
+            for (int tb = 0; tb < TB; ++tb) oq[tb] = state_times(&sm.q[0][0], tb, oq[tb]);
+        }
         __syncthreads();
 
         // ---- W^T = K^T T^T: wave w takes key channels [16w, 16w+16)
@@ -316,38 +359,6 @@ __global__ __launch_bounds__(Cfg::NT) void delta_chunk_kernel(const DeltaParams 
             store_run<BF16, 4>(&sm.w[s][bw_pos<Cfg, DM>(s, n0 + 4 * g)], xw);
         }
         __syncthreads();
-
-        // ---- the state as an operand: rows n of S^T, k-slots the state rows
-        // held by this lane (32 k2 + 4 g + i and 32 k2 + 16 + 4 g + i)
-        Frag sa[BF16 ? D / 32 : 1];
-        if constexpr (BF16) {
-#pragma unroll
-            for (int k2 = 0; k2 < D / 32; ++k2) {
-                const float x8[8] = {accS[2 * k2][0], accS[2 * k2][1], accS[2 * k2][2], accS[2 * k2][3],
-                                     accS[2 * k2 + 1][0], accS[2 * k2 + 1][1], accS[2 * k2 + 1][2],
-                                     accS[2 * k2 + 1][3]};
-                sa[k2] = T::from8(x8);
-            }
-        }
-        // S^T X^T for the rows s (or t) = 16 xb + r of tile X
-        auto state_times = [&](const E* X, int xb, f32x4_t acc) {
-            const int s = 16 * xb + r;
-            if constexpr (BF16) {
-#pragma unroll
-                for (int k2 = 0; k2 < D / 32; ++k2)
-                    acc = T::mma(sa[k2],
-                                 T::load2x4(X + s * D + bw_pos<Cfg, DM>(s, 32 * k2 + 4 * g),
-                                            X + s * D + bw_pos<Cfg, DM>(s, 32 * k2 + 16 + 4 * g)),
-                                 acc);
-            } else {
-#pragma unroll
-                for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        acc = T::mma(accS[mb][i], X[s * D + bw_pos<Cfg, DM>(s, 16 * mb + 4 * g + i)], acc);
-            }
-            return acc;
-        };
 
         // ---- U'^T = V^T T^T - S^T W^T for this wave's value columns
 #pragma unroll
@@ -370,7 +381,7 @@ __global__ __launch_bounds__(Cfg::NT) void delta_chunk_kernel(const DeltaParams 
         for (int kk = 0; kk < C / MK; ++kk) uf[kk] = tr_frag<Cfg, DM>(&sm.up[0][0], D, kk * MK, n0, lane);
 #pragma unroll
         for (int tb = 0; tb < TB; ++tb) {
-            f32x4_t acc = state_times(&sm.q[0][0], tb, f32x4_t{0.f, 0.f, 0.f, 0.f});
+            f32x4_t acc = wave != 0 ? oq[tb] : state_times(&sm.q[0][0], tb, oq[tb]);
 #pragma unroll
             for (int kk = 0; kk <= (16 * tb + 15) / MK; ++kk)
                 acc = T::mma(uf[kk], row_frag<Cfg, TM>(&sm.pm[0][0], C, 16 * tb, kk * MK, lane), acc);
