@@ -625,15 +625,38 @@ def cpu_baseline(workloads, w):
     inp = workloads.workload_inputs(w.name, seed=0, device="cpu")
     q, k, v = (inp[x].double().numpy() for x in ("q", "k", "v"))
     la = inp["log_alpha"].double().numpy()
-    nthreads = max(1, min(w.B * w.H, os.cpu_count() or 1, 16))
+    host = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    nthreads = max(1, min(w.B * w.H, host or 1, 16))
     t0 = time.perf_counter()
     oracle.run(q, k, v, gate_mode=w.gate_mode, log_alpha=la, phi=w.phi,
                normalize=w.normalize, nthreads=nthreads)
     dt = time.perf_counter() - t0
     return {"value": round(w.B * w.L / dt, 1), "unit": "tokens/s", "cores": nthreads,
-            "kind": "oracle",
+            "host_cpus": host, "kind": "oracle",
             "sample": f"whole workload {w.name} (B={w.B}, H={w.H}, L={w.L}) drawn on the host; "
                       f"fp64 token loop, {nthreads} threads over (b,h) pairs, {dt:.2f} s"}
+
+
+def hbm_copy_ceiling(torch, nbytes=1 << 30, reps=10):
+    """The practical HBM ceiling beside the 8 TB/s peak: a plain 1 GiB
+    device-to-device copy (torch's copy kernel), timed with events on the
+    stream; bytes = read + write."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) / reps * 1e3
+    gbs = 2 * nbytes / (us * 1e-6) / 1e9
+    del src, dst
+    return {"what": "1 GiB device-to-device copy, read + write bytes", "us": round(us, 2),
+            "GB/s": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
 
 
 def copy_calibration(torch, nbytes=1 << 30):
@@ -766,6 +789,7 @@ def main(argv=None):
             "kernels_avg_us": {k: (round(v["avg_us"], 2) if v["avg_us"] else None)
                                for k, v in sc["kernels"].items()},
             "roofline": sc["roofline"]}
+    line["hbm_copy_ceiling"] = hbm_copy_ceiling(torch)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(workloads, w)
     print(json.dumps(line), flush=True)

@@ -97,7 +97,9 @@ typedef struct la_desc {
  * Supported kernel shapes (else LA_ERR_UNSUPPORTED):
  *   dk == dv, dk in {16, 32, 64, 128}; chunk in {16, 32, 64}.
  *   LA_F32 runs fp32 matrix cores (no bf16 rounding); LA_BF16 runs bf16
- *   matrix cores with fp32 accumulation and fp32 states.
+ *   matrix cores with fp32 accumulation and fp32 states, which needs
+ *   dk >= 32 (la_decode_step runs no matrix cores and takes bf16 at every
+ *   dk; la_delta_decode_step is built for bf16 at dk >= 32).
  *   LA_GATE_GAMMA needs H <= LA_MAX_GAMMA_HEADS.
  *   LA_GATE_DIAG: the factorised in-chunk form multiplies by exp of the
  *   chunk-local cumulative log-gate measured from the chunk middle, so the

@@ -63,7 +63,10 @@ size_t order_bytes(const la_desc* d) { return align16((size_t)d->B * sizeof(int)
 bool supported_d(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
 bool supported_chunk(int c) { return c == 16 || c == 32 || c == 64; }
 
-la_status check_desc(const la_desc* d) {
+// mfma: the shape runs on matrix cores (every prefill-like path), where
+// bf16 operands need d_k >= 32; the decode step streams the state on the
+// vector units and takes bf16 at every built width
+la_status check_desc(const la_desc* d, bool mfma = true) {
     if (!d) return fail(LA_ERR_INVALID, "descriptor is NULL");
     if (d->B < 1 || d->H < 1 || d->L < 1 || d->dk < 1 || d->dv < 1)
         return fail(LA_ERR_INVALID, "dimensions must be >= 1 (B=%d H=%d L=%d dk=%d dv=%d)", d->B,
@@ -80,8 +83,8 @@ la_status check_desc(const la_desc* d) {
     if (!supported_d(d->dk) || d->dk != d->dv)
         return fail(LA_ERR_UNSUPPORTED, "built shapes need dk == dv in {16,32,64,128} (dk=%d dv=%d)",
                     d->dk, d->dv);
-    if (d->dtype == LA_BF16 && d->dk < 32)
-        return fail(LA_ERR_UNSUPPORTED, "bf16 inputs need dk >= 32 (dk=%d)", d->dk);
+    if (mfma && d->dtype == LA_BF16 && d->dk < 32)
+        return fail(LA_ERR_UNSUPPORTED, "bf16 prefill inputs need dk >= 32 (dk=%d)", d->dk);
     // kernels address one (b,h) slice of a tensor with 32-bit byte offsets
     if ((long long)d->L * (d->dk > d->dv ? d->dk : d->dv) * 4 > 0xFFFFFFFFLL)
         return fail(LA_ERR_UNSUPPORTED, "L*d*4 must stay below 2^32 bytes (L=%d)", d->L);
@@ -654,7 +657,7 @@ la_status la_decode_step(const la_desc* d, const void* q, const void* k, const v
                          int gate_mode, const float* gate, float* S, float* z, void* out,
                          void* stream) {
     g_errmsg[0] = '\0';
-    la_status st = check_desc(d);
+    la_status st = check_desc(d, false);
     if (st != LA_OK) return st;
     if (d->L != 1) return fail(LA_ERR_INVALID, "decode needs L == 1 (L=%d)", d->L);
     if (!q || !k || !v || !out || !S) return fail(LA_ERR_INVALID, "q, k, v, S and out must be non-NULL");

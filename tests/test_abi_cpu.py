@@ -82,6 +82,16 @@ def test_bf16_needs_dk_32():
     assert "dk >= 32" in api.la_last_error_message()
 
 
+def test_bf16_decode_takes_d16():
+    # the decode step runs on the vector units: bf16 at d = 16 passes the
+    # host checks (a NULL S is the first thing refused after them)
+    d = _desc(dk=16, dv=16, L=1)
+    assert api.la_decode_step(d, A, A, A, 0, None, None, None, A, None) == api.LA_ERR_INVALID
+    assert "non-NULL" in api.la_last_error_message()
+    # the delta rule's decode is built for bf16 at d >= 32 only
+    assert api.la_delta_decode_step(d, A, A, A, A, A, A, None) == api.LA_ERR_UNSUPPORTED
+
+
 @pytest.mark.parametrize("chunk", [0, 8, 48, 128])
 def test_chunk_rejects_unsupported_chunk(chunk):
     assert _chunk(_desc(), chunk=chunk) == api.LA_ERR_UNSUPPORTED
