@@ -210,6 +210,34 @@ la_status la_chunk_fwd_groupnorm(const la_desc* d, const void* q, const void* k,
                                  void* workspace, size_t workspace_bytes,
                                  void* stream);
 
+/*
+ * la_chunk_fwd_noalloc -- la_chunk_fwd for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, and
+ * harnesses that forbid hipMalloc.  Same arguments, result and kernels as
+ * la_chunk_fwd without the workspace pair: the segment states, decays and
+ * normaliser parts live instead in a static device array of
+ * LA_NOALLOC_SCRATCH_BYTES bytes that the library holds on every GPU it
+ * runs on until the process ends.
+ *   - Nothing is allocated: no hipMalloc, hipFree or allocating library
+ *     call.  The array's device address is looked up once per device (on
+ *     the first call whose stream belongs to that device) and kept.
+ *   - LA_ERR_UNSUPPORTED when the shape's workspace
+ *     (la_chunk_fwd_workspace_bytes) exceeds LA_NOALLOC_SCRATCH_BYTES; the
+ *     automatic segment choice needs at most about 34 MB at d = 128.
+ *   - Every call on one GPU shares that GPU's array, and the array keeps
+ *     the last call's contents (every slot a call reads it has written
+ *     first, so nothing needs clearing).  Calls that overlap in time on one
+ *     GPU (different streams, or different host threads) race on it and
+ *     give wrong results: serialise them.
+ */
+#define LA_NOALLOC_SCRATCH_BYTES (64u << 20)
+la_status la_chunk_fwd_noalloc(const la_desc* d, const void* q, const void* k,
+                               const void* v, int gate_mode,
+                               const float* gamma_or_log_alpha,
+                               const float* S0, const float* z0, int chunk,
+                               void* out, float* S_final, float* z_final,
+                               void* stream);
+
 /* Bytes of device workspace la_chunk_fwd needs for this shape (segment
  * states, their decays and normaliser parts); 0 for a single segment.
  * Returns 0 for an invalid descriptor as well. */

@@ -33,8 +33,9 @@ EXPORTED = (
     "la_chunk_bwd", "la_chunk_bwd_workspace_bytes", "la_chunk_bwd_chunk",
     "la_chunk_fwd_varlen", "la_chunk_fwd_varlen_workspace_bytes",
     "la_chunk_fwd_groupnorm", "la_delta_fwd", "la_delta_decode_step", "la_delta_chunk",
-    "la_chunk_fwd_train", "la_chunk_train_states_bytes",
+    "la_chunk_fwd_train", "la_chunk_train_states_bytes", "la_chunk_fwd_noalloc",
 )
+LA_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class LaError(RuntimeError):
@@ -74,6 +75,8 @@ def load_library():
     fp = ctypes.POINTER(ctypes.c_float)
     lib.la_chunk_fwd.argtypes = [dp, vp, vp, vp, i, vp, vp, vp, i, vp, vp, vp, vp, sz, vp]
     lib.la_chunk_fwd.restype = i
+    lib.la_chunk_fwd_noalloc.argtypes = [dp, vp, vp, vp, i, vp, vp, vp, i, vp, vp, vp, vp]
+    lib.la_chunk_fwd_noalloc.restype = i
     lib.la_chunk_fwd_workspace_bytes.argtypes = [dp, i]
     lib.la_chunk_fwd_workspace_bytes.restype = sz
     lib.la_chunk_fwd_segments.argtypes = [dp, i]
@@ -141,6 +144,15 @@ def la_chunk_fwd(desc, q, k, v, gate_mode, gamma_or_log_alpha, S0, z0, chunk,
     return load_library().la_chunk_fwd(
         ctypes.byref(desc), q, k, v, int(gate_mode), gamma_or_log_alpha, S0, z0,
         int(chunk), out, S_final, z_final, workspace, int(workspace_bytes), stream)
+
+
+def la_chunk_fwd_noalloc(desc, q, k, v, gate_mode, gamma_or_log_alpha, S0, z0, chunk,
+                         out, S_final, z_final, stream):
+    """Raw call of the entry point that allocates nothing (its workspace is
+    the library's static scratch array)."""
+    return load_library().la_chunk_fwd_noalloc(
+        ctypes.byref(desc), q, k, v, int(gate_mode), gamma_or_log_alpha, S0, z0,
+        int(chunk), out, S_final, z_final, stream)
 
 
 def la_chunk_fwd_groupnorm(desc, q, k, v, gate_mode, gamma_or_log_alpha, S0, z0, chunk, gn,

@@ -250,12 +250,56 @@ la_status hip_fail(hipError_t e, const char* what) {
     return fail(LA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// ------------------------------------------------------------ no-alloc scratch
+// The segment workspace of la_chunk_fwd_noalloc: one copy per GPU, held for
+// the life of the process.  In host code `scratch` only names the symbol; its
+// device address (a different one on every GPU) comes from
+// hipGetSymbolAddress with that GPU current, and only that address is ever
+// handed to a kernel.
+static __device__ __align__(256) unsigned char scratch[LA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// Device address of `scratch` on the GPU that `s` belongs to (the current
+// GPU for the null stream), looked up once per GPU.
+la_status scratch_address(hipStream_t s, void** out) {
+    int dev = -1;
+    hipError_t e = s ? hipStreamGetDevice(s, &dev) : hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(LA_ERR_HIP, "device of the stream: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxScratchDevices)
+        return fail(LA_ERR_UNSUPPORTED, "device %d is beyond the %d the scratch table holds", dev,
+                    kMaxScratchDevices);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        int cur = -1;
+        e = hipGetDevice(&cur);
+        if (e != hipSuccess) return fail(LA_ERR_HIP, "current device: %s", hipGetErrorString(e));
+        if (cur != dev && (e = hipSetDevice(dev)) != hipSuccess)
+            return fail(LA_ERR_HIP, "select device %d: %s", dev, hipGetErrorString(e));
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        const hipError_t e2 = cur != dev ? hipSetDevice(cur) : hipSuccess;
+        if (e != hipSuccess || !ptr)
+            return fail(LA_ERR_HIP, "scratch address on device %d: %s", dev,
+                        hipGetErrorString(e != hipSuccess ? e : hipErrorInvalidSymbol));
+        if (e2 != hipSuccess)
+            return fail(LA_ERR_HIP, "restore device %d: %s", cur, hipGetErrorString(e2));
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return LA_OK;
+}
+
+// use_scratch: take the workspace from the static scratch array (after all
+// validation, so an invalid call makes no HIP call at all)
 la_status chunk_fwd_impl(const la_desc* d, const int* cu_seqlens, int max_seqlen, const void* q,
                          const void* k, const void* v, int gate_mode,
                          const float* gamma_or_log_alpha, const float* S0, const float* z0,
                          int chunk, const la_groupnorm* gn, void* out, float* S_final,
                          float* z_final, void* workspace, size_t ws_bytes, void* stream,
-                         void* states = nullptr) {
+                         void* states = nullptr, bool use_scratch = false) {
     // packed sequences plan their segments for the longest one
     const la_desc dp = plan_desc(d, cu_seqlens != nullptr, max_seqlen);
     la_status st;
@@ -293,6 +337,15 @@ la_status chunk_fwd_impl(const la_desc* d, const int* cu_seqlens, int max_seqlen
     const Plan pl = make_plan(&dp, chunk);
     const size_t seg_bytes = align16(workspace_bytes(&dp, pl));
     const size_t need = seg_bytes + (cu_seqlens ? order_bytes(d) : 0);
+    if (use_scratch && need > 0) {
+        if (need > LA_NOALLOC_SCRATCH_BYTES)
+            return fail(LA_ERR_UNSUPPORTED,
+                        "this shape needs %zu bytes of workspace, above the %u of the no-alloc scratch",
+                        need, (unsigned)LA_NOALLOC_SCRATCH_BYTES);
+        st = scratch_address(static_cast<hipStream_t>(stream), &workspace);
+        if (st != LA_OK) return st;
+        ws_bytes = LA_NOALLOC_SCRATCH_BYTES;
+    }
     if (need > 0) {
         if (!workspace) return fail(LA_ERR_INVALID, "workspace of %zu bytes is required", need);
         if (!aligned16(workspace)) return fail(LA_ERR_INVALID, "workspace must be 16-byte aligned");
@@ -395,6 +448,17 @@ la_status la_chunk_fwd(const la_desc* d, const void* q, const void* k, const voi
     if (st != LA_OK) return st;
     return chunk_fwd_impl(d, nullptr, 0, q, k, v, gate_mode, gamma_or_log_alpha, S0, z0, chunk,
                           nullptr, out, S_final, z_final, workspace, ws_bytes, stream);
+}
+
+la_status la_chunk_fwd_noalloc(const la_desc* d, const void* q, const void* k, const void* v,
+                               int gate_mode, const float* gamma_or_log_alpha, const float* S0,
+                               const float* z0, int chunk, void* out, float* S_final,
+                               float* z_final, void* stream) {
+    g_errmsg[0] = '\0';
+    const la_status st = check_desc(d);
+    if (st != LA_OK) return st;
+    return chunk_fwd_impl(d, nullptr, 0, q, k, v, gate_mode, gamma_or_log_alpha, S0, z0, chunk,
+                          nullptr, out, S_final, z_final, nullptr, 0, stream, nullptr, true);
 }
 
 la_status la_chunk_fwd_groupnorm(const la_desc* d, const void* q, const void* k, const void* v,

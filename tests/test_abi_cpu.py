@@ -92,6 +92,28 @@ def test_bf16_decode_takes_d16():
     assert api.la_delta_decode_step(d, A, A, A, A, A, A, None) == api.LA_ERR_UNSUPPORTED
 
 
+def _noalloc(desc, chunk=64, gate_mode=0, gate=None, q=A, out=A):
+    return api.la_chunk_fwd_noalloc(desc, q, A, A, gate_mode, gate, None, None, chunk, out,
+                                    None, None, None)
+
+
+def test_noalloc_validates_on_the_host():
+    # every argument check of la_chunk_fwd runs before the scratch is touched
+    assert _noalloc(_desc(B=0)) == api.LA_ERR_INVALID
+    assert _noalloc(_desc(), q=None) == api.LA_ERR_INVALID
+    assert _noalloc(_desc(), q=MIS) == api.LA_ERR_INVALID
+    assert _noalloc(_desc(), chunk=8) == api.LA_ERR_UNSUPPORTED
+    assert _noalloc(_desc(), gate_mode=api.LA_GATE_DIAG) == api.LA_ERR_INVALID
+
+
+def test_noalloc_rejects_a_workspace_beyond_the_scratch():
+    # 64 x 16 heads x 8 segments of 66 KB each at d = 128
+    d = _desc(B=64, H=16, L=512, dk=128, dv=128, segments=8)
+    assert api.la_chunk_fwd_workspace_bytes(d, 64) > api.LA_NOALLOC_SCRATCH_BYTES
+    assert _noalloc(d) == api.LA_ERR_UNSUPPORTED
+    assert "scratch" in api.la_last_error_message()
+
+
 @pytest.mark.parametrize("chunk", [0, 8, 48, 128])
 def test_chunk_rejects_unsupported_chunk(chunk):
     assert _chunk(_desc(), chunk=chunk) == api.LA_ERR_UNSUPPORTED
