@@ -228,7 +228,7 @@ def bench_prefill(args, torch, api, workloads, name=None):
     # a second pass over as many steps with per-kernel HIP events on the stream
     kern = {name: {"avg_us": us} for name, us in
             kernel_avgs(torch, api, step, args, flush,
-                        ("chunk_main", "chunk_state", "state_scan")).items()}
+                        ("chunk_main", "chunk_sub", "chunk_state", "state_scan")).items()}
     # the same step's launches captured once in a HIP graph and replayed
     # (what a caller that captures its step gets): same protocol, and the
     # replayed output must equal the direct call's bit for bit
@@ -387,7 +387,8 @@ def bench_varlen(args, torch, api, workloads, segments=0):
     flush = CacheFlush(torch, dev, not args.no_flush)
     times = time_steps(torch, step, args, flush)
     kern = {k: (round(v, 2) if v else None) for k, v in kernel_avgs(
-        torch, api, step, args, flush, ("seq_order", "chunk_main", "chunk_state", "state_scan")).items()}
+        torch, api, step, args, flush, ("seq_order", "chunk_main", "chunk_sub", "chunk_state",
+                                        "state_scan")).items()}
     # hand-off: one decode step of all N sequences from their prefill states
     qd, kd, vd, lad = workloads.decode_tokens(N, H, d, d, 1, seed=1, device=dev, gate=True)
     od = torch.empty((N, H, d), dtype=torch.bfloat16, device=dev)

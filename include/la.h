@@ -101,11 +101,17 @@ typedef struct la_desc {
  *   dk >= 32 (la_decode_step runs no matrix cores and takes bf16 at every
  *   dk; la_delta_decode_step is built for bf16 at dk >= 32).
  *   LA_GATE_GAMMA needs H <= LA_MAX_GAMMA_HEADS.
- *   LA_GATE_DIAG: the factorised in-chunk form multiplies by exp of the
- *   chunk-local cumulative log-gate measured from the chunk middle, so the
- *   per-channel sum of log_alpha over any half chunk must stay above about
- *   -80 (e.g. mean log_alpha >= -2.5 per token at chunk 64); beyond that
- *   fp32 overflows.  Use a smaller chunk for stronger gates.
+ *   LA_GATE_DIAG / LA_GATE_SCALAR, prefill (la_chunk_fwd and its
+ *   variants): the in-chunk form factorises the decay around a reference
+ *   inside the chunk.  A chunk whose log-gates would push those factors
+ *   past the fp32 range (a channel's log-gate sum over a wave's share of the
+ *   chunk below about -83 / (waves per half chunk)) is recomputed as
+ *   sequential 16-token sub-chunks, each factorised around its eighth
+ *   token, with every factor applied to the state at most one.  The result
+ *   stays exact (to rounding) while every 8 consecutive log-gates of a
+ *   channel sum to more than about -83, e.g. log_alpha >= -10 per token.
+ *   la_chunk_bwd factorises around the chunk middle only: the per-channel
+ *   log-gate sum over any half chunk (32 tokens) must stay above about -83.
  */
 
 /*
@@ -124,8 +130,8 @@ typedef struct la_desc {
  *                      returned).  They may alias S0 / z0 (in-place
  *                      resumption).  z_final must be NULL unless normalize.
  *   workspace          device scratch of at least
- *                      la_chunk_fwd_workspace_bytes(d, chunk) bytes (may be
- *                      NULL when that is 0); contents are clobbered
+ *                      la_chunk_fwd_workspace_bytes(d, chunk) bytes, 16-byte
+ *                      aligned; contents are clobbered
  *   stream             hipStream_t
  */
 la_status la_chunk_fwd(const la_desc* d, const void* q, const void* k,
@@ -238,9 +244,10 @@ la_status la_chunk_fwd_noalloc(const la_desc* d, const void* q, const void* k,
                                void* out, float* S_final, float* z_final,
                                void* stream);
 
-/* Bytes of device workspace la_chunk_fwd needs for this shape (segment
- * states, their decays and normaliser parts); 0 for a single segment.
- * Returns 0 for an invalid descriptor as well. */
+/* Bytes of device workspace la_chunk_fwd needs for this shape: the segment
+ * states, their decays and normaliser parts (several segments only) and one
+ * int32 per segment (under a vector gate, whether the segment was
+ * recomputed in sub-chunks).  Returns 0 for an invalid descriptor. */
 size_t la_chunk_fwd_workspace_bytes(const la_desc* d, int chunk);
 
 /* Number of segments la_chunk_fwd will run per (b,h) for this shape. */
@@ -386,7 +393,7 @@ int la_version(void);
  * la_profile_end() every kernel the library enqueues is bracketed by a pair
  * of HIP events recorded on the stream it is launched on.  la_profile_query
  * waits for those events and reports, for one kernel family
- * ("chunk_main", "chunk_state", "state_scan", "decode", "chunk_store",
+ * ("chunk_main", "chunk_sub", "chunk_state", "state_scan", "decode", "chunk_store",
  * "chunk_bwd", "delta_chunk", "delta_decode"), the number of
  * launches and their summed duration in milliseconds.  la_profile_begin
  * clears earlier records.  Event creation happens inside la_profile_begin /

@@ -109,6 +109,20 @@ struct ChunkCfg {
     // would only take registers from the rest of its loop; the state pass
     // has a shorter chunk and registers to spare, so it keeps two (bf16)
     static constexpr int PD = (SONLY && BF16) ? 2 : 1;
+    // fp32 main passes at d = 128 hold 64 registers per chunk of k, v, q and
+    // gates; prefetched a chunk ahead they stay live through every phase
+    // and the kernel spills heavily, so those load each chunk as its step
+    // begins instead
+    static constexpr bool PREFETCH = BF16 || SONLY || DK < 128;
+    // main pass under a vector gate (DIAG, SCALAR): chunks whose gates are
+    // too strong for the chunk-middle reference take the sub-chunk path
+    static constexpr bool VGM = (GATE == LA_GATE_DIAG || GATE == LA_GATE_SCALAR) && !SONLY;
+    static constexpr int TPW = C / NW;                // tokens per wave (consecutive)
+    // the chunk-middle factors stay below 2^LIM while each half chunk's
+    // log2-gate sum does; a wave votes for the sub-chunk path when a
+    // channel's sum over its tokens is below LIM / (waves per half)
+    static constexpr float LIM = 120.f;
+    static constexpr float WAVE_THR = -LIM / (NW >= 2 ? NW / 2 : 1);
     static_assert(DV % (16 * NW) == 0 && DK % 16 == 0 && C % 16 == 0, "tile shape");
     static_assert(!BF16 || DK % 32 == 0, "bf16 needs d_k >= 32");
     static_assert(NT % KCP == 0 && NT % VCP == 0, "channel-run mapping");
@@ -116,6 +130,8 @@ struct ChunkCfg {
                   "a transposed run stays within one 16-byte unit");
     static_assert(KTG >= 2 && KTG % 2 == 0 && KTPG >= 1 && VTPG >= 1, "token groups");
     static_assert(KTG * KTPG == C && VTG * VTPG == C, "token groups cover the chunk");
+    static_assert(8 % KTPG == 0 && C % NW == 0,
+                  "a thread's run stays in one 16-token block, ending at or before its eighth token");
 };
 
 template <class Cfg>
@@ -127,7 +143,25 @@ struct ChunkSmem {
     alignas(16) E kt[Cfg::DK][Cfg::CP];  // Kt, [i][swizzled s]
     alignas(16) E vt[Cfg::DV][Cfg::CP];  // V^T, [n][swizzled s]
     alignas(16) E p[CQ][Cfg::CP];        // masked scores, [t][swizzled s]
-    alignas(16) float tot[Cfg::NW][Cfg::DK];   // per-wave log2-gate sums
+    // per-wave log2-gate sums (a2), and the group norm's per-wave token sums
+    // (store phase of the main pass): live between different barriers
+    // vector gates, main pass, sub-chunk path: per 16-token block the
+    // in-wave prefix at its eighth and at its last token (the wave prefix is
+    // added on use), the state factors around its state term and the
+    // normaliser entering it; one vote per wave
+    static constexpr int TBV = Cfg::VGM ? Cfg::TB : 1;
+    static constexpr int DKV = Cfg::VGM ? Cfg::DK : 1;
+    // also the sub-chunk normaliser (after op1, before the store phase)
+    union {
+        alignas(16) float tot[Cfg::NW][Cfg::DK];
+        float2 gnp[Cfg::SONLY ? 1 : Cfg::NW][Cfg::SONLY ? 1 : Cfg::C];
+        float zs[TBV][DKV];
+    };
+    alignas(16) float bmid[TBV][DKV];
+    alignas(16) float bend[TBV][DKV];
+    alignas(16) float sa[TBV][DKV];
+    alignas(16) float sb[TBV][DKV];
+    int wslow[Cfg::VGM ? Cfg::NW : 1];
     alignas(16) float scale[Cfg::DK];    // per-row state factor applied this chunk
     alignas(16) float pre[Cfg::DK];      // this chunk's before/after factors
     alignas(16) float post[Cfg::DK];
@@ -135,7 +169,6 @@ struct ChunkSmem {
     float gpow[Cfg::C + 2];              // gamma^j
     float z[Cfg::DK];
     float den[Cfg::C];
-    float2 gnp[Cfg::SONLY ? 1 : Cfg::NW][Cfg::SONLY ? 1 : Cfg::C];  // group norm: per-wave token sums
 };
 
 // Position of logical channel l in row `row` of a q/k tile.  bf16 tiles
@@ -227,7 +260,14 @@ __device__ __forceinline__ void quad_transpose(float (&x)[4], int q) {
     }
 }
 
-template <class Cfg, bool ELU1, bool REV = false, bool STORE = false, bool EPI = false>
+// 12 wait states: more than any matrix-core result needs (10 for the fp32
+// operation) before another instruction may touch its registers.  The
+// compiler pads straight-line code itself; after a matrix product that a
+// branch can follow, the sub-chunk kernel pads explicitly, since padding has
+// been seen to go missing across such branches.
+__device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 3" ::: "memory"); }
+
+template <class Cfg, bool ELU1, bool REV = false, bool STORE = false, bool EPI = false, bool ROB = false>
 __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
     constexpr int DK = Cfg::DK, DV = Cfg::DV, C = Cfg::C, GATE = Cfg::GATE;
     constexpr int NB = Cfg::NB, MB = Cfg::MB, TB = Cfg::TB, NW = Cfg::NW;
@@ -291,6 +331,15 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
     const int c_begin = seg * p.cps;
     const int c_end = min(c_begin + p.cps, nchunks);
     const bool norm = p.normalize != 0;
+    // vector gates, main pass: the kernel without the sub-chunk path (ROB
+    // false) hands a segment with a chunk too strong for the chunk-middle
+    // reference to the one with it (ROB true), which runs only such segments
+    static_assert(!ROB || Cfg::VGM, "the sub-chunk kernel is a vector-gate main pass");
+    constexpr bool SUB = Cfg::VGM && ROB;
+    int* const seg_flag = Cfg::VGM ? p.slow_flags + ((size_t)bh * P + seg) : nullptr;
+    if constexpr (ROB) {
+        if (__builtin_amdgcn_readfirstlane(*seg_flag) == 0) return;
+    }
 
     const int kcp = tid % KCP, ktg = tid / KCP;
     const int vcp = tid % VCP, vtg = tid / VCP;
@@ -476,10 +525,14 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
 
     // one chunk (iteration ci): consumes rg, then refills it with the chunk
     // PD iterations ahead
-    auto step = [&](const int ci, ChunkRegs& rg) {
+    auto step = [&](const int ci, ChunkRegs& rg) -> bool {
         const int c = cof(ci);
         const int t0 = c * C;
         const int clen = min(C, L - t0);
+        if constexpr (!Cfg::PREFETCH) {
+            load_q(c);
+            load_chunk(c, rg);
+        }
 
         // ---- a2: chunk-local log2-gate sums.  Each thread sums its own run;
         // the token groups of one wave (lanes KCP apart hold the same channels
@@ -523,6 +576,25 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
             }
             __syncthreads();  // the previous chunk is done with every LDS tile
             if (lane < KCP) lds_store_words<CW>(&sm.tot[wave][CW * kcp], pack_run<false, CW>(wsum));
+            if constexpr (Cfg::VGM) {
+                // for the sub-chunk path: the in-wave prefix at each block's
+                // eighth and last token, left by the run that ends there
+                float ginc[CW];
+#pragma unroll
+                for (int i = 0; i < CW; ++i) ginc[i] = i < GC ? incl[i] : incl[0];
+                if constexpr (SUB) {
+                    const int e = ((ktg + 1) * KTPG) % 16;
+                    if (e == 8) lds_store_words<CW>(&sm.bmid[(ktg * KTPG) / 16][CW * kcp], pack_run<false, CW>(ginc));
+                    if (e == 0) lds_store_words<CW>(&sm.bend[(ktg * KTPG) / 16][CW * kcp], pack_run<false, CW>(ginc));
+                }
+                // this wave's vote: a channel's sum over the wave's tokens
+                // beyond what the chunk-middle factors allow
+                bool bad = false;
+#pragma unroll
+                for (int i = 0; i < GC; ++i) bad = bad || wsum[i] < Cfg::WAVE_THR;
+                const bool wbad = __builtin_amdgcn_ballot_w64(bad) != 0;
+                if (lane == 0) sm.wslow[wave] = wbad ? 1 : 0;
+            }
         }
         // NONE/GAMMA: the previous chunk is done with every LDS tile.
         // DIAG: the wave sums are visible.
@@ -533,6 +605,14 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
         float gref[CW], gtot[CW], goff[CW];
 #pragma unroll
         for (int i = 0; i < CW; ++i) gref[i] = gtot[i] = goff[i] = 0.f;
+        // sub-chunk path (a chunk whose gates are too strong for the
+        // chunk-middle reference): each 16-token block j is factorised around
+        // m_j, its cumulative log2-gate at its eighth token; e2 = e^{E_j - m_j}
+        // with E_j the value at its last token.  The fast path has e2 = 1.
+        int slow = 0;
+        float e2[CW];
+#pragma unroll
+        for (int i = 0; i < CW; ++i) e2[i] = 1.f;
         if constexpr (VG) {
             // all wave sums are read before any is used, so the reads overlap
             float x[NW][CW];
@@ -571,6 +651,62 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
                 goff[i] = wpre[i] + gexc[i];
                 if constexpr (NW == 1) gref[i] = gmid[i];
             }
+            if constexpr (Cfg::VGM) {
+                int f = 0;
+#pragma unroll
+                for (int w2 = 0; w2 < NW; ++w2) f |= sm.wslow[w2];
+                f = __builtin_amdgcn_readfirstlane(f);
+                if constexpr (SUB) slow = f;
+                else if (f) return false;   // the sub-chunk kernel takes the segment
+                if (SUB && slow) {
+                    // references of this run's block j: m_j, E_j and the
+                    // block's start B_j = E_{j-1} (0 for the first), each a
+                    // fixed sum of wave totals plus an in-wave prefix
+                    const int jown = (ktg * KTPG) / 16;
+                    float m[CW], e[CW], b0[CW], run[CW];
+#pragma unroll
+                    for (int i = 0; i < CW; ++i) m[i] = e[i] = b0[i] = run[i] = 0.f;
+                    // run = total of the waves before w2; a block's eighth
+                    // and last token fall in known waves
+#pragma unroll
+                    for (int w2 = 0; w2 < NW; ++w2) {
+#pragma unroll
+                        for (int jb = 0; jb < TB; ++jb) {
+                            if ((16 * jb + 7) / Cfg::TPW == w2 && jb == jown) {
+                                const float* mv = &sm.bmid[jb][CW * kcp];
+#pragma unroll
+                                for (int i = 0; i < CW; ++i) m[i] = run[i] + mv[i];
+                            }
+                            if ((16 * jb + 15) / Cfg::TPW == w2 && (jb == jown || jb + 1 == jown)) {
+                                const float* ev = &sm.bend[jb][CW * kcp];
+#pragma unroll
+                                for (int i = 0; i < CW; ++i) {
+                                    const float ej = run[i] + ev[i];
+                                    if (jb == jown) e[i] = ej;
+                                    else b0[i] = ej;
+                                }
+                            }
+                        }
+#pragma unroll
+                        for (int i = 0; i < CW; ++i) run[i] += x[w2][i];
+                    }
+#pragma unroll
+                    for (int i = 0; i < CW; ++i) {
+                        gref[i] = m[i];
+                        e2[i] = __builtin_amdgcn_exp2f(e[i] - m[i]);
+                    }
+                    // the run at a block's start leaves the block's state
+                    // factors: e^{m_j - B_j} before its state term and
+                    // e^{E_j - m_j} after it (both at most one)
+                    if ((ktg * KTPG) % 16 == 0) {
+                        float fa[CW];
+#pragma unroll
+                        for (int i = 0; i < CW; ++i) fa[i] = __builtin_amdgcn_exp2f(m[i] - b0[i]);
+                        lds_store_words<CW>(&sm.sa[jown][CW * kcp], pack_run<false, CW>(fa));
+                        lds_store_words<CW>(&sm.sb[jown][CW * kcp], pack_run<false, CW>(e2));
+                    }
+                }
+            }
         }
         const float egam = seg_g;   // gamma^(tokens after this chunk), backward walk
         if constexpr (GATE == LA_GATE_GAMMA) seg_g *= sm.gpow[clen];
@@ -602,7 +738,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
                     const float d = bcur[0] - gref[0];
                     sq = __builtin_amdgcn_exp2f(d);
                     sk = __builtin_amdgcn_exp2f(-d);
-                    st = REV ? sq : sk;
+                    st = REV ? sq : sk * e2[0];
                     if constexpr (BACKAGG) st = __builtin_amdgcn_exp2f(gtot[0] - bcur[0] + eacc[0]);
                 }
 #pragma unroll
@@ -620,7 +756,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
                         const float d = bcur[i] - gref[i];
                         fq = __builtin_amdgcn_exp2f(d);
                         fk = __builtin_amdgcn_exp2f(-d);
-                        ft = REV ? fq : fk;
+                        ft = REV ? fq : fk * e2[i];
                         // backward walk: k e^{B - b} times the decay after the chunk
                         if constexpr (BACKAGG) ft = __builtin_amdgcn_exp2f(gtot[i] - bcur[i] + eacc[i]);
                     }
@@ -668,9 +804,14 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
                     for (int i = 0; i < CW; ++i) {
                         const int row = CW * kcp + i;
                         sm.segsum[row] += gtot[i];
+                        // the sub-chunk path keeps the true state between its
+                        // blocks (it applies the previous chunk's after-factor
+                        // only)
                         if constexpr (!BACKAGG) {
-                            pr[i] = __builtin_amdgcn_exp2f(REV ? gtot[i] - gref[i] : gref[i]);
-                            po[i] = __builtin_amdgcn_exp2f(REV ? gref[i] : gtot[i] - gref[i]);
+                            if (!(SUB && slow)) {
+                                pr[i] = __builtin_amdgcn_exp2f(REV ? gtot[i] - gref[i] : gref[i]);
+                                po[i] = __builtin_amdgcn_exp2f(REV ? gref[i] : gtot[i] - gref[i]);
+                            }
                         }
                         sc[i] = sm.post[row] * pr[i];
                     }
@@ -690,6 +831,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
         constexpr int NTILE = TB * (TB + 1) / 2;
         const bool late = !SONLY && NTILE % NW != 0 && wave_u >= NTILE % NW;
         auto refill = [&]() {
+            if constexpr (!Cfg::PREFETCH) return;
             if (ci + 1 < c_end) load_q(cof(ci + 1));
             if (ci + Cfg::PD < c_end) load_chunk(cof(ci + Cfg::PD), rg);
         };
@@ -699,38 +841,85 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
         // ---- op1: P^T = Kh Qh^T on the lower-triangular tiles; each lane
         // gets four consecutive s of one row t and writes them packed
         if constexpr (!SONLY) {
-            int idx = 0;
+            auto score_tile = [&](int tb, int sb) {
+                f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+                const int rs = 16 * sb + r, rt = 16 * tb + r;
 #pragma unroll
-            for (int tb = 0; tb < TB; ++tb) {
+                for (int kk = 0; kk < DK / MK; ++kk) {
+                    const int pp = kk * MK + KPL * g;  // this lane's k-slots (permuted order)
+                    const Frag a = T::load(&sm.k[rs][qk_phys<Cfg>(rs, pp)]);
+                    const Frag b = T::load(&sm.q[rt][qk_phys<Cfg>(rt, pp)]);
+                    acc = T::mma(a, b, acc);
+                }
+                float x[4];
 #pragma unroll
-                for (int sb = 0; sb <= tb; ++sb, ++idx) {
-                    if (idx % NW != wave) continue;
-                    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-                    const int rs = 16 * sb + r, rt = 16 * tb + r;
+                for (int i = 0; i < 4; ++i) {
+                    const int s = 16 * sb + 4 * g + i;
+                    float val = acc[i];
+                    if (s > rt) val = 0.f;
+                    else if constexpr (GATE == LA_GATE_GAMMA) val *= sm.gpow[rt - s];
+                    x[i] = val;
+                }
+                store_run<BF16, 4>(&sm.p[rt][p_pos<Cfg>(rt, 16 * sb + 4 * g)], x);
+                if constexpr (SUB) mfma_drain();
+            };
+            if (!(SUB && slow)) {
+                int idx = 0;
 #pragma unroll
-                    for (int kk = 0; kk < DK / MK; ++kk) {
-                        const int pp = kk * MK + KPL * g;  // this lane's k-slots (permuted order)
-                        const Frag a = T::load(&sm.k[rs][qk_phys<Cfg>(rs, pp)]);
-                        const Frag b = T::load(&sm.q[rt][qk_phys<Cfg>(rt, pp)]);
-                        acc = T::mma(a, b, acc);
+                for (int tb = 0; tb < TB; ++tb) {
+#pragma unroll
+                    for (int sb = 0; sb <= tb; ++sb, ++idx) {
+                        if (idx % NW != wave) continue;
+                        score_tile(tb, sb);
                     }
-                    float x[4];
+                }
+            } else {
+                // sub-chunk path: the diagonal tiles only; a bf16 contraction
+                // over s spans two blocks, so an odd block's row also reads
+                // the tile to its left, which is cleared here
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int s = 16 * sb + 4 * g + i;
-                        float val = acc[i];
-                        if (s > rt) val = 0.f;
-                        else if constexpr (GATE == LA_GATE_GAMMA) val *= sm.gpow[rt - s];
-                        x[i] = val;
+                for (int j = 0; j < TB; ++j) {
+                    if (j % NW != wave) continue;
+                    score_tile(j, j);
+                    if (BF16 && (j & 1)) {
+                        const float z4[4] = {0.f, 0.f, 0.f, 0.f};
+                        const int rt = 16 * j + r;
+                        store_run<BF16, 4>(&sm.p[rt][p_pos<Cfg>(rt, 16 * (j - 1) + 4 * g)], z4);
                     }
-                    store_run<BF16, 4>(&sm.p[rt][p_pos<Cfg>(rt, 16 * sb + 4 * g)], x);
                 }
             }
             if (late) refill();
             __syncthreads();
 
             // ---- a4: normaliser of each row, read with the state before this chunk
-            if (norm) {
+            if (norm && SUB && slow) {
+                // sub-chunk path: z entering each block (times the block's
+                // before-factor, as its state term reads the state), then
+                // each row from its block's diagonal tile
+                if (tid < DK) {
+                    float zz = sm.z[tid];
+#pragma unroll
+                    for (int j = 0; j < TB; ++j) {
+                        const float fa = sm.sa[j][tid], fb = sm.sb[j][tid];
+                        sm.zs[j][tid] = fa * zz;
+                        float cs = 0.f;
+                        for (int s2 = 16 * j; s2 < 16 * j + 16; ++s2)
+                            cs += T::tof(sm.kt[tid][tr_pos<Cfg>(tid, s2)]);
+                        zz = fb * fa * zz + cs;
+                    }
+                    sm.z[tid] = zz;
+                }
+                __syncthreads();
+                if (tid < C) {
+                    const int t = tid, j = t / 16;
+                    float rsum = 0.f;
+                    for (int s2 = 16 * j; s2 <= t; ++s2) rsum += T::tof(sm.p[t][p_pos<Cfg>(t, s2)]);
+                    float dq = 0.f;
+                    for (int i = 0; i < DK; ++i) dq += T::tof(sm.q[t][qk_pos<Cfg>(t, i)]) * sm.zs[j][i];
+                    sm.den[t] = dq + rsum;
+                }
+                __syncthreads();
+            } else if (norm) {
                 if (tid < C) {
                     const int t = tid;
                     float rsum = 0.f;
@@ -748,7 +937,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
             }
         }
         // z <- post * (pre * z + sum_s Kt[:, s])  (each thread its own channel)
-        if (norm && tid < DK) {
+        if (norm && !(SUB && slow) && tid < DK) {
             float cs = 0.f;
             for (int s = 0; s < C; ++s) cs += T::tof(sm.kt[tid][tr_pos<Cfg>(tid, s)]);
             sm.z[tid] = sm.post[tid] * (sm.pre[tid] * sm.z[tid] + cs);
@@ -773,61 +962,188 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
             for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
                 for (int tb = 0; tb < TB; ++tb) accO[nb][tb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-            if constexpr (BF16) {
-#pragma unroll
-                for (int k2 = 0; k2 < DK / 32; ++k2) {
-                    Frag as[NB];
-#pragma unroll
-                    for (int nb = 0; nb < NB; ++nb) {
-                        const float x[8] = {accS[2 * k2][nb][0], accS[2 * k2][nb][1],
-                                            accS[2 * k2][nb][2], accS[2 * k2][nb][3],
-                                            accS[2 * k2 + 1][nb][0], accS[2 * k2 + 1][nb][1],
-                                            accS[2 * k2 + 1][nb][2], accS[2 * k2 + 1][nb][3]};
-                        as[nb] = T::from8(x);
+            if (!(SUB && slow)) {
+                if constexpr (BF16) {
+    #pragma unroll
+                    for (int k2 = 0; k2 < DK / 32; ++k2) {
+                        Frag as[NB];
+    #pragma unroll
+                        for (int nb = 0; nb < NB; ++nb) {
+                            const float x[8] = {accS[2 * k2][nb][0], accS[2 * k2][nb][1],
+                                                accS[2 * k2][nb][2], accS[2 * k2][nb][3],
+                                                accS[2 * k2 + 1][nb][0], accS[2 * k2 + 1][nb][1],
+                                                accS[2 * k2 + 1][nb][2], accS[2 * k2 + 1][nb][3]};
+                            as[nb] = T::from8(x);
+                        }
+    #pragma unroll
+                        for (int tb = 0; tb < TB; ++tb) {
+                            const int t = 16 * tb + r;
+                            // one unit of the permuted layout = state rows 4g.. and 16+4g..
+                            const Frag b = T::load(&sm.q[t][qk_phys<Cfg>(t, 32 * k2 + 8 * g)]);
+    #pragma unroll
+                            for (int nb = 0; nb < NB; ++nb) accO[nb][tb] = T::mma(as[nb], b, accO[nb][tb]);
+                        }
                     }
-#pragma unroll
+                } else {
+    #pragma unroll
+                    for (int mb = 0; mb < MB; ++mb)
+    #pragma unroll
+                        for (int i = 0; i < 4; ++i)
+    #pragma unroll
+                            for (int tb = 0; tb < TB; ++tb) {
+                                const int t = 16 * tb + r;
+                                const Frag b = sm.q[t][qk_pos<Cfg>(t, 16 * mb + 4 * g + i)];
+    #pragma unroll
+                                for (int nb = 0; nb < NB; ++nb)
+                                    accO[nb][tb] = T::mma(accS[mb][nb][i], b, accO[nb][tb]);
+                            }
+                }
+                if constexpr (GATE == LA_GATE_GAMMA) {
+    #pragma unroll
                     for (int tb = 0; tb < TB; ++tb) {
-                        const int t = 16 * tb + r;
-                        // one unit of the permuted layout = state rows 4g.. and 16+4g..
-                        const Frag b = T::load(&sm.q[t][qk_phys<Cfg>(t, 32 * k2 + 8 * g)]);
-#pragma unroll
-                        for (int nb = 0; nb < NB; ++nb) accO[nb][tb] = T::mma(as[nb], b, accO[nb][tb]);
+                        const float f = sm.gpow[16 * tb + r + 1];
+    #pragma unroll
+                        for (int nb = 0; nb < NB; ++nb) accO[nb][tb] *= f;
+                    }
+                }
+    #pragma unroll
+                for (int tb = 0; tb < TB; ++tb) {
+                    const int t = 16 * tb + r;
+    #pragma unroll
+                    for (int kk = 0; kk <= (16 * tb + 15) / MK; ++kk) {
+                        const Frag b = T::load(&sm.p[t][p_pos<Cfg>(t, kk * MK + KPL * g)]);
+    #pragma unroll
+                        for (int nb = 0; nb < NB; ++nb) accO[nb][tb] = T::mma(vf[kk][nb], b, accO[nb][tb]);
                     }
                 }
             } else {
+                // sub-chunk path: block by block, the true state S_j taken to
+                // the block's reference (times e^{m_j - B_j}), its rows' state
+                // term and in-block scores, stored, then S_{j+1} = e^{E_j - m_j}
+                // (...) + Kt_j^T V_j over the block's own tokens.  A compact
+                // loop: one block's accumulators live at a time and the value
+                // operands are read again from LDS.
+                auto vfrag = [&](int kk, int nb) {
+                    const int row = colbase + 16 * nb + r;
+                    return T::load(&sm.vt[row][tr_pos<Cfg>(row, kk * MK + KPL * g)]);
+                };
+#pragma unroll 1
+                for (int j = 0; j < TB; ++j) {
+                    const int t = 16 * j + r;
+                    f32x4_t acc[NB];
 #pragma unroll
-                for (int mb = 0; mb < MB; ++mb)
+                    for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                    scale_rows<Cfg>(accS, sm.sa[j], g);
+                    if constexpr (BF16) {
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
+                        for (int k2 = 0; k2 < DK / 32; ++k2) {
+                            const Frag b = T::load(&sm.q[t][qk_phys<Cfg>(t, 32 * k2 + 8 * g)]);
 #pragma unroll
-                        for (int tb = 0; tb < TB; ++tb) {
-                            const int t = 16 * tb + r;
-                            const Frag b = sm.q[t][qk_pos<Cfg>(t, 16 * mb + 4 * g + i)];
-#pragma unroll
-                            for (int nb = 0; nb < NB; ++nb)
-                                accO[nb][tb] = T::mma(accS[mb][nb][i], b, accO[nb][tb]);
+                            for (int nb = 0; nb < NB; ++nb) {
+                                const float x[8] = {accS[2 * k2][nb][0], accS[2 * k2][nb][1],
+                                                    accS[2 * k2][nb][2], accS[2 * k2][nb][3],
+                                                    accS[2 * k2 + 1][nb][0], accS[2 * k2 + 1][nb][1],
+                                                    accS[2 * k2 + 1][nb][2], accS[2 * k2 + 1][nb][3]};
+                                acc[nb] = T::mma(T::from8(x), b, acc[nb]);
+                            }
                         }
-            }
-            if constexpr (GATE == LA_GATE_GAMMA) {
+                    } else {
 #pragma unroll
-                for (int tb = 0; tb < TB; ++tb) {
-                    const float f = sm.gpow[16 * tb + r + 1];
+                        for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-                    for (int nb = 0; nb < NB; ++nb) accO[nb][tb] *= f;
-                }
-            }
+                            for (int i = 0; i < 4; ++i) {
+                                const Frag b = sm.q[t][qk_pos<Cfg>(t, 16 * mb + 4 * g + i)];
 #pragma unroll
-            for (int tb = 0; tb < TB; ++tb) {
-                const int t = 16 * tb + r;
+                                for (int nb = 0; nb < NB; ++nb) acc[nb] = T::mma(accS[mb][nb][i], b, acc[nb]);
+                            }
+                    }
+                    // the k-blocks of the block's 16 tokens (one for bf16)
+                    constexpr int KPB = 16 / MK > 0 ? 16 / MK : 1;
 #pragma unroll
-                for (int kk = 0; kk <= (16 * tb + 15) / MK; ++kk) {
-                    const Frag b = T::load(&sm.p[t][p_pos<Cfg>(t, kk * MK + KPL * g)]);
+                    for (int u = 0; u < KPB; ++u) {
+                        const int kk = (16 * j) / MK + u;
+                        const Frag b = T::load(&sm.p[t][p_pos<Cfg>(t, kk * MK + KPL * g)]);
 #pragma unroll
-                    for (int nb = 0; nb < NB; ++nb) accO[nb][tb] = T::mma(vf[kk][nb], b, accO[nb][tb]);
+                        for (int nb = 0; nb < NB; ++nb) acc[nb] = T::mma(vfrag(kk, nb), b, acc[nb]);
+                    }
+                    mfma_drain();
+                    // the block's rows (group norm: statistics of these rows
+                    // across the waves)
+                    const float inv = __builtin_amdgcn_rcpf(sm.den[t]);
+                    float gmean = 0.f, grstd = 1.f;
+                    if constexpr (EPI) {
+                        float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+                        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                const float o = acc[nb][i] * inv;
+                                s1 += o;
+                                s2 += o * o;
+                            }
+                        s1 += lane_read(s1, lane ^ 16);
+                        s2 += lane_read(s2, lane ^ 16);
+                        s1 += lane_read(s1, lane ^ 32);
+                        s2 += lane_read(s2, lane ^ 32);
+                        if (g == 0) sm.gnp[wave][t] = make_float2(s1, s2);
+                        __syncthreads();
+                        s1 = s2 = 0.f;
+#pragma unroll
+                        for (int w2 = 0; w2 < NW; ++w2) {
+                            const float2 x = sm.gnp[w2][t];
+                            s1 += x.x;
+                            s2 += x.y;
+                        }
+                        gmean = s1 * (1.0f / DV);
+                        grstd = __builtin_amdgcn_rsqf(fmaxf(s2 * (1.0f / DV) - gmean * gmean, 0.f) + p.gn_eps);
+                        __syncthreads();   // every wave has read this block's sums
+                    }
+#pragma unroll
+                    for (int nb = 0; nb < NB; ++nb) {
+                        const uint32_t off = ((uint32_t)(t0 + t) * DV + colbase + 16 * nb + 4 * g) * ES;
+                        f32x4_t o = acc[nb] * inv;
+                        if constexpr (EPI) {
+                            const Words<OW> gw = buf_load_words<OW>(rgate, off);
+                            const bool gated = p.gn_gate != nullptr;
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                const float y = (o[i] - gmean) * grstd * gnw[nb][i] + gnb[nb][i];
+                                const float ga = run_elem<BF16>(gw, i);
+                                const float sw = ga * __builtin_amdgcn_rcpf(1.0f + __expf(-ga));
+                                o[i] = gated ? y * sw : y;
+                            }
+                        }
+                        if constexpr (BF16) {
+                            const u32x2_t w = {pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3])};
+                            __builtin_amdgcn_raw_buffer_store_b64(w, ro, off, 0, 0);
+                        } else {
+                            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, o), ro, off, 0, 0);
+                        }
+                    }
+                    scale_rows<Cfg>(accS, sm.sb[j], g);
+#pragma unroll
+                    for (int mb = 0; mb < MB; ++mb) {
+                        const int row = 16 * mb + r;
+#pragma unroll
+                        for (int u = 0; u < KPB; ++u) {
+                            const int kk = (16 * j) / MK + u;
+                            Frag a = T::load(&sm.kt[row][tr_pos<Cfg>(row, kk * MK + KPL * g)]);
+                            // a bf16 contraction spans blocks 2kk and 2kk+1
+                            // (lane groups 0-1 and 2-3): keep block j's half
+                            if constexpr (MK > 16) {
+                                if ((g >> 1) != (j & 1)) a = __builtin_bit_cast(Frag, make_uint4(0u, 0u, 0u, 0u));
+                            }
+#pragma unroll
+                            for (int nb = 0; nb < NB; ++nb) accS[mb][nb] = T::mma(a, vfrag(kk, nb), accS[mb][nb]);
+                        }
+                    }
+                    mfma_drain();
                 }
             }
             // ---- store: lane (r, g) holds 4 consecutive columns of token row t
+            // (the sub-chunk path has stored its rows block by block)
             float gmean[EPI ? TB : 1], grstd[EPI ? TB : 1];
+            if (!(SUB && slow)) {
             if constexpr (EPI) {
                 // group norm statistics of each token's d_v outputs: the
                 // lane's 4 NB values, the 4 lanes of the token in this wave,
@@ -892,22 +1208,25 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
                     }
                 }
             }
+            }
         }
 
         if constexpr (EPI) {
             if (ci + 1 < c_end) load_gate(cof(ci + 1));
         }
 
-        // ---- op3: state update
+        // ---- op3: state update (the sub-chunk path has done it block by block)
         if constexpr (GATE == LA_GATE_GAMMA) scale_rows<Cfg>(accS, sm.scale, g);
+        if (!(SUB && slow)) {
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-            const int row = 16 * mb + r;
+            for (int mb = 0; mb < MB; ++mb) {
+                const int row = 16 * mb + r;
 #pragma unroll
-            for (int kk = 0; kk < CP / MK; ++kk) {
-                const Frag a = T::load(&sm.kt[row][tr_pos<Cfg>(row, kk * MK + KPL * g)]);
+                for (int kk = 0; kk < CP / MK; ++kk) {
+                    const Frag a = T::load(&sm.kt[row][tr_pos<Cfg>(row, kk * MK + KPL * g)]);
 #pragma unroll
-                for (int nb = 0; nb < NB; ++nb) accS[mb][nb] = T::mma(a, vf[kk][nb], accS[mb][nb]);
+                    for (int nb = 0; nb < NB; ++nb) accS[mb][nb] = T::mma(a, vf[kk][nb], accS[mb][nb]);
+                }
             }
         }
         // ---- the state at the next chunk boundary (the entry state of the
@@ -916,6 +1235,8 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
             const int nxt = c + 1;
             if (nxt < c_end || seg == P - 1) store_state(nxt);
         }
+        if constexpr (SUB) mfma_drain();   // the loop's back-edge follows
+        return true;
     };
     if constexpr (STORE) {
         // the segment's entry state is the first boundary it owns (the
@@ -926,7 +1247,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
         }
     }
     {
-        if (c_begin < c_end) load_q(cof(c_begin));
+        if (Cfg::PREFETCH && c_begin < c_end) load_q(cof(c_begin));
         if (c_begin < c_end) load_gate(cof(c_begin));
         if constexpr (Cfg::PD == 2) {
             ChunkRegs ra, rb;
@@ -938,8 +1259,18 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
             }
         } else {
             ChunkRegs ra;
-            if (c_begin < c_end) load_chunk(cof(c_begin), ra);
-            for (int ci = c_begin; ci < c_end; ++ci) step(ci, ra);
+            if (Cfg::PREFETCH && c_begin < c_end) load_chunk(cof(c_begin), ra);
+            bool done = true;
+            for (int ci = c_begin; ci < c_end; ++ci)
+                if (!step(ci, ra)) {
+                    done = false;
+                    break;
+                }
+            if constexpr (Cfg::VGM && !ROB) {
+                // every segment records whether it was handed over
+                if (tid == 0) *seg_flag = done ? 0 : 1;
+                if (!done) return;
+            }
         }
     }
     // DIAG: the last chunk's after-factor
@@ -1066,22 +1397,31 @@ struct ChunkWaves {
 // The backward passes exist for the backward's chunk length only.
 template <int D, bool BF, int NWV = ChunkWaves<D>::value>
 hipError_t launch_chunk_dt(const ChunkParams& p, int chunk, int gate, int pass, hipStream_t s,
-                           int nblocks) {
-#define LA_CHUNK_LAUNCH(CC, GG, SO, RV, ST, EP)                                            \
+                           int nblocks, bool robust) {
+#define LA_CHUNK_LAUNCH(CC, GG, SO, RV, ST, EP, RB)                                        \
     do {                                                                                   \
         using Cfg = ChunkCfg<D, D, CC, BF, GG, SO, NWV>;                                   \
         if (p.phi_elu1)                                                                    \
-            hipLaunchKernelGGL((chunk_kernel<Cfg, true, RV, ST, EP>), dim3(nblocks), dim3(Cfg::NT), 0, s, p); \
+            hipLaunchKernelGGL((chunk_kernel<Cfg, true, RV, ST, EP, RB>), dim3(nblocks), dim3(Cfg::NT), 0, s, p); \
         else                                                                               \
-            hipLaunchKernelGGL((chunk_kernel<Cfg, false, RV, ST, EP>), dim3(nblocks), dim3(Cfg::NT), 0, s, p); \
+            hipLaunchKernelGGL((chunk_kernel<Cfg, false, RV, ST, EP, RB>), dim3(nblocks), dim3(Cfg::NT), 0, s, p); \
         return hipGetLastError();                                                          \
     } while (0)
-#define LA_CHUNK_GATES_EP(CC, SO, RV, ST, EP)                                \
-    do {                                                                     \
-        if (gate == LA_GATE_NONE) LA_CHUNK_LAUNCH(CC, 0, SO, RV, ST, EP);    \
-        if (gate == LA_GATE_GAMMA) LA_CHUNK_LAUNCH(CC, 1, SO, RV, ST, EP);   \
-        if (gate == LA_GATE_DIAG) LA_CHUNK_LAUNCH(CC, 2, SO, RV, ST, EP);    \
-        if (gate == LA_GATE_SCALAR) LA_CHUNK_LAUNCH(CC, 3, SO, RV, ST, EP);  \
+// main passes under a vector gate exist twice: without and with the
+// sub-chunk path (robust)
+#define LA_CHUNK_GATES_EP(CC, SO, RV, ST, EP)                                           \
+    do {                                                                                \
+        if (gate == LA_GATE_NONE) LA_CHUNK_LAUNCH(CC, 0, SO, RV, ST, EP, false);        \
+        if (gate == LA_GATE_GAMMA) LA_CHUNK_LAUNCH(CC, 1, SO, RV, ST, EP, false);       \
+        if constexpr (SO) {                                                             \
+            if (gate == LA_GATE_DIAG) LA_CHUNK_LAUNCH(CC, 2, SO, RV, ST, EP, false);    \
+            if (gate == LA_GATE_SCALAR) LA_CHUNK_LAUNCH(CC, 3, SO, RV, ST, EP, false);  \
+        } else {                                                                        \
+            if (gate == LA_GATE_DIAG && !robust) LA_CHUNK_LAUNCH(CC, 2, SO, RV, ST, EP, false); \
+            if (gate == LA_GATE_DIAG && robust) LA_CHUNK_LAUNCH(CC, 2, SO, RV, ST, EP, true);   \
+            if (gate == LA_GATE_SCALAR && !robust) LA_CHUNK_LAUNCH(CC, 3, SO, RV, ST, EP, false); \
+            if (gate == LA_GATE_SCALAR && robust) LA_CHUNK_LAUNCH(CC, 3, SO, RV, ST, EP, true);   \
+        }                                                                               \
     } while (0)
 #define LA_CHUNK_GATES(CC, SO, RV, ST) LA_CHUNK_GATES_EP(CC, SO, RV, ST, false)
 #define LA_CHUNK_FWD(CC)                                                 \
@@ -1109,8 +1449,8 @@ hipError_t launch_chunk_dt(const ChunkParams& p, int chunk, int gate, int pass, 
 // One explicit (d, dtype) instantiation per translation unit.
 #define LA_DEFINE_CHUNK_LAUNCHER(NAME, D, BF)                                                      \
     hipError_t NAME(const ChunkParams& p, int chunk, int gate, int pass, hipStream_t s,            \
-                    int nblocks) {                                                                 \
-        return launch_chunk_dt<D, BF>(p, chunk, gate, pass, s, nblocks);                           \
+                    int nblocks, bool robust) {                                                    \
+        return launch_chunk_dt<D, BF>(p, chunk, gate, pass, s, nblocks, robust);                   \
     }
 
 }  // namespace la

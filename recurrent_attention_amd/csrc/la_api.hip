@@ -49,15 +49,24 @@ Plan make_plan(const la_desc* d, int chunk) {
     return pl;
 }
 
-size_t workspace_bytes(const la_desc* d, const Plan& pl) {
+size_t align16(size_t n) { return (n + 15) & ~(size_t)15; }
+
+// Segment slots (states, decays, normaliser parts; several segments only),
+// rounded up to 16 bytes.
+size_t slot_bytes(const la_desc* d, const Plan& pl) {
     if (pl.P <= 1) return 0;
     const size_t slots = (size_t)d->B * d->H * pl.P;
-    return slots * ((size_t)d->dk * d->dv + 2 * (size_t)d->dk) * sizeof(float);
+    return align16(slots * ((size_t)d->dk * d->dv + 2 * (size_t)d->dk) * sizeof(float));
 }
+// One int32 per (b,h) segment: under a vector gate, whether the main pass
+// handed the segment to the sub-chunk kernel.
+size_t flag_bytes(const la_desc* d, const Plan& pl) {
+    return align16((size_t)d->B * d->H * pl.P * sizeof(int));
+}
+size_t workspace_bytes(const la_desc* d, const Plan& pl) { return slot_bytes(d, pl) + flag_bytes(d, pl); }
 
-// Packed sequences: after the segment slots, the launch order of the
-// sequences (int32 [B], rounded up to 16 bytes).
-size_t align16(size_t n) { return (n + 15) & ~(size_t)15; }
+// Packed sequences: after the segment slots and flags, the launch order of
+// the sequences (int32 [B], rounded up to 16 bytes).
 size_t order_bytes(const la_desc* d) { return align16((size_t)d->B * sizeof(int)); }
 
 bool supported_d(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
@@ -132,7 +141,7 @@ std::vector<hipEvent_t> g_event_pool;
 
 const char* kKernelNames[la::K_COUNT] = {"chunk_main", "chunk_state", "state_scan", "decode",
                                          "chunk_store", "chunk_bwd", "delta_chunk",
-                                         "delta_decode", "seq_order"};
+                                         "delta_decode", "seq_order", "chunk_sub"};
 
 hipEvent_t take_event() {
     if (!g_event_pool.empty()) {
@@ -166,16 +175,16 @@ hipError_t timed_launch(int kernel, hipStream_t s, F&& launch) {
 }
 
 hipError_t chunk_launch(const la_desc* d, const la::ChunkParams& p, int chunk, int gate, int pass,
-                        hipStream_t s, int nblocks) {
+                        hipStream_t s, int nblocks, bool robust = false) {
     const bool bf16 = d->dtype == LA_BF16;
     switch (d->dk) {
-        case 16: return la::launch_chunk_f32_d16(p, chunk, gate, pass, s, nblocks);
-        case 32: return bf16 ? la::launch_chunk_bf16_d32(p, chunk, gate, pass, s, nblocks)
-                             : la::launch_chunk_f32_d32(p, chunk, gate, pass, s, nblocks);
-        case 64: return bf16 ? la::launch_chunk_bf16_d64(p, chunk, gate, pass, s, nblocks)
-                             : la::launch_chunk_f32_d64(p, chunk, gate, pass, s, nblocks);
-        default: return bf16 ? la::launch_chunk_bf16_d128(p, chunk, gate, pass, s, nblocks)
-                             : la::launch_chunk_f32_d128(p, chunk, gate, pass, s, nblocks);
+        case 16: return la::launch_chunk_f32_d16(p, chunk, gate, pass, s, nblocks, robust);
+        case 32: return bf16 ? la::launch_chunk_bf16_d32(p, chunk, gate, pass, s, nblocks, robust)
+                             : la::launch_chunk_f32_d32(p, chunk, gate, pass, s, nblocks, robust);
+        case 64: return bf16 ? la::launch_chunk_bf16_d64(p, chunk, gate, pass, s, nblocks, robust)
+                             : la::launch_chunk_f32_d64(p, chunk, gate, pass, s, nblocks, robust);
+        default: return bf16 ? la::launch_chunk_bf16_d128(p, chunk, gate, pass, s, nblocks, robust)
+                             : la::launch_chunk_f32_d128(p, chunk, gate, pass, s, nblocks, robust);
     }
 }
 
@@ -335,8 +344,10 @@ la_status chunk_fwd_impl(const la_desc* d, const int* cu_seqlens, int max_seqlen
     if (st != LA_OK) return st;
 
     const Plan pl = make_plan(&dp, chunk);
-    const size_t seg_bytes = align16(workspace_bytes(&dp, pl));
-    const size_t need = seg_bytes + (cu_seqlens ? order_bytes(d) : 0);
+    const size_t seg_bytes = slot_bytes(&dp, pl);
+    const size_t flags_at = seg_bytes;
+    const size_t order_at = seg_bytes + flag_bytes(&dp, pl);
+    const size_t need = order_at + (cu_seqlens ? order_bytes(d) : 0);
     if (use_scratch && need > 0) {
         if (need > LA_NOALLOC_SCRATCH_BYTES)
             return fail(LA_ERR_UNSUPPORTED,
@@ -383,11 +394,12 @@ la_status chunk_fwd_impl(const la_desc* d, const int* cu_seqlens, int max_seqlen
         p.ws_a = ws + slots * d->dk * d->dv;
         p.ws_z = p.ws_a + slots * d->dk;
     }
+    p.slow_flags = reinterpret_cast<int*>(static_cast<char*>(workspace) + flags_at);
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e;
     if (cu_seqlens) {
-        int* order = reinterpret_cast<int*>(static_cast<char*>(workspace) + seg_bytes);
+        int* order = reinterpret_cast<int*>(static_cast<char*>(workspace) + order_at);
         e = timed_launch(la::K_SEQ_ORDER, s, [&] {
             return la::launch_seq_order(cu_seqlens, d->B, d->L, chunk, max_seqlen, order, s);
         });
@@ -403,11 +415,20 @@ la_status chunk_fwd_impl(const la_desc* d, const int* cu_seqlens, int max_seqlen
         e = timed_launch(la::K_STATE_SCAN, s, [&] { return la::launch_state_scan(p, d->dk, false, s); });
         if (e != hipSuccess) return hip_fail(e, "segment scan launch");
     }
+    const int pass = states ? la::PASS_MAIN_STORE : gn ? la::PASS_MAIN_NORM : la::PASS_MAIN;
     e = timed_launch(la::K_CHUNK_MAIN, s, [&] {
-        const int pass = states ? la::PASS_MAIN_STORE : gn ? la::PASS_MAIN_NORM : la::PASS_MAIN;
         return chunk_launch(d, p, chunk, gate_mode, pass, s, BH * pl.P);
     });
     if (e != hipSuccess) return hip_fail(e, "main pass launch");
+    if (device_gate(gate_mode)) {
+        // segments with a chunk whose gates are too strong for the
+        // chunk-middle reference, again with the sub-chunk path (every other
+        // workgroup reads its flag and exits)
+        e = timed_launch(la::K_CHUNK_SUB, s, [&] {
+            return chunk_launch(d, p, chunk, gate_mode, pass, s, BH * pl.P, true);
+        });
+        if (e != hipSuccess) return hip_fail(e, "sub-chunk pass launch");
+    }
     return LA_OK;
 }
 
@@ -516,7 +537,7 @@ size_t la_chunk_fwd_varlen_workspace_bytes(const la_desc* d, int max_seqlen, int
     if (check_desc(d) != LA_OK || !supported_chunk(chunk) || max_seqlen < 1 || max_seqlen > d->L)
         return 0;
     const la_desc dp = plan_desc(d, true, max_seqlen);
-    return align16(workspace_bytes(&dp, make_plan(&dp, chunk))) + order_bytes(d);
+    return workspace_bytes(&dp, make_plan(&dp, chunk)) + order_bytes(d);
 }
 
 size_t la_chunk_bwd_workspace_bytes(const la_desc* d) {

@@ -25,6 +25,7 @@ struct ChunkParams {
     float* ws_S;            // [BH, P, dk*dv] segment states (P > 1)
     float* ws_a;            // [BH, P, dk]    segment decay products
     float* ws_z;            // [BH, P, dk]    segment normaliser parts
+    int* slow_flags;        // [BH, P] vector-gate main pass: segments handed to the sub-chunk kernel
     const int* cu_seqlens;  // packed sequences: [B + 1] token offsets into each head's L tokens, or null
     const int* seq_order;   // packed sequences: the launch order of the sequences (a permutation of [0, B)), or null
     const float* gn_w;      // output group norm: per-channel scale [H, dv] or null (ones)
@@ -104,14 +105,16 @@ constexpr int bwd_chunk(int d, bool bf16) { return (!bf16 && d >= 128) ? 32 : 64
 // Kernel families, as named by the profiling interface.
 enum KernelId {
     K_CHUNK_MAIN = 0, K_CHUNK_STATE = 1, K_STATE_SCAN = 2, K_DECODE = 3,
-    K_CHUNK_STORE = 4, K_BWD = 5, K_DELTA = 6, K_DELTA_DECODE = 7, K_SEQ_ORDER = 8, K_COUNT = 9
+    K_CHUNK_STORE = 4, K_BWD = 5, K_DELTA = 6, K_DELTA_DECODE = 7, K_SEQ_ORDER = 8,
+    K_CHUNK_SUB = 9, K_COUNT = 10
 };
 
 // Launch hooks implemented in the kernel files.  Each returns hipSuccess or
 // the launch error; shapes have been validated by the caller.  The chunk
 // launchers take the pass (ChunkPass) and `nblocks` workgroups.
 #define LA_DECLARE_CHUNK_LAUNCHER(NAME) \
-    hipError_t NAME(const ChunkParams& p, int chunk, int gate, int pass, hipStream_t s, int nblocks);
+    hipError_t NAME(const ChunkParams& p, int chunk, int gate, int pass, hipStream_t s, int nblocks, \
+                    bool robust);
 LA_DECLARE_CHUNK_LAUNCHER(launch_chunk_f32_d16)
 LA_DECLARE_CHUNK_LAUNCHER(launch_chunk_f32_d32)
 LA_DECLARE_CHUNK_LAUNCHER(launch_chunk_f32_d64)

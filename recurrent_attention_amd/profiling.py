@@ -22,15 +22,18 @@ import re
 import sys
 from collections import defaultdict
 
-# chunk_kernel<ChunkCfg<dk, dv, C, bf16, gate, state-only, waves>, elu1, reversed, store, epilogue>
+# chunk_kernel<ChunkCfg<dk, dv, C, bf16, gate, state-only, waves>, elu1, reversed, store,
+#              epilogue, sub-chunk path>
 _CHUNK = (r"la::chunk_kernel<la::ChunkCfg<\d+, \d+, \d+, \w+, \d, {so}, \d+>, "
-          r"\w+, \w+, {store}, \w+>")
+          r"\w+, \w+, {store}, \w+, {sub}>")
 # chunk_main: every pass with outputs (the group-norm epilogue and the
-# training forward that also stores its boundary states included)
+# training forward that also stores its boundary states included);
+# chunk_sub: the same passes with the sub-chunk path (vector gates)
 FAMILIES = [
-    ("chunk_main", re.compile(_CHUNK.format(so="false", store=r"\w+"))),
-    ("chunk_store", re.compile(_CHUNK.format(so="true", store="true"))),
-    ("chunk_state", re.compile(_CHUNK.format(so="true", store="false"))),
+    ("chunk_main", re.compile(_CHUNK.format(so="false", store=r"\w+", sub="false"))),
+    ("chunk_sub", re.compile(_CHUNK.format(so="false", store=r"\w+", sub="true"))),
+    ("chunk_store", re.compile(_CHUNK.format(so="true", store="true", sub="false"))),
+    ("chunk_state", re.compile(_CHUNK.format(so="true", store="false", sub="false"))),
     ("state_scan", re.compile(r"la::state_scan_kernel")),
     ("chunk_bwd", re.compile(r"la::bwd_kernel")),
     ("delta_chunk", re.compile(r"la::delta_chunk_kernel")),

@@ -155,7 +155,7 @@ def test_chunk_normaliser_contract():
 def test_chunk_workspace_contract():
     d = _desc(B=1, H=1, L=4096, segments=4)
     need = api.la_chunk_fwd_workspace_bytes(d, 64)
-    assert need == 1 * 1 * 4 * (64 * 64 + 2 * 64) * 4
+    assert need == 1 * 1 * 4 * (64 * 64 + 2 * 64) * 4 + 16   # slots, then 4 segment flags
     assert _chunk(d, ws=None) == api.LA_ERR_INVALID
     assert _chunk(d, ws=A, ws_bytes=need - 4) == api.LA_ERR_INVALID
     assert _chunk(d, ws=MIS, ws_bytes=need) == api.LA_ERR_INVALID
@@ -177,7 +177,10 @@ def test_segment_plan(B, H, L, chunk, segments, P):
     d = _desc(B=B, H=H, L=L, segments=segments)
     assert api.la_chunk_fwd_segments(d, chunk) == P
     ws = api.la_chunk_fwd_workspace_bytes(d, chunk)
-    assert ws == (0 if P == 1 else B * H * P * (64 * 64 + 128) * 4)
+    # segment slots (several segments only), then one int32 flag per
+    # segment, each part rounded up to 16 bytes
+    flags = -(-B * H * P * 4 // 16) * 16
+    assert ws == (0 if P == 1 else B * H * P * (64 * 64 + 128) * 4) + flags
 
 
 def test_decode_validation():
@@ -276,11 +279,12 @@ def test_varlen_workspace_plans_for_the_longest_sequence():
     # automatic plan gives every (sequence, head) ceil(256 / 6) -> 16 segments
     d = _desc(B=3, H=2, L=1500)
     need = api.la_chunk_fwd_varlen_workspace_bytes(d, 1000, 64)
-    # segment slots, then the launch order of the 3 sequences (int32, 16-byte rounded)
-    assert need == 3 * 2 * 16 * (64 * 64 + 2 * 64) * 4 + 16
-    # one segment each: only the order array
+    # segment slots, the segment flags (int32), then the launch order of the
+    # 3 sequences (int32), each 16-byte rounded
+    assert need == 3 * 2 * 16 * (64 * 64 + 2 * 64) * 4 + 3 * 2 * 16 * 4 + 16
+    # one segment each: the flags and the order array
     d1 = _desc(B=3, H=2, L=1500, segments=1)
-    assert api.la_chunk_fwd_varlen_workspace_bytes(d1, 1000, 64) == 16
+    assert api.la_chunk_fwd_varlen_workspace_bytes(d1, 1000, 64) == 32 + 16
     assert _varlen(d1, max_seqlen=1000, ws=None) == api.LA_ERR_INVALID
     assert api.la_chunk_fwd_varlen_workspace_bytes(d, 1501, 64) == 0   # invalid
     assert _varlen(d, max_seqlen=1000, ws=None) == api.LA_ERR_INVALID

@@ -108,6 +108,112 @@ def test_diag_strong_gates_within_contract():
     check(got, ref, torch.bfloat16, "strong gates, chunk 16")
 
 
+# Gates far past the half-chunk range of a single chunk-wide reference: every
+# factor above one is now confined to half a 16-token block, so the kernel
+# holds while any 8 consecutive log-gates of a channel sum to more than about
+# -88.  -3 per token puts a half chunk of 64 at -96 (beyond fp32 for a
+# chunk-wide reference); -7 per token, drawn between -3.5 and -10.5, puts
+# 8 tokens down to -84.
+@pytest.mark.parametrize("C", [16, 32, 64])
+@pytest.mark.parametrize("level", [-3.0, -5.0, -7.0])
+@pytest.mark.parametrize("mode", [DIAG, SCALAR])
+def test_strong_gates_beyond_half_chunk(C, level, mode):
+    dt = torch.bfloat16
+    inp = _inputs(1, 2, 5 * C + 7, 128, dt, mode, seed=40 + C, state=True)
+    g = torch.Generator().manual_seed(41)
+    shape = inp["log_alpha"].shape
+    # around the level, from 0.5x to 1.5x, so the channels decay differently
+    inp["log_alpha"] = level * (0.5 + torch.rand(shape, generator=g))
+    got, ref = run_pair(inp, mode, C, S0=inp["S0"])
+    check(got, ref, dt, f"log-gates near {level} per token, chunk {C}, mode {mode}")
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_exercise_gates_0_95_and_0_1(dt):
+    # the gate values of "Module 22", "Exercise 3: You are the gate": a high
+    # gate (0.95, the state holds) at some positions and a low one (0.1)
+    # elsewhere; here chosen at random per token and channel
+    dtype = DTYPES[dt]
+    inp = _inputs(2, 2, 3 * 64 + 21, 64, dtype, DIAG, seed=44, state=True)
+    g = torch.Generator().manual_seed(45)
+    pick = torch.rand(inp["log_alpha"].shape, generator=g) < 0.5
+    inp["log_alpha"] = torch.where(pick, torch.tensor(0.95).log(), torch.tensor(0.1).log())
+    for C in (16, 64):
+        got, ref = run_pair(inp, DIAG, C, S0=inp["S0"])
+        check(got, ref, dtype, f"0.95/0.1 gates, chunk {C}")
+
+
+def _strong_in_ranges(inp, ranges, level, seed):
+    """log-gates of `level` (times 0.5..1.5) on the given (head, t0, t1)
+    token ranges of every batch entry, the workload's mild gates elsewhere."""
+    g = torch.Generator().manual_seed(seed)
+    la = inp["log_alpha"].clone()
+    for h, t0, t1 in ranges:
+        sl = la[:, h, t0:t1]
+        la[:, h, t0:t1] = level * (0.5 + torch.rand(sl.shape, generator=g))
+    inp["log_alpha"] = la
+
+
+# Strong gates in a few segments only: the main pass hands just those
+# segments to the sub-chunk kernel (a flag per segment); the others keep the
+# chunk-middle factors.  With one segment per (b,h) a whole head is handed
+# over, with the automatic plan (16 segments of one chunk) single chunks.
+@pytest.mark.parametrize("segments", [1, 0])
+@pytest.mark.parametrize("mode", [DIAG, SCALAR])
+def test_strong_gates_in_some_segments(mode, segments):
+    dt = torch.bfloat16
+    inp = _inputs(2, 3, 1000, 128, dt, mode, seed=46, state=True)
+    _strong_in_ranges(inp, [(1, 300, 400), (2, 990, 1000)], -6.0, seed=47)
+    got, ref = run_pair(inp, mode, 64, S0=inp["S0"], segments=segments)
+    check(got, ref, dt, f"strong gates in some segments, mode {mode}, segments {segments}")
+
+
+@pytest.mark.parametrize("mode", [DIAG, SCALAR])
+def test_strong_gates_with_normaliser(mode):
+    dt = torch.bfloat16
+    inp = _inputs(2, 2, 333, 64, dt, mode, seed=48, state=True)
+    _strong_in_ranges(inp, [(0, 0, 333), (1, 100, 200)], -5.0, seed=49)
+    got, ref = run_pair(inp, mode, 64, phi=api.LA_PHI_ELU1, normalize=True, S0=inp["S0"],
+                        z0=inp["z0"])
+    check(got, ref, dt, f"strong gates, normalised, mode {mode}", normalize=True)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_strong_gates_with_groupnorm_epilogue(dt):
+    dtype = DTYPES[dt]
+    inp, w, b, gate = _gn_case(2, 2, 5 * 64 + 7, 64, dtype, DIAG, seed=50)
+    _strong_in_ranges(inp, [(0, 0, 327), (1, 64, 200)], -5.0, seed=51)
+    got, S, ref, ref_S = _gn_run(inp, DIAG, w, b, gate, 1e-5)
+    assert slice_rel_err(got, ref) <= TOL[dtype]
+    assert slice_rel_err(S, ref_S) <= TOL[dtype]
+
+
+def test_strong_gates_training_forward():
+    # the forward that keeps its boundary states: out, S_final and every
+    # boundary state against the oracle's token loop
+    dt = torch.bfloat16
+    inp = _inputs(1, 2, 700, 64, dt, DIAG, seed=52, state=True)
+    _strong_in_ranges(inp, [(1, 128, 400)], -5.0, seed=53)
+    dev = "cuda"
+    out, S, states = api.chunk_fwd_train(inp["q"].to(dev), inp["k"].to(dev), inp["v"].to(dev),
+                                         gate_mode=DIAG, log_alpha=inp["log_alpha"].to(dev),
+                                         S0=inp["S0"].to(dev))
+    torch.cuda.synchronize()
+    ref = oracle.run(*(to_host64(inp[x]) for x in ("q", "k", "v")), gate_mode=DIAG,
+                     log_alpha=to_host64(inp["log_alpha"]), S0=to_host64(inp["S0"]))
+    assert slice_rel_err(to_host64(out), ref[0]) <= TOL[dt]
+    assert slice_rel_err(to_host64(S), ref[1]) <= TOL[dt]
+    C = api.la_chunk_bwd_chunk(api.make_desc(1, 2, 700, 64, 64, api.LA_BF16))
+    nslots = -(-700 // C) + 1          # the state before every chunk, then the final one (bf16)
+    st = to_host64(states.view(torch.bfloat16)[: 2 * nslots * 64 * 64]).reshape(1, 2, nslots, 64, 64)
+    for c in (1, 3, 5, 7):   # the state after c chunks = the state of a prefill of c*C tokens
+        n = c * C
+        ref_c = oracle.run(*(to_host64(inp[x])[:, :, :n] for x in ("q", "k", "v")), gate_mode=DIAG,
+                           log_alpha=to_host64(inp["log_alpha"])[:, :, :n],
+                           S0=to_host64(inp["S0"]))[1]
+        assert slice_rel_err(st[:, :, c], ref_c) <= TOL[dt], c
+
+
 def test_many_heads_gamma():
     H = api.LA_MAX_GAMMA_HEADS
     gam = [1.0 - 2.0 ** (-1 - (h % 12)) for h in range(H)]

@@ -1,8 +1,9 @@
 """The kernel-family names of the profiling summaries cover every kernel the
 library builds: each chunk_kernel instantiation in the built library (its
 host-side symbols, demangled) falls into exactly the family its template
-flags say (outputs -> chunk_main; state-only -> chunk_store when it stores
-every boundary state, else chunk_state), and the other kernels into theirs.
+flags say (outputs -> chunk_main, or chunk_sub with the sub-chunk path;
+state-only -> chunk_store when it stores every boundary state, else
+chunk_state), and the other kernels into theirs.
 A kernel left out of every family would drop out of the trace tables."""
 import os
 import re
@@ -15,7 +16,7 @@ from recurrent_attention_amd import api
 from recurrent_attention_amd.profiling import family
 
 _CFG = re.compile(r"la::chunk_kernel<la::ChunkCfg<\d+, \d+, \d+, \w+, \d, (\w+), \d+>, "
-                  r"(\w+), (\w+), (\w+), (\w+)>")
+                  r"(\w+), (\w+), (\w+), (\w+), (\w+)>")
 
 
 def _kernel_names():
@@ -41,11 +42,12 @@ def test_every_chunk_kernel_has_its_family():
     for n in names:
         m = _CFG.search(n)
         assert m, n
-        sonly, _elu1, _rev, store, _epi = m.groups()
-        want = "chunk_main" if sonly == "false" else ("chunk_store" if store == "true" else "chunk_state")
+        sonly, _elu1, _rev, store, _epi, sub = m.groups()
+        want = (("chunk_sub" if sub == "true" else "chunk_main") if sonly == "false"
+                else ("chunk_store" if store == "true" else "chunk_state"))
         assert family(n) == want, (n, family(n))
         seen.add(want)
-    assert seen == {"chunk_main", "chunk_state", "chunk_store"}
+    assert seen == {"chunk_main", "chunk_sub", "chunk_state", "chunk_store"}
 
 
 def test_other_kernels_have_their_families():
