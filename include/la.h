@@ -95,7 +95,11 @@ typedef struct la_desc {
 
 /*
  * Supported kernel shapes (else LA_ERR_UNSUPPORTED):
- *   dk == dv, dk in {16, 32, 64, 128}; chunk in {16, 32, 64}.
+ *   dk == dv, dk in {16, 32, 64, 128}; chunk a multiple of 16 in [16, 64],
+ *   or in [80, 128] for bf16 at dk <= 64 and fp32 at dk <= 32 (the
+ *   128-token tile of the in-chunk products fits the LDS there only).
+ *   Chunks shorter than their tile (48; 80 to 112) run in the next tile
+ *   up with its later tokens masked.
  *   LA_F32 runs fp32 matrix cores (no bf16 rounding); LA_BF16 runs bf16
  *   matrix cores with fp32 accumulation and fp32 states, which needs
  *   dk >= 32 (la_decode_step runs no matrix cores and takes bf16 at every

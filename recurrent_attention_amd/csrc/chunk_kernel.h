@@ -126,8 +126,9 @@ struct ChunkCfg {
     static_assert(DV % (16 * NW) == 0 && DK % 16 == 0 && C % 16 == 0, "tile shape");
     static_assert(!BF16 || DK % 32 == 0, "bf16 needs d_k >= 32");
     static_assert(NT % KCP == 0 && NT % VCP == 0, "channel-run mapping");
-    static_assert(KTPG * (int)sizeof(E) <= 16 && VTPG * (int)sizeof(E) <= 16,
-                  "a transposed run stays within one 16-byte unit");
+    static_assert((KTPG * (int)sizeof(E) <= 16 || KTPG * (int)sizeof(E) % 16 == 0) &&
+                  (VTPG * (int)sizeof(E) <= 16 || VTPG * (int)sizeof(E) % 16 == 0),
+                  "a transposed run stays within one 16-byte unit or is whole units");
     static_assert(KTG >= 2 && KTG % 2 == 0 && KTPG >= 1 && VTPG >= 1, "token groups");
     static_assert(KTG * KTPG == C && VTG * VTPG == C, "token groups cover the chunk");
     static_assert(8 % KTPG == 0 && C % NW == 0,
@@ -327,7 +328,11 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
         L = s1 - s0;
         rows0 = (size_t)h * p.L + s0;
     }
-    const int nchunks = (L + C - 1) / C;
+    // the chunk length: the tile C, or a multiple of 16 below it (the rest
+    // of the tile then holds no tokens: its gates and keys are masked and
+    // its output rows dropped)
+    const int CR = C > 16 ? p.chunk : C;
+    const int nchunks = (L + CR - 1) / CR;
     const int c_begin = seg * p.cps;
     const int c_end = min(c_begin + p.cps, nchunks);
     const bool norm = p.normalize != 0;
@@ -448,7 +453,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
             }
     }
     auto load_chunk = [&](int c, ChunkRegs& rg) {
-        const uint32_t t0 = (uint32_t)c * C;
+        const uint32_t t0 = (uint32_t)c * CR;
         const uint32_t okk = ((t0 + ktg * KTPG) * DK + CW * kcp) * ES;
         const uint32_t ovv = ((t0 + vtg * VTPG) * DV + VW * vcp) * ES;
         const uint32_t oaa = ((t0 + ktg * KTPG) * DK + CW * kcp) * 4;
@@ -469,7 +474,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
     };
     auto load_q = [&](int c) {
         if constexpr (!SONLY) {
-            const uint32_t okk = (((uint32_t)c * C + ktg * KTPG) * DK + CW * kcp) * ES;
+            const uint32_t okk = (((uint32_t)c * CR + ktg * KTPG) * DK + CW * kcp) * ES;
 #pragma unroll
             for (int j = 0; j < KTPG; ++j) qreg[j] = buf_load_words<Cfg::KWORDS, LAUX>(rq, okk + j * DK * ES);
         }
@@ -482,7 +487,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
             for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
                 for (int tb = 0; tb < TB; ++tb) {
-                    const uint32_t og = (((uint32_t)c * C + 16 * tb + r) * DV + colbase + 16 * nb + 4 * g) * ES;
+                    const uint32_t og = (((uint32_t)c * CR + 16 * tb + r) * DV + colbase + 16 * nb + 4 * g) * ES;
                     greg[nb][tb] = buf_load_words<OW>(rgate, og);
                 }
         }
@@ -527,12 +532,30 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
     // PD iterations ahead
     auto step = [&](const int ci, ChunkRegs& rg) -> bool {
         const int c = cof(ci);
-        const int t0 = c * C;
-        const int clen = min(C, L - t0);
+        const int t0 = c * CR;
+        const int clen = min(CR, L - t0);
         if constexpr (!Cfg::PREFETCH) {
             load_q(c);
             load_chunk(c, rg);
         }
+        // a chunk shorter than the tile: the tile's later tokens are the next
+        // chunk's, so their gates count as zero and their output rows fall
+        // outside the store descriptor's range (tokens past L read as zeros
+        // by themselves)
+        if constexpr (VG && C > 16) {
+            if (CR < C) {
+#pragma unroll
+                for (int j = 0; j < KTPG; ++j)
+                    if (ktg * KTPG + j >= clen) {
+#pragma unroll
+                        for (int i = 0; i < CW; ++i) rg.la[j].w[i] = 0u;
+                    }
+            }
+        }
+        const __amdgpu_buffer_rsrc_t roc =
+            (C > 16 && CR < C) ? make_rsrc(SONLY ? p.q : (const void*)(reinterpret_cast<const E*>(p.out) + rows0 * DV),
+                                           SONLY ? 0u : (uint32_t)(t0 + clen) * DV * ES)
+                               : ro;
 
         // ---- a2: chunk-local log2-gate sums.  Each thread sums its own run;
         // the token groups of one wave (lanes KCP apart hold the same channels
@@ -1115,9 +1138,9 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
                         }
                         if constexpr (BF16) {
                             const u32x2_t w = {pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3])};
-                            __builtin_amdgcn_raw_buffer_store_b64(w, ro, off, 0, 0);
+                            __builtin_amdgcn_raw_buffer_store_b64(w, roc, off, 0, 0);
                         } else {
-                            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, o), ro, off, 0, 0);
+                            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, o), roc, off, 0, 0);
                         }
                     }
                     scale_rows<Cfg>(accS, sm.sb[j], g);
@@ -1202,9 +1225,9 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
                     }
                     if constexpr (BF16) {
                         const u32x2_t w = {pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3])};
-                        __builtin_amdgcn_raw_buffer_store_b64(w, ro, off, 0, 0);
+                        __builtin_amdgcn_raw_buffer_store_b64(w, roc, off, 0, 0);
                     } else {
-                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, o), ro, off, 0, 0);
+                        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, o), roc, off, 0, 0);
                     }
                 }
             }
@@ -1429,6 +1452,10 @@ hipError_t launch_chunk_dt(const ChunkParams& p, int chunk, int gate, int pass, 
         if (pass == PASS_STATE) LA_CHUNK_GATES(CC, true, false, false);  \
         if (pass == PASS_MAIN) LA_CHUNK_GATES(CC, false, false, false);  \
     } while (0)
+    // chunk lengths below a tile run in it (48 in the 64 tile; 80, 96 and
+    // 112 in the 128 tile, which fits the LDS for bf16 at d <= 64 and fp32 at
+    // d <= 32)
+    const int tile = chunk <= 16 ? 16 : chunk <= 32 ? 32 : chunk <= 64 ? 64 : 128;
     constexpr int CB = bwd_chunk(D, BF);
     if (chunk == CB) {
         if (pass == PASS_STATE_REV) LA_CHUNK_GATES(CB, true, true, false);
@@ -1436,9 +1463,12 @@ hipError_t launch_chunk_dt(const ChunkParams& p, int chunk, int gate, int pass, 
         if (pass == PASS_MAIN_STORE) LA_CHUNK_GATES(CB, false, false, true);
     }
     if (pass == PASS_MAIN_NORM && chunk == 64) LA_CHUNK_GATES_EP(64, false, false, false, true);
-    if (chunk == 16) LA_CHUNK_FWD(16);
-    if (chunk == 32) LA_CHUNK_FWD(32);
-    if (chunk == 64) LA_CHUNK_FWD(64);
+    if (tile == 16) LA_CHUNK_FWD(16);
+    if (tile == 32) LA_CHUNK_FWD(32);
+    if (tile == 64) LA_CHUNK_FWD(64);
+    if constexpr (chunk_tile128<D, BF>()) {
+        if (tile == 128) LA_CHUNK_FWD(128);
+    }
     return hipErrorInvalidValue;
 #undef LA_CHUNK_FWD
 #undef LA_CHUNK_GATES

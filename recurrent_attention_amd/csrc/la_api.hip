@@ -70,7 +70,21 @@ size_t workspace_bytes(const la_desc* d, const Plan& pl) { return slot_bytes(d, 
 size_t order_bytes(const la_desc* d) { return align16((size_t)d->B * sizeof(int)); }
 
 bool supported_d(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
-bool supported_chunk(int c) { return c == 16 || c == 32 || c == 64; }
+// Chunk lengths of the prefill: multiples of 16 from 16 to 128; above 64
+// only where the 128-token tile is built.
+bool supported_chunk(const la_desc* d, int c) {
+    if (c < 16 || c > 128 || c % 16 != 0) return false;
+    return c <= 64 || la::chunk_tile128_rt(d->dk, d->dtype == LA_BF16);
+}
+la_status check_chunk(const la_desc* d, int c) {
+    if (c < 16 || c > 128 || c % 16 != 0)
+        return fail(LA_ERR_UNSUPPORTED, "chunk must be a multiple of 16 in [16, 128] (got %d)", c);
+    if (!supported_chunk(d, c))
+        return fail(LA_ERR_UNSUPPORTED,
+                    "chunks above 64 are built for bf16 at dk <= 64 and fp32 at dk <= 32 "
+                    "(chunk %d, dk %d)", c, d->dk);
+    return LA_OK;
+}
 
 // mfma: the shape runs on matrix cores (every prefill-like path), where
 // bf16 operands need d_k >= 32; the decode step streams the state on the
@@ -312,8 +326,8 @@ la_status chunk_fwd_impl(const la_desc* d, const int* cu_seqlens, int max_seqlen
     // packed sequences plan their segments for the longest one
     const la_desc dp = plan_desc(d, cu_seqlens != nullptr, max_seqlen);
     la_status st;
-    if (!supported_chunk(chunk))
-        return fail(LA_ERR_UNSUPPORTED, "chunk must be 16, 32 or 64 (got %d)", chunk);
+    st = check_chunk(d, chunk);
+    if (st != LA_OK) return st;
     if (!q || !k || !v || !out) return fail(LA_ERR_INVALID, "q, k, v and out must be non-NULL");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
         (S0 && !aligned16(S0)) || (z0 && !aligned16(z0)) || (S_final && !aligned16(S_final)) ||
@@ -380,6 +394,7 @@ la_status chunk_fwd_impl(const la_desc* d, const int* cu_seqlens, int max_seqlen
     p.P = pl.P;
     p.cps = pl.cps;
     p.nchunks = pl.nchunks;
+    p.chunk = chunk;
     p.phi_elu1 = d->phi == LA_PHI_ELU1;
     p.normalize = d->normalize;
     p.cu_seqlens = cu_seqlens;
@@ -451,12 +466,12 @@ const char* la_last_error_message(void) { return g_errmsg; }
 int la_version(void) { return LA_VERSION; }
 
 int la_chunk_fwd_segments(const la_desc* d, int chunk) {
-    if (check_desc(d) != LA_OK || !supported_chunk(chunk)) return 0;
+    if (check_desc(d) != LA_OK || !supported_chunk(d, chunk)) return 0;
     return make_plan(d, chunk).P;
 }
 
 size_t la_chunk_fwd_workspace_bytes(const la_desc* d, int chunk) {
-    if (check_desc(d) != LA_OK || !supported_chunk(chunk)) return 0;
+    if (check_desc(d) != LA_OK || !supported_chunk(d, chunk)) return 0;
     return workspace_bytes(d, make_plan(d, chunk));
 }
 
@@ -534,7 +549,7 @@ la_status la_chunk_fwd_varlen(const la_desc* d, const int* cu_seqlens, int max_s
 }
 
 size_t la_chunk_fwd_varlen_workspace_bytes(const la_desc* d, int max_seqlen, int chunk) {
-    if (check_desc(d) != LA_OK || !supported_chunk(chunk) || max_seqlen < 1 || max_seqlen > d->L)
+    if (check_desc(d) != LA_OK || !supported_chunk(d, chunk) || max_seqlen < 1 || max_seqlen > d->L)
         return 0;
     const la_desc dp = plan_desc(d, true, max_seqlen);
     return workspace_bytes(&dp, make_plan(&dp, chunk)) + order_bytes(d);
@@ -596,6 +611,7 @@ la_status la_chunk_bwd(const la_desc* d, const void* q, const void* k, const voi
     p.P = pl.P;
     p.cps = pl.cps;
     p.nchunks = pl.nchunks;
+    p.chunk = chunk;
     p.phi_elu1 = d->phi == LA_PHI_ELU1;
     if (pl.P > 1) {
         const size_t slots = (size_t)BH * pl.P;

@@ -38,6 +38,8 @@ struct ChunkParams {
     int P;                  // segments per (b,h)
     int cps;                // chunks per segment (last one may be shorter)
     int nchunks;            // ceil(L / C)
+    int chunk;              // C, the chunk length: at most the kernel's tile, the rest of a
+                            // tile masked
     int phi_elu1, normalize;
     float log2_gamma[LA_MAX_GAMMA_HEADS];  // GAMMA: log2(gamma_h), -inf for 0
 };
@@ -97,6 +99,12 @@ enum ChunkPass {
     PASS_MAIN_NORM = 5,  // main pass with the group-norm / swish-gate output epilogue (chunk 64)
     PASS_MAIN_STORE = 6  // main pass that also stores the state at every chunk boundary
 };
+
+// Whether the prefill builds the 128-token tile (chunks of 80 to 128
+// tokens) for this width and element type: its q, k, K^T, V^T and score
+// tiles fit the 160 KiB of LDS for bf16 at d <= 64 and fp32 at d <= 32.
+template <int D, bool BF> constexpr bool chunk_tile128() { return BF ? D <= 64 : D <= 32; }
+inline bool chunk_tile128_rt(int d, bool bf) { return bf ? d <= 64 : d <= 32; }
 
 // Chunk length of the backward: 64 tokens, 32 for fp32 at d = 128 (whose
 // six tiles of 64 tokens would not fit in the 160 KiB of LDS).

@@ -114,9 +114,21 @@ def test_noalloc_rejects_a_workspace_beyond_the_scratch():
     assert "scratch" in api.la_last_error_message()
 
 
-@pytest.mark.parametrize("chunk", [0, 8, 48, 128])
+@pytest.mark.parametrize("chunk", [0, 8, 24, 144, -16])
 def test_chunk_rejects_unsupported_chunk(chunk):
     assert _chunk(_desc(), chunk=chunk) == api.LA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("dk,dtype,chunk,ok", [
+    (64, api.LA_BF16, 48, True), (64, api.LA_BF16, 128, True), (128, api.LA_BF16, 112, False),
+    (128, api.LA_BF16, 64, True), (32, api.LA_F32, 96, True), (64, api.LA_F32, 80, False)])
+def test_chunk_lengths_by_shape(dk, dtype, chunk, ok):
+    # multiples of 16 up to 64 everywhere; above 64 where the 128-token tile
+    # is built (bf16 at dk <= 64, fp32 at dk <= 32)
+    d = _desc(dk=dk, dv=dk, dtype=dtype, L=1000)
+    assert (api.la_chunk_fwd_segments(d, chunk) > 0) == ok
+    st = _chunk(d, chunk=chunk, q=None)          # NULL q: refused after the chunk check
+    assert st == (api.LA_ERR_INVALID if ok else api.LA_ERR_UNSUPPORTED)
 
 
 def test_chunk_rejects_null_and_misaligned_pointers():
@@ -269,7 +281,7 @@ def test_varlen_validation():
     assert _varlen(d, max_seqlen=0) == api.LA_ERR_INVALID
     assert _varlen(d, max_seqlen=301) == api.LA_ERR_INVALID
     assert _varlen(d, q=None) == api.LA_ERR_INVALID
-    assert _varlen(d, chunk=48) == api.LA_ERR_UNSUPPORTED
+    assert _varlen(d, chunk=40) == api.LA_ERR_UNSUPPORTED
     assert _varlen(_desc(B=3, H=2, L=300, segments=3), max_seqlen=100) == api.LA_ERR_INVALID
     assert _varlen(_desc(B=0, H=2, L=300)) == api.LA_ERR_INVALID
 

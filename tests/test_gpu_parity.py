@@ -37,10 +37,18 @@ def _inputs(B, H, L, d, dtype, mode, seed=0, gamma=None, state=False):
 
 # ------------------------------------------------------------------ prefill grid
 
+def _chunks(dt, d):
+    """Chunk lengths built for a shape: multiples of 16 up to 64 everywhere,
+    up to 128 where the 128-token tile fits the LDS (bf16 at d <= 64, fp32
+    at d <= 32)."""
+    big = d <= 64 if dt == "bf16" else d <= 32
+    return (16, 32, 48, 64) + ((80, 96, 112, 128) if big else ())
+
+
 GRID = [(dt, d, C, mode)
         for dt in ("f32", "bf16")
         for d in ((16, 32, 64, 128) if dt == "f32" else (32, 64, 128))
-        for C in (16, 32, 64)
+        for C in _chunks(dt, d)
         for mode in (NONE, GAMMA, DIAG, SCALAR)]
 
 
@@ -51,6 +59,25 @@ def test_chunk_fwd_grid(dt, d, C, mode):
     inp = _inputs(1, 2, L, d, dtype, mode, seed=d + C + mode)
     got, ref = run_pair(inp, mode, C)
     check(got, ref, dtype, f"{dt} d={d} C={C} mode={mode}")
+
+
+# chunks shorter than their tile (48 in the 64-token tile; 80, 96, 112 in the
+# 128-token one) with several segments, an initial state and the normaliser
+@pytest.mark.parametrize("C", [48, 80, 112])
+@pytest.mark.parametrize("mode", [NONE, GAMMA, DIAG, SCALAR])
+def test_chunk_shorter_than_its_tile(C, mode):
+    dt = torch.bfloat16
+    inp = _inputs(2, 2, 7 * C + 5, 64, dt, mode, seed=C + 60 + mode, state=True)
+    got, ref = run_pair(inp, mode, C, phi=api.LA_PHI_ELU1, normalize=True, S0=inp["S0"],
+                        z0=inp["z0"], segments=3)
+    check(got, ref, dt, f"chunk {C} mode {mode}", normalize=True)
+
+
+def test_chunk_128_unsupported_at_d128_bf16():
+    inp = _inputs(1, 1, 256, 128, torch.bfloat16, NONE, seed=1)
+    with pytest.raises(api.LaError) as e:
+        api.chunk_fwd(inp["q"].cuda(), inp["k"].cuda(), inp["v"].cuda(), chunk=128)
+    assert e.value.status == api.LA_ERR_UNSUPPORTED
 
 
 @pytest.mark.parametrize("mode", [NONE, GAMMA, DIAG, SCALAR])
