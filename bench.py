@@ -8,8 +8,8 @@ inputs resident in HBM.  ``value`` is sequence tokens per second.
 
 Timing of every prefill-like part (the prefill, its backward and training
 step, the packed, scalar-gate, retention and delta prefills): warm-up
-steps, then K steps, each after a 512 MiB write that evicts the 256 MB
-Infinity Cache and bracketed by HIP events on the stream; ``ms_per_step``
+steps, then K steps, each after a 512 MiB write and a 512 MiB read that
+evict the 256 MB Infinity Cache, and bracketed by HIP events on the stream; ``ms_per_step``
 is their mean (``step_ms`` adds the median, the minimum and the mean of K
 steps run back to back without the flush).  Per-kernel averages come from
 a further K flushed steps.  Decode steps run back to back (1 GiB of state
@@ -32,9 +32,14 @@ Also reported, in the same line:
   them from their final states.
 * ``scalar_gate``: the same prefill with one gate per token and head
   (``scalar_gate_B1H16_L32768_d128``), which drops the d_k-wide gate stream.
-* ``retention``: the retention workload (B=2, H=16, L=8192, d=128,
-  multi-scale gamma), plain and with the fused group-norm / swish-gate
-  output epilogue.
+* ``configs``: every prefill workload of the workload table (plain linear
+  attention L=64 d=16 fp32; plain linear attention B=4 H=8 L=2048 d=64
+  normalised; retention B=2 H=16 L=8192 d=128; the headline) with tokens/s,
+  TFLOP/s, GB/s, the step's fraction of its attainable roofline and its main
+  pass's roofline, and the decode workload plain and with phi = elu+1 and
+  the normaliser.
+* ``retention_groupnorm``: the retention workload with the fused group-norm
+  / swish-gate output epilogue.
 * ``delta``: the delta rule's prefill (``delta_B16H16_L4096_d128``) and
   100 decode steps at the decode workload's shape.
 * ``cpu_baseline``: the fp64 oracle (test infrastructure, untuned) on the
@@ -62,6 +67,9 @@ METRIC = ("chunkwise fwd tokens/s + % bf16 MFMA peak (H16 d128 L32k); "
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 matrix peak
 PROFILES = os.path.join(ROOT, "profiles")
+# the prefill workloads timed beside the headline, in the workload table's order
+PREFILL_CONFIGS = ("linear_elu1_L64_d16_fp32", "linear_elu1_B4H8_L2048_d64",
+                   "retention_B2H16_L8192_d128", "gla_B1H16_L32768_d128")
 
 
 def kernel_source_hash():
@@ -120,19 +128,27 @@ FLUSH_BYTES = 512 << 20
 
 
 class CacheFlush:
-    """Writes a 512 MiB scratch buffer, twice the 256 MB Infinity Cache, so
-    that a step timed after it finds none of its inputs cached (the 34 MB
-    and 270 MB workloads would otherwise run partly from the cache when
-    repeated back to back)."""
+    """Writes a 512 MiB scratch buffer, twice the 256 MB Infinity Cache, and
+    then reads another 512 MiB buffer, so that a step timed after it finds
+    none of its inputs cached (the 34 MB and 270 MB workloads would
+    otherwise run partly from the cache when repeated back to back) and no
+    dirty lines of the flush itself left to write back.  A write alone made
+    the event-timed step of the 806 MB prefill about 30 us longer than the
+    same step after a read, or with no flush at all, while the per-kernel
+    durations stayed the same: the timed region billed the flush's tail."""
 
     def __init__(self, torch, dev, on=True):
+        self.torch = torch
         self.buf = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev) if on else None
+        self.rbuf = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device=dev) if on else None
+        self.acc = torch.empty((), dtype=torch.float32, device=dev) if on else None
         self.n = 0
 
     def __call__(self):
         if self.buf is not None:
             self.n += 1
             self.buf.fill_(float(self.n & 7))
+            self.torch.sum(self.rbuf, dim=0, out=self.acc)
 
 
 def time_steps(torch, step, args, flush):
@@ -185,13 +201,22 @@ def step_times(t):
     return out
 
 
+FP32_PEAK_TFLOPS = 157.3       # MI355X dense fp32 matrix peak
+
+
+def esize(w):
+    return 4 if str(w.dtype).endswith("float32") else 2
+
+
 def prefill_bytes(w):
-    """Algorithmic bytes of one prefill: q, k, v, out in bf16 (+ fp32 log
-    gates: d_k per token-head for the diagonal gate, one for the scalar
-    gate) per token-head, plus the fp32 final state per (b,h)."""
+    """Algorithmic bytes of one prefill: q, k, v read and out written in the
+    input type (+ fp32 log-gates: d_k per token-head for the diagonal gate,
+    one for the scalar gate) per token-head, plus the fp32 final state (and
+    normaliser) per (b,h)."""
     gate = {2: 4 * w.dk, 3: 4}.get(w.gate_mode, 0)
-    per_th = 2 * (2 * w.dk + w.dv) + 2 * w.dv + gate
-    return w.B * w.H * w.L * per_th + w.B * w.H * w.dk * w.dv * 4
+    per_th = esize(w) * (2 * w.dk + 2 * w.dv) + gate
+    fin = w.dk * w.dv * 4 + (w.dk * 4 if w.normalize else 0)
+    return w.B * w.H * w.L * per_th + w.B * w.H * fin
 
 
 def prefill_flops(w):
@@ -199,24 +224,42 @@ def prefill_flops(w):
     return w.B * w.H * w.L * (2 * w.chunk * (w.dk + w.dv) + 4 * w.dk * w.dv)
 
 
+def attainable_frac(w, ms):
+    """Fraction of the attainable roofline of one step: the larger of its
+    HBM floor and its matrix-core floor over the measured step time."""
+    peak_f = (BF16_PEAK_TFLOPS if esize(w) == 2 else FP32_PEAK_TFLOPS) * 1e12
+    floor_s = max(prefill_bytes(w) / (HBM_PEAK_GBS * 1e9), prefill_flops(w) / peak_f)
+    return floor_s / (ms * 1e-3), floor_s * 1e6
+
+
 def bench_prefill(args, torch, api, workloads, name=None):
     w = workloads.WORKLOADS[name or workloads.PREFILL_HEADLINE]
     dev = torch.device("cuda", 0)
     inp = workloads.workload_inputs(w.name, seed=0, device=dev)
     q, k, v, la = inp["q"], inp["k"], inp["v"], inp["log_alpha"]
-    desc = api.make_desc(w.B, w.H, w.L, w.dk, w.dv, api.LA_BF16, w.phi, w.normalize, 0)
+    ldt = api.LA_BF16 if esize(w) == 2 else api.LA_F32
+    desc = api.make_desc(w.B, w.H, w.L, w.dk, w.dv, ldt, w.phi, w.normalize, 0)
     P = api.la_chunk_fwd_segments(desc, w.chunk)
     need = api.la_chunk_fwd_workspace_bytes(desc, w.chunk)
     out = torch.empty_like(v)
     S_final = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
+    z_final = (torch.empty((w.B, w.H, w.dk), dtype=torch.float32, device=dev)
+               if w.normalize else None)
     ws = torch.empty(max(need // 4, 1), dtype=torch.float32, device=dev)
     stream = torch.cuda.current_stream(dev)
     sp = ctypes.c_void_p(stream.cuda_stream)
     lib = api.load_library()
     dref = ctypes.byref(desc)
-    argv = (dref, q.data_ptr(), k.data_ptr(), v.data_ptr(), w.gate_mode, la.data_ptr(),
-            None, None, w.chunk, out.data_ptr(), S_final.data_ptr(), None,
-            ws.data_ptr(), need, sp)
+    g_host = torch.tensor(w.gamma or (0.0,), dtype=torch.float32)
+    if w.gate_mode in (api.LA_GATE_DIAG, api.LA_GATE_SCALAR):
+        gate = la.data_ptr()
+    elif w.gate_mode == api.LA_GATE_GAMMA:
+        gate = ctypes.c_void_p(g_host.data_ptr())
+    else:
+        gate = None
+    argv = (dref, q.data_ptr(), k.data_ptr(), v.data_ptr(), w.gate_mode, gate,
+            None, None, w.chunk, out.data_ptr(), S_final.data_ptr(),
+            None if z_final is None else z_final.data_ptr(), ws.data_ptr(), need, sp)
 
     def step():
         st = lib.la_chunk_fwd(*argv)
@@ -252,6 +295,7 @@ def bench_prefill(args, torch, api, workloads, name=None):
     main_us = kern["chunk_main"]["avg_us"]
     achieved = bytes_alg / (main_us * 1e-6) / 1e9
     traffic = measured_traffic(f"chunk_main_{w.name}", kernel_source_hash())
+    frac, floor_us = attainable_frac(w, ms_step)
     return {
         "w": w, "P": P, "ms_step": ms_step, "tokens_per_s": tokens / (ms_step * 1e-3),
         "times": step_times(times),
@@ -260,9 +304,29 @@ def bench_prefill(args, torch, api, workloads, name=None):
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic, "kernel": "chunk_main",
                      "bytes_per_launch": bytes_alg, "avg_launch_us": round(main_us, 2)},
-        "mfma_pct": 100.0 * flops / (ms_step * 1e-3) / (BF16_PEAK_TFLOPS * 1e12),
+        "mfma_pct": 100.0 * flops / (ms_step * 1e-3) /
+                    ((BF16_PEAK_TFLOPS if esize(w) == 2 else FP32_PEAK_TFLOPS) * 1e12),
         "hbm_pct_step": 100.0 * bytes_alg / (ms_step * 1e-3) / (HBM_PEAK_GBS * 1e9),
+        "attainable_frac": frac, "floor_us": floor_us,
     }
+
+
+def config_entry(pre):
+    """One config's figures for the line's ``configs`` object."""
+    w = pre["w"]
+    ms = pre["ms_step"]
+    return {"workload": w.name, "ms_per_step": round(ms, 4), "step_ms": pre["times"],
+            "tokens_per_s": round(pre["tokens_per_s"], 1),
+            "tflops": round(pre["flops"] / (ms * 1e-3) / 1e12, 3),
+            "gbs": round(pre["bytes"] / (ms * 1e-3) / 1e9, 1),
+            "matrix_peak_pct": round(pre["mfma_pct"], 3),
+            "hbm_peak_pct_step": round(pre["hbm_pct_step"], 2),
+            "attainable_roofline_frac_step": round(pre["attainable_frac"], 4),
+            "floor_us": round(pre["floor_us"], 2),
+            "segments": pre["P"],
+            "kernels_avg_us": {k: (round(v["avg_us"], 2) if v["avg_us"] else None)
+                               for k, v in pre["kernels"].items()},
+            "roofline": pre["roofline"]}
 
 
 def backward_bytes(w):
@@ -422,9 +486,10 @@ def bench_varlen(args, torch, api, workloads, segments=0):
     }
 
 
-def bench_retention(args, torch, api, workloads):
-    """The retention workload, plain and with the fused group-norm / swish
-    output epilogue (la_chunk_fwd_groupnorm)."""
+def bench_retention_groupnorm(args, torch, api, workloads):
+    """The retention workload with the fused group-norm / swish-gate output
+    epilogue (la_chunk_fwd_groupnorm); the plain retention prefill is one of
+    the configs."""
     name = "retention_B2H16_L8192_d128"
     w = workloads.WORKLOADS[name]
     dev = torch.device("cuda", 0)
@@ -444,33 +509,28 @@ def bench_retention(args, torch, api, workloads):
     sp = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
     lib = api.load_library()
     gn = api.LaGroupNorm(gnw.data_ptr(), gnb.data_ptr(), gate.data_ptr(), 1e-5)
-    head = (ctypes.byref(desc), q.data_ptr(), k.data_ptr(), v.data_ptr(), w.gate_mode, gp,
-            None, None, w.chunk)
-    tail = (out.data_ptr(), S.data_ptr(), None, ws.data_ptr(), need, sp)
+    argv = (ctypes.byref(desc), q.data_ptr(), k.data_ptr(), v.data_ptr(), w.gate_mode, gp,
+            None, None, w.chunk, ctypes.byref(gn), out.data_ptr(), S.data_ptr(), None,
+            ws.data_ptr(), need, sp)
+
+    def step():
+        if lib.la_chunk_fwd_groupnorm(*argv) != 0:
+            raise RuntimeError(api.la_last_error_message())
 
     flush = CacheFlush(torch, dev, not args.no_flush)
-
-    def timed(fn):
-        t = time_steps(torch, fn, args, flush)
-        return t["mean"], kernel_avgs(torch, api, fn, args, flush, ("chunk_main",))["chunk_main"], t
-
-    def plain():
-        if lib.la_chunk_fwd(*head, *tail) != 0:
-            raise RuntimeError(api.la_last_error_message())
-
-    def normed():
-        if lib.la_chunk_fwd_groupnorm(*head, ctypes.byref(gn), *tail) != 0:
-            raise RuntimeError(api.la_last_error_message())
-
-    ms0, k0, t0 = timed(plain)
-    ms1, k1, t1 = timed(normed)
-    tokens = w.B * w.L
-    return {"workload": name, "tokens_per_s": round(tokens / (ms0 * 1e-3), 1),
-            "ms_per_step": round(ms0, 4), "step_ms": step_times(t0), "main_avg_us": round(k0, 2),
-            "groupnorm_swish": {"tokens_per_s": round(tokens / (ms1 * 1e-3), 1),
-                                "ms_per_step": round(ms1, 4), "step_ms": step_times(t1),
-                                "main_avg_us": round(k1, 2),
-                                "extra_bytes": w.B * w.H * w.L * w.dv * 2}}
+    t = time_steps(torch, step, args, flush)
+    main_us = kernel_avgs(torch, api, step, args, flush, ("chunk_main",))["chunk_main"]
+    ms = t["mean"]
+    extra = w.B * w.H * w.L * w.dv * 2 + 2 * w.H * w.dv * 4    # swish gate (bf16), scale, shift
+    alg = prefill_bytes(w) + extra
+    achieved = alg / (main_us * 1e-6) / 1e9
+    return {"workload": name + "_groupnorm_swish", "tokens_per_s": round(w.B * w.L / (ms * 1e-3), 1),
+            "ms_per_step": round(ms, 4), "step_ms": step_times(t),
+            "main_avg_us": round(main_us, 2), "extra_bytes": extra,
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                         "traffic": None, "kernel": "chunk_main",
+                         "bytes_per_launch": alg, "avg_launch_us": round(main_us, 2)}}
 
 
 def bench_delta(args, torch, api, workloads):
@@ -560,17 +620,22 @@ def bench_delta(args, torch, api, workloads):
     }
 
 
-def bench_decode(args, torch, api, workloads):
+def bench_decode(args, torch, api, workloads, with_z=False):
+    """Consecutive recurrent steps of the decode workload (retention, gamma =
+    0.97, phi = identity, no normaliser).  ``with_z``: the same steps with
+    phi = elu+1 and the normaliser, z0 = 1 + |N(0,1)| following gamma."""
     w = workloads.WORKLOADS[workloads.DECODE_HEADLINE]
     dev = torch.device("cuda", 0)
     steps = args.decode_steps
-    S0, _ = workloads.decode_state(w.B, w.H, w.dk, w.dv, seed=0, device=dev)
+    S0, z0 = workloads.decode_state(w.B, w.H, w.dk, w.dv, seed=0, device=dev, with_z=with_z)
     q, k, v, _ = workloads.decode_tokens(w.B, w.H, w.dk, w.dv, steps, seed=1, device=dev)
     S = S0.clone()
+    z = z0.clone() if with_z else None
     out = torch.empty((w.B, w.H, w.dv), dtype=torch.bfloat16, device=dev)
     gamma = torch.tensor(w.gamma, dtype=torch.float32)
     g_ptr = ctypes.c_void_p(gamma.data_ptr())
-    desc = api.make_desc(w.B, w.H, 1, w.dk, w.dv, api.LA_BF16, w.phi, False, 0)
+    phi = api.LA_PHI_ELU1 if with_z else w.phi
+    desc = api.make_desc(w.B, w.H, 1, w.dk, w.dv, api.LA_BF16, phi, with_z, 0)
     dref = ctypes.byref(desc)
     sp = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
     lib = api.load_library()
@@ -578,22 +643,28 @@ def bench_decode(args, torch, api, workloads):
     kp = [k[t].data_ptr() for t in range(steps)]
     vp = [v[t].data_ptr() for t in range(steps)]
     Sp, op = S.data_ptr(), out.data_ptr()
+    zp = None if z is None else z.data_ptr()
+
+    def reset():
+        S.copy_(S0)
+        if z is not None:
+            z.copy_(z0)
 
     def run(n):
         for t in range(n):
             st = lib.la_decode_step(dref, qp[t], kp[t], vp[t], w.gate_mode, g_ptr, Sp,
-                                    None, op, sp)
+                                    zp, op, sp)
             if st != 0:
                 raise RuntimeError(api.la_last_error_message())
 
     run(min(steps, 20))
-    S.copy_(S0)
+    reset()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     run(steps)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    S.copy_(S0)
+    reset()
     torch.cuda.synchronize()
     api.la_profile_begin()
     run(steps)
@@ -601,20 +672,21 @@ def bench_decode(args, torch, api, workloads):
     api.la_profile_end()
     n, ms = api.la_profile_query("decode")
     avg_us = ms / n * 1e3
-    state_bytes = w.B * w.H * w.dk * w.dv * 4
+    state_bytes = w.B * w.H * w.dk * w.dv * 4 + (w.B * w.H * w.dk * 4 if with_z else 0)
     step_bytes = 2 * state_bytes + w.B * w.H * (2 * w.dk + 2 * w.dv) * 2   # + tokens and out
     us_step = elapsed / steps * 1e6
     gbs = step_bytes / (us_step * 1e-6) / 1e9
     achieved = step_bytes / (avg_us * 1e-6) / 1e9
     del q, k, v
+    name = w.name + ("_z_elu1" if with_z else "")
     return {
-        "workload": w.name, "steps": steps, "us_per_step": round(us_step, 2),
+        "workload": name, "steps": steps, "us_per_step": round(us_step, 2),
         "value": round(gbs, 1), "unit": "GB/s", "pct_of_hbm_peak": round(100 * gbs / HBM_PEAK_GBS, 2),
         "steps_per_s": round(1e6 / us_step, 1), "tokens_per_s": round(w.B * 1e6 / us_step, 1),
         "bytes_per_step": step_bytes,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(f"decode_{w.name}", decode_source_hash()),
+                     "traffic": measured_traffic(f"decode_{name}", decode_source_hash()),
                      "kernel": "decode", "avg_launch_us": round(avg_us, 2)},
     }
 
@@ -633,7 +705,7 @@ def cpu_baseline(workloads, w):
                normalize=w.normalize, nthreads=nthreads)
     dt = time.perf_counter() - t0
     return {"value": round(w.B * w.L / dt, 1), "unit": "tokens/s", "cores": nthreads,
-            "host_cpus": host, "kind": "oracle",
+            "nproc": host, "kind": "oracle",
             "sample": f"whole workload {w.name} (B={w.B}, H={w.H}, L={w.L}) drawn on the host; "
                       f"fp64 token loop, {nthreads} threads over (b,h) pairs, {dt:.2f} s"}
 
@@ -658,6 +730,20 @@ def hbm_copy_ceiling(torch, nbytes=1 << 30, reps=10):
     del src, dst
     return {"what": "1 GiB device-to-device copy, read + write bytes", "us": round(us, 2),
             "GB/s": round(gbs, 1), "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
+
+
+def gpu_warmup(torch, seconds=1.0):
+    """About a second of bf16 matrix products before anything is timed, so
+    that the first timed launches do not run at idle clocks (the kernel
+    durations of a part run first in a process fell by 5-10% over its first
+    launches without it)."""
+    a = torch.randn((8192, 8192), device="cuda").to(torch.bfloat16)
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            b = a @ a
+        torch.cuda.synchronize()
+    del a, b
 
 
 def copy_calibration(torch, nbytes=1 << 30):
@@ -693,6 +779,10 @@ def main(argv=None):
                              "copy"], default=None,
                     help="run one part only (copy: a 1 GiB device copy used to scale "
                          "rocprofv3 byte counters); prints no metric line")
+    ap.add_argument("--workload", default=None, choices=list(PREFILL_CONFIGS),
+                    help="prefill workload for --only prefill (default: the headline)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other prefill configs and the normalised decode run")
     args = ap.parse_args(argv)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -712,8 +802,10 @@ def main(argv=None):
     if args.only == "copy":
         copy_calibration(torch)
         return 0
+    gpu_warmup(torch)
     if args.only == "decode":
-        print(json.dumps(bench_decode(args, torch, api, workloads)), flush=True)
+        print(json.dumps({"decode": bench_decode(args, torch, api, workloads),
+                          "decode_z": bench_decode(args, torch, api, workloads, True)}), flush=True)
         return 0
     if args.only == "backward":
         print(json.dumps(bench_backward(args, torch, api, workloads)), flush=True)
@@ -725,7 +817,7 @@ def main(argv=None):
         print(json.dumps(bench_delta(args, torch, api, workloads)), flush=True)
         return 0
     if args.only == "retention":
-        print(json.dumps(bench_retention(args, torch, api, workloads)), flush=True)
+        print(json.dumps(bench_retention_groupnorm(args, torch, api, workloads)), flush=True)
         return 0
     if args.only == "scalar":
         sc = bench_prefill(args, torch, api, workloads, "scalar_gate_B1H16_L32768_d128")
@@ -733,17 +825,22 @@ def main(argv=None):
                           "roofline": sc["roofline"]}), flush=True)
         return 0
     if args.only == "prefill":
-        pre = bench_prefill(args, torch, api, workloads)
-        print(json.dumps({"ms_per_step": pre["ms_step"], "kernels": pre["kernels"],
-                          "roofline": pre["roofline"]}), flush=True)
+        pre = bench_prefill(args, torch, api, workloads, args.workload)
+        print(json.dumps(config_entry(pre)), flush=True)
         return 0
     pre = bench_prefill(args, torch, api, workloads)
+    w_head = pre["w"].name
     dec = None if args.no_decode else bench_decode(args, torch, api, workloads)
     bwd = None if args.no_backward else bench_backward(args, torch, api, workloads)
     vl = None if args.no_varlen else bench_varlen(args, torch, api, workloads)
     sc = None if args.no_scalar else bench_prefill(args, torch, api, workloads,
                                                    "scalar_gate_B1H16_L32768_d128")
-    ret = None if args.no_retention else bench_retention(args, torch, api, workloads)
+    ret = None if args.no_retention else bench_retention_groupnorm(args, torch, api, workloads)
+    cfgs = {}
+    if not args.no_configs:
+        for cname in PREFILL_CONFIGS:
+            cfgs[cname] = pre if cname == w_head else bench_prefill(args, torch, api, workloads, cname)
+        dec_z = None if args.no_decode else bench_decode(args, torch, api, workloads, True)
     dl = None if args.no_delta else bench_delta(args, torch, api, workloads)
     w = pre["w"]
     line = {
@@ -767,10 +864,17 @@ def main(argv=None):
         "pct_of_bf16_mfma_peak": round(pre["mfma_pct"], 3),
         "tflops": round(pre["flops"] / (pre["ms_step"] * 1e-3) / 1e12, 2),
         "pct_of_hbm_peak_step": round(pre["hbm_pct_step"], 2),
+        "attainable_roofline_frac_step": round(pre["attainable_frac"], 4),
         "kernels_avg_us": {k: (round(v["avg_us"], 2) if v["avg_us"] else None)
                            for k, v in pre["kernels"].items()},
         "roofline": pre["roofline"],
     }
+    if cfgs:
+        line["configs"] = {n: config_entry(c) for n, c in cfgs.items()}
+        if dec is not None:
+            line["configs"][dec["workload"]] = {k: dec[k] for k in (
+                "us_per_step", "value", "unit", "steps_per_s", "tokens_per_s", "roofline")}
+            line["configs"][dec_z["workload"]] = dec_z
     if dec is not None:
         line["decode"] = dec
     if bwd is not None:
@@ -778,7 +882,7 @@ def main(argv=None):
     if vl is not None:
         line["varlen"] = vl
     if ret is not None:
-        line["retention"] = ret
+        line["retention_groupnorm"] = ret
     if dl is not None:
         line["delta"] = dl
     if sc is not None:

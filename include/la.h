@@ -90,7 +90,8 @@ typedef struct la_desc {
     int normalize; /* 1: divide by phi(q).z and carry z; 0: no z at all     */
     int segments;  /* prefill: sequence segments per (b,h) that run in
                       parallel and are joined by a state scan; 0 = choose
-                      automatically, otherwise 1..ceil(L/chunk)             */
+                      automatically (about 256 workgroups in all, at least
+                      4 chunks a segment), otherwise 1..ceil(L/chunk)      */
 } la_desc;
 
 /*

@@ -31,6 +31,10 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 // Workgroups the automatic segment choice aims for: one per compute unit of
 // an MI355X (256 CUs).
 constexpr int kTargetBlocks = 256;
+// Fewest chunks the automatic choice gives a segment: below that the state
+// pass and the scan (two more launches) cost more than the shorter walk
+// saves (a 4-chunk sequence runs in one launch).
+constexpr int kMinSegmentChunks = 4;
 
 struct Plan {
     int nchunks, P, cps;
@@ -41,7 +45,10 @@ Plan make_plan(const la_desc* d, int chunk) {
     pl.nchunks = (d->L + chunk - 1) / chunk;
     const long bh = (long)d->B * d->H;
     int P = d->segments;
-    if (P <= 0) P = (int)((kTargetBlocks + bh - 1) / bh);
+    if (P <= 0) {
+        P = (int)((kTargetBlocks + bh - 1) / bh);
+        if (P > pl.nchunks / kMinSegmentChunks) P = pl.nchunks / kMinSegmentChunks;
+    }
     if (P < 1) P = 1;
     if (P > pl.nchunks) P = pl.nchunks;
     pl.cps = (pl.nchunks + P - 1) / P;

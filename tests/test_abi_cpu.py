@@ -179,7 +179,9 @@ def test_chunk_workspace_contract():
     (1, 16, 32768, 64, 0, 16),    # 16 pairs -> 16 segments of 32 chunks
     (2, 16, 8192, 64, 0, 8),
     (4, 8, 2048, 64, 0, 8),
-    (1, 1, 64, 16, 0, 4),         # never more segments than chunks
+    (1, 1, 64, 16, 0, 1),         # 4 chunks: one segment (at least 4 chunks each)
+    (1, 1, 160, 16, 0, 2),        # 10 chunks: two segments of 5
+    (1, 1, 64, 16, 6, 4),         # asked for: never more segments than chunks
     (1, 1, 100, 64, 5, 2),
     (256, 1, 100, 16, 0, 1),
     (1, 1, 1000, 64, 3, 3),       # 16 chunks: 6 + 6 + 4
@@ -288,12 +290,13 @@ def test_varlen_validation():
 
 def test_varlen_workspace_plans_for_the_longest_sequence():
     # 3 sequences x 2 heads, longest 1000 tokens (16 chunks of 64): the
-    # automatic plan gives every (sequence, head) ceil(256 / 6) -> 16 segments
+    # automatic plan gives every (sequence, head) ceil(256 / 6) = 43
+    # segments, at most 16 / 4 = 4 (4 chunks or more each)
     d = _desc(B=3, H=2, L=1500)
     need = api.la_chunk_fwd_varlen_workspace_bytes(d, 1000, 64)
     # segment slots, the segment flags (int32), then the launch order of the
     # 3 sequences (int32), each 16-byte rounded
-    assert need == 3 * 2 * 16 * (64 * 64 + 2 * 64) * 4 + 3 * 2 * 16 * 4 + 16
+    assert need == 3 * 2 * 4 * (64 * 64 + 2 * 64) * 4 + 3 * 2 * 4 * 4 + 16
     # one segment each: the flags and the order array
     d1 = _desc(B=3, H=2, L=1500, segments=1)
     assert api.la_chunk_fwd_varlen_workspace_bytes(d1, 1000, 64) == 32 + 16

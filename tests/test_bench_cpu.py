@@ -68,3 +68,31 @@ def test_time_steps_orders_flush_event_step():
     assert log[:4] == ["flush", "step", "flush", "step"]          # warm-up, flushed
     assert log[-4:] == ["step", "step", "step", "sync"]           # back to back
     assert t["mean"] == 2.0 and t["min"] == 2.0
+
+
+def test_algorithmic_counts_of_the_configs():
+    # bytes: q, k, v, out once in the input type (+ fp32 log-gates), plus the
+    # final state (and z when normalised); flops: 2C(dk+dv) + 4 dk dv per
+    # token-head -- the per-token-head figures of the workloads' definitions
+    sys.path.insert(0, ROOT)
+    import bench
+    from recurrent_attention_amd import workloads
+    W = workloads.WORKLOADS
+    w1 = W["linear_elu1_L64_d16_fp32"]
+    assert bench.prefill_bytes(w1) == 64 * 4 * 4 * 16 + 16 * 16 * 4 + 16 * 4
+    assert bench.prefill_flops(w1) == 64 * 2048
+    w2 = W["linear_elu1_B4H8_L2048_d64"]
+    assert bench.prefill_bytes(w2) == 32 * 2048 * 512 + 32 * (64 * 64 * 4 + 64 * 4)
+    assert bench.prefill_flops(w2) == 32 * 2048 * 32768
+    w3 = W["retention_B2H16_L8192_d128"]
+    assert bench.prefill_bytes(w3) == 32 * 8192 * 1024 + 32 * 128 * 128 * 4
+    w4 = W["gla_B1H16_L32768_d128"]
+    assert bench.prefill_bytes(w4) == 16 * 32768 * 1536 + 16 * 128 * 128 * 4
+    assert bench.prefill_flops(w4) == 16 * 32768 * 98304
+    # the headline's floor is its HBM time at 8 TB/s
+    frac, floor_us = bench.attainable_frac(w4, 0.2016)
+    assert abs(floor_us - bench.prefill_bytes(w4) / 8e12 * 1e6) < 1e-9
+    assert abs(frac - floor_us / 201.6) < 1e-12
+    # fp32 inputs take the fp32 matrix peak for their flop floor
+    assert bench.attainable_frac(w1, 1.0)[1] == max(
+        bench.prefill_bytes(w1) / 8e12, bench.prefill_flops(w1) / 157.3e12) * 1e6
