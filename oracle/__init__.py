@@ -65,6 +65,9 @@ MUTATIONS = {
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
+# another build of oracle.c to load instead (the sanitizer build of the CPU
+# tests); build() always writes _LIB
+_LOAD = os.environ.get("ORACLE_LIBRARY") or _LIB
 _lib = None
 
 
@@ -82,9 +85,9 @@ def build(force: bool = True) -> str:
 def _load():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
+        if _LOAD == _LIB and not os.path.exists(_LIB):
             build(force=False)
-        lib = ctypes.CDLL(_LIB)
+        lib = ctypes.CDLL(_LOAD)
         dp = ctypes.POINTER(ctypes.c_double)
         i = ctypes.c_int
         common = [i, i, i, i, i, i, dp, dp, i, i, dp, dp, dp, dp, dp]
