@@ -264,9 +264,15 @@ __device__ __forceinline__ void quad_transpose(float (&x)[4], int q) {
 // 12 wait states: more than any matrix-core result needs (10 for the fp32
 // operation) before another instruction may touch its registers.  The
 // compiler pads straight-line code itself; after a matrix product that a
-// branch can follow, the sub-chunk kernel pads explicitly, since padding has
-// been seen to go missing across such branches.
-__device__ __forceinline__ void mfma_drain() { asm volatile("s_nop 7\n\ts_nop 3" ::: "memory"); }
+// branch can follow, the kernels pad explicitly, since padding has been seen
+// to go missing across such branches.  The scheduling barriers keep the
+// compiler from moving matrix products (register-only instructions) past
+// the padding.
+__device__ __forceinline__ void mfma_drain() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 7\n\ts_nop 3" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
 
 template <class Cfg, bool ELU1, bool REV = false, bool STORE = false, bool EPI = false, bool ROB = false>
 __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
@@ -277,6 +283,13 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
     constexpr int VCP = Cfg::VCP, VTPG = Cfg::VTPG, VW = Cfg::VW;
     constexpr bool SONLY = Cfg::SONLY, BF16 = Cfg::BF16;
     constexpr int ES = (int)sizeof(typename Cfg::E);
+    // lanes that share one normaliser row (NRL) or one z channel (NCL): the
+    // workgroup's threads over the rows or channels, 1 to 16
+    constexpr int NRL = Cfg::NT / C >= 16 ? 16 : (Cfg::NT / C < 1 ? 1 : Cfg::NT / C);
+    constexpr int NCL = Cfg::NT / DK >= 16 ? 16 : (Cfg::NT / DK < 1 ? 1 : Cfg::NT / DK);
+    // unroll of the normaliser's sums: whole, or by four where the whole
+    // unroll spills registers (d = 128; fp32 at d = 32 in the 128-token tile)
+    constexpr int NUNR = (DK >= 128 || (!BF16 && DK == 32 && C >= 128)) ? 4 : 32;
     using T = typename Cfg::T;
     using E = typename Cfg::E;
     using Pair = typename Cfg::Pair;
@@ -933,8 +946,8 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
                     sm.z[tid] = zz;
                 }
                 __syncthreads();
-                if (tid < C) {
-                    const int t = tid, j = t / 16;
+                for (int t = tid; t < C; t += Cfg::NT) {
+                    const int j = t / 16;
                     float rsum = 0.f;
                     for (int s2 = 16 * j; s2 <= t; ++s2) rsum += T::tof(sm.p[t][p_pos<Cfg>(t, s2)]);
                     float dq = 0.f;
@@ -943,27 +956,45 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
                 }
                 __syncthreads();
             } else if (norm) {
-                if (tid < C) {
-                    const int t = tid;
+                // row t: sum_{s<=t} P[t][s] + (decayed q_t) . z, split over
+                // the NRL lanes of an aligned group (interleaved columns and
+                // channels) and added up by DPP moves inside the group
+                // (fixed trip counts, unrolled: reads in flight together)
+                const int part = tid % NRL;
+                for (int t = tid / NRL; t < C; t += Cfg::NT / NRL) {
                     float rsum = 0.f;
-                    for (int s = 0; s <= t; ++s) rsum += T::tof(sm.p[t][p_pos<Cfg>(t, s)]);
+#pragma unroll NUNR
+                    for (int n = 0; n < C / NRL; ++n) {
+                        const int s = part + n * NRL;
+                        const float x = T::tof(sm.p[t][p_pos<Cfg>(t, s)]);
+                        rsum += s <= t ? x : 0.f;
+                    }
                     float dq = 0.f;
-                    for (int i = 0; i < DK; ++i) {
+#pragma unroll NUNR
+                    for (int n = 0; n < DK / NRL; ++n) {
+                        const int i = part + n * NRL;
                         float zz = sm.z[i];
                         if constexpr (VG) zz *= sm.pre[i];
                         dq += T::tof(sm.q[t][qk_pos<Cfg>(t, i)]) * zz;
                     }
                     if constexpr (GATE == LA_GATE_GAMMA) dq *= sm.gpow[t + 1];
-                    sm.den[t] = dq + rsum;
+                    const float den = lane_group_sum<NRL>(dq + rsum);
+                    if (part == 0) sm.den[t] = den;
                 }
                 __syncthreads();
             }
         }
-        // z <- post * (pre * z + sum_s Kt[:, s])  (each thread its own channel)
-        if (norm && !(SUB && slow) && tid < DK) {
-            float cs = 0.f;
-            for (int s = 0; s < C; ++s) cs += T::tof(sm.kt[tid][tr_pos<Cfg>(tid, s)]);
-            sm.z[tid] = sm.post[tid] * (sm.pre[tid] * sm.z[tid] + cs);
+        // z <- post * (pre * z + sum_s Kt[:, s]): channel i over the NCL lanes
+        // of an aligned group, added up by DPP moves
+        if (norm && !(SUB && slow)) {
+            const int i = tid / NCL, part = tid % NCL;
+            if (i < DK) {
+                float cs = 0.f;
+#pragma unroll NUNR
+                for (int n = 0; n < C / NCL; ++n) cs += T::tof(sm.kt[i][tr_pos<Cfg>(i, part + n * NCL)]);
+                cs = lane_group_sum<NCL>(cs);
+                if (part == 0) sm.z[i] = sm.post[i] * (sm.pre[i] * sm.z[i] + cs);
+            }
         }
 
         // ---- value fragments: A operand of op2 and B operand of op3
@@ -1258,7 +1289,11 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
             const int nxt = c + 1;
             if (nxt < c_end || seg == P - 1) store_state(nxt);
         }
-        if constexpr (SUB) mfma_drain();   // the loop's back-edge follows
+        // the loop's back-edge follows: the compiler's wait states after the
+        // last state products do not always survive it (the assembly check
+        // finds it in the sub-chunk kernels and, with d < 128, in the
+        // vector-gate main passes)
+        if constexpr (SUB || (Cfg::VGM && DK < 128)) mfma_drain();
         return true;
     };
     if constexpr (STORE) {

@@ -166,6 +166,28 @@ __device__ __forceinline__ void lds_store_words(void* p, const Words<N>& x) {
 __device__ __forceinline__ float lane_read(float x, int src) {
     return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(x)));
 }
+// x of the lane that the DPP control CTRL selects within the lane's 16-lane row.
+template <int CTRL>
+__device__ __forceinline__ float dpp_sel(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+// Sum of x over each aligned group of N adjacent lanes (N = 1, 2, 4, 8 or
+// 16), received by every lane of the group, in DPP moves inside a 16-lane
+// row: rotations by 8 and 4 (N = 16) or the half-row mirror (N = 8) gather
+// the lanes that are equal modulo 4, then the quad permutations [2,3,0,1]
+// and [1,0,3,2] add the four residues.
+template <int N>
+__device__ __forceinline__ float lane_group_sum(float x) {
+    static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16, "groups of 1 to 16 lanes");
+    if constexpr (N == 16) {
+        x += dpp_sel<0x128>(x);    // row_ror:8
+        x += dpp_sel<0x124>(x);    // row_ror:4
+    }
+    if constexpr (N == 8) x += dpp_sel<0x141>(x);    // row_half_mirror
+    if constexpr (N >= 4) x += dpp_sel<0x4E>(x);     // quad_perm [2,3,0,1]
+    if constexpr (N >= 2) x += dpp_sel<0xB1>(x);     // quad_perm [1,0,3,2]
+    return x;
+}
 // Buffer descriptor over [base, base + bytes); reads past the end return 0
 // and writes past the end are dropped.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {

@@ -90,6 +90,25 @@ def test_chunk_fwd_normalised_elu1_with_state(mode, dt):
     check(got, ref, dtype, f"normalised {dt} mode={mode}", normalize=True)
 
 
+# the normaliser's row sums over every lane-group width (1 to 16 lanes a row:
+# the workgroup's threads over the rows of the tile) and, where the tile has
+# more rows than the workgroup threads (d = 16 in the 128-token tile), more
+# than one row a thread
+NORM_TILES = [("f32", 16, 128), ("f32", 16, 80), ("f32", 16, 16), ("f32", 32, 96),
+              ("f32", 32, 16), ("bf16", 32, 128), ("bf16", 64, 112), ("bf16", 64, 16),
+              ("bf16", 128, 16), ("bf16", 128, 32), ("f32", 128, 64)]
+
+
+@pytest.mark.parametrize("dt,d,C", NORM_TILES)
+@pytest.mark.parametrize("mode", [NONE, GAMMA, DIAG, SCALAR])
+def test_chunk_fwd_normalised_every_row_width(dt, d, C, mode):
+    dtype = DTYPES[dt]
+    inp = _inputs(1, 2, 4 * C + 9, d, dtype, mode, seed=d + C + 17 * mode, state=True)
+    got, ref = run_pair(inp, mode, C, phi=api.LA_PHI_ELU1, normalize=True, S0=inp["S0"],
+                        z0=inp["z0"], segments=2)
+    check(got, ref, dtype, f"normalised {dt} d={d} C={C} mode={mode}", normalize=True)
+
+
 @pytest.mark.parametrize("mode", [NONE, GAMMA, DIAG, SCALAR])
 def test_chunk_fwd_initial_state(mode):
     inp = _inputs(1, 4, 700, 128, torch.bfloat16, mode, seed=9, state=True)
