@@ -101,6 +101,10 @@ typedef struct la_desc {
  *   128-token tile of the in-chunk products fits the LDS there only).
  *   Chunks shorter than their tile (48; 80 to 112) run in the next tile
  *   up with its later tokens masked.
+ *   dk != dv: (dk, dv) = (64, 128) or (128, 64), for the bf16 prefill
+ *   (la_chunk_fwd, its group-norm, no-alloc and packed-sequence forms;
+ *   chunk <= 64) and for la_decode_step in either type; the backward, the
+ *   training forward and the delta rule need dk == dv.
  *   LA_F32 runs fp32 matrix cores (no bf16 rounding); LA_BF16 runs bf16
  *   matrix cores with fp32 accumulation and fp32 states, which needs
  *   dk >= 32 (la_decode_step runs no matrix cores and takes bf16 at every

@@ -1453,12 +1453,16 @@ struct ChunkWaves {
 
 // Host-side dispatch over chunk length, gate mode and pass for one (d, dtype).
 // The backward passes exist for the backward's chunk length only.
-template <int D, bool BF, int NWV = ChunkWaves<D>::value>
+// dk != dv (64 and 128 either way, bf16): the waves of the narrower width,
+// and neither the backward's passes nor the 128-token tile.
+template <int DK, int DV, bool BF, int NWV = ChunkWaves<(DK < DV ? DK : DV)>::value>
 hipError_t launch_chunk_dt(const ChunkParams& p, int chunk, int gate, int pass, hipStream_t s,
                            int nblocks, bool robust) {
+    constexpr int D = DK;
+    constexpr bool SQUARE = DK == DV;
 #define LA_CHUNK_LAUNCH(CC, GG, SO, RV, ST, EP, RB)                                        \
     do {                                                                                   \
-        using Cfg = ChunkCfg<D, D, CC, BF, GG, SO, NWV>;                                   \
+        using Cfg = ChunkCfg<DK, DV, CC, BF, GG, SO, NWV>;                                 \
         if (p.phi_elu1)                                                                    \
             hipLaunchKernelGGL((chunk_kernel<Cfg, true, RV, ST, EP, RB>), dim3(nblocks), dim3(Cfg::NT), 0, s, p); \
         else                                                                               \
@@ -1492,16 +1496,18 @@ hipError_t launch_chunk_dt(const ChunkParams& p, int chunk, int gate, int pass, 
     // d <= 32)
     const int tile = chunk <= 16 ? 16 : chunk <= 32 ? 32 : chunk <= 64 ? 64 : 128;
     constexpr int CB = bwd_chunk(D, BF);
-    if (chunk == CB) {
-        if (pass == PASS_STATE_REV) LA_CHUNK_GATES(CB, true, true, false);
-        if (pass == PASS_STORE) LA_CHUNK_GATES(CB, true, false, true);
-        if (pass == PASS_MAIN_STORE) LA_CHUNK_GATES(CB, false, false, true);
+    if constexpr (SQUARE) {
+        if (chunk == CB) {
+            if (pass == PASS_STATE_REV) LA_CHUNK_GATES(CB, true, true, false);
+            if (pass == PASS_STORE) LA_CHUNK_GATES(CB, true, false, true);
+            if (pass == PASS_MAIN_STORE) LA_CHUNK_GATES(CB, false, false, true);
+        }
     }
     if (pass == PASS_MAIN_NORM && chunk == 64) LA_CHUNK_GATES_EP(64, false, false, false, true);
     if (tile == 16) LA_CHUNK_FWD(16);
     if (tile == 32) LA_CHUNK_FWD(32);
     if (tile == 64) LA_CHUNK_FWD(64);
-    if constexpr (chunk_tile128<D, BF>()) {
+    if constexpr (SQUARE && chunk_tile128<D, BF>()) {
         if (tile == 128) LA_CHUNK_FWD(128);
     }
     return hipErrorInvalidValue;
@@ -1515,7 +1521,13 @@ hipError_t launch_chunk_dt(const ChunkParams& p, int chunk, int gate, int pass, 
 #define LA_DEFINE_CHUNK_LAUNCHER(NAME, D, BF)                                                      \
     hipError_t NAME(const ChunkParams& p, int chunk, int gate, int pass, hipStream_t s,            \
                     int nblocks, bool robust) {                                                    \
-        return launch_chunk_dt<D, BF>(p, chunk, gate, pass, s, nblocks, robust);                   \
+        return launch_chunk_dt<D, D, BF>(p, chunk, gate, pass, s, nblocks, robust);                \
+    }
+// (d_k, d_v, dtype) with d_k != d_v.
+#define LA_DEFINE_CHUNK_LAUNCHER_KV(NAME, DK, DV, BF)                                              \
+    hipError_t NAME(const ChunkParams& p, int chunk, int gate, int pass, hipStream_t s,            \
+                    int nblocks, bool robust) {                                                    \
+        return launch_chunk_dt<DK, DV, BF>(p, chunk, gate, pass, s, nblocks, robust);              \
     }
 
 }  // namespace la

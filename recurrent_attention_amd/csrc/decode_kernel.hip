@@ -119,25 +119,35 @@ void decode_kernel(const DecodeParams p) {
     }
 }
 
-template <int D, bool BF>
+template <int DK, int DV, bool BF>
 static hipError_t launch_decode_dt(const DecodeParams& p, int gate, hipStream_t s) {
-    const dim3 grid(p.BH), block(DecodeShape<D, D>::NT);
-    if (gate == LA_GATE_NONE) hipLaunchKernelGGL((decode_kernel<D, D, BF, 0>), grid, block, 0, s, p);
-    else if (gate == LA_GATE_GAMMA) hipLaunchKernelGGL((decode_kernel<D, D, BF, 1>), grid, block, 0, s, p);
-    else if (gate == LA_GATE_DIAG) hipLaunchKernelGGL((decode_kernel<D, D, BF, 2>), grid, block, 0, s, p);
-    else if (gate == LA_GATE_SCALAR) hipLaunchKernelGGL((decode_kernel<D, D, BF, 3>), grid, block, 0, s, p);
+    const dim3 grid(p.BH), block(DecodeShape<DK, DV>::NT);
+    if (gate == LA_GATE_NONE) hipLaunchKernelGGL((decode_kernel<DK, DV, BF, 0>), grid, block, 0, s, p);
+    else if (gate == LA_GATE_GAMMA) hipLaunchKernelGGL((decode_kernel<DK, DV, BF, 1>), grid, block, 0, s, p);
+    else if (gate == LA_GATE_DIAG) hipLaunchKernelGGL((decode_kernel<DK, DV, BF, 2>), grid, block, 0, s, p);
+    else if (gate == LA_GATE_SCALAR) hipLaunchKernelGGL((decode_kernel<DK, DV, BF, 3>), grid, block, 0, s, p);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
-hipError_t launch_decode(const DecodeParams& p, int d, bool bf16, int gate, hipStream_t s) {
-    switch (d) {
-        case 16: return bf16 ? launch_decode_dt<16, true>(p, gate, s) : launch_decode_dt<16, false>(p, gate, s);
-        case 32: return bf16 ? launch_decode_dt<32, true>(p, gate, s) : launch_decode_dt<32, false>(p, gate, s);
-        case 64: return bf16 ? launch_decode_dt<64, true>(p, gate, s) : launch_decode_dt<64, false>(p, gate, s);
-        case 128: return bf16 ? launch_decode_dt<128, true>(p, gate, s) : launch_decode_dt<128, false>(p, gate, s);
-        default: return hipErrorInvalidValue;
+template <int DK, int DV>
+static hipError_t launch_decode_kv(const DecodeParams& p, bool bf16, int gate, hipStream_t s) {
+    return bf16 ? launch_decode_dt<DK, DV, true>(p, gate, s) : launch_decode_dt<DK, DV, false>(p, gate, s);
+}
+
+hipError_t launch_decode(const DecodeParams& p, int dk, int dv, bool bf16, int gate, hipStream_t s) {
+    if (dk == dv) {
+        switch (dk) {
+            case 16: return launch_decode_kv<16, 16>(p, bf16, gate, s);
+            case 32: return launch_decode_kv<32, 32>(p, bf16, gate, s);
+            case 64: return launch_decode_kv<64, 64>(p, bf16, gate, s);
+            case 128: return launch_decode_kv<128, 128>(p, bf16, gate, s);
+            default: return hipErrorInvalidValue;
+        }
     }
+    if (dk == 64 && dv == 128) return launch_decode_kv<64, 128>(p, bf16, gate, s);
+    if (dk == 128 && dv == 64) return launch_decode_kv<128, 64>(p, bf16, gate, s);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace la

@@ -77,26 +77,31 @@ size_t workspace_bytes(const la_desc* d, const Plan& pl) { return slot_bytes(d, 
 size_t order_bytes(const la_desc* d) { return align16((size_t)d->B * sizeof(int)); }
 
 bool supported_d(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+// d_k != d_v: 64 and 128 either way (prefill in bf16, decode in both types)
+bool mixed_pair(const la_desc* d) {
+    return (d->dk == 64 && d->dv == 128) || (d->dk == 128 && d->dv == 64);
+}
 // Chunk lengths of the prefill: multiples of 16 from 16 to 128; above 64
-// only where the 128-token tile is built.
+// only where the 128-token tile is built (d_k == d_v).
 bool supported_chunk(const la_desc* d, int c) {
     if (c < 16 || c > 128 || c % 16 != 0) return false;
-    return c <= 64 || la::chunk_tile128_rt(d->dk, d->dtype == LA_BF16);
+    return c <= 64 || (d->dk == d->dv && la::chunk_tile128_rt(d->dk, d->dtype == LA_BF16));
 }
 la_status check_chunk(const la_desc* d, int c) {
     if (c < 16 || c > 128 || c % 16 != 0)
         return fail(LA_ERR_UNSUPPORTED, "chunk must be a multiple of 16 in [16, 128] (got %d)", c);
     if (!supported_chunk(d, c))
         return fail(LA_ERR_UNSUPPORTED,
-                    "chunks above 64 are built for bf16 at dk <= 64 and fp32 at dk <= 32 "
-                    "(chunk %d, dk %d)", c, d->dk);
+                    "chunks above 64 are built for dk == dv, bf16 at dk <= 64 and fp32 at "
+                    "dk <= 32 (chunk %d, dk %d, dv %d)", c, d->dk, d->dv);
     return LA_OK;
 }
 
 // mfma: the shape runs on matrix cores (every prefill-like path), where
 // bf16 operands need d_k >= 32; the decode step streams the state on the
-// vector units and takes bf16 at every built width
-la_status check_desc(const la_desc* d, bool mfma = true) {
+// vector units and takes bf16 at every built width.  mixed: the entry point
+// is built for d_k != d_v (the prefill in bf16, the decode step).
+la_status check_desc(const la_desc* d, bool mfma = true, bool mixed = false) {
     if (!d) return fail(LA_ERR_INVALID, "descriptor is NULL");
     if (d->B < 1 || d->H < 1 || d->L < 1 || d->dk < 1 || d->dv < 1)
         return fail(LA_ERR_INVALID, "dimensions must be >= 1 (B=%d H=%d L=%d dk=%d dv=%d)", d->B,
@@ -110,9 +115,11 @@ la_status check_desc(const la_desc* d, bool mfma = true) {
     if (d->segments < 0) return fail(LA_ERR_INVALID, "segments must be >= 0");
     if ((long long)d->B * d->H > (1LL << 24))
         return fail(LA_ERR_UNSUPPORTED, "B*H = %lld exceeds 2^24", (long long)d->B * d->H);
-    if (!supported_d(d->dk) || d->dk != d->dv)
-        return fail(LA_ERR_UNSUPPORTED, "built shapes need dk == dv in {16,32,64,128} (dk=%d dv=%d)",
-                    d->dk, d->dv);
+    if (!supported_d(d->dk) || !supported_d(d->dv) ||
+        (d->dk != d->dv && !(mixed && mixed_pair(d) && (d->dtype == LA_BF16 || !mfma))))
+        return fail(LA_ERR_UNSUPPORTED,
+                    "built shapes: dk == dv in {16,32,64,128}; dk, dv = 64, 128 either way for the "
+                    "bf16 prefill and the decode step (dk=%d dv=%d)", d->dk, d->dv);
     if (mfma && d->dtype == LA_BF16 && d->dk < 32)
         return fail(LA_ERR_UNSUPPORTED, "bf16 prefill inputs need dk >= 32 (dk=%d)", d->dk);
     // kernels address one (b,h) slice of a tensor with 32-bit byte offsets
@@ -198,6 +205,9 @@ hipError_t timed_launch(int kernel, hipStream_t s, F&& launch) {
 hipError_t chunk_launch(const la_desc* d, const la::ChunkParams& p, int chunk, int gate, int pass,
                         hipStream_t s, int nblocks, bool robust = false) {
     const bool bf16 = d->dtype == LA_BF16;
+    if (d->dk != d->dv)
+        return d->dk == 64 ? la::launch_chunk_bf16_k64v128(p, chunk, gate, pass, s, nblocks, robust)
+                           : la::launch_chunk_bf16_k128v64(p, chunk, gate, pass, s, nblocks, robust);
     switch (d->dk) {
         case 16: return la::launch_chunk_f32_d16(p, chunk, gate, pass, s, nblocks, robust);
         case 32: return bf16 ? la::launch_chunk_bf16_d32(p, chunk, gate, pass, s, nblocks, robust)
@@ -266,7 +276,7 @@ la_desc plan_desc(const la_desc* d, bool packed, int max_seqlen) {
 }
 
 la_status check_varlen(const la_desc* d, const int* cu_seqlens, int max_seqlen) {
-    const la_status st = check_desc(d);
+    const la_status st = check_desc(d, true, true);
     if (st != LA_OK) return st;
     if (!cu_seqlens) return fail(LA_ERR_INVALID, "cu_seqlens must be non-NULL");
     if (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u)
@@ -434,7 +444,7 @@ la_status chunk_fwd_impl(const la_desc* d, const int* cu_seqlens, int max_seqlen
             return chunk_launch(d, p, chunk, gate_mode, la::PASS_STATE, s, BH * (pl.P - 1));
         });
         if (e != hipSuccess) return hip_fail(e, "state pass launch");
-        e = timed_launch(la::K_STATE_SCAN, s, [&] { return la::launch_state_scan(p, d->dk, false, s); });
+        e = timed_launch(la::K_STATE_SCAN, s, [&] { return la::launch_state_scan(p, d->dk, d->dv, false, s); });
         if (e != hipSuccess) return hip_fail(e, "segment scan launch");
     }
     const int pass = states ? la::PASS_MAIN_STORE : gn ? la::PASS_MAIN_NORM : la::PASS_MAIN;
@@ -473,12 +483,12 @@ const char* la_last_error_message(void) { return g_errmsg; }
 int la_version(void) { return LA_VERSION; }
 
 int la_chunk_fwd_segments(const la_desc* d, int chunk) {
-    if (check_desc(d) != LA_OK || !supported_chunk(d, chunk)) return 0;
+    if (check_desc(d, true, true) != LA_OK || !supported_chunk(d, chunk)) return 0;
     return make_plan(d, chunk).P;
 }
 
 size_t la_chunk_fwd_workspace_bytes(const la_desc* d, int chunk) {
-    if (check_desc(d) != LA_OK || !supported_chunk(d, chunk)) return 0;
+    if (check_desc(d, true, true) != LA_OK || !supported_chunk(d, chunk)) return 0;
     return workspace_bytes(d, make_plan(d, chunk));
 }
 
@@ -487,7 +497,7 @@ la_status la_chunk_fwd(const la_desc* d, const void* q, const void* k, const voi
                        const float* z0, int chunk, void* out, float* S_final, float* z_final,
                        void* workspace, size_t ws_bytes, void* stream) {
     g_errmsg[0] = '\0';
-    const la_status st = check_desc(d);
+    const la_status st = check_desc(d, true, true);
     if (st != LA_OK) return st;
     return chunk_fwd_impl(d, nullptr, 0, q, k, v, gate_mode, gamma_or_log_alpha, S0, z0, chunk,
                           nullptr, out, S_final, z_final, workspace, ws_bytes, stream);
@@ -498,7 +508,7 @@ la_status la_chunk_fwd_noalloc(const la_desc* d, const void* q, const void* k, c
                                const float* z0, int chunk, void* out, float* S_final,
                                float* z_final, void* stream) {
     g_errmsg[0] = '\0';
-    const la_status st = check_desc(d);
+    const la_status st = check_desc(d, true, true);
     if (st != LA_OK) return st;
     return chunk_fwd_impl(d, nullptr, 0, q, k, v, gate_mode, gamma_or_log_alpha, S0, z0, chunk,
                           nullptr, out, S_final, z_final, nullptr, 0, stream, nullptr, true);
@@ -510,7 +520,7 @@ la_status la_chunk_fwd_groupnorm(const la_desc* d, const void* q, const void* k,
                                  float* S_final, float* z_final, void* workspace, size_t ws_bytes,
                                  void* stream) {
     g_errmsg[0] = '\0';
-    const la_status st = check_desc(d);
+    const la_status st = check_desc(d, true, true);
     if (st != LA_OK) return st;
     if (!gn) return fail(LA_ERR_INVALID, "the group-norm description is NULL");
     return chunk_fwd_impl(d, nullptr, 0, q, k, v, gate_mode, gamma_or_log_alpha, S0, z0, chunk,
@@ -556,7 +566,7 @@ la_status la_chunk_fwd_varlen(const la_desc* d, const int* cu_seqlens, int max_s
 }
 
 size_t la_chunk_fwd_varlen_workspace_bytes(const la_desc* d, int max_seqlen, int chunk) {
-    if (check_desc(d) != LA_OK || !supported_chunk(d, chunk) || max_seqlen < 1 || max_seqlen > d->L)
+    if (check_desc(d, true, true) != LA_OK || !supported_chunk(d, chunk) || max_seqlen < 1 || max_seqlen > d->L)
         return 0;
     const la_desc dp = plan_desc(d, true, max_seqlen);
     return workspace_bytes(&dp, make_plan(&dp, chunk)) + order_bytes(d);
@@ -643,7 +653,7 @@ la_status la_chunk_bwd(const la_desc* d, const void* q, const void* k, const voi
             return chunk_launch(d, p, chunk, gate_mode, la::PASS_STATE, s, BH * (pl.P - 1));
         });
         if (e != hipSuccess) return hip_fail(e, "state pass launch");
-        e = timed_launch(la::K_STATE_SCAN, s, [&] { return la::launch_state_scan(p, d->dk, false, s); });
+        e = timed_launch(la::K_STATE_SCAN, s, [&] { return la::launch_state_scan(p, d->dk, d->dv, false, s); });
         if (e != hipSuccess) return hip_fail(e, "segment scan launch");
     }
     if (!states) {
@@ -666,7 +676,7 @@ la_status la_chunk_bwd(const la_desc* d, const void* q, const void* k, const voi
             return chunk_launch(d, p, chunk, gate_mode, la::PASS_STATE_REV, s, BH * (pl.P - 1));
         });
         if (e != hipSuccess) return hip_fail(e, "reverse state pass launch");
-        e = timed_launch(la::K_STATE_SCAN, s, [&] { return la::launch_state_scan(p, d->dk, true, s); });
+        e = timed_launch(la::K_STATE_SCAN, s, [&] { return la::launch_state_scan(p, d->dk, d->dv, true, s); });
         if (e != hipSuccess) return hip_fail(e, "reverse segment scan launch");
     }
 
@@ -765,7 +775,7 @@ la_status la_decode_step(const la_desc* d, const void* q, const void* k, const v
                          int gate_mode, const float* gate, float* S, float* z, void* out,
                          void* stream) {
     g_errmsg[0] = '\0';
-    la_status st = check_desc(d, false);
+    la_status st = check_desc(d, false, true);
     if (st != LA_OK) return st;
     if (d->L != 1) return fail(LA_ERR_INVALID, "decode needs L == 1 (L=%d)", d->L);
     if (!q || !k || !v || !out || !S) return fail(LA_ERR_INVALID, "q, k, v, S and out must be non-NULL");
@@ -791,7 +801,7 @@ la_status la_decode_step(const la_desc* d, const void* q, const void* k, const v
     p.normalize = d->normalize;
     hipStream_t s = static_cast<hipStream_t>(stream);
     const hipError_t e = timed_launch(la::K_DECODE, s, [&] {
-        return la::launch_decode(p, d->dk, d->dtype == LA_BF16, gate_mode, s);
+        return la::launch_decode(p, d->dk, d->dv, d->dtype == LA_BF16, gate_mode, s);
     });
     if (e != hipSuccess) return hip_fail(e, "decode launch");
     return LA_OK;

@@ -130,8 +130,10 @@ LA_DECLARE_CHUNK_LAUNCHER(launch_chunk_f32_d128)
 LA_DECLARE_CHUNK_LAUNCHER(launch_chunk_bf16_d32)
 LA_DECLARE_CHUNK_LAUNCHER(launch_chunk_bf16_d64)
 LA_DECLARE_CHUNK_LAUNCHER(launch_chunk_bf16_d128)
+LA_DECLARE_CHUNK_LAUNCHER(launch_chunk_bf16_k64v128)    // d_k = 64, d_v = 128
+LA_DECLARE_CHUNK_LAUNCHER(launch_chunk_bf16_k128v64)    // d_k = 128, d_v = 64
 #undef LA_DECLARE_CHUNK_LAUNCHER
-hipError_t launch_state_scan(const ChunkParams& p, int d, bool rev, hipStream_t s);
+hipError_t launch_state_scan(const ChunkParams& p, int dk, int dv, bool rev, hipStream_t s);
 // Packed sequences: order[0..B) = the sequences by decreasing chunk count.
 hipError_t launch_seq_order(const int* cu_seqlens, int B, int T, int chunk, int max_seqlen,
                             int* order, hipStream_t s);
@@ -155,6 +157,6 @@ LA_DECLARE_BWD_LAUNCHER(launch_bwd_bf16_d32)
 LA_DECLARE_BWD_LAUNCHER(launch_bwd_bf16_d64)
 LA_DECLARE_BWD_LAUNCHER(launch_bwd_bf16_d128)
 #undef LA_DECLARE_BWD_LAUNCHER
-hipError_t launch_decode(const DecodeParams& p, int d, bool bf16, int gate, hipStream_t s);
+hipError_t launch_decode(const DecodeParams& p, int dk, int dv, bool bf16, int gate, hipStream_t s);
 
 }  // namespace la

@@ -7,21 +7,29 @@
 namespace la {
 
 template <bool REV>
-hipError_t launch_state_scan_dir(const ChunkParams& p, int d, hipStream_t s) {
-    const int nbx = (d * d / 4 + 255) / 256;
+hipError_t launch_state_scan_dir(const ChunkParams& p, int dk, int dv, hipStream_t s) {
+    const int nbx = (dk * dv / 4 + 255) / 256;
     const dim3 grid((unsigned)(nbx * p.BH)), block(256);
-    switch (d) {
-        case 16: hipLaunchKernelGGL((state_scan_kernel<16, 16, REV>), grid, block, 0, s, p); break;
-        case 32: hipLaunchKernelGGL((state_scan_kernel<32, 32, REV>), grid, block, 0, s, p); break;
-        case 64: hipLaunchKernelGGL((state_scan_kernel<64, 64, REV>), grid, block, 0, s, p); break;
-        case 128: hipLaunchKernelGGL((state_scan_kernel<128, 128, REV>), grid, block, 0, s, p); break;
-        default: return hipErrorInvalidValue;
+    if (dk == dv) {
+        switch (dk) {
+            case 16: hipLaunchKernelGGL((state_scan_kernel<16, 16, REV>), grid, block, 0, s, p); break;
+            case 32: hipLaunchKernelGGL((state_scan_kernel<32, 32, REV>), grid, block, 0, s, p); break;
+            case 64: hipLaunchKernelGGL((state_scan_kernel<64, 64, REV>), grid, block, 0, s, p); break;
+            case 128: hipLaunchKernelGGL((state_scan_kernel<128, 128, REV>), grid, block, 0, s, p); break;
+            default: return hipErrorInvalidValue;
+        }
+    } else if (dk == 64 && dv == 128) {
+        hipLaunchKernelGGL((state_scan_kernel<64, 128, REV>), grid, block, 0, s, p);
+    } else if (dk == 128 && dv == 64) {
+        hipLaunchKernelGGL((state_scan_kernel<128, 64, REV>), grid, block, 0, s, p);
+    } else {
+        return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
-hipError_t launch_state_scan(const ChunkParams& p, int d, bool rev, hipStream_t s) {
-    return rev ? launch_state_scan_dir<true>(p, d, s) : launch_state_scan_dir<false>(p, d, s);
+hipError_t launch_state_scan(const ChunkParams& p, int dk, int dv, bool rev, hipStream_t s) {
+    return rev ? launch_state_scan_dir<true>(p, dk, dv, s) : launch_state_scan_dir<false>(p, dk, dv, s);
 }
 
 }  // namespace la

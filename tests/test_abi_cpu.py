@@ -349,3 +349,32 @@ def test_train_forward_validation():
     assert call(d, nbytes=100) == api.LA_ERR_INVALID
     assert api.la_chunk_bwd(d, A, A, A, A, 0, None, None, None, MIS, A, A, A, None, None, A,
                             1 << 40, None) == api.LA_ERR_INVALID
+
+
+@pytest.mark.parametrize("dk,dv", [(64, 128), (128, 64)])
+def test_dk_ne_dv_pairs(dk, dv):
+    # the bf16 prefill (chunks up to 64) and the decode step in either type
+    d = _desc(dk=dk, dv=dv, L=1000)
+    P = api.la_chunk_fwd_segments(d, 64)
+    assert P == 4          # 16 chunks, 2 pairs: ceil(256 / 2) segments, at most 16 / 4
+    assert api.la_chunk_fwd_workspace_bytes(d, 64) == 2 * P * (dk * dv + 2 * dk) * 4 + 2 * P * 4
+    assert api.la_chunk_fwd_workspace_bytes(d, 128) == 0
+    assert _chunk(d, chunk=128) == api.LA_ERR_UNSUPPORTED
+    assert _chunk(_desc(dk=dk, dv=dv, dtype=api.LA_F32)) == api.LA_ERR_UNSUPPORTED
+    for dt in (api.LA_BF16, api.LA_F32):
+        dd = _desc(dk=dk, dv=dv, L=1, dtype=dt)
+        assert api.la_decode_step(dd, A, A, A, 0, None, None, None, A, None) == api.LA_ERR_INVALID
+        assert "non-NULL" in api.la_last_error_message()
+    # the backward, the training forward and the delta rule need dk == dv
+    assert _bwd(d) == api.LA_ERR_UNSUPPORTED
+    assert api.la_chunk_bwd_workspace_bytes(d) == 0
+    assert api.la_chunk_train_states_bytes(d) == 0
+    assert api.la_delta_fwd(d, A, A, A, A, None, A, None, None) == api.LA_ERR_UNSUPPORTED
+
+
+def test_other_dk_dv_pairs_unsupported():
+    assert _chunk(_desc(dk=32, dv=64)) == api.LA_ERR_UNSUPPORTED
+    assert api.la_decode_step(_desc(dk=32, dv=64, L=1), A, A, A, 0, None, A, None, A,
+                              None) == api.LA_ERR_UNSUPPORTED
+    assert api.la_decode_step(_desc(dk=128, dv=16, L=1), A, A, A, 0, None, A, None, A,
+                              None) == api.LA_ERR_UNSUPPORTED
