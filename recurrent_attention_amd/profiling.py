@@ -6,6 +6,13 @@
 ``python -m recurrent_attention_amd.profiling counters <counter_collection.csv> ...``
     prints the per-dispatch average of each counter for each of the
     library's kernels from ``rocprofv3 --pmc`` CSVs (one file per pass).
+``python -m recurrent_attention_amd.profiling trace <kernel_trace.csv>``
+    the same table per launch shape (family, kernel, grid), from the
+    per-dispatch ``rocprofv3 --kernel-trace`` CSV, so that one kernel run
+    by several parts of a program is told apart by its grid.
+``python -m recurrent_attention_amd.profiling counters-md <counter_collection.csv> ...``
+    the per-dispatch means as a markdown table per kernel family, with the
+    matrix-core and LDS ratios derived from them (see ``derived``).
 ``python -m recurrent_attention_amd.profiling traffic --fetch F.csv --write W.csv
     --fetch-copy FC.csv --write-copy WC.csv --kernel NAME --copy-bytes N
     --out profiles/traffic_X.json --hash H``
@@ -64,6 +71,69 @@ def stats_table(path: str) -> str:
            "|---|---|---:|---:|---:|---:|"]
     for fam, name, n, avg, mn, mx in rows:
         out.append(f"| {fam} | `{name}` | {n} | {avg:.2f} | {mn:.2f} | {mx:.2f} |")
+    return "\n".join(out)
+
+
+def trace_table(path: str) -> str:
+    """calls / avg / min / max duration per (family, kernel, grid) from a
+    per-dispatch kernel-trace CSV."""
+    acc = defaultdict(list)
+    for r in csv.DictReader(open(path)):
+        fam = family(r["Kernel_Name"])
+        if fam in (None, "copy"):
+            continue
+        grid = int(r["Grid_Size_X"]) // max(int(r["Workgroup_Size_X"]), 1)
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        acc[(fam, r["Kernel_Name"], grid, int(r["Workgroup_Size_X"]))].append(dur)
+    out = ["| family | kernel | workgroups x threads | calls | avg us | min us | max us |",
+           "|---|---|---|---:|---:|---:|---:|"]
+    for (fam, name, grid, wg), d in sorted(acc.items(), key=lambda x: (x[0][0], x[0][2])):
+        out.append(f"| {fam} | `{name}` | {grid} x {wg} | {len(d)} | {sum(d) / len(d):.2f} | "
+                   f"{min(d):.2f} | {max(d):.2f} |")
+    return "\n".join(out)
+
+
+# MI355X: compute units, SIMDs per compute unit, bf16 flops per MFMA "MOP"
+CUS, SIMDS = 256, 4
+FLOPS_PER_MOP = 512
+
+
+def derived(cs):
+    """Ratios from the per-dispatch means of one kernel (None where a counter
+    is missing): GRBM_GUI_ACTIVE is summed over the 8 XCDs, so a dispatch's
+    busy cycles per XCD are GRBM / 8;
+      mfma_busy_pct   = SQ_VALU_MFMA_BUSY_CYCLES / (busy cycles x CUs x SIMDs)
+      bf16_flops      = 512 x SQ_INSTS_VALU_MFMA_MOPS_BF16 (matrix-core work done)
+      lds_conflict_pct = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE (cycles
+                         lost to bank conflicts per cycle of LDS index work)."""
+    g = cs.get("GRBM_GUI_ACTIVE")
+    out = {}
+    if g and "SQ_VALU_MFMA_BUSY_CYCLES" in cs:
+        out["mfma_busy_pct"] = 100.0 * cs["SQ_VALU_MFMA_BUSY_CYCLES"] / (g / 8 * CUS * SIMDS)
+    if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in cs:
+        out["bf16_flops"] = FLOPS_PER_MOP * cs["SQ_INSTS_VALU_MFMA_MOPS_BF16"]
+    if cs.get("SQ_LDS_IDX_ACTIVE") and "SQ_LDS_BANK_CONFLICT" in cs:
+        out["lds_conflict_pct"] = 100.0 * cs["SQ_LDS_BANK_CONFLICT"] / cs["SQ_LDS_IDX_ACTIVE"]
+    return out
+
+
+def counters_md(paths) -> str:
+    rows = []
+    for name, cs in counter_means(paths).items():
+        fam = family(name)
+        if fam in (None, "copy"):
+            continue
+        rows.append((fam, name, cs, derived(cs)))
+    out = []
+    for fam, name, cs, dv in sorted(rows):
+        out.append(f"**{fam}** `{name}`\n")
+        out.append("| counter | mean per dispatch |")
+        out.append("|---|---:|")
+        for k in sorted(cs):
+            out.append(f"| {k} | {cs[k]:.6g} |")
+        for k in sorted(dv):
+            out.append(f"| *{k}* | {dv[k]:.4g} |")
+        out.append("")
     return "\n".join(out)
 
 
@@ -134,6 +204,10 @@ def main(argv=None):
     s.add_argument("csv")
     c = sub.add_parser("counters")
     c.add_argument("csv", nargs="+")
+    tr = sub.add_parser("trace")
+    tr.add_argument("csv")
+    cm = sub.add_parser("counters-md")
+    cm.add_argument("csv", nargs="+")
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
     t.add_argument("--write", required=True)
@@ -147,6 +221,10 @@ def main(argv=None):
     a = ap.parse_args(argv)
     if a.cmd == "stats":
         print(stats_table(a.csv))
+    elif a.cmd == "trace":
+        print(trace_table(a.csv))
+    elif a.cmd == "counters-md":
+        print(counters_md(a.csv))
     elif a.cmd == "counters":
         for name, cs in counter_means(a.csv).items():
             fam = family(name)

@@ -61,3 +61,36 @@ def test_other_kernels_have_their_families():
         for n in hits:
             assert family(n) == fam, (n, family(n))
     assert family("void la::(anonymous namespace)::seq_order_kernel(int const*, int, int, int, int, int*)") == "seq_order"
+
+
+def test_trace_table_groups_launch_shapes(tmp_path):
+    # one kernel run with two grids (two parts of a program) gives two rows,
+    # each averaging its own dispatches; the copy and unknown kernels drop out
+    from recurrent_attention_amd.profiling import trace_table
+    name = "void la::decode_kernel<128, 128, true, 1>(la::DecodeParams)"
+    rows = [(name, 8192 * 512, 512, 0, 100_000), (name, 8192 * 512, 512, 0, 120_000),
+            (name, 32 * 512, 512, 0, 7_000), ("__amd_rocclr_copyBuffer", 64, 64, 0, 9),
+            ("void other(int)", 64, 64, 0, 9)]
+    path = tmp_path / "t_kernel_trace.csv"
+    with open(path, "w") as f:
+        f.write("Kernel_Name,Grid_Size_X,Workgroup_Size_X,Start_Timestamp,End_Timestamp\n")
+        for n, g, w, a, b in rows:
+            f.write(f'"{n}",{g},{w},{a},{b}\n')
+    out = trace_table(str(path)).splitlines()
+    assert len(out) == 4
+    assert "| 32 x 512 | 1 | 7.00 | 7.00 | 7.00 |" in out[2]
+    assert "| 8192 x 512 | 2 | 110.00 | 100.00 | 120.00 |" in out[3]
+
+
+def test_derived_counter_ratios():
+    from recurrent_attention_amd.profiling import derived
+    # GRBM summed over 8 XCDs: 8000 -> 1000 busy cycles per XCD; 256 CUs x 4
+    # SIMDs x 1000 cycles = 1.024e6 SIMD-cycles, a quarter of them in MFMA
+    cs = {"GRBM_GUI_ACTIVE": 8000.0, "SQ_VALU_MFMA_BUSY_CYCLES": 256000.0,
+          "SQ_INSTS_VALU_MFMA_MOPS_BF16": 10.0, "SQ_LDS_BANK_CONFLICT": 5.0,
+          "SQ_LDS_IDX_ACTIVE": 50.0}
+    d = derived(cs)
+    assert d["mfma_busy_pct"] == 25.0
+    assert d["bf16_flops"] == 5120.0
+    assert d["lds_conflict_pct"] == 10.0
+    assert derived({}) == {}
