@@ -828,20 +828,30 @@ def main(argv=None):
         pre = bench_prefill(args, torch, api, workloads, args.workload)
         print(json.dumps(config_entry(pre)), flush=True)
         return 0
-    pre = bench_prefill(args, torch, api, workloads)
+    def part(name, fn):
+        t0 = time.perf_counter()
+        r = fn()
+        print(f"bench: {name} {time.perf_counter() - t0:.1f} s", file=sys.stderr, flush=True)
+        return r
+
+    pre = part("prefill", lambda: bench_prefill(args, torch, api, workloads))
     w_head = pre["w"].name
-    dec = None if args.no_decode else bench_decode(args, torch, api, workloads)
-    bwd = None if args.no_backward else bench_backward(args, torch, api, workloads)
-    vl = None if args.no_varlen else bench_varlen(args, torch, api, workloads)
-    sc = None if args.no_scalar else bench_prefill(args, torch, api, workloads,
-                                                   "scalar_gate_B1H16_L32768_d128")
-    ret = None if args.no_retention else bench_retention_groupnorm(args, torch, api, workloads)
+    dec = None if args.no_decode else part("decode", lambda: bench_decode(args, torch, api, workloads))
+    bwd = None if args.no_backward else part("backward", lambda: bench_backward(args, torch, api, workloads))
+    vl = None if args.no_varlen else part("varlen", lambda: bench_varlen(args, torch, api, workloads))
+    sc = None if args.no_scalar else part("scalar gate", lambda: bench_prefill(
+        args, torch, api, workloads, "scalar_gate_B1H16_L32768_d128"))
+    ret = None if args.no_retention else part("retention group norm", lambda: bench_retention_groupnorm(
+        args, torch, api, workloads))
     cfgs = {}
+    dec_z = None
     if not args.no_configs:
         for cname in PREFILL_CONFIGS:
-            cfgs[cname] = pre if cname == w_head else bench_prefill(args, torch, api, workloads, cname)
-        dec_z = None if args.no_decode else bench_decode(args, torch, api, workloads, True)
-    dl = None if args.no_delta else bench_delta(args, torch, api, workloads)
+            cfgs[cname] = pre if cname == w_head else part(cname, lambda: bench_prefill(
+                args, torch, api, workloads, cname))
+        dec_z = None if args.no_decode else part("decode with z", lambda: bench_decode(
+            args, torch, api, workloads, True))
+    dl = None if args.no_delta else part("delta", lambda: bench_delta(args, torch, api, workloads))
     w = pre["w"]
     line = {
         "metric": METRIC,
@@ -874,7 +884,8 @@ def main(argv=None):
         if dec is not None:
             line["configs"][dec["workload"]] = {k: dec[k] for k in (
                 "us_per_step", "value", "unit", "steps_per_s", "tokens_per_s", "roofline")}
-            line["configs"][dec_z["workload"]] = dec_z
+            if dec_z is not None:
+                line["configs"][dec_z["workload"]] = dec_z
     if dec is not None:
         line["decode"] = dec
     if bwd is not None:
