@@ -668,9 +668,9 @@ hipError_t launch_bwd_dt(const BwdParams& p, int gate, hipStream_t s) {
     do {                                                                                        \
         using Cfg = BwdCfg<D, C, BF, GG>;                                                       \
         if (p.phi_elu1)                                                                         \
-            hipLaunchKernelGGL((bwd_kernel<Cfg, true>), grid, dim3(Cfg::NT), 0, s, p);          \
+            LA_LAUNCH((bwd_kernel<Cfg, true>), grid, dim3(Cfg::NT), s, p);          \
         else                                                                                    \
-            hipLaunchKernelGGL((bwd_kernel<Cfg, false>), grid, dim3(Cfg::NT), 0, s, p);         \
+            LA_LAUNCH((bwd_kernel<Cfg, false>), grid, dim3(Cfg::NT), s, p);         \
         return hipGetLastError();                                                               \
     } while (0)
     if (gate == LA_GATE_NONE) LA_BWD_LAUNCH(LA_GATE_NONE);

@@ -1464,9 +1464,9 @@ hipError_t launch_chunk_dt(const ChunkParams& p, int chunk, int gate, int pass, 
     do {                                                                                   \
         using Cfg = ChunkCfg<DK, DV, CC, BF, GG, SO, NWV>;                                 \
         if (p.phi_elu1)                                                                    \
-            hipLaunchKernelGGL((chunk_kernel<Cfg, true, RV, ST, EP, RB>), dim3(nblocks), dim3(Cfg::NT), 0, s, p); \
+            LA_LAUNCH((chunk_kernel<Cfg, true, RV, ST, EP, RB>), dim3(nblocks), dim3(Cfg::NT), s, p); \
         else                                                                               \
-            hipLaunchKernelGGL((chunk_kernel<Cfg, false, RV, ST, EP, RB>), dim3(nblocks), dim3(Cfg::NT), 0, s, p); \
+            LA_LAUNCH((chunk_kernel<Cfg, false, RV, ST, EP, RB>), dim3(nblocks), dim3(Cfg::NT), s, p); \
         return hipGetLastError();                                                          \
     } while (0)
 // main passes under a vector gate exist twice: without and with the

@@ -122,10 +122,10 @@ void decode_kernel(const DecodeParams p) {
 template <int DK, int DV, bool BF>
 static hipError_t launch_decode_dt(const DecodeParams& p, int gate, hipStream_t s) {
     const dim3 grid(p.BH), block(DecodeShape<DK, DV>::NT);
-    if (gate == LA_GATE_NONE) hipLaunchKernelGGL((decode_kernel<DK, DV, BF, 0>), grid, block, 0, s, p);
-    else if (gate == LA_GATE_GAMMA) hipLaunchKernelGGL((decode_kernel<DK, DV, BF, 1>), grid, block, 0, s, p);
-    else if (gate == LA_GATE_DIAG) hipLaunchKernelGGL((decode_kernel<DK, DV, BF, 2>), grid, block, 0, s, p);
-    else if (gate == LA_GATE_SCALAR) hipLaunchKernelGGL((decode_kernel<DK, DV, BF, 3>), grid, block, 0, s, p);
+    if (gate == LA_GATE_NONE) LA_LAUNCH((decode_kernel<DK, DV, BF, 0>), grid, block, s, p);
+    else if (gate == LA_GATE_GAMMA) LA_LAUNCH((decode_kernel<DK, DV, BF, 1>), grid, block, s, p);
+    else if (gate == LA_GATE_DIAG) LA_LAUNCH((decode_kernel<DK, DV, BF, 2>), grid, block, s, p);
+    else if (gate == LA_GATE_SCALAR) LA_LAUNCH((decode_kernel<DK, DV, BF, 3>), grid, block, s, p);
     else return hipErrorInvalidValue;
     return hipGetLastError();
 }

@@ -512,10 +512,10 @@ constexpr int delta_chunk(int d, bool bf16) { return (!bf16 && d >= 128) ? 32 : 
 template <int D, bool BF>
 hipError_t launch_delta_dt(const DeltaParams& p, bool decode, hipStream_t s) {
     if (decode) {
-        hipLaunchKernelGGL((delta_decode_kernel<D, BF>), dim3(p.BH), dim3(DeltaDecodeShape<D>::NT), 0, s, p);
+        LA_LAUNCH((delta_decode_kernel<D, BF>), dim3(p.BH), dim3(DeltaDecodeShape<D>::NT), s, p);
     } else {
         using Cfg = DeltaCfg<D, delta_chunk(D, BF), BF>;
-        hipLaunchKernelGGL((delta_chunk_kernel<Cfg>), dim3(p.BH), dim3(Cfg::NT), 0, s, p);
+        LA_LAUNCH((delta_chunk_kernel<Cfg>), dim3(p.BH), dim3(Cfg::NT), s, p);
     }
     return hipGetLastError();
 }

@@ -14,6 +14,13 @@
 
 #include "la_internal.h"
 
+namespace la {
+LaunchEvents& launch_events() {
+    static thread_local LaunchEvents ev;
+    return ev;
+}
+}  // namespace la
+
 namespace {
 
 thread_local char g_errmsg[512] = "";
@@ -182,9 +189,11 @@ hipEvent_t take_event() {
     return e;
 }
 
-// Wraps one launch; records an event pair around it while profiling.
+// Wraps one launch; while profiling, the launch records an event pair
+// around its kernel (la::LA_LAUNCH).
 template <class F>
 hipError_t timed_launch(int kernel, hipStream_t s, F&& launch) {
+    (void)s;
     std::unique_lock<std::mutex> lk(g_prof_mu);
     if (!g_prof_on) {
         lk.unlock();
@@ -192,11 +201,9 @@ hipError_t timed_launch(int kernel, hipStream_t s, F&& launch) {
     }
     ProfRec rec{kernel, take_event(), take_event()};
     if (!rec.a || !rec.b) return hipErrorOutOfMemory;
-    hipError_t e = hipEventRecord(rec.a, s);
-    if (e != hipSuccess) return e;
-    e = launch();
-    if (e != hipSuccess) return e;
-    e = hipEventRecord(rec.b, s);
+    la::launch_events() = la::LaunchEvents{rec.a, rec.b};
+    const hipError_t e = launch();
+    la::launch_events() = la::LaunchEvents{};
     if (e != hipSuccess) return e;
     g_prof.push_back(rec);
     return hipSuccess;

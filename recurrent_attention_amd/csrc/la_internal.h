@@ -2,6 +2,7 @@
 // kernels, and the launch entry points each kernel file provides.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -116,6 +117,25 @@ enum KernelId {
     K_CHUNK_STORE = 4, K_BWD = 5, K_DELTA = 6, K_DELTA_DECODE = 7, K_SEQ_ORDER = 8,
     K_CHUNK_SUB = 9, K_COUNT = 10
 };
+
+// Event pair that the library's launches record around their kernel while
+// it profiles (hipExtLaunchKernel takes the timestamps from the kernel's own
+// dispatch, so no marker packet sits between an event and its kernel), or
+// nulls: set by the host API around one launch, per calling thread.
+struct LaunchEvents {
+    hipEvent_t start = nullptr, stop = nullptr;
+};
+LaunchEvents& launch_events();
+
+#define LA_LAUNCH(KERNEL, GRID, BLOCK, S, ...)                                                    \
+    do {                                                                                          \
+        const ::la::LaunchEvents& la_ev_ = ::la::launch_events();                                 \
+        if (la_ev_.start)                                                                         \
+            hipExtLaunchKernelGGL(KERNEL, GRID, BLOCK, 0, S, la_ev_.start, la_ev_.stop, 0,        \
+                                  __VA_ARGS__);                                                   \
+        else                                                                                      \
+            hipLaunchKernelGGL(KERNEL, GRID, BLOCK, 0, S, __VA_ARGS__);                           \
+    } while (0)
 
 // Launch hooks implemented in the kernel files.  Each returns hipSuccess or
 // the launch error; shapes have been validated by the caller.  The chunk

@@ -61,7 +61,7 @@ __global__ __launch_bounds__(kOrderThreads) void seq_order_kernel(const int* cu,
 hipError_t launch_seq_order(const int* cu_seqlens, int B, int T, int chunk, int max_seqlen,
                             int* order, hipStream_t s) {
     const int maxc = (max_seqlen + chunk - 1) / chunk;
-    hipLaunchKernelGGL(seq_order_kernel, dim3(1), dim3(kOrderThreads), 0, s, cu_seqlens, B, T, chunk,
+    LA_LAUNCH(seq_order_kernel, dim3(1), dim3(kOrderThreads), s, cu_seqlens, B, T, chunk,
                        maxc, order);
     return hipGetLastError();
 }

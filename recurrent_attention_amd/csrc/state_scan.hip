@@ -12,16 +12,16 @@ hipError_t launch_state_scan_dir(const ChunkParams& p, int dk, int dv, hipStream
     const dim3 grid((unsigned)(nbx * p.BH)), block(256);
     if (dk == dv) {
         switch (dk) {
-            case 16: hipLaunchKernelGGL((state_scan_kernel<16, 16, REV>), grid, block, 0, s, p); break;
-            case 32: hipLaunchKernelGGL((state_scan_kernel<32, 32, REV>), grid, block, 0, s, p); break;
-            case 64: hipLaunchKernelGGL((state_scan_kernel<64, 64, REV>), grid, block, 0, s, p); break;
-            case 128: hipLaunchKernelGGL((state_scan_kernel<128, 128, REV>), grid, block, 0, s, p); break;
+            case 16: LA_LAUNCH((state_scan_kernel<16, 16, REV>), grid, block, s, p); break;
+            case 32: LA_LAUNCH((state_scan_kernel<32, 32, REV>), grid, block, s, p); break;
+            case 64: LA_LAUNCH((state_scan_kernel<64, 64, REV>), grid, block, s, p); break;
+            case 128: LA_LAUNCH((state_scan_kernel<128, 128, REV>), grid, block, s, p); break;
             default: return hipErrorInvalidValue;
         }
     } else if (dk == 64 && dv == 128) {
-        hipLaunchKernelGGL((state_scan_kernel<64, 128, REV>), grid, block, 0, s, p);
+        LA_LAUNCH((state_scan_kernel<64, 128, REV>), grid, block, s, p);
     } else if (dk == 128 && dv == 64) {
-        hipLaunchKernelGGL((state_scan_kernel<128, 64, REV>), grid, block, 0, s, p);
+        LA_LAUNCH((state_scan_kernel<128, 64, REV>), grid, block, s, p);
     } else {
         return hipErrorInvalidValue;
     }
