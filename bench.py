@@ -294,7 +294,10 @@ def bench_prefill(args, torch, api, workloads, name=None):
     flops = prefill_flops(w)
     main_us = kern["chunk_main"]["avg_us"]
     achieved = bytes_alg / (main_us * 1e-6) / 1e9
-    traffic = measured_traffic(f"chunk_main_{w.name}", kernel_source_hash())
+    khash = kernel_source_hash()
+    traffic = measured_traffic(f"chunk_main_{w.name}", khash)
+    for fam in kern:
+        kern[fam]["traffic"] = measured_traffic(f"{fam}_{w.name}", khash)
     frac, floor_us = attainable_frac(w, ms_step)
     return {
         "w": w, "P": P, "ms_step": ms_step, "tokens_per_s": tokens / (ms_step * 1e-3),
@@ -326,7 +329,25 @@ def config_entry(pre):
             "segments": pre["P"],
             "kernels_avg_us": {k: (round(v["avg_us"], 2) if v["avg_us"] else None)
                                for k, v in pre["kernels"].items()},
+            "kernels_traffic_bytes": {k: (round(v["traffic"]) if v.get("traffic") else None)
+                                      for k, v in pre["kernels"].items() if v["avg_us"]},
+            "step_traffic_vs_algorithmic": step_traffic_ratio(pre),
             "roofline": pre["roofline"]}
+
+
+def step_traffic_ratio(pre):
+    """Measured HBM bytes of every launch of one step (from the committed
+    counter records of its kernels) over the algorithmic bytes, or None
+    when a launched kernel has no current record.  The sub-chunk kernel,
+    when no segment needs it, only reads one flag per workgroup."""
+    tot = 0.0
+    for fam, v in pre["kernels"].items():
+        if not v["avg_us"] or fam == "chunk_sub":
+            continue
+        if not v.get("traffic"):
+            return None
+        tot += v["traffic"]
+    return round(tot / pre["bytes"], 3)
 
 
 def backward_bytes(w):
@@ -875,6 +896,7 @@ def main(argv=None):
         "tflops": round(pre["flops"] / (pre["ms_step"] * 1e-3) / 1e12, 2),
         "pct_of_hbm_peak_step": round(pre["hbm_pct_step"], 2),
         "attainable_roofline_frac_step": round(pre["attainable_frac"], 4),
+        "step_traffic_vs_algorithmic": step_traffic_ratio(pre),
         "kernels_avg_us": {k: (round(v["avg_us"], 2) if v["avg_us"] else None)
                            for k, v in pre["kernels"].items()},
         "roofline": pre["roofline"],

@@ -104,7 +104,8 @@ def test_decode_retention_256x32_d128(with_z):
                      S0=to_host64(S0[bi, hi])[:, None],
                      z0=to_host64(z0[bi, hi])[:, None] if with_z else None, nthreads=8)
     got_o = to_host64(outs[:, bi, hi].permute(1, 0, 2))[:, None]
-    assert slice_rel_err(got_o, ref[0]) <= TOL[torch.bfloat16]
-    assert slice_rel_err(to_host64(S[bi, hi])[:, None], ref[1]) <= TOL[torch.bfloat16]
+    errs = {"out": slice_rel_err(got_o, ref[0]), "S": slice_rel_err(to_host64(S[bi, hi])[:, None], ref[1])}
     if with_z:
-        assert slice_rel_err(to_host64(z[bi, hi])[:, None], ref[2]) <= TOL[torch.bfloat16]
+        errs["z"] = slice_rel_err(to_host64(z[bi, hi])[:, None], ref[2])
+    print(f"decode 1000 steps, 64 sampled pairs, z={with_z}: {errs}")
+    assert all(e <= TOL[torch.bfloat16] for e in errs.values()), errs
