@@ -65,7 +65,10 @@ struct BwdCfg {
     static constexpr int KPL = T::KPL, MK = T::MK;
     static constexpr int UE = 16 / (int)sizeof(E);     // elements per 16-byte unit
     static constexpr int DU = D / UE, TU = C / UE;     // units per row
-    static constexpr int DMASK = (DU < 8 ? DU : 8) - 1;
+    // the D-wide tiles swizzle over up to 16 units (256 bytes): the LDS has
+    // 64 four-byte banks, so 16 consecutive rows of a fragment read fall on
+    // 16 different bank groups
+    static constexpr int DMASK = (DU < 16 ? DU : 16) - 1;
     static constexpr int TMASK = (TU < 8 ? TU : 8) - 1;
     static constexpr int RW = 4 * (int)sizeof(E) / 4;  // words of a 4-channel run
     static_assert(D % 16 == 0 && C % MK == 0 && C % 16 == 0, "tile shape");

@@ -94,7 +94,10 @@ struct ChunkCfg {
     static constexpr int UE = 16 / (int)sizeof(E);     // elements per 16-byte unit
     static constexpr int QU = DK / UE;                 // units per q/k row
     static constexpr int TU = CP / UE;                 // units per transposed row / P row
-    static constexpr int QMASK = (QU < 8 ? QU : 8) - 1;
+    // q/k tiles swizzle over up to 16 units (256 bytes): the LDS has 64
+    // four-byte banks, so 16 consecutive rows of a fragment read fall on 16
+    // different bank groups
+    static constexpr int QMASK = (QU < 16 ? QU : 16) - 1;
     static constexpr int TMASK = (TU < 8 ? TU : 8) - 1;
     // global -> register mapping: each thread owns a run of CW adjacent key
     // channels (VW value channels) over KTPG (VTPG) consecutive tokens and

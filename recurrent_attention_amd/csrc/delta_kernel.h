@@ -48,7 +48,10 @@ struct DeltaCfg {
     static constexpr int KPL = T::KPL, MK = T::MK;
     static constexpr int UE = 16 / (int)sizeof(E);
     static constexpr int DU = D / UE, TU = C / UE;
-    static constexpr int DMASK = (DU < 8 ? DU : 8) - 1;
+    // the D-wide tiles swizzle over up to 16 units (256 bytes): the LDS has
+    // 64 four-byte banks, so 16 consecutive rows of a fragment read fall on
+    // 16 different bank groups
+    static constexpr int DMASK = (DU < 16 ? DU : 16) - 1;
     static constexpr int TMASK = (TU < 8 ? TU : 8) - 1;
     static constexpr int RUNS = D / 4;                 // 4-channel runs per token row
     static constexpr int RPP = NT / RUNS;              // token rows per load pass (16)
