@@ -45,6 +45,8 @@ struct DeltaCfg {
     static constexpr int NW = D / 16;                  // waves: one value block each
     static constexpr int NT = 64 * NW;
     static constexpr int TB = C / 16, NBLK = C / 16, MB = D / 16;
+    // waves that own a block column of the off-diagonal solve
+    static constexpr int NXS = NBLK < 2 ? 1 : (NW < NBLK - 1 ? NW : NBLK - 1);
     static constexpr int KPL = T::KPL, MK = T::MK;
     static constexpr int UE = 16 / (int)sizeof(E);
     static constexpr int DU = D / UE, TU = C / UE;
@@ -68,17 +70,23 @@ struct DeltaSmem {
     static constexpr int C = Cfg::C, D = Cfg::D;
     alignas(16) E q[C][D];        // Q   [t][swizzled i]
     alignas(16) E k[C][D];        // K   [s][swizzled i]
-    alignas(16) E v[C][D];        // V   [s][swizzled n]
-    alignas(16) E w[C][D];        // W   [s][swizzled i]
-    alignas(16) E up[C][D];       // U'  [s][swizzled n]
+    alignas(16) E vu[C][D];       // V, then U' in its place: [s][swizzled n]
     alignas(16) E pm[C][C];       // P = Q K^T * mask  [t][swizzled s]
     alignas(16) E tm[C][C];       // T   [s][swizzled j]
-    // fp32 rows padded by 4 so that 16 lanes reading one column of 16
-    // rows spread over the banks
+    // A (strictly lower) and N = (I + A)^-1 in fp32, rows padded by 4 so
+    // that 16 lanes reading one column of 16 rows spread over the banks (only
+    // their lower blocks are ever used); W, formed once both are spent, in
+    // the same bytes
     static constexpr int LDP = C + 4;
-    alignas(16) float lm[C][LDP];   // A (strictly lower)
-    alignas(16) float nm[C][LDP];   // (I + A)^-1, lower blocks
-    alignas(16) float xs[Cfg::NW][16][16];   // per-wave staging of a 16 x 16 block
+    union Solve {
+        struct Blocks {
+            float lm[C][LDP];
+            float nm[C][LDP];
+        } b;
+        E w[C][D];                // W   [s][swizzled i]
+    };
+    alignas(16) Solve sv;
+    alignas(16) float xs[Cfg::NXS][16][16];   // per-wave staging of a 16 x 16 block
     float beta[C];
 };
 
@@ -96,6 +104,9 @@ __global__ __launch_bounds__(Cfg::NT) void delta_chunk_kernel(const DeltaParams 
     using Frag = typename Cfg::Frag;
 
     __shared__ DeltaSmem<Cfg> sm;
+    auto& lm = sm.sv.b.lm;
+    auto& nm = sm.sv.b.nm;
+    auto& ws = sm.sv.w;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -112,14 +123,12 @@ __global__ __launch_bounds__(Cfg::NT) void delta_chunk_kernel(const DeltaParams 
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.beta + rows0, (uint32_t)L * 4);
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(reinterpret_cast<E*>(p.out) + rows0 * D, (uint32_t)L * D * ES);
 
-    // the triangular tiles: only their lower parts are ever written
+    // the triangular tiles: only their lower parts are ever written (A and N
+    // have their lower blocks written in full in every chunk, and nothing
+    // reads the rest)
     for (int i = tid; i < C * C; i += Cfg::NT) {
         (&sm.pm[0][0])[i] = E(0);
         (&sm.tm[0][0])[i] = E(0);
-    }
-    for (int i = tid; i < C * DeltaSmem<Cfg>::LDP; i += Cfg::NT) {
-        (&sm.lm[0][0])[i] = 0.f;
-        (&sm.nm[0][0])[i] = 0.f;
     }
 
     // state block of this wave: rows 16 mb + 4 g + i, column n0 + r
@@ -165,7 +174,7 @@ __global__ __launch_bounds__(Cfg::NT) void delta_chunk_kernel(const DeltaParams 
             const int pos = bw_pos<Cfg, DM>(t, 4 * run);
             lds_store_words(&sm.q[t][pos], qr[ps]);
             lds_store_words(&sm.k[t][pos], kr[ps]);
-            lds_store_words(&sm.v[t][pos], vr[ps]);
+            lds_store_words(&sm.vu[t][pos], vr[ps]);
         }
         if (tid < C) sm.beta[tid] = __uint_as_float(br);
         __syncthreads();
@@ -189,7 +198,7 @@ __global__ __launch_bounds__(Cfg::NT) void delta_chunk_kernel(const DeltaParams 
                     float xl[4];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) xl[i] = s0 + i < t ? bt * ag[i] : 0.f;
-                    *reinterpret_cast<float4*>(&sm.lm[t][s0]) = make_float4(xl[0], xl[1], xl[2], xl[3]);
+                    *reinterpret_cast<float4*>(&lm[t][s0]) = make_float4(xl[0], xl[1], xl[2], xl[3]);
                 }
         }
         __syncthreads();
@@ -216,7 +225,7 @@ __global__ __launch_bounds__(Cfg::NT) void delta_chunk_kernel(const DeltaParams 
                         for (int m = 0; m < 4; ++m) {
                             if (4 * m >= rr) break;
                             const int cc = 4 * m + qq;
-                            const float a = sm.lm[b0 + rr][b0 + cc];   // 0 for cc >= rr
+                            const float a = lm[b0 + rr][b0 + cc];   // 0 for cc >= rr
                             part += a * xo[m];
                         }
                         part += dpp_row<0xB1>(part);   // quad_perm [1,0,3,2]
@@ -228,7 +237,7 @@ __global__ __launch_bounds__(Cfg::NT) void delta_chunk_kernel(const DeltaParams 
 #pragma unroll
                     for (int m = 0; m < 4; ++m) {
                         const int row = b0 + 4 * m + qq;
-                        sm.nm[row][b0 + j] = xo[m];
+                        nm[row][b0 + j] = xo[m];
                         sm.tm[row][bw_pos<Cfg, TM>(row, b0 + j)] = T::fromf(xo[m] * bj);
                     }
                 }
@@ -314,7 +323,7 @@ __global__ __launch_bounds__(Cfg::NT) void delta_chunk_kernel(const DeltaParams 
                     xm[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                     for (int k4 = 0; k4 < 4; ++k4)
-                        xm[m] = F::mma(sm.lm[bi + r][bm + 4 * k4 + g], sm.nm[bm + 4 * k4 + g][bj + r], xm[m]);
+                        xm[m] = F::mma(lm[bi + r][bm + 4 * k4 + g], nm[bm + 4 * k4 + g][bj + r], xm[m]);
                 }
                 f32x4_t x = xm[jb];
 #pragma unroll
@@ -327,11 +336,11 @@ __global__ __launch_bounds__(Cfg::NT) void delta_chunk_kernel(const DeltaParams 
                 f32x4_t y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int k4 = 0; k4 < 4; ++k4)
-                    y = F::mma(sm.nm[bi + r][bi + 4 * k4 + g], sm.xs[wave][4 * k4 + g][r], y);
+                    y = F::mma(nm[bi + r][bi + 4 * k4 + g], sm.xs[wave][4 * k4 + g][r], y);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int row = bi + 4 * g + i;
-                    sm.nm[row][bj + r] = -y[i];
+                    nm[row][bj + r] = -y[i];
                     sm.tm[row][bw_pos<Cfg, TM>(row, bj + r)] = T::fromf(-y[i] * betj);
                 }
                 __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -349,7 +358,8 @@ __global__ __launch_bounds__(Cfg::NT) void delta_chunk_kernel(const DeltaParams 
         }
         __syncthreads();
 
-        // ---- W^T = K^T T^T: wave w takes key channels [16w, 16w+16)
+        // ---- W^T = K^T T^T: wave w takes key channels [16w, 16w+16) (W goes
+        // into the bytes of A and N, which are spent)
 #pragma unroll
         for (int sb = 0; sb < TB; ++sb) {
             f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
@@ -359,29 +369,32 @@ __global__ __launch_bounds__(Cfg::NT) void delta_chunk_kernel(const DeltaParams 
                              row_frag<Cfg, TM>(&sm.tm[0][0], C, 16 * sb, kk * MK, lane), acc);
             const int s = 16 * sb + r;
             float xw[4] = {acc[0], acc[1], acc[2], acc[3]};
-            store_run<BF16, 4>(&sm.w[s][bw_pos<Cfg, DM>(s, n0 + 4 * g)], xw);
+            store_run<BF16, 4>(&ws[s][bw_pos<Cfg, DM>(s, n0 + 4 * g)], xw);
         }
         __syncthreads();
 
-        // ---- U'^T = V^T T^T - S^T W^T for this wave's value columns
+        // ---- U'^T = V^T T^T - S^T W^T for this wave's value columns, written
+        // over its own columns of V (read whole first)
+        Frag vf[C / MK];
+#pragma unroll
+        for (int kk = 0; kk < C / MK; ++kk) vf[kk] = tr_frag<Cfg, DM>(&sm.vu[0][0], D, kk * MK, n0, lane);
 #pragma unroll
         for (int sb = 0; sb < TB; ++sb) {
-            f32x4_t acc = state_times(&sm.w[0][0], sb, f32x4_t{0.f, 0.f, 0.f, 0.f});
+            f32x4_t acc = state_times(&ws[0][0], sb, f32x4_t{0.f, 0.f, 0.f, 0.f});
             acc = -acc;
 #pragma unroll
             for (int kk = 0; kk <= (16 * sb + 15) / MK; ++kk)
-                acc = T::mma(tr_frag<Cfg, DM>(&sm.v[0][0], D, kk * MK, n0, lane),
-                             row_frag<Cfg, TM>(&sm.tm[0][0], C, 16 * sb, kk * MK, lane), acc);
+                acc = T::mma(vf[kk], row_frag<Cfg, TM>(&sm.tm[0][0], C, 16 * sb, kk * MK, lane), acc);
             const int s = 16 * sb + r;
             float xu[4] = {acc[0], acc[1], acc[2], acc[3]};
-            store_run<BF16, 4>(&sm.up[s][bw_pos<Cfg, DM>(s, n0 + 4 * g)], xu);
+            store_run<BF16, 4>(&sm.vu[s][bw_pos<Cfg, DM>(s, n0 + 4 * g)], xu);
         }
-        __syncthreads();
+        // (no barrier: each wave reads back only its own columns of U')
 
         // ---- O^T = S^T Q^T + U'^T P^T, then S += K^T U'
         Frag uf[C / MK];
 #pragma unroll
-        for (int kk = 0; kk < C / MK; ++kk) uf[kk] = tr_frag<Cfg, DM>(&sm.up[0][0], D, kk * MK, n0, lane);
+        for (int kk = 0; kk < C / MK; ++kk) uf[kk] = tr_frag<Cfg, DM>(&sm.vu[0][0], D, kk * MK, n0, lane);
 #pragma unroll
         for (int tb = 0; tb < TB; ++tb) {
             f32x4_t acc = wave != 0 ? oq[tb] : state_times(&sm.q[0][0], tb, oq[tb]);
