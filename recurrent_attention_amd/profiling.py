@@ -26,6 +26,7 @@ import argparse
 import csv
 import json
 import re
+import statistics
 import sys
 from collections import defaultdict
 
@@ -75,8 +76,9 @@ def stats_table(path: str) -> str:
 
 
 def trace_table(path: str) -> str:
-    """calls / avg / min / max duration per (family, kernel, grid) from a
-    per-dispatch kernel-trace CSV."""
+    """calls / avg / median / min / max duration per (family, kernel, grid)
+    from a per-dispatch kernel-trace CSV (the median is robust to the slower
+    first launches of a run)."""
     acc = defaultdict(list)
     for r in csv.DictReader(open(path)):
         fam = family(r["Kernel_Name"])
@@ -85,11 +87,11 @@ def trace_table(path: str) -> str:
         grid = int(r["Grid_Size_X"]) // max(int(r["Workgroup_Size_X"]), 1)
         dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
         acc[(fam, r["Kernel_Name"], grid, int(r["Workgroup_Size_X"]))].append(dur)
-    out = ["| family | kernel | workgroups x threads | calls | avg us | min us | max us |",
-           "|---|---|---|---:|---:|---:|---:|"]
+    out = ["| family | kernel | workgroups x threads | calls | avg us | median us | min us | max us |",
+           "|---|---|---|---:|---:|---:|---:|---:|"]
     for (fam, name, grid, wg), d in sorted(acc.items(), key=lambda x: (x[0][0], x[0][2])):
         out.append(f"| {fam} | `{name}` | {grid} x {wg} | {len(d)} | {sum(d) / len(d):.2f} | "
-                   f"{min(d):.2f} | {max(d):.2f} |")
+                   f"{statistics.median(d):.2f} | {min(d):.2f} | {max(d):.2f} |")
     return "\n".join(out)
 
 

@@ -65,7 +65,8 @@ def test_other_kernels_have_their_families():
 
 def test_trace_table_groups_launch_shapes(tmp_path):
     # one kernel run with two grids (two parts of a program) gives two rows,
-    # each averaging its own dispatches; the copy and unknown kernels drop out
+    # each with the mean and median of its own dispatches; the copy and
+    # unknown kernels drop out
     from recurrent_attention_amd.profiling import trace_table
     name = "void la::decode_kernel<128, 128, true, 1>(la::DecodeParams)"
     rows = [(name, 8192 * 512, 512, 0, 100_000), (name, 8192 * 512, 512, 0, 120_000),
@@ -78,8 +79,8 @@ def test_trace_table_groups_launch_shapes(tmp_path):
             f.write(f'"{n}",{g},{w},{a},{b}\n')
     out = trace_table(str(path)).splitlines()
     assert len(out) == 4
-    assert "| 32 x 512 | 1 | 7.00 | 7.00 | 7.00 |" in out[2]
-    assert "| 8192 x 512 | 2 | 110.00 | 100.00 | 120.00 |" in out[3]
+    assert "| 32 x 512 | 1 | 7.00 | 7.00 | 7.00 | 7.00 |" in out[2]
+    assert "| 8192 x 512 | 2 | 110.00 | 110.00 | 100.00 | 120.00 |" in out[3]
 
 
 def test_derived_counter_ratios():
