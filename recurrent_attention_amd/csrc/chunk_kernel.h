@@ -193,11 +193,18 @@ __device__ __forceinline__ int qk_phys(int row, int pp) {
     const int u = pp / Cfg::UE, e = pp % Cfg::UE;
     return ((u ^ (row & Cfg::QMASK)) * Cfg::UE) + e;
 }
-// Position of token s in row `row` of a transposed tile (kt, vt).
+// Position of token s in row `row` of a transposed tile (kt, vt).  With
+// 128-byte rows (bf16, 64-token chunks) the units are XOR-swizzled by
+// row ^ (row >> 2): the 16-row fragment reads of the state update and of
+// the value operands then run without bank conflicts, where row ^ (row >> 3)
+// left every one of them two-way conflicted (measured per access pattern on
+// gfx950; the 8-byte stores that fill the tile are two-way under every XOR
+// swizzle tried).
 template <class Cfg>
 __device__ __forceinline__ int tr_pos(int row, int s) {
+    constexpr int SH = Cfg::CP * (int)sizeof(typename Cfg::E) == 128 ? 2 : 3;
     const int u = s / Cfg::UE, e = s % Cfg::UE;
-    return ((u ^ ((row ^ (row >> 3)) & Cfg::TMASK)) * Cfg::UE) + e;
+    return ((u ^ ((row ^ (row >> SH)) & Cfg::TMASK)) * Cfg::UE) + e;
 }
 // Position of token s in row t of the score tile.
 template <class Cfg>
