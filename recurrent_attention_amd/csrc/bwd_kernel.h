@@ -101,13 +101,24 @@ __device__ __forceinline__ typename Cfg::Frag mem_frag(const typename Cfg::E* M,
     return Cfg::T::load(M + (size_t)row * ld + col);
 }
 // Position of (row, col) in the fp32 G tile: row-major, 16-byte units
-// XOR-swizzled by (row ^ row / 16), so that 16 consecutive rows, and rows
-// 16 apart, fall on different banks.
-template <int D>
+// XOR-swizzled by the row.  For the bf16 kernel at d = 128 (512-byte rows)
+// the unit XOR is (row & 3) | (r2 ^ r3) << 2 | r2 << 3 (r_i: bit i of the
+// row): on gfx950 the column reads of G (4-byte reads of rows 8 apart, two
+// passes of 32 lanes over 128 bytes of banks) were two-way bank-conflicted
+// under row ^ row / 16, and this keeps the 16-row float4 reads and writes
+// conflict-free as well.  Elsewhere row ^ row / 16, so that 16 consecutive
+// rows, and rows 16 apart, fall on different banks.
+template <class Cfg>
 __device__ __forceinline__ int g_pos(int row, int col) {
+    constexpr int D = Cfg::D;
     constexpr int U = D / 4;
     constexpr int M = (U < 16 ? U : 16) - 1;
-    return row * D + ((((col >> 2) ^ ((row ^ (row >> 4)) & M)) << 2) | (col & 3));
+    int x;
+    if constexpr (Cfg::BF16 && D == 128)
+        x = (row & 3) | ((((row >> 2) ^ (row >> 3)) & 1) << 2) | (((row >> 2) & 1) << 3);
+    else
+        x = (row ^ (row >> 4)) & M;
+    return row * D + ((((col >> 2) ^ x) << 2) | (col & 3));
 }
 
 // The KPL k-slots of G's row `row` from column `col` on, as floats.
@@ -115,12 +126,12 @@ template <class Cfg>
 __device__ __forceinline__ void g_row(const float* gm, int row, int col, float* x) {
     constexpr int D = Cfg::D;
     if constexpr (Cfg::BF16) {
-        const float4 a = *reinterpret_cast<const float4*>(gm + g_pos<D>(row, col));
-        const float4 b = *reinterpret_cast<const float4*>(gm + g_pos<D>(row, col + 4));
+        const float4 a = *reinterpret_cast<const float4*>(gm + g_pos<Cfg>(row, col));
+        const float4 b = *reinterpret_cast<const float4*>(gm + g_pos<Cfg>(row, col + 4));
         x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
         x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
     } else {
-        x[0] = gm[g_pos<D>(row, col)];
+        x[0] = gm[g_pos<Cfg>(row, col)];
     }
 }
 
@@ -213,7 +224,7 @@ __global__ __launch_bounds__(Cfg::NT) void bwd_kernel(const BwdParams p) {
 #pragma unroll
         for (int j = 0; j < GQ; ++j) {
             const int u = tid + j * Cfg::NT;
-            *reinterpret_cast<float4*>(&sm.gm[g_pos<D>(u / (D / 4), 4 * (u % (D / 4)))]) = x[j];
+            *reinterpret_cast<float4*>(&sm.gm[g_pos<Cfg>(u / (D / 4), 4 * (u % (D / 4)))]) = x[j];
         }
     }
 
@@ -511,7 +522,7 @@ __global__ __launch_bounds__(Cfg::NT) void bwd_kernel(const BwdParams p) {
 #pragma unroll
                 for (int j = 0; j < KPL; ++j) {
                     const int i = kk * MK + KPL * g + j;
-                    xg[j] = sm.gm[g_pos<D>(i, 16 * nb + r)];
+                    xg[j] = sm.gm[g_pos<Cfg>(i, 16 * nb + r)];
                     if constexpr (VG) xg[j] *= sm.ebr[i];
                 }
                 const Frag a = to_frag<Cfg>(xg);
@@ -635,7 +646,7 @@ __global__ __launch_bounds__(Cfg::NT) void bwd_kernel(const BwdParams p) {
                 const float fo = VG ? sm.er[gi] : 1.f;
 #pragma unroll
                 for (int m = 0; m < NG; ++m) {
-                    float4* pg = reinterpret_cast<float4*>(&sm.gm[g_pos<D>(gi, 16 * (nb0 + m) + 4 * g)]);
+                    float4* pg = reinterpret_cast<float4*>(&sm.gm[g_pos<Cfg>(gi, 16 * (nb0 + m) + 4 * g)]);
                     float4 x = *pg;
                     x.x = fo * (fg * x.x + gacc[ii][m][0]);
                     x.y = fo * (fg * x.y + gacc[ii][m][1]);
@@ -656,7 +667,7 @@ __global__ __launch_bounds__(Cfg::NT) void bwd_kernel(const BwdParams p) {
 #pragma unroll
         for (int j = 0; j < GQ; ++j) {
             const int u = tid + j * Cfg::NT;
-            out[u] = *reinterpret_cast<const float4*>(&sm.gm[g_pos<D>(u / (D / 4), 4 * (u % (D / 4)))]);
+            out[u] = *reinterpret_cast<const float4*>(&sm.gm[g_pos<Cfg>(u / (D / 4), 4 * (u % (D / 4)))]);
         }
     }
 }
