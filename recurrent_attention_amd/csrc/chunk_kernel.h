@@ -142,10 +142,17 @@ template <class Cfg>
 struct ChunkSmem {
     using E = typename Cfg::E;
     static constexpr int CQ = Cfg::SONLY ? 1 : Cfg::C;
+    // the scalar-gate passes without outputs keep two sets of the per-chunk
+    // tiles and factors (chunk parity), so that a chunk's tiles are filled
+    // while the previous chunk's state products still read theirs, with no
+    // barrier between: 75 -> 66 us for the state pass of the 32768-token,
+    // 16-head scalar-gate workload.  The same for the diagonal-gate and
+    // gamma state passes measured 2% slower, so those keep one set.
+    static constexpr int NBUF = (Cfg::SONLY && Cfg::GATE == LA_GATE_SCALAR) ? 2 : 1;
     alignas(16) E q[CQ][Cfg::DK];        // Qh, [t][permuted, swizzled i]
     alignas(16) E k[CQ][Cfg::DK];        // Kh, [s][permuted, swizzled i]
-    alignas(16) E kt[Cfg::DK][Cfg::CP];  // Kt, [i][swizzled s]
-    alignas(16) E vt[Cfg::DV][Cfg::CP];  // V^T, [n][swizzled s]
+    alignas(16) E kt[NBUF][Cfg::DK][Cfg::CP];  // Kt, [i][swizzled s]
+    alignas(16) E vt[NBUF][Cfg::DV][Cfg::CP];  // V^T, [n][swizzled s]
     alignas(16) E p[CQ][Cfg::CP];        // masked scores, [t][swizzled s]
     // per-wave log2-gate sums (a2), and the group norm's per-wave token sums
     // (store phase of the main pass): live between different barriers
@@ -157,7 +164,7 @@ struct ChunkSmem {
     static constexpr int DKV = Cfg::VGM ? Cfg::DK : 1;
     // also the sub-chunk normaliser (after op1, before the store phase)
     union {
-        alignas(16) float tot[Cfg::NW][Cfg::DK];
+        alignas(16) float tot[NBUF][Cfg::NW][Cfg::DK];
         float2 gnp[Cfg::SONLY ? 1 : Cfg::NW][Cfg::SONLY ? 1 : Cfg::C];
         float zs[TBV][DKV];
     };
@@ -166,9 +173,9 @@ struct ChunkSmem {
     alignas(16) float sa[TBV][DKV];
     alignas(16) float sb[TBV][DKV];
     int wslow[Cfg::VGM ? Cfg::NW : 1];
-    alignas(16) float scale[Cfg::DK];    // per-row state factor applied this chunk
-    alignas(16) float pre[Cfg::DK];      // this chunk's before/after factors
-    alignas(16) float post[Cfg::DK];
+    alignas(16) float scale[NBUF][Cfg::DK];    // per-row state factor applied this chunk
+    alignas(16) float pre[NBUF][Cfg::DK];      // this chunk's before/after factors
+    alignas(16) float post[NBUF][Cfg::DK];
     alignas(16) float segsum[Cfg::DK];   // DIAG: summed log2-gates of this segment
     float gpow[Cfg::C + 2];              // gamma^j
     float z[Cfg::DK];
@@ -292,6 +299,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
     constexpr int KCP = Cfg::KCP, KTG = Cfg::KTG, KTPG = Cfg::KTPG, CW = Cfg::CW;
     constexpr int VCP = Cfg::VCP, VTPG = Cfg::VTPG, VW = Cfg::VW;
     constexpr bool SONLY = Cfg::SONLY, BF16 = Cfg::BF16;
+    constexpr int NBUF = ChunkSmem<Cfg>::NBUF;
     constexpr int ES = (int)sizeof(typename Cfg::E);
     // lanes that share one normaliser row (NRL) or one z channel (NCL): the
     // workgroup's threads over the rows or channels, 1 to 16
@@ -393,10 +401,10 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
     // ---- one-time LDS set-up: zero the tiles whose padding is read as zeros
     {
         if constexpr (CP > C) {
-            E* z0p = &sm.kt[0][0];
-            for (int i = tid; i < DK * CP; i += Cfg::NT) z0p[i] = E(0);
-            E* z1p = &sm.vt[0][0];
-            for (int i = tid; i < DV * CP; i += Cfg::NT) z1p[i] = E(0);
+            E* z0p = &sm.kt[0][0][0];
+            for (int i = tid; i < NBUF * DK * CP; i += Cfg::NT) z0p[i] = E(0);
+            E* z1p = &sm.vt[0][0][0];
+            for (int i = tid; i < NBUF * DV * CP; i += Cfg::NT) z1p[i] = E(0);
         }
         if constexpr (!SONLY) {
             E* z2p = &sm.p[0][0];
@@ -442,7 +450,8 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
     // segment bookkeeping of the ktg == 0 threads lives in LDS: the previous
     // chunk's after-factor (post) and the segment's summed log2-gates
     if (tid < DK) {
-        sm.post[tid] = 1.0f;
+#pragma unroll
+        for (int b = 0; b < NBUF; ++b) sm.post[b][tid] = 1.0f;
         sm.segsum[tid] = 0.0f;
     }
     float seg_g = 1.0f;                  // GAMMA: product of gamma^c
@@ -533,13 +542,13 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
     // element type: rows times the after-factor still pending (diagonal
     // gate), then a 4x4 transpose within each lane quad so that every lane
     // writes four consecutive columns of one row
-    auto store_state = [&](int slot) {
+    auto store_state = [&](int slot, int bsel) {
         E* rows = reinterpret_cast<E*>(p.st_rows) + ((size_t)bh * p.st_slots + slot) * SS;
         const int q4 = lane & 3;
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
             f32x4_t f = {1.f, 1.f, 1.f, 1.f};
-            if constexpr (VG) f = *reinterpret_cast<const f32x4_t*>(&sm.post[16 * mb + 4 * g]);
+            if constexpr (VG) f = *reinterpret_cast<const f32x4_t*>(&sm.post[bsel][16 * mb + 4 * g]);
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
                 float x[4] = {accS[mb][nb][0] * f[0], accS[mb][nb][1] * f[1],
@@ -555,6 +564,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
     // PD iterations ahead
     auto step = [&](const int ci, ChunkRegs& rg) -> bool {
         const int c = cof(ci);
+        const int bsel = NBUF > 1 ? (ci & 1) : 0;   // this chunk's tile and factor set
         const int t0 = c * CR;
         const int clen = min(CR, L - t0);
         if constexpr (!Cfg::PREFETCH) {
@@ -620,8 +630,10 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
                 wsum[i] = wsum[0];
                 gmid[i] = gmid[0];
             }
-            __syncthreads();  // the previous chunk is done with every LDS tile
-            if (lane < KCP) lds_store_words<CW>(&sm.tot[wave][CW * kcp], pack_run<false, CW>(wsum));
+            // the previous chunk is done with every LDS tile (with two sets,
+            // this chunk's set was last read before the previous barrier)
+            if constexpr (NBUF == 1) __syncthreads();
+            if (lane < KCP) lds_store_words<CW>(&sm.tot[bsel][wave][CW * kcp], pack_run<false, CW>(wsum));
             if constexpr (Cfg::VGM) {
                 // for the sub-chunk path: the in-wave prefix at each block's
                 // eighth and last token, left by the run that ends there
@@ -642,9 +654,9 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
                 if (lane == 0) sm.wslow[wave] = wbad ? 1 : 0;
             }
         }
-        // NONE/GAMMA: the previous chunk is done with every LDS tile.
-        // DIAG: the wave sums are visible.
-        __syncthreads();
+        // NONE/GAMMA: the previous chunk is done with every LDS tile (not
+        // needed with two sets).  DIAG: the wave sums are visible.
+        if constexpr (VG || NBUF == 1) __syncthreads();
 
         // this group's offset (exclusive prefix over the chunk), the
         // chunk-middle reference and the chunk total, in log2 units
@@ -664,7 +676,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
             float x[NW][CW];
 #pragma unroll
             for (int w2 = 0; w2 < NW; ++w2) {
-                const float* tv = &sm.tot[w2][CW * kcp];
+                const float* tv = &sm.tot[bsel][w2][CW * kcp];
                 if constexpr (GATE == LA_GATE_SCALAR) {
 #pragma unroll
                     for (int i = 0; i < CW; ++i) x[w2][i] = tv[0];
@@ -824,7 +836,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
             }
 #pragma unroll
             for (int i = 0; i < CW; ++i)
-                store_pairs<Cfg, KTPG>(&sm.kt[CW * kcp + i][0], CW * kcp + i, ktg * KTPG, kp[i]);
+                store_pairs<Cfg, KTPG>(&sm.kt[bsel][CW * kcp + i][0], CW * kcp + i, ktg * KTPG, kp[i]);
             // V^T: regroup the loaded channel runs into token pairs
             W vp[VW][VTPG / 2];
 #pragma unroll
@@ -833,7 +845,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
                 for (int i = 0; i < VW; ++i) vp[i][m] = token_pair<Cfg>(rg.v[2 * m], rg.v[2 * m + 1], i);
 #pragma unroll
             for (int i = 0; i < VW; ++i)
-                store_pairs<Cfg, VTPG>(&sm.vt[VW * vcp + i][0], VW * vcp + i, vtg * VTPG, vp[i]);
+                store_pairs<Cfg, VTPG>(&sm.vt[bsel][VW * vcp + i][0], VW * vcp + i, vtg * VTPG, vp[i]);
             if constexpr (BACKAGG && VG) {
 #pragma unroll
                 for (int i = 0; i < CW; ++i) eacc[i] += gtot[i];
@@ -859,15 +871,15 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
                                 po[i] = __builtin_amdgcn_exp2f(REV ? gref[i] : gtot[i] - gref[i]);
                             }
                         }
-                        sc[i] = sm.post[row] * pr[i];
+                        sc[i] = sm.post[NBUF > 1 ? bsel ^ 1 : 0][row] * pr[i];
                     }
                 } else if constexpr (GATE == LA_GATE_GAMMA && !BACKAGG) {
 #pragma unroll
                     for (int i = 0; i < CW; ++i) sc[i] = pr[i] = sm.gpow[clen];
                 }
-                lds_store_words<CW>(&sm.scale[CW * kcp], pack_run<false, CW>(sc));
-                lds_store_words<CW>(&sm.pre[CW * kcp], pack_run<false, CW>(pr));
-                lds_store_words<CW>(&sm.post[CW * kcp], pack_run<false, CW>(po));
+                lds_store_words<CW>(&sm.scale[bsel][CW * kcp], pack_run<false, CW>(sc));
+                lds_store_words<CW>(&sm.pre[bsel][CW * kcp], pack_run<false, CW>(pr));
+                lds_store_words<CW>(&sm.post[bsel][CW * kcp], pack_run<false, CW>(po));
             }
         }
 
@@ -950,7 +962,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
                         sm.zs[j][tid] = fa * zz;
                         float cs = 0.f;
                         for (int s2 = 16 * j; s2 < 16 * j + 16; ++s2)
-                            cs += T::tof(sm.kt[tid][tr_pos<Cfg>(tid, s2)]);
+                            cs += T::tof(sm.kt[bsel][tid][tr_pos<Cfg>(tid, s2)]);
                         zz = fb * fa * zz + cs;
                     }
                     sm.z[tid] = zz;
@@ -984,7 +996,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
                     for (int n = 0; n < DK / NRL; ++n) {
                         const int i = part + n * NRL;
                         float zz = sm.z[i];
-                        if constexpr (VG) zz *= sm.pre[i];
+                        if constexpr (VG) zz *= sm.pre[bsel][i];
                         dq += T::tof(sm.q[t][qk_pos<Cfg>(t, i)]) * zz;
                     }
                     if constexpr (GATE == LA_GATE_GAMMA) dq *= sm.gpow[t + 1];
@@ -1001,9 +1013,9 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
             if (i < DK) {
                 float cs = 0.f;
 #pragma unroll NUNR
-                for (int n = 0; n < C / NCL; ++n) cs += T::tof(sm.kt[i][tr_pos<Cfg>(i, part + n * NCL)]);
+                for (int n = 0; n < C / NCL; ++n) cs += T::tof(sm.kt[bsel][i][tr_pos<Cfg>(i, part + n * NCL)]);
                 cs = lane_group_sum<NCL>(cs);
-                if (part == 0) sm.z[i] = sm.post[i] * (sm.pre[i] * sm.z[i] + cs);
+                if (part == 0) sm.z[i] = sm.post[bsel][i] * (sm.pre[bsel][i] * sm.z[i] + cs);
             }
         }
 
@@ -1014,10 +1026,10 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
                 const int row = colbase + 16 * nb + r;
-                vf[kk][nb] = T::load(&sm.vt[row][tr_pos<Cfg>(row, kk * MK + KPL * g)]);
+                vf[kk][nb] = T::load(&sm.vt[bsel][row][tr_pos<Cfg>(row, kk * MK + KPL * g)]);
             }
 
-        if constexpr (VG) scale_rows<Cfg>(accS, sm.scale, g);
+        if constexpr (VG) scale_rows<Cfg>(accS, sm.scale[bsel], g);
 
         if constexpr (!SONLY) {
             // ---- op2: O^T = S'^T Qh^T (+ per-token decay) + V^T P^T
@@ -1089,7 +1101,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
                 // operands are read again from LDS.
                 auto vfrag = [&](int kk, int nb) {
                     const int row = colbase + 16 * nb + r;
-                    return T::load(&sm.vt[row][tr_pos<Cfg>(row, kk * MK + KPL * g)]);
+                    return T::load(&sm.vt[bsel][row][tr_pos<Cfg>(row, kk * MK + KPL * g)]);
                 };
 #pragma unroll 1
                 for (int j = 0; j < TB; ++j) {
@@ -1191,7 +1203,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
 #pragma unroll
                         for (int u = 0; u < KPB; ++u) {
                             const int kk = (16 * j) / MK + u;
-                            Frag a = T::load(&sm.kt[row][tr_pos<Cfg>(row, kk * MK + KPL * g)]);
+                            Frag a = T::load(&sm.kt[bsel][row][tr_pos<Cfg>(row, kk * MK + KPL * g)]);
                             // a bf16 contraction spans blocks 2kk and 2kk+1
                             // (lane groups 0-1 and 2-3): keep block j's half
                             if constexpr (MK > 16) {
@@ -1280,14 +1292,14 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
         }
 
         // ---- op3: state update (the sub-chunk path has done it block by block)
-        if constexpr (GATE == LA_GATE_GAMMA) scale_rows<Cfg>(accS, sm.scale, g);
+        if constexpr (GATE == LA_GATE_GAMMA) scale_rows<Cfg>(accS, sm.scale[bsel], g);
         if (!(SUB && slow)) {
 #pragma unroll
             for (int mb = 0; mb < MB; ++mb) {
                 const int row = 16 * mb + r;
 #pragma unroll
                 for (int kk = 0; kk < CP / MK; ++kk) {
-                    const Frag a = T::load(&sm.kt[row][tr_pos<Cfg>(row, kk * MK + KPL * g)]);
+                    const Frag a = T::load(&sm.kt[bsel][row][tr_pos<Cfg>(row, kk * MK + KPL * g)]);
 #pragma unroll
                     for (int nb = 0; nb < NB; ++nb) accS[mb][nb] = T::mma(a, vf[kk][nb], accS[mb][nb]);
                 }
@@ -1297,7 +1309,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
         // next segment is stored by that segment's workgroup)
         if constexpr (STORE) {
             const int nxt = c + 1;
-            if (nxt < c_end || seg == P - 1) store_state(nxt);
+            if (nxt < c_end || seg == P - 1) store_state(nxt, bsel);
         }
         // the loop's back-edge follows: the compiler's wait states after the
         // last state products do not always survive it (the assembly check
@@ -1311,7 +1323,7 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
         // diagonal after-factor of a previous chunk is 1 here)
         if (c_begin < c_end) {
             __syncthreads();   // sm.post set up
-            store_state(c_begin);
+            store_state(c_begin, 0);
         }
     }
     {
@@ -1341,10 +1353,11 @@ __global__ __launch_bounds__(Cfg::NT) void chunk_kernel(const ChunkParams p) {
             }
         }
     }
-    // DIAG: the last chunk's after-factor
+    // DIAG: the last chunk's after-factor (in the set of the last chunk
+    // walked; both sets hold ones before the first)
     if constexpr (VG) {
         __syncthreads();
-        scale_rows<Cfg>(accS, sm.post, g);
+        scale_rows<Cfg>(accS, sm.post[NBUF > 1 ? (c_end - 1) & 1 : 0], g);
     }
 
     // ---- epilogue
