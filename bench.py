@@ -809,7 +809,7 @@ def main(argv=None):
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, "
-              f"WORLD_SIZE={world}); multi-GPU sharding is not part of this build.",
+              f"WORLD_SIZE={world}); sharding over several GPUs is designed, not implemented.",
               file=sys.stderr)
         return 2
 
