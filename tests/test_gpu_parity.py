@@ -116,11 +116,14 @@ def test_chunk_fwd_initial_state(mode):
     check(got, ref, torch.bfloat16, f"S0 mode={mode}")
 
 
+# 11 chunks: 1 to 11 chunks a segment, odd and even counts (the scalar-gate
+# state pass alternates two tile sets by chunk parity)
 @pytest.mark.parametrize("segments", [1, 2, 3, 0, 11])
-def test_segmentations_agree(segments):
-    inp = _inputs(1, 2, 11 * 64 - 5, 128, torch.bfloat16, DIAG, seed=3, state=True)
-    got, ref = run_pair(inp, DIAG, 64, S0=inp["S0"], segments=segments)
-    check(got, ref, torch.bfloat16, f"segments={segments}")
+@pytest.mark.parametrize("mode", [DIAG, SCALAR])
+def test_segmentations_agree(segments, mode):
+    inp = _inputs(1, 2, 11 * 64 - 5, 128, torch.bfloat16, mode, seed=3, state=True)
+    got, ref = run_pair(inp, mode, 64, S0=inp["S0"], segments=segments)
+    check(got, ref, torch.bfloat16, f"segments={segments} mode={mode}")
 
 
 @pytest.mark.parametrize("L", [1, 15, 16, 17, 63, 64, 65, 128])
