@@ -10,19 +10,22 @@
 // standard triangular factorisation of the product of the chunk's erase
 // matrices, restated): for a chunk of C tokens with state S before it,
 //   A  = strict_lower(diag(beta) K K^T),  T = (I + A)^-1 diag(beta)
-//   W  = T K,  U = T V,  U' = U - W S
+//   U' = T (V - K S)
 //   O  = Q S + (Q K^T * inclusive causal mask) U',   S <- S + K^T U'
 // because the chunk's product of (I - beta k k^T) factors is I - K^T W and
-// its accumulated writes are K^T U.  Everything but T is a dense product on
-// the matrix cores; T is formed in fp32 by blocked forward substitution
-// (16 x 16 diagonal blocks inverted by one lane per column, the blocks
-// below them by fp32 matrix-core products, one block column per wave).
+// its accumulated writes are K^T U, with W = T K and U = T V (so that
+// U' = U - W S; W itself is never formed).  Everything but T is a dense
+// product on the matrix cores; T is formed in fp32 by blocked forward
+// substitution (16 x 16 diagonal blocks inverted by one lane per column, the
+// blocks below them by fp32 matrix-core products, one block column per wave).
 //
 // One workgroup per (b,h) runs the chunks in order (the chunk-to-chunk map
 // S -> (I - K^T W) S + K^T U is a full d_k x d_k matrix, so the segment
 // split of the gated kernels does not carry over cheaply).  Wave w owns
 // value columns [16w, 16w+16): its state block stays in fp32 accumulators
-// and it produces those columns of U' and of the outputs.
+// and it produces those columns of V - K S, U' and the outputs, all three
+// in registers (a matrix-core result becomes the next product's operand
+// with its token index permuted, the other operand read to match).
 //
 // Decode: one workgroup per (b,h) streams its fp32 state once:
 //   u = S^T k, w = S^T q (one reduction pass), S += beta k (v - u)^T,
@@ -45,8 +48,6 @@ struct DeltaCfg {
     static constexpr int NW = D / 16;                  // waves: one value block each
     static constexpr int NT = 64 * NW;
     static constexpr int TB = C / 16, NBLK = C / 16, MB = D / 16;
-    // waves that own a block column of the off-diagonal solve
-    static constexpr int NXS = NBLK < 2 ? 1 : (NW < NBLK - 1 ? NW : NBLK - 1);
     static constexpr int KPL = T::KPL, MK = T::MK;
     static constexpr int UE = 16 / (int)sizeof(E);
     static constexpr int DU = D / UE, TU = C / UE;
@@ -70,32 +71,39 @@ struct DeltaSmem {
     static constexpr int C = Cfg::C, D = Cfg::D;
     alignas(16) E q[C][D];        // Q   [t][swizzled i]
     alignas(16) E k[C][D];        // K   [s][swizzled i]
-    alignas(16) E vu[C][D];       // V, then U' in its place: [s][swizzled n]
+    alignas(16) E v[C][D];        // V   [s][swizzled n]
     alignas(16) E pm[C][C];       // P = Q K^T * mask  [t][swizzled s]
     alignas(16) E tm[C][C];       // T   [s][swizzled j]
-    // A (strictly lower) and N = (I + A)^-1 in fp32, rows padded by 4 so
-    // that 16 lanes reading one column of 16 rows spread over the banks (only
-    // their lower blocks are ever used); W, formed once both are spent, in
-    // the same bytes
+    // A (strictly lower) and the diagonal blocks of N = (I + A)^-1 in fp32,
+    // rows padded by 4 so that 16 lanes reading one column of 16 rows spread
+    // over the banks (only those blocks are ever used)
     static constexpr int LDP = C + 4;
-    union Solve {
-        struct Blocks {
-            float lm[C][LDP];
-            float nm[C][LDP];
-        } b;
-        E w[C][D];                // W   [s][swizzled i]
-    };
-    alignas(16) Solve sv;
-    alignas(16) float xs[Cfg::NXS][16][16];   // per-wave staging of a 16 x 16 block
+    alignas(16) float lm[C][LDP];
+    alignas(16) float nm[C][LDP];
     float beta[C];
 };
+
+// Position of column `col` in row `row` of the C x C tiles (P and T).  Their
+// bf16 rows of 128 bytes XOR the unit index with row ^ (row >> 3): the tiles
+// are read in 8-byte row reads (16 rows, two half-units each, per pass of 32
+// lanes), which the plain row index leaves two-way conflicted (rows 8 apart
+// share their banks).
+template <class Cfg>
+__device__ __forceinline__ int cc_pos(int row, int col) {
+    if constexpr (Cfg::BF16 && Cfg::C == 64) {
+        const int u = col / Cfg::UE, e = col % Cfg::UE;
+        return ((u ^ ((row ^ (row >> 3)) & 7)) * Cfg::UE) + e;
+    } else {
+        return bw_pos<Cfg, Cfg::TMASK>(row, col);
+    }
+}
 
 template <class Cfg>
 __global__ __launch_bounds__(Cfg::NT) void delta_chunk_kernel(const DeltaParams p) {
     constexpr int D = Cfg::D, C = Cfg::C, TB = Cfg::TB, NW = Cfg::NW, NBLK = Cfg::NBLK;
     constexpr int MB = Cfg::MB, MK = Cfg::MK, KPL = Cfg::KPL, RW = Cfg::RW;
     constexpr int RUNS = Cfg::RUNS, NPASS = Cfg::NPASS, RPP = Cfg::RPP;
-    constexpr int DM = Cfg::DMASK, TM = Cfg::TMASK;
+    constexpr int DM = Cfg::DMASK;
     constexpr bool BF16 = Cfg::BF16;
     constexpr int ES = (int)sizeof(typename Cfg::E);
     using T = typename Cfg::T;
@@ -104,9 +112,8 @@ __global__ __launch_bounds__(Cfg::NT) void delta_chunk_kernel(const DeltaParams 
     using Frag = typename Cfg::Frag;
 
     __shared__ DeltaSmem<Cfg> sm;
-    auto& lm = sm.sv.b.lm;
-    auto& nm = sm.sv.b.nm;
-    auto& ws = sm.sv.w;
+    auto& lm = sm.lm;
+    auto& nm = sm.nm;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -123,9 +130,9 @@ __global__ __launch_bounds__(Cfg::NT) void delta_chunk_kernel(const DeltaParams 
     const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.beta + rows0, (uint32_t)L * 4);
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(reinterpret_cast<E*>(p.out) + rows0 * D, (uint32_t)L * D * ES);
 
-    // the triangular tiles: only their lower parts are ever written (A and N
-    // have their lower blocks written in full in every chunk, and nothing
-    // reads the rest)
+    // the triangular tiles: only their lower parts are ever written (the
+    // blocks of A and N that are used are written in full in every chunk,
+    // and nothing reads the rest)
     for (int i = tid; i < C * C; i += Cfg::NT) {
         (&sm.pm[0][0])[i] = E(0);
         (&sm.tm[0][0])[i] = E(0);
@@ -174,10 +181,100 @@ __global__ __launch_bounds__(Cfg::NT) void delta_chunk_kernel(const DeltaParams 
             const int pos = bw_pos<Cfg, DM>(t, 4 * run);
             lds_store_words(&sm.q[t][pos], qr[ps]);
             lds_store_words(&sm.k[t][pos], kr[ps]);
-            lds_store_words(&sm.vu[t][pos], vr[ps]);
+            lds_store_words(&sm.v[t][pos], vr[ps]);
         }
         if (tid < C) sm.beta[tid] = __uint_as_float(br);
         __syncthreads();
+
+        // waves on the diagonal blocks of the solve and on P: where they
+        // differ, every wave forms V - K S (which needs only the state, K and
+        // V) after its diagonal block or its P tiles, in the phase whose
+        // length the latency-bound diagonal solve sets; otherwise every wave
+        // forms it after the solve
+        constexpr int DW = NW > NBLK ? NBLK : NW;
+        constexpr int PW0 = NW > NBLK ? NBLK : 0;
+        constexpr int PW = NW - PW0;
+        constexpr bool XT_EARLY = PW0 > 0;
+
+        // ---- the state as an operand: rows n of S^T (or columns n of S),
+        // k-slots the state rows held by this lane (32 k2 + 4 g + i and
+        // 32 k2 + 16 + 4 g + i)
+        Frag sa[BF16 ? D / 32 : 1];
+        if constexpr (BF16) {
+#pragma unroll
+            for (int k2 = 0; k2 < D / 32; ++k2) {
+                const float x8[8] = {accS[2 * k2][0], accS[2 * k2][1], accS[2 * k2][2], accS[2 * k2][3],
+                                     accS[2 * k2 + 1][0], accS[2 * k2 + 1][1], accS[2 * k2 + 1][2],
+                                     accS[2 * k2 + 1][3]};
+                sa[k2] = T::from8(x8);
+            }
+        }
+        // the rows s = 16 xb + r of a D-wide tile X, k-slots matching sa
+        auto x_frag = [&](const E* X, int xb, int k2) -> Frag {
+            if constexpr (BF16) {
+                const int s = 16 * xb + r;
+                return T::load2x4(X + s * D + bw_pos<Cfg, DM>(s, 32 * k2 + 4 * g),
+                                  X + s * D + bw_pos<Cfg, DM>(s, 32 * k2 + 16 + 4 * g));
+            } else {
+                return Frag{};
+            }
+        };
+        // S^T X^T for the rows s (or t) = 16 xb + r of tile X: lane slot i
+        // holds value column n0 + 4 g + i
+        auto state_times = [&](const E* X, int xb, f32x4_t acc) {
+            if constexpr (BF16) {
+#pragma unroll
+                for (int k2 = 0; k2 < D / 32; ++k2) acc = T::mma(sa[k2], x_frag(X, xb, k2), acc);
+            } else {
+                const int s = 16 * xb + r;
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        acc = T::mma(accS[mb][i], X[s * D + bw_pos<Cfg, DM>(s, 16 * mb + 4 * g + i)], acc);
+            }
+            return acc;
+        };
+        // X S for the rows 16 xb + 4 g + i of tile X (lane slot i) and this
+        // lane's value column n0 + r: the same reads, operands swapped
+        auto times_state = [&](const E* X, int xb, f32x4_t acc) {
+            if constexpr (BF16) {
+#pragma unroll
+                for (int k2 = 0; k2 < D / 32; ++k2) acc = T::mma(x_frag(X, xb, k2), sa[k2], acc);
+            } else {
+                const int s = 16 * xb + r;
+#pragma unroll
+                for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        acc = T::mma(X[s * D + bw_pos<Cfg, DM>(s, 16 * mb + 4 * g + i)], accS[mb][i], acc);
+            }
+            return acc;
+        };
+        // V - K S for this wave's value columns, tokens 16 xb + 4 g + i of
+        // lane slot i (V read transposed into that layout)
+        f32x4_t xt[TB];
+        auto form_xt = [&]() {
+#pragma unroll
+            for (int xb = 0; xb < TB; ++xb) {
+                f32x4_t vx;
+                if constexpr (BF16) {
+                    const int row = 16 * xb + 4 * g + (r >> 2);
+                    const auto* pv = &sm.v[row][bw_pos<Cfg, DM>(row, n0 + 4 * (r & 3))];
+                    const bw_i16x4 t4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) bw_i16x4*)(pv));
+                    const uint2 u = __builtin_bit_cast(uint2, t4);
+                    vx = f32x4_t{-bf16lo(u.x), -bf16hi(u.x), -bf16lo(u.y), -bf16hi(u.y)};
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int row = 16 * xb + 4 * g + i;
+                        vx[i] = -sm.v[row][bw_pos<Cfg, DM>(row, n0 + r)];
+                    }
+                }
+                xt[xb] = -times_state(&sm.k[0][0], xb, vx);
+            }
+        };
 
         // ---- A = strict_lower(diag(beta) K K^T), computed transposed ([s][t]
         // tiles) so each lane holds 4 consecutive s of one t
@@ -210,9 +307,6 @@ __global__ __launch_bounds__(Cfg::NT) void delta_chunk_kernel(const DeltaParams 
         // T = N diag(beta) with them.  The other waves meanwhile form
         // P = Q K^T * inclusive mask ([s][t] tiles, as for A)
         {
-            constexpr int DW = NW > NBLK ? NBLK : NW;       // waves on diagonal blocks
-            constexpr int PW0 = NW > NBLK ? NBLK : 0;       // first wave on P tiles
-            constexpr int PW = NW - PW0;
             if (wave < DW) {
                 const int j = lane >> 2, qq = lane & 3;
                 for (int blk = wave; blk < NBLK; blk += DW) {
@@ -238,10 +332,11 @@ __global__ __launch_bounds__(Cfg::NT) void delta_chunk_kernel(const DeltaParams 
                     for (int m = 0; m < 4; ++m) {
                         const int row = b0 + 4 * m + qq;
                         nm[row][b0 + j] = xo[m];
-                        sm.tm[row][bw_pos<Cfg, TM>(row, b0 + j)] = T::fromf(xo[m] * bj);
+                        sm.tm[row][cc_pos<Cfg>(row, b0 + j)] = T::fromf(xo[m] * bj);
                     }
                 }
             }
+            if (XT_EARLY && wave < PW0) form_xt();
             if (wave >= PW0) {
                 int idx = 0;
 #pragma unroll
@@ -258,47 +353,17 @@ __global__ __launch_bounds__(Cfg::NT) void delta_chunk_kernel(const DeltaParams 
                         float xp[4];
 #pragma unroll
                         for (int i = 0; i < 4; ++i) xp[i] = s0 + i <= t ? ap[i] : 0.f;
-                        store_run<BF16, 4>(&sm.pm[t][bw_pos<Cfg, TM>(t, s0)], xp);
+                        store_run<BF16, 4>(&sm.pm[t][cc_pos<Cfg>(t, s0)], xp);
                     }
+                if (XT_EARLY) form_xt();
             }
         }
         __syncthreads();
 
-        // ---- the state as an operand: rows n of S^T, k-slots the state rows
-        // held by this lane (32 k2 + 4 g + i and 32 k2 + 16 + 4 g + i)
-        Frag sa[BF16 ? D / 32 : 1];
-        if constexpr (BF16) {
-#pragma unroll
-            for (int k2 = 0; k2 < D / 32; ++k2) {
-                const float x8[8] = {accS[2 * k2][0], accS[2 * k2][1], accS[2 * k2][2], accS[2 * k2][3],
-                                     accS[2 * k2 + 1][0], accS[2 * k2 + 1][1], accS[2 * k2 + 1][2],
-                                     accS[2 * k2 + 1][3]};
-                sa[k2] = T::from8(x8);
-            }
-        }
-        // S^T X^T for the rows s (or t) = 16 xb + r of tile X
-        auto state_times = [&](const E* X, int xb, f32x4_t acc) {
-            const int s = 16 * xb + r;
-            if constexpr (BF16) {
-#pragma unroll
-                for (int k2 = 0; k2 < D / 32; ++k2)
-                    acc = T::mma(sa[k2],
-                                 T::load2x4(X + s * D + bw_pos<Cfg, DM>(s, 32 * k2 + 4 * g),
-                                            X + s * D + bw_pos<Cfg, DM>(s, 32 * k2 + 16 + 4 * g)),
-                                 acc);
-            } else {
-#pragma unroll
-                for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        acc = T::mma(accS[mb][i], X[s * D + bw_pos<Cfg, DM>(s, 16 * mb + 4 * g + i)], acc);
-            }
-            return acc;
-        };
-
         // S^T Q^T of the output, formed by the waves other than wave 0 while
         // wave 0 runs the longest off-diagonal chain (it involves neither T
-        // nor this chunk's update)
+        // nor this chunk's update; V - K S there as well measured slower: the
+        // chain is short enough that the two products outlast it)
         f32x4_t oq[TB];
 #pragma unroll
         for (int tb = 0; tb < TB; ++tb) oq[tb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -306,46 +371,43 @@ __global__ __launch_bounds__(Cfg::NT) void delta_chunk_kernel(const DeltaParams 
         // ---- the blocks below the diagonal, one block column per wave (the
         // blocks of column j need only N_jj, the diagonal blocks and the
         // column's own earlier blocks, so no workgroup barrier between them):
-        // N_ij = -N_ii sum_{j <= m < i} A_im N_mj, and T_ij = N_ij beta_j
+        // N_ij = -N_ii sum_{j <= m < i} A_im N_mj, and T_ij = N_ij beta_j.
+        // The column's blocks stay in registers: a product's result (lane
+        // slot i holding row 4 g + i) is the next product's B operand with
+        // the k index 4 g + i at step i, the A operand read from LDS to match
 #pragma unroll
         for (int jb = 0; jb < NBLK - 1; ++jb) {
             if (jb % NW != wave) continue;   // uniform: compile-time block indices below
             const int bj = 16 * jb;
             const float betj = sm.beta[bj + r];
+            f32x4_t nb[NBLK];   // N_mj, m > jb: slot i holds row 16 m + 4 g + i, column bj + r
 #pragma unroll
             for (int ib = jb + 1; ib < NBLK; ++ib) {
                 const int bi = 16 * ib;
                 // one accumulator per term, so the products do not wait on each other
                 f32x4_t xm[NBLK];
+                xm[jb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int m = jb; m < ib; ++m) {
-                    const int bm = 16 * m;
+                for (int i = 0; i < 4; ++i)
+                    xm[jb] = F::mma(lm[bi + r][bj + 4 * g + i], nm[bj + 4 * g + i][bj + r], xm[jb]);
+#pragma unroll
+                for (int m = jb + 1; m < ib; ++m) {
                     xm[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int k4 = 0; k4 < 4; ++k4)
-                        xm[m] = F::mma(lm[bi + r][bm + 4 * k4 + g], nm[bm + 4 * k4 + g][bj + r], xm[m]);
+                    for (int i = 0; i < 4; ++i) xm[m] = F::mma(lm[bi + r][16 * m + 4 * g + i], nb[m][i], xm[m]);
                 }
                 f32x4_t x = xm[jb];
 #pragma unroll
                 for (int m = jb + 1; m < ib; ++m) x += xm[m];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sm.xs[wave][4 * g + i][r] = x[i];
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-                __builtin_amdgcn_wave_barrier();
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
                 f32x4_t y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int k4 = 0; k4 < 4; ++k4)
-                    y = F::mma(nm[bi + r][bi + 4 * k4 + g], sm.xs[wave][4 * k4 + g][r], y);
+                for (int i = 0; i < 4; ++i) y = F::mma(nm[bi + r][bi + 4 * g + i], x[i], y);
+                nb[ib] = -y;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int row = bi + 4 * g + i;
-                    nm[row][bj + r] = -y[i];
-                    sm.tm[row][bw_pos<Cfg, TM>(row, bj + r)] = T::fromf(-y[i] * betj);
+                    sm.tm[row][cc_pos<Cfg>(row, bj + r)] = T::fromf(-y[i] * betj);
                 }
-                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-                __builtin_amdgcn_wave_barrier();
-                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             }
         }
         // the next chunk's loads: issued here, where the waves without a block
@@ -357,59 +419,105 @@ __global__ __launch_bounds__(Cfg::NT) void delta_chunk_kernel(const DeltaParams 
             for (int tb = 0; tb < TB; ++tb) oq[tb] = state_times(&sm.q[0][0], tb, oq[tb]);
         }
         __syncthreads();
+        if (!XT_EARLY) form_xt();
 
-        // ---- W^T = K^T T^T: wave w takes key channels [16w, 16w+16) (W goes
-        // into the bytes of A and N, which are spent)
+        // ---- U' = T (V - K S) for this wave's value columns: V - K S as the
+        // B operand (k-slots tokens 32 k2 + 4 g + i and 32 k2 + 16 + 4 g + i,
+        // T read to match); lane slot i of ut[sb] holds token 16 sb + 4 g + i
+        f32x4_t ut[TB];
+        if constexpr (BF16) {
+            Frag xf[C / 32];
 #pragma unroll
-        for (int sb = 0; sb < TB; ++sb) {
-            f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+            for (int k2 = 0; k2 < C / 32; ++k2) {
+                const float x8[8] = {xt[2 * k2][0], xt[2 * k2][1], xt[2 * k2][2], xt[2 * k2][3],
+                                     xt[2 * k2 + 1][0], xt[2 * k2 + 1][1], xt[2 * k2 + 1][2],
+                                     xt[2 * k2 + 1][3]};
+                xf[k2] = T::from8(x8);
+            }
 #pragma unroll
-            for (int kk = 0; kk <= (16 * sb + 15) / MK; ++kk)
-                acc = T::mma(tr_frag<Cfg, DM>(&sm.k[0][0], D, kk * MK, n0, lane),
-                             row_frag<Cfg, TM>(&sm.tm[0][0], C, 16 * sb, kk * MK, lane), acc);
-            const int s = 16 * sb + r;
-            float xw[4] = {acc[0], acc[1], acc[2], acc[3]};
-            store_run<BF16, 4>(&ws[s][bw_pos<Cfg, DM>(s, n0 + 4 * g)], xw);
+            for (int sb = 0; sb < TB; ++sb) {
+                const int s = 16 * sb + r;
+                ut[sb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int k2 = 0; k2 <= sb / 2; ++k2)
+                    ut[sb] = T::mma(T::load2x4(&sm.tm[s][cc_pos<Cfg>(s, 32 * k2 + 4 * g)],
+                                               &sm.tm[s][cc_pos<Cfg>(s, 32 * k2 + 16 + 4 * g)]),
+                                    xf[k2], ut[sb]);
+            }
+        } else {
+#pragma unroll
+            for (int sb = 0; sb < TB; ++sb) {
+                const int s = 16 * sb + r;
+                ut[sb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int xb = 0; xb <= sb; ++xb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        ut[sb] = T::mma(sm.tm[s][cc_pos<Cfg>(s, 16 * xb + 4 * g + i)], xt[xb][i], ut[sb]);
+            }
         }
-        __syncthreads();
 
-        // ---- U'^T = V^T T^T - S^T W^T for this wave's value columns, written
-        // over its own columns of V (read whole first)
-        Frag vf[C / MK];
+        // ---- O^T = S^T Q^T + U'^T P^T, then S += K^T U', with U' as the
+        // operand in the same token order (P and K read to match)
+        Frag uf[BF16 ? C / 32 : 1];
+        if constexpr (BF16) {
 #pragma unroll
-        for (int kk = 0; kk < C / MK; ++kk) vf[kk] = tr_frag<Cfg, DM>(&sm.vu[0][0], D, kk * MK, n0, lane);
-#pragma unroll
-        for (int sb = 0; sb < TB; ++sb) {
-            f32x4_t acc = state_times(&ws[0][0], sb, f32x4_t{0.f, 0.f, 0.f, 0.f});
-            acc = -acc;
-#pragma unroll
-            for (int kk = 0; kk <= (16 * sb + 15) / MK; ++kk)
-                acc = T::mma(vf[kk], row_frag<Cfg, TM>(&sm.tm[0][0], C, 16 * sb, kk * MK, lane), acc);
-            const int s = 16 * sb + r;
-            float xu[4] = {acc[0], acc[1], acc[2], acc[3]};
-            store_run<BF16, 4>(&sm.vu[s][bw_pos<Cfg, DM>(s, n0 + 4 * g)], xu);
+            for (int k2 = 0; k2 < C / 32; ++k2) {
+                const float x8[8] = {ut[2 * k2][0], ut[2 * k2][1], ut[2 * k2][2], ut[2 * k2][3],
+                                     ut[2 * k2 + 1][0], ut[2 * k2 + 1][1], ut[2 * k2 + 1][2],
+                                     ut[2 * k2 + 1][3]};
+                uf[k2] = T::from8(x8);
+            }
         }
-        // (no barrier: each wave reads back only its own columns of U')
-
-        // ---- O^T = S^T Q^T + U'^T P^T, then S += K^T U'
-        Frag uf[C / MK];
-#pragma unroll
-        for (int kk = 0; kk < C / MK; ++kk) uf[kk] = tr_frag<Cfg, DM>(&sm.vu[0][0], D, kk * MK, n0, lane);
 #pragma unroll
         for (int tb = 0; tb < TB; ++tb) {
             f32x4_t acc = wave != 0 ? oq[tb] : state_times(&sm.q[0][0], tb, oq[tb]);
+            const int t = 16 * tb + r;
+            if constexpr (BF16) {
 #pragma unroll
-            for (int kk = 0; kk <= (16 * tb + 15) / MK; ++kk)
-                acc = T::mma(uf[kk], row_frag<Cfg, TM>(&sm.pm[0][0], C, 16 * tb, kk * MK, lane), acc);
-            const uint32_t off = ((uint32_t)(t0 + 16 * tb + r) * D + n0 + 4 * g) * ES;
+                for (int k2 = 0; k2 <= tb / 2; ++k2)
+                    acc = T::mma(uf[k2],
+                                 T::load2x4(&sm.pm[t][cc_pos<Cfg>(t, 32 * k2 + 4 * g)],
+                                            &sm.pm[t][cc_pos<Cfg>(t, 32 * k2 + 16 + 4 * g)]),
+                                 acc);
+            } else {
+#pragma unroll
+                for (int sb = 0; sb <= tb; ++sb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        acc = T::mma(ut[sb][i], sm.pm[t][cc_pos<Cfg>(t, 16 * sb + 4 * g + i)], acc);
+            }
+            const uint32_t off = ((uint32_t)(t0 + t) * D + n0 + 4 * g) * ES;
             float xo[4] = {acc[0], acc[1], acc[2], acc[3]};
             buf_store_run4<BF16>(ro, off, xo);
         }
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
+        for (int mb = 0; mb < MB; ++mb) {
+            if constexpr (BF16) {
+                // K^T: state rows 16 mb + r, k-slots tokens 32 k2 + 4 g + i
+                // and 32 k2 + 16 + 4 g + i (two transposing reads)
 #pragma unroll
-            for (int kk = 0; kk < C / MK; ++kk)
-                accS[mb] = T::mma(tr_frag<Cfg, DM>(&sm.k[0][0], D, kk * MK, 16 * mb, lane), uf[kk], accS[mb]);
+                for (int k2 = 0; k2 < C / 32; ++k2) {
+                    const int rowa = 32 * k2 + 4 * g + (r >> 2), rowb = rowa + 16;
+                    const int col = 16 * mb + 4 * (r & 3);
+                    const bw_i16x4 ka = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) bw_i16x4*)(&sm.k[rowa][bw_pos<Cfg, DM>(rowa, col)]));
+                    const bw_i16x4 kb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (__attribute__((address_space(3))) bw_i16x4*)(&sm.k[rowb][bw_pos<Cfg, DM>(rowb, col)]));
+                    const uint2 ua = __builtin_bit_cast(uint2, ka), ub = __builtin_bit_cast(uint2, kb);
+                    accS[mb] = T::mma(__builtin_bit_cast(Frag, make_uint4(ua.x, ua.y, ub.x, ub.y)), uf[k2],
+                                      accS[mb]);
+                }
+            } else {
+#pragma unroll
+                for (int sb = 0; sb < TB; ++sb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int row = 16 * sb + 4 * g + i;
+                        accS[mb] = T::mma(sm.k[row][bw_pos<Cfg, DM>(row, 16 * mb + r)], ut[sb][i], accS[mb]);
+                    }
+            }
+        }
         __syncthreads();
     }
 
