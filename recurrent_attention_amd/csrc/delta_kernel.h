@@ -168,10 +168,13 @@ __global__ __launch_bounds__(Cfg::NT) void delta_chunk_kernel(const DeltaParams 
     for (int c = 0; c < nchunks; ++c) {
         // the lane index, opaque to the compiler in each chunk: otherwise the
         // many lane-dependent LDS addresses of a chunk are hoisted out of the
-        // walk and held in registers across it
+        // walk and held in registers across it; masked again, so that the
+        // compiler still knows its range (a lane index it must take as
+        // possibly negative turns every column / 8 of the tile addresses
+        // into a signed division)
         int lane_o = tid & 63;
         asm volatile("" : "+v"(lane_o));
-        const int lane = lane_o;
+        const int lane = lane_o & 63;
         const int r = lane & 15, g = lane >> 4;
         const int t0 = c * C;
         // ---- tiles (tokens past the end read as zeros: no key, no write)
