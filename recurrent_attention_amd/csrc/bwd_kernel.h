@@ -234,6 +234,7 @@ __global__ __launch_bounds__(Cfg::NT) void bwd_kernel(const BwdParams p) {
         // out of the walk and held in registers across it
         int lane = tid & 63;
         asm volatile("" : "+v"(lane));
+        lane &= 63;
         const int r = lane & 15, g = lane >> 4;
         const int ch0 = 16 * wave + 4 * g;    // this thread's 4 channels (keys and values)
         const int t0 = c * C;
