@@ -30,6 +30,14 @@ def tr_128_old(row):
     return (row ^ (row >> 3)) & 7
 
 
+def cc_128(row):            # 64 x 64 bf16 P and T tiles of the delta rule (delta_kernel.h cc_pos)
+    return (row ^ (row >> 3)) & 7
+
+
+def cc_128_old(row):
+    return row & 7
+
+
 def g_512(row):             # fp32 G tile of the gradient kernel (bwd_kernel.h g_pos)
     return (row & 3) | ((((row >> 2) ^ (row >> 3)) & 1) << 2) | (((row >> 2) & 1) << 3)
 
@@ -68,6 +76,28 @@ def test_256_byte_rows():
     assert old["tr"] == 2 and old["rowfrag"] == 0
 
 
+def test_256_byte_rows_token_pairs_16_apart():
+    """The delta rule's transposing reads of K and V (rows 4 g + i and
+    16 + 4 g + i of a 32-token group, matching a matrix-core result used as
+    the next operand) stay conflict-free under the same swizzle."""
+    a = bf16_addr(bf16_256, 256)
+    tr = [conflict_cycles("read_tr8", [a(k0 + 4 * (l >> 4) + ((l & 15) >> 2) + ex, c0 + 4 * (l & 3))
+                                       for l in LANES])
+          for k0 in (0, 32) for c0 in range(0, 128, 16) for ex in (0, 16)]
+    assert max(tr) == 0
+
+
+def test_delta_64_by_64_tiles():
+    """P and T, [64][64] bf16 (rows of 128 bytes), read in 8-byte row reads
+    (rows 16 b + r, columns 32 k + 4 g and 32 k + 16 + 4 g)."""
+    def rowread(f):
+        a = bf16_addr(f, 128)
+        return max(conflict_cycles("read8", [a(16 * xb + (l & 15), 32 * k2 + off + 4 * (l >> 4)) for l in LANES])
+                   for xb in range(4) for k2 in range(2) for off in (0, 16))
+    assert rowread(cc_128) == 0
+    assert rowread(cc_128_old) == 2
+
+
 def pats_tr128(a):
     """The transposed K / V tiles of the chunk kernels: [128][64] bf16."""
     frag = [conflict_cycles("read16", [a(16 * mb + (l & 15), 32 * kk + 8 * (l >> 4)) for l in LANES])
@@ -104,7 +134,7 @@ def test_g_tile():
     assert pats_g(g_addr(g_512_old))[0] == 2
 
 
-@pytest.mark.parametrize("f,units", [(bf16_256, 16), (tr_128, 8), (g_512, 32)])
+@pytest.mark.parametrize("f,units", [(bf16_256, 16), (tr_128, 8), (cc_128, 8), (g_512, 32)])
 def test_swizzles_keep_each_row_a_permutation(f, units):
     for row in range(128):
         assert sorted(u ^ f(row) for u in range(units)) == list(range(units))
