@@ -189,16 +189,6 @@ __global__ __launch_bounds__(Cfg::NT) void delta_chunk_kernel(const DeltaParams 
         if (tid < C) sm.beta[tid] = __uint_as_float(br);
         __syncthreads();
 
-        // waves on the diagonal blocks of the solve and on P: where they
-        // differ, every wave forms V - K S (which needs only the state, K and
-        // V) after its diagonal block or its P tiles, in the phase whose
-        // length the latency-bound diagonal solve sets; otherwise every wave
-        // forms it after the solve
-        constexpr int DW = NW > NBLK ? NBLK : NW;
-        constexpr int PW0 = NW > NBLK ? NBLK : 0;
-        constexpr int PW = NW - PW0;
-        constexpr bool XT_EARLY = PW0 > 0;
-
         // ---- the state as an operand: rows n of S^T (or columns n of S),
         // k-slots the state rows held by this lane (32 k2 + 4 g + i and
         // 32 k2 + 16 + 4 g + i)
@@ -304,49 +294,62 @@ __global__ __launch_bounds__(Cfg::NT) void delta_chunk_kernel(const DeltaParams 
         __syncthreads();
 
         // ---- the diagonal 16 x 16 blocks of N = (I + A)^-1 by forward
-        // substitution, one wave per block: the lane quad 4j..4j+3 solves
-        // for column j, lane q of it holding rows q, q+4, q+8, q+12 and
-        // summing every fourth term of each row's dot product; their part of
-        // T = N diag(beta) with them.  The other waves meanwhile form
-        // P = Q K^T * inclusive mask ([s][t] tiles, as for A)
+        // substitution in wave 0, one lane per column (lane 16 blk + j solves
+        // column j of block blk: no exchange between lanes, A's rows read as
+        // broadcasts); their part of T = N diag(beta) with them.  The other
+        // waves meanwhile form P = Q K^T * inclusive mask ([s][t] tiles, as
+        // for A).  Then every wave forms its columns of V - K S, which needs
+        // only the state, K and V.
         {
-            if (wave < DW) {
-                const int j = lane >> 2, qq = lane & 3;
-                for (int blk = wave; blk < NBLK; blk += DW) {
+            if (wave == 0) {
+                const int blk = lane >> 4, j = lane & 15;
+                if (blk < NBLK) {
                     const int b0 = 16 * blk;
-                    float xo[4] = {0.f, 0.f, 0.f, 0.f};   // x[4 m + qq]
+                    float x[16];   // column j of the block, rows 0..15
+                    // A's rows, read two rows ahead of their use (the
+                    // scheduling barriers keep that order: left alone, the
+                    // compiler issues each row's reads just before it)
+                    float4 arow[16][4];
+                    auto read_row = [&](int rr) {
+#pragma unroll
+                        for (int m4 = 0; 4 * m4 < rr; ++m4)
+                            arow[rr][m4] = *reinterpret_cast<const float4*>(&lm[b0 + rr][b0 + 4 * m4]);
+                    };
+                    read_row(1);
+                    read_row(2);
 #pragma unroll
                     for (int rr = 0; rr < 16; ++rr) {
-                        float part = 0.f;
+                        if (rr + 2 < 16) read_row(rr + 2);
+                        // one partial sum per group of four earlier rows, so
+                        // that only the newest group waits on row rr - 1
+                        float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                        for (int m = 0; m < 4; ++m) {
-                            if (4 * m >= rr) break;
-                            const int cc = 4 * m + qq;
-                            const float a = lm[b0 + rr][b0 + cc];   // 0 for cc >= rr
-                            part += a * xo[m];
+                        for (int m4 = 0; 4 * m4 < rr; ++m4) {
+                            const float av[4] = {arow[rr][m4].x, arow[rr][m4].y, arow[rr][m4].z, arow[rr][m4].w};
+#pragma unroll
+                            for (int i = 0; i < 4; ++i)
+                                if (4 * m4 + i < rr) part[m4] += av[i] * x[4 * m4 + i];
                         }
-                        part += dpp_row<0xB1>(part);   // quad_perm [1,0,3,2]
-                        part += dpp_row<0x4E>(part);   // quad_perm [2,3,0,1]
-                        const float xr = (rr == j ? 1.f : 0.f) - part;
-                        if (qq == (rr & 3)) xo[rr >> 2] = xr;
+                        x[rr] = (rr == j ? 1.f : 0.f) - ((part[0] + part[1]) + (part[2] + part[3]));
+                        __builtin_amdgcn_sched_barrier(0);
                     }
                     const float bj = sm.beta[b0 + j];
 #pragma unroll
-                    for (int m = 0; m < 4; ++m) {
-                        const int row = b0 + 4 * m + qq;
-                        nm[row][b0 + j] = xo[m];
-                        sm.tm[row][cc_pos<Cfg>(row, b0 + j)] = T::fromf(xo[m] * bj);
+                    for (int m = 0; m < 16; ++m) {
+                        nm[b0 + m][b0 + j] = x[m];
+                        sm.tm[b0 + m][cc_pos<Cfg>(b0 + m, b0 + j)] = T::fromf(x[m] * bj);
                     }
                 }
             }
-            if (XT_EARLY && wave < PW0) form_xt();
-            if (wave >= PW0) {
+            // P on the other waves (on every wave when there are fewer than 4)
+            constexpr int P0 = NW >= 4 ? 1 : 0, PW = NW - P0;
+            if (wave >= P0) {
                 int idx = 0;
 #pragma unroll
                 for (int tb = 0; tb < TB; ++tb)
 #pragma unroll
                     for (int sb = 0; sb <= tb; ++sb, ++idx) {
-                        if (idx % PW != wave - PW0) continue;
+                        if (idx % PW != wave - P0) continue;
                         f32x4_t ap = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                         for (int kk = 0; kk < D / MK; ++kk)
@@ -358,8 +361,8 @@ __global__ __launch_bounds__(Cfg::NT) void delta_chunk_kernel(const DeltaParams 
                         for (int i = 0; i < 4; ++i) xp[i] = s0 + i <= t ? ap[i] : 0.f;
                         store_run<BF16, 4>(&sm.pm[t][cc_pos<Cfg>(t, s0)], xp);
                     }
-                if (XT_EARLY) form_xt();
             }
+            form_xt();
         }
         __syncthreads();
 
@@ -422,7 +425,6 @@ __global__ __launch_bounds__(Cfg::NT) void delta_chunk_kernel(const DeltaParams 
             for (int tb = 0; tb < TB; ++tb) oq[tb] = state_times(&sm.q[0][0], tb, oq[tb]);
         }
         __syncthreads();
-        if (!XT_EARLY) form_xt();
 
         // ---- U' = T (V - K S) for this wave's value columns: V - K S as the
         // B operand (k-slots tokens 32 k2 + 4 g + i and 32 k2 + 16 + 4 g + i,
