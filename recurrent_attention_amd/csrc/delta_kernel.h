@@ -80,6 +80,11 @@ struct DeltaSmem {
     static constexpr int LDP = C + 4;
     alignas(16) float lm[C][LDP];
     alignas(16) float nm[C][LDP];
+    // with 8 waves over 64-token chunks, wave 0's state block as operand
+    // fragments (lane-major) and the S^T Q^T that wave 3 forms from them
+    static constexpr bool HELP = Cfg::BF16 && Cfg::NW == 8 && Cfg::NBLK == 4;
+    alignas(16) uint4 sa0[HELP ? D / 32 : 1][64];
+    alignas(16) f32x4_t oq0[HELP ? Cfg::TB : 1][64];
     float beta[C];
 };
 
@@ -201,6 +206,16 @@ __global__ __launch_bounds__(Cfg::NT) void delta_chunk_kernel(const DeltaParams 
                                      accS[2 * k2 + 1][3]};
                 sa[k2] = T::from8(x8);
             }
+        }
+        // wave 0 lends its state block to the helper wave (read after the
+        // barrier that ends the diagonal solve, rewritten only after the
+        // next chunk's first barrier)
+        constexpr bool HELP = DeltaSmem<Cfg>::HELP;
+        constexpr int HW = 3;   // the helper: no block column, SIMD shared with wave 7
+        if constexpr (HELP) {
+            if (wave == 0)
+#pragma unroll
+                for (int k2 = 0; k2 < D / 32; ++k2) sm.sa0[k2][lane] = __builtin_bit_cast(uint4, sa[k2]);
         }
         // the rows s = 16 xb + r of a D-wide tile X, k-slots matching sa
         auto x_frag = [&](const E* X, int xb, int k2) -> Frag {
@@ -420,7 +435,26 @@ __global__ __launch_bounds__(Cfg::NT) void delta_chunk_kernel(const DeltaParams 
         // column would otherwise wait for the off-diagonal chain (the
         // registers were emptied into this chunk's tiles)
         if (c + 1 < nchunks) load(c + 1);
-        if (wave != 0) {
+        if (HELP && wave == HW) {
+            // its own S^T Q^T and wave 0's, over the same Q fragments; wave
+            // 0's handed back through LDS (read after the next barrier)
+            if constexpr (HELP) {
+                Frag s0[D / 32];
+#pragma unroll
+                for (int k2 = 0; k2 < D / 32; ++k2) s0[k2] = __builtin_bit_cast(Frag, sm.sa0[k2][lane]);
+#pragma unroll
+                for (int tb = 0; tb < TB; ++tb) {
+                    f32x4_t o0 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int k2 = 0; k2 < D / 32; ++k2) {
+                        const Frag qf = x_frag(&sm.q[0][0], tb, k2);
+                        oq[tb] = T::mma(sa[k2], qf, oq[tb]);
+                        o0 = T::mma(s0[k2], qf, o0);
+                    }
+                    sm.oq0[tb][lane] = o0;
+                }
+            }
+        } else if (wave != 0) {
 #pragma unroll
             for (int tb = 0; tb < TB; ++tb) oq[tb] = state_times(&sm.q[0][0], tb, oq[tb]);
         }
@@ -476,7 +510,9 @@ __global__ __launch_bounds__(Cfg::NT) void delta_chunk_kernel(const DeltaParams 
         }
 #pragma unroll
         for (int tb = 0; tb < TB; ++tb) {
-            f32x4_t acc = wave != 0 ? oq[tb] : state_times(&sm.q[0][0], tb, oq[tb]);
+            f32x4_t acc;
+            if constexpr (HELP) acc = wave != 0 ? oq[tb] : sm.oq0[tb][lane];
+            else acc = wave != 0 ? oq[tb] : state_times(&sm.q[0][0], tb, oq[tb]);
             const int t = 16 * tb + r;
             if constexpr (BF16) {
 #pragma unroll
