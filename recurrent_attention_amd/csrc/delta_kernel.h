@@ -316,48 +316,98 @@ __global__ __launch_bounds__(Cfg::NT) void delta_chunk_kernel(const DeltaParams 
         // for A).  Then every wave forms its columns of V - K S, which needs
         // only the state, K and V.
         {
-            if (wave == 0) {
-                const int blk = lane >> 4, j = lane & 15;
-                if (blk < NBLK) {
-                    const int b0 = 16 * blk;
-                    float x[16];   // column j of the block, rows 0..15
-                    // A's rows, read two rows ahead of their use (the
-                    // scheduling barriers keep that order: left alone, the
-                    // compiler issues each row's reads just before it)
-                    float4 arow[16][4];
-                    auto read_row = [&](int rr) {
+            // with 8 waves: two lanes per column on waves 0 and 1 (two blocks
+            // each), each lane summing half of every row's terms
+            constexpr bool SOLVE2 = NW == 8;
+            if (SOLVE2 ? wave < 2 : wave == 0) {
+                if constexpr (SOLVE2) {
+                    // lane 32 bs + 2 j + h solves column j of block 2 w + bs; it
+                    // keeps the rows of the groups of four 4 h.. and 8 + 4 h..
+                    // (slot p: row 8 (p >> 2) + 4 h + (p & 3)) and sums their
+                    // terms (terms of rows not yet solved are zero: their A
+                    // entries are on or above the diagonal); one DPP swap
+                    // adds the partner lane's half
+                    const int bs = lane >> 5, j = (lane >> 1) & 15, h = lane & 1;
+                    const int blk = 2 * wave + bs;
+                    if (blk < NBLK) {
+                        const int b0 = 16 * blk;
+                        float xs[8];
 #pragma unroll
-                        for (int m4 = 0; 4 * m4 < rr; ++m4)
-                            arow[rr][m4] = *reinterpret_cast<const float4*>(&lm[b0 + rr][b0 + 4 * m4]);
-                    };
-                    read_row(1);
-                    read_row(2);
+                        for (int q = 0; q < 8; ++q) xs[q] = 0.f;
+                        float4 arow[16][2];
+                        auto read_row = [&](int rr) {
 #pragma unroll
-                    for (int rr = 0; rr < 16; ++rr) {
-                        if (rr + 2 < 16) read_row(rr + 2);
-                        // one partial sum per group of four earlier rows, so
-                        // that only the newest group waits on row rr - 1
-                        float part[4] = {0.f, 0.f, 0.f, 0.f};
+                            for (int q = 0; 8 * q < rr; ++q)
+                                arow[rr][q] = *reinterpret_cast<const float4*>(&lm[b0 + rr][b0 + 8 * q + 4 * h]);
+                        };
+                        read_row(1);
+                        read_row(2);
 #pragma unroll
-                        for (int m4 = 0; 4 * m4 < rr; ++m4) {
-                            const float av[4] = {arow[rr][m4].x, arow[rr][m4].y, arow[rr][m4].z, arow[rr][m4].w};
+                        for (int rr = 0; rr < 16; ++rr) {
+                            if (rr + 2 < 16) read_row(rr + 2);
+                            float part[2] = {0.f, 0.f};
 #pragma unroll
-                            for (int i = 0; i < 4; ++i)
-                                if (4 * m4 + i < rr) part[m4] += av[i] * x[4 * m4 + i];
+                            for (int q = 0; 8 * q < rr; ++q)
+                                part[q] = (arow[rr][q].x * xs[4 * q] + arow[rr][q].y * xs[4 * q + 1]) +
+                                          (arow[rr][q].z * xs[4 * q + 2] + arow[rr][q].w * xs[4 * q + 3]);
+                            float sum = part[0] + part[1];
+                            sum += dpp_row<0xB1>(sum);   // quad_perm [1,0,3,2]: the partner lane
+                            const float xr = (rr == j ? 1.f : 0.f) - sum;
+                            const int pslot = 4 * (rr >> 3) + (rr & 3);
+                            xs[pslot] = ((rr >> 2) & 1) == h ? xr : xs[pslot];
+                            __builtin_amdgcn_sched_barrier(0);
                         }
-                        x[rr] = (rr == j ? 1.f : 0.f) - ((part[0] + part[1]) + (part[2] + part[3]));
-                        __builtin_amdgcn_sched_barrier(0);
-                    }
-                    const float bj = sm.beta[b0 + j];
+                        const float bj = sm.beta[b0 + j];
 #pragma unroll
-                    for (int m = 0; m < 16; ++m) {
-                        nm[b0 + m][b0 + j] = x[m];
-                        sm.tm[b0 + m][cc_pos<Cfg>(b0 + m, b0 + j)] = T::fromf(x[m] * bj);
+                        for (int q = 0; q < 8; ++q) {
+                            const int row = b0 + 8 * (q >> 2) + 4 * h + (q & 3);
+                            nm[row][b0 + j] = xs[q];
+                            sm.tm[row][cc_pos<Cfg>(row, b0 + j)] = T::fromf(xs[q] * bj);
+                        }
+                    }
+                } else {
+                    const int blk = lane >> 4, j = lane & 15;
+                    if (blk < NBLK) {
+                        const int b0 = 16 * blk;
+                        float x[16];   // column j of the block, rows 0..15
+                        // A's rows, read two rows ahead of their use (the
+                        // scheduling barriers keep that order: left alone, the
+                        // compiler issues each row's reads just before it)
+                        float4 arow[16][4];
+                        auto read_row = [&](int rr) {
+#pragma unroll
+                            for (int m4 = 0; 4 * m4 < rr; ++m4)
+                                arow[rr][m4] = *reinterpret_cast<const float4*>(&lm[b0 + rr][b0 + 4 * m4]);
+                        };
+                        read_row(1);
+                        read_row(2);
+#pragma unroll
+                        for (int rr = 0; rr < 16; ++rr) {
+                            if (rr + 2 < 16) read_row(rr + 2);
+                            // one partial sum per group of four earlier rows, so
+                            // that only the newest group waits on row rr - 1
+                            float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                            for (int m4 = 0; 4 * m4 < rr; ++m4) {
+                                const float av[4] = {arow[rr][m4].x, arow[rr][m4].y, arow[rr][m4].z, arow[rr][m4].w};
+#pragma unroll
+                                for (int i = 0; i < 4; ++i)
+                                    if (4 * m4 + i < rr) part[m4] += av[i] * x[4 * m4 + i];
+                            }
+                            x[rr] = (rr == j ? 1.f : 0.f) - ((part[0] + part[1]) + (part[2] + part[3]));
+                            __builtin_amdgcn_sched_barrier(0);
+                        }
+                        const float bj = sm.beta[b0 + j];
+#pragma unroll
+                        for (int m = 0; m < 16; ++m) {
+                            nm[b0 + m][b0 + j] = x[m];
+                            sm.tm[b0 + m][cc_pos<Cfg>(b0 + m, b0 + j)] = T::fromf(x[m] * bj);
+                        }
                     }
                 }
             }
             // P on the other waves (on every wave when there are fewer than 4)
-            constexpr int P0 = NW >= 4 ? 1 : 0, PW = NW - P0;
+            constexpr int P0 = SOLVE2 ? 2 : NW >= 4 ? 1 : 0, PW = NW - P0;
             if (wave >= P0) {
                 int idx = 0;
 #pragma unroll
