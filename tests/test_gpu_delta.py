@@ -75,6 +75,16 @@ def test_delta_edge_lengths(L):
     _check(got, ref, torch.bfloat16, f"delta L={L}")
 
 
+# bf16 at d = 128 with 64-token chunks is the 8-wave layout: diagonal
+# blocks solved two lanes per column on two waves, wave 0's output product
+# formed by another wave; lengths from one token to ragged multi-chunk tails
+@pytest.mark.parametrize("L", [1, 17, 64, 65, 130, 200])
+def test_delta_edge_lengths_d128(L):
+    inp = workloads.delta_inputs(1, 3, L, 128, 128, torch.bfloat16, seed=1000 + L, with_state=True)
+    got, ref = _run(inp)
+    _check(got, ref, torch.bfloat16, f"delta d=128 L={L}")
+
+
 @pytest.mark.parametrize("beta", [0.0, 1.0])
 def test_delta_write_strength_limits(beta):
     inp = workloads.delta_inputs(1, 2, 150, 64, 64, torch.float32, seed=7, with_state=True)
