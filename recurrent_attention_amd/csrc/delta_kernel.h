@@ -451,33 +451,74 @@ __global__ __launch_bounds__(Cfg::NT) void delta_chunk_kernel(const DeltaParams 
             if (jb % NW != wave) continue;   // uniform: compile-time block indices below
             const int bj = 16 * jb;
             const float betj = sm.beta[bj + r];
-            f32x4_t nb[NBLK];   // N_mj, m > jb: slot i holds row 16 m + 4 g + i, column bj + r
+            if constexpr (BF16) {
+                // bf16 inputs: the products on 16x16x16 bf16 matrix cores (one
+                // instruction per block product, against four fp32 ones),
+                // whose B operand is a result's accumulator layout as it
+                // stands (k = 4 g + i in slot i); A, the diagonal blocks of N
+                // and the column's blocks rounded to bf16 as operands, sums in
+                // fp32 (T itself is stored in bf16)
+                auto pk4 = [](float a, float b, float c, float d) {
+                    return __builtin_bit_cast(bw_i16x4, make_uint2(pack_bf16(a, b), pack_bf16(c, d)));
+                };
+                auto row4 = [&](const float* p) {
+                    const float4 v = *reinterpret_cast<const float4*>(p);
+                    return pk4(v.x, v.y, v.z, v.w);
+                };
+                const bw_i16x4 njj = pk4(nm[bj + 4 * g][bj + r], nm[bj + 4 * g + 1][bj + r],
+                                         nm[bj + 4 * g + 2][bj + r], nm[bj + 4 * g + 3][bj + r]);
+                bw_i16x4 nbp[NBLK];   // N_mj, m > jb, as B operands
 #pragma unroll
-            for (int ib = jb + 1; ib < NBLK; ++ib) {
-                const int bi = 16 * ib;
-                // one accumulator per term, so the products do not wait on each other
-                f32x4_t xm[NBLK];
-                xm[jb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                for (int ib = jb + 1; ib < NBLK; ++ib) {
+                    const int bi = 16 * ib;
+                    f32x4_t xm[NBLK];
+                    xm[jb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(row4(&lm[bi + r][bj + 4 * g]), njj,
+                                                                      f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    xm[jb] = F::mma(lm[bi + r][bj + 4 * g + i], nm[bj + 4 * g + i][bj + r], xm[jb]);
+                    for (int m = jb + 1; m < ib; ++m)
+                        xm[m] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(row4(&lm[bi + r][16 * m + 4 * g]), nbp[m],
+                                                                         f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                    f32x4_t x = xm[jb];
 #pragma unroll
-                for (int m = jb + 1; m < ib; ++m) {
-                    xm[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+                    for (int m = jb + 1; m < ib; ++m) x += xm[m];
+                    const f32x4_t y = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+                        row4(&nm[bi + r][bi + 4 * g]), pk4(x[0], x[1], x[2], x[3]), f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+                    nbp[ib] = pk4(-y[0], -y[1], -y[2], -y[3]);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) xm[m] = F::mma(lm[bi + r][16 * m + 4 * g + i], nb[m][i], xm[m]);
+                    for (int i = 0; i < 4; ++i) {
+                        const int row = bi + 4 * g + i;
+                        sm.tm[row][cc_pos<Cfg>(row, bj + r)] = T::fromf(-y[i] * betj);
+                    }
                 }
-                f32x4_t x = xm[jb];
+            } else {
+                f32x4_t nb[NBLK];   // N_mj, m > jb: slot i holds row 16 m + 4 g + i, column bj + r
 #pragma unroll
-                for (int m = jb + 1; m < ib; ++m) x += xm[m];
-                f32x4_t y = {0.f, 0.f, 0.f, 0.f};
+                for (int ib = jb + 1; ib < NBLK; ++ib) {
+                    const int bi = 16 * ib;
+                    // one accumulator per term, so the products do not wait on each other
+                    f32x4_t xm[NBLK];
+                    xm[jb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int i = 0; i < 4; ++i) y = F::mma(nm[bi + r][bi + 4 * g + i], x[i], y);
-                nb[ib] = -y;
+                    for (int i = 0; i < 4; ++i)
+                        xm[jb] = F::mma(lm[bi + r][bj + 4 * g + i], nm[bj + 4 * g + i][bj + r], xm[jb]);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int row = bi + 4 * g + i;
-                    sm.tm[row][cc_pos<Cfg>(row, bj + r)] = T::fromf(-y[i] * betj);
+                    for (int m = jb + 1; m < ib; ++m) {
+                        xm[m] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) xm[m] = F::mma(lm[bi + r][16 * m + 4 * g + i], nb[m][i], xm[m]);
+                    }
+                    f32x4_t x = xm[jb];
+#pragma unroll
+                    for (int m = jb + 1; m < ib; ++m) x += xm[m];
+                    f32x4_t y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) y = F::mma(nm[bi + r][bi + 4 * g + i], x[i], y);
+                    nb[ib] = -y;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int row = bi + 4 * g + i;
+                        sm.tm[row][cc_pos<Cfg>(row, bj + r)] = T::fromf(-y[i] * betj);
+                    }
                 }
             }
         }

@@ -28,6 +28,7 @@ from dataclasses import dataclass
 
 REQUIRED_WAIT_STATES = {
     "v_mfma_f32_16x16x32_bf16": 8,
+    "v_mfma_f32_16x16x16_bf16": 8,
     "v_mfma_f32_16x16x4_f32": 10,
 }
 
