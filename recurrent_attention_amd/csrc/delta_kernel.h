@@ -15,9 +15,11 @@
 // because the chunk's product of (I - beta k k^T) factors is I - K^T W and
 // its accumulated writes are K^T U, with W = T K and U = T V (so that
 // U' = U - W S; W itself is never formed).  Everything but T is a dense
-// product on the matrix cores; T is formed in fp32 by blocked forward
-// substitution (16 x 16 diagonal blocks inverted by one lane per column, the
-// blocks below them by fp32 matrix-core products, one block column per wave).
+// product on the matrix cores; T is formed by blocked forward substitution
+// (16 x 16 diagonal blocks inverted in fp32 by one or two lanes per column,
+// the blocks below them by matrix-core products, bf16 operands with fp32
+// sums for bf16 inputs and fp32 throughout for fp32 inputs, one block
+// column per wave).
 //
 // One workgroup per (b,h) runs the chunks in order (the chunk-to-chunk map
 // S -> (I - K^T W) S + K^T U is a full d_k x d_k matrix, so the segment
