@@ -58,10 +58,11 @@ struct DeltaCfg {
     // 16 different bank groups
     static constexpr int DMASK = (DU < 16 ? DU : 16) - 1;
     static constexpr int TMASK = (TU < 8 ? TU : 8) - 1;
-    static constexpr int RUNS = D / 4;                 // 4-channel runs per token row
-    static constexpr int RPP = NT / RUNS;              // token rows per load pass (16)
+    static constexpr int CPR = 16 / (int)sizeof(E);   // channels of a 16-byte run
+    static constexpr int RUNS = D / CPR;               // runs per token row
+    static constexpr int RPP = NT / RUNS;              // token rows per load pass
     static constexpr int NPASS = C / RPP;
-    static constexpr int RW = 4 * (int)sizeof(E) / 4;  // words of a 4-channel run
+    static constexpr int RW = 4;                       // words of a run
     static_assert(D % 16 == 0 && C % 16 == 0 && C % MK == 0, "tile shape");
     static_assert(!BF16 || D % 32 == 0, "bf16 needs d >= 32");
     static_assert(NT % RUNS == 0 && C % RPP == 0, "load mapping");
@@ -154,7 +155,7 @@ __global__ __launch_bounds__(Cfg::NT) void delta_chunk_kernel(const DeltaParams 
         for (int i = 0; i < 4; ++i)
             accS[mb][i] = S0 ? S0[(size_t)(16 * mb + 4 * g + i) * D + n0 + r] : 0.f;
 
-    // global -> registers, one chunk ahead: a 4-channel run of q, k, v for
+    // global -> registers, one chunk ahead: a 16-byte run of q, k, v for
     // NPASS token rows, and one write strength (non-temporal loads: each
     // element is read once)
     const int run = tid % RUNS, row0 = tid / RUNS;
@@ -163,7 +164,7 @@ __global__ __launch_bounds__(Cfg::NT) void delta_chunk_kernel(const DeltaParams 
     auto load = [&](int c) {
 #pragma unroll
         for (int ps = 0; ps < NPASS; ++ps) {
-            const uint32_t off = (((uint32_t)c * C + row0 + RPP * ps) * D + 4 * run) * ES;
+            const uint32_t off = (((uint32_t)c * C + row0 + RPP * ps) * D + Cfg::CPR * run) * ES;
             qr[ps] = buf_load_words<RW, LOAD_NT>(rq, off);
             kr[ps] = buf_load_words<RW, LOAD_NT>(rk, off);
             vr[ps] = buf_load_words<RW, LOAD_NT>(rv, off);
@@ -188,7 +189,7 @@ __global__ __launch_bounds__(Cfg::NT) void delta_chunk_kernel(const DeltaParams 
 #pragma unroll
         for (int ps = 0; ps < NPASS; ++ps) {
             const int t = row0 + RPP * ps;
-            const int pos = bw_pos<Cfg, DM>(t, 4 * run);
+            const int pos = bw_pos<Cfg, DM>(t, Cfg::CPR * run);
             lds_store_words(&sm.q[t][pos], qr[ps]);
             lds_store_words(&sm.k[t][pos], kr[ps]);
             lds_store_words(&sm.v[t][pos], vr[ps]);
